@@ -1,0 +1,291 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU oracle for the LoRA-bypass linear.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline use it.  It shares no code with the GPU library: its dtype
+ * policy, its rounding and its contractions are written here from the
+ * definitions, independently of the HIP kernels.
+ *
+ * What it computes (all arithmetic in IEEE binary64, rounding only at the
+ * declared boundaries):
+ *
+ *   policy   -- LyCORIS "Precision" page, section "Dtype policy": compute
+ *               dtype is the 16-bit type when any operand is 16-bit, else
+ *               fp32; output dtype is the promotion of every operand's dtype;
+ *               fp16 together with bf16 is rejected as a caller bug.
+ *   cast     -- matmul operands (x, W, down, up) are rounded from their
+ *               stored value to the compute dtype (exact when equal).  The
+ *               bias is not a matmul operand and keeps its stored value.
+ *   h        -- h = x_c . down_c^T summed in fp64, then rounded to the
+ *               compute (storage) dtype before the second dot, as the eager
+ *               two-Linear chain does (same page, "Measured accuracy").
+ *   lora     -- y = round_out( x_c.W_c^T + scale * h_r.up_c^T + b ), one
+ *               final rounding.
+ *   linear   -- Luminal FP16 page, "What Was Fixed": the projection
+ *               p = x.W^T (fp32 compute) is rounded to the output dtype,
+ *               then the bias is added and the sum rounded again; the bias is
+ *               never fused across the projection's rounding boundary.
+ *   rounding -- IEEE round-to-nearest, ties-to-even, directly from fp64 (never
+ *               via fp32), gradual underflow, overflow to +-inf at or beyond
+ *               max + half an ulp, NaN propagated.
+ *
+ * Sums run over k in increasing order.  Products of two fp16/bf16 values,
+ * and of two fp32 values, are exact in fp64.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F16 = 1, OR_BF16 = 2, OR_F32 = 3 };
+enum { OR_OK = 0, OR_MIXED_HALF = 1, OR_INVALID = 2 };
+
+/* ---- formats ------------------------------------------------------------ */
+
+/* p = significand bits (incl. the implicit one), emin = exponent of the
+ * smallest normal, emax = exponent of the largest finite value. */
+static int fmt(int dt, int* p, int* emin, int* emax) {
+    switch (dt) {
+    case OR_F16:  *p = 11; *emin = -14;  *emax = 15;  return 0;
+    case OR_BF16: *p = 8;  *emin = -126; *emax = 127; return 0;
+    case OR_F32:  *p = 24; *emin = -126; *emax = 127; return 0;
+    default: return -1;
+    }
+}
+
+/* Round v (binary64) to the nearest value of format dt, ties to even.
+ * Returned as the binary64 value of the result. */
+double oracle_round(double v, int dt) {
+    int p, emin, emax;
+    if (fmt(dt, &p, &emin, &emax)) return NAN;
+    if (isnan(v)) return v;
+    if (v == 0.0 || isinf(v)) return v;
+    double a = fabs(v);
+    /* largest finite value and the overflow threshold max + ulp(max)/2 */
+    double maxv = ldexp(2.0 - ldexp(1.0, 1 - p), emax);
+    if (a >= maxv + ldexp(1.0, emax - p)) return copysign(INFINITY, v);
+    int ex;
+    frexp(a, &ex);                  /* a = f * 2^ex, f in [0.5, 1) */
+    int e = ex - 1;                 /* floor(log2(a)) */
+    if (e < emin) e = emin;         /* subnormal range: fixed quantum */
+    double q = ldexp(1.0, e - p + 1);   /* spacing of the format around a */
+    double n = a / q;               /* exact: division by a power of two */
+    double fl = floor(n);
+    double d = n - fl;              /* exact fractional part */
+    if (d > 0.5 || (d == 0.5 && fmod(fl, 2.0) == 1.0)) fl += 1.0;
+    return copysign(fl * q, v);
+}
+
+/* Stored element -> exact binary64 value. */
+static double widen(const void* base, int dt, int64_t i) {
+    if (dt == OR_F32) return (double)((const float*)base)[i];
+    uint16_t b = ((const uint16_t*)base)[i];
+    if (dt == OR_BF16) {
+        uint32_t u = (uint32_t)b << 16;
+        float f;
+        memcpy(&f, &u, 4);
+        return (double)f;
+    }
+    /* fp16: 1 sign, 5 exponent, 10 fraction bits */
+    int s = b >> 15, e = (b >> 10) & 0x1f, m = b & 0x3ff;
+    double v;
+    if (e == 0) v = ldexp((double)m, -24);
+    else if (e == 31) v = m ? NAN : INFINITY;
+    else v = ldexp((double)(1024 + m), e - 25);
+    return s ? -v : v;
+}
+
+double oracle_widen(const void* base, int dt, int64_t i) { return widen(base, dt, i); }
+
+/* Store a value that is already representable in dt. */
+static void store(void* base, int dt, int64_t i, double v) {
+    if (dt == OR_F32) { ((float*)base)[i] = (float)v; return; }
+    uint16_t bits;
+    if (dt == OR_BF16) {
+        float f = (float)v;            /* exact: v is a bf16 value */
+        uint32_t u;
+        memcpy(&u, &f, 4);
+        bits = isnan(v) ? (uint16_t)0x7fc0 : (uint16_t)(u >> 16);
+    } else {
+        uint16_t s = signbit(v) ? 0x8000 : 0;
+        double a = fabs(v);
+        if (isnan(v)) bits = 0x7e00;
+        else if (isinf(v)) bits = s | 0x7c00;
+        else if (a == 0.0) bits = s;
+        else {
+            int ex;
+            frexp(a, &ex);
+            int e = ex - 1;
+            if (e < -14) bits = s | (uint16_t)ldexp(a, 24);           /* subnormal: a / 2^-24 */
+            else bits = s | (uint16_t)((e + 15) << 10) | (uint16_t)(ldexp(a, 10 - e) - 1024.0);
+        }
+    }
+    ((uint16_t*)base)[i] = bits;
+}
+
+void oracle_store(void* base, int dt, int64_t i, double v) { store(base, dt, i, v); }
+
+/* Array forms of the three element helpers above. */
+void oracle_round_n(const double* in, double* out, int64_t n, int dt) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_round(in[i], dt);
+}
+void oracle_widen_n(const void* base, int dt, double* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = widen(base, dt, i);
+}
+void oracle_store_n(void* base, int dt, const double* in, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) store(base, dt, i, in[i]);
+}
+
+/* ---- dtype policy ------------------------------------------------------- */
+
+int oracle_resolve(const int* dts, int n, int* compute, int* output) {
+    if (!dts || n <= 0) return OR_INVALID;
+    int h16 = 0, hbf = 0, h32 = 0;
+    for (int i = 0; i < n; ++i) {
+        if (dts[i] == OR_F16) h16 = 1;
+        else if (dts[i] == OR_BF16) hbf = 1;
+        else if (dts[i] == OR_F32) h32 = 1;
+        else return OR_INVALID;
+    }
+    if (h16 && hbf) return OR_MIXED_HALF;
+    int c = h16 ? OR_F16 : (hbf ? OR_BF16 : OR_F32);
+    if (compute) *compute = c;
+    if (output) *output = h32 ? OR_F32 : c;
+    return OR_OK;
+}
+
+/* ---- the forward ---------------------------------------------------------- */
+
+typedef struct {
+    /* problem */
+    const void *x, *w, *b, *down, *up;
+    int x_dt, w_dt, b_dt, down_dt, up_dt;
+    int64_t M, N, K, r;
+    double scale;
+    int lora;                    /* 1: LoRA bypass, 0: plain affine (two roundings) */
+    int c_dt, o_dt;
+    /* cast operands, binary64 */
+    const double *wc, *dc, *uc;  /* [N,K], [r,K], [N,r] */
+    /* rows to evaluate */
+    const int64_t* rows;
+    int64_t nrows;
+    /* outputs, [nrows][N] / [nrows][r]; any may be NULL */
+    void* y;
+    double* ref;
+    double* hr;
+    /* work split */
+    int64_t lo, hi;
+} job_t;
+
+static void* run_rows(void* arg) {
+    job_t* J = (job_t*)arg;
+    const int64_t N = J->N, K = J->K, r = J->r;
+    double* xc = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    double* h = (double*)malloc(sizeof(double) * (size_t)(r > 0 ? r : 1));
+    for (int64_t i = J->lo; i < J->hi; ++i) {
+        int64_t m = J->rows ? J->rows[i] : i;
+        for (int64_t k = 0; k < K; ++k) xc[k] = oracle_round(widen(J->x, J->x_dt, m * K + k), J->c_dt);
+        if (J->lora) {
+            for (int64_t j = 0; j < r; ++j) {
+                double s = 0.0;
+                for (int64_t k = 0; k < K; ++k) s += xc[k] * J->dc[j * K + k];
+                h[j] = oracle_round(s, J->c_dt);               /* h rounded before the second dot */
+                if (J->hr) J->hr[i * r + j] = h[j];
+            }
+        }
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            const double* wr = J->wc + n * K;
+            for (int64_t k = 0; k < K; ++k) acc += xc[k] * wr[k];
+            double bias = J->b ? widen(J->b, J->b_dt, n) : 0.0;
+            double v;
+            if (J->lora) {
+                double f = 0.0;
+                for (int64_t j = 0; j < r; ++j) f += h[j] * J->uc[n * r + j];
+                v = acc + J->scale * f + bias;
+            } else {
+                v = oracle_round(acc, J->o_dt) + bias;         /* projection rounded, then bias */
+            }
+            if (J->ref) J->ref[i * N + n] = v;
+            if (J->y) store(J->y, J->o_dt, i * N + n, oracle_round(v, J->o_dt));
+        }
+    }
+    free(xc);
+    free(h);
+    return NULL;
+}
+
+static double* cast_all(const void* src, int dt, int c_dt, int64_t n) {
+    double* d = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    for (int64_t i = 0; i < n; ++i) d[i] = oracle_round(widen(src, dt, i), c_dt);
+    return d;
+}
+
+/*
+ * Evaluate the forward for the given rows.
+ *   lora = 0: plain affine (down/up/r/scale ignored).
+ *   rows = NULL evaluates rows 0..nrows-1.
+ *   y (o_dt storage), ref (value before the final rounding), hr (h rounded,
+ *   LoRA only) are written as [nrows][N] / [nrows][r]; each may be NULL.
+ *   b may be NULL (no bias).  Returns OR_OK, OR_MIXED_HALF or OR_INVALID and
+ *   the resolved dtypes in *c_out / *o_out.
+ */
+int oracle_forward(int lora,
+                   const void* x, int x_dt, const void* w, int w_dt, const void* b, int b_dt,
+                   const void* down, int down_dt, const void* up, int up_dt, int64_t r, double scale,
+                   int64_t M, int64_t N, int64_t K, const int64_t* rows, int64_t nrows,
+                   void* y, double* ref, double* hr, int nthreads, int* c_out, int* o_out) {
+    int dts[5], n = 0;
+    dts[n++] = x_dt;
+    dts[n++] = w_dt;
+    if (b) dts[n++] = b_dt;
+    if (lora) { dts[n++] = down_dt; dts[n++] = up_dt; }
+    int c_dt, o_dt;
+    int st = oracle_resolve(dts, n, &c_dt, &o_dt);
+    if (st != OR_OK) return st;
+    if (c_out) *c_out = c_dt;
+    if (o_out) *o_out = o_dt;
+    if (M < 0 || N < 0 || K < 0 || r < 0 || nrows < 0) return OR_INVALID;
+    if (!lora) r = 0;
+    for (int64_t i = 0; rows && i < nrows; ++i)
+        if (rows[i] < 0 || rows[i] >= M) return OR_INVALID;
+    if (!rows && nrows > M) return OR_INVALID;
+
+    double* wc = cast_all(w, w_dt, c_dt, N * K);
+    double* dc = lora ? cast_all(down, down_dt, c_dt, r * K) : NULL;
+    double* uc = lora ? cast_all(up, up_dt, c_dt, N * r) : NULL;
+
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > nrows) nthreads = nrows > 0 ? (int)nrows : 1;
+    job_t* jobs = (job_t*)calloc((size_t)nthreads, sizeof(job_t));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    for (int t = 0; t < nthreads; ++t) {
+        job_t* J = &jobs[t];
+        J->x = x; J->w = w; J->b = b; J->down = down; J->up = up;
+        J->x_dt = x_dt; J->w_dt = w_dt; J->b_dt = b_dt; J->down_dt = down_dt; J->up_dt = up_dt;
+        J->M = M; J->N = N; J->K = K; J->r = r; J->scale = scale; J->lora = lora;
+        J->c_dt = c_dt; J->o_dt = o_dt;
+        J->wc = wc; J->dc = dc; J->uc = uc;
+        J->rows = rows; J->nrows = nrows;
+        J->y = y; J->ref = ref; J->hr = hr;
+        J->lo = nrows * t / nthreads;
+        J->hi = nrows * (t + 1) / nthreads;
+    }
+    int* started = (int*)calloc((size_t)nthreads, sizeof(int));
+    for (int t = 1; t < nthreads; ++t)
+        started[t] = pthread_create(&th[t], NULL, run_rows, &jobs[t]) == 0;
+    run_rows(&jobs[0]);
+    for (int t = 1; t < nthreads; ++t) {
+        if (started[t]) pthread_join(th[t], NULL);
+        else run_rows(&jobs[t]);      /* no thread: run the share here */
+    }
+    free(started);
+    free(jobs);
+    free(th);
+    free(wc);
+    free(dc);
+    free(uc);
+    return OR_OK;
+}

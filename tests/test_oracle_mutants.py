@@ -1,0 +1,50 @@
+"""The pins have teeth: each plausible mistake, planted in a copy of the
+oracle's C source on the CPU, makes at least one pin test fail.
+
+The planted copies live in a temporary directory; the oracle itself is never
+modified.  Each mutant is built with the same gcc flags and the pin suite is
+run against it in a subprocess (stopping at the first failure)."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+# (name, original text, replacement) -- each must match exactly once
+MUTANTS = [
+    ("h-not-rounded", "h[j] = oracle_round(s, J->c_dt);", "h[j] = s;"),
+    ("h-rounded-to-output-dtype", "h[j] = oracle_round(s, J->c_dt);", "h[j] = oracle_round(s, J->o_dt);"),
+    ("bias-fused-in-affine", "v = oracle_round(acc, J->o_dt) + bias;", "v = acc + bias;"),
+    ("ties-away-from-zero", "(d > 0.5 || (d == 0.5 && fmod(fl, 2.0) == 1.0))", "(d >= 0.5)"),
+    ("round-via-fp32", "    if (isnan(v)) return v;\n    if (v == 0.0", "    v = (double)(float)v;\n    if (isnan(v)) return v;\n    if (v == 0.0"),
+    ("flush-subnormals", "if (e < emin) e = emin;", "if (e < emin) return copysign(0.0, v);"),
+    ("operands-not-cast", "xc[k] = oracle_round(widen(J->x, J->x_dt, m * K + k), J->c_dt);", "xc[k] = widen(J->x, J->x_dt, m * K + k);"),
+    ("output-is-compute", "*output = h32 ? OR_F32 : c;", "*output = c;"),
+    ("mixed-half-accepted", "if (h16 && hbf) return OR_MIXED_HALF;", ""),
+    ("bypass-sign", "v = acc + J->scale * f + bias;", "v = acc - J->scale * f + bias;"),
+    ("up-transposed", "f += h[j] * J->uc[n * r + j];", "f += h[j] * J->uc[j * N + n];"),
+    ("lora-bias-dropped", "v = acc + J->scale * f + bias;", "v = acc + J->scale * f;"),
+    ("overflow-threshold", "if (a >= maxv + ldexp(1.0, emax - p))", "if (a > maxv + ldexp(1.0, emax - p))"),
+    ("scale-ignored", "v = acc + J->scale * f + bias;", "v = acc + f + bias;"),
+    ("down-index", "s += xc[k] * J->dc[j * K + k];", "s += xc[k] * J->dc[k];"),
+    ("fp16-exponent-bias", "else v = ldexp((double)(1024 + m), e - 25);", "else v = ldexp((double)(1024 + m), e - 24);"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(name, old, new, tmp_path):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutant {name}: pattern not unique in oracle.c"
+    mutant = tmp_path / "oracle_mutant.c"
+    mutant.write_text(src.replace(old, new))
+    lib = tmp_path / "liboracle_mutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-o", str(lib),
+                           str(mutant), "-lm", "-lpthread"])
+    env = dict(os.environ, ORACLE_LIB_OVERRIDE=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"

@@ -1,0 +1,353 @@
+"""Pins for the CPU oracle: checks against what the pages and mathematics fix,
+never against the oracle itself or the GPU path.
+
+Covers: rounding (exhaustive round trips, every midpoint, library conversions,
+overflow and subnormal edges, direct-from-fp64 rounding), the dtype-policy
+table, the hand-built boundary fixtures, exact-rational brute force on tiny
+shapes, closed forms and invariants.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import exact
+from tests.exact import BF16, F16, F32
+
+# ---- rounding ------------------------------------------------------------------
+
+
+def _all_finite(dt):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):
+        if dt == F16:
+            vals = bits.view(np.float16).astype(np.float64)
+        else:
+            vals = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    keep = np.isfinite(vals)
+    return bits[keep], vals[keep]
+
+
+@pytest.mark.parametrize("dt", [F16, BF16])
+def test_roundtrip_every_16bit_pattern(dt):
+    bits, vals = _all_finite(dt)
+    # widening agrees with the library decode of every pattern
+    np.testing.assert_array_equal(oracle.widen(bits, dt), vals)
+    # rounding a representable value is the identity, and storing it restores the pattern
+    np.testing.assert_array_equal(oracle.round_array(vals, dt), vals)
+    np.testing.assert_array_equal(oracle.encode(vals, dt), bits)
+
+
+@pytest.mark.parametrize("dt", [F16, BF16])
+def test_every_midpoint_ties_to_even(dt):
+    bits, vals = _all_finite(dt)
+    pos = np.unique(vals[vals >= 0])
+    lo, hi = pos[:-1], pos[1:]
+    mid = (lo + hi) / 2                      # exact in fp64
+    got = oracle.round_array(mid, dt)
+    even_lo = (oracle.encode(lo, dt) & 1) == 0
+    np.testing.assert_array_equal(got, np.where(even_lo, lo, hi))
+    np.testing.assert_array_equal(oracle.round_array(-mid, dt), -np.where(even_lo, lo, hi))
+    # one fp64 step either side of the midpoint goes to the nearer neighbour
+    np.testing.assert_array_equal(oracle.round_array(np.nextafter(mid, -np.inf), dt), lo)
+    np.testing.assert_array_equal(oracle.round_array(np.nextafter(mid, np.inf), dt), hi)
+
+
+def test_fp16_matches_numpy_direct_conversion():
+    # numpy converts binary64 -> binary16 directly with round-to-nearest-even
+    rng = np.random.default_rng(0)
+    v = np.concatenate([rng.standard_normal(200000) * 10.0 ** rng.uniform(-9, 5, 200000),
+                        np.array([65504.0, 65519.99, 65520.0, -65520.0, 2.0 ** -25, 2.0 ** -25 * 1.0000001,
+                                  3 * 2.0 ** -26, 2.0 ** -24, 6e-8, 0.0, -0.0])])
+    with np.errstate(over="ignore"):
+        lib = v.astype(np.float16).astype(np.float64)
+    np.testing.assert_array_equal(oracle.round_array(v, F16), lib)
+
+
+def test_fp32_matches_c_conversion():
+    rng = np.random.default_rng(1)
+    v = rng.standard_normal(200000) * 10.0 ** rng.uniform(-46, 39, 200000)
+    v = np.concatenate([v, [3.4028235677973366e38, 3.4028235677973362e38, 2.0 ** -149, 2.0 ** -150,
+                            2.0 ** -150 * 1.5, 1.401298464324817e-45]])
+    with np.errstate(over="ignore"):
+        lib = v.astype(np.float32).astype(np.float64)
+    np.testing.assert_array_equal(oracle.round_array(v, F32), lib)
+
+
+def test_bf16_matches_torch_on_fp32_inputs():
+    # torch rounds fp32 -> bf16 to nearest even; on fp32 inputs no double rounding is involved
+    rng = np.random.default_rng(2)
+    v32 = (rng.standard_normal(200000) * 10.0 ** rng.uniform(-40, 38, 200000)).astype(np.float32)
+    lib = torch.from_numpy(v32).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.round_array(v32.astype(np.float64), BF16), lib)
+
+
+def test_overflow_thresholds():
+    # overflow to inf at or beyond max + half an ulp (ties go to the even "next" value)
+    assert oracle.round_to(65504.0 + 16.0, F16) == np.inf
+    assert oracle.round_to(np.nextafter(65504.0 + 16.0, 0), F16) == 65504.0
+    bmax = float(torch.finfo(torch.bfloat16).max)
+    half_ulp = 2.0 ** (127 - 8)
+    assert oracle.round_to(bmax + half_ulp, BF16) == np.inf
+    assert oracle.round_to(np.nextafter(bmax + half_ulp, 0), BF16) == bmax
+    assert oracle.round_to(-(bmax + half_ulp), BF16) == -np.inf
+    assert np.isnan(oracle.round_to(np.nan, F16))
+
+
+def test_rounds_directly_from_fp64_not_via_fp32():
+    # 1 + 2^-8 + 2^-30: bf16 neighbours 1 and 1 + 2^-7, midpoint 1 + 2^-8; the value is just above it.
+    # Going through fp32 first loses the 2^-30 and lands on the midpoint, which ties down to 1.
+    v = 1 + 2.0 ** -8 + 2.0 ** -30
+    assert oracle.round_to(v, BF16) == 1 + 2.0 ** -7
+    assert float(torch.tensor(v, dtype=torch.float64).to(torch.float32).to(torch.bfloat16)) == 1.0
+
+
+def test_subnormals_kept():
+    assert oracle.round_to(2.0 ** -20, F16) == 2.0 ** -20           # fp16 subnormal
+    assert oracle.round_to(2.0 ** -25, F16) == 0.0                  # half of the smallest: ties to even (0)
+    assert oracle.round_to(3 * 2.0 ** -26, F16) == 2.0 ** -24
+    assert oracle.round_to(2.0 ** -133, BF16) == 2.0 ** -133        # smallest bf16 subnormal
+
+
+# ---- dtype policy -------------------------------------------------------------
+
+
+def test_policy_table_exact():
+    for x_dt, w_dt, c_dt, o_dt in exact.load_policy_table():
+        # the module weights W, b, down, up share w_dt
+        st, c, o = oracle.resolve([x_dt, w_dt, w_dt, w_dt, w_dt])
+        if c_dt is None:
+            assert st == oracle.MIXED_HALF
+        else:
+            assert (st, c, o) == (oracle.OK, c_dt, o_dt)
+
+
+_TORCH = {F16: torch.float16, BF16: torch.bfloat16, F32: torch.float32}
+_BACK = {v: k for k, v in _TORCH.items()}
+
+
+def test_policy_every_operand_tuple():
+    """All 3^5 operand tuples: output is torch's type promotion over the
+    operands; rejection exactly when both 16-bit types are present; compute is
+    the 16-bit type present, else fp32."""
+    import itertools
+    for tup in itertools.product([F16, BF16, F32], repeat=5):
+        st, c, o = oracle.resolve(list(tup))
+        if F16 in tup and BF16 in tup:
+            assert st == oracle.MIXED_HALF, tup
+            continue
+        prom = _TORCH[tup[0]]
+        for t in tup[1:]:
+            prom = torch.promote_types(prom, _TORCH[t])
+        assert st == oracle.OK and o == _BACK[prom], tup
+        sixteen = [t for t in tup if t != F32]
+        assert c == (sixteen[0] if sixteen else F32), tup
+
+
+def test_policy_invalid():
+    assert oracle.resolve([])[0] == oracle.INVALID
+    assert oracle.resolve([1, 7])[0] == oracle.INVALID
+
+
+# ---- fixtures -----------------------------------------------------------------
+
+FIXTURES = exact.load_fixtures()
+
+
+def _run_fixture(fx):
+    a = exact.fixture_arrays(fx)
+    dt = a["dt"]
+    lora = fx["kind"] == "lora"
+    res = oracle.forward(a["x"], dt, a["w"], dt, a["b"], dt if a["b"] is not None else None,
+                         a.get("down"), dt if lora else None, a.get("up"), dt if lora else None,
+                         scale=a.get("scale", 1.0), lora=lora, nthreads=1)
+    return a, res
+
+
+@pytest.mark.parametrize("fx", FIXTURES, ids=[f["name"] for f in FIXTURES])
+def test_fixture_oracle_value(fx):
+    a, res = _run_fixture(fx)
+    y = oracle.as_float64(res["y"], res["output"])[0, 0]
+    assert Fraction(float(y)) == fx["expect"], (fx["name"], y, float(fx["expect"]))
+
+
+@pytest.mark.parametrize("fx", FIXTURES, ids=[f["name"] for f in FIXTURES])
+def test_fixture_has_teeth(fx):
+    """Every named wrong implementation falls outside the tolerance."""
+    dt = {"f16": F16, "bf16": BF16}[fx["dtype"]]
+    ref = np.array([float(fx["expect"])])
+    tol = oracle.tolerance(ref, dt, 8, 1)[0]
+    for wrong, what in fx["wrong"]:
+        assert abs(float(wrong) - float(fx["expect"])) > tol, (fx["name"], what)
+
+
+@pytest.mark.parametrize("fx", FIXTURES, ids=[f["name"] for f in FIXTURES])
+def test_fixture_exact_rational(fx):
+    """The hand-derived expectation is what exact rational evaluation gives."""
+    a = exact.fixture_arrays(fx)
+    dt = a["dt"]
+    lora = fx["kind"] == "lora"
+    y, _ = exact.exact_forward(a["x"], dt, a["w"], dt, dt, dt, b=a["b"], b_dt=dt, down=a.get("down"), d_dt=dt,
+                               up=a.get("up"), u_dt=dt, scale=Fraction(a.get("scale", 1.0)), lora=lora)
+    assert y[0][0] == fx["expect"]
+
+
+# ---- exact-rational brute force -------------------------------------------------
+
+def _draw(rng, shape, dt, std=1.0):
+    v = (rng.standard_normal(shape) * std).astype(np.float32)
+    return {F16: lambda: v.astype(np.float16).view(np.uint16),
+            BF16: lambda: torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16),
+            F32: lambda: v}[dt]()
+
+
+CASES = [  # (x_dt, w_dt, M, N, K, r)
+    (F16, F16, 4, 4, 8, 1), (F16, F16, 4, 4, 8, 2), (F16, F16, 4, 4, 8, 4),
+    (BF16, BF16, 4, 4, 8, 2), (BF16, BF16, 3, 5, 7, 3),
+    (F16, F32, 3, 5, 7, 1), (F32, BF16, 3, 5, 7, 2), (BF16, F32, 4, 4, 8, 4), (F32, F32, 3, 4, 8, 2),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_bruteforce_lora_exact(case, seed):
+    x_dt, w_dt, M, N, K, r = case
+    rng = np.random.default_rng(100 + seed)
+    x = _draw(rng, (M, K), x_dt)
+    w = _draw(rng, (N, K), w_dt, 0.5)
+    b = _draw(rng, (N,), w_dt, 0.3)
+    down = _draw(rng, (r, K), w_dt, 0.5)
+    up = _draw(rng, (N, r), w_dt, 0.5)
+    scale = [1.0, 0.5, 3.0][seed]
+    res = oracle.forward(x, x_dt, w, w_dt, b, w_dt, down, w_dt, up, w_dt, scale=scale, nthreads=2)
+    y, hr = exact.exact_forward(x, x_dt, w, w_dt, res["compute"], res["output"], b=b, b_dt=w_dt, down=down,
+                                d_dt=w_dt, up=up, u_dt=w_dt, scale=Fraction(scale))
+    got = oracle.as_float64(res["y"], res["output"])
+    for m in range(M):
+        for j in range(r):
+            assert Fraction(float(res["h"][m, j])) == hr[m][j]
+        for n in range(N):
+            assert Fraction(float(got[m, n])) == y[m][n], (m, n)
+
+
+@pytest.mark.parametrize("dt", [F16, BF16, F32])
+def test_bruteforce_linear_exact(dt):
+    rng = np.random.default_rng(7)
+    M, N, K = 4, 4, 8
+    x, w, b = _draw(rng, (M, K), dt), _draw(rng, (N, K), dt, 0.4), _draw(rng, (N,), dt, 0.2)
+    res = oracle.forward(x, dt, w, dt, b, dt, lora=False, nthreads=1)
+    y, _ = exact.exact_forward(x, dt, w, dt, dt, dt, b=b, b_dt=dt, lora=False)
+    got = oracle.as_float64(res["y"], res["output"])
+    for m in range(M):
+        for n in range(N):
+            assert Fraction(float(got[m, n])) == y[m][n]
+
+
+# ---- closed forms and invariants -------------------------------------------------
+
+def _medium(seed, dt=F16, M=24, N=40, K=96, r=8):
+    rng = np.random.default_rng(seed)
+    return (_draw(rng, (M, K), dt), _draw(rng, (N, K), dt, K ** -0.5), _draw(rng, (N,), dt, 0.3),
+            _draw(rng, (r, K), dt, K ** -0.5), _draw(rng, (N, r), dt, r ** -0.5))
+
+
+def _np_vals(a, dt):
+    return oracle.as_float64(a, dt)
+
+
+@pytest.mark.parametrize("dt", [F16, BF16])
+def test_closed_form_zero_bypass(dt):
+    """down = 0, up = 0 or scale = 0: y = round(x.W^T + b), a single rounding,
+    computed here with numpy's fp64 matmul and numpy/torch rounding."""
+    x, w, b, down, up = _medium(11, dt)
+    X, Wv, Bv = _np_vals(x, dt), _np_vals(w, dt), _np_vals(b, dt)
+    expect = X @ Wv.T + Bv
+    if dt == F16:
+        expect_r = expect.astype(np.float16).astype(np.float64)
+    else:
+        expect_r = oracle.round_array(expect, BF16)  # checked against torch below
+        np.testing.assert_array_equal(expect_r[np.abs(expect_r) > 0],
+                                      torch.from_numpy(expect).to(torch.float32).to(torch.bfloat16)
+                                      .to(torch.float64).numpy()[np.abs(expect_r) > 0])
+    zeros_d = np.zeros_like(down)
+    zeros_u = np.zeros_like(up)
+    for d_, u_, s_ in ((zeros_d, up, 1.0), (down, zeros_u, 1.0), (down, up, 0.0)):
+        res = oracle.forward(x, dt, w, dt, b, dt, d_, dt, u_, dt, scale=s_)
+        np.testing.assert_array_equal(oracle.as_float64(res["y"], dt), expect_r)
+
+
+def test_closed_form_zero_weight_f16():
+    """W = 0: y = round(scale * h_r.up^T + b) with h_r = round(x.down^T)."""
+    x, w, b, down, up = _medium(12, F16)
+    X, D, U, Bv = (_np_vals(a, F16) for a in (x, down, up, b))
+    h_r = (X @ D.T).astype(np.float16).astype(np.float64)
+    expect = (2.0 * (h_r @ U.T) + Bv).astype(np.float16).astype(np.float64)
+    res = oracle.forward(x, F16, np.zeros_like(w), F16, b, F16, down, F16, up, F16, scale=2.0)
+    np.testing.assert_array_equal(res["h"], h_r)
+    np.testing.assert_array_equal(oracle.as_float64(res["y"], F16), expect)
+
+
+def test_closed_form_unit_rows():
+    """x = e_k: h = down[:, k] exactly, so h_r = down[:, k]."""
+    K, r = 16, 4
+    x = np.zeros((K, K), dtype=np.float16)
+    np.fill_diagonal(x, 1.0)
+    x = x.view(np.uint16)
+    _, w, b, down, up = _medium(13, F16, M=K, N=8, K=K, r=r)
+    res = oracle.forward(x, F16, w, F16, b, F16, down, F16, up, F16, scale=1.0)
+    np.testing.assert_array_equal(res["h"], _np_vals(down, F16).T)
+
+
+@pytest.mark.parametrize("k", [-3, 2])
+def test_invariant_power_of_two_scaling(k):
+    """With b = 0, scaling x by 2^k scales y (and h) by 2^k exactly in the normal range."""
+    x, w, b, down, up = _medium(14, F16)
+    x2 = (_np_vals(x, F16) * 2.0 ** k).astype(np.float16).view(np.uint16)
+    r1 = oracle.forward(x, F16, w, F16, None, None, down, F16, up, F16, scale=1.0)
+    r2 = oracle.forward(x2, F16, w, F16, None, None, down, F16, up, F16, scale=1.0)
+    y1, y2 = oracle.as_float64(r1["y"], F16), oracle.as_float64(r2["y"], F16)
+    normal = (np.abs(y1) >= 2.0 ** -14 * 2 ** max(0, -k)) & (np.abs(y1) * 2.0 ** k < 32768)
+    assert normal.mean() > 0.9
+    np.testing.assert_array_equal(y2[normal], y1[normal] * 2.0 ** k)
+
+
+def test_invariant_consistent_k_permutation():
+    x, w, b, down, up = _medium(15, F16)
+    perm = np.random.default_rng(3).permutation(x.shape[1])
+    r1 = oracle.forward(x, F16, w, F16, b, F16, down, F16, up, F16, scale=1.0)
+    r2 = oracle.forward(x[:, perm], F16, w[:, perm], F16, b, F16, down[:, perm], F16, up, F16, scale=1.0)
+    np.testing.assert_array_equal(r1["y"], r2["y"])
+    np.testing.assert_array_equal(r1["h"], r2["h"])
+
+
+def test_rows_subset_matches_full():
+    x, w, b, down, up = _medium(16, BF16)
+    full = oracle.forward(x, BF16, w, BF16, b, BF16, down, BF16, up, BF16, scale=0.5)
+    rows = np.array([3, 0, 23, 11])
+    part = oracle.forward(x, BF16, w, BF16, b, BF16, down, BF16, up, BF16, scale=0.5, rows=rows)
+    np.testing.assert_array_equal(part["y"], full["y"][rows])
+    np.testing.assert_array_equal(part["ref"], full["ref"][rows])
+
+
+def test_mixed_half_rejected_by_forward():
+    x, w, b, down, up = _medium(17, F16)
+    with pytest.raises(oracle.OracleError):
+        oracle.forward(x, F16, w, BF16, None, None, down, BF16, up, BF16)
+
+
+# ---- scoring --------------------------------------------------------------------
+
+def test_tolerance_constants_from_pages():
+    # abs(actual-reference) <= 2e-4 + 2e-3*abs(reference) (Luminal FP16 page)
+    assert oracle.tolerance(np.array([0.0, 1.0, -10.0]), F16, 64, 0).tolist() == [2e-4, 2e-4 + 2e-3, 2e-4 + 2e-2]
+
+
+def test_ulp_report():
+    ref = np.array([1.0, -1.0, 1.0, -1.0])
+    act = ref + np.array([2.0 ** -10, 0, 0, 2.0 ** -11])     # fp16 ulp at RMS 1 is 2^-10
+    mx, rms = oracle.ulp_report(act, ref, F16)
+    assert mx == 1.0 and rms == pytest.approx(np.sqrt((1 + 0.25) / 4))
+    assert oracle.ulp_of(1.0, BF16) == 2.0 ** -7
+    assert oracle.ulp_of(1.0, F32) == 2.0 ** -23
