@@ -1,0 +1,197 @@
+"""Benchmark of the fused LoRA-bypass linear on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one full forward -- operand preparation, the h contraction with its
+rounding guard, and the fused main contraction with the bypass fold and the
+bias/cast epilogue -- over inputs already resident in HBM.  W untimed steps,
+then K timed steps bracketed by device synchronisation.  One JSON line is
+printed with throughput (algorithmic TFLOP/s), the fraction of the MFMA
+fp16/bf16 dense peak, max/RMS ULP against the fp64 oracle on sampled rows,
+the roofline of the dominant kernel (its device time measured with HIP events
+around each launch of the timed region), the oracle's own throughput on host
+cores, and the eager two-GEMM torch chain as a comparator.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused LoRA-linear TFLOP/s & % MFMA peak (fp16/bf16); max ULP vs fp64 oracle"
+PEAK_TFLOPS = {1: 2500.0, 2: 2500.0, 3: 157.3}   # MI355X dense MFMA: fp16/bf16, fp32
+HBM_GBS = 8000.0
+DEFAULT = "lora_f16_4096x3072x3072_r16"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-eager", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import lora_bypass_linear_amd as L
+    import workloads as WL
+
+    wl = WL.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    inputs = WL.generate(wl)
+    d = {k: v.to(dev) for k, v in inputs.items()}
+    lora = wl.kind == "lora"
+    dts = [L.dtype_code(d["x"]), L.dtype_code(d["w"])] + ([L.dtype_code(d["b"])] if "b" in d else []) + \
+          ([L.dtype_code(d["down"]), L.dtype_code(d["up"])] if lora else [])
+    c_dt, o_dt = L.resolve_dtypes(dts)
+    y = torch.empty((wl.M, wl.N), dtype=L.torch_dtype(o_dt), device=dev)
+    if lora:
+        nws = L.lora_workspace_size(wl.M, wl.N, wl.K, wl.r, dts[0], dts[1], L.dtype_code(d["b"]) if "b" in d else 0,
+                                    L.dtype_code(d["down"]), L.dtype_code(d["up"]))
+    else:
+        nws = L.linear_workspace_size(wl.M, wl.N, wl.K, dts[0], dts[1], L.dtype_code(d["b"]) if "b" in d else 0)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        if lora:
+            L.lora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, d.get("b"), out=y, workspace=ws)
+        else:
+            L.linear(d["x"], d["w"], d.get("b"), out=y, workspace=ws)
+
+    print(f"[bench] {wl.name}: warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    L.profile_begin(8 * args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prof = L.profile_end()
+    ms_per_step = wall * 1e3 / args.steps
+    tflops = wl.flops / (ms_per_step * 1e-3) / 1e12
+
+    # dominant kernel: the fused main contraction (fold + K loop + epilogue)
+    n_g, t_g = prof["gemm"]
+    gemm_ms = t_g / max(n_g, 1)
+    gemm_flops = 2.0 * wl.M * wl.N * wl.K + 2.0 * wl.M * wl.r * wl.N
+    achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[c_dt]
+    roofline = {"bound": "mfma", "kernel": "gemm_kernel", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "flops_per_launch": gemm_flops, "avg_us": round(gemm_ms * 1e3, 3)}
+    kernels = {k: {"launches": n, "avg_us": round(t * 1e3 / n, 3)} for k, (n, t) in prof.items() if n}
+
+    out = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": {1: "f16", 2: "bf16", 3: "f32"}[c_dt],
+           "data": "synthetic (seeded Philox draws, shapes and distributions of the workload)",
+           "config": {"workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K, "rank": wl.r, "scale": wl.scale,
+                      "x_dtype": WL.NAME[wl.x_dt], "w_dtype": WL.NAME[wl.w_dt],
+                      "bias": WL.NAME[wl.b_dt] if wl.b_dt else None, "accumulate": "f32",
+                      "parallelism": "single GPU"},
+           "frac_of_peak": round(tflops / peak, 4), "hbm_gbs": round(wl.bytes / (ms_per_step * 1e-3) / 1e9, 1),
+           "input_digest": WL.digest(inputs), "kernels": kernels, "roofline": roofline}
+
+    # accuracy on sampled rows against the fp64 oracle (this is also the CPU-baseline leg)
+    if not args.no_cpu_baseline:
+        import oracle
+        from tests.gpu_cases import oracle_forward, score
+
+        y_cpu = y.cpu()
+        try:
+            cores = min(16, len(os.sched_getaffinity(0)))
+        except AttributeError:
+            cores = min(16, os.cpu_count() or 1)
+        row_flops = wl.flops / wl.M
+        rng = np.random.default_rng(wl.seed)
+        t1 = time.perf_counter()
+        probe_rows = np.sort(rng.choice(wl.M, size=min(wl.M, 2 * cores), replace=False))
+        oracle.forward(*_oracle_args(inputs, wl), rows=probe_rows, nthreads=cores, lora=lora)
+        t_probe = time.perf_counter() - t1
+        n_rows = int(min(wl.M, max(cores, probe_rows.size * args.cpu_seconds / max(t_probe, 1e-3))))
+        rows = np.sort(rng.choice(wl.M, size=n_rows, replace=False))
+        print(f"[bench] oracle on {n_rows} rows, {cores} threads", file=sys.stderr, flush=True)
+        t1 = time.perf_counter()
+        res = oracle_forward(inputs, wl, rows=rows)
+        t_cpu = time.perf_counter() - t1
+        s = score(y_cpu, res, rows, wl.K, wl.r)
+        out["max_ulp"] = round(s["ulp_max"], 4)
+        out["rms_ulp"] = round(s["ulp_rms"], 4)
+        out["tol_fail"] = s["fail"]
+        out["tol_checked"] = s["n"]
+        out["worst_err_over_tol"] = round(s["worst"], 4)
+        out["cpu_baseline"] = {"value": round(row_flops * n_rows / t_cpu / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": cores, "kind": "oracle",
+                               "sample": f"{n_rows} of {wl.M} output rows (all {wl.N} columns), {t_cpu:.1f} s"}
+        if not args.no_eager:
+            out["eager_baseline"] = _eager(d, wl, c_dt, o_dt, rows, res, args.steps, score)
+    print(json.dumps(out))
+
+
+def _oracle_args(inputs, wl):
+    import workloads as WL
+    bits = {k: WL.raw_bits(v) for k, v in inputs.items()}
+    dt = {k: WL.dtype_code(v) for k, v in inputs.items()}
+    return (bits["x"], dt["x"], bits["w"], dt["w"], bits.get("b"), dt.get("b"), bits.get("down"), dt.get("down"),
+            bits.get("up"), dt.get("up"), wl.scale)
+
+
+def _eager(d, wl, c_dt, o_dt, rows, res, steps, score):
+    """The unfused torch chain, each op rounding to the compute dtype (comparator only)."""
+    import torch
+    import torch.nn.functional as F
+
+    import lora_bypass_linear_amd as L
+
+    ct = L.torch_dtype(c_dt)
+    ot = L.torch_dtype(o_dt)
+
+    def run():
+        x = d["x"].to(ct)
+        w = d["w"].to(ct)
+        if wl.kind == "lora":
+            h = F.linear(x, d["down"].to(ct))
+            yv = F.linear(x, w) + wl.scale * F.linear(h, d["up"].to(ct))
+            if "b" in d:
+                yv = yv + d["b"].to(ct)
+        else:
+            yv = F.linear(x, w)
+            if "b" in d:
+                yv = yv + d["b"].to(ct)
+        return yv.to(ot)
+
+    yv = run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = max(5, steps // 2)
+    for _ in range(n):
+        yv = run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / n
+    s = score(yv.cpu(), res, rows, wl.K, wl.r)
+    return {"ms_per_step": round(ms, 5), "tflops": round(wl.flops / (ms * 1e-3) / 1e12, 2),
+            "max_ulp": round(s["ulp_max"], 4), "rms_ulp": round(s["ulp_rms"], 4), "tol_fail": s["fail"]}
+
+
+if __name__ == "__main__":
+    main()

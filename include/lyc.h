@@ -1,0 +1,173 @@
+/*
+ * lyc.h -- C ABI of the MI355X (gfx950) fused LoRA-bypass linear.
+ *
+ * The library computes, on one GPU,
+ *
+ *   lyc_lora_linear_fwd:  y = round_out( x.W^T + scale * round_c(x.down^T) . up^T + b )
+ *   lyc_linear_fwd:       y = round_out( round_out(x.W^T) + b )
+ *
+ * with the dtype policy of the LyCORIS "Precision" page (section "Dtype
+ * policy"): the compute dtype c is the 16-bit type when any operand is
+ * 16-bit, else fp32; the output dtype is the promotion of every operand's
+ * dtype; fp16 together with bf16 is refused.  Accumulation is fp32 under
+ * every policy.  h = x.down^T is rounded to the compute (storage) dtype
+ * before the second dot, as the eager two-Linear chain does (same page,
+ * "Measured accuracy"); the bypass is folded into the same fp32
+ * accumulators as x.W^T, so the product up.down (Delta W) never exists
+ * ("VRAM" section of the same page).  The plain affine form rounds the
+ * projection before adding the bias and never fuses the bias across that
+ * rounding (Luminal FP16 page, "What Was Fixed").  Rounding is IEEE
+ * round-to-nearest-even; subnormals are kept.
+ *
+ * Conventions shared by every call:
+ *  - dtype codes: LYC_F16, LYC_BF16, LYC_F32.  A bias dtype of 0 means "no
+ *    bias" and requires bias == NULL.
+ *  - Layouts are row-major and contiguous: x [M,K], W [N,K] (the nn.Linear
+ *    layout), down [rank,K], up [N,rank], b [N], y [M,N].
+ *  - Pointers x, w, down, up, b, y and workspace are DEVICE pointers on the
+ *    device that owns `stream`.  The caller owns every buffer; the library
+ *    allocates, frees and synchronises nothing.  Inputs are only read.  y and
+ *    the workspace must not overlap any input or each other.
+ *  - x and W must be 16-byte aligned and K a multiple of 8 (16-byte rows);
+ *    down, up, b and y need only element alignment.  The workspace must be
+ *    256-byte aligned and at least the size the matching *_workspace_size
+ *    call reports.  Its contents on entry do not matter.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *    asynchronous on that stream and deterministic (fixed reduction order, no
+ *    atomics in any result path).
+ *  - Every argument is checked before any GPU work is queued: a call that
+ *    returns an error has launched nothing and written nothing.  M == 0 or
+ *    N == 0 is a valid empty call (nothing launched).  K == 0 gives the
+ *    empty-sum result (y = round(b)).
+ *  - No call throws, aborts or prints.
+ */
+#ifndef LYC_H
+#define LYC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { LYC_F16 = 1, LYC_BF16 = 2, LYC_F32 = 3 };
+
+enum {
+    LYC_OK = 0,
+    LYC_ERR_MIXED_HALF = 1,     /* fp16 and bf16 operands in one call (a caller bug) */
+    LYC_ERR_INVALID_ARG = 2,    /* null pointer, negative size, unknown dtype code, ... */
+    LYC_ERR_DTYPE_MISMATCH = 3, /* y_dt is not the resolved output dtype */
+    LYC_ERR_UNSUPPORTED = 4,    /* K not a multiple of 8, misaligned x/W, rank > 256, sizes too large */
+    LYC_ERR_HIP = 5,            /* the HIP runtime refused a launch */
+    LYC_ERR_WORKSPACE = 6       /* workspace missing, too small or not 256-byte aligned */
+};
+
+/*
+ * Resolve the dtype policy over the dtypes of the operands present in a call
+ * (x, W, b if any, down and up for the LoRA form) -- LyCORIS "Precision"
+ * page, "Dtype policy".
+ *   operand_dtypes: host array of n dtype codes (n >= 1).
+ *   compute, output: host out-parameters (may be NULL), written on success.
+ * Returns LYC_OK, LYC_ERR_MIXED_HALF (fp16 with bf16; nothing written) or
+ * LYC_ERR_INVALID_ARG (n < 1, NULL array, unknown code).  Host only.
+ */
+int lyc_resolve_dtypes(const int* operand_dtypes, int n, int* compute, int* output);
+
+/*
+ * Workspace bytes lyc_linear_fwd needs for this problem (0 when no operand
+ * has to be cast: the compute dtype equals both storage dtypes).  The
+ * workspace holds compute-dtype copies of fp32 operands that feed a 16-bit
+ * contraction.  Returns the same argument errors as lyc_linear_fwd.
+ */
+int lyc_linear_workspace_size(int64_t M, int64_t N, int64_t K, int x_dt, int w_dt, int bias_dt,
+                              size_t* bytes);
+
+/*
+ * Plain affine forward with a declared rounding boundary (Luminal FP16
+ * page, "What Was Fixed"): p = x.W^T with fp32 accumulation of the
+ * compute-dtype operands, p rounded to the output dtype, then
+ * y = round_out(p + b).  bias may be NULL (bias_dt 0): y = round_out(p).
+ */
+int lyc_linear_fwd(const void* x, int x_dt, const void* w, int w_dt, const void* bias, int bias_dt,
+                   void* y, int y_dt, int64_t M, int64_t N, int64_t K,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes lyc_lora_linear_fwd needs.  It holds the rounded h
+ * [M, rank padded to 32] in the compute dtype, compute-dtype copies of down
+ * and up (rank padded), the row norms of down used by the h guard, a
+ * counter, and compute-dtype copies of fp32 x/W when they feed a 16-bit
+ * contraction.  Returns the same argument errors as lyc_lora_linear_fwd.
+ */
+int lyc_lora_linear_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt,
+                                   int bias_dt, int down_dt, int up_dt, size_t* bytes);
+
+/*
+ * LoRA-bypass forward (LyCORIS "Precision" page, "Dtype policy", "Measured
+ * accuracy" and "VRAM"):
+ *   h   = x_c . down_c^T           exact to within the rounding decision:
+ *                                  h is rounded once, to nearest even, from
+ *                                  its exact value (a guard re-evaluates in
+ *                                  fp64 every element whose fp32-partial sum
+ *                                  lies near a rounding midpoint)
+ *   h_r = round_c(h)
+ *   y   = round_out( x_c.W_c^T + scale * h_r.up_c^T + b )   fp32 accumulation,
+ *                                                           one final rounding
+ * where _c denotes an operand rounded (to nearest even) to the compute dtype.
+ * scale is a host value applied as an fp32 multiply of the bypass sum.
+ * rank == 0 is allowed (no bypass; down/up may be NULL).
+ */
+int lyc_lora_linear_fwd(const void* x, int x_dt, const void* w, int w_dt, const void* bias, int bias_dt,
+                        const void* down, int down_dt, const void* up, int up_dt, int64_t rank, double scale,
+                        void* y, int y_dt, int64_t M, int64_t N, int64_t K,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Where lyc_lora_linear_fwd leaves its intermediate results inside the
+ * workspace, for inspection after the call has completed on its stream:
+ *   h_offset:  byte offset of h_r, [M][h_ld] in the compute dtype (columns
+ *              >= rank are zero);
+ *   h_ld:      leading dimension of h_r in elements (rank rounded up to 32);
+ *   flagged_offset: byte offset of a uint32 count of h elements that the
+ *              guard re-evaluated in fp64 during the last call.
+ * Any out-pointer may be NULL.  Same argument errors as the size query.
+ */
+int lyc_lora_workspace_layout(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt, int bias_dt,
+                              int down_dt, int up_dt, size_t* h_offset, int64_t* h_ld, size_t* flagged_offset);
+
+/*
+ * Output tile (rows of W x rows of x) that the forward calls use for an
+ * M x N problem in compute dtype compute_dt; one workgroup computes one tile.
+ * Host only.  Returns LYC_ERR_INVALID_ARG for negative sizes or an unknown
+ * dtype code.
+ */
+int lyc_gemm_tile(int64_t M, int64_t N, int compute_dt, int* tile_n, int* tile_m);
+
+/*
+ * Per-kernel device time, recorded with HIP events around each kernel the
+ * forward calls launch (the measurement discipline of the Luminal FP16 page,
+ * "One Identical Implementation Through Timing and Profiling": per-kernel
+ * durations of the very launches being timed).  Off unless started.
+ *   lyc_profile_begin(capacity): create `capacity` event pairs (host call;
+ *     no device memory) and record every following launch, up to capacity.
+ *     Returns LYC_ERR_INVALID_ARG for capacity < 1, LYC_ERR_HIP if the events
+ *     cannot be created.
+ *   lyc_profile_end(total_ms, launches): wait for the recorded events, write
+ *     per kernel kind k (LYC_KERNEL_CAST .. LYC_KERNEL_GEMM) the summed
+ *     duration in ms and the launch count into the host arrays total_ms[4],
+ *     launches[4] (either may be NULL), free the events, stop recording.
+ * Process-wide state: begin/end must not race with each other.
+ */
+enum { LYC_KERNEL_CAST = 0, LYC_KERNEL_PREP = 1, LYC_KERNEL_HPASS = 2, LYC_KERNEL_GEMM = 3 };
+int lyc_profile_begin(int capacity);
+int lyc_profile_end(double* total_ms, int* launches);
+
+/* Static, NUL-terminated description of a status code. */
+const char* lyc_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LYC_H */

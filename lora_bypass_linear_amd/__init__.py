@@ -1,0 +1,212 @@
+"""Python binding of liblyc.so, the gfx950 fused LoRA-bypass linear.
+
+Argument marshalling only: every step of the forward runs in the library's
+HIP kernels.  PyTorch provides device memory and the current stream.  The
+library must have been built (``python -m lora_bypass_linear_amd.build``);
+nothing here falls back to another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+__all__ = ["F16", "BF16", "F32", "LycError", "MixedHalfError", "lib", "resolve_dtypes", "linear", "lora_linear",
+           "linear_workspace_size", "lora_workspace_size", "lora_workspace_layout", "gemm_tile", "profile_begin", "profile_end", "dtype_code",
+           "torch_dtype"]
+
+F16, BF16, F32 = 1, 2, 3
+OK, ERR_MIXED_HALF, ERR_INVALID_ARG, ERR_DTYPE_MISMATCH, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = range(7)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblyc.so")
+_lib = None
+
+_CODE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+_TORCH = {v: k for k, v in _CODE.items()}
+
+
+class LycError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"lyc status {status}: {message}")
+        self.status = status
+
+
+class MixedHalfError(LycError, ValueError):
+    pass
+
+
+def lib():
+    """Load liblyc.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m lora_bypass_linear_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        c_i64, c_int, c_vp, c_sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+        L.lyc_resolve_dtypes.argtypes = [ctypes.POINTER(c_int), c_int, ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
+        L.lyc_linear_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_int, c_int, c_int, ctypes.POINTER(c_sz)]
+        L.lyc_linear_fwd.argtypes = [c_vp, c_int, c_vp, c_int, c_vp, c_int, c_vp, c_int, c_i64, c_i64, c_i64,
+                                     c_vp, c_sz, c_vp]
+        L.lyc_lora_linear_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_i64, c_int, c_int, c_int, c_int, c_int,
+                                                     ctypes.POINTER(c_sz)]
+        L.lyc_lora_linear_fwd.argtypes = [c_vp, c_int, c_vp, c_int, c_vp, c_int, c_vp, c_int, c_vp, c_int, c_i64,
+                                          ctypes.c_double, c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_sz, c_vp]
+        L.lyc_lora_workspace_layout.argtypes = [c_i64, c_i64, c_i64, c_i64, c_int, c_int, c_int, c_int, c_int,
+                                                ctypes.POINTER(c_sz), ctypes.POINTER(c_i64), ctypes.POINTER(c_sz)]
+        L.lyc_gemm_tile.argtypes = [c_i64, c_i64, c_int, ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
+        L.lyc_profile_begin.argtypes = [c_int]
+        L.lyc_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_int)]
+        L.lyc_status_str.argtypes = [c_int]
+        L.lyc_status_str.restype = ctypes.c_char_p
+        for fn in (L.lyc_resolve_dtypes, L.lyc_linear_workspace_size, L.lyc_linear_fwd,
+                   L.lyc_lora_linear_workspace_size, L.lyc_lora_linear_fwd, L.lyc_lora_workspace_layout,
+                   L.lyc_gemm_tile, L.lyc_profile_begin, L.lyc_profile_end):
+            fn.restype = c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        msg = lib().lyc_status_str(status).decode()
+        raise (MixedHalfError if status == ERR_MIXED_HALF else LycError)(status, msg)
+
+
+def dtype_code(t) -> int:
+    dt = t.dtype if isinstance(t, torch.Tensor) else t
+    if dt not in _CODE:
+        raise TypeError(f"unsupported dtype {dt}")
+    return _CODE[dt]
+
+
+def torch_dtype(code: int):
+    return _TORCH[code]
+
+
+def resolve_dtypes(dtypes: Sequence[int]) -> Tuple[int, int]:
+    """Dtype policy over the operands' dtype codes -> (compute, output)."""
+    arr = (ctypes.c_int * max(1, len(dtypes)))(*dtypes)
+    c, o = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().lyc_resolve_dtypes(arr, len(dtypes), ctypes.byref(c), ctypes.byref(o)))
+    return c.value, o.value
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need_device(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("lyc operands must be GPU tensors")
+        if not t.is_contiguous():
+            raise ValueError("lyc operands must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("lyc operands must be on one device")
+    return dev
+
+
+def linear_workspace_size(M, N, K, x_dt, w_dt, b_dt=0) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().lyc_linear_workspace_size(M, N, K, x_dt, w_dt, b_dt, ctypes.byref(n)))
+    return n.value
+
+
+def lora_workspace_size(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().lyc_lora_linear_workspace_size(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt, ctypes.byref(n)))
+    return n.value
+
+
+def lora_workspace_layout(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt):
+    """(h_offset, h_ld, flagged_offset) inside the LoRA workspace."""
+    ho, ld, fo = ctypes.c_size_t(0), ctypes.c_int64(0), ctypes.c_size_t(0)
+    _check(lib().lyc_lora_workspace_layout(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt, ctypes.byref(ho),
+                                           ctypes.byref(ld), ctypes.byref(fo)))
+    return ho.value, ld.value, fo.value
+
+
+def gemm_tile(M: int, N: int, compute_dt: int) -> Tuple[int, int]:
+    """(tile_n, tile_m) of the output tile one workgroup computes for this shape."""
+    tn, tm = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().lyc_gemm_tile(M, N, compute_dt, ctypes.byref(tn), ctypes.byref(tm)))
+    return tn.value, tm.value
+
+
+KERNELS = ("cast", "prep", "hpass", "gemm")
+
+
+def profile_begin(capacity: int) -> None:
+    """Record the device time of each following kernel launch (HIP events)."""
+    _check(lib().lyc_profile_begin(capacity))
+
+
+def profile_end():
+    """Stop recording; returns {kernel: (launches, total_ms)}."""
+    t = (ctypes.c_double * 4)()
+    n = (ctypes.c_int * 4)()
+    _check(lib().lyc_profile_end(t, n))
+    return {KERNELS[k]: (n[k], t[k]) for k in range(4)}
+
+
+def _workspace(nbytes: int, dev, workspace: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return workspace
+    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+
+def linear(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None,
+           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = round_out(round_out(x.W^T) + b) on the GPU (plain affine contract)."""
+    dev = _need_device(x, w, bias, out)
+    M, K = x.shape
+    N = w.shape[0]
+    x_dt, w_dt = dtype_code(x), dtype_code(w)
+    b_dt = dtype_code(bias) if bias is not None else 0
+    _, o_dt = resolve_dtypes([x_dt, w_dt] + ([b_dt] if b_dt else []))
+    if out is None:
+        out = torch.empty((M, N), dtype=_TORCH[o_dt], device=dev)
+    ws = _workspace(linear_workspace_size(M, N, K, x_dt, w_dt, b_dt), dev, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().lyc_linear_fwd(_ptr(x), x_dt, _ptr(w), w_dt, _ptr(bias), b_dt, _ptr(out), dtype_code(out),
+                                M, N, K, _ptr(ws), nbytes, _stream(dev)))
+    return out
+
+
+def lora_linear(x: torch.Tensor, w: torch.Tensor, down: torch.Tensor, up: torch.Tensor, scale: float,
+                bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, return_workspace: bool = False):
+    """y = round_out(x.W^T + scale * round_c(x.down^T).up^T + b) on the GPU.
+
+    x [M,K], w [N,K], down [r,K], up [N,r], bias [N] (optional).  With
+    ``return_workspace`` the workspace tensor is returned too (h_r and the
+    guard counter live in it; see ``lora_workspace_layout``)."""
+    dev = _need_device(x, w, down, up, bias, out)
+    M, K = x.shape
+    N = w.shape[0]
+    r = down.shape[0]
+    x_dt, w_dt, d_dt, u_dt = dtype_code(x), dtype_code(w), dtype_code(down), dtype_code(up)
+    b_dt = dtype_code(bias) if bias is not None else 0
+    _, o_dt = resolve_dtypes([x_dt, w_dt] + ([b_dt] if b_dt else []) + [d_dt, u_dt])
+    if out is None:
+        out = torch.empty((M, N), dtype=_TORCH[o_dt], device=dev)
+    ws = _workspace(lora_workspace_size(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt), dev, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().lyc_lora_linear_fwd(_ptr(x), x_dt, _ptr(w), w_dt, _ptr(bias), b_dt, _ptr(down), d_dt, _ptr(up),
+                                     u_dt, r, float(scale), _ptr(out), dtype_code(out), M, N, K, _ptr(ws), nbytes,
+                                     _stream(dev)))
+    return (out, ws) if return_workspace else out

@@ -1,0 +1,358 @@
+// api.cpp -- the C ABI (include/lyc.h): argument checks, the dtype policy,
+// the workspace layout and the launch sequence.  Every check happens before
+// the first launch, so a failed call has queued nothing.
+#include "../../include/lyc.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <mutex>
+#include <vector>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr int64_t MAX_RANK = 256;
+constexpr int64_t MAX_DIM = (int64_t)1 << 30;
+constexpr int64_t MAX_K = (int64_t)1 << 20;  // keeps per-tile byte offsets below 2^31
+
+bool valid_dt(int dt) { return dt == LYC_F16 || dt == LYC_BF16 || dt == LYC_F32; }
+size_t esize(int dt) { return dt == LYC_F32 ? 4 : 2; }
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Dtype policy (LyCORIS "Precision" page, "Dtype policy").
+int resolve(const int* dts, int n, int* compute, int* output) {
+    if (dts == nullptr || n < 1) return LYC_ERR_INVALID_ARG;
+    bool h16 = false, hbf = false, h32 = false;
+    for (int i = 0; i < n; ++i) {
+        switch (dts[i]) {
+        case LYC_F16: h16 = true; break;
+        case LYC_BF16: hbf = true; break;
+        case LYC_F32: h32 = true; break;
+        default: return LYC_ERR_INVALID_ARG;
+        }
+    }
+    if (h16 && hbf) return LYC_ERR_MIXED_HALF;
+    const int c = h16 ? LYC_F16 : (hbf ? LYC_BF16 : LYC_F32);
+    if (compute) *compute = c;
+    if (output) *output = h32 ? LYC_F32 : c;
+    return LYC_OK;
+}
+
+struct Problem {
+    bool lora;
+    int64_t M, N, K, rank;
+    int x_dt, w_dt, b_dt, d_dt, u_dt;
+    int c_dt, o_dt;
+    int r_pad;
+};
+
+// Shape and dtype checks shared by the size queries and the forward calls.
+int check_problem(Problem& P) {
+    if (P.M < 0 || P.N < 0 || P.K < 0 || P.rank < 0) return LYC_ERR_INVALID_ARG;
+    if (!valid_dt(P.x_dt) || !valid_dt(P.w_dt)) return LYC_ERR_INVALID_ARG;
+    if (P.b_dt != 0 && !valid_dt(P.b_dt)) return LYC_ERR_INVALID_ARG;
+    int dts[5], n = 0;
+    dts[n++] = P.x_dt;
+    dts[n++] = P.w_dt;
+    if (P.b_dt != 0) dts[n++] = P.b_dt;
+    if (P.lora) {
+        if (!valid_dt(P.d_dt) || !valid_dt(P.u_dt)) return LYC_ERR_INVALID_ARG;
+        dts[n++] = P.d_dt;
+        dts[n++] = P.u_dt;
+    }
+    const int st = resolve(dts, n, &P.c_dt, &P.o_dt);
+    if (st != LYC_OK) return st;
+    if (P.M > MAX_DIM || P.N > MAX_DIM || P.K > MAX_K) return LYC_ERR_UNSUPPORTED;
+    if (P.K % 8 != 0) return LYC_ERR_UNSUPPORTED;
+    if (P.rank > MAX_RANK) return LYC_ERR_UNSUPPORTED;
+    if (!P.lora) P.rank = 0;
+    P.r_pad = P.rank == 0 ? 0 : (P.rank <= 32 ? 32 : P.rank <= 64 ? 64 : P.rank <= 128 ? 128 : 256);
+    return LYC_OK;
+}
+
+struct Layout {
+    size_t xc = 0, wc = 0, dc = 0, uc = 0, h = 0, dnorm = 0, flagged = 0, total = 0;
+    bool cast_x = false, cast_w = false;
+};
+
+Layout layout(const Problem& P) {
+    Layout L;
+    size_t off = 0;
+    const size_t ce = esize(P.c_dt);
+    L.cast_x = P.x_dt == LYC_F32 && P.c_dt != LYC_F32;
+    L.cast_w = P.w_dt == LYC_F32 && P.c_dt != LYC_F32;
+    if (L.cast_x) { L.xc = off; off = align256(off + (size_t)(P.M * P.K) * 2); }
+    if (L.cast_w) { L.wc = off; off = align256(off + (size_t)(P.N * P.K) * 2); }
+    if (P.r_pad > 0) {
+        L.dc = off; off = align256(off + (size_t)P.r_pad * (size_t)P.K * ce);
+        L.uc = off; off = align256(off + (size_t)P.N * (size_t)P.r_pad * ce);
+        L.h = off; off = align256(off + (size_t)P.M * (size_t)P.r_pad * ce);
+        L.dnorm = off; off = align256(off + (size_t)P.r_pad * sizeof(double));
+        L.flagged = off; off = align256(off + sizeof(unsigned));
+    }
+    L.total = off;
+    return L;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// ---- optional per-kernel timing (lyc_profile_begin / lyc_profile_end) -------
+struct ProfSlot {
+    hipEvent_t a, b;
+    int kind;
+};
+std::mutex g_prof_mu;
+std::vector<ProfSlot> g_prof;   // created events
+size_t g_prof_used = 0;
+bool g_prof_on = false;
+
+// Launch through `fn`, bracketed by an event pair when profiling is on.
+template <class F>
+hipError_t timed(int kind, hipStream_t s, F fn) {
+    ProfSlot* slot = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        if (g_prof_on && g_prof_used < g_prof.size()) {
+            slot = &g_prof[g_prof_used++];
+            slot->kind = kind;
+        }
+    }
+    if (slot && hipEventRecord(slot->a, s) != hipSuccess) return hipErrorUnknown;
+    const hipError_t e = fn();
+    if (slot && hipEventRecord(slot->b, s) != hipSuccess) return hipErrorUnknown;
+    return e;
+}
+
+// The guard's error factor for one MFMA step, in units of 2^-24 times the
+// Cauchy-Schwarz bound of the step's absolute products.
+constexpr double GUARD_FACTOR = 64.0;
+
+int forward(const Problem& P, const void* x, const void* w, const void* bias, const void* down, const void* up,
+            double scale, void* y, int y_dt, void* ws, size_t ws_bytes, void* stream) {
+    if (y_dt != P.o_dt) return LYC_ERR_DTYPE_MISMATCH;
+    if ((bias == nullptr) != (P.b_dt == 0)) return LYC_ERR_INVALID_ARG;
+    if (P.M == 0 || P.N == 0) return LYC_OK;
+    if (y == nullptr) return LYC_ERR_INVALID_ARG;
+    if (P.K > 0) {
+        if (x == nullptr || w == nullptr) return LYC_ERR_INVALID_ARG;
+        if (!aligned(x, 16) || !aligned(w, 16)) return LYC_ERR_UNSUPPORTED;
+    }
+    if (P.rank > 0) {
+        if (up == nullptr || (P.K > 0 && down == nullptr)) return LYC_ERR_INVALID_ARG;
+        if (!aligned(up, esize(P.u_dt)) || !aligned(down, esize(P.d_dt))) return LYC_ERR_UNSUPPORTED;
+    }
+    if (bias && !aligned(bias, esize(P.b_dt))) return LYC_ERR_UNSUPPORTED;
+    if (!aligned(y, esize(y_dt))) return LYC_ERR_UNSUPPORTED;
+    const Layout L = layout(P);
+    if (L.total > 0) {
+        if (ws == nullptr || ws_bytes < L.total || !aligned(ws, 256)) return LYC_ERR_WORKSPACE;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    char* W = (char*)ws;
+    (void)hipGetLastError();  // clear a stale error so the checks below see only ours
+
+    const void* xa = x;
+    const void* wa = w;
+    if (L.cast_x && P.K > 0) {
+        if (timed(LYC_KERNEL_CAST, s, [&] { return lyc::launch_cast((const float*)x, W + L.xc, P.M * P.K, P.c_dt, s); }) !=
+            hipSuccess)
+            return LYC_ERR_HIP;
+        xa = W + L.xc;
+    }
+    if (L.cast_w && P.K > 0) {
+        if (timed(LYC_KERNEL_CAST, s, [&] { return lyc::launch_cast((const float*)w, W + L.wc, P.N * P.K, P.c_dt, s); }) !=
+            hipSuccess)
+            return LYC_ERR_HIP;
+        wa = W + L.wc;
+    }
+
+    lyc::GemmParams g{};
+    g.a = wa;
+    g.b = xa;
+    g.M = P.M;
+    g.N = P.N;
+    g.K = P.K;
+    g.bias = bias;
+    g.bias_dt = P.b_dt;
+    g.y = y;
+    g.y_dt = y_dt;
+    g.double_round = P.lora ? 0 : 1;
+    g.scale = (float)scale;
+    g.rf = 0;
+    const uintptr_t vec_align = y_dt == LYC_F32 ? 16 : 8;
+    g.vec_store = (P.N % 4 == 0) && aligned(y, vec_align);
+
+    if (P.r_pad > 0) {
+        lyc::PrepParams pp{};
+        pp.down = down;
+        pp.down_dt = P.d_dt;
+        pp.up = up;
+        pp.up_dt = P.u_dt;
+        pp.dc = W + L.dc;
+        pp.uc = W + L.uc;
+        pp.dnorm = (double*)(W + L.dnorm);
+        pp.flagged = (unsigned*)(W + L.flagged);
+        pp.N = P.N;
+        pp.K = P.K;
+        pp.rank = P.rank;
+        pp.r_pad = P.r_pad;
+        pp.c_dt = P.c_dt;
+        if (timed(LYC_KERNEL_PREP, s, [&] { return lyc::launch_prep(pp, s); }) != hipSuccess) return LYC_ERR_HIP;
+
+        lyc::HpassParams hp{};
+        hp.x = xa;
+        hp.d = W + L.dc;
+        hp.dnorm = (const double*)(W + L.dnorm);
+        hp.h = W + L.h;
+        hp.M = P.M;
+        hp.K = P.K;
+        hp.r_pad = P.r_pad;
+        hp.guard = GUARD_FACTOR;
+        hp.flagged = (unsigned*)(W + L.flagged);
+        if (timed(LYC_KERNEL_HPASS, s, [&] { return lyc::launch_hpass(P.c_dt, hp, s); }) != hipSuccess)
+            return LYC_ERR_HIP;
+
+        g.af = W + L.uc;
+        g.bf = W + L.h;
+        g.rf = P.r_pad;
+    }
+    if (timed(LYC_KERNEL_GEMM, s, [&] { return lyc::launch_gemm(P.c_dt, g, s); }) != hipSuccess) return LYC_ERR_HIP;
+    return LYC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lyc_resolve_dtypes(const int* operand_dtypes, int n, int* compute, int* output) {
+    return resolve(operand_dtypes, n, compute, output);
+}
+
+int lyc_linear_workspace_size(int64_t M, int64_t N, int64_t K, int x_dt, int w_dt, int bias_dt, size_t* bytes) {
+    Problem P{false, M, N, K, 0, x_dt, w_dt, bias_dt, 0, 0, 0, 0, 0};
+    const int st = check_problem(P);
+    if (st != LYC_OK) return st;
+    if (bytes) *bytes = layout(P).total;
+    return LYC_OK;
+}
+
+int lyc_linear_fwd(const void* x, int x_dt, const void* w, int w_dt, const void* bias, int bias_dt, void* y,
+                   int y_dt, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+    Problem P{false, M, N, K, 0, x_dt, w_dt, bias_dt, 0, 0, 0, 0, 0};
+    const int st = check_problem(P);
+    if (st != LYC_OK) return st;
+    if (!valid_dt(y_dt)) return LYC_ERR_INVALID_ARG;
+    return forward(P, x, w, bias, nullptr, nullptr, 1.0, y, y_dt, workspace, workspace_bytes, stream);
+}
+
+int lyc_lora_linear_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt, int bias_dt,
+                                   int down_dt, int up_dt, size_t* bytes) {
+    Problem P{true, M, N, K, rank, x_dt, w_dt, bias_dt, down_dt, up_dt, 0, 0, 0};
+    const int st = check_problem(P);
+    if (st != LYC_OK) return st;
+    if (bytes) *bytes = layout(P).total;
+    return LYC_OK;
+}
+
+int lyc_lora_linear_fwd(const void* x, int x_dt, const void* w, int w_dt, const void* bias, int bias_dt,
+                        const void* down, int down_dt, const void* up, int up_dt, int64_t rank, double scale,
+                        void* y, int y_dt, int64_t M, int64_t N, int64_t K, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    Problem P{true, M, N, K, rank, x_dt, w_dt, bias_dt, down_dt, up_dt, 0, 0, 0};
+    const int st = check_problem(P);
+    if (st != LYC_OK) return st;
+    if (!valid_dt(y_dt)) return LYC_ERR_INVALID_ARG;
+    if (!(scale == scale) || scale > 3.4e38 || scale < -3.4e38) return LYC_ERR_INVALID_ARG;
+    return forward(P, x, w, bias, down, up, scale, y, y_dt, workspace, workspace_bytes, stream);
+}
+
+int lyc_lora_workspace_layout(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt, int bias_dt,
+                              int down_dt, int up_dt, size_t* h_offset, int64_t* h_ld, size_t* flagged_offset) {
+    Problem P{true, M, N, K, rank, x_dt, w_dt, bias_dt, down_dt, up_dt, 0, 0, 0};
+    const int st = check_problem(P);
+    if (st != LYC_OK) return st;
+    const Layout L = layout(P);
+    if (h_offset) *h_offset = L.h;
+    if (h_ld) *h_ld = P.r_pad;
+    if (flagged_offset) *flagged_offset = L.flagged;
+    return LYC_OK;
+}
+
+int lyc_profile_begin(int capacity) {
+    if (capacity < 1) return LYC_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (auto& p : g_prof) {
+        (void)hipEventDestroy(p.a);
+        (void)hipEventDestroy(p.b);
+    }
+    g_prof.clear();
+    g_prof_used = 0;
+    g_prof_on = false;
+    for (int i = 0; i < capacity; ++i) {
+        ProfSlot p{};
+        if (hipEventCreate(&p.a) != hipSuccess) return LYC_ERR_HIP;
+        if (hipEventCreate(&p.b) != hipSuccess) {
+            (void)hipEventDestroy(p.a);
+            return LYC_ERR_HIP;
+        }
+        g_prof.push_back(p);
+    }
+    g_prof_on = true;
+    return LYC_OK;
+}
+
+int lyc_profile_end(double* total_ms, int* launches) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    double t[4] = {0, 0, 0, 0};
+    int n[4] = {0, 0, 0, 0};
+    int st = LYC_OK;
+    for (size_t i = 0; i < g_prof_used; ++i) {
+        float ms = 0.f;
+        if (hipEventSynchronize(g_prof[i].b) != hipSuccess ||
+            hipEventElapsedTime(&ms, g_prof[i].a, g_prof[i].b) != hipSuccess) {
+            st = LYC_ERR_HIP;
+            continue;
+        }
+        t[g_prof[i].kind] += ms;
+        n[g_prof[i].kind] += 1;
+    }
+    for (auto& p : g_prof) {
+        (void)hipEventDestroy(p.a);
+        (void)hipEventDestroy(p.b);
+    }
+    g_prof.clear();
+    g_prof_used = 0;
+    g_prof_on = false;
+    for (int k = 0; k < 4; ++k) {
+        if (total_ms) total_ms[k] = t[k];
+        if (launches) launches[k] = n[k];
+    }
+    return st;
+}
+
+int lyc_gemm_tile(int64_t M, int64_t N, int compute_dt, int* tile_n, int* tile_m) {
+    if (M < 0 || N < 0 || !valid_dt(compute_dt)) return LYC_ERR_INVALID_ARG;
+    int tn = 0, tm = 0;
+    lyc::gemm_tile_shape(M, N, compute_dt, &tn, &tm);
+    if (tile_n) *tile_n = tn;
+    if (tile_m) *tile_m = tm;
+    return LYC_OK;
+}
+
+const char* lyc_status_str(int status) {
+    switch (status) {
+    case LYC_OK: return "ok";
+    case LYC_ERR_MIXED_HALF: return "fp16 and bf16 operands in one call (no common 16-bit type; refused)";
+    case LYC_ERR_INVALID_ARG: return "invalid argument";
+    case LYC_ERR_DTYPE_MISMATCH: return "output dtype differs from the resolved output dtype";
+    case LYC_ERR_UNSUPPORTED: return "unsupported shape, alignment or rank";
+    case LYC_ERR_HIP: return "HIP runtime error while launching";
+    case LYC_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,125 @@
+// lyc_device.h -- device-side building blocks shared by the gfx950 kernels:
+// vector types, IEEE round-to-nearest-even conversions, buffer resources and
+// the MFMA step for each compute dtype.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lyc {
+
+enum : int { DT_F16 = 1, DT_BF16 = 2, DT_F32 = 3 };
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// ---- scalar conversions ------------------------------------------------------
+
+__device__ __forceinline__ float f16_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+
+// fp32 -> fp16, round to nearest even (v_cvt_f16_f32 under the default mode;
+// subnormal results kept, overflow to inf).
+__device__ __forceinline__ uint16_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// fp32 -> bf16, round to nearest even on the bit pattern; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float load_as_f32(const void* p, int dt, int64_t i) {
+    if (dt == DT_F32) return ((const float*)p)[i];
+    uint16_t b = ((const uint16_t*)p)[i];
+    return dt == DT_F16 ? f16_to_f32(b) : bf16_to_f32(b);
+}
+
+// binary64 -> 16-bit format (t = stored fraction bits, bias = exponent bias,
+// maxe = all-ones exponent field), round to nearest even, computed on the
+// integer significand so that there is exactly one rounding.
+__device__ __forceinline__ uint16_t f64_to_16(double d, int t, int bias, int maxe) {
+    uint64_t b = __builtin_bit_cast(uint64_t, d);
+    uint16_t sign = (uint16_t)((b >> 63) << 15);
+    int ex = (int)((b >> 52) & 0x7ff);
+    uint64_t frac = b & ((1ull << 52) - 1);
+    if (ex == 0x7ff) return frac ? (uint16_t)(sign | (maxe << t) | (1u << (t - 1))) : (uint16_t)(sign | (maxe << t));
+    if (ex == 0) return sign;  // |d| < 2^-1022 rounds to zero in both 16-bit formats
+    uint64_t m = (1ull << 52) | frac;
+    int e = ex - 1023;
+    int emin = 1 - bias;
+    int shift = 52 - t + (e < emin ? (emin - e) : 0);
+    if (shift >= 54) return sign;  // below half of the smallest subnormal
+    uint64_t q = m >> shift;
+    uint64_t rem = m & ((1ull << shift) - 1);
+    uint64_t half = 1ull << (shift - 1);
+    if (rem > half || (rem == half && (q & 1))) ++q;
+    uint32_t bits;
+    if (e < emin) bits = (uint32_t)q;  // subnormal (q == 2^t carries into the first normal)
+    else bits = ((uint32_t)(e + bias) << t) + (uint32_t)q - (1u << t);
+    if (bits >= ((uint32_t)maxe << t)) bits = (uint32_t)maxe << t;  // overflow -> inf
+    return (uint16_t)(sign | bits);
+}
+
+__device__ __forceinline__ uint16_t f64_to_f16(double d) { return f64_to_16(d, 10, 15, 31); }
+__device__ __forceinline__ uint16_t f64_to_bf16(double d) { return f64_to_16(d, 7, 127, 255); }
+
+// ---- buffer resources (hardware range checking: out-of-range loads read 0) --
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// An offset that is always beyond num_records (which stays below 2^31).
+constexpr uint32_t OOB = 0x80000000u;
+
+__device__ __forceinline__ i32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// ---- MFMA per compute dtype ---------------------------------------------------
+// One "step" consumes, per lane, one 16-byte fragment of A and of B:
+//  16-bit: v_mfma_f32_16x16x32_{f16,bf16}: the 8 elements are 8 k values.
+//  fp32:   four v_mfma_f32_16x16x4_f32, element e of each lane's 4 floats in
+//          the e-th instruction (A and B take the same element, so every
+//          (n,m) pair meets each k exactly once).
+// Output layout (16x16 blocks): lane l, register e holds row 4*(l>>4)+e of the
+// A side and column l&15 of the B side.
+
+struct CF16 {
+    static constexpr int dt = DT_F16;
+    static constexpr int es = 2;
+    __device__ static __forceinline__ f32x4 step(i32x4 a, i32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    }
+};
+struct CBF16 {
+    static constexpr int dt = DT_BF16;
+    static constexpr int es = 2;
+    __device__ static __forceinline__ f32x4 step(i32x4 a, i32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       c, 0, 0, 0);
+    }
+};
+struct CF32 {
+    static constexpr int dt = DT_F32;
+    static constexpr int es = 4;
+    __device__ static __forceinline__ f32x4 step(i32x4 a, i32x4 b, f32x4 c) {
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.x), __builtin_bit_cast(float, b.x), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.y), __builtin_bit_cast(float, b.y), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.z), __builtin_bit_cast(float, b.z), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.w), __builtin_bit_cast(float, b.w), c, 0, 0, 0);
+        return c;
+    }
+};
+
+// LDS tiles: rows of 128 bytes (8 chunks of 16 bytes); chunk kc of row r sits
+// at slot kc ^ (r & 7) so that the 16-byte fragment reads of 8 consecutive rows
+// hit 8 different bank groups.
+__device__ __forceinline__ int lds_off(int row, int kc) { return row * 128 + ((kc ^ (row & 7)) << 4); }
+
+}  // namespace lyc

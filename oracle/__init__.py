@@ -78,6 +78,15 @@ def _ptr(a: Optional[np.ndarray]):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
+def default_threads() -> int:
+    """Host threads for the oracle: the CPUs this process may run on, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def storage_np(dt: int):
     return np.float32 if dt == F32 else np.uint16
 
@@ -161,7 +170,7 @@ def forward(x, x_dt, w, w_dt, b=None, b_dt=None, down=None, down_dt=None, up=Non
         rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
         nrows = rows_arr.size
     if nthreads is None:
-        nthreads = os.cpu_count() or 1
+        nthreads = default_threads()
     st, c_dt, o_dt = resolve([x_dt, w_dt] + ([b_dt] if b is not None else []) +
                              ([down_dt, up_dt] if lora else []))
     if st != OK:

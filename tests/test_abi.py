@@ -1,0 +1,131 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol that
+include/lyc.h declares, resolves the dtype policy exactly, and refuses bad
+arguments with the documented codes before any GPU work (fake pointers are
+never dereferenced because every check precedes the first launch)."""
+import ctypes
+import itertools
+import os
+import re
+
+import pytest
+
+import lora_bypass_linear_amd as L
+import oracle
+from tests import exact
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lyc.h")
+V = ctypes.c_void_p
+P = V(4096)            # a fake, 256-aligned "device pointer" that is never touched
+
+
+def declared_symbols():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lyc_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert len(names) >= 7, names
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), f"liblyc.so does not export {n}"
+
+
+def test_status_strings():
+    lib = L.lib()
+    for s in range(7):
+        assert lib.lyc_status_str(s)
+    assert lib.lyc_status_str(99) == b"unknown status"
+
+
+def test_policy_table_through_abi():
+    for x_dt, w_dt, c_dt, o_dt in exact.load_policy_table():
+        if c_dt is None:
+            with pytest.raises(L.MixedHalfError):
+                L.resolve_dtypes([x_dt, w_dt, w_dt, w_dt, w_dt])
+        else:
+            assert L.resolve_dtypes([x_dt, w_dt, w_dt, w_dt, w_dt]) == (c_dt, o_dt)
+
+
+def test_policy_matches_oracle_on_every_tuple():
+    for n in range(1, 6):
+        for tup in itertools.product([1, 2, 3], repeat=n):
+            st, c, o = oracle.resolve(list(tup))
+            if st == oracle.MIXED_HALF:
+                with pytest.raises(L.MixedHalfError):
+                    L.resolve_dtypes(list(tup))
+            else:
+                assert L.resolve_dtypes(list(tup)) == (c, o), tup
+
+
+def _lin(**kw):
+    a = dict(x=P, x_dt=1, w=P, w_dt=1, b=None, b_dt=0, y=P, y_dt=1, M=4, N=4, K=8, ws=None, nws=0, s=None)
+    a.update(kw)
+    return L.lib().lyc_linear_fwd(a["x"], a["x_dt"], a["w"], a["w_dt"], a["b"], a["b_dt"], a["y"], a["y_dt"],
+                                  a["M"], a["N"], a["K"], a["ws"], a["nws"], a["s"])
+
+
+def _lora(**kw):
+    a = dict(x=P, x_dt=1, w=P, w_dt=1, b=None, b_dt=0, d=P, d_dt=1, u=P, u_dt=1, r=4, scale=1.0, y=P, y_dt=1,
+             M=4, N=4, K=8, ws=P, nws=1 << 20, s=None)
+    a.update(kw)
+    return L.lib().lyc_lora_linear_fwd(a["x"], a["x_dt"], a["w"], a["w_dt"], a["b"], a["b_dt"], a["d"], a["d_dt"],
+                                       a["u"], a["u_dt"], a["r"], ctypes.c_double(a["scale"]), a["y"], a["y_dt"],
+                                       a["M"], a["N"], a["K"], a["ws"], a["nws"], a["s"])
+
+
+def test_linear_argument_errors():
+    assert _lin(w_dt=2) == L.ERR_MIXED_HALF
+    assert _lin(y_dt=3) == L.ERR_DTYPE_MISMATCH
+    assert _lin(x_dt=3, y_dt=1) == L.ERR_DTYPE_MISMATCH      # fp32 x promotes the output to fp32
+    assert _lin(x_dt=7) == L.ERR_INVALID_ARG
+    assert _lin(M=-1) == L.ERR_INVALID_ARG
+    assert _lin(K=12) == L.ERR_UNSUPPORTED                   # rows must be 16-byte multiples
+    assert _lin(x=V(4098)) == L.ERR_UNSUPPORTED              # misaligned x
+    assert _lin(x=None) == L.ERR_INVALID_ARG
+    assert _lin(y=None) == L.ERR_INVALID_ARG
+    assert _lin(b=P, b_dt=0) == L.ERR_INVALID_ARG             # bias pointer without a dtype
+    assert _lin(b=None, b_dt=1) == L.ERR_INVALID_ARG          # dtype without a bias
+    assert _lin(b=P, b_dt=2) == L.ERR_MIXED_HALF
+    # an fp16 bias counts as a 16-bit operand: compute fp16 (fp32 x and W need fp16 copies), output fp32
+    assert _lin(x_dt=3, w_dt=3, y_dt=1, b=P, b_dt=1) == L.ERR_DTYPE_MISMATCH
+    assert _lin(x_dt=3, w_dt=3, y_dt=3, b=P, b_dt=1) == L.ERR_WORKSPACE
+    # fp32 W under fp16 compute needs a workspace for its fp16 copy
+    assert _lin(w_dt=3, y_dt=3) == L.ERR_WORKSPACE
+    assert _lin(w_dt=3, y_dt=3, ws=V(4100), nws=1 << 20) == L.ERR_WORKSPACE   # not 256-aligned
+
+
+def test_empty_calls_are_noops():
+    # nothing is launched for an empty output, so null data pointers are fine
+    assert _lin(M=0, x=None, y=None) == L.OK
+    assert _lin(N=0, w=None, y=None) == L.OK
+    assert _lora(M=0, x=None, y=None, ws=None, nws=0) == L.OK
+
+
+def test_lora_argument_errors():
+    assert _lora(d_dt=2) == L.ERR_MIXED_HALF
+    assert _lora(r=257) == L.ERR_UNSUPPORTED                  # rank beyond the kernel budget
+    assert _lora(r=-1) == L.ERR_INVALID_ARG
+    assert _lora(u=None) == L.ERR_INVALID_ARG
+    assert _lora(d=None) == L.ERR_INVALID_ARG
+    assert _lora(ws=None, nws=0) == L.ERR_WORKSPACE
+    assert _lora(nws=16) == L.ERR_WORKSPACE
+    assert _lora(scale=float("nan")) == L.ERR_INVALID_ARG
+    assert _lora(scale=float("inf")) == L.ERR_INVALID_ARG
+    assert _lora(y_dt=2) == L.ERR_DTYPE_MISMATCH               # y is not a policy operand: bf16 y for fp16 operands
+    assert _lora(u_dt=3, y_dt=1) == L.ERR_DTYPE_MISMATCH
+
+
+def test_workspace_sizes():
+    # LoRA workspace = h [M, r_pad] + down/up copies + norms + counter (+ casts of fp32 x/W)
+    n16 = L.lora_workspace_size(1000, 300, 64, 17, 1, 1, 0, 1, 1)
+    assert n16 >= 1000 * 32 * 2 + 32 * 64 * 2 + 300 * 32 * 2 + 32 * 8
+    ho, ld, fo = L.lora_workspace_layout(1000, 300, 64, 17, 1, 1, 0, 1, 1)
+    assert ld == 32 and ho % 256 == 0 and fo % 256 == 0 and fo < n16
+    assert L.linear_workspace_size(64, 64, 64, 1, 1) == 0
+    assert L.linear_workspace_size(64, 32, 64, 2, 3) >= 32 * 64 * 2     # bf16 copy of an fp32 W
+    assert L.lora_workspace_size(8, 8, 8, 0, 1, 1, 0, 1, 1) == 0        # rank 0: no bypass
+    for r, pad in ((1, 32), (32, 32), (33, 64), (64, 64), (65, 128), (129, 256), (256, 256)):
+        assert L.lora_workspace_layout(16, 16, 16, r, 2, 2, 0, 2, 2)[1] == pad

@@ -1,0 +1,225 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the
+same seeded inputs, element by element.
+
+Bar: every element within abs(gpu - ref) <= atol + rtol*|ref| (fp16: 2e-4 +
+2e-3|ref|, Luminal FP16 page; bf16: 2e-3 + 1.6e-2|ref|; fp32 output from
+16-bit compute: the 16-bit bound; fp32 compute: 8*2^-24*sqrt(K+r)*(1+|ref|)),
+and the rounded h identical, bit for bit, to the oracle's for 16-bit compute.
+"""
+import numpy as np
+import pytest
+import torch
+
+import lora_bypass_linear_amd as L
+import oracle
+import workloads as WL
+from tests import exact
+from tests.gpu_cases import gpu_forward, oracle_forward, say, sample_rows, score
+
+pytestmark = pytest.mark.gpu
+
+BASE = WL.WORKLOADS
+
+
+def _check(wl, inputs=None, rows=None, scale=None, h_exact=True):
+    inputs = inputs if inputs is not None else WL.generate(wl)
+    y, h, flagged = gpu_forward(inputs, wl, scale=scale)
+    res = oracle_forward(inputs, wl, rows=rows, scale=scale)
+    s = score(y, res, rows, wl.K, wl.r)
+    print(wl.name, {k: v for k, v in s.items() if k != "first_bad"}, "flagged", flagged)
+    assert s["fail"] == 0, s
+    if wl.kind == "lora" and wl.r > 0:
+        hr = h if rows is None else h[np.asarray(rows)]
+        if s["compute"] != L.F32 and h_exact:
+            mism = np.argwhere(hr != res["h"])
+            assert mism.size == 0, f"h_r differs from the oracle at {mism[:5].tolist()}"
+    return s
+
+
+# ---- the hand-built boundary fixtures, through the library ----------------------
+
+FIXTURES = exact.load_fixtures()
+
+
+@pytest.mark.parametrize("fx", FIXTURES, ids=[f["name"] for f in FIXTURES])
+def test_fixture_on_gpu(fx):
+    a = exact.fixture_arrays(fx)
+    dt = a["dt"]
+    tdt = {1: torch.float16, 2: torch.bfloat16}[dt]
+    dev = torch.device("cuda:0")
+
+    def t(arr):
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(tdt).to(dev)
+
+    say("fixture", fx["name"])
+    b = t(a["b"]) if a["b"] is not None else None
+    if fx["kind"] == "lora":
+        y = L.lora_linear(t(a["x"]), t(a["w"]), t(a["down"]), t(a["up"]), a["scale"], b)
+    else:
+        y = L.linear(t(a["x"]), t(a["w"]), b)
+    torch.cuda.synchronize()
+    assert float(y.float().item()) == float(fx["expect"]), (fx["name"], float(y.float().item()))
+
+
+# ---- every workload at oracle-friendly sizes (all tiles, ragged tails) -----------
+
+SMALL = {
+    "affine_f16_1024x768x1024": dict(M=300, K=264, N=333),
+    "lora_f16_4096x3072x3072_r16": dict(M=300, K=392, N=333),
+    "lora_bf16x_f32w_8192x4096x4096_r64": dict(M=257, K=264, N=200),
+    "lora_bf16_16384x8192x8192_r128": dict(M=270, K=520, N=300),
+}
+SMALL.update({n: dict(M=130, K=136, N=260) for n in WL.SWEEP})
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_full_output(name):
+    wl = BASE[name].resized(**SMALL[name])
+    if wl.kind == "lora" and ((wl.x_dt, wl.w_dt) in ((1, 2), (2, 1))):
+        inputs = WL.generate(wl)
+        with pytest.raises(L.MixedHalfError):
+            gpu_forward(inputs, wl)
+        return
+    _check(wl)
+
+
+# shapes chosen so that each output-tile configuration runs, with ragged M, N and K
+TILE_SHAPES = [(300, 333, 264), (1000, 2500, 392), (2600, 3100, 264), (3100, 4000, 136)]
+
+
+@pytest.mark.parametrize("M,N,K", TILE_SHAPES)
+@pytest.mark.parametrize("name", ["lora_f16_4096x3072x3072_r16", "lora_bf16_16384x8192x8192_r128",
+                                  "affine_f16_1024x768x1024"])
+def test_tiles_sampled_rows(name, M, N, K):
+    wl = BASE[name].resized(M=M, N=N, K=K)
+    _check(wl, rows=sample_rows(M, 24, seed=M))
+
+
+def test_every_tile_configuration_is_covered():
+    tiles = {L.gemm_tile(M, N, L.F16) for M, N, _ in TILE_SHAPES}
+    assert tiles == {(64, 64), (128, 128), (192, 256), (256, 256)}
+
+
+def test_fp32_compute_tiles():
+    wl = BASE["sweep_xf32_wf32_2048x1280x5120_r32"].resized(M=1000, N=2500, K=136)
+    assert L.gemm_tile(1000, 2500, L.F32) == (128, 128)
+    _check(wl, rows=sample_rows(1000, 24))
+
+
+# ---- edge cases ---------------------------------------------------------------------
+
+EDGE = [
+    ("one_by_one", "lora_f16_4096x3072x3072_r16", dict(M=1, N=1, K=8, r=1), None),
+    ("k_zero", "lora_bf16_16384x8192x8192_r128", dict(M=5, N=7, K=0, r=3), None),
+    ("rank_one", "lora_f16_4096x3072x3072_r16", dict(M=65, N=70, K=72, r=1), None),
+    ("rank_17", "lora_f16_4096x3072x3072_r16", dict(M=65, N=70, K=72, r=17), None),
+    ("rank_200", "lora_bf16_16384x8192x8192_r128", dict(M=100, N=90, K=264, r=200), None),
+    ("rank_256", "lora_f16_4096x3072x3072_r16", dict(M=70, N=64, K=128, r=256), None),
+    ("odd_n", "lora_f16_4096x3072x3072_r16", dict(M=67, N=131, K=64, r=16), None),
+    ("scale_3", "lora_f16_4096x3072x3072_r16", dict(M=64, N=64, K=256, r=16), 3.0),
+    ("scale_neg", "lora_bf16_16384x8192x8192_r128", dict(M=64, N=96, K=256, r=32), -0.75),
+    ("affine_k8", "affine_f16_1024x768x1024", dict(M=3, N=5, K=8), None),
+    ("affine_odd_n", "affine_f16_1024x768x1024", dict(M=70, N=99, K=64), None),
+]
+
+
+@pytest.mark.parametrize("tag,name,dims,scale", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_cases(tag, name, dims, scale):
+    wl = BASE[name].resized(**dims)
+    _check(wl, scale=scale)
+
+
+def test_rank_zero_is_single_rounding():
+    wl = BASE["lora_f16_4096x3072x3072_r16"].resized(M=40, N=48, K=64, r=0)
+    _check(wl)
+
+
+def test_empty_tokens():
+    dev = torch.device("cuda:0")
+    x = torch.empty((0, 64), dtype=torch.float16, device=dev)
+    w = torch.randn(32, 64, device=dev).half()
+    d = torch.randn(4, 64, device=dev).half()
+    u = torch.randn(32, 4, device=dev).half()
+    say("empty tokens")
+    y = L.lora_linear(x, w, d, u, 1.0)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 32)
+
+
+def test_overflow_to_inf_matches():
+    wl = BASE["lora_f16_4096x3072x3072_r16"].resized(M=32, N=40, K=64, r=16)
+    inputs = WL.generate(wl)
+    inputs["x"] = (inputs["x"].float() * 3000).clamp(-60000, 60000).half()
+    inputs["w"] = (inputs["w"].float() * 200).half()                          # many outputs beyond fp16 range
+    res = oracle_forward(inputs, wl)
+    assert np.isinf(oracle.as_float64(res["y"], oracle.F16)).mean() > 0.2
+    _check(wl, inputs=inputs)
+
+
+def test_unaligned_output_rows():
+    """y that is a view starting one element into a buffer: only element alignment."""
+    wl = BASE["lora_f16_4096x3072x3072_r16"].resized(M=33, N=64, K=64, r=16)
+    inputs = WL.generate(wl)
+    dev = torch.device("cuda:0")
+    d = {k: v.to(dev) for k, v in inputs.items()}
+    buf = torch.zeros(33 * 64 + 1, dtype=torch.float16, device=dev)
+    out = buf[1:].view(33, 64)
+    say("unaligned y")
+    L.lora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, out=out)
+    ref, _, _ = gpu_forward(inputs, wl)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), ref)
+    assert buf[0].item() == 0
+
+
+def test_deterministic():
+    wl = BASE["lora_bf16_16384x8192x8192_r128"].resized(M=300, N=400, K=520)
+    inputs = WL.generate(wl)
+    y1, h1, _ = gpu_forward(inputs, wl)
+    y2, h2, _ = gpu_forward(inputs, wl)
+    assert torch.equal(y1, y2) and np.array_equal(h1, h2)
+
+
+def test_h_guard_resolves_midpoints():
+    """h values placed exactly on fp16 rounding midpoints, or 2^-20 either side,
+    behind large terms that cancel exactly in pairs (so fp32 partial sums are
+    inexact): h_r must still be the correctly rounded exact value."""
+    K, r, M = 64, 16, 64
+    rng = np.random.default_rng(5)
+    x = np.zeros((M, K))
+    down = np.zeros((r, K))
+    down[:, 0] = 1 + rng.integers(0, 1024, size=r) / 1024      # fp16 values in [1, 2)
+    x[:, 0] = 1
+    down[:, 1] = 2.0 ** -11                                     # + half an ulp: on the midpoint
+    x[:, 1] = 1
+    down[:, 2] = 2.0 ** -20                                     # a hair below, on, or above it
+    x[:, 2] = rng.choice([-1.0, 0.0, 1.0], size=M)
+    for k in range(3, K - 1, 2):
+        v = rng.integers(1, 64, size=r) * 4.0
+        u = rng.integers(1, 64, size=M) / 4.0
+        down[:, k], down[:, k + 1] = v, -v
+        x[:, k] = x[:, k + 1] = u
+    wl = BASE["lora_f16_4096x3072x3072_r16"].resized(M=M, N=32, K=K, r=r)
+    inputs = WL.generate(wl)
+    inputs["x"] = torch.from_numpy(x).half()
+    inputs["down"] = torch.from_numpy(down).half()
+    assert np.array_equal(inputs["x"].double().numpy(), x) and np.array_equal(inputs["down"].double().numpy(), down)
+    _check(wl, inputs=inputs)
+
+
+# ---- the full-size workloads, in the launch configuration the benchmark uses -----
+
+FULL = ["affine_f16_1024x768x1024", "lora_f16_4096x3072x3072_r16", "lora_bf16x_f32w_8192x4096x4096_r64",
+        "lora_bf16_16384x8192x8192_r128"] + WL.SWEEP
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_rows(name):
+    wl = BASE[name]
+    if (wl.x_dt, wl.w_dt) in ((1, 2), (2, 1)):
+        inputs = WL.generate(wl.resized(M=8))
+        with pytest.raises(L.MixedHalfError):
+            gpu_forward(inputs, wl.resized(M=8))
+        return
+    rows = sample_rows(wl.M, 24 if wl.M * wl.N * wl.K > 1e11 else 48, seed=wl.seed)
+    _check(wl, rows=rows)
