@@ -75,18 +75,19 @@ enum {
 int lyc_resolve_dtypes(const int* operand_dtypes, int n, int* compute, int* output);
 
 /*
- * Workspace bytes lyc_linear_fwd needs for this problem (0 when no operand
- * has to be cast: the compute dtype equals both storage dtypes).  The
- * workspace holds compute-dtype copies of fp32 operands that feed a 16-bit
- * contraction.  Returns the same argument errors as lyc_linear_fwd.
+ * Workspace bytes lyc_linear_fwd needs for this problem: the row norms of W
+ * and a counter used by the projection's rounding guard, plus compute-dtype
+ * copies of fp32 operands that feed a 16-bit contraction.  Returns the same
+ * argument errors as lyc_linear_fwd.
  */
 int lyc_linear_workspace_size(int64_t M, int64_t N, int64_t K, int x_dt, int w_dt, int bias_dt,
                               size_t* bytes);
 
 /*
  * Plain affine forward with a declared rounding boundary (Luminal FP16
- * page, "What Was Fixed"): p = x.W^T with fp32 accumulation of the
- * compute-dtype operands, p rounded to the output dtype, then
+ * page, "What Was Fixed"): p = x_c.W_c^T (fp32 MFMA steps summed in fp64),
+ * p rounded to the output dtype exactly as its exact value rounds (a guard
+ * re-evaluates in fp64 every element near a rounding midpoint), then
  * y = round_out(p + b).  bias may be NULL (bias_dt 0): y = round_out(p).
  */
 int lyc_linear_fwd(const void* x, int x_dt, const void* w, int w_dt, const void* bias, int bias_dt,

@@ -73,7 +73,8 @@ int check_problem(Problem& P) {
 }
 
 struct Layout {
-    size_t xc = 0, wc = 0, dc = 0, uc = 0, h = 0, dnorm = 0, flagged = 0, total = 0;
+    size_t xc = 0, wc = 0, dc = 0, dh = 0, dl = 0, uc = 0, h = 0, dnorm = 0, wh = 0, wl = 0, wnorm = 0, flagged = 0,
+           total = 0;
     bool cast_x = false, cast_w = false;
 };
 
@@ -85,11 +86,25 @@ Layout layout(const Problem& P) {
     L.cast_w = P.w_dt == LYC_F32 && P.c_dt != LYC_F32;
     if (L.cast_x) { L.xc = off; off = align256(off + (size_t)(P.M * P.K) * 2); }
     if (L.cast_w) { L.wc = off; off = align256(off + (size_t)(P.N * P.K) * 2); }
+    const bool split = P.c_dt != LYC_F32;   // hi/lo split of the second contraction operand
     if (P.r_pad > 0) {
         L.dc = off; off = align256(off + (size_t)P.r_pad * (size_t)P.K * ce);
+        if (split) {
+            L.dh = off; off = align256(off + (size_t)P.r_pad * (size_t)P.K * ce);
+            L.dl = off; off = align256(off + (size_t)P.r_pad * (size_t)P.K * ce);
+        }
         L.uc = off; off = align256(off + (size_t)P.N * (size_t)P.r_pad * ce);
         L.h = off; off = align256(off + (size_t)P.M * (size_t)P.r_pad * ce);
-        L.dnorm = off; off = align256(off + (size_t)P.r_pad * sizeof(double));
+        L.dnorm = off; off = align256(off + (size_t)P.r_pad * 2 * sizeof(double));
+        L.flagged = off; off = align256(off + sizeof(unsigned));
+    }
+    if (!P.lora) {
+        // the projection's rounding guard: hi/lo split and row norms of W_c, a counter
+        if (split) {
+            L.wh = off; off = align256(off + (size_t)P.N * (size_t)P.K * ce);
+            L.wl = off; off = align256(off + (size_t)P.N * (size_t)P.K * ce);
+        }
+        L.wnorm = off; off = align256(off + (size_t)P.N * 2 * sizeof(double));
         L.flagged = off; off = align256(off + sizeof(unsigned));
     }
     L.total = off;
@@ -124,10 +139,6 @@ hipError_t timed(int kind, hipStream_t s, F fn) {
     if (slot && hipEventRecord(slot->b, s) != hipSuccess) return hipErrorUnknown;
     return e;
 }
-
-// The guard's error factor for one MFMA step, in units of 2^-24 times the
-// Cauchy-Schwarz bound of the step's absolute products.
-constexpr double GUARD_FACTOR = 64.0;
 
 int forward(const Problem& P, const void* x, const void* w, const void* bias, const void* down, const void* up,
             double scale, void* y, int y_dt, void* ws, size_t ws_bytes, void* stream) {
@@ -168,6 +179,38 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
         wa = W + L.wc;
     }
 
+    if (!P.lora) {
+        // plain affine: exact-rounding contraction with the round-then-add-bias epilogue
+        const bool guard = P.c_dt != LYC_F32 && y_dt != LYC_F32;
+        double2* wn = (double2*)(W + L.wnorm);
+        unsigned* fl = (unsigned*)(W + L.flagged);
+        const bool split = P.c_dt != LYC_F32;
+        if (split && timed(LYC_KERNEL_PREP, s, [&] {
+                return lyc::launch_rownorm(wa, P.c_dt, P.N, P.K, W + L.wh, W + L.wl, wn, fl, s);
+            }) != hipSuccess)
+            return LYC_ERR_HIP;
+        lyc::XrParams xp{};
+        xp.x = xa;
+        xp.b = split ? (const void*)(W + L.wh) : wa;
+        xp.b_lo = split ? (const void*)(W + L.wl) : nullptr;
+        xp.b_full = wa;
+        xp.bnorm = wn;
+        xp.M = P.M;
+        xp.Nc = P.N;
+        xp.K = P.K;
+        xp.guard = guard ? 1 : 0;
+        xp.flagged = fl;
+        xp.mode = lyc::XR_AFFINE;
+        xp.out = y;
+        xp.ld_out = P.N;
+        xp.out_dt = y_dt;
+        xp.bias = bias;
+        xp.bias_dt = P.b_dt;
+        xp.vec_store = (P.N % 4 == 0) && aligned(y, y_dt == LYC_F32 ? 16 : 8);
+        if (timed(LYC_KERNEL_GEMM, s, [&] { return lyc::launch_xr(P.c_dt, xp, s); }) != hipSuccess) return LYC_ERR_HIP;
+        return LYC_OK;
+    }
+
     lyc::GemmParams g{};
     g.a = wa;
     g.b = xa;
@@ -178,7 +221,6 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
     g.bias_dt = P.b_dt;
     g.y = y;
     g.y_dt = y_dt;
-    g.double_round = P.lora ? 0 : 1;
     g.scale = (float)scale;
     g.rf = 0;
     const uintptr_t vec_align = y_dt == LYC_F32 ? 16 : 8;
@@ -191,8 +233,10 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
         pp.up = up;
         pp.up_dt = P.u_dt;
         pp.dc = W + L.dc;
+        pp.dh = W + L.dh;
+        pp.dl = W + L.dl;
         pp.uc = W + L.uc;
-        pp.dnorm = (double*)(W + L.dnorm);
+        pp.dnorm = (double2*)(W + L.dnorm);
         pp.flagged = (unsigned*)(W + L.flagged);
         pp.N = P.N;
         pp.K = P.K;
@@ -201,17 +245,22 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
         pp.c_dt = P.c_dt;
         if (timed(LYC_KERNEL_PREP, s, [&] { return lyc::launch_prep(pp, s); }) != hipSuccess) return LYC_ERR_HIP;
 
-        lyc::HpassParams hp{};
+        lyc::XrParams hp{};
+        const bool split = P.c_dt != LYC_F32;
         hp.x = xa;
-        hp.d = W + L.dc;
-        hp.dnorm = (const double*)(W + L.dnorm);
-        hp.h = W + L.h;
+        hp.b = W + (split ? L.dh : L.dc);
+        hp.b_lo = split ? (const void*)(W + L.dl) : nullptr;
+        hp.b_full = W + L.dc;
+        hp.bnorm = (const double2*)(W + L.dnorm);
         hp.M = P.M;
+        hp.Nc = P.r_pad;
         hp.K = P.K;
-        hp.r_pad = P.r_pad;
-        hp.guard = GUARD_FACTOR;
+        hp.guard = P.c_dt != LYC_F32 ? 1 : 0;
         hp.flagged = (unsigned*)(W + L.flagged);
-        if (timed(LYC_KERNEL_HPASS, s, [&] { return lyc::launch_hpass(P.c_dt, hp, s); }) != hipSuccess)
+        hp.mode = lyc::XR_H;
+        hp.out = W + L.h;
+        hp.ld_out = P.r_pad;
+        if (timed(LYC_KERNEL_HPASS, s, [&] { return lyc::launch_xr(P.c_dt, hp, s); }) != hipSuccess)
             return LYC_ERR_HIP;
 
         g.af = W + L.uc;

@@ -9,14 +9,11 @@
 //   1. fold   (LoRA only)  acc  = h_r . up_c^T   over the padded rank, then
 //                          acc *= scale          (one fp32 multiply)
 //   2. main               acc += x_c . W_c^T     K loop, LDS double buffer
-//   3. epilogue           y = round_out(acc + b)            (LoRA)
-//                         y = round_out(round_out(acc) + b) (plain affine)
+//   3. epilogue           y = round_out(acc + b), one rounding
 //
 // Accumulation is fp32 throughout (LyCORIS "Precision" page, "Dtype policy");
 // the bypass lands in the same accumulators as x.W^T, so Delta W = up.down is
-// never formed ("VRAM" section).  The plain affine epilogue keeps the
-// projection's rounding boundary before the bias (Luminal FP16 page, "What Was
-// Fixed").
+// never formed ("VRAM" section).
 #include "kernels.h"
 #include "lyc_device.h"
 
@@ -98,12 +95,6 @@ __device__ __forceinline__ void mma_stage(const char* sa, const char* sb, f32x4 
     }
 }
 
-__device__ __forceinline__ float round_as(float v, int dt) {
-    if (dt == DT_F16) return f16_to_f32(f32_to_f16(v));
-    if (dt == DT_BF16) return bf16_to_f32(f32_to_bf16(v));
-    return v;
-}
-
 template <class CT, class TL>
 __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles_n, int tiles_m, int group_m) {
     __shared__ __attribute__((aligned(16))) char smem[2 * TL::STAGE];
@@ -146,31 +137,50 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
             for (int j = 0; j < FM; ++j) acc[i][j] *= p.scale;
     }
 
-    // 2. main K loop, double-buffered through LDS
+    // 2. main K loop: two LDS stages, and global loads issued two K steps ahead
+    //    into alternating register sets, so a load has a full compute phase of
+    //    the previous step plus its own to arrive.
     const uint32_t kbytes = (uint32_t)(p.K * CT::es);
     if (kbytes > 0) {
         const auto rsa = make_rsrc((const char*)p.a + n0 * kbytes, (uint32_t)rows_a * kbytes);
         const auto rsb = make_rsrc((const char*)p.b + m0 * kbytes, (uint32_t)rows_b * kbytes);
         const int KT = (int)((kbytes + 127) / 128);
+        i32x4 ra2[TL::CA], rb2[TL::CB];
         load_chunks<TL::CA, NT>(ra, rsa, kbytes, 0, tid);
         load_chunks<TL::CB, NT>(rb, rsb, kbytes, 0, tid);
+        if (KT > 1) {
+            load_chunks<TL::CA, NT>(ra2, rsa, kbytes, 128, tid);
+            load_chunks<TL::CB, NT>(rb2, rsb, kbytes, 128, tid);
+        }
         store_chunks<TL::CA, NT>(st0, ra, tid);
         store_chunks<TL::CB, NT>(st0 + TL::TN * 128, rb, tid);
         __syncthreads();
-        for (int kt = 0; kt < KT; ++kt) {
-            char* cur = (kt & 1) ? st1 : st0;
-            char* nxt = (kt & 1) ? st0 : st1;
-            const bool more = kt + 1 < KT;
-            if (more) {
-                load_chunks<TL::CA, NT>(ra, rsa, kbytes, (uint32_t)(kt + 1) * 128, tid);
-                load_chunks<TL::CB, NT>(rb, rsb, kbytes, (uint32_t)(kt + 1) * 128, tid);
+        // invariant at the top of step kt: LDS stage kt&1 holds step kt; the
+        // register set (kt+1)&1 holds (or is receiving) step kt+1
+        for (int kt = 0; kt < KT; kt += 2) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int k = kt + half;
+                if (k >= KT) break;
+                char* cur = half ? st1 : st0;
+                char* nxt = half ? st0 : st1;
+                i32x4(&rn_a)[TL::CA] = half ? ra2 : ra;      // receives step k+2
+                i32x4(&rn_b)[TL::CB] = half ? rb2 : rb;
+                i32x4(&rs_a)[TL::CA] = half ? ra : ra2;      // holds step k+1
+                i32x4(&rs_b)[TL::CB] = half ? rb : rb2;
+                if (k + 2 < KT) {
+                    load_chunks<TL::CA, NT>(rn_a, rsa, kbytes, (uint32_t)(k + 2) * 128, tid);
+                    load_chunks<TL::CB, NT>(rn_b, rsb, kbytes, (uint32_t)(k + 2) * 128, tid);
+                }
+                __builtin_amdgcn_s_setprio(1);
+                mma_stage<CT, TL>(cur, cur + TL::TN * 128, acc, lane, wn, wm);
+                __builtin_amdgcn_s_setprio(0);
+                if (k + 1 < KT) {
+                    store_chunks<TL::CA, NT>(nxt, rs_a, tid);
+                    store_chunks<TL::CB, NT>(nxt + TL::TN * 128, rs_b, tid);
+                }
+                __syncthreads();
             }
-            mma_stage<CT, TL>(cur, cur + TL::TN * 128, acc, lane, wn, wm);
-            if (more) {
-                store_chunks<TL::CA, NT>(nxt, ra, tid);
-                store_chunks<TL::CB, NT>(nxt + TL::TN * 128, rb, tid);
-            }
-            __syncthreads();
         }
     }
 
@@ -190,7 +200,7 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float a = acc[i][j][e];
-                v[e] = p.double_round ? round_as(a, p.y_dt) + bias[e] : a + bias[e];
+                v[e] = a + bias[e];
             }
             const int64_t base = m * p.N + nb;
             if (p.y_dt == DT_F32) {

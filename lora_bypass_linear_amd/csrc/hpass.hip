@@ -1,73 +1,127 @@
-// hpass.hip -- the low-rank contraction h = x_c . down_c^T and its rounding to
-// the compute (storage) dtype, h_r = round_c(h) (LyCORIS "Precision" page,
-// "Measured accuracy": the intermediate is rounded to the storage dtype before
-// its second dot, as the eager two-Linear chain does).
+// hpass.hip -- contractions whose result is rounded to a 16-bit format and
+// then used again, so that the rounding decision must be the one the exact
+// value gets:
+//   * h = x_c . down_c^T, rounded to the compute (storage) dtype before its
+//     second dot (LyCORIS "Precision" page, "Measured accuracy");
+//   * the plain affine projection p = x_c . W_c^T, rounded to the output dtype
+//     before the bias is added (Luminal FP16 page, "What Was Fixed").
+// A value that lands on the wrong side of a rounding midpoint moves by one
+// 16-bit ulp, and the following sum (bias, or the whole bypass row) can cancel
+// down to where that ulp is far outside any per-element tolerance.
 //
-// The rounding decision is taken on the exact h, not on an fp32 running sum:
-// an fp32 sum that lands on the other side of a rounding midpoint than the
-// exact value would move the whole output row by scale * ulp(h) * up.  So:
-//   * each MFMA step (32 products for 16-bit compute) starts from zero and its
-//     fp32 result is added into an fp64 accumulator;
-//   * the error of that sum is bounded by  guard * 2^-24 * |x_m|_2 * |d_j|_2
-//     (Cauchy-Schwarz bound on sum_k |x_mk d_jk|, times the per-step error
-//     factor of the MFMA);
-//   * when [h - E, h + E] straddles a rounding boundary of the 16-bit format,
-//     the element is re-evaluated as an fp64 dot product over K (one wave per
-//     element, products exact) before rounding.
-// For fp32 compute the rounding to fp32 moves y by O(2^-24) and no guard is
-// needed.
+// Method (16-bit compute).  K is cut into blocks of 64.  In each block a row
+// of x and a row of b (down_c or W_c) are split as v = v_hi + v_lo, v_hi the
+// value rounded to the grid 2^(e-7), e = floor(log2 max|v|) over the block.
+//   hh:    b_hi . x_hi   every product is an integer times the block's grid
+//                        product with magnitude <= 2^16, so every partial sum
+//                        of the block's 64 products is an integer below 2^22
+//                        times that grid: exact in fp32 however the MFMA
+//                        orders or aligns its additions.  Added to an fp64
+//                        accumulator once per block (exact).
+//   cross: b_lo . x + b_hi . x_lo   small (|v_lo| <= 2^(e-8)); one MFMA chain
+//                        per 32-k step, added to the fp64 accumulator.
+// gfx950 MFMA steps keep about two bits below the ulp of their running sum
+// and truncate (measured), so a step adding terms of total magnitude S to an
+// accumulator C errs by less than 18 * 2^-24 * (|C| + S); the cross chain of
+// a step therefore errs by less than 36 * 2^-24 * S_cross, and over all steps
+// (Cauchy-Schwarz on the sums of |products|)
+//   E(m, j) = 36 * 2^-24 * (|x_m| |b_lo,j| + |x_lo,m| (|b_j| + |b_lo,j|)) + fp64 slack,
+// with |x_m| and |x_lo,m| bounded from the block maxima (64 max^2 and
+// 16 * 4^g per block), which stay valid however small the values are.
+// When [h - E, h + E] straddles a rounding boundary of the 16-bit format, the
+// element is re-evaluated as an fp64 dot product over K (products exact) by
+// one wave before rounding.  fp32 compute, or an fp32 rounding target, needs
+// no guard: a flip there moves the result by 2^-24 relative.
 //
-// Work split: a workgroup of 4 waves owns 64 rows; a wave owns 16 rows and all
-// r_pad = 16*JB columns.  down_c is staged through LDS (shared by the 4 waves);
-// each lane streams its own x fragment straight from HBM (x is read once).
+// Work split: a workgroup of 4 waves owns RW*16 rows and RP = 16*JB columns;
+// its waves form RW row groups x KS k groups (k group g takes the blocks
+// g, g+KS, ...; partial sums meet in LDS at the end).  b_hi and b_lo tiles are
+// staged through LDS; each lane streams its own x fragments from HBM.
 #include "kernels.h"
 #include "lyc_device.h"
 
 namespace lyc {
 
+// Step error factor of the cross chain, in units of 2^-24 of its absolute sums
+// (two chained steps, each below 18 * 2^-24 of |accumulator| + sum|products|).
+constexpr double GUARD_CROSS = 36.0;
+
 template <class CT>
-__device__ __forceinline__ float sumsq16(i32x4 v) {
-    float s = 0.f;
-    if (CT::dt == DT_F32) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float f = __builtin_bit_cast(float, v[i]);
-            s += f * f;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t u = (uint32_t)v[i];
-            const float a = CT::dt == DT_F16 ? f16_to_f32((uint16_t)u) : bf16_to_f32((uint16_t)u);
-            const float b = CT::dt == DT_F16 ? f16_to_f32((uint16_t)(u >> 16)) : bf16_to_f32((uint16_t)(u >> 16));
-            s += a * a + b * b;
-        }
-    }
-    return s;
+__device__ __forceinline__ float unpack_lo(uint32_t u) {
+    return CT::dt == DT_F16 ? f16_to_f32((uint16_t)u) : bf16_to_f32((uint16_t)u);
+}
+template <class CT>
+__device__ __forceinline__ float unpack_hi(uint32_t u) {
+    return CT::dt == DT_F16 ? f16_to_f32((uint16_t)(u >> 16)) : __builtin_bit_cast(float, u & 0xffff0000u);
+}
+// two floats that are exactly representable in the 16-bit format -> packed pair
+template <class CT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    if (CT::dt == DT_F16) return (uint32_t)f32_to_f16(a) | ((uint32_t)f32_to_f16(b) << 16);
+    return (__builtin_bit_cast(uint32_t, a) >> 16) | (__builtin_bit_cast(uint32_t, b) & 0xffff0000u);
 }
 
-// exact products of two 16-byte fragments, summed in fp64
+// largest |value| among the 8 16-bit values of a fragment, as its bit pattern
+// (for finite values the magnitude order is the integer order without the sign)
+__device__ __forceinline__ uint32_t absmax_bits(i32x4 v) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t u = (uint32_t)v[i] & 0x7fff7fffu;
+        const uint32_t lo = u & 0xffffu, hi = u >> 16;
+        m = m > lo ? m : lo;
+        m = m > hi ? m : hi;
+    }
+    return m;
+}
+
+// grid exponent g = floor(log2 m) - 7 of a positive 16-bit magnitude m (bits)
+template <class CT>
+__device__ __forceinline__ int grid_exp(uint32_t m) {
+    if (CT::dt == DT_F16) {
+        const int E = (int)(m >> 10);
+        const int e = E > 0 ? E - 15 : (31 - __builtin_clz(m | 1u)) - 24;
+        return e - 7;
+    }
+    const int E = (int)(m >> 7);
+    const int e = E > 0 ? E - 127 : (31 - __builtin_clz(m | 1u)) - 133;
+    return e - 7;
+}
+
+// Split a fragment on the grid 2^g (round to nearest): hi on the grid, lo = v - hi.
+// Adding and subtracting 1.5 * 2^(g+23) rounds an fp32 value of magnitude below
+// 2^(g+22) to a multiple of 2^g.
+template <class CT>
+__device__ __forceinline__ void split16(i32x4 v, float magic, i32x4& hi, i32x4& lo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t u = (uint32_t)v[i];
+        const float a = unpack_lo<CT>(u), b = unpack_hi<CT>(u);
+        const float ah = (a + magic) - magic, bh = (b + magic) - magic;
+        hi[i] = (int)pack2<CT>(ah, bh);
+        lo[i] = (int)pack2<CT>(a - ah, b - bh);
+    }
+}
+
+// exact products of two 16-byte fragments, summed in fp64 (two chains)
 template <class CT>
 __device__ __forceinline__ double dot16_f64(i32x4 a, i32x4 b) {
-    double s = 0.0;
+    double s0 = 0.0, s1 = 0.0;
     if (CT::dt == DT_F32) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            s = __builtin_fma((double)__builtin_bit_cast(float, a[i]), (double)__builtin_bit_cast(float, b[i]), s);
+        const f32x4 fa = __builtin_bit_cast(f32x4, a), fb = __builtin_bit_cast(f32x4, b);
+        s0 = __builtin_fma((double)fa[0], (double)fb[0], s0);
+        s1 = __builtin_fma((double)fa[1], (double)fb[1], s1);
+        s0 = __builtin_fma((double)fa[2], (double)fb[2], s0);
+        s1 = __builtin_fma((double)fa[3], (double)fb[3], s1);
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int hlf = 0; hlf < 2; ++hlf) {
-                const uint16_t ua = (uint16_t)((uint32_t)a[i] >> (16 * hlf));
-                const uint16_t ub = (uint16_t)((uint32_t)b[i] >> (16 * hlf));
-                const double fa = CT::dt == DT_F16 ? (double)f16_to_f32(ua) : (double)bf16_to_f32(ua);
-                const double fb = CT::dt == DT_F16 ? (double)f16_to_f32(ub) : (double)bf16_to_f32(ub);
-                s = __builtin_fma(fa, fb, s);
-            }
+            const uint32_t ua = (uint32_t)a[i], ub = (uint32_t)b[i];
+            s0 = __builtin_fma((double)unpack_lo<CT>(ua), (double)unpack_lo<CT>(ub), s0);
+            s1 = __builtin_fma((double)unpack_hi<CT>(ua), (double)unpack_hi<CT>(ub), s1);
         }
     }
-    return s;
+    return s0 + s1;
 }
 
 template <class CT>
@@ -75,44 +129,60 @@ __device__ __forceinline__ uint16_t round16(double v) {
     return CT::dt == DT_F16 ? f64_to_f16(v) : f64_to_bf16(v);
 }
 
-template <class CT, int JB>
-__global__ __launch_bounds__(256) void hpass_kernel(HpassParams p) {
-    constexpr int RP = JB * 16;           // padded rank
-    constexpr int DCH = RP * 8 / 256;     // 16-byte chunks of the down tile per thread
-    __shared__ __attribute__((aligned(16))) char sd[2][RP * 128];
+template <class CT, int JB, int KS>
+__global__ __launch_bounds__(256) void xr_kernel(XrParams p) {
+    constexpr bool SPLIT = CT::dt != DT_F32;     // 16-bit compute: hi/lo split and guard
+    constexpr int NB = SPLIT ? 2 : 1;            // B arrays staged per k block (hi, lo)
+    constexpr int RW = 4 / KS;                   // row groups
+    constexpr int RP = JB * 16;                  // columns per workgroup
+    constexpr int TILE = RP * 128;               // bytes of one B tile (RP rows x 128 B)
+    constexpr int BCH = KS * NB * RP * 8 / 256;  // 16-byte chunks per thread per round
+    static_assert((KS * NB * RP * 8) % 256 == 0, "loader split");
+    __shared__ __attribute__((aligned(16))) char sd[2][KS * NB * TILE];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t wg_m0 = (int64_t)blockIdx.x * 64;
-    const int rows_wg = (int)((p.M - wg_m0) < 64 ? (p.M - wg_m0) : 64);
+    const int rg = wave % RW, kg = wave / RW;
+    const int64_t wg_m0 = (int64_t)blockIdx.x * (RW * 16);
+    const int64_t j0 = (int64_t)blockIdx.y * RP;
+    const int rows_wg = (int)((p.M - wg_m0) < RW * 16 ? (p.M - wg_m0) : RW * 16);
+    const int cols_wg = (int)((p.Nc - j0) < RP ? (p.Nc - j0) : RP);
     const uint32_t kbytes = (uint32_t)(p.K * CT::es);
-    const int my_row = wave * 16 + (lane & 15);   // row within the workgroup
+    const int my_row = rg * 16 + (lane & 15);   // row within the workgroup
     const auto rsx = make_rsrc((const char*)p.x + wg_m0 * kbytes, (uint32_t)rows_wg * kbytes);
-    const auto rsd = make_rsrc(p.d, (uint32_t)RP * kbytes);
+    const auto rsh = make_rsrc((const char*)p.b + j0 * kbytes, (uint32_t)cols_wg * kbytes);
+    const auto rsl = make_rsrc((const char*)(SPLIT ? p.b_lo : p.b) + j0 * kbytes, (uint32_t)cols_wg * kbytes);
 
     double acc[JB][4];
 #pragma unroll
     for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[jb][e] = 0.0;
-    float sq = 0.f;
+    double xm2 = 0.0, xl2 = 0.0;   // sums over blocks of 64*max|x|^2 and of 16*4^g (bounds on |x|^2, |x_lo|^2)
 
-    const int KT = (int)((kbytes + 127) / 128);
-    i32x4 dr[DCH], xr[2], xn[2];
-    auto load_d = [&](uint32_t kb0) {
+    const int KT = (int)((kbytes + 127) / 128);   // k blocks of 128 bytes
+    const int ROUNDS = (KT + KS - 1) / KS;
+    i32x4 br[BCH], xr[2], xn[2];
+    // round r stages blocks r*KS .. r*KS+KS-1: tile (g, a) = block r*KS+g of array a
+    auto load_b = [&](int r) {
 #pragma unroll
-        for (int i = 0; i < DCH; ++i) {
+        for (int i = 0; i < BCH; ++i) {
             const int c = tid + i * 256;
-            const uint32_t kb = kb0 + ((c & 7) << 4);
-            dr[i] = buf_load16(rsd, kb < kbytes ? (uint32_t)(c >> 3) * kbytes + kb : OOB);
+            const int t = c / (RP * 8), w = c % (RP * 8);
+            const int g = t / NB, a = t % NB;
+            const uint32_t kb = (uint32_t)(r * KS + g) * 128 + ((w & 7) << 4);
+            const uint32_t off = kb < kbytes ? (uint32_t)(w >> 3) * kbytes + kb : OOB;
+            br[i] = buf_load16(a ? rsl : rsh, off);
         }
     };
-    auto store_d = [&](char* dst) {
+    auto store_b = [&](char* dst) {
 #pragma unroll
-        for (int i = 0; i < DCH; ++i) {
+        for (int i = 0; i < BCH; ++i) {
             const int c = tid + i * 256;
-            *(i32x4*)(dst + lds_off(c >> 3, c & 7)) = dr[i];
+            const int t = c / (RP * 8), w = c % (RP * 8);
+            *(i32x4*)(dst + t * TILE + lds_off(w >> 3, w & 7)) = br[i];
         }
     };
-    auto load_x = [&](i32x4 (&dst)[2], uint32_t kb0) {
+    auto load_x = [&](i32x4 (&dst)[2], int r) {
+        const uint32_t kb0 = (uint32_t)(r * KS + kg) * 128;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const uint32_t kb = kb0 + (uint32_t)((s * 4 + (lane >> 4)) << 4);
@@ -120,68 +190,147 @@ __global__ __launch_bounds__(256) void hpass_kernel(HpassParams p) {
         }
     };
 
-    if (KT > 0) {
-        load_d(0);
+    bool wide = false;   // a block beyond the split's exponent range: re-evaluate the row
+    if (ROUNDS > 0) {
+        load_b(0);
         load_x(xr, 0);
-        store_d(sd[0]);
+        store_b(sd[0]);
         __syncthreads();
     }
-    for (int kt = 0; kt < KT; ++kt) {
-        const char* cur = sd[kt & 1];
-        const bool more = kt + 1 < KT;
+    for (int r = 0; r < ROUNDS; ++r) {
+        const char* cur = sd[r & 1];
+        const bool more = r + 1 < ROUNDS;
         if (more) {
-            load_d((uint32_t)(kt + 1) * 128);
-            load_x(xn, (uint32_t)(kt + 1) * 128);
+            load_b(r + 1);
+            load_x(xn, r + 1);
         }
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            sq += sumsq16<CT>(xr[s]);
-            const int kc = s * 4 + (lane >> 4);
+        const char* th = cur + (kg * NB) * TILE;    // this k group's b_hi (or b) tile
+        if (SPLIT) {
+            // block maximum of |x| for the lane's row (4 lane groups x 16 values)
+            uint32_t mb = absmax_bits(xr[0]);
+            const uint32_t m1 = absmax_bits(xr[1]);
+            mb = mb > m1 ? mb : m1;
+            const uint32_t o1 = (uint32_t)__shfl_xor((int)mb, 16);
+            mb = mb > o1 ? mb : o1;
+            const uint32_t o2 = (uint32_t)__shfl_xor((int)mb, 32);
+            mb = mb > o2 ? mb : o2;
+            const int g = grid_exp<CT>(mb);
+            wide |= (g > 100);
+            const float magic = __builtin_ldexpf(1.5f, (g > 100 ? 100 : g) + 23);
+            if (mb) {
+                const double mv = (double)unpack_lo<CT>(mb);
+                xm2 = __builtin_fma(64.0 * mv, mv, xm2);        // 64 values, each |x| <= max
+                xl2 += __builtin_ldexp(16.0, 2 * g);            // 64 values, each |x_lo| <= 2^(g-1)
+            }
+            i32x4 xh[2], xlo[2];
+            split16<CT>(xr[0], magic, xh[0], xlo[0]);
+            split16<CT>(xr[1], magic, xh[1], xlo[1]);
+            const char* tl = th + TILE;             // this k group's b_lo tile
 #pragma unroll
             for (int jb = 0; jb < JB; ++jb) {
-                const i32x4 df = *(const i32x4*)(cur + lds_off(jb * 16 + (lane & 15), kc));
-                const f32x4 c = CT::step(df, xr[s], f32x4{0.f, 0.f, 0.f, 0.f});
+                const int row = jb * 16 + (lane & 15);
+                f32x4 hh = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[jb][e] += (double)c[e];
+                for (int s = 0; s < 2; ++s) {
+                    const int kc = s * 4 + (lane >> 4);
+                    const i32x4 bh = *(const i32x4*)(th + lds_off(row, kc));
+                    const i32x4 bl = *(const i32x4*)(tl + lds_off(row, kc));
+                    hh = CT::step(bh, xh[s], hh);                                   // exact
+                    f32x4 cx = CT::step(bl, xr[s], f32x4{0.f, 0.f, 0.f, 0.f});      // cross chain
+                    cx = CT::step(bh, xlo[s], cx);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[jb][e] += (double)cx[e];
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[jb][e] += (double)hh[e];
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int kc = s * 4 + (lane >> 4);
+#pragma unroll
+                for (int jb = 0; jb < JB; ++jb) {
+                    const i32x4 bf = *(const i32x4*)(th + lds_off(jb * 16 + (lane & 15), kc));
+                    const f32x4 c = CT::step(bf, xr[s], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[jb][e] += (double)c[e];
+                }
             }
         }
         if (more) {
-            store_d(sd[(kt + 1) & 1]);
+            store_b(sd[(r + 1) & 1]);
             xr[0] = xn[0];
             xr[1] = xn[1];
         }
         __syncthreads();
     }
 
-    // |x_m|^2 for this lane's row: the four lane groups hold disjoint k ranges
-    sq += __shfl_xor(sq, 16);
-    sq += __shfl_xor(sq, 32);
+    // meet the k groups' partial sums in LDS (the B tiles are no longer needed);
+    // the row bounds are already identical across the lane groups of a row
+    if (KS > 1) {
+        constexpr int W = JB * 4 + 3;
+        static_assert((KS - 1) * RW * 64 * W * 8 <= 2 * KS * NB * TILE, "reduction buffer");
+        double* red = (double*)&sd[0][0];          // [KS-1][RW][64 lanes][W]
+        if (kg > 0) {
+            double* dst = red + ((size_t)((kg - 1) * RW + rg) * 64 + lane) * W;
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[jb * 4 + e] = acc[jb][e];
+            dst[JB * 4] = xm2;
+            dst[JB * 4 + 1] = xl2;
+            dst[JB * 4 + 2] = wide ? 1.0 : 0.0;
+        }
+        __syncthreads();
+        if (kg > 0) return;
+        for (int g2 = 1; g2 < KS; ++g2) {
+            const double* src = red + ((size_t)((g2 - 1) * RW + rg) * 64 + lane) * W;
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[jb][e] += src[jb * 4 + e];
+            xm2 += src[JB * 4];
+            xl2 += src[JB * 4 + 1];
+            wide |= src[JB * 4 + 2] != 0.0;
+        }
+    }
     const int64_t m = wg_m0 + my_row;
     const bool row_ok = m < p.M;
 
-    if (CT::dt != DT_F32) {
-        // guard: flag elements whose error interval straddles a rounding boundary
-        const double xnorm = (double)__builtin_sqrtf(sq) * (1.0 + 0x1p-8);
+    if (SPLIT && p.guard) {
+        const double xn2 = __builtin_sqrt(xm2) * (1.0 + 0x1p-20);
+        const double xln = __builtin_sqrt(xl2) * (1.0 + 0x1p-20);
         unsigned nflag = 0;
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int j = jb * 16 + 4 * (lane >> 4) + e;
-                const double E = (p.guard * 0x1p-24 + 0x1p-37) * xnorm * p.dnorm[j] * (1.0 + 0x1p-20);
+                const int jl = jb * 16 + 4 * (lane >> 4) + e;
+                const bool col_ok = jl < cols_wg;
+                const double2 bn = col_ok ? p.bnorm[j0 + jl] : double2{0.0, 0.0};  // {|b|, |b_lo|}
+                const double E = (0x1p-24 * GUARD_CROSS * (xn2 * bn.y + xln * (bn.x + bn.y)) + 0x1p-37 * xn2 * bn.x) *
+                                 (1.0 + 0x1p-20);
                 const double h = acc[jb][e];
-                const bool flag = row_ok && round16<CT>(h - E) != round16<CT>(h + E);
+                const bool bwide = !(bn.y < 1e300);   // a block of b could not be split
+                const bool flag = row_ok && col_ok && (wide || bwide || round16<CT>(h - E) != round16<CT>(h + E));
                 uint64_t mask = __ballot(flag);
                 nflag += (unsigned)__builtin_popcountll(mask);
                 while (mask) {
                     const int L = __builtin_ctzll(mask);
                     mask &= mask - 1;
-                    const int64_t mL = wg_m0 + wave * 16 + (L & 15);
-                    const int jL = jb * 16 + 4 * (L >> 4) + e;
+                    const int64_t mL = wg_m0 + rg * 16 + (L & 15);
+                    const int64_t jL = j0 + jb * 16 + 4 * (L >> 4) + e;
                     const i32x4* xrow = (const i32x4*)((const char*)p.x + mL * kbytes);
-                    const i32x4* drow = (const i32x4*)((const char*)p.d + (int64_t)jL * kbytes);
-                    double part = 0.0;
-                    for (uint32_t c = lane; c < kbytes / 16; c += 64) part += dot16_f64<CT>(xrow[c], drow[c]);
+                    const i32x4* brow = (const i32x4*)((const char*)p.b_full + jL * kbytes);
+                    const uint32_t nch = kbytes / 16;
+                    double p0 = 0.0, p1 = 0.0;
+                    uint32_t c = lane;
+                    for (; c + 64 < nch; c += 128) {
+                        p0 += dot16_f64<CT>(xrow[c], brow[c]);
+                        p1 += dot16_f64<CT>(xrow[c + 64], brow[c + 64]);
+                    }
+                    if (c < nch) p0 += dot16_f64<CT>(xrow[c], brow[c]);
+                    double part = p0 + p1;
 #pragma unroll
                     for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
                     if (lane == L) acc[jb][e] = part;
@@ -191,41 +340,109 @@ __global__ __launch_bounds__(256) void hpass_kernel(HpassParams p) {
         if (lane == 0 && nflag) atomicAdd(p.flagged, nflag);
     }
 
-    if (row_ok) {
+    if (!row_ok) return;
+    if (p.mode == XR_H) {
+        // h_r [M][ld_out] in the compute dtype (all RP columns, padding included)
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) {
-            const int j0 = jb * 16 + 4 * (lane >> 4);
+            const int64_t jg = j0 + jb * 16 + 4 * (lane >> 4);
             if (CT::dt == DT_F32) {
-                float* hp = (float*)p.h + m * p.r_pad + j0;
+                float* hp = (float*)p.out + m * p.ld_out + jg;
                 *(f32x4*)hp = f32x4{(float)acc[jb][0], (float)acc[jb][1], (float)acc[jb][2], (float)acc[jb][3]};
             } else {
                 uint16_t o[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o[e] = round16<CT>(acc[jb][e]);
-                uint16_t* hp = (uint16_t*)p.h + m * p.r_pad + j0;
+                uint16_t* hp = (uint16_t*)p.out + m * p.ld_out + jg;
                 *(i32x2*)hp = i32x2{(int)(o[0] | ((uint32_t)o[1] << 16)), (int)(o[2] | ((uint32_t)o[3] << 16))};
+            }
+        }
+        return;
+    }
+    // plain affine: y = round_out(round_out(p) + b)
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) {
+        const int jl0 = jb * 16 + 4 * (lane >> 4);
+        const int64_t n0 = j0 + jl0;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float pr;
+            if (p.out_dt == DT_F32) pr = (float)acc[jb][e];                     // one rounding, fp64 -> fp32
+            else if (CT::dt == DT_F16) pr = f16_to_f32(round16<CT>(acc[jb][e]));
+            else pr = bf16_to_f32(round16<CT>(acc[jb][e]));
+            const float bias = (p.bias != nullptr && jl0 + e < cols_wg) ? load_as_f32(p.bias, p.bias_dt, n0 + e) : 0.f;
+            v[e] = pr + bias;
+        }
+        const int64_t base = m * p.ld_out + n0;
+        if (p.out_dt == DT_F32) {
+            float* y = (float*)p.out;
+            if (p.vec_store && jl0 + 3 < cols_wg) {
+                *(f32x4*)(y + base) = f32x4{v[0], v[1], v[2], v[3]};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (jl0 + e < cols_wg) y[base + e] = v[e];
+            }
+        } else {
+            uint16_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = p.out_dt == DT_F16 ? f32_to_f16(v[e]) : f32_to_bf16(v[e]);
+            uint16_t* y = (uint16_t*)p.out;
+            if (p.vec_store && jl0 + 3 < cols_wg) {
+                *(i32x2*)(y + base) = i32x2{(int)(o[0] | ((uint32_t)o[1] << 16)), (int)(o[2] | ((uint32_t)o[3] << 16))};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (jl0 + e < cols_wg) y[base + e] = o[e];
             }
         }
     }
 }
 
-template <class CT>
-static hipError_t run_h(const HpassParams& p, hipStream_t s) {
-    const dim3 grid((unsigned)((p.M + 63) / 64));
-    switch (p.r_pad) {
-    case 32: hipLaunchKernelGGL((hpass_kernel<CT, 2>), grid, dim3(256), 0, s, p); break;
-    case 64: hipLaunchKernelGGL((hpass_kernel<CT, 4>), grid, dim3(256), 0, s, p); break;
-    case 128: hipLaunchKernelGGL((hpass_kernel<CT, 8>), grid, dim3(256), 0, s, p); break;
-    case 256: hipLaunchKernelGGL((hpass_kernel<CT, 16>), grid, dim3(256), 0, s, p); break;
-    default: return hipErrorInvalidValue;
-    }
+template <class CT, int JB, int KS>
+static hipError_t run_xr(const XrParams& p, hipStream_t s) {
+    constexpr int RP = JB * 16, RW = 4 / KS;
+    const dim3 grid((unsigned)((p.M + RW * 16 - 1) / (RW * 16)), (unsigned)((p.Nc + RP - 1) / RP));
+    hipLaunchKernelGGL((xr_kernel<CT, JB, KS>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
-hipError_t launch_hpass(int c_dt, const HpassParams& p, hipStream_t s) {
-    if (c_dt == DT_F16) return run_h<CF16>(p, s);
-    if (c_dt == DT_BF16) return run_h<CBF16>(p, s);
-    return run_h<CF32>(p, s);
+// k groups: enough waves to cover the chip (about 1024 row-block waves)
+static int pick_ks(int64_t M, int64_t col_tiles) {
+    const int64_t row_blocks = (M + 15) / 16;
+    if (row_blocks * col_tiles >= 1024) return 1;
+    if (row_blocks * col_tiles * 2 >= 1024) return 2;
+    return 4;
+}
+
+// JB (column blocks) bounds the k groups through LDS: two stages of KS*2 tiles
+// of JB*2 KiB must fit in 160 KiB.
+template <class CT, int JB, int KSMAX>
+static hipError_t run_xr_jb(const XrParams& p, hipStream_t s) {
+    const int64_t col_tiles = (p.Nc + JB * 16 - 1) / (JB * 16);
+    const int ks = pick_ks(p.M, col_tiles);
+    if (ks == 1 || KSMAX == 1) return run_xr<CT, JB, 1>(p, s);
+    if (ks == 2 || KSMAX == 2) return run_xr<CT, JB, (KSMAX >= 2 ? 2 : 1)>(p, s);
+    return run_xr<CT, JB, (KSMAX >= 4 ? 4 : 1)>(p, s);
+}
+
+template <class CT>
+static hipError_t run_xr_ct(const XrParams& p, hipStream_t s) {
+    if (p.mode == XR_AFFINE) return run_xr_jb<CT, 4, 4>(p, s);
+    switch (p.Nc) {
+    case 32: return run_xr_jb<CT, 2, 4>(p, s);
+    case 64: return run_xr_jb<CT, 4, 4>(p, s);
+    case 128: return run_xr_jb<CT, 8, 2>(p, s);
+    case 256: return run_xr<CT, 16, 1>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_xr(int c_dt, const XrParams& p, hipStream_t s) {
+    if (c_dt == DT_F16) return run_xr_ct<CF16>(p, s);
+    if (c_dt == DT_BF16) return run_xr_ct<CBF16>(p, s);
+    return run_xr_ct<CF32>(p, s);
 }
 
 }  // namespace lyc

@@ -21,32 +21,44 @@ struct GemmParams {
     int bias_dt;
     void* y;
     int y_dt;
-    int double_round;  // 1: y = round(round(acc) + b)  (plain affine contract)
     int vec_store;     // 1: y rows allow 4-element vector stores
 };
 
-// h_r = round_c(x_c . d_c^T), the guard and its fp64 re-evaluation.
-struct HpassParams {
-    const void* x;        // [M,K] compute dtype
-    const void* d;        // [r_pad,K] compute dtype (rows >= rank are zero)
-    const double* dnorm;  // [r_pad] Euclidean norms of the rows of d
-    void* h;              // [M,r_pad] compute dtype
-    int64_t M, K;
-    int r_pad;
-    double guard;         // error bound factor (units of 2^-24 * |x_m| * |d_j|)
-    unsigned* flagged;    // count of re-evaluated elements
+// Exact-rounding contraction (h pass and plain affine projection):
+// C = x_c . b^T with fp64-folded MFMA steps, a rounding guard and fp64
+// re-evaluation, then either h_r = round_c(C) or y = round_out(round_out(C) + b).
+enum { XR_H = 0, XR_AFFINE = 1 };
+struct XrParams {
+    const void* x;          // [M,K] compute dtype
+    const void* b;          // [Nc,K] compute dtype: b_hi (16-bit compute) or b itself (fp32)
+    const void* b_lo;       // [Nc,K] b - b_hi (16-bit compute)
+    const void* b_full;     // [Nc,K] b (down_c or W_c), for the fp64 re-evaluation
+    const double2* bnorm;   // [Nc] {|b_j|_2, |b_lo,j|_2}
+    int64_t M, Nc, K;
+    int guard;              // 1: apply the rounding guard (16-bit rounding target)
+    unsigned* flagged;      // count of re-evaluated elements
+    int mode;               // XR_H or XR_AFFINE
+    void* out;              // h [M][ld_out] (compute dtype) or y [M][ld_out] (out_dt)
+    int64_t ld_out;
+    int out_dt;             // XR_AFFINE
+    const void* bias;       // XR_AFFINE, nullptr: none
+    int bias_dt;
+    int vec_store;          // XR_AFFINE: rows allow 4-element vector stores
 };
 
-// Compute-dtype copies of down [rank,K] -> [r_pad,K] (+ row norms) and
-// up [N,rank] -> [N,r_pad]; zero padding; clears *flagged.
+// Compute-dtype copies of down [rank,K] -> [r_pad,K] (+ its hi/lo split per
+// 64-k block and row norms) and up [N,rank] -> [N,r_pad]; zero padding;
+// clears *flagged.
 struct PrepParams {
     const void* down;
     int down_dt;
     const void* up;
     int up_dt;
     void* dc;
+    void* dh;   // hi part of down_c (16-bit compute), else unused
+    void* dl;   // lo part
     void* uc;
-    double* dnorm;
+    double2* dnorm;   // {|down_c,j|, |lo_j|}
     unsigned* flagged;
     int64_t N, K, rank;
     int r_pad;
@@ -56,7 +68,11 @@ struct PrepParams {
 hipError_t launch_gemm(int c_dt, const GemmParams& p, hipStream_t s);
 // the output tile launch_gemm uses for this shape
 void gemm_tile_shape(int64_t M, int64_t N, int c_dt, int* tn, int* tm);
-hipError_t launch_hpass(int c_dt, const HpassParams& p, hipStream_t s);
+hipError_t launch_xr(int c_dt, const XrParams& p, hipStream_t s);
+// hi/lo split (per 64-k block) of each row of b [rows,K] (16-bit compute
+// dtype) and {|b_j|_2, |b_lo,j|_2}; also clears *flagged (if not null)
+hipError_t launch_rownorm(const void* b, int c_dt, int64_t rows, int64_t K, void* b_hi, void* b_lo, double2* out,
+                          unsigned* flagged, hipStream_t s);
 hipError_t launch_prep(const PrepParams& p, hipStream_t s);
 // fp32 [n] -> 16-bit compute dtype [n], round to nearest even
 hipError_t launch_cast(const float* src, void* dst, int64_t n, int c_dt, hipStream_t s);

@@ -27,27 +27,83 @@ __device__ __forceinline__ void store_c(void* dst, int64_t i, float v, int c_dt,
     }
 }
 
-// blocks [0, r_pad): one row of down each (+ its norm); the rest: up, grid-stride
+// floor(log2 v) of a positive finite fp32 value (subnormals included)
+__device__ __forceinline__ int floor_log2(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const int E = (int)(u >> 23);
+    return E > 0 ? E - 127 : (31 - __builtin_clz(u)) - 149;
+}
+
+__device__ __forceinline__ void store16(void* dst, int64_t i, float v, int c_dt) {
+    ((uint16_t*)dst)[i] = c_dt == DT_F16 ? f32_to_f16(v) : f32_to_bf16(v);
+}
+
+// One row of a [rows, K] operand per workgroup (256 threads; wave w of an
+// iteration holds one aligned 64-k block).  Optionally writes the row's
+// compute-dtype copy; for 16-bit compute also its split v = hi + lo per 64-k
+// block (hi = v rounded to the grid 2^(e-7), e = floor(log2 max|v|) of the
+// block, the same split the contraction applies to x); returns {|v|_2, |lo|_2}.
+// A block whose grid exponent exceeds 100 cannot be split with the fp32
+// rounding constant: |lo|_2 is then reported as +inf, which makes the
+// contraction re-evaluate that row's elements in fp64.
+__device__ void row_pass(const void* src, int src_dt, int c_dt, int64_t row, int64_t K, bool zero, void* dst,
+                         void* dst_hi, void* dst_lo, double2* norm_out) {
+    __shared__ double red[2][256];
+    const int tid = threadIdx.x;
+    double ss = 0.0, ll = 0.0;
+    bool wide = false;
+    for (int64_t k0 = 0; k0 < K; k0 += 256) {
+        const int64_t k = k0 + tid;
+        float c = 0.f;
+        if (k < K) {
+            const float v = zero ? 0.f : load_as_f32(src, src_dt, row * K + k);
+            double cd;
+            if (dst) store_c(dst, row * K + k, v, c_dt, &cd);
+            else cd = (double)v;
+            c = (float)cd;   // compute-dtype value, exact in fp32
+        }
+        ss = __builtin_fma((double)c, (double)c, ss);
+        if (dst_hi) {
+            float mx = __builtin_fabsf(c);
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, o));
+            float hi = 0.f, lo = 0.f;
+            if (mx > 0.f) {
+                const int g = floor_log2(mx) - 7;
+                wide |= g > 100;
+                const float magic = __builtin_ldexpf(1.5f, (g > 100 ? 100 : g) + 23);
+                hi = (c + magic) - magic;
+                lo = c - hi;
+            }
+            if (k < K) {
+                store16(dst_hi, row * K + k, hi, c_dt);
+                store16(dst_lo, row * K + k, lo, c_dt);
+            }
+            ll = __builtin_fma((double)lo, (double)lo, ll);
+        }
+    }
+    red[0][tid] = ss;
+    red[1][tid] = ll + (wide ? __builtin_inf() : 0.0);
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (tid < o) {
+            red[0][tid] += red[0][tid + o];
+            red[1][tid] += red[1][tid + o];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) *norm_out = double2{__builtin_sqrt(red[0][0]), __builtin_sqrt(red[1][0])};
+}
+
+// blocks [0, r_pad): one row of down each (+ its split and norms); the rest:
+// up, grid-stride
 __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
-    __shared__ double red[256];
     const int b = blockIdx.x, tid = threadIdx.x;
     if (b == 0 && tid == 0) *p.flagged = 0u;
     if (b < p.r_pad) {
-        const int j = b;
-        double ss = 0.0;
-        for (int64_t k = tid; k < p.K; k += 256) {
-            const float v = j < p.rank ? load_as_f32(p.down, p.down_dt, (int64_t)j * p.K + k) : 0.f;
-            double c;
-            store_c(p.dc, (int64_t)j * p.K + k, v, p.c_dt, &c);
-            ss = __builtin_fma(c, c, ss);
-        }
-        red[tid] = ss;
-        __syncthreads();
-        for (int o = 128; o > 0; o >>= 1) {
-            if (tid < o) red[tid] += red[tid + o];
-            __syncthreads();
-        }
-        if (tid == 0) p.dnorm[j] = __builtin_sqrt(red[0]);
+        const bool split = p.c_dt != DT_F32;
+        row_pass(p.down, p.down_dt, p.c_dt, b, p.K, b >= p.rank, p.dc, split ? p.dh : nullptr,
+                 split ? p.dl : nullptr, &p.dnorm[b]);
     } else {
         const int64_t total = p.N * (int64_t)p.r_pad;
         const int64_t stride = (int64_t)(gridDim.x - p.r_pad) * 256;
@@ -59,6 +115,20 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
             store_c(p.uc, i, v, p.c_dt, &c);
         }
     }
+}
+
+// split and norms of the rows of an operand already in the 16-bit compute
+// dtype; clears *flagged
+__global__ __launch_bounds__(256) void rownorm_kernel(const void* b, int c_dt, int64_t K, void* b_hi, void* b_lo,
+                                                      double2* out, unsigned* flagged) {
+    if (blockIdx.x == 0 && threadIdx.x == 0 && flagged) *flagged = 0u;
+    row_pass(b, c_dt, c_dt, blockIdx.x, K, false, nullptr, b_hi, b_lo, &out[blockIdx.x]);
+}
+
+hipError_t launch_rownorm(const void* b, int c_dt, int64_t rows, int64_t K, void* b_hi, void* b_lo, double2* out,
+                          unsigned* flagged, hipStream_t s) {
+    hipLaunchKernelGGL(rownorm_kernel, dim3((unsigned)rows), dim3(256), 0, s, b, c_dt, K, b_hi, b_lo, out, flagged);
+    return hipGetLastError();
 }
 
 hipError_t launch_prep(const PrepParams& p, hipStream_t s) {

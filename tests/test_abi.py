@@ -60,20 +60,28 @@ def test_policy_matches_oracle_on_every_tuple():
                 assert L.resolve_dtypes(list(tup)) == (c, o), tup
 
 
-def _lin(**kw):
+# The pointers below are fake: every call must be refused by the argument
+# checks (or be an empty no-op) so that nothing is ever launched with them.
+def _refused(st, allow_ok=False):
+    assert st != L.ERR_HIP and (allow_ok or st != L.OK), f"call was not refused before launching (status {st})"
+    return st
+
+
+def _lin(allow_ok=False, **kw):
     a = dict(x=P, x_dt=1, w=P, w_dt=1, b=None, b_dt=0, y=P, y_dt=1, M=4, N=4, K=8, ws=None, nws=0, s=None)
     a.update(kw)
-    return L.lib().lyc_linear_fwd(a["x"], a["x_dt"], a["w"], a["w_dt"], a["b"], a["b_dt"], a["y"], a["y_dt"],
-                                  a["M"], a["N"], a["K"], a["ws"], a["nws"], a["s"])
+    return _refused(L.lib().lyc_linear_fwd(a["x"], a["x_dt"], a["w"], a["w_dt"], a["b"], a["b_dt"], a["y"],
+                                           a["y_dt"], a["M"], a["N"], a["K"], a["ws"], a["nws"], a["s"]), allow_ok)
 
 
-def _lora(**kw):
+def _lora(allow_ok=False, **kw):
     a = dict(x=P, x_dt=1, w=P, w_dt=1, b=None, b_dt=0, d=P, d_dt=1, u=P, u_dt=1, r=4, scale=1.0, y=P, y_dt=1,
-             M=4, N=4, K=8, ws=P, nws=1 << 20, s=None)
+             M=4, N=4, K=8, ws=None, nws=0, s=None)
     a.update(kw)
-    return L.lib().lyc_lora_linear_fwd(a["x"], a["x_dt"], a["w"], a["w_dt"], a["b"], a["b_dt"], a["d"], a["d_dt"],
-                                       a["u"], a["u_dt"], a["r"], ctypes.c_double(a["scale"]), a["y"], a["y_dt"],
-                                       a["M"], a["N"], a["K"], a["ws"], a["nws"], a["s"])
+    return _refused(L.lib().lyc_lora_linear_fwd(a["x"], a["x_dt"], a["w"], a["w_dt"], a["b"], a["b_dt"], a["d"],
+                                                a["d_dt"], a["u"], a["u_dt"], a["r"], ctypes.c_double(a["scale"]),
+                                                a["y"], a["y_dt"], a["M"], a["N"], a["K"], a["ws"], a["nws"], a["s"]),
+                    allow_ok)
 
 
 def test_linear_argument_errors():
@@ -92,16 +100,17 @@ def test_linear_argument_errors():
     # an fp16 bias counts as a 16-bit operand: compute fp16 (fp32 x and W need fp16 copies), output fp32
     assert _lin(x_dt=3, w_dt=3, y_dt=1, b=P, b_dt=1) == L.ERR_DTYPE_MISMATCH
     assert _lin(x_dt=3, w_dt=3, y_dt=3, b=P, b_dt=1) == L.ERR_WORKSPACE
-    # fp32 W under fp16 compute needs a workspace for its fp16 copy
+    # the projection guard (and fp16 copies of fp32 operands) need a workspace
+    assert _lin() == L.ERR_WORKSPACE
     assert _lin(w_dt=3, y_dt=3) == L.ERR_WORKSPACE
     assert _lin(w_dt=3, y_dt=3, ws=V(4100), nws=1 << 20) == L.ERR_WORKSPACE   # not 256-aligned
 
 
 def test_empty_calls_are_noops():
     # nothing is launched for an empty output, so null data pointers are fine
-    assert _lin(M=0, x=None, y=None) == L.OK
-    assert _lin(N=0, w=None, y=None) == L.OK
-    assert _lora(M=0, x=None, y=None, ws=None, nws=0) == L.OK
+    assert _lin(M=0, x=None, y=None, allow_ok=True) == L.OK
+    assert _lin(N=0, w=None, y=None, allow_ok=True) == L.OK
+    assert _lora(M=0, x=None, y=None, allow_ok=True) == L.OK
 
 
 def test_lora_argument_errors():
@@ -110,8 +119,8 @@ def test_lora_argument_errors():
     assert _lora(r=-1) == L.ERR_INVALID_ARG
     assert _lora(u=None) == L.ERR_INVALID_ARG
     assert _lora(d=None) == L.ERR_INVALID_ARG
-    assert _lora(ws=None, nws=0) == L.ERR_WORKSPACE
-    assert _lora(nws=16) == L.ERR_WORKSPACE
+    assert _lora() == L.ERR_WORKSPACE
+    assert _lora(ws=P, nws=16) == L.ERR_WORKSPACE
     assert _lora(scale=float("nan")) == L.ERR_INVALID_ARG
     assert _lora(scale=float("inf")) == L.ERR_INVALID_ARG
     assert _lora(y_dt=2) == L.ERR_DTYPE_MISMATCH               # y is not a policy operand: bf16 y for fp16 operands
@@ -124,8 +133,9 @@ def test_workspace_sizes():
     assert n16 >= 1000 * 32 * 2 + 32 * 64 * 2 + 300 * 32 * 2 + 32 * 8
     ho, ld, fo = L.lora_workspace_layout(1000, 300, 64, 17, 1, 1, 0, 1, 1)
     assert ld == 32 and ho % 256 == 0 and fo % 256 == 0 and fo < n16
-    assert L.linear_workspace_size(64, 64, 64, 1, 1) == 0
-    assert L.linear_workspace_size(64, 32, 64, 2, 3) >= 32 * 64 * 2     # bf16 copy of an fp32 W
+    # affine: row norms of W for the projection guard (+ a bf16 copy of an fp32 W)
+    assert L.linear_workspace_size(64, 64, 64, 1, 1) >= 64 * 16
+    assert L.linear_workspace_size(64, 32, 64, 2, 3) >= 32 * 64 * 2 + 32 * 16
     assert L.lora_workspace_size(8, 8, 8, 0, 1, 1, 0, 1, 1) == 0        # rank 0: no bypass
     for r, pad in ((1, 32), (32, 32), (33, 64), (64, 64), (65, 128), (129, 256), (256, 256)):
         assert L.lora_workspace_layout(16, 16, 16, r, 2, 2, 0, 2, 2)[1] == pad
