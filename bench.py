@@ -100,6 +100,13 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
                 "flops_per_launch": gemm_flops, "avg_us": round(gemm_ms * 1e3, 3)}
     kernels = {k: {"launches": n, "avg_us": round(t * 1e3 / n, 3)} for k, (n, t) in prof.items() if n}
+    guard = None
+    if lora and wl.r > 0 and c_dt != L.F32:
+        _, _, fo = L.lora_workspace_layout(wl.M, wl.N, wl.K, wl.r, dts[0], dts[1],
+                                           L.dtype_code(d["b"]) if "b" in d else 0, L.dtype_code(d["down"]),
+                                           L.dtype_code(d["up"]))
+        nflag = int(ws[fo: fo + 4].cpu().view(torch.int32).item())
+        guard = {"h_reevaluated_fp64": nflag, "of": wl.M * wl.r, "fraction": round(nflag / (wl.M * wl.r), 6)}
 
     out = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
@@ -110,7 +117,7 @@ def main():
                       "bias": WL.NAME[wl.b_dt] if wl.b_dt else None, "accumulate": "f32",
                       "parallelism": "single GPU"},
            "frac_of_peak": round(tflops / peak, 4), "hbm_gbs": round(wl.bytes / (ms_per_step * 1e-3) / 1e9, 1),
-           "input_digest": WL.digest(inputs), "kernels": kernels, "roofline": roofline}
+           "input_digest": WL.digest(inputs), "kernels": kernels, "h_guard": guard, "roofline": roofline}
 
     # accuracy on sampled rows against the fp64 oracle (this is also the CPU-baseline leg)
     if not args.no_cpu_baseline:

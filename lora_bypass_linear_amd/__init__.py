@@ -145,7 +145,7 @@ def gemm_tile(M: int, N: int, compute_dt: int) -> Tuple[int, int]:
     return tn.value, tm.value
 
 
-KERNELS = ("cast", "prep", "hpass", "gemm")
+KERNELS = ("cast", "prep", "hpass", "gemm", "fix")
 
 
 def profile_begin(capacity: int) -> None:
@@ -155,10 +155,10 @@ def profile_begin(capacity: int) -> None:
 
 def profile_end():
     """Stop recording; returns {kernel: (launches, total_ms)}."""
-    t = (ctypes.c_double * 4)()
-    n = (ctypes.c_int * 4)()
+    t = (ctypes.c_double * len(KERNELS))()
+    n = (ctypes.c_int * len(KERNELS))()
     _check(lib().lyc_profile_end(t, n))
-    return {KERNELS[k]: (n[k], t[k]) for k in range(4)}
+    return {KERNELS[k]: (n[k], t[k]) for k in range(len(KERNELS))}
 
 
 def _workspace(nbytes: int, dev, workspace: Optional[torch.Tensor]) -> Optional[torch.Tensor]:

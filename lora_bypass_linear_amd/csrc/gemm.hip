@@ -19,23 +19,27 @@
 
 namespace lyc {
 
-// TN x TM output tile, WN x WM per wave (multiples of 16), K step of 128 bytes.
-template <int TN_, int TM_, int WN_, int WM_>
+// TN x TM output tile, WN x WM per wave (multiples of 16), NS pipeline stages
+// of one K step each; a K step is 64 bytes of every row (32 16-bit values).
+template <int TN_, int TM_, int WN_, int WM_, int NS_>
 struct Tile {
-    static constexpr int TN = TN_, TM = TM_, WN = WN_, WM = WM_;
+    static constexpr int TN = TN_, TM = TM_, WN = WN_, WM = WM_, NS = NS_;
     static constexpr int WAVES_N = TN / WN, WAVES_M = TM / WM;
     static constexpr int NW = WAVES_N * WAVES_M, NT = NW * 64;
     static constexpr int FN = WN / 16, FM = WM / 16;
-    static constexpr int CA = TN * 8 / NT, CB = TM * 8 / NT;  // 16-byte chunks per thread per K step
-    static constexpr int STAGE = (TN + TM) * 128;              // LDS bytes per pipeline stage
+    static constexpr int NBLK = (TN + TM) / 16;                 // 1 KiB LDS blocks (16 rows) per step
+    static constexpr int QMAX = (NBLK + NW - 1) / NW;           // loads per wave per step, at most
+    static constexpr int QMIN = NBLK / NW;                      // ... at least
+    static constexpr int STAGE = (TN + TM) * 64;                // LDS bytes per stage
     static_assert(TN % WN == 0 && TM % WM == 0 && WN % 16 == 0 && WM % 16 == 0, "tile shape");
-    static_assert((TN * 8) % NT == 0 && (TM * 8) % NT == 0, "loader split");
+    static_assert(TN % 16 == 0 && TM % 16 == 0 && QMIN >= 1, "loader split");
+    static_assert(NS * STAGE <= 160 * 1024, "LDS");
 };
 
-using TileL = Tile<256, 256, 128, 64>;  // 8 waves
-using TileG = Tile<192, 256, 96, 64>;   // 8 waves
-using TileM = Tile<128, 128, 64, 64>;   // 4 waves
-using TileS = Tile<64, 64, 32, 32>;     // 4 waves
+using TileL = Tile<256, 256, 128, 64, 4>;  // 8 waves, 128 KiB
+using TileG = Tile<192, 256, 96, 64, 5>;   // 8 waves, 140 KiB
+using TileM = Tile<128, 128, 64, 64, 4>;   // 4 waves, 64 KiB
+using TileS = Tile<64, 64, 32, 32, 4>;     // 4 waves, 32 KiB
 
 // Workgroup id -> output tile.  Workgroups are dispatched round-robin over the
 // 8 XCDs (id % 8), each with its own L2: give every XCD a contiguous range of
@@ -55,51 +59,99 @@ __device__ __forceinline__ void tile_coords(int bid, int nblk, int tiles_n, int 
     tn = r / gsz;
 }
 
-template <int CH, int NT>
-__device__ __forceinline__ void load_chunks(i32x4 (&reg)[CH], __amdgpu_buffer_rsrc_t rs, uint32_t row_bytes,
-                                            uint32_t kb0, int tid) {
+// LDS rows are 64 bytes (4 chunks of 16); chunk kc of row r sits at slot
+// kc ^ ((r >> 1) & 3), so the 16-byte fragment reads of 8 consecutive rows
+// (two rows per 128 bytes) hit 8 different bank groups.
+__device__ __forceinline__ int lds64(int row, int kc) { return row * 64 + ((kc ^ ((row >> 1) & 3)) << 4); }
+
+// Global -> LDS without registers: one buffer_load_dwordx4 ... lds per wave
+// fills 1 KiB of LDS = 16 rows x 64 bytes of a K step.  The LDS side of such a
+// load is fixed (lane l writes bytes 16l .. 16l+15 of the KiB), so each lane
+// fetches the global chunk that belongs in that slot of the swizzled layout:
+// row 16 blk + (l >> 2), logical chunk (l & 3) ^ ((l >> 3) & 3).  The blocks of
+// the A (W-side) and B (x-side) tiles are numbered together and dealt to the
+// waves round-robin.
+template <class TL>
+struct Loader {
+    uint32_t vo[TL::QMAX];
+    __device__ __forceinline__ void init(uint32_t a_bytes, uint32_t b_bytes, int wave, int lane) {
+        const uint32_t kc16 = (uint32_t)((lane & 3) ^ ((lane >> 3) & 3)) << 4;
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-        const int c = tid + i * NT;
-        const uint32_t kb = kb0 + ((c & 7) << 4);
-        const uint32_t off = kb < row_bytes ? (uint32_t)(c >> 3) * row_bytes + kb : OOB;
-        reg[i] = buf_load16(rs, off);
+        for (int q = 0; q < TL::QMAX; ++q) {
+            const int blk = wave + q * TL::NW;
+            const bool is_a = blk < TL::TN / 16;
+            const int row = (is_a ? blk : blk - TL::TN / 16) * 16 + (lane >> 2);
+            vo[q] = (uint32_t)row * (is_a ? a_bytes : b_bytes) + kc16;
+        }
     }
+    // loads of one K step (kb0 = its first byte within a row) into an LDS stage;
+    // rows past a tile's valid rows read zeros through the buffer range check, and
+    // in the last, ragged step the chunks past K are sent out of range too
+    __device__ __forceinline__ void issue(char* stage, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                          uint32_t row_bytes, uint32_t kb0, int wave, int lane) const {
+        const bool full = kb0 + 64 <= row_bytes;
+        const uint32_t kc16 = (uint32_t)((lane & 3) ^ ((lane >> 3) & 3)) << 4;
+#pragma unroll
+        for (int q = 0; q < TL::QMAX; ++q) {
+            const int blk = wave + q * TL::NW;
+            if (q >= TL::QMIN && blk >= TL::NBLK) break;
+            uint32_t v = vo[q];
+            if (!full) v = (kb0 + kc16 < row_bytes) ? v : OOB;
+            // (an if, not ?:, on the resource: the host pass silently drops the
+            // kernel stub for a conditional over __amdgpu_buffer_rsrc_t)
+            auto* dst = (__attribute__((address_space(3))) void*)(stage + blk * 1024);
+            if (blk < TL::TN / 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, v, (int)kb0, 0, 0);
+            else __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, v, (int)kb0, 0, 0);
+        }
+    }
+};
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-template <int CH, int NT>
-__device__ __forceinline__ void store_chunks(char* lds, const i32x4 (&reg)[CH], int tid) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-        const int c = tid + i * NT;
-        *(i32x4*)(lds + lds_off(c >> 3, c & 7)) = reg[i];
-    }
+// Workgroup barrier that orders LDS only.  A __syncthreads() also waits for
+// every outstanding global load (vmcnt(0)), which defeats loads issued several
+// steps ahead; here the wave's own LDS reads are drained (lgkmcnt(0)), so a
+// stage read before the barrier may be refilled after it, and completion of
+// its own LDS-bound loads is established by an explicit wait_vm before it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// MFMAs over one 128-byte K step held in LDS (two 64-byte halves).
+__device__ __forceinline__ void publish() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+}
+
+// MFMAs over one K step (64 bytes per row) held in an LDS stage.
 template <class CT, class TL>
 __device__ __forceinline__ void mma_stage(const char* sa, const char* sb, f32x4 (&acc)[TL::FN][TL::FM], int lane,
                                           int wn, int wm) {
+    i32x4 fa[TL::FN], fb[TL::FM];
+    const int kc = lane >> 4;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        i32x4 fa[TL::FN], fb[TL::FM];
-        const int kc = s * 4 + (lane >> 4);
+    for (int i = 0; i < TL::FN; ++i) fa[i] = *(const i32x4*)(sa + lds64(wn * TL::WN + i * 16 + (lane & 15), kc));
 #pragma unroll
-        for (int i = 0; i < TL::FN; ++i) fa[i] = *(const i32x4*)(sa + lds_off(wn * TL::WN + i * 16 + (lane & 15), kc));
+    for (int j = 0; j < TL::FM; ++j) fb[j] = *(const i32x4*)(sb + lds64(wm * TL::WM + j * 16 + (lane & 15), kc));
 #pragma unroll
-        for (int j = 0; j < TL::FM; ++j) fb[j] = *(const i32x4*)(sb + lds_off(wm * TL::WM + j * 16 + (lane & 15), kc));
+    for (int i = 0; i < TL::FN; ++i)
 #pragma unroll
-        for (int i = 0; i < TL::FN; ++i)
-#pragma unroll
-            for (int j = 0; j < TL::FM; ++j) acc[i][j] = CT::step(fa[i], fb[j], acc[i][j]);
-    }
+        for (int j = 0; j < TL::FM; ++j) acc[i][j] = CT::step(fa[i], fb[j], acc[i][j]);
 }
 
 template <class CT, class TL>
 __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles_n, int tiles_m, int group_m) {
-    __shared__ __attribute__((aligned(16))) char smem[2 * TL::STAGE];
-    constexpr int NT = TL::NT, FN = TL::FN, FM = TL::FM;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ __attribute__((aligned(16))) char smem[TL::NS * TL::STAGE];
+    constexpr int FN = TL::FN, FM = TL::FM;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index in a scalar register: everything derived from it stays uniform
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    (void)tid;
     const int wn = wave % TL::WAVES_N, wm = wave / TL::WAVES_N;
     int tn, tm;
     tile_coords(blockIdx.x, gridDim.x, tiles_n, tiles_m, group_m, tn, tm);
@@ -113,22 +165,19 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
 #pragma unroll
         for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    char* const st0 = smem;
-    char* const st1 = smem + TL::STAGE;
-    i32x4 ra[TL::CA], rb[TL::CB];
+    constexpr int AOFF = TL::TN * 64;   // B tile offset within a stage
 
-    // 1. fold: acc = scale * (h_r . up_c^T)
+    // 1. fold: acc = scale * (h_r . up_c^T), one stage at a time
     if (p.rf > 0) {
         const uint32_t fb = (uint32_t)(p.rf * CT::es);
         const auto rsa = make_rsrc((const char*)p.af + n0 * fb, (uint32_t)rows_a * fb);
         const auto rsb = make_rsrc((const char*)p.bf + m0 * fb, (uint32_t)rows_b * fb);
-        for (uint32_t kb = 0; kb < fb; kb += 128) {
-            load_chunks<TL::CA, NT>(ra, rsa, fb, kb, tid);
-            load_chunks<TL::CB, NT>(rb, rsb, fb, kb, tid);
-            store_chunks<TL::CA, NT>(st0, ra, tid);
-            store_chunks<TL::CB, NT>(st0 + TL::TN * 128, rb, tid);
-            __syncthreads();
-            mma_stage<CT, TL>(st0, st0 + TL::TN * 128, acc, lane, wn, wm);
+        Loader<TL> ld;
+        ld.init(fb, fb, wave, lane);
+        for (uint32_t kb = 0; kb < fb; kb += 64) {
+            ld.issue(smem, rsa, rsb, fb, kb, wave, lane);
+            publish();
+            mma_stage<CT, TL>(smem, smem + AOFF, acc, lane, wn, wm);
             __syncthreads();
         }
 #pragma unroll
@@ -137,50 +186,30 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
             for (int j = 0; j < FM; ++j) acc[i][j] *= p.scale;
     }
 
-    // 2. main K loop: two LDS stages, and global loads issued two K steps ahead
-    //    into alternating register sets, so a load has a full compute phase of
-    //    the previous step plus its own to arrive.
+    // 2. main K loop: NS LDS stages filled straight from global memory, loads
+    //    issued NS-1 steps ahead; each step waits only for its own loads.
     const uint32_t kbytes = (uint32_t)(p.K * CT::es);
     if (kbytes > 0) {
         const auto rsa = make_rsrc((const char*)p.a + n0 * kbytes, (uint32_t)rows_a * kbytes);
         const auto rsb = make_rsrc((const char*)p.b + m0 * kbytes, (uint32_t)rows_b * kbytes);
-        const int KT = (int)((kbytes + 127) / 128);
-        i32x4 ra2[TL::CA], rb2[TL::CB];
-        load_chunks<TL::CA, NT>(ra, rsa, kbytes, 0, tid);
-        load_chunks<TL::CB, NT>(rb, rsb, kbytes, 0, tid);
-        if (KT > 1) {
-            load_chunks<TL::CA, NT>(ra2, rsa, kbytes, 128, tid);
-            load_chunks<TL::CB, NT>(rb2, rsb, kbytes, 128, tid);
-        }
-        store_chunks<TL::CA, NT>(st0, ra, tid);
-        store_chunks<TL::CB, NT>(st0 + TL::TN * 128, rb, tid);
-        __syncthreads();
-        // invariant at the top of step kt: LDS stage kt&1 holds step kt; the
-        // register set (kt+1)&1 holds (or is receiving) step kt+1
-        for (int kt = 0; kt < KT; kt += 2) {
+        const int KT = (int)((kbytes + 63) / 64);
+        Loader<TL> ld;
+        ld.init(kbytes, kbytes, wave, lane);
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int k = kt + half;
-                if (k >= KT) break;
-                char* cur = half ? st1 : st0;
-                char* nxt = half ? st0 : st1;
-                i32x4(&rn_a)[TL::CA] = half ? ra2 : ra;      // receives step k+2
-                i32x4(&rn_b)[TL::CB] = half ? rb2 : rb;
-                i32x4(&rs_a)[TL::CA] = half ? ra : ra2;      // holds step k+1
-                i32x4(&rs_b)[TL::CB] = half ? rb : rb2;
-                if (k + 2 < KT) {
-                    load_chunks<TL::CA, NT>(rn_a, rsa, kbytes, (uint32_t)(k + 2) * 128, tid);
-                    load_chunks<TL::CB, NT>(rn_b, rsb, kbytes, (uint32_t)(k + 2) * 128, tid);
-                }
-                __builtin_amdgcn_s_setprio(1);
-                mma_stage<CT, TL>(cur, cur + TL::TN * 128, acc, lane, wn, wm);
-                __builtin_amdgcn_s_setprio(0);
-                if (k + 1 < KT) {
-                    store_chunks<TL::CA, NT>(nxt, rs_a, tid);
-                    store_chunks<TL::CB, NT>(nxt + TL::TN * 128, rs_b, tid);
-                }
-                __syncthreads();
-            }
+        for (int s0 = 0; s0 < TL::NS - 1; ++s0)
+            if (s0 < KT) ld.issue((smem + s0 * TL::STAGE), rsa, rsb, kbytes, (uint32_t)s0 * 64, wave, lane);
+        for (int kt = 0; kt < KT; ++kt) {
+            // steps kt .. kt+NS-2 are in flight; step kt must have landed
+            if (kt + TL::NS - 2 < KT) wait_vm<(TL::NS - 2) * TL::QMIN>();
+            else wait_vm<0>();
+            lds_barrier();   // every wave's part of step kt is in LDS; stage of step kt-1 is free
+            if (kt + TL::NS - 1 < KT)
+                ld.issue(smem + ((kt + TL::NS - 1) % TL::NS) * TL::STAGE, rsa, rsb, kbytes, (uint32_t)(kt + TL::NS - 1) * 64, wave,
+                         lane);
+            const char* cur = smem + (kt % TL::NS) * TL::STAGE;
+            __builtin_amdgcn_s_setprio(1);
+            mma_stage<CT, TL>(cur, cur + AOFF, acc, lane, wn, wm);
+            __builtin_amdgcn_s_setprio(0);
         }
     }
 

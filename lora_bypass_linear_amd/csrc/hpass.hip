@@ -26,11 +26,12 @@
 // a step therefore errs by less than 36 * 2^-24 * S_cross, and over all steps
 // (Cauchy-Schwarz on the sums of |products|)
 //   E(m, j) = 36 * 2^-24 * (|x_m| |b_lo,j| + |x_lo,m| (|b_j| + |b_lo,j|)) + fp64 slack,
-// with |x_m| and |x_lo,m| bounded from the block maxima (64 max^2 and
-// 16 * 4^g per block), which stay valid however small the values are.
+// with |x_m| and |x_lo,m| summed per block in fp32 after scaling by the
+// block's grid (so tiny values cannot underflow the bound away).
 // When [h - E, h + E] straddles a rounding boundary of the 16-bit format, the
-// element is re-evaluated as an fp64 dot product over K (products exact) by
-// one wave before rounding.  fp32 compute, or an fp32 rounding target, needs
+// element is marked in a bitmap; a second kernel re-evaluates every marked
+// element as an fp64 dot product over K (products exact) and overwrites its
+// output.  fp32 compute, or an fp32 rounding target, needs
 // no guard: a flip there moves the result by 2^-24 relative.
 //
 // Work split: a workgroup of 4 waves owns RW*16 rows and RP = 16*JB columns;
@@ -91,15 +92,22 @@ __device__ __forceinline__ int grid_exp(uint32_t m) {
 // Split a fragment on the grid 2^g (round to nearest): hi on the grid, lo = v - hi.
 // Adding and subtracting 1.5 * 2^(g+23) rounds an fp32 value of magnitude below
 // 2^(g+22) to a multiple of 2^g.
+// Also accumulates sum (v 2^-g)^2 and sum (lo 2^-g)^2 (scaled by the grid, so
+// nothing underflows that matters; |v 2^-g| <= 2^8).
 template <class CT>
-__device__ __forceinline__ void split16(i32x4 v, float magic, i32x4& hi, i32x4& lo) {
+__device__ __forceinline__ void split16(i32x4 v, float magic, int g, i32x4& hi, i32x4& lo, float& sv, float& sl) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t u = (uint32_t)v[i];
         const float a = unpack_lo<CT>(u), b = unpack_hi<CT>(u);
         const float ah = (a + magic) - magic, bh = (b + magic) - magic;
+        const float al = a - ah, bl = b - bh;
         hi[i] = (int)pack2<CT>(ah, bh);
-        lo[i] = (int)pack2<CT>(a - ah, b - bh);
+        lo[i] = (int)pack2<CT>(al, bl);
+        const float as = __builtin_ldexpf(a, -g), bs = __builtin_ldexpf(b, -g);
+        const float ls = __builtin_ldexpf(al, -g), ms = __builtin_ldexpf(bl, -g);
+        sv = __builtin_fmaf(as, as, __builtin_fmaf(bs, bs, sv));
+        sl = __builtin_fmaf(ls, ls, __builtin_fmaf(ms, ms, sl));
     }
 }
 
@@ -129,6 +137,14 @@ __device__ __forceinline__ uint16_t round16(double v) {
     return CT::dt == DT_F16 ? f64_to_f16(v) : f64_to_bf16(v);
 }
 
+// the projection rounded to the output dtype (exactly, from the fp64 value), as fp32
+template <class CT>
+__device__ __forceinline__ float affine_value(double acc, int out_dt) {
+    if (out_dt == DT_F32) return (float)acc;   // one rounding, fp64 -> fp32
+    if (CT::dt == DT_F16) return f16_to_f32(round16<CT>(acc));
+    return bf16_to_f32(round16<CT>(acc));
+}
+
 template <class CT, int JB, int KS>
 __global__ __launch_bounds__(256) void xr_kernel(XrParams p) {
     constexpr bool SPLIT = CT::dt != DT_F32;     // 16-bit compute: hi/lo split and guard
@@ -136,10 +152,10 @@ __global__ __launch_bounds__(256) void xr_kernel(XrParams p) {
     constexpr int RW = 4 / KS;                   // row groups
     constexpr int RP = JB * 16;                  // columns per workgroup
     constexpr int TILE = RP * 128;               // bytes of one B tile (RP rows x 128 B)
-    constexpr int BCH = KS * NB * RP * 8 / 256;  // 16-byte chunks per thread per round
-    static_assert((KS * NB * RP * 8) % 256 == 0, "loader split");
     __shared__ __attribute__((aligned(16))) char sd[2][KS * NB * TILE];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index in a scalar register: everything derived from it stays uniform
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rg = wave % RW, kg = wave / RW;
     const int64_t wg_m0 = (int64_t)blockIdx.x * (RW * 16);
     const int64_t j0 = (int64_t)blockIdx.y * RP;
@@ -156,54 +172,71 @@ __global__ __launch_bounds__(256) void xr_kernel(XrParams p) {
     for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[jb][e] = 0.0;
-    double xm2 = 0.0, xl2 = 0.0;   // sums over blocks of 64*max|x|^2 and of 16*4^g (bounds on |x|^2, |x_lo|^2)
+    double xm2 = 0.0, xl2 = 0.0;   // this lane's parts of |x_m|^2 and |x_lo,m|^2
 
     const int KT = (int)((kbytes + 127) / 128);   // k blocks of 128 bytes
     const int ROUNDS = (KT + KS - 1) / KS;
-    i32x4 br[BCH], xr[2], xn[2];
     // round r stages blocks r*KS .. r*KS+KS-1: tile (g, a) = block r*KS+g of array a
-    auto load_b = [&](int r) {
+    // B tiles go straight from global memory to LDS (buffer_load ... lds): one
+    // load per wave fills 1 KiB = 8 rows x 128 bytes of one tile; lane l fetches
+    // the chunk that the swizzled layout puts in its slot.  Block blk of a round
+    // is tile blk / (RP/8) (k group t / NB, array t % NB), rows 8*(blk % (RP/8)) + ...
+    constexpr int QBLK = KS * NB * RP / 8 / 4;   // loads per wave per round
+    static_assert(KS * NB * RP / 8 % 4 == 0, "loader split");
+    uint32_t boff[QBLK];
+    const uint32_t kc16 = (uint32_t)((lane & 7) ^ (lane >> 3)) << 4;
 #pragma unroll
-        for (int i = 0; i < BCH; ++i) {
-            const int c = tid + i * 256;
-            const int t = c / (RP * 8), w = c % (RP * 8);
-            const int g = t / NB, a = t % NB;
-            const uint32_t kb = (uint32_t)(r * KS + g) * 128 + ((w & 7) << 4);
-            const uint32_t off = kb < kbytes ? (uint32_t)(w >> 3) * kbytes + kb : OOB;
-            br[i] = buf_load16(a ? rsl : rsh, off);
+    for (int q = 0; q < QBLK; ++q) {
+        const int blk = wave + q * 4;
+        const int t = blk / (RP / 8);
+        const int row = (blk % (RP / 8)) * 8 + (lane >> 3);
+        boff[q] = (uint32_t)row * kbytes + (uint32_t)(t / NB) * 128 + kc16;
+    }
+    auto issue_b = [&](char* stage, int r) {
+        const uint32_t kb0 = (uint32_t)(r * KS) * 128;
+        const bool full = kb0 + KS * 128 <= kbytes;
+#pragma unroll
+        for (int q = 0; q < QBLK; ++q) {
+            const int blk = wave + q * 4;
+            const int t = blk / (RP / 8);
+            uint32_t v = boff[q];
+            if (!full) v = (kb0 + (uint32_t)(t / NB) * 128 + kc16 < kbytes) ? v : OOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds((t % NB) ? rsl : rsh,
+                                                     (__attribute__((address_space(3))) void*)(stage + blk * 1024), 16,
+                                                     v, (int)kb0, 0, 0);
         }
     };
-    auto store_b = [&](char* dst) {
-#pragma unroll
-        for (int i = 0; i < BCH; ++i) {
-            const int c = tid + i * 256;
-            const int t = c / (RP * 8), w = c % (RP * 8);
-            *(i32x4*)(dst + t * TILE + lds_off(w >> 3, w & 7)) = br[i];
-        }
-    };
-    auto load_x = [&](i32x4 (&dst)[2], int r) {
-        const uint32_t kb0 = (uint32_t)(r * KS + kg) * 128;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const uint32_t kb = kb0 + (uint32_t)((s * 4 + (lane >> 4)) << 4);
-            dst[s] = buf_load16(rsx, kb < kbytes ? (uint32_t)my_row * kbytes + kb : OOB);
-        }
-    };
+    // x fragments of round r: 16 bytes at k bytes kb0 + 16*(lane>>4) (+64)
+    const uint32_t xoff = (uint32_t)my_row * kbytes + (uint32_t)((lane >> 4) << 4);
+    const uint32_t xk16 = (uint32_t)((lane >> 4) << 4);
 
     bool wide = false;   // a block beyond the split's exponent range: re-evaluate the row
+    i32x4 xr0, xr1, xn0, xn1;
+#define LYC_LOAD_X(D0, D1, R)                                                             \
+    do {                                                                                  \
+        const uint32_t kb0_ = (uint32_t)((R) * KS + kg) * 128;                           \
+        if (kb0_ + 128 <= kbytes) {                                                       \
+            D0 = buf_load16(rsx, xoff + kb0_);                                            \
+            D1 = buf_load16(rsx, xoff + kb0_ + 64);                                       \
+        } else {                                                                          \
+            D0 = buf_load16(rsx, kb0_ + xk16 < kbytes ? xoff + kb0_ : OOB);               \
+            D1 = buf_load16(rsx, kb0_ + xk16 + 64 < kbytes ? xoff + kb0_ + 64 : OOB);     \
+        }                                                                                 \
+    } while (0)
     if (ROUNDS > 0) {
-        load_b(0);
-        load_x(xr, 0);
-        store_b(sd[0]);
+        issue_b(sd[0], 0);
+        LYC_LOAD_X(xr0, xr1, 0);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
     for (int r = 0; r < ROUNDS; ++r) {
         const char* cur = sd[r & 1];
         const bool more = r + 1 < ROUNDS;
         if (more) {
-            load_b(r + 1);
-            load_x(xn, r + 1);
+            issue_b(sd[(r + 1) & 1], r + 1);
+            LYC_LOAD_X(xn0, xn1, r + 1);
         }
+        const i32x4 xr[2] = {xr0, xr1};
         const char* th = cur + (kg * NB) * TILE;    // this k group's b_hi (or b) tile
         if (SPLIT) {
             // block maximum of |x| for the lane's row (4 lane groups x 16 values)
@@ -217,14 +250,13 @@ __global__ __launch_bounds__(256) void xr_kernel(XrParams p) {
             const int g = grid_exp<CT>(mb);
             wide |= (g > 100);
             const float magic = __builtin_ldexpf(1.5f, (g > 100 ? 100 : g) + 23);
-            if (mb) {
-                const double mv = (double)unpack_lo<CT>(mb);
-                xm2 = __builtin_fma(64.0 * mv, mv, xm2);        // 64 values, each |x| <= max
-                xl2 += __builtin_ldexp(16.0, 2 * g);            // 64 values, each |x_lo| <= 2^(g-1)
-            }
             i32x4 xh[2], xlo[2];
-            split16<CT>(xr[0], magic, xh[0], xlo[0]);
-            split16<CT>(xr[1], magic, xh[1], xlo[1]);
+            float sv = 0.f, sl = 0.f;
+            split16<CT>(xr[0], magic, g, xh[0], xlo[0], sv, sl);
+            split16<CT>(xr[1], magic, g, xh[1], xlo[1], sv, sl);
+            // 16 values per lane; 2^-120 per value covers squares that underflowed
+            xm2 += __builtin_ldexp((double)sv + 0x1p-116, 2 * g);
+            xl2 += __builtin_ldexp((double)sl + 0x1p-116, 2 * g);
             const char* tl = th + TILE;             // this k group's b_lo tile
 #pragma unroll
             for (int jb = 0; jb < JB; ++jb) {
@@ -257,16 +289,21 @@ __global__ __launch_bounds__(256) void xr_kernel(XrParams p) {
                 }
             }
         }
-        if (more) {
-            store_b(sd[(r + 1) & 1]);
-            xr[0] = xn[0];
-            xr[1] = xn[1];
-        }
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of round r+1 (LDS and x)
         __syncthreads();
+        if (more) {
+            xr0 = xn0;
+            xr1 = xn1;
+        }
     }
+#undef LYC_LOAD_X
 
-    // meet the k groups' partial sums in LDS (the B tiles are no longer needed);
-    // the row bounds are already identical across the lane groups of a row
+    // row sums: the four lane groups of a row hold disjoint k
+    xm2 += __shfl_xor(xm2, 16);
+    xm2 += __shfl_xor(xm2, 32);
+    xl2 += __shfl_xor(xl2, 16);
+    xl2 += __shfl_xor(xl2, 32);
+    // meet the k groups' partial sums in LDS (the B tiles are no longer needed)
     if (KS > 1) {
         constexpr int W = JB * 4 + 3;
         static_assert((KS - 1) * RW * 64 * W * 8 <= 2 * KS * NB * TILE, "reduction buffer");
@@ -297,10 +334,13 @@ __global__ __launch_bounds__(256) void xr_kernel(XrParams p) {
     const int64_t m = wg_m0 + my_row;
     const bool row_ok = m < p.M;
 
+    // guard: flag the elements whose error interval straddles a rounding
+    // boundary (bit jb*4+e of `flags`); they are re-evaluated after the
+    // outputs are written, so the accumulators are only ever indexed statically
+    uint32_t flags = 0;
     if (SPLIT && p.guard) {
         const double xn2 = __builtin_sqrt(xm2) * (1.0 + 0x1p-20);
         const double xln = __builtin_sqrt(xl2) * (1.0 + 0x1p-20);
-        unsigned nflag = 0;
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) {
 #pragma unroll
@@ -313,91 +353,149 @@ __global__ __launch_bounds__(256) void xr_kernel(XrParams p) {
                 const double h = acc[jb][e];
                 const bool bwide = !(bn.y < 1e300);   // a block of b could not be split
                 const bool flag = row_ok && col_ok && (wide || bwide || round16<CT>(h - E) != round16<CT>(h + E));
-                uint64_t mask = __ballot(flag);
-                nflag += (unsigned)__builtin_popcountll(mask);
-                while (mask) {
-                    const int L = __builtin_ctzll(mask);
-                    mask &= mask - 1;
-                    const int64_t mL = wg_m0 + rg * 16 + (L & 15);
-                    const int64_t jL = j0 + jb * 16 + 4 * (L >> 4) + e;
-                    const i32x4* xrow = (const i32x4*)((const char*)p.x + mL * kbytes);
-                    const i32x4* brow = (const i32x4*)((const char*)p.b_full + jL * kbytes);
-                    const uint32_t nch = kbytes / 16;
-                    double p0 = 0.0, p1 = 0.0;
-                    uint32_t c = lane;
-                    for (; c + 64 < nch; c += 128) {
-                        p0 += dot16_f64<CT>(xrow[c], brow[c]);
-                        p1 += dot16_f64<CT>(xrow[c + 64], brow[c + 64]);
-                    }
-                    if (c < nch) p0 += dot16_f64<CT>(xrow[c], brow[c]);
-                    double part = p0 + p1;
+                flags |= flag ? (1u << (jb * 4 + e)) : 0u;
+            }
+        }
+    }
+
+    if (row_ok) {
+        if (p.mode == XR_H) {
+            // h_r [M][ld_out] in the compute dtype (all RP columns, padding included)
 #pragma unroll
-                    for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
-                    if (lane == L) acc[jb][e] = part;
+            for (int jb = 0; jb < JB; ++jb) {
+                const int64_t jg = j0 + jb * 16 + 4 * (lane >> 4);
+                if (CT::dt == DT_F32) {
+                    float* hp = (float*)p.out + m * p.ld_out + jg;
+                    *(f32x4*)hp = f32x4{(float)acc[jb][0], (float)acc[jb][1], (float)acc[jb][2], (float)acc[jb][3]};
+                } else {
+                    uint16_t o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = round16<CT>(acc[jb][e]);
+                    uint16_t* hp = (uint16_t*)p.out + m * p.ld_out + jg;
+                    *(i32x2*)hp = i32x2{(int)(o[0] | ((uint32_t)o[1] << 16)), (int)(o[2] | ((uint32_t)o[3] << 16))};
+                }
+            }
+        } else {
+            // plain affine: y = round_out(round_out(p) + b)
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb) {
+                const int jl0 = jb * 16 + 4 * (lane >> 4);
+                const int64_t n0 = j0 + jl0;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float bias =
+                        (p.bias != nullptr && jl0 + e < cols_wg) ? load_as_f32(p.bias, p.bias_dt, n0 + e) : 0.f;
+                    v[e] = affine_value<CT>(acc[jb][e], p.out_dt) + bias;
+                }
+                const int64_t base = m * p.ld_out + n0;
+                if (p.out_dt == DT_F32) {
+                    float* y = (float*)p.out;
+                    if (p.vec_store && jl0 + 3 < cols_wg) {
+                        *(f32x4*)(y + base) = f32x4{v[0], v[1], v[2], v[3]};
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (jl0 + e < cols_wg) y[base + e] = v[e];
+                    }
+                } else {
+                    uint16_t o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = p.out_dt == DT_F16 ? f32_to_f16(v[e]) : f32_to_bf16(v[e]);
+                    uint16_t* y = (uint16_t*)p.out;
+                    if (p.vec_store && jl0 + 3 < cols_wg) {
+                        *(i32x2*)(y + base) =
+                            i32x2{(int)(o[0] | ((uint32_t)o[1] << 16)), (int)(o[2] | ((uint32_t)o[3] << 16))};
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (jl0 + e < cols_wg) y[base + e] = o[e];
+                    }
                 }
             }
         }
-        if (lane == 0 && nflag) atomicAdd(p.flagged, nflag);
     }
 
-    if (!row_ok) return;
-    if (p.mode == XR_H) {
-        // h_r [M][ld_out] in the compute dtype (all RP columns, padding included)
-#pragma unroll
-        for (int jb = 0; jb < JB; ++jb) {
-            const int64_t jg = j0 + jb * 16 + 4 * (lane >> 4);
-            if (CT::dt == DT_F32) {
-                float* hp = (float*)p.out + m * p.ld_out + jg;
-                *(f32x4*)hp = f32x4{(float)acc[jb][0], (float)acc[jb][1], (float)acc[jb][2], (float)acc[jb][3]};
-            } else {
-                uint16_t o[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = round16<CT>(acc[jb][e]);
-                uint16_t* hp = (uint16_t*)p.out + m * p.ld_out + jg;
-                *(i32x2*)hp = i32x2{(int)(o[0] | ((uint32_t)o[1] << 16)), (int)(o[2] | ((uint32_t)o[3] << 16))};
+    if (SPLIT && p.guard) {
+        // mark the flagged elements for the fp64 re-evaluation kernel
+        if (flags) {
+            uint32_t* row = p.bitmap + m * p.words_per_row;
+            for (uint32_t f = flags; f; f &= f - 1) {
+                const int bit = __builtin_ctz(f);
+                const int64_t j = j0 + (bit >> 2) * 16 + 4 * (lane >> 4) + (bit & 3);
+                atomicOr(&row[j >> 5], 1u << (j & 31));
             }
         }
-        return;
+        const unsigned nflag = (unsigned)__builtin_popcount(flags);
+        unsigned tot = nflag;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) tot += (unsigned)__shfl_xor((int)tot, o);
+        if (lane == 0 && tot) atomicAdd(p.flagged, tot);
     }
-    // plain affine: y = round_out(round_out(p) + b)
-#pragma unroll
-    for (int jb = 0; jb < JB; ++jb) {
-        const int jl0 = jb * 16 + 4 * (lane >> 4);
-        const int64_t n0 = j0 + jl0;
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float pr;
-            if (p.out_dt == DT_F32) pr = (float)acc[jb][e];                     // one rounding, fp64 -> fp32
-            else if (CT::dt == DT_F16) pr = f16_to_f32(round16<CT>(acc[jb][e]));
-            else pr = bf16_to_f32(round16<CT>(acc[jb][e]));
-            const float bias = (p.bias != nullptr && jl0 + e < cols_wg) ? load_as_f32(p.bias, p.bias_dt, n0 + e) : 0.f;
-            v[e] = pr + bias;
-        }
-        const int64_t base = m * p.ld_out + n0;
-        if (p.out_dt == DT_F32) {
-            float* y = (float*)p.out;
-            if (p.vec_store && jl0 + 3 < cols_wg) {
-                *(f32x4*)(y + base) = f32x4{v[0], v[1], v[2], v[3]};
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (jl0 + e < cols_wg) y[base + e] = v[e];
+}
+
+// Re-evaluation of marked elements: one wave per bitmap word (32 columns of
+// one row); for every marked element the wave computes the dot product of x
+// row m and b row j in fp64 (products exact) with all 64 lanes, rounds it and
+// writes the output as the contraction's epilogue would.  Marked elements are
+// rare and scattered, so spreading words over many waves hides the latency of
+// the row reads.
+template <class CT>
+__global__ __launch_bounds__(256) void xr_fix_kernel(XrParams p) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    const int64_t total = p.M * p.words_per_row;
+    const uint32_t kbytes = (uint32_t)(p.K * CT::es);
+    const uint32_t nch = kbytes / 16;
+    for (int64_t w = (int64_t)blockIdx.x * 4 + wave; w < total; w += nwaves) {
+        uint32_t bits = (uint32_t)__builtin_amdgcn_readfirstlane((int)p.bitmap[w]);
+        if (!bits) continue;
+        const int64_t m = w / p.words_per_row;
+        const int64_t jbase = (w - m * p.words_per_row) * 32;
+        const i32x4* xrow = (const i32x4*)((const char*)p.x + m * kbytes);
+        while (bits) {
+            const int b = __builtin_ctz(bits);
+            bits &= bits - 1;
+            const int64_t j = jbase + b;
+            const i32x4* brow = (const i32x4*)((const char*)p.b_full + j * kbytes);
+            double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+            uint32_t c = lane;
+            for (; c + 192 < nch; c += 256) {
+                const i32x4 x0 = xrow[c], x1 = xrow[c + 64], x2 = xrow[c + 128], x3 = xrow[c + 192];
+                const i32x4 b0 = brow[c], b1 = brow[c + 64], b2 = brow[c + 128], b3 = brow[c + 192];
+                s0 += dot16_f64<CT>(x0, b0);
+                s1 += dot16_f64<CT>(x1, b1);
+                s2 += dot16_f64<CT>(x2, b2);
+                s3 += dot16_f64<CT>(x3, b3);
             }
-        } else {
-            uint16_t o[4];
+            for (; c < nch; c += 64) s0 += dot16_f64<CT>(xrow[c], brow[c]);
+            double part = (s0 + s1) + (s2 + s3);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = p.out_dt == DT_F16 ? f32_to_f16(v[e]) : f32_to_bf16(v[e]);
-            uint16_t* y = (uint16_t*)p.out;
-            if (p.vec_store && jl0 + 3 < cols_wg) {
-                *(i32x2*)(y + base) = i32x2{(int)(o[0] | ((uint32_t)o[1] << 16)), (int)(o[2] | ((uint32_t)o[3] << 16))};
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (jl0 + e < cols_wg) y[base + e] = o[e];
+            for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+            if (lane == 0) {
+                if (p.mode == XR_H) {
+                    ((uint16_t*)p.out)[m * p.ld_out + j] = round16<CT>(part);
+                } else {
+                    const float bias = p.bias != nullptr ? load_as_f32(p.bias, p.bias_dt, j) : 0.f;
+                    const float v = affine_value<CT>(part, p.out_dt) + bias;
+                    // the guard runs for 16-bit outputs only
+                    ((uint16_t*)p.out)[m * p.ld_out + j] = p.out_dt == DT_F16 ? f32_to_f16(v) : f32_to_bf16(v);
+                }
             }
         }
     }
+}
+
+hipError_t launch_xr_fix(int c_dt, const XrParams& p, hipStream_t s) {
+    const int64_t total = p.M * p.words_per_row;
+    int64_t blocks = (total + 3) / 4;   // one wave per word, up to 16384 waves
+    if (blocks > 4096) blocks = 4096;
+    if (blocks < 1) blocks = 1;
+    if (c_dt == DT_F16) hipLaunchKernelGGL(xr_fix_kernel<CF16>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+    else if (c_dt == DT_BF16) hipLaunchKernelGGL(xr_fix_kernel<CBF16>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 template <class CT, int JB, int KS>

@@ -37,6 +37,8 @@ struct XrParams {
     int64_t M, Nc, K;
     int guard;              // 1: apply the rounding guard (16-bit rounding target)
     unsigned* flagged;      // count of re-evaluated elements
+    uint32_t* bitmap;       // [M][words_per_row] bits of the elements to re-evaluate (zeroed beforehand)
+    int64_t words_per_row;  // ceil(Nc / 32)
     int mode;               // XR_H or XR_AFFINE
     void* out;              // h [M][ld_out] (compute dtype) or y [M][ld_out] (out_dt)
     int64_t ld_out;
@@ -59,6 +61,8 @@ struct PrepParams {
     void* dl;   // lo part
     void* uc;
     double2* dnorm;   // {|down_c,j|, |lo_j|}
+    uint32_t* zero;   // words to clear (the re-evaluation bitmap)
+    int64_t nzero;
     unsigned* flagged;
     int64_t N, K, rank;
     int r_pad;
@@ -69,10 +73,13 @@ hipError_t launch_gemm(int c_dt, const GemmParams& p, hipStream_t s);
 // the output tile launch_gemm uses for this shape
 void gemm_tile_shape(int64_t M, int64_t N, int c_dt, int* tn, int* tm);
 hipError_t launch_xr(int c_dt, const XrParams& p, hipStream_t s);
+// re-evaluate in fp64 the elements the contraction marked in p.bitmap, and
+// overwrite their outputs
+hipError_t launch_xr_fix(int c_dt, const XrParams& p, hipStream_t s);
 // hi/lo split (per 64-k block) of each row of b [rows,K] (16-bit compute
 // dtype) and {|b_j|_2, |b_lo,j|_2}; also clears *flagged (if not null)
 hipError_t launch_rownorm(const void* b, int c_dt, int64_t rows, int64_t K, void* b_hi, void* b_lo, double2* out,
-                          unsigned* flagged, hipStream_t s);
+                          unsigned* flagged, uint32_t* zero, int64_t nzero, hipStream_t s);
 hipError_t launch_prep(const PrepParams& p, hipStream_t s);
 // fp32 [n] -> 16-bit compute dtype [n], round to nearest even
 hipError_t launch_cast(const float* src, void* dst, int64_t n, int c_dt, hipStream_t s);

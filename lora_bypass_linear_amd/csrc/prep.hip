@@ -38,48 +38,59 @@ __device__ __forceinline__ void store16(void* dst, int64_t i, float v, int c_dt)
     ((uint16_t*)dst)[i] = c_dt == DT_F16 ? f32_to_f16(v) : f32_to_bf16(v);
 }
 
-// One row of a [rows, K] operand per workgroup (256 threads; wave w of an
-// iteration holds one aligned 64-k block).  Optionally writes the row's
-// compute-dtype copy; for 16-bit compute also its split v = hi + lo per 64-k
-// block (hi = v rounded to the grid 2^(e-7), e = floor(log2 max|v|) of the
-// block, the same split the contraction applies to x); returns {|v|_2, |lo|_2}.
-// A block whose grid exponent exceeds 100 cannot be split with the fp32
-// rounding constant: |lo|_2 is then reported as +inf, which makes the
-// contraction re-evaluate that row's elements in fp64.
+// One row of a [rows, K] operand per workgroup of 256 threads; thread t takes
+// the 8 consecutive elements k0 + 8t .. 8t+7, so an aligned 64-k block is held
+// by 8 neighbouring lanes.  Optionally writes the row's compute-dtype copy;
+// for 16-bit compute also its split v = hi + lo per 64-k block (hi = v rounded
+// to the grid 2^(e-7), e = floor(log2 max|v|) of the block, the same split the
+// contraction applies to x); returns {|v|_2, |lo|_2}.  A block whose grid
+// exponent exceeds 100 cannot be split with the fp32 rounding constant: |lo|_2
+// is then reported as +inf, which makes the contraction re-evaluate that row's
+// elements in fp64.
 __device__ void row_pass(const void* src, int src_dt, int c_dt, int64_t row, int64_t K, bool zero, void* dst,
                          void* dst_hi, void* dst_lo, double2* norm_out) {
     __shared__ double red[2][256];
     const int tid = threadIdx.x;
     double ss = 0.0, ll = 0.0;
     bool wide = false;
-    for (int64_t k0 = 0; k0 < K; k0 += 256) {
-        const int64_t k = k0 + tid;
-        float c = 0.f;
-        if (k < K) {
-            const float v = zero ? 0.f : load_as_f32(src, src_dt, row * K + k);
-            double cd;
-            if (dst) store_c(dst, row * K + k, v, c_dt, &cd);
-            else cd = (double)v;
-            c = (float)cd;   // compute-dtype value, exact in fp32
-        }
-        ss = __builtin_fma((double)c, (double)c, ss);
-        if (dst_hi) {
-            float mx = __builtin_fabsf(c);
+    for (int64_t k0 = 0; k0 < K; k0 += 2048) {
+        const int64_t kt = k0 + 8 * tid;
+        float c[8];
+        float mx = 0.f;
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, o));
-            float hi = 0.f, lo = 0.f;
+        for (int i = 0; i < 8; ++i) {
+            c[i] = 0.f;
+            if (kt + i < K) {
+                const float v = zero ? 0.f : load_as_f32(src, src_dt, row * K + kt + i);
+                double cd;
+                if (dst) store_c(dst, row * K + kt + i, v, c_dt, &cd);
+                else cd = (double)v;
+                c[i] = (float)cd;   // compute-dtype value, exact in fp32
+            }
+            ss = __builtin_fma((double)c[i], (double)c[i], ss);
+            mx = __builtin_fmaxf(mx, __builtin_fabsf(c[i]));
+        }
+        if (dst_hi) {
+            // maximum over the 64-k block: 8 lanes
+#pragma unroll
+            for (int o = 4; o >= 1; o >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, o));
+            int g = 0;
+            float magic = 0.f;
             if (mx > 0.f) {
-                const int g = floor_log2(mx) - 7;
+                g = floor_log2(mx) - 7;
                 wide |= g > 100;
-                const float magic = __builtin_ldexpf(1.5f, (g > 100 ? 100 : g) + 23);
-                hi = (c + magic) - magic;
-                lo = c - hi;
+                magic = __builtin_ldexpf(1.5f, (g > 100 ? 100 : g) + 23);
             }
-            if (k < K) {
-                store16(dst_hi, row * K + k, hi, c_dt);
-                store16(dst_lo, row * K + k, lo, c_dt);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float hi = mx > 0.f ? (c[i] + magic) - magic : 0.f;
+                const float lo = c[i] - hi;
+                if (kt + i < K) {
+                    store16(dst_hi, row * K + kt + i, hi, c_dt);
+                    store16(dst_lo, row * K + kt + i, lo, c_dt);
+                }
+                ll = __builtin_fma((double)lo, (double)lo, ll);
             }
-            ll = __builtin_fma((double)lo, (double)lo, ll);
         }
     }
     red[0][tid] = ss;
@@ -100,6 +111,7 @@ __device__ void row_pass(const void* src, int src_dt, int c_dt, int64_t row, int
 __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
     const int b = blockIdx.x, tid = threadIdx.x;
     if (b == 0 && tid == 0) *p.flagged = 0u;
+    for (int64_t i = (int64_t)b * 256 + tid; i < p.nzero; i += (int64_t)gridDim.x * 256) p.zero[i] = 0u;
     if (b < p.r_pad) {
         const bool split = p.c_dt != DT_F32;
         row_pass(p.down, p.down_dt, p.c_dt, b, p.K, b >= p.rank, p.dc, split ? p.dh : nullptr,
@@ -120,14 +132,16 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
 // split and norms of the rows of an operand already in the 16-bit compute
 // dtype; clears *flagged
 __global__ __launch_bounds__(256) void rownorm_kernel(const void* b, int c_dt, int64_t K, void* b_hi, void* b_lo,
-                                                      double2* out, unsigned* flagged) {
+                                                      double2* out, unsigned* flagged, uint32_t* zero, int64_t nzero) {
     if (blockIdx.x == 0 && threadIdx.x == 0 && flagged) *flagged = 0u;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nzero; i += (int64_t)gridDim.x * 256) zero[i] = 0u;
     row_pass(b, c_dt, c_dt, blockIdx.x, K, false, nullptr, b_hi, b_lo, &out[blockIdx.x]);
 }
 
 hipError_t launch_rownorm(const void* b, int c_dt, int64_t rows, int64_t K, void* b_hi, void* b_lo, double2* out,
-                          unsigned* flagged, hipStream_t s) {
-    hipLaunchKernelGGL(rownorm_kernel, dim3((unsigned)rows), dim3(256), 0, s, b, c_dt, K, b_hi, b_lo, out, flagged);
+                          unsigned* flagged, uint32_t* zero, int64_t nzero, hipStream_t s) {
+    hipLaunchKernelGGL(rownorm_kernel, dim3((unsigned)rows), dim3(256), 0, s, b, c_dt, K, b_hi, b_lo, out, flagged, zero,
+                       nzero);
     return hipGetLastError();
 }
 
