@@ -39,6 +39,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-eager", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -73,6 +75,13 @@ def main():
         else:
             L.linear(d["x"], d["w"], d.get("b"), out=y, workspace=ws)
 
+    if args.copy_calibration_mib > 0:
+        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     print(f"[bench] {wl.name}: warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -90,15 +99,20 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     tflops = wl.flops / (ms_per_step * 1e-3) / 1e12
 
-    # dominant kernel: the fused main contraction (fold + K loop + epilogue)
-    n_g, t_g = prof["gemm"]
-    gemm_ms = t_g / max(n_g, 1)
-    gemm_flops = 2.0 * wl.M * wl.N * wl.K + 2.0 * wl.M * wl.r * wl.N
-    achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    # dominant kernel: the fused main contraction (fold + K loop + epilogue) of
+    # the LoRA path, or the exactly rounded projection of the plain affine path
+    dom = "gemm" if lora else "hpass"
+    n_g, t_g = prof[dom]
+    dom_ms = t_g / max(n_g, 1)
+    dom_flops = 2.0 * wl.M * wl.N * wl.K + (2.0 * wl.M * wl.r * wl.N if lora else 0.0)
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else 0.0
     peak = PEAK_TFLOPS[c_dt]
-    roofline = {"bound": "mfma", "kernel": "gemm_kernel", "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                "flops_per_launch": gemm_flops, "avg_us": round(gemm_ms * 1e3, 3)}
+    from lora_bypass_linear_amd.profsum import read_traffic
+    traffic = read_traffic(os.path.join(ROOT, "profiles", f"traffic_{dom}_{wl.name}.txt"), dom)
+    roofline = {"bound": "mfma", "kernel": {"gemm": "gemm_kernel", "hpass": "xr_kernel"}[dom],
+                "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": None if traffic is None else int(traffic),
+                "flops_per_launch": dom_flops, "avg_us": round(dom_ms * 1e3, 3)}
     kernels = {k: {"launches": n, "avg_us": round(t * 1e3 / n, 3)} for k, (n, t) in prof.items() if n}
     guard = None
     if lora and wl.r > 0 and c_dt != L.F32:

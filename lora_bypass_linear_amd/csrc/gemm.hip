@@ -8,7 +8,7 @@
 //
 //   1. fold   (LoRA only)  acc  = h_r . up_c^T   over the padded rank, then
 //                          acc *= scale          (one fp32 multiply)
-//   2. main               acc += x_c . W_c^T     K loop, LDS double buffer
+//   2. main               acc += x_c . W_c^T     K loop, multi-stage LDS pipeline
 //   3. epilogue           y = round_out(acc + b), one rounding
 //
 // Accumulation is fp32 throughout (LyCORIS "Precision" page, "Dtype policy");
@@ -120,28 +120,82 @@ __device__ __forceinline__ void wait_vm() {
 // stage read before the barrier may be refilled after it, and completion of
 // its own LDS-bound loads is established by an explicit wait_vm before it.
 __device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt and expcnt unconstrained
+    asm volatile("s_barrier" ::: "memory");
 }
 
-__device__ __forceinline__ void publish() {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-}
-
-// MFMAs over one K step (64 bytes per row) held in an LDS stage.
-template <class CT, class TL>
-__device__ __forceinline__ void mma_stage(const char* sa, const char* sb, f32x4 (&acc)[TL::FN][TL::FM], int lane,
-                                          int wn, int wm) {
-    i32x4 fa[TL::FN], fb[TL::FM];
+// This wave's operand fragments of one K step (64 bytes per row) from an LDS
+// stage: FN 16-row blocks of the A tile, FM of the B tile.
+template <class TL>
+__device__ __forceinline__ void read_frags(const char* st, i32x4 (&fa)[TL::FN], i32x4 (&fb)[TL::FM], int lane,
+                                           int wn, int wm) {
     const int kc = lane >> 4;
+    const char* sb = st + TL::TN * 64;
 #pragma unroll
-    for (int i = 0; i < TL::FN; ++i) fa[i] = *(const i32x4*)(sa + lds64(wn * TL::WN + i * 16 + (lane & 15), kc));
+    for (int i = 0; i < TL::FN; ++i) fa[i] = *(const i32x4*)(st + lds64(wn * TL::WN + i * 16 + (lane & 15), kc));
 #pragma unroll
     for (int j = 0; j < TL::FM; ++j) fb[j] = *(const i32x4*)(sb + lds64(wm * TL::WM + j * 16 + (lane & 15), kc));
+}
+
+template <class CT, class TL>
+__device__ __forceinline__ void mma(const i32x4 (&fa)[TL::FN], const i32x4 (&fb)[TL::FM],
+                                    f32x4 (&acc)[TL::FN][TL::FM]) {
 #pragma unroll
     for (int i = 0; i < TL::FN; ++i)
 #pragma unroll
         for (int j = 0; j < TL::FM; ++j) acc[i][j] = CT::step(fa[i], fb[j], acc[i][j]);
+}
+
+// The K steps of one tile: first the fold steps over the padded rank (A = up_c,
+// B = h_r), then the main steps over K (A = W_c, B = x_c).
+template <class TL>
+struct Steps {
+    Loader<TL> lf, lm;
+    __amdgpu_buffer_rsrc_t fa, fb, ma, mb;
+    uint32_t fbytes, kbytes;
+    int RF, KT;
+    __device__ __forceinline__ void issue(char* smem, int s, int wave, int lane) const {
+        char* st = smem + (s % TL::NS) * TL::STAGE;
+        if (s < RF) lf.issue(st, fa, fb, fbytes, (uint32_t)s * 64, wave, lane);
+        else lm.issue(st, ma, mb, kbytes, (uint32_t)(s - RF) * 64, wave, lane);
+    }
+};
+
+// One pipeline step kt: wait until step kt+1 has landed in LDS (steps up to
+// kt+NS-1 are in flight), barrier, refill the stage of step kt (its fragments
+// are already in registers) with step kt+NS, read step kt+1's fragments into
+// (nfa, nfb) while the MFMAs of step kt run on (cfa, cfb).
+template <class CT, class TL>
+__device__ __forceinline__ void pipe_step(const Steps<TL>& S, char* smem, int kt, const i32x4 (&cfa)[TL::FN],
+                                          const i32x4 (&cfb)[TL::FM], i32x4 (&nfa)[TL::FN], i32x4 (&nfb)[TL::FM],
+                                          f32x4 (&acc)[TL::FN][TL::FM], int wave, int lane, int wn, int wm) {
+    if (kt + TL::NS - 1 < S.KT) wait_vm<(TL::NS - 2) * TL::QMIN>();
+    else wait_vm<0>();
+    lds_barrier();
+    if (kt + TL::NS < S.KT) S.issue(smem, kt + TL::NS, wave, lane);
+    if (kt + 1 < S.KT) read_frags<TL>(smem + ((kt + 1) % TL::NS) * TL::STAGE, nfa, nfb, lane, wn, wm);
+    __builtin_amdgcn_s_setprio(1);
+    mma<CT, TL>(cfa, cfb, acc);
+    __builtin_amdgcn_s_setprio(0);
+}
+
+// Steps [kt, end) of the pipeline, two per iteration so that the register sets
+// alternate statically; on return the fragments of step `end` are in (fa0, fb0).
+template <class CT, class TL>
+__device__ __forceinline__ void pipe_run(const Steps<TL>& S, char* smem, int kt, int end, i32x4 (&fa0)[TL::FN],
+                                         i32x4 (&fb0)[TL::FM], i32x4 (&fa1)[TL::FN], i32x4 (&fb1)[TL::FM],
+                                         f32x4 (&acc)[TL::FN][TL::FM], int wave, int lane, int wn, int wm) {
+    for (; kt + 1 < end; kt += 2) {
+        pipe_step<CT, TL>(S, smem, kt, fa0, fb0, fa1, fb1, acc, wave, lane, wn, wm);
+        pipe_step<CT, TL>(S, smem, kt + 1, fa1, fb1, fa0, fb0, acc, wave, lane, wn, wm);
+    }
+    if (kt < end) {
+        pipe_step<CT, TL>(S, smem, kt, fa0, fb0, fa1, fb1, acc, wave, lane, wn, wm);
+#pragma unroll
+        for (int i = 0; i < TL::FN; ++i) fa0[i] = fa1[i];
+#pragma unroll
+        for (int j = 0; j < TL::FM; ++j) fb0[j] = fb1[j];
+    }
 }
 
 template <class CT, class TL>
@@ -165,52 +219,40 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
 #pragma unroll
         for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    constexpr int AOFF = TL::TN * 64;   // B tile offset within a stage
-
-    // 1. fold: acc = scale * (h_r . up_c^T), one stage at a time
-    if (p.rf > 0) {
-        const uint32_t fb = (uint32_t)(p.rf * CT::es);
-        const auto rsa = make_rsrc((const char*)p.af + n0 * fb, (uint32_t)rows_a * fb);
-        const auto rsb = make_rsrc((const char*)p.bf + m0 * fb, (uint32_t)rows_b * fb);
-        Loader<TL> ld;
-        ld.init(fb, fb, wave, lane);
-        for (uint32_t kb = 0; kb < fb; kb += 64) {
-            ld.issue(smem, rsa, rsb, fb, kb, wave, lane);
-            publish();
-            mma_stage<CT, TL>(smem, smem + AOFF, acc, lane, wn, wm);
-            __syncthreads();
+    // 1-2. fold and main contraction in one pipeline of K steps: NS LDS stages
+    //      filled straight from global memory, NS steps ahead of their use;
+    //      fragments are read one step ahead into a second register set.
+    Steps<TL> S;
+    S.fbytes = (uint32_t)(p.rf * CT::es);
+    S.kbytes = (uint32_t)(p.K * CT::es);
+    S.RF = (int)(S.fbytes / 64);
+    S.KT = S.RF + (int)((S.kbytes + 63) / 64);
+    S.fa = make_rsrc((const char*)p.af + n0 * S.fbytes, (uint32_t)rows_a * S.fbytes);
+    S.fb = make_rsrc((const char*)p.bf + m0 * S.fbytes, (uint32_t)rows_b * S.fbytes);
+    S.ma = make_rsrc((const char*)p.a + n0 * S.kbytes, (uint32_t)rows_a * S.kbytes);
+    S.mb = make_rsrc((const char*)p.b + m0 * S.kbytes, (uint32_t)rows_b * S.kbytes);
+    S.lf.init(S.fbytes, S.fbytes, wave, lane);
+    S.lm.init(S.kbytes, S.kbytes, wave, lane);
+    const int KT = S.KT;
+    if (KT > 0) {
+        i32x4 fa0[FN], fb0[FM], fa1[FN], fb1[FM];
+#pragma unroll
+        for (int s0 = 0; s0 < TL::NS; ++s0)
+            if (s0 < KT) S.issue(smem, s0, wave, lane);
+        if (TL::NS - 1 < KT) wait_vm<(TL::NS - 1) * TL::QMIN>();
+        else wait_vm<0>();
+        lds_barrier();
+        read_frags<TL>(smem, fa0, fb0, lane, wn, wm);
+        // fold steps, then acc = scale * (h_r . up_c^T) once, then the main steps:
+        // the accumulators see no vector ALU work inside either loop
+        pipe_run<CT, TL>(S, smem, 0, S.RF, fa0, fb0, fa1, fb1, acc, wave, lane, wn, wm);
+        if (S.RF > 0) {
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j) acc[i][j] *= p.scale;
         }
-#pragma unroll
-        for (int i = 0; i < FN; ++i)
-#pragma unroll
-            for (int j = 0; j < FM; ++j) acc[i][j] *= p.scale;
-    }
-
-    // 2. main K loop: NS LDS stages filled straight from global memory, loads
-    //    issued NS-1 steps ahead; each step waits only for its own loads.
-    const uint32_t kbytes = (uint32_t)(p.K * CT::es);
-    if (kbytes > 0) {
-        const auto rsa = make_rsrc((const char*)p.a + n0 * kbytes, (uint32_t)rows_a * kbytes);
-        const auto rsb = make_rsrc((const char*)p.b + m0 * kbytes, (uint32_t)rows_b * kbytes);
-        const int KT = (int)((kbytes + 63) / 64);
-        Loader<TL> ld;
-        ld.init(kbytes, kbytes, wave, lane);
-#pragma unroll
-        for (int s0 = 0; s0 < TL::NS - 1; ++s0)
-            if (s0 < KT) ld.issue((smem + s0 * TL::STAGE), rsa, rsb, kbytes, (uint32_t)s0 * 64, wave, lane);
-        for (int kt = 0; kt < KT; ++kt) {
-            // steps kt .. kt+NS-2 are in flight; step kt must have landed
-            if (kt + TL::NS - 2 < KT) wait_vm<(TL::NS - 2) * TL::QMIN>();
-            else wait_vm<0>();
-            lds_barrier();   // every wave's part of step kt is in LDS; stage of step kt-1 is free
-            if (kt + TL::NS - 1 < KT)
-                ld.issue(smem + ((kt + TL::NS - 1) % TL::NS) * TL::STAGE, rsa, rsb, kbytes, (uint32_t)(kt + TL::NS - 1) * 64, wave,
-                         lane);
-            const char* cur = smem + (kt % TL::NS) * TL::STAGE;
-            __builtin_amdgcn_s_setprio(1);
-            mma_stage<CT, TL>(cur, cur + AOFF, acc, lane, wn, wm);
-            __builtin_amdgcn_s_setprio(0);
-        }
+        pipe_run<CT, TL>(S, smem, S.RF, KT, fa0, fb0, fa1, fb1, acc, wave, lane, wn, wm);
     }
 
     // 3. epilogue: lane holds, per 16x16 block, 4 consecutive n for one m
@@ -264,7 +306,7 @@ static hipError_t run(const GemmParams& p, hipStream_t s) {
     const int tiles_n = (int)((p.N + TL::TN - 1) / TL::TN);
     const int tiles_m = (int)((p.M + TL::TM - 1) / TL::TM);
     const int nblk = tiles_n * tiles_m;
-    hipLaunchKernelGGL((gemm_kernel<CT, TL>), dim3(nblk), dim3(TL::NT), 0, s, p, tiles_n, tiles_m, 8);
+    hipLaunchKernelGGL((gemm_kernel<CT, TL>), dim3(nblk), dim3(TL::NT), 0, s, p, tiles_n, tiles_m, 4);
     return hipGetLastError();
 }
 
