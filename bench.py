@@ -5,12 +5,13 @@
 A step is one full forward -- operand preparation, the h contraction with its
 rounding guard, and the fused main contraction with the bypass fold and the
 bias/cast epilogue -- over inputs already resident in HBM.  W untimed steps,
-then K timed steps bracketed by device synchronisation.  One JSON line is
-printed with throughput (algorithmic TFLOP/s), the fraction of the MFMA
-fp16/bf16 dense peak, max/RMS ULP against the fp64 oracle on sampled rows,
-the roofline of the dominant kernel (its device time measured with HIP events
-around each launch of the timed region), the oracle's own throughput on host
-cores, and the eager two-GEMM torch chain as a comparator.
+then K timed steps bracketed by device synchronisation (this sets `value`),
+then the same K steps again with a HIP event pair around every kernel launch
+for per-kernel device durations.  One JSON line is printed with throughput
+(algorithmic TFLOP/s), the fraction of the MFMA fp16/bf16 dense peak, max/RMS
+ULP against the fp64 oracle on sampled rows, the roofline of the dominant
+kernel, the oracle's own throughput on host cores, and the eager two-GEMM
+torch chain as a comparator.
 """
 from __future__ import annotations
 
@@ -87,17 +88,29 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # timed region: K whole steps, nothing else on the stream
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    L.profile_begin(8 * args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    prof = L.profile_end()
     ms_per_step = wall * 1e3 / args.steps
     tflops = wl.flops / (ms_per_step * 1e-3) / 1e12
+
+    # the same K steps again with a HIP event pair around every kernel launch,
+    # on the launch stream, for per-kernel device durations (the event records
+    # add gaps between kernels, so this region does not set `value`)
+    print(f"[bench] timing {args.steps} instrumented steps", file=sys.stderr, flush=True)
+    L.profile_begin(8 * args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall_i = time.perf_counter() - t0
+    prof = L.profile_end()
 
     # dominant kernel: the fused main contraction (fold + K loop + epilogue) of
     # the LoRA path, or the exactly rounded projection of the plain affine path
@@ -131,6 +144,7 @@ def main():
                       "bias": WL.NAME[wl.b_dt] if wl.b_dt else None, "accumulate": "f32",
                       "parallelism": "single GPU"},
            "frac_of_peak": round(tflops / peak, 4), "hbm_gbs": round(wl.bytes / (ms_per_step * 1e-3) / 1e9, 1),
+           "instrumented_ms_per_step": round(wall_i * 1e3 / args.steps, 5),
            "input_digest": WL.digest(inputs), "kernels": kernels, "h_guard": guard, "roofline": roofline}
 
     # accuracy on sampled rows against the fp64 oracle (this is also the CPU-baseline leg)
