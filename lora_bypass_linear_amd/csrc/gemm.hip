@@ -20,26 +20,31 @@
 namespace lyc {
 
 // TN x TM output tile, WN x WM per wave (multiples of 16), NS pipeline stages
-// of one K step each; a K step is 64 bytes of every row (32 16-bit values).
-template <int TN_, int TM_, int WN_, int WM_, int NS_>
+// of one K step each.  A K step is BKB bytes of every row (64: 32 16-bit
+// values; 128: 64), made of SUB = BKB/64 MFMA substeps of 64 bytes.
+template <int TN_, int TM_, int WN_, int WM_, int NS_, int BKB_>
 struct Tile {
-    static constexpr int TN = TN_, TM = TM_, WN = WN_, WM = WM_, NS = NS_;
+    static constexpr int TN = TN_, TM = TM_, WN = WN_, WM = WM_, NS = NS_, BKB = BKB_;
     static constexpr int WAVES_N = TN / WN, WAVES_M = TM / WM;
     static constexpr int NW = WAVES_N * WAVES_M, NT = NW * 64;
     static constexpr int FN = WN / 16, FM = WM / 16;
-    static constexpr int NBLK = (TN + TM) / 16;                 // 1 KiB LDS blocks (16 rows) per step
-    static constexpr int QMAX = (NBLK + NW - 1) / NW;           // loads per wave per step, at most
-    static constexpr int QMIN = NBLK / NW;                      // ... at least
-    static constexpr int STAGE = (TN + TM) * 64;                // LDS bytes per stage
+    static constexpr int SUB = BKB / 64;                        // MFMA substeps per K step
+    static constexpr int CH = BKB / 16;                         // 16-byte chunks per row
+    static constexpr int RPB = 64 / CH;                         // rows per 1 KiB wave load
+    static constexpr int NBLK = (TN + TM) / RPB;                // wave loads per step
+    static constexpr int Q = NBLK / NW;                         // loads per wave per step
+    static constexpr int STAGE = (TN + TM) * BKB;               // LDS bytes per stage
+    static_assert(BKB == 64 || BKB == 128, "K step");
     static_assert(TN % WN == 0 && TM % WM == 0 && WN % 16 == 0 && WM % 16 == 0, "tile shape");
-    static_assert(TN % 16 == 0 && TM % 16 == 0 && QMIN >= 1, "loader split");
-    static_assert(NS * STAGE <= 160 * 1024, "LDS");
+    static_assert(NBLK % NW == 0 && Q >= 1, "loader split");
+    static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "LDS");
+    static_assert((NS - 1) * Q < 64, "vmcnt range");
 };
 
-using TileL = Tile<256, 256, 128, 64, 4>;  // 8 waves, 128 KiB
-using TileG = Tile<192, 256, 96, 64, 5>;   // 8 waves, 140 KiB
-using TileM = Tile<128, 128, 64, 64, 4>;   // 4 waves, 64 KiB
-using TileS = Tile<64, 64, 32, 32, 4>;     // 4 waves, 32 KiB
+using TileL = Tile<256, 256, 128, 64, 2, 128>;  // 8 waves, 128 KiB
+using TileG = Tile<192, 256, 96, 64, 2, 128>;   // 8 waves, 112 KiB
+using TileM = Tile<128, 128, 64, 64, 4, 128>;   // 4 waves, 128 KiB
+using TileS = Tile<64, 64, 32, 32, 4, 128>;     // 4 waves, 64 KiB
 
 // Workgroup id -> output tile.  Workgroups are dispatched round-robin over the
 // 8 XCDs (id % 8), each with its own L2: give every XCD a contiguous range of
@@ -59,82 +64,79 @@ __device__ __forceinline__ void tile_coords(int bid, int nblk, int tiles_n, int 
     tn = r / gsz;
 }
 
-// LDS rows are 64 bytes (4 chunks of 16); chunk kc of row r sits at slot
-// kc ^ ((r >> 1) & 3), so the 16-byte fragment reads of 8 consecutive rows
-// (two rows per 128 bytes) hit 8 different bank groups.
-__device__ __forceinline__ int lds64(int row, int kc) { return row * 64 + ((kc ^ ((row >> 1) & 3)) << 4); }
+// LDS rows hold BKB bytes (CH chunks of 16).  Chunk kc of row r sits at slot
+// kc ^ swz(r), swz(r) = (r / (128 / BKB)) mod CH, so the 16-byte fragment
+// reads of 8 consecutive rows (one or two rows per 128 bytes) hit 8 different
+// bank groups.
+template <class TL>
+__device__ __forceinline__ int swz(int row) {
+    return TL::BKB == 128 ? (row & 7) : ((row >> 1) & 3);
+}
+template <class TL>
+__device__ __forceinline__ int lds_at(int row, int kc) {
+    return row * TL::BKB + ((kc ^ swz<TL>(row)) << 4);
+}
 
 // Global -> LDS without registers: one buffer_load_dwordx4 ... lds per wave
-// fills 1 KiB of LDS = 16 rows x 64 bytes of a K step.  The LDS side of such a
-// load is fixed (lane l writes bytes 16l .. 16l+15 of the KiB), so each lane
+// fills 1 KiB of LDS = RPB rows x BKB bytes of a K step.  The LDS side of such
+// a load is fixed (lane l writes bytes 16l .. 16l+15 of the KiB), so each lane
 // fetches the global chunk that belongs in that slot of the swizzled layout:
-// row 16 blk + (l >> 2), logical chunk (l & 3) ^ ((l >> 3) & 3).  The blocks of
+// row RPB blk + l / CH, logical chunk (l mod CH) ^ swz(that row).  The blocks of
 // the A (W-side) and B (x-side) tiles are numbered together and dealt to the
 // waves round-robin.
 template <class TL>
 struct Loader {
-    uint32_t vo[TL::QMAX];
+    // The blocks of the A (W-side) and B (x-side) tiles are dealt round-robin,
+    // so a wave's load q covers A block wave + q NW (q < QA) or B block
+    // wave + (q - QA) NW: its lane offset is the lane's offset in the wave's
+    // first block of that side plus a uniform stride.
+    static constexpr int QA = TL::TN / TL::RPB / TL::NW, QB = TL::TM / TL::RPB / TL::NW;
+    static_assert(QA * TL::RPB * TL::NW == TL::TN && QB * TL::RPB * TL::NW == TL::TM, "loader split");
+    uint32_t va, vb;          // lane offsets in the first A / B block, k step 0
+    uint32_t sa, sb;          // byte stride between a wave's consecutive blocks (uniform)
+    __device__ __forceinline__ static uint32_t chunk16(int lane) {
+        return (uint32_t)((lane % TL::CH) ^ swz<TL>(lane / TL::CH)) << 4;
+    }
     __device__ __forceinline__ void init(uint32_t a_bytes, uint32_t b_bytes, int wave, int lane) {
-        const uint32_t kc16 = (uint32_t)((lane & 3) ^ ((lane >> 3) & 3)) << 4;
-#pragma unroll
-        for (int q = 0; q < TL::QMAX; ++q) {
-            const int blk = wave + q * TL::NW;
-            const bool is_a = blk < TL::TN / 16;
-            const int row = (is_a ? blk : blk - TL::TN / 16) * 16 + (lane >> 2);
-            vo[q] = (uint32_t)row * (is_a ? a_bytes : b_bytes) + kc16;
-        }
+        const uint32_t row = (uint32_t)(wave * TL::RPB + lane / TL::CH);
+        va = row * a_bytes + chunk16(lane);
+        vb = row * b_bytes + chunk16(lane);
+        sa = (uint32_t)(TL::NW * TL::RPB) * a_bytes;
+        sb = (uint32_t)(TL::NW * TL::RPB) * b_bytes;
     }
     // loads of one K step (kb0 = its first byte within a row) into an LDS stage;
-    // rows past a tile's valid rows read zeros through the buffer range check, and
-    // in the last, ragged step the chunks past K are sent out of range too
+    // rows past a tile's valid rows read zeros through the buffer range check
+    // (the row offset is in the range-checked vector offset), and in the last,
+    // ragged step the chunks past the row end are sent out of range too
     __device__ __forceinline__ void issue(char* stage, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                           uint32_t row_bytes, uint32_t kb0, int wave, int lane) const {
-        const bool full = kb0 + 64 <= row_bytes;
-        const uint32_t kc16 = (uint32_t)((lane & 3) ^ ((lane >> 3) & 3)) << 4;
+        const bool ok = kb0 + TL::BKB <= row_bytes || kb0 + chunk16(lane) < row_bytes;
 #pragma unroll
-        for (int q = 0; q < TL::QMAX; ++q) {
-            const int blk = wave + q * TL::NW;
-            if (q >= TL::QMIN && blk >= TL::NBLK) break;
-            uint32_t v = vo[q];
-            if (!full) v = (kb0 + kc16 < row_bytes) ? v : OOB;
-            // (an if, not ?:, on the resource: the host pass silently drops the
-            // kernel stub for a conditional over __amdgpu_buffer_rsrc_t)
-            auto* dst = (__attribute__((address_space(3))) void*)(stage + blk * 1024);
-            if (blk < TL::TN / 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, v, (int)kb0, 0, 0);
-            else __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, v, (int)kb0, 0, 0);
+        for (int q = 0; q < QA; ++q) {
+            const uint32_t v = ok ? va + (uint32_t)q * sa : OOB;
+            auto* dst = (__attribute__((address_space(3))) void*)(stage + (wave + q * TL::NW) * 1024);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, v, (int)kb0, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+            const uint32_t v = ok ? vb + (uint32_t)q * sb : OOB;
+            auto* dst = (__attribute__((address_space(3))) void*)(stage + (wave + (QA + q) * TL::NW) * 1024);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, v, (int)kb0, 0, 0);
         }
     }
 };
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// Workgroup barrier that orders LDS only.  A __syncthreads() also waits for
-// every outstanding global load (vmcnt(0)), which defeats loads issued several
-// steps ahead; here the wave's own LDS reads are drained (lgkmcnt(0)), so a
-// stage read before the barrier may be refilled after it, and completion of
-// its own LDS-bound loads is established by an explicit wait_vm before it.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt and expcnt unconstrained
-    asm volatile("s_barrier" ::: "memory");
-}
-
-// This wave's operand fragments of one K step (64 bytes per row) from an LDS
-// stage: FN 16-row blocks of the A tile, FM of the B tile.
+// This wave's operand fragments of MFMA substep `sub` (64 bytes per row) from
+// an LDS stage: FN 16-row blocks of the A tile, FM of the B tile.
 template <class TL>
-__device__ __forceinline__ void read_frags(const char* st, i32x4 (&fa)[TL::FN], i32x4 (&fb)[TL::FM], int lane,
-                                           int wn, int wm) {
-    const int kc = lane >> 4;
-    const char* sb = st + TL::TN * 64;
+__device__ __forceinline__ void read_frags(const char* st, int sub, i32x4 (&fa)[TL::FN], i32x4 (&fb)[TL::FM],
+                                           int lane, int wn, int wm) {
+    const int kc = sub * 4 + (lane >> 4);
+    const char* sb = st + TL::TN * TL::BKB;
 #pragma unroll
-    for (int i = 0; i < TL::FN; ++i) fa[i] = *(const i32x4*)(st + lds64(wn * TL::WN + i * 16 + (lane & 15), kc));
+    for (int i = 0; i < TL::FN; ++i) fa[i] = *(const i32x4*)(st + lds_at<TL>(wn * TL::WN + i * 16 + (lane & 15), kc));
 #pragma unroll
-    for (int j = 0; j < TL::FM; ++j) fb[j] = *(const i32x4*)(sb + lds64(wm * TL::WM + j * 16 + (lane & 15), kc));
+    for (int j = 0; j < TL::FM; ++j) fb[j] = *(const i32x4*)(sb + lds_at<TL>(wm * TL::WM + j * 16 + (lane & 15), kc));
 }
 
 template <class CT, class TL>
@@ -156,41 +158,55 @@ struct Steps {
     int RF, KT;
     __device__ __forceinline__ void issue(char* smem, int s, int wave, int lane) const {
         char* st = smem + (s % TL::NS) * TL::STAGE;
-        if (s < RF) lf.issue(st, fa, fb, fbytes, (uint32_t)s * 64, wave, lane);
-        else lm.issue(st, ma, mb, kbytes, (uint32_t)(s - RF) * 64, wave, lane);
+        if (s < RF) lf.issue(st, fa, fb, fbytes, (uint32_t)s * TL::BKB, wave, lane);
+        else lm.issue(st, ma, mb, kbytes, (uint32_t)(s - RF) * TL::BKB, wave, lane);
     }
 };
 
-// One pipeline step kt: wait until step kt+1 has landed in LDS (steps up to
-// kt+NS-1 are in flight), barrier, refill the stage of step kt (its fragments
-// are already in registers) with step kt+NS, read step kt+1's fragments into
-// (nfa, nfb) while the MFMAs of step kt run on (cfa, cfb).
+// One MFMA substep u of the pipeline (substeps u = SUB*kt + sub run over the
+// K steps kt).  Steps up to kt+NS-1 have been issued when step kt+1 is about
+// to be read.  Before the fragments of a new K step kn are read: wait until it
+// has landed in LDS (the NS-2 steps after it may still be in flight), barrier,
+// and refill the stage of the step just finished (its fragments are all in
+// registers) with step kn+NS-1.  Then read substep u+1 into
+// (nfa, nfb) while the MFMAs of substep u run on (cfa, cfb).
 template <class CT, class TL>
-__device__ __forceinline__ void pipe_step(const Steps<TL>& S, char* smem, int kt, const i32x4 (&cfa)[TL::FN],
+__device__ __forceinline__ void pipe_step(const Steps<TL>& S, char* smem, int u, const i32x4 (&cfa)[TL::FN],
                                           const i32x4 (&cfb)[TL::FM], i32x4 (&nfa)[TL::FN], i32x4 (&nfb)[TL::FM],
                                           f32x4 (&acc)[TL::FN][TL::FM], int wave, int lane, int wn, int wm) {
-    if (kt + TL::NS - 1 < S.KT) wait_vm<(TL::NS - 2) * TL::QMIN>();
-    else wait_vm<0>();
-    lds_barrier();
-    if (kt + TL::NS < S.KT) S.issue(smem, kt + TL::NS, wave, lane);
-    if (kt + 1 < S.KT) read_frags<TL>(smem + ((kt + 1) % TL::NS) * TL::STAGE, nfa, nfb, lane, wn, wm);
+    const int un = u + 1, kn = un / TL::SUB;
+    // this substep's fragments were read one substep ago: they have landed
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    if (kn < S.KT) {
+        if (un % TL::SUB == 0) {
+            if (kn + TL::NS - 2 < S.KT) wait_vm<(TL::NS - 2) * TL::Q>();
+            else wait_vm<0>();
+            lds_barrier();
+            if (kn + TL::NS - 1 < S.KT) S.issue(smem, kn + TL::NS - 1, wave, lane);
+        }
+        read_frags<TL>(smem + (kn % TL::NS) * TL::STAGE, un % TL::SUB, nfa, nfb, lane, wn, wm);
+    }
+    // keep the next substep's LDS reads ahead of this substep's MFMAs (under
+    // register pressure the scheduler would otherwise sink them to their use)
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
     mma<CT, TL>(cfa, cfb, acc);
     __builtin_amdgcn_s_setprio(0);
 }
 
-// Steps [kt, end) of the pipeline, two per iteration so that the register sets
-// alternate statically; on return the fragments of step `end` are in (fa0, fb0).
+// Substeps [u, end) of the pipeline, two per iteration so that the register
+// sets alternate statically; on return the fragments of substep `end` are in
+// (fa0, fb0).
 template <class CT, class TL>
-__device__ __forceinline__ void pipe_run(const Steps<TL>& S, char* smem, int kt, int end, i32x4 (&fa0)[TL::FN],
+__device__ __forceinline__ void pipe_run(const Steps<TL>& S, char* smem, int u, int end, i32x4 (&fa0)[TL::FN],
                                          i32x4 (&fb0)[TL::FM], i32x4 (&fa1)[TL::FN], i32x4 (&fb1)[TL::FM],
                                          f32x4 (&acc)[TL::FN][TL::FM], int wave, int lane, int wn, int wm) {
-    for (; kt + 1 < end; kt += 2) {
-        pipe_step<CT, TL>(S, smem, kt, fa0, fb0, fa1, fb1, acc, wave, lane, wn, wm);
-        pipe_step<CT, TL>(S, smem, kt + 1, fa1, fb1, fa0, fb0, acc, wave, lane, wn, wm);
+    for (; u + 1 < end; u += 2) {
+        pipe_step<CT, TL>(S, smem, u, fa0, fb0, fa1, fb1, acc, wave, lane, wn, wm);
+        pipe_step<CT, TL>(S, smem, u + 1, fa1, fb1, fa0, fb0, acc, wave, lane, wn, wm);
     }
-    if (kt < end) {
-        pipe_step<CT, TL>(S, smem, kt, fa0, fb0, fa1, fb1, acc, wave, lane, wn, wm);
+    if (u < end) {
+        pipe_step<CT, TL>(S, smem, u, fa0, fb0, fa1, fb1, acc, wave, lane, wn, wm);
 #pragma unroll
         for (int i = 0; i < TL::FN; ++i) fa0[i] = fa1[i];
 #pragma unroll
@@ -225,8 +241,8 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
     Steps<TL> S;
     S.fbytes = (uint32_t)(p.rf * CT::es);
     S.kbytes = (uint32_t)(p.K * CT::es);
-    S.RF = (int)(S.fbytes / 64);
-    S.KT = S.RF + (int)((S.kbytes + 63) / 64);
+    S.RF = (int)((S.fbytes + TL::BKB - 1) / TL::BKB);
+    S.KT = S.RF + (int)((S.kbytes + TL::BKB - 1) / TL::BKB);
     S.fa = make_rsrc((const char*)p.af + n0 * S.fbytes, (uint32_t)rows_a * S.fbytes);
     S.fb = make_rsrc((const char*)p.bf + m0 * S.fbytes, (uint32_t)rows_b * S.fbytes);
     S.ma = make_rsrc((const char*)p.a + n0 * S.kbytes, (uint32_t)rows_a * S.kbytes);
@@ -236,23 +252,24 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
     const int KT = S.KT;
     if (KT > 0) {
         i32x4 fa0[FN], fb0[FM], fa1[FN], fb1[FM];
+        // steps 0 .. NS-1 fill every stage; step 0 must land (NS-1 steps may follow it)
 #pragma unroll
         for (int s0 = 0; s0 < TL::NS; ++s0)
             if (s0 < KT) S.issue(smem, s0, wave, lane);
-        if (TL::NS - 1 < KT) wait_vm<(TL::NS - 1) * TL::QMIN>();
+        if (TL::NS - 1 < KT) wait_vm<(TL::NS - 1) * TL::Q>();
         else wait_vm<0>();
         lds_barrier();
-        read_frags<TL>(smem, fa0, fb0, lane, wn, wm);
+        read_frags<TL>(smem, 0, fa0, fb0, lane, wn, wm);
         // fold steps, then acc = scale * (h_r . up_c^T) once, then the main steps:
         // the accumulators see no vector ALU work inside either loop
-        pipe_run<CT, TL>(S, smem, 0, S.RF, fa0, fb0, fa1, fb1, acc, wave, lane, wn, wm);
+        pipe_run<CT, TL>(S, smem, 0, S.RF * TL::SUB, fa0, fb0, fa1, fb1, acc, wave, lane, wn, wm);
         if (S.RF > 0) {
 #pragma unroll
             for (int i = 0; i < FN; ++i)
 #pragma unroll
                 for (int j = 0; j < FM; ++j) acc[i][j] *= p.scale;
         }
-        pipe_run<CT, TL>(S, smem, S.RF, KT, fa0, fb0, fa1, fb1, acc, wave, lane, wn, wm);
+        pipe_run<CT, TL>(S, smem, S.RF * TL::SUB, KT * TL::SUB, fa0, fb0, fa1, fb1, acc, wave, lane, wn, wm);
     }
 
     // 3. epilogue: lane holds, per 16x16 block, 4 consecutive n for one m

@@ -145,18 +145,36 @@ __device__ __forceinline__ float affine_value(double acc, int out_dt) {
     return bf16_to_f32(round16<CT>(acc));
 }
 
-template <class CT, int JB, int KS>
-__global__ __launch_bounds__(256) void xr_kernel(XrParams p) {
+// LDS pipeline of the contraction: a round stages KS k blocks of 128 bytes,
+// each with its b tile(s) (RP rows; b_hi and b_lo under the split) and its x
+// tile (RW*16 rows), all filled straight from global memory.  The workgroup's
+// NW = 4*CG waves are RW row groups x KS k groups x CG column groups; a wave
+// owns 16 rows and JB*16 columns.
+template <int JB, int KS, int CG, bool SPLIT>
+struct XrStage {
+    static constexpr int NB = SPLIT ? 2 : 1;
+    static constexpr int RW = 4 / KS, RP = JB * 16 * CG, NW = 4 * CG;
+    static constexpr int TILE = RP * 128, XT = RW * 16 * 128;
+    static constexpr int BYTES = KS * (NB * TILE + XT);
+    static constexpr int NBB = KS * NB * RP / 8;      // 1 KiB wave loads of b per round
+    static constexpr int NBLK = NBB + KS * RW * 2;    // ... of b and x
+    static constexpr int Q = NBLK / NW;               // per wave
+    static constexpr int NS = 4 * BYTES <= 159 * 1024 ? 4 : (3 * BYTES <= 159 * 1024 ? 3 : 2);
+    static_assert(NBLK % NW == 0, "loader split");
+    static_assert(NS * BYTES <= 160 * 1024 && (NS - 1) * Q < 64, "LDS stages");
+};
+
+template <class CT, int JB, int KS, int CG>
+__global__ __launch_bounds__(256 * CG, CG == 1 ? 2 : 1) void xr_kernel(XrParams p) {
     constexpr bool SPLIT = CT::dt != DT_F32;     // 16-bit compute: hi/lo split and guard
-    constexpr int NB = SPLIT ? 2 : 1;            // B arrays staged per k block (hi, lo)
-    constexpr int RW = 4 / KS;                   // row groups
-    constexpr int RP = JB * 16;                  // columns per workgroup
-    constexpr int TILE = RP * 128;               // bytes of one B tile (RP rows x 128 B)
-    __shared__ __attribute__((aligned(16))) char sd[2][KS * NB * TILE];
+    using ST = XrStage<JB, KS, CG, SPLIT>;
+    constexpr int NB = ST::NB, RW = ST::RW, RP = ST::RP, TILE = ST::TILE, NS = ST::NS, Q = ST::Q, NW = ST::NW;
+    __shared__ __attribute__((aligned(16))) char sd[NS * ST::BYTES];
     const int tid = threadIdx.x, lane = tid & 63;
     // wave index in a scalar register: everything derived from it stays uniform
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int rg = wave % RW, kg = wave / RW;
+    const int rg = wave % RW, kg = (wave / RW) % KS, cg = wave / (RW * KS);
+    const int c0 = cg * JB * 16;                // the wave's first column within the workgroup
     const int64_t wg_m0 = (int64_t)blockIdx.x * (RW * 16);
     const int64_t j0 = (int64_t)blockIdx.y * RP;
     const int rows_wg = (int)((p.M - wg_m0) < RW * 16 ? (p.M - wg_m0) : RW * 16);
@@ -176,68 +194,62 @@ __global__ __launch_bounds__(256) void xr_kernel(XrParams p) {
 
     const int KT = (int)((kbytes + 127) / 128);   // k blocks of 128 bytes
     const int ROUNDS = (KT + KS - 1) / KS;
-    // round r stages blocks r*KS .. r*KS+KS-1: tile (g, a) = block r*KS+g of array a
-    // B tiles go straight from global memory to LDS (buffer_load ... lds): one
-    // load per wave fills 1 KiB = 8 rows x 128 bytes of one tile; lane l fetches
-    // the chunk that the swizzled layout puts in its slot.  Block blk of a round
-    // is tile blk / (RP/8) (k group t / NB, array t % NB), rows 8*(blk % (RP/8)) + ...
-    constexpr int QBLK = KS * NB * RP / 8 / 4;   // loads per wave per round
-    static_assert(KS * NB * RP / 8 % 4 == 0, "loader split");
-    uint32_t boff[QBLK];
+    // Wave load blk of a round fills 1 KiB = 8 rows x 128 bytes of LDS: blocks
+    // below NBB belong to b tile t = blk / (RP/8) (k group t / NB, array t % NB),
+    // the rest to the x tile of k group (blk - NBB) / (2 RW).  Lane l fetches the
+    // chunk that the swizzled layout (lds_off) puts in its slot.
     const uint32_t kc16 = (uint32_t)((lane & 7) ^ (lane >> 3)) << 4;
+    uint32_t voff[Q];   // offset of the lane's chunk within its array, k block 0
+    uint32_t kpos[Q];   // byte position of that chunk within a row, k block 0
 #pragma unroll
-    for (int q = 0; q < QBLK; ++q) {
-        const int blk = wave + q * 4;
-        const int t = blk / (RP / 8);
-        const int row = (blk % (RP / 8)) * 8 + (lane >> 3);
-        boff[q] = (uint32_t)row * kbytes + (uint32_t)(t / NB) * 128 + kc16;
-    }
-    auto issue_b = [&](char* stage, int r) {
-        const uint32_t kb0 = (uint32_t)(r * KS) * 128;
-        const bool full = kb0 + KS * 128 <= kbytes;
-#pragma unroll
-        for (int q = 0; q < QBLK; ++q) {
-            const int blk = wave + q * 4;
+    for (int q = 0; q < Q; ++q) {
+        const int blk = wave + q * NW;
+        int g, row;
+        if (blk < ST::NBB) {
             const int t = blk / (RP / 8);
-            uint32_t v = boff[q];
-            if (!full) v = (kb0 + (uint32_t)(t / NB) * 128 + kc16 < kbytes) ? v : OOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds((t % NB) ? rsl : rsh,
-                                                     (__attribute__((address_space(3))) void*)(stage + blk * 1024), 16,
-                                                     v, (int)kb0, 0, 0);
+            g = t / NB;
+            row = (blk % (RP / 8)) * 8 + (lane >> 3);
+        } else {
+            const int xb = blk - ST::NBB;
+            g = xb / (RW * 2);
+            row = (xb % (RW * 2)) * 8 + (lane >> 3);
         }
-    };
-    // x fragments of round r: 16 bytes at k bytes kb0 + 16*(lane>>4) (+64)
-    const uint32_t xoff = (uint32_t)my_row * kbytes + (uint32_t)((lane >> 4) << 4);
-    const uint32_t xk16 = (uint32_t)((lane >> 4) << 4);
+        kpos[q] = (uint32_t)g * 128 + kc16;
+        voff[q] = (uint32_t)row * kbytes + kpos[q];
+    }
+    auto stage_at = [&](int r) { return sd + (r % NS) * ST::BYTES; };
+#define LYC_ISSUE_ROUND(R)                                                                          \
+    do {                                                                                            \
+        char* st_ = stage_at(R);                                                                    \
+        const uint32_t kb0_ = (uint32_t)((R) * KS) * 128;                                           \
+        const bool full_ = kb0_ + KS * 128 <= kbytes;                                               \
+        _Pragma("unroll") for (int q = 0; q < Q; ++q) {                                             \
+            const int blk = wave + q * NW;                                                          \
+            const uint32_t v = (full_ || kb0_ + kpos[q] < kbytes) ? voff[q] : OOB;                  \
+            auto* dst = (__attribute__((address_space(3))) void*)(st_ + blk * 1024);                \
+            if (blk >= ST::NBB) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, dst, 16, v, (int)kb0_, 0, 0); \
+            else if ((blk / (RP / 8)) % NB) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsl, dst, 16, v, (int)kb0_, 0, 0); \
+            else __builtin_amdgcn_raw_ptr_buffer_load_lds(rsh, dst, 16, v, (int)kb0_, 0, 0);        \
+        }                                                                                           \
+    } while (0)
 
     bool wide = false;   // a block beyond the split's exponent range: re-evaluate the row
-    i32x4 xr0, xr1, xn0, xn1;
-#define LYC_LOAD_X(D0, D1, R)                                                             \
-    do {                                                                                  \
-        const uint32_t kb0_ = (uint32_t)((R) * KS + kg) * 128;                           \
-        if (kb0_ + 128 <= kbytes) {                                                       \
-            D0 = buf_load16(rsx, xoff + kb0_);                                            \
-            D1 = buf_load16(rsx, xoff + kb0_ + 64);                                       \
-        } else {                                                                          \
-            D0 = buf_load16(rsx, kb0_ + xk16 < kbytes ? xoff + kb0_ : OOB);               \
-            D1 = buf_load16(rsx, kb0_ + xk16 + 64 < kbytes ? xoff + kb0_ + 64 : OOB);     \
-        }                                                                                 \
-    } while (0)
     if (ROUNDS > 0) {
-        issue_b(sd[0], 0);
-        LYC_LOAD_X(xr0, xr1, 0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        // rounds 0 .. NS-1 fill every stage; round 0 must land
+#pragma unroll
+        for (int r0 = 0; r0 < NS; ++r0)
+            if (r0 < ROUNDS) LYC_ISSUE_ROUND(r0);
+        if (NS - 1 < ROUNDS) wait_vm<(NS - 1) * Q>();
+        else wait_vm<0>();
+        lds_barrier();
     }
     for (int r = 0; r < ROUNDS; ++r) {
-        const char* cur = sd[r & 1];
-        const bool more = r + 1 < ROUNDS;
-        if (more) {
-            issue_b(sd[(r + 1) & 1], r + 1);
-            LYC_LOAD_X(xn0, xn1, r + 1);
-        }
-        const i32x4 xr[2] = {xr0, xr1};
-        const char* th = cur + (kg * NB) * TILE;    // this k group's b_hi (or b) tile
+        const char* cur = stage_at(r);
+        const char* th = cur + (kg * NB) * TILE;                       // this k group's b_hi (or b) tile
+        const char* xs = cur + KS * NB * TILE + kg * (RW * 16 * 128);  // this k group's x tile
+        i32x4 xr[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) xr[s] = *(const i32x4*)(xs + lds_off(my_row, s * 4 + (lane >> 4)));
         if (SPLIT) {
             // block maximum of |x| for the lane's row (4 lane groups x 16 values)
             uint32_t mb = absmax_bits(xr[0]);
@@ -260,7 +272,7 @@ __global__ __launch_bounds__(256) void xr_kernel(XrParams p) {
             const char* tl = th + TILE;             // this k group's b_lo tile
 #pragma unroll
             for (int jb = 0; jb < JB; ++jb) {
-                const int row = jb * 16 + (lane & 15);
+                const int row = c0 + jb * 16 + (lane & 15);
                 f32x4 hh = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
@@ -282,21 +294,24 @@ __global__ __launch_bounds__(256) void xr_kernel(XrParams p) {
                 const int kc = s * 4 + (lane >> 4);
 #pragma unroll
                 for (int jb = 0; jb < JB; ++jb) {
-                    const i32x4 bf = *(const i32x4*)(th + lds_off(jb * 16 + (lane & 15), kc));
+                    const i32x4 bf = *(const i32x4*)(th + lds_off(c0 + jb * 16 + (lane & 15), kc));
                     const f32x4 c = CT::step(bf, xr[s], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
                     for (int e = 0; e < 4; ++e) acc[jb][e] += (double)c[e];
                 }
             }
         }
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of round r+1 (LDS and x)
-        __syncthreads();
-        if (more) {
-            xr0 = xn0;
-            xr1 = xn1;
+        if (r + 1 < ROUNDS) {
+            // round r+1 must land (NS-2 rounds after it may be in flight); then
+            // refill the stage just read with round r+NS
+            if (r + NS - 1 < ROUNDS) wait_vm<(NS - 2) * Q>();
+            else wait_vm<0>();
+            lds_barrier();
+            if (r + NS < ROUNDS) LYC_ISSUE_ROUND(r + NS);
         }
     }
-#undef LYC_LOAD_X
+#undef LYC_ISSUE_ROUND
+    __syncthreads();   // every wave is done with the stages (they hold the k-group reduction next)
 
     // row sums: the four lane groups of a row hold disjoint k
     xm2 += __shfl_xor(xm2, 16);
@@ -306,10 +321,10 @@ __global__ __launch_bounds__(256) void xr_kernel(XrParams p) {
     // meet the k groups' partial sums in LDS (the B tiles are no longer needed)
     if (KS > 1) {
         constexpr int W = JB * 4 + 3;
-        static_assert((KS - 1) * RW * 64 * W * 8 <= 2 * KS * NB * TILE, "reduction buffer");
-        double* red = (double*)&sd[0][0];          // [KS-1][RW][64 lanes][W]
+        static_assert((KS - 1) * CG * RW * 64 * W * 8 <= NS * ST::BYTES, "reduction buffer");
+        double* red = (double*)sd;                 // [KS-1][CG][RW][64 lanes][W]
         if (kg > 0) {
-            double* dst = red + ((size_t)((kg - 1) * RW + rg) * 64 + lane) * W;
+            double* dst = red + ((size_t)(((kg - 1) * CG + cg) * RW + rg) * 64 + lane) * W;
 #pragma unroll
             for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
@@ -321,7 +336,7 @@ __global__ __launch_bounds__(256) void xr_kernel(XrParams p) {
         __syncthreads();
         if (kg > 0) return;
         for (int g2 = 1; g2 < KS; ++g2) {
-            const double* src = red + ((size_t)((g2 - 1) * RW + rg) * 64 + lane) * W;
+            const double* src = red + ((size_t)(((g2 - 1) * CG + cg) * RW + rg) * 64 + lane) * W;
 #pragma unroll
             for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
@@ -345,7 +360,7 @@ __global__ __launch_bounds__(256) void xr_kernel(XrParams p) {
         for (int jb = 0; jb < JB; ++jb) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int jl = jb * 16 + 4 * (lane >> 4) + e;
+                const int jl = c0 + jb * 16 + 4 * (lane >> 4) + e;
                 const bool col_ok = jl < cols_wg;
                 const double2 bn = col_ok ? p.bnorm[j0 + jl] : double2{0.0, 0.0};  // {|b|, |b_lo|}
                 const double E = (0x1p-24 * GUARD_CROSS * (xn2 * bn.y + xln * (bn.x + bn.y)) + 0x1p-37 * xn2 * bn.x) *
@@ -363,7 +378,7 @@ __global__ __launch_bounds__(256) void xr_kernel(XrParams p) {
             // h_r [M][ld_out] in the compute dtype (all RP columns, padding included)
 #pragma unroll
             for (int jb = 0; jb < JB; ++jb) {
-                const int64_t jg = j0 + jb * 16 + 4 * (lane >> 4);
+                const int64_t jg = j0 + c0 + jb * 16 + 4 * (lane >> 4);
                 if (CT::dt == DT_F32) {
                     float* hp = (float*)p.out + m * p.ld_out + jg;
                     *(f32x4*)hp = f32x4{(float)acc[jb][0], (float)acc[jb][1], (float)acc[jb][2], (float)acc[jb][3]};
@@ -379,7 +394,7 @@ __global__ __launch_bounds__(256) void xr_kernel(XrParams p) {
             // plain affine: y = round_out(round_out(p) + b)
 #pragma unroll
             for (int jb = 0; jb < JB; ++jb) {
-                const int jl0 = jb * 16 + 4 * (lane >> 4);
+                const int jl0 = c0 + jb * 16 + 4 * (lane >> 4);
                 const int64_t n0 = j0 + jl0;
                 float v[4];
 #pragma unroll
@@ -422,7 +437,7 @@ __global__ __launch_bounds__(256) void xr_kernel(XrParams p) {
             uint32_t* row = p.bitmap + m * p.words_per_row;
             for (uint32_t f = flags; f; f &= f - 1) {
                 const int bit = __builtin_ctz(f);
-                const int64_t j = j0 + (bit >> 2) * 16 + 4 * (lane >> 4) + (bit & 3);
+                const int64_t j = j0 + c0 + (bit >> 2) * 16 + 4 * (lane >> 4) + (bit & 3);
                 atomicOr(&row[j >> 5], 1u << (j & 31));
             }
         }
@@ -498,41 +513,40 @@ hipError_t launch_xr_fix(int c_dt, const XrParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <class CT, int JB, int KS>
+template <class CT, int JB, int KS, int CG>
 static hipError_t run_xr(const XrParams& p, hipStream_t s) {
-    constexpr int RP = JB * 16, RW = 4 / KS;
+    constexpr int RP = JB * 16 * CG, RW = 4 / KS;
     const dim3 grid((unsigned)((p.M + RW * 16 - 1) / (RW * 16)), (unsigned)((p.Nc + RP - 1) / RP));
-    hipLaunchKernelGGL((xr_kernel<CT, JB, KS>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((xr_kernel<CT, JB, KS, CG>), grid, dim3(256 * CG), 0, s, p);
     return hipGetLastError();
 }
 
-// k groups: enough waves to cover the chip (about 1024 row-block waves)
+// k groups: the fewest that still give one workgroup per CU (256), at most 4
 static int pick_ks(int64_t M, int64_t col_tiles) {
-    const int64_t row_blocks = (M + 15) / 16;
-    if (row_blocks * col_tiles >= 1024) return 1;
-    if (row_blocks * col_tiles * 2 >= 1024) return 2;
-    return 4;
+    int ks = 1;
+    while (ks < 4 && ((M + 64 / ks - 1) / (64 / ks)) * col_tiles < 256) ks *= 2;
+    return ks;
 }
 
-// JB (column blocks) bounds the k groups through LDS: two stages of KS*2 tiles
-// of JB*2 KiB must fit in 160 KiB.
-template <class CT, int JB, int KSMAX>
+template <class CT, int JB, int CG, int KSMAX>
 static hipError_t run_xr_jb(const XrParams& p, hipStream_t s) {
-    const int64_t col_tiles = (p.Nc + JB * 16 - 1) / (JB * 16);
+    const int64_t col_tiles = (p.Nc + JB * 16 * CG - 1) / (JB * 16 * CG);
     const int ks = pick_ks(p.M, col_tiles);
-    if (ks == 1 || KSMAX == 1) return run_xr<CT, JB, 1>(p, s);
-    if (ks == 2 || KSMAX == 2) return run_xr<CT, JB, (KSMAX >= 2 ? 2 : 1)>(p, s);
-    return run_xr<CT, JB, (KSMAX >= 4 ? 4 : 1)>(p, s);
+    if (ks == 1 || KSMAX == 1) return run_xr<CT, JB, 1, CG>(p, s);
+    if (ks == 2 || KSMAX == 2) return run_xr<CT, JB, (KSMAX >= 2 ? 2 : 1), CG>(p, s);
+    return run_xr<CT, JB, (KSMAX >= 4 ? 4 : 1), CG>(p, s);
 }
 
+// Columns per wave (JB blocks of 16) and column groups per workgroup (CG):
+// eight waves of 16 x 64 for the wider ranks keep two waves per SIMD.
 template <class CT>
 static hipError_t run_xr_ct(const XrParams& p, hipStream_t s) {
-    if (p.mode == XR_AFFINE) return run_xr_jb<CT, 4, 4>(p, s);
+    if (p.mode == XR_AFFINE) return run_xr_jb<CT, 4, 1, 4>(p, s);
     switch (p.Nc) {
-    case 32: return run_xr_jb<CT, 2, 4>(p, s);
-    case 64: return run_xr_jb<CT, 4, 4>(p, s);
-    case 128: return run_xr_jb<CT, 8, 2>(p, s);
-    case 256: return run_xr<CT, 16, 1>(p, s);
+    case 32: return run_xr_jb<CT, 2, 1, 4>(p, s);
+    case 64: return run_xr_jb<CT, 2, 2, 4>(p, s);
+    case 128: return run_xr_jb<CT, 4, 2, 2>(p, s);
+    case 256: return run_xr<CT, 8, 1, 2>(p, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -125,4 +125,22 @@ struct CF32 {
 // hit 8 different bank groups.
 __device__ __forceinline__ int lds_off(int row, int kc) { return row * 128 + ((kc ^ (row & 7)) << 4); }
 
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier that orders LDS only.  A __syncthreads() also waits for
+// every outstanding global load (vmcnt(0)), which defeats loads issued several
+// steps ahead; here the wave's own LDS reads are drained (lgkmcnt(0)), so a
+// stage read before the barrier may be refilled after it, and completion of
+// its own LDS-bound loads is established by an explicit wait_vm before it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt and expcnt unconstrained
+    asm volatile("s_barrier" ::: "memory");
+}
+
 }  // namespace lyc
