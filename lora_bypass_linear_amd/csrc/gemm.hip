@@ -149,69 +149,75 @@ __device__ __forceinline__ void mma(const i32x4 (&fa)[TL::FN], const i32x4 (&fb)
 }
 
 // The K steps of one tile: first the fold steps over the padded rank (A = up_c,
-// B = h_r), then the main steps over K (A = W_c, B = x_c).
+// B = h_r), then the main steps over K (A = W_c, B = x_c).  Steps at or past
+// KT are issued too, entirely out of range: they write zeros into a stage that
+// is never read again, so every pipeline step issues exactly Q loads per wave
+// and the vmcnt bookkeeping needs no branches.
 template <class TL>
 struct Steps {
     Loader<TL> lf, lm;
-    __amdgpu_buffer_rsrc_t fa, fb, ma, mb;
+    const char *fa, *fb, *ma, *mb;   // operand rows of this tile
+    uint32_t nfa, nfb, nma, nmb;     // their byte extents (buffer range)
     uint32_t fbytes, kbytes;
     int RF, KT;
     __device__ __forceinline__ void issue(char* smem, int s, int wave, int lane) const {
         char* st = smem + (s % TL::NS) * TL::STAGE;
-        if (s < RF) lf.issue(st, fa, fb, fbytes, (uint32_t)s * TL::BKB, wave, lane);
-        else lm.issue(st, ma, mb, kbytes, (uint32_t)(s - RF) * TL::BKB, wave, lane);
+        const bool fold = s < RF;
+        // select plain values, then build the resources (a conditional over
+        // the resource type itself loses the kernel's host stub)
+        const auto ra = make_rsrc(fold ? fa : ma, fold ? nfa : nma);
+        const auto rb = make_rsrc(fold ? fb : mb, fold ? nfb : nmb);
+        Loader<TL> l;
+        l.va = fold ? lf.va : lm.va;
+        l.vb = fold ? lf.vb : lm.vb;
+        l.sa = fold ? lf.sa : lm.sa;
+        l.sb = fold ? lf.sb : lm.sb;
+        const uint32_t row_bytes = s < KT ? (fold ? fbytes : kbytes) : 0u;   // 0: all out of range
+        l.issue(st, ra, rb, row_bytes, (uint32_t)(fold ? s : s - RF) * TL::BKB, wave, lane);
     }
 };
 
-// One MFMA substep u of the pipeline (substeps u = SUB*kt + sub run over the
-// K steps kt).  Steps up to kt+NS-1 have been issued when step kt+1 is about
-// to be read.  Before the fragments of a new K step kn are read: wait until it
-// has landed in LDS (the NS-2 steps after it may still be in flight), barrier,
-// and refill the stage of the step just finished (its fragments are all in
-// registers) with step kn+NS-1.  Then read substep u+1 into
-// (nfa, nfb) while the MFMAs of substep u run on (cfa, cfb).
-template <class CT, class TL>
-__device__ __forceinline__ void pipe_step(const Steps<TL>& S, char* smem, int u, const i32x4 (&cfa)[TL::FN],
-                                          const i32x4 (&cfb)[TL::FM], i32x4 (&nfa)[TL::FN], i32x4 (&nfb)[TL::FM],
-                                          f32x4 (&acc)[TL::FN][TL::FM], int wave, int lane, int wn, int wm) {
-    const int un = u + 1, kn = un / TL::SUB;
-    // this substep's fragments were read one substep ago: they have landed
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    if (kn < S.KT) {
-        if (un % TL::SUB == 0) {
-            if (kn + TL::NS - 2 < S.KT) wait_vm<(TL::NS - 2) * TL::Q>();
-            else wait_vm<0>();
-            lds_barrier();
-            if (kn + TL::NS - 1 < S.KT) S.issue(smem, kn + TL::NS - 1, wave, lane);
-        }
-        read_frags<TL>(smem + (kn % TL::NS) * TL::STAGE, un % TL::SUB, nfa, nfb, lane, wn, wm);
+// MFMAs of one substep with NV global loads and ND LDS reads (issued just
+// before, for later steps) spread between them: the matrix pipe never waits
+// for a burst of memory instructions to issue.
+template <class CT, class TL, int NV, int ND>
+__device__ __forceinline__ void mma_spread(const i32x4 (&fa)[TL::FN], const i32x4 (&fb)[TL::FM],
+                                           f32x4 (&acc)[TL::FN][TL::FM]) {
+    mma<CT, TL>(fa, fb, acc);
+    constexpr int G = NV > ND ? NV : ND;
+    constexpr int PER = TL::FN * TL::FM / (G + 1);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        if (g < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+        if (g < ND) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);             // MFMA
     }
-    // keep the next substep's LDS reads ahead of this substep's MFMAs (under
-    // register pressure the scheduler would otherwise sink them to their use)
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(1);
-    mma<CT, TL>(cfa, cfb, acc);
-    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_group_barrier(0x008, TL::FN * TL::FM - G * PER, 0);
 }
 
-// Substeps [u, end) of the pipeline, two per iteration so that the register
-// sets alternate statically; on return the fragments of substep `end` are in
-// (fa0, fb0).
+// One K step kt (two MFMA substeps of 32 k).  On entry the fragments of its
+// substep 0 are in (f0a, f0b) and steps up to kt+NS-1 have been issued.
+//   substep 0: read substep 1 into (f1a, f1b); MFMAs on (f0a, f0b)
+//   substep 1: wait until step kt+1 has landed (NS-2 steps after it may still be
+//              in flight), barrier, refill the stage of step kt with step
+//              kt+NS, read step kt+1's substep 0 into (f0a, f0b); MFMAs on (f1a, f1b)
 template <class CT, class TL>
-__device__ __forceinline__ void pipe_run(const Steps<TL>& S, char* smem, int u, int end, i32x4 (&fa0)[TL::FN],
-                                         i32x4 (&fb0)[TL::FM], i32x4 (&fa1)[TL::FN], i32x4 (&fb1)[TL::FM],
-                                         f32x4 (&acc)[TL::FN][TL::FM], int wave, int lane, int wn, int wm) {
-    for (; u + 1 < end; u += 2) {
-        pipe_step<CT, TL>(S, smem, u, fa0, fb0, fa1, fb1, acc, wave, lane, wn, wm);
-        pipe_step<CT, TL>(S, smem, u + 1, fa1, fb1, fa0, fb0, acc, wave, lane, wn, wm);
-    }
-    if (u < end) {
-        pipe_step<CT, TL>(S, smem, u, fa0, fb0, fa1, fb1, acc, wave, lane, wn, wm);
-#pragma unroll
-        for (int i = 0; i < TL::FN; ++i) fa0[i] = fa1[i];
-#pragma unroll
-        for (int j = 0; j < TL::FM; ++j) fb0[j] = fb1[j];
-    }
+__device__ __forceinline__ void k_step(const Steps<TL>& S, char* smem, int kt, i32x4 (&f0a)[TL::FN],
+                                       i32x4 (&f0b)[TL::FM], i32x4 (&f1a)[TL::FN], i32x4 (&f1b)[TL::FM],
+                                       f32x4 (&acc)[TL::FN][TL::FM], int wave, int lane, int wn, int wm) {
+    static_assert(TL::SUB == 2, "two substeps per K step");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // substep 0's fragments have landed
+    read_frags<TL>(smem + (kt % TL::NS) * TL::STAGE, 1, f1a, f1b, lane, wn, wm);
+    mma_spread<CT, TL, 0, TL::FN + TL::FM>(f0a, f0b, acc);
+    // every MFMA of substep 0 is issued before this wave waits on memory
+    __builtin_amdgcn_sched_barrier(0);
+
+    wait_vm<(TL::NS - 2) * TL::Q>();
+    lds_barrier();
+    S.issue(smem, kt + TL::NS, wave, lane);
+    // (past the last step this reads a stage that is never used: in bounds)
+    read_frags<TL>(smem + ((kt + 1) % TL::NS) * TL::STAGE, 0, f0a, f0b, lane, wn, wm);
+    mma_spread<CT, TL, TL::Q, TL::FN + TL::FM>(f1a, f1b, acc);
 }
 
 template <class CT, class TL>
@@ -243,33 +249,36 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
     S.kbytes = (uint32_t)(p.K * CT::es);
     S.RF = (int)((S.fbytes + TL::BKB - 1) / TL::BKB);
     S.KT = S.RF + (int)((S.kbytes + TL::BKB - 1) / TL::BKB);
-    S.fa = make_rsrc((const char*)p.af + n0 * S.fbytes, (uint32_t)rows_a * S.fbytes);
-    S.fb = make_rsrc((const char*)p.bf + m0 * S.fbytes, (uint32_t)rows_b * S.fbytes);
-    S.ma = make_rsrc((const char*)p.a + n0 * S.kbytes, (uint32_t)rows_a * S.kbytes);
-    S.mb = make_rsrc((const char*)p.b + m0 * S.kbytes, (uint32_t)rows_b * S.kbytes);
+    S.fa = (const char*)p.af + n0 * S.fbytes;
+    S.fb = (const char*)p.bf + m0 * S.fbytes;
+    S.ma = (const char*)p.a + n0 * S.kbytes;
+    S.mb = (const char*)p.b + m0 * S.kbytes;
+    S.nfa = (uint32_t)rows_a * S.fbytes;
+    S.nfb = (uint32_t)rows_b * S.fbytes;
+    S.nma = (uint32_t)rows_a * S.kbytes;
+    S.nmb = (uint32_t)rows_b * S.kbytes;
     S.lf.init(S.fbytes, S.fbytes, wave, lane);
     S.lm.init(S.kbytes, S.kbytes, wave, lane);
     const int KT = S.KT;
     if (KT > 0) {
-        i32x4 fa0[FN], fb0[FM], fa1[FN], fb1[FM];
-        // steps 0 .. NS-1 fill every stage; step 0 must land (NS-1 steps may follow it)
+        i32x4 f0a[FN], f0b[FM], f1a[FN], f1b[FM];
+        // steps 0 .. NS-1 fill every stage; step 0 must land (NS-1 steps follow it)
 #pragma unroll
-        for (int s0 = 0; s0 < TL::NS; ++s0)
-            if (s0 < KT) S.issue(smem, s0, wave, lane);
-        if (TL::NS - 1 < KT) wait_vm<(TL::NS - 1) * TL::Q>();
-        else wait_vm<0>();
+        for (int s0 = 0; s0 < TL::NS; ++s0) S.issue(smem, s0, wave, lane);
+        wait_vm<(TL::NS - 1) * TL::Q>();
         lds_barrier();
-        read_frags<TL>(smem, 0, fa0, fb0, lane, wn, wm);
+        read_frags<TL>(smem, 0, f0a, f0b, lane, wn, wm);
         // fold steps, then acc = scale * (h_r . up_c^T) once, then the main steps:
         // the accumulators see no vector ALU work inside either loop
-        pipe_run<CT, TL>(S, smem, 0, S.RF * TL::SUB, fa0, fb0, fa1, fb1, acc, wave, lane, wn, wm);
+        for (int kt = 0; kt < S.RF; ++kt) k_step<CT, TL>(S, smem, kt, f0a, f0b, f1a, f1b, acc, wave, lane, wn, wm);
         if (S.RF > 0) {
 #pragma unroll
             for (int i = 0; i < FN; ++i)
 #pragma unroll
                 for (int j = 0; j < FM; ++j) acc[i][j] *= p.scale;
         }
-        pipe_run<CT, TL>(S, smem, S.RF * TL::SUB, KT * TL::SUB, fa0, fb0, fa1, fb1, acc, wave, lane, wn, wm);
+        for (int kt = S.RF; kt < KT; ++kt) k_step<CT, TL>(S, smem, kt, f0a, f0b, f1a, f1b, acc, wave, lane, wn, wm);
+        wait_vm<0>();   // the out-of-range loads past the last step still write LDS
     }
 
     // 3. epilogue: lane holds, per 16x16 block, 4 consecutive n for one m
