@@ -155,7 +155,7 @@ int lyc_gemm_tile(int64_t M, int64_t N, int compute_dt, int* tile_n, int* tile_m
  *     Returns LYC_ERR_INVALID_ARG for capacity < 1, LYC_ERR_HIP if the events
  *     cannot be created.
  *   lyc_profile_end(total_ms, launches): wait for the recorded events, write
- *     per kernel kind k (LYC_KERNEL_CAST .. LYC_KERNEL_FIX) the summed
+ *     per kernel kind k (LYC_KERNEL_CAST .. LYC_KERNEL_GEMM) the summed
  *     duration in ms and the launch count into the host arrays
  *     total_ms[LYC_KERNEL_KINDS], launches[LYC_KERNEL_KINDS] (either may be
  *     NULL), free the events, stop recording.
@@ -164,10 +164,9 @@ int lyc_gemm_tile(int64_t M, int64_t N, int compute_dt, int* tile_n, int* tile_m
 enum {
     LYC_KERNEL_CAST = 0,   /* fp32 operand -> 16-bit compute copy */
     LYC_KERNEL_PREP = 1,   /* low-rank factor / W preparation (copies, split, norms) */
-    LYC_KERNEL_HPASS = 2,  /* h = x.down^T and its rounding */
-    LYC_KERNEL_GEMM = 3,   /* the main contraction and epilogue */
-    LYC_KERNEL_FIX = 4,    /* fp64 re-evaluation of guard-marked elements */
-    LYC_KERNEL_KINDS = 5
+    LYC_KERNEL_HPASS = 2,  /* h = x.down^T, its rounding guard and fp64 re-evaluations */
+    LYC_KERNEL_GEMM = 3,   /* the main contraction and epilogue (plain affine: the exactly rounded projection) */
+    LYC_KERNEL_KINDS = 4
 };
 int lyc_profile_begin(int capacity);
 int lyc_profile_end(double* total_ms, int* launches);

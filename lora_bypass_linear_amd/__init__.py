@@ -145,7 +145,7 @@ def gemm_tile(M: int, N: int, compute_dt: int) -> Tuple[int, int]:
     return tn.value, tm.value
 
 
-KERNELS = ("cast", "prep", "hpass", "gemm", "fix")
+KERNELS = ("cast", "prep", "hpass", "gemm")
 
 
 def profile_begin(capacity: int) -> None:

@@ -74,8 +74,7 @@ int check_problem(Problem& P) {
 
 struct Layout {
     size_t xc = 0, wc = 0, dc = 0, dh = 0, dl = 0, uc = 0, h = 0, dnorm = 0, wh = 0, wl = 0, wnorm = 0, flagged = 0,
-           bitmap = 0, total = 0;
-    int64_t wpr = 0;   // bitmap words per row
+           total = 0;
     bool cast_x = false, cast_w = false;
 };
 
@@ -98,10 +97,6 @@ Layout layout(const Problem& P) {
         L.h = off; off = align256(off + (size_t)P.M * (size_t)P.r_pad * ce);
         L.dnorm = off; off = align256(off + (size_t)P.r_pad * 2 * sizeof(double));
         L.flagged = off; off = align256(off + sizeof(unsigned));
-        if (split) {
-            L.wpr = (P.r_pad + 31) / 32;
-            L.bitmap = off; off = align256(off + (size_t)P.M * (size_t)L.wpr * 4);
-        }
     }
     if (!P.lora) {
         // the projection's rounding guard: hi/lo split and row norms of W_c, a counter
@@ -111,10 +106,6 @@ Layout layout(const Problem& P) {
         }
         L.wnorm = off; off = align256(off + (size_t)P.N * 2 * sizeof(double));
         L.flagged = off; off = align256(off + sizeof(unsigned));
-        if (split) {
-            L.wpr = (P.N + 31) / 32;
-            L.bitmap = off; off = align256(off + (size_t)P.M * (size_t)L.wpr * 4);
-        }
     }
     L.total = off;
     return L;
@@ -194,10 +185,8 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
         double2* wn = (double2*)(W + L.wnorm);
         unsigned* fl = (unsigned*)(W + L.flagged);
         const bool split = P.c_dt != LYC_F32;
-        uint32_t* bm = (uint32_t*)(W + L.bitmap);
-        const int64_t nbm = guard ? P.M * L.wpr : 0;
         if (split && timed(LYC_KERNEL_PREP, s, [&] {
-                return lyc::launch_rownorm(wa, P.c_dt, P.N, P.K, W + L.wh, W + L.wl, wn, fl, bm, nbm, s);
+                return lyc::launch_rownorm(wa, P.c_dt, P.N, P.K, W + L.wh, W + L.wl, wn, fl, s);
             }) != hipSuccess)
             return LYC_ERR_HIP;
         lyc::XrParams xp{};
@@ -211,8 +200,6 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
         xp.K = P.K;
         xp.guard = guard ? 1 : 0;
         xp.flagged = fl;
-        xp.bitmap = bm;
-        xp.words_per_row = L.wpr;
         xp.mode = lyc::XR_AFFINE;
         xp.out = y;
         xp.ld_out = P.N;
@@ -221,8 +208,6 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
         xp.bias_dt = P.b_dt;
         xp.vec_store = (P.N % 4 == 0) && aligned(y, y_dt == LYC_F32 ? 16 : 8);
         if (timed(LYC_KERNEL_GEMM, s, [&] { return lyc::launch_xr(P.c_dt, xp, s); }) != hipSuccess) return LYC_ERR_HIP;
-        if (guard && timed(LYC_KERNEL_FIX, s, [&] { return lyc::launch_xr_fix(P.c_dt, xp, s); }) != hipSuccess)
-            return LYC_ERR_HIP;
         return LYC_OK;
     }
 
@@ -258,8 +243,6 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
         pp.rank = P.rank;
         pp.r_pad = P.r_pad;
         pp.c_dt = P.c_dt;
-        pp.zero = (uint32_t*)(W + L.bitmap);
-        pp.nzero = L.bitmap ? P.M * L.wpr : 0;
         if (timed(LYC_KERNEL_PREP, s, [&] { return lyc::launch_prep(pp, s); }) != hipSuccess) return LYC_ERR_HIP;
 
         lyc::XrParams hp{};
@@ -274,14 +257,10 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
         hp.K = P.K;
         hp.guard = P.c_dt != LYC_F32 ? 1 : 0;
         hp.flagged = (unsigned*)(W + L.flagged);
-        hp.bitmap = (uint32_t*)(W + L.bitmap);
-        hp.words_per_row = L.wpr;
         hp.mode = lyc::XR_H;
         hp.out = W + L.h;
         hp.ld_out = P.r_pad;
         if (timed(LYC_KERNEL_HPASS, s, [&] { return lyc::launch_xr(P.c_dt, hp, s); }) != hipSuccess)
-            return LYC_ERR_HIP;
-        if (split && timed(LYC_KERNEL_FIX, s, [&] { return lyc::launch_xr_fix(P.c_dt, hp, s); }) != hipSuccess)
             return LYC_ERR_HIP;
 
         g.af = W + L.uc;
@@ -376,8 +355,8 @@ int lyc_profile_begin(int capacity) {
 
 int lyc_profile_end(double* total_ms, int* launches) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    double t[LYC_KERNEL_KINDS] = {0, 0, 0, 0, 0};
-    int n[LYC_KERNEL_KINDS] = {0, 0, 0, 0, 0};
+    double t[LYC_KERNEL_KINDS] = {};
+    int n[LYC_KERNEL_KINDS] = {};
     int st = LYC_OK;
     for (size_t i = 0; i < g_prof_used; ++i) {
         float ms = 0.f;

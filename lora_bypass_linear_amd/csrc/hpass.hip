@@ -29,10 +29,11 @@
 // with |x_m| and |x_lo,m| summed per block in fp32 after scaling by the
 // block's grid (so tiny values cannot underflow the bound away).
 // When [h - E, h + E] straddles a rounding boundary of the 16-bit format, the
-// element is marked in a bitmap; a second kernel re-evaluates every marked
-// element as an fp64 dot product over K (products exact) and overwrites its
-// output.  fp32 compute, or an fp32 rounding target, needs
-// no guard: a flip there moves the result by 2^-24 relative.
+// element is re-evaluated by its wave before the outputs are written: the
+// wave computes the dot product of the x row and the b row in fp64 (products
+// exact) with all 64 lanes and replaces the accumulator.  fp32 compute, or an
+// fp32 rounding target, needs no guard: a flip there moves the result by
+// 2^-24 relative.
 //
 // Work split: a workgroup of 4 waves owns RW*16 rows and RP = 16*JB columns;
 // its waves form RW row groups x KS k groups (k group g takes the blocks
@@ -145,6 +146,138 @@ __device__ __forceinline__ float affine_value(double acc, int out_dt) {
     return bf16_to_f32(round16<CT>(acc));
 }
 
+// fp64 dot product of two K-contiguous rows (exact products), computed by the
+// whole wave: lane l takes the 16-byte chunks l, l+64, ...; loads are issued
+// in batches of 8 chunks per row per lane so that each batch costs one memory
+// round trip.  Every lane gets the sum.
+template <class CT>
+__device__ __forceinline__ double wave_dot(const i32x4* xrow, const i32x4* brow, uint32_t nch, int lane) {
+    constexpr int B = 8;
+    double s0 = 0.0, s1 = 0.0;
+    for (uint32_t c0 = (uint32_t)lane; c0 < nch; c0 += 64 * B) {
+        i32x4 xv[B], bv[B];
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+            const uint32_t c = c0 + 64u * i;
+            xv[i] = c < nch ? xrow[c] : i32x4{0, 0, 0, 0};
+            bv[i] = c < nch ? brow[c] : i32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < B; i += 2) {
+            s0 += dot16_f64<CT>(xv[i], bv[i]);
+            s1 += dot16_f64<CT>(xv[i + 1], bv[i + 1]);
+        }
+    }
+    double part = s0 + s1;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+    return part;
+}
+
+// Epilogue of one wave's accumulators: rounding guard (flagged elements are
+// appended to the workgroup's work list), then h_r or the affine output.
+template <class CT, int JB>
+__device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB][4], double xm2, double xl2, bool wide,
+                                            int64_t wg_m0, int64_t j0, int my_row, int c0, int cols_wg, int lane,
+                                            unsigned* lcount, uint32_t* list) {
+    constexpr bool SPLIT = CT::dt != DT_F32;
+    const int64_t m = wg_m0 + my_row;
+    const bool row_ok = m < p.M;
+
+    // guard: flag the elements whose error interval straddles a rounding
+    // boundary (bit jb*4+e of `flags`); they are re-evaluated after the
+    // outputs are written, so the accumulators are only ever indexed statically
+    uint32_t flags = 0;
+    if (SPLIT && p.guard) {
+        const double xn2 = __builtin_sqrt(xm2) * (1.0 + 0x1p-20);
+        const double xln = __builtin_sqrt(xl2) * (1.0 + 0x1p-20);
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int jl = c0 + jb * 16 + 4 * (lane >> 4) + e;
+                const bool col_ok = jl < cols_wg;
+                const double2 bn = col_ok ? p.bnorm[j0 + jl] : double2{0.0, 0.0};  // {|b|, |b_lo|}
+                const double E = (0x1p-24 * GUARD_CROSS * (xn2 * bn.y + xln * (bn.x + bn.y)) + 0x1p-37 * xn2 * bn.x) *
+                                 (1.0 + 0x1p-20);
+                const double h = acc[jb][e];
+                const bool bwide = !(bn.y < 1e300);   // a block of b could not be split
+                const bool flag = row_ok && col_ok && (wide || bwide || round16<CT>(h - E) != round16<CT>(h + E));
+                flags |= flag ? (1u << (jb * 4 + e)) : 0u;
+            }
+        }
+        // guarded elements go to the workgroup's work list
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if ((flags >> (jb * 4 + e)) & 1u) {
+                    const unsigned at = atomicAdd(lcount, 1u);
+                    list[at] = ((uint32_t)my_row << 16) | (uint32_t)(c0 + jb * 16 + 4 * (lane >> 4) + e);
+                }
+            }
+        }
+    }
+
+    if (row_ok) {
+        if (p.mode == XR_H) {
+            // h_r [M][ld_out] in the compute dtype (all RP columns, padding included)
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb) {
+                const int64_t jg = j0 + c0 + jb * 16 + 4 * (lane >> 4);
+                if (CT::dt == DT_F32) {
+                    float* hp = (float*)p.out + m * p.ld_out + jg;
+                    *(f32x4*)hp = f32x4{(float)acc[jb][0], (float)acc[jb][1], (float)acc[jb][2], (float)acc[jb][3]};
+                } else {
+                    uint16_t o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = round16<CT>(acc[jb][e]);
+                    uint16_t* hp = (uint16_t*)p.out + m * p.ld_out + jg;
+                    *(i32x2*)hp = i32x2{(int)(o[0] | ((uint32_t)o[1] << 16)), (int)(o[2] | ((uint32_t)o[3] << 16))};
+                }
+            }
+        } else {
+            // plain affine: y = round_out(round_out(p) + b)
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb) {
+                const int jl0 = c0 + jb * 16 + 4 * (lane >> 4);
+                const int64_t n0 = j0 + jl0;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float bias =
+                        (p.bias != nullptr && jl0 + e < cols_wg) ? load_as_f32(p.bias, p.bias_dt, n0 + e) : 0.f;
+                    v[e] = affine_value<CT>(acc[jb][e], p.out_dt) + bias;
+                }
+                const int64_t base = m * p.ld_out + n0;
+                if (p.out_dt == DT_F32) {
+                    float* y = (float*)p.out;
+                    if (p.vec_store && jl0 + 3 < cols_wg) {
+                        *(f32x4*)(y + base) = f32x4{v[0], v[1], v[2], v[3]};
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (jl0 + e < cols_wg) y[base + e] = v[e];
+                    }
+                } else {
+                    uint16_t o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = p.out_dt == DT_F16 ? f32_to_f16(v[e]) : f32_to_bf16(v[e]);
+                    uint16_t* y = (uint16_t*)p.out;
+                    if (p.vec_store && jl0 + 3 < cols_wg) {
+                        *(i32x2*)(y + base) =
+                            i32x2{(int)(o[0] | ((uint32_t)o[1] << 16)), (int)(o[2] | ((uint32_t)o[3] << 16))};
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (jl0 + e < cols_wg) y[base + e] = o[e];
+                    }
+                }
+            }
+        }
+    }
+}
+
 // LDS pipeline of the contraction: a round stages KS k blocks of 128 bytes,
 // each with its b tile(s) (RP rows; b_hi and b_lo under the split) and its x
 // tile (RW*16 rows), all filled straight from global memory.  The workgroup's
@@ -165,7 +298,7 @@ struct XrStage {
 };
 
 template <class CT, int JB, int KS, int CG>
-__global__ __launch_bounds__(256 * CG, CG == 1 ? 2 : 1) void xr_kernel(XrParams p) {
+__global__ __launch_bounds__(256 * CG) __attribute__((amdgpu_num_vgpr(256))) void xr_kernel(XrParams p) {
     constexpr bool SPLIT = CT::dt != DT_F32;     // 16-bit compute: hi/lo split and guard
     using ST = XrStage<JB, KS, CG, SPLIT>;
     constexpr int NB = ST::NB, RW = ST::RW, RP = ST::RP, TILE = ST::TILE, NS = ST::NS, Q = ST::Q, NW = ST::NW;
@@ -313,6 +446,15 @@ __global__ __launch_bounds__(256 * CG, CG == 1 ? 2 : 1) void xr_kernel(XrParams 
 #undef LYC_ISSUE_ROUND
     __syncthreads();   // every wave is done with the stages (they hold the k-group reduction next)
 
+    // LDS after the main loop: [k-group reduction][count][work list of guarded elements]
+    constexpr int W = JB * 4 + 3;
+    constexpr int RED = KS > 1 ? (KS - 1) * CG * RW * 64 * W * 8 : 0;
+    constexpr int CAP = RW * 16 * RP;                      // every element of the workgroup
+    static_assert(RED + 16 + CAP * 4 <= NS * ST::BYTES, "reduction buffer and work list");
+    unsigned* lcount = (unsigned*)(sd + RED);
+    uint32_t* list = (uint32_t*)(sd + RED + 16);
+    if (tid == 0) *lcount = 0u;
+
     // row sums: the four lane groups of a row hold disjoint k
     xm2 += __shfl_xor(xm2, 16);
     xm2 += __shfl_xor(xm2, 32);
@@ -320,8 +462,6 @@ __global__ __launch_bounds__(256 * CG, CG == 1 ? 2 : 1) void xr_kernel(XrParams 
     xl2 += __shfl_xor(xl2, 32);
     // meet the k groups' partial sums in LDS (the B tiles are no longer needed)
     if (KS > 1) {
-        constexpr int W = JB * 4 + 3;
-        static_assert((KS - 1) * CG * RW * 64 * W * 8 <= NS * ST::BYTES, "reduction buffer");
         double* red = (double*)sd;                 // [KS-1][CG][RW][64 lanes][W]
         if (kg > 0) {
             double* dst = red + ((size_t)(((kg - 1) * CG + cg) * RW + rg) * 64 + lane) * W;
@@ -333,184 +473,51 @@ __global__ __launch_bounds__(256 * CG, CG == 1 ? 2 : 1) void xr_kernel(XrParams 
             dst[JB * 4 + 1] = xl2;
             dst[JB * 4 + 2] = wide ? 1.0 : 0.0;
         }
-        __syncthreads();
-        if (kg > 0) return;
-        for (int g2 = 1; g2 < KS; ++g2) {
-            const double* src = red + ((size_t)(((g2 - 1) * CG + cg) * RW + rg) * 64 + lane) * W;
-#pragma unroll
-            for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[jb][e] += src[jb * 4 + e];
-            xm2 += src[JB * 4];
-            xl2 += src[JB * 4 + 1];
-            wide |= src[JB * 4 + 2] != 0.0;
-        }
     }
-    const int64_t m = wg_m0 + my_row;
-    const bool row_ok = m < p.M;
-
-    // guard: flag the elements whose error interval straddles a rounding
-    // boundary (bit jb*4+e of `flags`); they are re-evaluated after the
-    // outputs are written, so the accumulators are only ever indexed statically
-    uint32_t flags = 0;
+    __syncthreads();   // partial sums and the cleared count are visible
+    if (kg == 0) {
+        if (KS > 1) {
+            const double* red = (const double*)sd;
+            for (int g2 = 1; g2 < KS; ++g2) {
+                const double* src = red + ((size_t)(((g2 - 1) * CG + cg) * RW + rg) * 64 + lane) * W;
+#pragma unroll
+                for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[jb][e] += src[jb * 4 + e];
+                xm2 += src[JB * 4];
+                xl2 += src[JB * 4 + 1];
+                wide |= src[JB * 4 + 2] != 0.0;
+            }
+        }
+        xr_epilogue<CT, JB>(p, acc, xm2, xl2, wide, wg_m0, j0, my_row, c0, cols_wg, lane, lcount, list);
+    }
+    // The guarded elements: every wave takes its share of the list and
+    // overwrites the stored output with the value rounded from the fp64 dot
+    // product.  The barrier's release makes the first stores complete before.
+    __syncthreads();
     if (SPLIT && p.guard) {
-        const double xn2 = __builtin_sqrt(xm2) * (1.0 + 0x1p-20);
-        const double xln = __builtin_sqrt(xl2) * (1.0 + 0x1p-20);
-#pragma unroll
-        for (int jb = 0; jb < JB; ++jb) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int jl = c0 + jb * 16 + 4 * (lane >> 4) + e;
-                const bool col_ok = jl < cols_wg;
-                const double2 bn = col_ok ? p.bnorm[j0 + jl] : double2{0.0, 0.0};  // {|b|, |b_lo|}
-                const double E = (0x1p-24 * GUARD_CROSS * (xn2 * bn.y + xln * (bn.x + bn.y)) + 0x1p-37 * xn2 * bn.x) *
-                                 (1.0 + 0x1p-20);
-                const double h = acc[jb][e];
-                const bool bwide = !(bn.y < 1e300);   // a block of b could not be split
-                const bool flag = row_ok && col_ok && (wide || bwide || round16<CT>(h - E) != round16<CT>(h + E));
-                flags |= flag ? (1u << (jb * 4 + e)) : 0u;
-            }
-        }
-    }
-
-    if (row_ok) {
-        if (p.mode == XR_H) {
-            // h_r [M][ld_out] in the compute dtype (all RP columns, padding included)
-#pragma unroll
-            for (int jb = 0; jb < JB; ++jb) {
-                const int64_t jg = j0 + c0 + jb * 16 + 4 * (lane >> 4);
-                if (CT::dt == DT_F32) {
-                    float* hp = (float*)p.out + m * p.ld_out + jg;
-                    *(f32x4*)hp = f32x4{(float)acc[jb][0], (float)acc[jb][1], (float)acc[jb][2], (float)acc[jb][3]};
-                } else {
-                    uint16_t o[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) o[e] = round16<CT>(acc[jb][e]);
-                    uint16_t* hp = (uint16_t*)p.out + m * p.ld_out + jg;
-                    *(i32x2*)hp = i32x2{(int)(o[0] | ((uint32_t)o[1] << 16)), (int)(o[2] | ((uint32_t)o[3] << 16))};
-                }
-            }
-        } else {
-            // plain affine: y = round_out(round_out(p) + b)
-#pragma unroll
-            for (int jb = 0; jb < JB; ++jb) {
-                const int jl0 = c0 + jb * 16 + 4 * (lane >> 4);
-                const int64_t n0 = j0 + jl0;
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float bias =
-                        (p.bias != nullptr && jl0 + e < cols_wg) ? load_as_f32(p.bias, p.bias_dt, n0 + e) : 0.f;
-                    v[e] = affine_value<CT>(acc[jb][e], p.out_dt) + bias;
-                }
-                const int64_t base = m * p.ld_out + n0;
-                if (p.out_dt == DT_F32) {
-                    float* y = (float*)p.out;
-                    if (p.vec_store && jl0 + 3 < cols_wg) {
-                        *(f32x4*)(y + base) = f32x4{v[0], v[1], v[2], v[3]};
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (jl0 + e < cols_wg) y[base + e] = v[e];
-                    }
-                } else {
-                    uint16_t o[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) o[e] = p.out_dt == DT_F16 ? f32_to_f16(v[e]) : f32_to_bf16(v[e]);
-                    uint16_t* y = (uint16_t*)p.out;
-                    if (p.vec_store && jl0 + 3 < cols_wg) {
-                        *(i32x2*)(y + base) =
-                            i32x2{(int)(o[0] | ((uint32_t)o[1] << 16)), (int)(o[2] | ((uint32_t)o[3] << 16))};
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (jl0 + e < cols_wg) y[base + e] = o[e];
-                    }
-                }
-            }
-        }
-    }
-
-    if (SPLIT && p.guard) {
-        // mark the flagged elements for the fp64 re-evaluation kernel
-        if (flags) {
-            uint32_t* row = p.bitmap + m * p.words_per_row;
-            for (uint32_t f = flags; f; f &= f - 1) {
-                const int bit = __builtin_ctz(f);
-                const int64_t j = j0 + c0 + (bit >> 2) * 16 + 4 * (lane >> 4) + (bit & 3);
-                atomicOr(&row[j >> 5], 1u << (j & 31));
-            }
-        }
-        const unsigned nflag = (unsigned)__builtin_popcount(flags);
-        unsigned tot = nflag;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) tot += (unsigned)__shfl_xor((int)tot, o);
-        if (lane == 0 && tot) atomicAdd(p.flagged, tot);
-    }
-}
-
-// Re-evaluation of marked elements: one wave per bitmap word (32 columns of
-// one row); for every marked element the wave computes the dot product of x
-// row m and b row j in fp64 (products exact) with all 64 lanes, rounds it and
-// writes the output as the contraction's epilogue would.  Marked elements are
-// rare and scattered, so spreading words over many waves hides the latency of
-// the row reads.
-template <class CT>
-__global__ __launch_bounds__(256) void xr_fix_kernel(XrParams p) {
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t nwaves = (int64_t)gridDim.x * 4;
-    const int64_t total = p.M * p.words_per_row;
-    const uint32_t kbytes = (uint32_t)(p.K * CT::es);
-    const uint32_t nch = kbytes / 16;
-    for (int64_t w = (int64_t)blockIdx.x * 4 + wave; w < total; w += nwaves) {
-        uint32_t bits = (uint32_t)__builtin_amdgcn_readfirstlane((int)p.bitmap[w]);
-        if (!bits) continue;
-        const int64_t m = w / p.words_per_row;
-        const int64_t jbase = (w - m * p.words_per_row) * 32;
-        const i32x4* xrow = (const i32x4*)((const char*)p.x + m * kbytes);
-        while (bits) {
-            const int b = __builtin_ctz(bits);
-            bits &= bits - 1;
-            const int64_t j = jbase + b;
-            const i32x4* brow = (const i32x4*)((const char*)p.b_full + j * kbytes);
-            double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-            uint32_t c = lane;
-            for (; c + 192 < nch; c += 256) {
-                const i32x4 x0 = xrow[c], x1 = xrow[c + 64], x2 = xrow[c + 128], x3 = xrow[c + 192];
-                const i32x4 b0 = brow[c], b1 = brow[c + 64], b2 = brow[c + 128], b3 = brow[c + 192];
-                s0 += dot16_f64<CT>(x0, b0);
-                s1 += dot16_f64<CT>(x1, b1);
-                s2 += dot16_f64<CT>(x2, b2);
-                s3 += dot16_f64<CT>(x3, b3);
-            }
-            for (; c < nch; c += 64) s0 += dot16_f64<CT>(xrow[c], brow[c]);
-            double part = (s0 + s1) + (s2 + s3);
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+        const unsigned n = *lcount;
+        const uint32_t nch = kbytes / 16;
+        const i32x4* xbase = (const i32x4*)((const char*)p.x + wg_m0 * kbytes);
+        const i32x4* bbase = (const i32x4*)((const char*)p.b_full + j0 * kbytes);
+        for (unsigned i = (unsigned)wave; i < n; i += (unsigned)ST::NW) {
+            const uint32_t ent = list[i];
+            const int row = (int)(ent >> 16), col = (int)(ent & 0xffffu);
+            const double d = wave_dot<CT>(xbase + (size_t)row * nch, bbase + (size_t)col * nch, nch, lane);
             if (lane == 0) {
+                const int64_t m = wg_m0 + row, j = j0 + col;
                 if (p.mode == XR_H) {
-                    ((uint16_t*)p.out)[m * p.ld_out + j] = round16<CT>(part);
+                    ((uint16_t*)p.out)[m * p.ld_out + j] = round16<CT>(d);
                 } else {
                     const float bias = p.bias != nullptr ? load_as_f32(p.bias, p.bias_dt, j) : 0.f;
-                    const float v = affine_value<CT>(part, p.out_dt) + bias;
+                    const float v = affine_value<CT>(d, p.out_dt) + bias;
                     // the guard runs for 16-bit outputs only
                     ((uint16_t*)p.out)[m * p.ld_out + j] = p.out_dt == DT_F16 ? f32_to_f16(v) : f32_to_bf16(v);
                 }
             }
         }
+        if (tid == 0 && n) atomicAdd(p.flagged, n);
     }
-}
-
-hipError_t launch_xr_fix(int c_dt, const XrParams& p, hipStream_t s) {
-    const int64_t total = p.M * p.words_per_row;
-    int64_t blocks = (total + 3) / 4;   // one wave per word, up to 16384 waves
-    if (blocks > 4096) blocks = 4096;
-    if (blocks < 1) blocks = 1;
-    if (c_dt == DT_F16) hipLaunchKernelGGL(xr_fix_kernel<CF16>, dim3((unsigned)blocks), dim3(256), 0, s, p);
-    else if (c_dt == DT_BF16) hipLaunchKernelGGL(xr_fix_kernel<CBF16>, dim3((unsigned)blocks), dim3(256), 0, s, p);
-    else return hipErrorInvalidValue;
-    return hipGetLastError();
 }
 
 template <class CT, int JB, int KS, int CG>

@@ -25,8 +25,9 @@ struct GemmParams {
 };
 
 // Exact-rounding contraction (h pass and plain affine projection):
-// C = x_c . b^T with fp64-folded MFMA steps, a rounding guard and fp64
-// re-evaluation, then either h_r = round_c(C) or y = round_out(round_out(C) + b).
+// C = x_c . b^T with fp64-folded MFMA steps, a rounding guard and in-kernel
+// fp64 re-evaluation of the guarded elements, then either h_r = round_c(C) or
+// y = round_out(round_out(C) + b).
 enum { XR_H = 0, XR_AFFINE = 1 };
 struct XrParams {
     const void* x;          // [M,K] compute dtype
@@ -36,9 +37,7 @@ struct XrParams {
     const double2* bnorm;   // [Nc] {|b_j|_2, |b_lo,j|_2}
     int64_t M, Nc, K;
     int guard;              // 1: apply the rounding guard (16-bit rounding target)
-    unsigned* flagged;      // count of re-evaluated elements
-    uint32_t* bitmap;       // [M][words_per_row] bits of the elements to re-evaluate (zeroed beforehand)
-    int64_t words_per_row;  // ceil(Nc / 32)
+    unsigned* flagged;      // count of re-evaluated elements (zeroed beforehand)
     int mode;               // XR_H or XR_AFFINE
     void* out;              // h [M][ld_out] (compute dtype) or y [M][ld_out] (out_dt)
     int64_t ld_out;
@@ -61,8 +60,6 @@ struct PrepParams {
     void* dl;   // lo part
     void* uc;
     double2* dnorm;   // {|down_c,j|, |lo_j|}
-    uint32_t* zero;   // words to clear (the re-evaluation bitmap)
-    int64_t nzero;
     unsigned* flagged;
     int64_t N, K, rank;
     int r_pad;
@@ -73,13 +70,10 @@ hipError_t launch_gemm(int c_dt, const GemmParams& p, hipStream_t s);
 // the output tile launch_gemm uses for this shape
 void gemm_tile_shape(int64_t M, int64_t N, int c_dt, int* tn, int* tm);
 hipError_t launch_xr(int c_dt, const XrParams& p, hipStream_t s);
-// re-evaluate in fp64 the elements the contraction marked in p.bitmap, and
-// overwrite their outputs
-hipError_t launch_xr_fix(int c_dt, const XrParams& p, hipStream_t s);
 // hi/lo split (per 64-k block) of each row of b [rows,K] (16-bit compute
 // dtype) and {|b_j|_2, |b_lo,j|_2}; also clears *flagged (if not null)
 hipError_t launch_rownorm(const void* b, int c_dt, int64_t rows, int64_t K, void* b_hi, void* b_lo, double2* out,
-                          unsigned* flagged, uint32_t* zero, int64_t nzero, hipStream_t s);
+                          unsigned* flagged, hipStream_t s);
 hipError_t launch_prep(const PrepParams& p, hipStream_t s);
 // fp32 [n] -> 16-bit compute dtype [n], round to nearest even
 hipError_t launch_cast(const float* src, void* dst, int64_t n, int c_dt, hipStream_t s);

@@ -111,7 +111,6 @@ __device__ void row_pass(const void* src, int src_dt, int c_dt, int64_t row, int
 __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
     const int b = blockIdx.x, tid = threadIdx.x;
     if (b == 0 && tid == 0) *p.flagged = 0u;
-    for (int64_t i = (int64_t)b * 256 + tid; i < p.nzero; i += (int64_t)gridDim.x * 256) p.zero[i] = 0u;
     if (b < p.r_pad) {
         const bool split = p.c_dt != DT_F32;
         row_pass(p.down, p.down_dt, p.c_dt, b, p.K, b >= p.rank, p.dc, split ? p.dh : nullptr,
@@ -132,16 +131,14 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
 // split and norms of the rows of an operand already in the 16-bit compute
 // dtype; clears *flagged
 __global__ __launch_bounds__(256) void rownorm_kernel(const void* b, int c_dt, int64_t K, void* b_hi, void* b_lo,
-                                                      double2* out, unsigned* flagged, uint32_t* zero, int64_t nzero) {
+                                                      double2* out, unsigned* flagged) {
     if (blockIdx.x == 0 && threadIdx.x == 0 && flagged) *flagged = 0u;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nzero; i += (int64_t)gridDim.x * 256) zero[i] = 0u;
     row_pass(b, c_dt, c_dt, blockIdx.x, K, false, nullptr, b_hi, b_lo, &out[blockIdx.x]);
 }
 
 hipError_t launch_rownorm(const void* b, int c_dt, int64_t rows, int64_t K, void* b_hi, void* b_lo, double2* out,
-                          unsigned* flagged, uint32_t* zero, int64_t nzero, hipStream_t s) {
-    hipLaunchKernelGGL(rownorm_kernel, dim3((unsigned)rows), dim3(256), 0, s, b, c_dt, K, b_hi, b_lo, out, flagged, zero,
-                       nzero);
+                          unsigned* flagged, hipStream_t s) {
+    hipLaunchKernelGGL(rownorm_kernel, dim3((unsigned)rows), dim3(256), 0, s, b, c_dt, K, b_hi, b_lo, out, flagged);
     return hipGetLastError();
 }
 
