@@ -243,6 +243,7 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
         pp.rank = P.rank;
         pp.r_pad = P.r_pad;
         pp.c_dt = P.c_dt;
+        pp.vec = aligned(down, 16) ? 1 : 0;
         if (timed(LYC_KERNEL_PREP, s, [&] { return lyc::launch_prep(pp, s); }) != hipSuccess) return LYC_ERR_HIP;
 
         lyc::XrParams hp{};

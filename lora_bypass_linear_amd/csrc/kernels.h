@@ -60,6 +60,7 @@ struct PrepParams {
     void* dl;   // lo part
     void* uc;
     double2* dnorm;   // {|down_c,j|, |lo_j|}
+    int vec;          // down rows start 16-byte aligned: vector loads
     unsigned* flagged;
     int64_t N, K, rank;
     int r_pad;

@@ -46,27 +46,64 @@ __device__ __forceinline__ void store16(void* dst, int64_t i, float v, int c_dt)
 // contraction applies to x); returns {|v|_2, |lo|_2}.  A block whose grid
 // exponent exceeds 100 cannot be split with the fp32 rounding constant: |lo|_2
 // is then reported as +inf, which makes the contraction re-evaluate that row's
-// elements in fp64.
-__device__ void row_pass(const void* src, int src_dt, int c_dt, int64_t row, int64_t K, bool zero, void* dst,
-                         void* dst_hi, void* dst_lo, double2* norm_out) {
-    __shared__ double red[2][256];
-    const int tid = threadIdx.x;
+// elements in fp64.  With `vec` the source row is read, and the outputs
+// written, 16 bytes at a time (rows start 16-byte aligned and K % 8 == 0).
+__device__ void row_pass(const void* src, int src_dt, int c_dt, int64_t row, int64_t K, bool zero, bool vec,
+                         void* dst, void* dst_hi, void* dst_lo, double2* norm_out) {
+    __shared__ double red[2][4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     double ss = 0.0, ll = 0.0;
     bool wide = false;
     for (int64_t k0 = 0; k0 < K; k0 += 2048) {
         const int64_t kt = k0 + 8 * tid;
+        const bool in = kt < K;   // K % 8 == 0: a thread's 8 elements are all in or all out
         float c[8];
+        if (vec && in && !zero) {
+            if (src_dt == DT_F32) {
+                const f32x4 a = *(const f32x4*)((const float*)src + row * K + kt);
+                const f32x4 b = *(const f32x4*)((const float*)src + row * K + kt + 4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { c[i] = a[i]; c[i + 4] = b[i]; }
+            } else {
+                const i32x4 v = *(const i32x4*)((const uint16_t*)src + row * K + kt);
+                const i32x4 w = v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t u = (uint32_t)w[i];
+                    c[2 * i] = src_dt == DT_F16 ? f16_to_f32((uint16_t)u) : bf16_to_f32((uint16_t)u);
+                    c[2 * i + 1] = src_dt == DT_F16 ? f16_to_f32((uint16_t)(u >> 16)) : bf16_to_f32((uint16_t)(u >> 16));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) c[i] = (in && !zero) ? load_as_f32(src, src_dt, row * K + kt + i) : 0.f;
+        }
+        // round to the compute dtype (exact when the stored dtype is the compute dtype)
+        uint16_t h16[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (c_dt == DT_F16) { h16[i] = f32_to_f16(c[i]); c[i] = f16_to_f32(h16[i]); }
+            else if (c_dt == DT_BF16) { h16[i] = f32_to_bf16(c[i]); c[i] = bf16_to_f32(h16[i]); }
+        }
+        if (dst && in) {
+            if (c_dt == DT_F32) {
+                float* d = (float*)dst + row * K + kt;
+                if (vec) {
+                    *(f32x4*)d = f32x4{c[0], c[1], c[2], c[3]};
+                    *(f32x4*)(d + 4) = f32x4{c[4], c[5], c[6], c[7]};
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) d[i] = c[i];
+                }
+            } else {
+                *(i32x4*)((uint16_t*)dst + row * K + kt) =
+                    i32x4{(int)(h16[0] | ((uint32_t)h16[1] << 16)), (int)(h16[2] | ((uint32_t)h16[3] << 16)),
+                          (int)(h16[4] | ((uint32_t)h16[5] << 16)), (int)(h16[6] | ((uint32_t)h16[7] << 16))};
+            }
+        }
         float mx = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            c[i] = 0.f;
-            if (kt + i < K) {
-                const float v = zero ? 0.f : load_as_f32(src, src_dt, row * K + kt + i);
-                double cd;
-                if (dst) store_c(dst, row * K + kt + i, v, c_dt, &cd);
-                else cd = (double)v;
-                c[i] = (float)cd;   // compute-dtype value, exact in fp32
-            }
             ss = __builtin_fma((double)c[i], (double)c[i], ss);
             mx = __builtin_fmaxf(mx, __builtin_fabsf(c[i]));
         }
@@ -81,29 +118,41 @@ __device__ void row_pass(const void* src, int src_dt, int c_dt, int64_t row, int
                 wide |= g > 100;
                 magic = __builtin_ldexpf(1.5f, (g > 100 ? 100 : g) + 23);
             }
+            uint16_t hb[8], lb[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float hi = mx > 0.f ? (c[i] + magic) - magic : 0.f;
                 const float lo = c[i] - hi;
-                if (kt + i < K) {
-                    store16(dst_hi, row * K + kt + i, hi, c_dt);
-                    store16(dst_lo, row * K + kt + i, lo, c_dt);
-                }
+                hb[i] = c_dt == DT_F16 ? f32_to_f16(hi) : f32_to_bf16(hi);
+                lb[i] = c_dt == DT_F16 ? f32_to_f16(lo) : f32_to_bf16(lo);
                 ll = __builtin_fma((double)lo, (double)lo, ll);
+            }
+            if (in) {
+                *(i32x4*)((uint16_t*)dst_hi + row * K + kt) =
+                    i32x4{(int)(hb[0] | ((uint32_t)hb[1] << 16)), (int)(hb[2] | ((uint32_t)hb[3] << 16)),
+                          (int)(hb[4] | ((uint32_t)hb[5] << 16)), (int)(hb[6] | ((uint32_t)hb[7] << 16))};
+                *(i32x4*)((uint16_t*)dst_lo + row * K + kt) =
+                    i32x4{(int)(lb[0] | ((uint32_t)lb[1] << 16)), (int)(lb[2] | ((uint32_t)lb[3] << 16)),
+                          (int)(lb[4] | ((uint32_t)lb[5] << 16)), (int)(lb[6] | ((uint32_t)lb[7] << 16))};
             }
         }
     }
-    red[0][tid] = ss;
-    red[1][tid] = ll + (wide ? __builtin_inf() : 0.0);
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-        if (tid < o) {
-            red[0][tid] += red[0][tid + o];
-            red[1][tid] += red[1][tid + o];
-        }
-        __syncthreads();
+    // row sums: 64 lanes by shuffles, then the 4 waves through LDS
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        ss += __shfl_xor(ss, o);
+        ll += __shfl_xor(ll, o);
     }
-    if (tid == 0) *norm_out = double2{__builtin_sqrt(red[0][0]), __builtin_sqrt(red[1][0])};
+    if (lane == 0) {
+        red[0][wave] = ss;
+        red[1][wave] = ll;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const double s2 = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+        const double l2 = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+        *norm_out = double2{__builtin_sqrt(s2), wide ? __builtin_inf() : __builtin_sqrt(l2)};
+    }
 }
 
 // blocks [0, r_pad): one row of down each (+ its split and norms); the rest:
@@ -113,7 +162,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
     if (b == 0 && tid == 0) *p.flagged = 0u;
     if (b < p.r_pad) {
         const bool split = p.c_dt != DT_F32;
-        row_pass(p.down, p.down_dt, p.c_dt, b, p.K, b >= p.rank, p.dc, split ? p.dh : nullptr,
+        row_pass(p.down, p.down_dt, p.c_dt, b, p.K, b >= p.rank, p.vec, p.dc, split ? p.dh : nullptr,
                  split ? p.dl : nullptr, &p.dnorm[b]);
     } else {
         const int64_t total = p.N * (int64_t)p.r_pad;
@@ -133,7 +182,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
 __global__ __launch_bounds__(256) void rownorm_kernel(const void* b, int c_dt, int64_t K, void* b_hi, void* b_lo,
                                                       double2* out, unsigned* flagged) {
     if (blockIdx.x == 0 && threadIdx.x == 0 && flagged) *flagged = 0u;
-    row_pass(b, c_dt, c_dt, blockIdx.x, K, false, nullptr, b_hi, b_lo, &out[blockIdx.x]);
+    row_pass(b, c_dt, c_dt, blockIdx.x, K, false, true, nullptr, b_hi, b_lo, &out[blockIdx.x]);
 }
 
 hipError_t launch_rownorm(const void* b, int c_dt, int64_t rows, int64_t K, void* b_hi, void* b_lo, double2* out,
