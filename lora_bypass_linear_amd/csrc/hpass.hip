@@ -91,24 +91,17 @@ __device__ __forceinline__ int grid_exp(uint32_t m) {
 }
 
 // Split a fragment on the grid 2^g (round to nearest): hi on the grid, lo = v - hi.
-// Adding and subtracting 1.5 * 2^(g+23) rounds an fp32 value of magnitude below
-// 2^(g+22) to a multiple of 2^g.
-// Also accumulates sum (v 2^-g)^2 and sum (lo 2^-g)^2 (scaled by the grid, so
-// nothing underflows that matters; |v 2^-g| <= 2^8).
+// Adding and subtracting magic = 1.5 * 2^(g+23) rounds an fp32 value of
+// magnitude below 2^(g+22) to a multiple of 2^g.
 template <class CT>
-__device__ __forceinline__ void split16(i32x4 v, float magic, int g, i32x4& hi, i32x4& lo, float& sv, float& sl) {
+__device__ __forceinline__ void split16(i32x4 v, float magic, i32x4& hi, i32x4& lo) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t u = (uint32_t)v[i];
         const float a = unpack_lo<CT>(u), b = unpack_hi<CT>(u);
         const float ah = (a + magic) - magic, bh = (b + magic) - magic;
-        const float al = a - ah, bl = b - bh;
         hi[i] = (int)pack2<CT>(ah, bh);
-        lo[i] = (int)pack2<CT>(al, bl);
-        const float as = __builtin_ldexpf(a, -g), bs = __builtin_ldexpf(b, -g);
-        const float ls = __builtin_ldexpf(al, -g), ms = __builtin_ldexpf(bl, -g);
-        sv = __builtin_fmaf(as, as, __builtin_fmaf(bs, bs, sv));
-        sl = __builtin_fmaf(ls, ls, __builtin_fmaf(ms, ms, sl));
+        lo[i] = (int)pack2<CT>(a - ah, b - bh);
     }
 }
 
@@ -323,7 +316,8 @@ __global__ __launch_bounds__(256 * CG) __attribute__((amdgpu_num_vgpr(256))) voi
     for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[jb][e] = 0.0;
-    double xm2 = 0.0, xl2 = 0.0;   // this lane's parts of |x_m|^2 and |x_lo,m|^2
+    double xm2 = 0.0, xl2 = 0.0;   // |x_m|^2 and |x_lo,m|^2 of this lane's row (16-bit compute)
+    f32x4 gx = f32x4{0.f, 0.f, 0.f, 0.f}, gl = f32x4{0.f, 0.f, 0.f, 0.f};   // Gram accumulators
 
     const int KT = (int)((kbytes + 127) / 128);   // k blocks of 128 bytes
     const int ROUNDS = (KT + KS - 1) / KS;
@@ -396,12 +390,15 @@ __global__ __launch_bounds__(256 * CG) __attribute__((amdgpu_num_vgpr(256))) voi
             wide |= (g > 100);
             const float magic = __builtin_ldexpf(1.5f, (g > 100 ? 100 : g) + 23);
             i32x4 xh[2], xlo[2];
-            float sv = 0.f, sl = 0.f;
-            split16<CT>(xr[0], magic, g, xh[0], xlo[0], sv, sl);
-            split16<CT>(xr[1], magic, g, xh[1], xlo[1], sv, sl);
-            // 16 values per lane; 2^-120 per value covers squares that underflowed
-            xm2 += __builtin_ldexp((double)sv + 0x1p-116, 2 * g);
-            xl2 += __builtin_ldexp((double)sl + 0x1p-116, 2 * g);
+            split16<CT>(xr[0], magic, xh[0], xlo[0]);
+            split16<CT>(xr[1], magic, xh[1], xlo[1]);
+            // squared norms of the wave's rows of x and x_lo: the diagonals of
+            // their 16 x 16 Gram matrices, accumulated by the MFMA
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                gx = CT::step(xr[s], xr[s], gx);
+                gl = CT::step(xlo[s], xlo[s], gl);
+            }
             const char* tl = th + TILE;             // this k group's b_lo tile
 #pragma unroll
             for (int jb = 0; jb < JB; ++jb) {
@@ -455,11 +452,21 @@ __global__ __launch_bounds__(256 * CG) __attribute__((amdgpu_num_vgpr(256))) voi
     uint32_t* list = (uint32_t*)(sd + RED + 16);
     if (tid == 0) *lcount = 0u;
 
-    // row sums: the four lane groups of a row hold disjoint k
-    xm2 += __shfl_xor(xm2, 16);
-    xm2 += __shfl_xor(xm2, 32);
-    xl2 += __shfl_xor(xl2, 16);
-    xl2 += __shfl_xor(xl2, 32);
+    if (SPLIT) {
+        // Gram diagonal: row r of the wave sits in lane r + 16 (r >> 2), element
+        // r & 3.  The MFMA steps' error (below STEP * 2^-24 of |accumulator| +
+        // sum|products| per step, every term >= 0, so at most (steps + 1) STEP
+        // 2^-24 relative) is covered by inflating, and products that underflowed
+        // by 2^-120 per step (a step adds 32 squares per element).
+        const int r = lane & 15, e = r & 3;
+        const float dx = e == 0 ? gx[0] : e == 1 ? gx[1] : e == 2 ? gx[2] : gx[3];
+        const float dl = e == 0 ? gl[0] : e == 1 ? gl[1] : e == 2 ? gl[2] : gl[3];
+        const int src = r + 16 * (r >> 2);
+        const double steps = 2.0 * ROUNDS;
+        const double infl = 1.0 + 2.0 * (GUARD_CROSS / 2) * 0x1p-24 * (steps + 1.0) + 0x1p-20;
+        xm2 = (double)__shfl(dx, src) * infl + steps * 0x1p-120;
+        xl2 = (double)__shfl(dl, src) * infl + steps * 0x1p-120;
+    }
     // meet the k groups' partial sums in LDS (the B tiles are no longer needed)
     if (KS > 1) {
         double* red = (double*)sd;                 // [KS-1][CG][RW][64 lanes][W]
