@@ -75,10 +75,11 @@ enum {
 int lyc_resolve_dtypes(const int* operand_dtypes, int n, int* compute, int* output);
 
 /*
- * Workspace bytes lyc_linear_fwd needs for this problem: the row norms of W
- * and a counter used by the projection's rounding guard, plus compute-dtype
- * copies of fp32 operands that feed a 16-bit contraction.  Returns the same
- * argument errors as lyc_linear_fwd.
+ * Workspace bytes lyc_linear_fwd needs for this problem: for 16-bit compute
+ * the hi/lo split of W_c (per 64-k block) and its row norms, used by the
+ * projection's rounding guard, a counter, plus compute-dtype copies of fp32
+ * operands that feed a 16-bit contraction.  Returns the same argument errors
+ * as lyc_linear_fwd.
  */
 int lyc_linear_workspace_size(int64_t M, int64_t N, int64_t K, int x_dt, int w_dt, int bias_dt,
                               size_t* bytes);
@@ -96,10 +97,12 @@ int lyc_linear_fwd(const void* x, int x_dt, const void* w, int w_dt, const void*
 
 /*
  * Workspace bytes lyc_lora_linear_fwd needs.  It holds the rounded h
- * [M, rank padded to 32] in the compute dtype, compute-dtype copies of down
- * and up (rank padded), the row norms of down used by the h guard, a
- * counter, and compute-dtype copies of fp32 x/W when they feed a 16-bit
- * contraction.  Returns the same argument errors as lyc_lora_linear_fwd.
+ * [M, r_pad] in the compute dtype (r_pad: the rank rounded up to 32, 64, 128
+ * or 256), compute-dtype copies of down and up (rank padded with zeros), for
+ * 16-bit compute the hi/lo split of down_c and its row norms used by the h
+ * guard, a counter, and compute-dtype copies of fp32 x/W when they feed a
+ * 16-bit contraction.  Returns the same argument errors as
+ * lyc_lora_linear_fwd.
  */
 int lyc_lora_linear_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt,
                                    int bias_dt, int down_dt, int up_dt, size_t* bytes);
@@ -129,7 +132,7 @@ int lyc_lora_linear_fwd(const void* x, int x_dt, const void* w, int w_dt, const 
  * workspace, for inspection after the call has completed on its stream:
  *   h_offset:  byte offset of h_r, [M][h_ld] in the compute dtype (columns
  *              >= rank are zero);
- *   h_ld:      leading dimension of h_r in elements (rank rounded up to 32);
+ *   h_ld:      leading dimension of h_r in elements (r_pad);
  *   flagged_offset: byte offset of a uint32 count of h elements that the
  *              guard re-evaluated in fp64 during the last call.
  * Any out-pointer may be NULL.  Same argument errors as the size query.
