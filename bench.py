@@ -40,6 +40,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-eager", action="store_true")
+    ap.add_argument("--no-small-m", action="store_true", help="skip the small-M (decode-like) timings")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (HBM counter calibration)")
     args = ap.parse_args()
@@ -149,27 +150,33 @@ def main():
            "instrumented_ms_per_step": round(wall_i * 1e3 / args.steps, 5),
            "input_digest": WL.digest(inputs), "kernels": kernels, "h_guard": guard, "roofline": roofline}
 
+    if not args.no_small_m:
+        out["small_m"] = _small_m(dev)
+
     # accuracy on sampled rows against the fp64 oracle (this is also the CPU-baseline leg)
     if not args.no_cpu_baseline:
         import oracle
         from tests.gpu_cases import oracle_forward, score
 
         y_cpu = y.cpu()
-        try:
-            cores = min(16, len(os.sched_getaffinity(0)))
-        except AttributeError:
-            cores = min(16, os.cpu_count() or 1)
+        cores = oracle.default_threads()
         row_flops = wl.flops / wl.M
         rng = np.random.default_rng(wl.seed)
+        # size the sample from a second, timed probe (the first one pays one-time costs)
+        probe_rows = np.sort(rng.choice(wl.M, size=min(wl.M, 4 * cores), replace=False))
+        oracle_forward(inputs, wl, rows=probe_rows[: cores])
         t1 = time.perf_counter()
-        probe_rows = np.sort(rng.choice(wl.M, size=min(wl.M, 2 * cores), replace=False))
-        oracle.forward(*_oracle_args(inputs, wl), rows=probe_rows, nthreads=cores, lora=lora)
+        oracle_forward(inputs, wl, rows=probe_rows)
         t_probe = time.perf_counter() - t1
-        n_rows = int(min(wl.M, max(cores, probe_rows.size * args.cpu_seconds / max(t_probe, 1e-3))))
+        want_rows = probe_rows.size * args.cpu_seconds / max(t_probe, 1e-3)
+        n_rows = int(min(wl.M, max(cores, want_rows)))
+        # a workload whose every row fits in the budget is passed over whole, several times
+        passes = int(max(1, min(20, round(want_rows / wl.M)))) if n_rows == wl.M else 1
         rows = np.sort(rng.choice(wl.M, size=n_rows, replace=False))
-        print(f"[bench] oracle on {n_rows} rows, {cores} threads", file=sys.stderr, flush=True)
+        print(f"[bench] oracle on {n_rows} rows x {passes}, {cores} threads", file=sys.stderr, flush=True)
         t1 = time.perf_counter()
-        res = oracle_forward(inputs, wl, rows=rows)
+        for _ in range(passes):
+            res = oracle_forward(inputs, wl, rows=rows)
         t_cpu = time.perf_counter() - t1
         s = score(y_cpu, res, rows, wl.K, wl.r)
         out["max_ulp"] = round(s["ulp_max"], 4)
@@ -177,12 +184,60 @@ def main():
         out["tol_fail"] = s["fail"]
         out["tol_checked"] = s["n"]
         out["worst_err_over_tol"] = round(s["worst"], 4)
-        out["cpu_baseline"] = {"value": round(row_flops * n_rows / t_cpu / 1e12, 6), "unit": "TFLOP/s",
+        out["cpu_baseline"] = {"value": round(row_flops * n_rows * passes / t_cpu / 1e12, 6), "unit": "TFLOP/s",
                                "cores": cores, "kind": "oracle",
-                               "sample": f"{n_rows} of {wl.M} output rows (all {wl.N} columns), {t_cpu:.1f} s"}
+                               "sample": f"{n_rows} of {wl.M} output rows (all {wl.N} columns)"
+                                         + (f", {passes} passes" if passes > 1 else "") + f", {t_cpu:.1f} s"}
         if not args.no_eager:
             out["eager_baseline"] = _eager(d, wl, c_dt, o_dt, rows, res, args.steps, score)
     print(json.dumps(out))
+
+
+def _small_m(dev, reps=50):
+    """Few-token calls of config 1's plain affine shape and of the fp16 LoRA
+    shape: wall time per back-to-back call (host launch cost included), the
+    summed device time of the kernels of one call (HIP events), and the
+    algorithmic HBM GB/s and TFLOP/s over that device time."""
+    import torch
+
+    import lora_bypass_linear_amd as L
+    import workloads as WL
+
+    res = []
+    for base in ("affine_f16_1024x768x1024", "lora_f16_4096x3072x3072_r16"):
+        for M in (16, 128):
+            wl = WL.WORKLOADS[base].resized(M=M)
+            d = {k: v.to(dev) for k, v in WL.generate(wl).items()}
+            if wl.kind == "lora":
+                y, ws = L.lora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, d.get("b"), return_workspace=True)
+                call = lambda: L.lora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, d.get("b"), out=y,
+                                             workspace=ws)
+            else:
+                y = L.linear(d["x"], d["w"], d.get("b"))
+                nb = L.linear_workspace_size(wl.M, wl.N, wl.K, L.dtype_code(d["x"]), L.dtype_code(d["w"]),
+                                             L.dtype_code(d["b"]) if "b" in d else 0)
+                ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+                call = lambda: L.linear(d["x"], d["w"], d.get("b"), out=y, workspace=ws)
+            for _ in range(5):
+                call()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                call()
+            torch.cuda.synchronize()
+            wall_us = (time.perf_counter() - t0) * 1e6 / reps
+            L.profile_begin(8 * reps)
+            for _ in range(reps):
+                call()
+            torch.cuda.synchronize()
+            prof = L.profile_end()
+            dev_us = sum(ms for _, ms in prof.values()) * 1e3 / reps
+            res.append({"workload": f"{base} at M={M}", "wall_us_per_call": round(wall_us, 2),
+                        "device_us_per_call": round(dev_us, 2),
+                        "kernels": {k: round(ms * 1e3 / reps, 2) for k, (n, ms) in prof.items() if n},
+                        "hbm_gbs": round(wl.bytes / (dev_us * 1e-6) / 1e9, 1),
+                        "tflops": round(wl.flops / (dev_us * 1e-6) / 1e12, 3)})
+    return res
 
 
 def _oracle_args(inputs, wl):

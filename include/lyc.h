@@ -141,6 +141,17 @@ int lyc_lora_workspace_layout(int64_t M, int64_t N, int64_t K, int64_t rank, int
                               int down_dt, int up_dt, size_t* h_offset, int64_t* h_ld, size_t* flagged_offset);
 
 /*
+ * Where lyc_linear_fwd keeps its guard counter inside the workspace:
+ *   flagged_offset: byte offset of a uint32 count of projection elements that
+ *              the rounding guard re-evaluated in fp64 during the last call
+ *              (16-bit compute; 0 when the output is fp32, which needs no
+ *              guard; not written at all under fp32 compute).
+ * The out-pointer may be NULL.  Same argument errors as the size query.
+ */
+int lyc_linear_workspace_layout(int64_t M, int64_t N, int64_t K, int x_dt, int w_dt, int bias_dt,
+                                size_t* flagged_offset);
+
+/*
  * Output tile (rows of W x rows of x) that the forward calls use for an
  * M x N problem in compute dtype compute_dt; one workgroup computes one tile.
  * Host only.  Returns LYC_ERR_INVALID_ARG for negative sizes or an unknown

@@ -14,7 +14,7 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 __all__ = ["F16", "BF16", "F32", "LycError", "MixedHalfError", "lib", "resolve_dtypes", "linear", "lora_linear",
-           "linear_workspace_size", "lora_workspace_size", "lora_workspace_layout", "gemm_tile", "profile_begin", "profile_end", "dtype_code",
+           "linear_workspace_size", "lora_workspace_size", "lora_workspace_layout", "linear_workspace_layout", "gemm_tile", "profile_begin", "profile_end", "dtype_code",
            "torch_dtype"]
 
 F16, BF16, F32 = 1, 2, 3
@@ -56,6 +56,7 @@ def lib():
                                           ctypes.c_double, c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_sz, c_vp]
         L.lyc_lora_workspace_layout.argtypes = [c_i64, c_i64, c_i64, c_i64, c_int, c_int, c_int, c_int, c_int,
                                                 ctypes.POINTER(c_sz), ctypes.POINTER(c_i64), ctypes.POINTER(c_sz)]
+        L.lyc_linear_workspace_layout.argtypes = [c_i64, c_i64, c_i64, c_int, c_int, c_int, ctypes.POINTER(c_sz)]
         L.lyc_gemm_tile.argtypes = [c_i64, c_i64, c_int, ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
         L.lyc_profile_begin.argtypes = [c_int]
         L.lyc_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_int)]
@@ -63,6 +64,7 @@ def lib():
         L.lyc_status_str.restype = ctypes.c_char_p
         for fn in (L.lyc_resolve_dtypes, L.lyc_linear_workspace_size, L.lyc_linear_fwd,
                    L.lyc_lora_linear_workspace_size, L.lyc_lora_linear_fwd, L.lyc_lora_workspace_layout,
+                   L.lyc_linear_workspace_layout,
                    L.lyc_gemm_tile, L.lyc_profile_begin, L.lyc_profile_end):
             fn.restype = c_int
         _lib = L
@@ -136,6 +138,13 @@ def lora_workspace_layout(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt):
     _check(lib().lyc_lora_workspace_layout(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt, ctypes.byref(ho),
                                            ctypes.byref(ld), ctypes.byref(fo)))
     return ho.value, ld.value, fo.value
+
+
+def linear_workspace_layout(M, N, K, x_dt, w_dt, b_dt=0) -> int:
+    """flagged_offset: the guard counter inside the plain affine workspace."""
+    fo = ctypes.c_size_t(0)
+    _check(lib().lyc_linear_workspace_layout(M, N, K, x_dt, w_dt, b_dt, ctypes.byref(fo)))
+    return fo.value
 
 
 def gemm_tile(M: int, N: int, compute_dt: int) -> Tuple[int, int]:

@@ -68,7 +68,7 @@ int check_problem(Problem& P) {
     if (P.K % 8 != 0) return LYC_ERR_UNSUPPORTED;
     if (P.rank > MAX_RANK) return LYC_ERR_UNSUPPORTED;
     if (!P.lora) P.rank = 0;
-    P.r_pad = P.rank == 0 ? 0 : (P.rank <= 32 ? 32 : P.rank <= 64 ? 64 : P.rank <= 128 ? 128 : 256);
+    P.r_pad = P.rank == 0 ? 0 : (P.rank <= 16 && P.c_dt != LYC_F32) ? 16 : (P.rank <= 32 ? 32 : P.rank <= 64 ? 64 : P.rank <= 128 ? 128 : 256);
     return LYC_OK;
 }
 
@@ -328,6 +328,15 @@ int lyc_lora_workspace_layout(int64_t M, int64_t N, int64_t K, int64_t rank, int
     if (h_offset) *h_offset = L.h;
     if (h_ld) *h_ld = P.r_pad;
     if (flagged_offset) *flagged_offset = L.flagged;
+    return LYC_OK;
+}
+
+int lyc_linear_workspace_layout(int64_t M, int64_t N, int64_t K, int x_dt, int w_dt, int bias_dt,
+                                size_t* flagged_offset) {
+    Problem P{false, M, N, K, 0, x_dt, w_dt, bias_dt, 0, 0, 0, 0, 0};
+    const int st = check_problem(P);
+    if (st != LYC_OK) return st;
+    if (flagged_offset) *flagged_offset = layout(P).flagged;
     return LYC_OK;
 }
 

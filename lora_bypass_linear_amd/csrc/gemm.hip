@@ -281,14 +281,19 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
         wait_vm<0>();   // the out-of-range loads past the last step still write LDS
     }
 
-    // 3. epilogue: lane holds, per 16x16 block, 4 consecutive n for one m
+    // 3. epilogue: lane holds, per 16x16 block, 4 consecutive n for one m.
+    //    The bias of every block is loaded before the first store.
+    float biasv[FN * 4] = {};
+    if (p.bias != nullptr) {
+        int64_t idx[FN * 4];
+#pragma unroll
+        for (int i = 0; i < FN * 4; ++i) idx[i] = n0 + wn * TL::WN + (i >> 2) * 16 + 4 * (lane >> 4) + (i & 3);
+        load_n_as_f32<FN * 4>(p.bias, p.bias_dt, idx, p.N, biasv);
+    }
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
         const int64_t nb = n0 + wn * TL::WN + i * 16 + 4 * (lane >> 4);
-        float bias[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            bias[e] = (p.bias != nullptr && nb + e < p.N) ? load_as_f32(p.bias, p.bias_dt, nb + e) : 0.f;
+        const float* bias = biasv + 4 * i;
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
             const int64_t m = m0 + wm * TL::WM + j * 16 + (lane & 15);

@@ -26,21 +26,28 @@
 // a step therefore errs by less than 36 * 2^-24 * S_cross, and over all steps
 // (Cauchy-Schwarz on the sums of |products|)
 //   E(m, j) = 36 * 2^-24 * (|x_m| |b_lo,j| + |x_lo,m| (|b_j| + |b_lo,j|)) + fp64 slack,
-// with |x_m| and |x_lo,m| summed per block in fp32 after scaling by the
-// block's grid (so tiny values cannot underflow the bound away).
+// with |x_m| and |x_lo,m| the diagonals of the MFMA Gram matrices of x and
+// x_lo (inflated by their own step error) and the norms of b from the
+// preparation pass.
 // When [h - E, h + E] straddles a rounding boundary of the 16-bit format, the
-// element is re-evaluated by its wave before the outputs are written: the
-// wave computes the dot product of the x row and the b row in fp64 (products
-// exact) with all 64 lanes and replaces the accumulator.  fp32 compute, or an
+// element goes on the workgroup's work list in LDS; after the outputs are
+// stored, the workgroup's waves take the list in groups and overwrite each
+// listed output with the value rounded from the fp64 dot product of its x row
+// and b row (products exact, batched 16-byte loads).  fp32 compute, or an
 // fp32 rounding target, needs no guard: a flip there moves the result by
 // 2^-24 relative.
 //
-// Work split: a workgroup of 4 waves owns RW*16 rows and RP = 16*JB columns;
-// its waves form RW row groups x KS k groups (k group g takes the blocks
-// g, g+KS, ...; partial sums meet in LDS at the end).  b_hi and b_lo tiles are
-// staged through LDS; each lane streams its own x fragments from HBM.
+// Work split: a workgroup owns RW*16 rows and RP = 16*JB*CG columns; its
+// waves form RW row groups x KS k groups x CG column groups (k group g takes
+// the blocks g, g+KS, ...; partial sums meet in LDS at the end).  The b_hi,
+// b_lo and x tiles of KS blocks at a time are staged through LDS straight
+// from global memory, several rounds ahead.
 #include "kernels.h"
 #include "lyc_device.h"
+
+#ifndef LYC_R16_KS
+#define LYC_R16_KS 8
+#endif
 
 namespace lyc {
 
@@ -139,19 +146,19 @@ __device__ __forceinline__ float affine_value(double acc, int out_dt) {
     return bf16_to_f32(round16<CT>(acc));
 }
 
-// fp64 dot product of two K-contiguous rows (exact products), computed by the
-// whole wave: lane l takes the 16-byte chunks l, l+64, ...; loads are issued
-// in batches of 8 chunks per row per lane so that each batch costs one memory
-// round trip.  Every lane gets the sum.
-template <class CT>
-__device__ __forceinline__ double wave_dot(const i32x4* xrow, const i32x4* brow, uint32_t nch, int lane) {
-    constexpr int B = 8;
+// fp64 dot products of K-contiguous row pairs (exact products), 64 / L pairs
+// per wave: lane j of an L-lane group takes the 16-byte chunks j, j + L, ...
+// of its group's pair; the loads of up to B chunks per row per lane are issued
+// together, so that each batch costs one memory round trip.  Every lane of a
+// group gets its group's sum.  L is a power of two, uniform over the wave.
+template <class CT, int B>
+__device__ __forceinline__ double group_dot(const i32x4* xrow, const i32x4* brow, uint32_t nch, int j, int L) {
     double s0 = 0.0, s1 = 0.0;
-    for (uint32_t c0 = (uint32_t)lane; c0 < nch; c0 += 64 * B) {
+    for (uint32_t c0 = (uint32_t)j; c0 < nch; c0 += (uint32_t)(L * B)) {
         i32x4 xv[B], bv[B];
 #pragma unroll
         for (int i = 0; i < B; ++i) {
-            const uint32_t c = c0 + 64u * i;
+            const uint32_t c = c0 + (uint32_t)(L * i);
             xv[i] = c < nch ? xrow[c] : i32x4{0, 0, 0, 0};
             bv[i] = c < nch ? brow[c] : i32x4{0, 0, 0, 0};
         }
@@ -163,8 +170,20 @@ __device__ __forceinline__ double wave_dot(const i32x4* xrow, const i32x4* brow,
     }
     double part = s0 + s1;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+    for (int o = 32; o >= 1; o >>= 1)
+        if (o < L) part += __shfl_xor(part, o);
     return part;
+}
+
+// element e (lane-dependent) of a 4-vector, by bit masks: a conditional chain
+// here becomes branches.  The whole vector is bit_cast (a bit_cast of one
+// element of a vector is folded to element 0 by this compiler).
+__device__ __forceinline__ float pick4(f32x4 v, int e) {
+    const i32x4 u = __builtin_bit_cast(i32x4, v);
+    uint32_t r = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r |= (uint32_t)u[i] & (0u - (uint32_t)(e == i));
+    return __builtin_bit_cast(float, r);
 }
 
 // Epilogue of one wave's accumulators: rounding guard (flagged elements are
@@ -176,6 +195,19 @@ __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB]
     constexpr bool SPLIT = CT::dt != DT_F32;
     const int64_t m = wg_m0 + my_row;
     const bool row_ok = m < p.M;
+    // the bias (plain affine form) is loaded before the first store: the
+    // compiler cannot move a load past a store that may alias it.  The affine
+    // form runs with JB = 4; wider instances never read it.
+    float bias[JB][4] = {};
+    if (JB <= 4 && p.mode != XR_H && p.bias != nullptr) {
+        int64_t idx[JB * 4];
+        float v[JB * 4];
+#pragma unroll
+        for (int i = 0; i < JB * 4; ++i) idx[i] = j0 + c0 + (i >> 2) * 16 + 4 * (lane >> 4) + (i & 3);
+        load_n_as_f32<JB * 4>(p.bias, p.bias_dt, idx, j0 + cols_wg, v);
+#pragma unroll
+        for (int i = 0; i < JB * 4; ++i) bias[i >> 2][i & 3] = v[i];
+    }
 
     // guard: flag the elements whose error interval straddles a rounding
     // boundary (bit jb*4+e of `flags`); they are re-evaluated after the
@@ -190,11 +222,11 @@ __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB]
             for (int e = 0; e < 4; ++e) {
                 const int jl = c0 + jb * 16 + 4 * (lane >> 4) + e;
                 const bool col_ok = jl < cols_wg;
-                const double2 bn = col_ok ? p.bnorm[j0 + jl] : double2{0.0, 0.0};  // {|b|, |b_lo|}
-                const double E = (0x1p-24 * GUARD_CROSS * (xn2 * bn.y + xln * (bn.x + bn.y)) + 0x1p-37 * xn2 * bn.x) *
+                const double2 b2 = col_ok ? p.bnorm[j0 + jl] : double2{0.0, 0.0};   // {|b|, |b_lo|}
+                const double E = (0x1p-24 * GUARD_CROSS * (xn2 * b2.y + xln * (b2.x + b2.y)) + 0x1p-37 * xn2 * b2.x) *
                                  (1.0 + 0x1p-20);
                 const double h = acc[jb][e];
-                const bool bwide = !(bn.y < 1e300);   // a block of b could not be split
+                const bool bwide = !(b2.y < 1e300);   // a block of b could not be split
                 const bool flag = row_ok && col_ok && (wide || bwide || round16<CT>(h - E) != round16<CT>(h + E));
                 flags |= flag ? (1u << (jb * 4 + e)) : 0u;
             }
@@ -237,11 +269,7 @@ __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB]
                 const int64_t n0 = j0 + jl0;
                 float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float bias =
-                        (p.bias != nullptr && jl0 + e < cols_wg) ? load_as_f32(p.bias, p.bias_dt, n0 + e) : 0.f;
-                    v[e] = affine_value<CT>(acc[jb][e], p.out_dt) + bias;
-                }
+                for (int e = 0; e < 4; ++e) v[e] = affine_value<CT>(acc[jb][e], p.out_dt) + bias[jb][e];
                 const int64_t base = m * p.ld_out + n0;
                 if (p.out_dt == DT_F32) {
                     float* y = (float*)p.out;
@@ -276,10 +304,13 @@ __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB]
 // tile (RW*16 rows), all filled straight from global memory.  The workgroup's
 // NW = 4*CG waves are RW row groups x KS k groups x CG column groups; a wave
 // owns 16 rows and JB*16 columns.
+// row groups of a workgroup with KS k groups: 4 / KS (16 rows per group), at least 1
+constexpr int xr_row_groups(int KS) { return KS >= 4 ? 1 : 4 / KS; }
+
 template <int JB, int KS, int CG, bool SPLIT>
 struct XrStage {
     static constexpr int NB = SPLIT ? 2 : 1;
-    static constexpr int RW = 4 / KS, RP = JB * 16 * CG, NW = 4 * CG;
+    static constexpr int RW = xr_row_groups(KS), RP = JB * 16 * CG, NW = RW * KS * CG;
     static constexpr int TILE = RP * 128, XT = RW * 16 * 128;
     static constexpr int BYTES = KS * (NB * TILE + XT);
     static constexpr int NBB = KS * NB * RP / 8;      // 1 KiB wave loads of b per round
@@ -291,7 +322,8 @@ struct XrStage {
 };
 
 template <class CT, int JB, int KS, int CG>
-__global__ __launch_bounds__(256 * CG) __attribute__((amdgpu_num_vgpr(256))) void xr_kernel(XrParams p) {
+__global__ __launch_bounds__(64 * xr_row_groups(KS) * KS * CG) __attribute__((amdgpu_num_vgpr(256)))
+void xr_kernel(XrParams p) {
     constexpr bool SPLIT = CT::dt != DT_F32;     // 16-bit compute: hi/lo split and guard
     using ST = XrStage<JB, KS, CG, SPLIT>;
     constexpr int NB = ST::NB, RW = ST::RW, RP = ST::RP, TILE = ST::TILE, NS = ST::NS, Q = ST::Q, NW = ST::NW;
@@ -459,8 +491,7 @@ __global__ __launch_bounds__(256 * CG) __attribute__((amdgpu_num_vgpr(256))) voi
         // 2^-24 relative) is covered by inflating, and products that underflowed
         // by 2^-120 per step (a step adds 32 squares per element).
         const int r = lane & 15, e = r & 3;
-        const float dx = e == 0 ? gx[0] : e == 1 ? gx[1] : e == 2 ? gx[2] : gx[3];
-        const float dl = e == 0 ? gl[0] : e == 1 ? gl[1] : e == 2 ? gl[2] : gl[3];
+        const float dx = pick4(gx, e), dl = pick4(gl, e);
         const int src = r + 16 * (r >> 2);
         const double steps = 2.0 * ROUNDS;
         const double infl = 1.0 + 2.0 * (GUARD_CROSS / 2) * 0x1p-24 * (steps + 1.0) + 0x1p-20;
@@ -507,11 +538,19 @@ __global__ __launch_bounds__(256 * CG) __attribute__((amdgpu_num_vgpr(256))) voi
         const uint32_t nch = kbytes / 16;
         const i32x4* xbase = (const i32x4*)((const char*)p.x + wg_m0 * kbytes);
         const i32x4* bbase = (const i32x4*)((const char*)p.b_full + j0 * kbytes);
-        for (unsigned i = (unsigned)wave; i < n; i += (unsigned)ST::NW) {
-            const uint32_t ent = list[i];
+        // entries per wave and pass: as many as keep every lane's share of a
+        // row within one batch of B chunks (B = 8 where the accumulators of
+        // 8 column blocks leave fewer registers)
+        constexpr int B = JB >= 8 ? 8 : 16;
+        const int G = nch <= 16 * B ? 4 : (nch <= 32 * B ? 2 : 1);
+        const int L = 64 / G, j = lane & (L - 1);
+        for (unsigned i0 = (unsigned)(wave * G); i0 < n; i0 += (unsigned)(ST::NW * G)) {
+            const unsigned i = i0 + (unsigned)(lane / L);
+            const bool mine = i < n;
+            const uint32_t ent = list[mine ? i : i0];
             const int row = (int)(ent >> 16), col = (int)(ent & 0xffffu);
-            const double d = wave_dot<CT>(xbase + (size_t)row * nch, bbase + (size_t)col * nch, nch, lane);
-            if (lane == 0) {
+            const double d = group_dot<CT, B>(xbase + (size_t)row * nch, bbase + (size_t)col * nch, nch, j, L);
+            if (mine && j == 0) {
                 const int64_t m = wg_m0 + row, j = j0 + col;
                 if (p.mode == XR_H) {
                     ((uint16_t*)p.out)[m * p.ld_out + j] = round16<CT>(d);
@@ -529,9 +568,9 @@ __global__ __launch_bounds__(256 * CG) __attribute__((amdgpu_num_vgpr(256))) voi
 
 template <class CT, int JB, int KS, int CG>
 static hipError_t run_xr(const XrParams& p, hipStream_t s) {
-    constexpr int RP = JB * 16 * CG, RW = 4 / KS;
+    constexpr int RP = JB * 16 * CG, RW = xr_row_groups(KS);
     const dim3 grid((unsigned)((p.M + RW * 16 - 1) / (RW * 16)), (unsigned)((p.Nc + RP - 1) / RP));
-    hipLaunchKernelGGL((xr_kernel<CT, JB, KS, CG>), grid, dim3(256 * CG), 0, s, p);
+    hipLaunchKernelGGL((xr_kernel<CT, JB, KS, CG>), grid, dim3(64 * RW * KS * CG), 0, s, p);
     return hipGetLastError();
 }
 
@@ -542,13 +581,15 @@ static int pick_ks(int64_t M, int64_t col_tiles) {
     return ks;
 }
 
+// KSMAX 8: where 16 rows per workgroup are needed, 8 k groups (two waves per
+// SIMD) instead of 4
 template <class CT, int JB, int CG, int KSMAX>
 static hipError_t run_xr_jb(const XrParams& p, hipStream_t s) {
     const int64_t col_tiles = (p.Nc + JB * 16 * CG - 1) / (JB * 16 * CG);
     const int ks = pick_ks(p.M, col_tiles);
     if (ks == 1 || KSMAX == 1) return run_xr<CT, JB, 1, CG>(p, s);
     if (ks == 2 || KSMAX == 2) return run_xr<CT, JB, (KSMAX >= 2 ? 2 : 1), CG>(p, s);
-    return run_xr<CT, JB, (KSMAX >= 4 ? 4 : 1), CG>(p, s);
+    return run_xr<CT, JB, (KSMAX >= 4 ? KSMAX : 1), CG>(p, s);
 }
 
 // Columns per wave (JB blocks of 16) and column groups per workgroup (CG):
@@ -557,6 +598,9 @@ template <class CT>
 static hipError_t run_xr_ct(const XrParams& p, hipStream_t s) {
     if (p.mode == XR_AFFINE) return run_xr_jb<CT, 4, 1, 4>(p, s);
     switch (p.Nc) {
+    case 16:   // 16-bit compute only (fp32 compute pads the rank to 32)
+        if (CT::dt == DT_F32) return hipErrorInvalidValue;
+        return run_xr_jb<CT, (CT::dt == DT_F32 ? 2 : 1), 1, LYC_R16_KS>(p, s);
     case 32: return run_xr_jb<CT, 2, 1, 4>(p, s);
     case 64: return run_xr_jb<CT, 2, 2, 4>(p, s);
     case 128: return run_xr_jb<CT, 4, 2, 2>(p, s);

@@ -39,34 +39,63 @@ __device__ __forceinline__ float load_as_f32(const void* p, int dt, int64_t i) {
     return dt == DT_F16 ? f16_to_f32(b) : bf16_to_f32(b);
 }
 
-// binary64 -> 16-bit format (t = stored fraction bits, bias = exponent bias,
-// maxe = all-ones exponent field), round to nearest even, computed on the
-// integer significand so that there is exactly one rounding.
-__device__ __forceinline__ uint16_t f64_to_16(double d, int t, int bias, int maxe) {
-    uint64_t b = __builtin_bit_cast(uint64_t, d);
-    uint16_t sign = (uint16_t)((b >> 63) << 15);
-    int ex = (int)((b >> 52) & 0x7ff);
-    uint64_t frac = b & ((1ull << 52) - 1);
-    if (ex == 0x7ff) return frac ? (uint16_t)(sign | (maxe << t) | (1u << (t - 1))) : (uint16_t)(sign | (maxe << t));
-    if (ex == 0) return sign;  // |d| < 2^-1022 rounds to zero in both 16-bit formats
-    uint64_t m = (1ull << 52) | frac;
-    int e = ex - 1023;
-    int emin = 1 - bias;
-    int shift = 52 - t + (e < emin ? (emin - e) : 0);
-    if (shift >= 54) return sign;  // below half of the smallest subnormal
-    uint64_t q = m >> shift;
-    uint64_t rem = m & ((1ull << shift) - 1);
-    uint64_t half = 1ull << (shift - 1);
-    if (rem > half || (rem == half && (q & 1))) ++q;
-    uint32_t bits;
-    if (e < emin) bits = (uint32_t)q;  // subnormal (q == 2^t carries into the first normal)
-    else bits = ((uint32_t)(e + bias) << t) + (uint32_t)q - (1u << t);
-    if (bits >= ((uint32_t)maxe << t)) bits = (uint32_t)maxe << t;  // overflow -> inf
-    return (uint16_t)(sign | bits);
+// N elements idx[i] of a vector of n >= 1 elements stored in dtype dt,
+// widened to fp32 (0 where idx[i] >= n).  All N loads are issued, unmasked at
+// clamped indices, before the first conversion: around a per-element dtype
+// switch the compiler waits for each load before issuing the next.
+template <int N>
+__device__ __forceinline__ void load_n_as_f32(const void* p, int dt, const int64_t (&idx)[N], int64_t n,
+                                              float (&out)[N]) {
+    uint32_t raw[N];
+    if (dt == DT_F32) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) raw[i] = ((const uint32_t*)p)[idx[i] < n ? idx[i] : n - 1];
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) raw[i] = ((const uint16_t*)p)[idx[i] < n ? idx[i] : n - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float v = dt == DT_F32 ? __builtin_bit_cast(float, raw[i])
+                                     : (dt == DT_F16 ? f16_to_f32((uint16_t)raw[i]) : bf16_to_f32((uint16_t)raw[i]));
+        out[i] = idx[i] < n ? v : 0.f;
+    }
 }
 
-__device__ __forceinline__ uint16_t f64_to_f16(double d) { return f64_to_16(d, 10, 15, 31); }
-__device__ __forceinline__ uint16_t f64_to_bf16(double d) { return f64_to_16(d, 7, 127, 255); }
+// binary64 -> binary32 rounded to odd: the value truncated toward zero, with
+// the last significand bit set when that truncation was inexact.  Rounding
+// this to nearest even in a format with at least two fewer significand bits
+// gives the same result as rounding the binary64 value directly (Boldo and
+// Melquiond, "Emulation of FMA and correctly rounded sums: proved algorithms
+// using rounding to odd", IEEE Trans. Computers 2008).  Valid where the
+// binary32 result is normal, |d| >= 2^-126 (the conversion may flush
+// subnormal results).  Overflow gives the largest finite binary32 value
+// (odd), which then overflows either 16-bit format.  Branch-free.
+__device__ __forceinline__ float f64_to_f32_odd(double d) {
+    const float f = (float)d;   // round to nearest even
+    const double back = (double)f;
+    const uint32_t u = __builtin_bit_cast(uint32_t, f);
+    const uint32_t t = u - (__builtin_fabs(back) > __builtin_fabs(d) ? 1u : 0u);   // toward zero
+    return (back == d || d != d) ? f : __builtin_bit_cast(float, t | 1u);
+}
+
+// binary64 -> fp16 / bf16, round to nearest even, one rounding from the
+// binary64 value; subnormal results kept, overflow to inf, NaN stays NaN.
+// Below 2^-126: fp16 gives a signed zero (its smallest subnormal is 2^-24);
+// bf16 rounds on its subnormal grid 2^-133 by adding and subtracting
+// 1.5 * 2^-81, whose binary64 ulp is that grid.
+__device__ __forceinline__ uint16_t f64_to_f16(double d) {
+    const uint16_t r = f32_to_f16(f64_to_f32_odd(d));
+    const uint16_t z = (uint16_t)((__builtin_bit_cast(uint64_t, d) >> 48) & 0x8000u);
+    return __builtin_fabs(d) < 0x1p-126 ? z : r;
+}
+__device__ __forceinline__ uint16_t f64_to_bf16(double d) {
+    const uint16_t r = f32_to_bf16(f64_to_f32_odd(d));
+    const double q = (d + 0x1.8p-81) - 0x1.8p-81;   // a multiple of 2^-133, |q| <= 2^-126
+    const uint16_t t = (uint16_t)((uint32_t)(__builtin_fabs(q) * 0x1p133) |
+                                  (uint32_t)((__builtin_bit_cast(uint64_t, d) >> 48) & 0x8000u));
+    return __builtin_fabs(d) < 0x1p-126 ? t : r;
+}
 
 // ---- buffer resources (hardware range checking: out-of-range loads read 0) --
 

@@ -44,9 +44,14 @@ def gpu_forward(inputs: Dict[str, torch.Tensor], wl: WL.Workload, scale: Optiona
             h = hv[:, :wl.r]
             flagged = int(ws[fo: fo + 4].cpu().view(torch.int32).item())
         return y.cpu(), h, flagged
-    y = L.linear(d["x"], d["w"], d.get("b"))
+    args = (wl.M, wl.N, wl.K, L.dtype_code(d["x"]), L.dtype_code(d["w"]), L.dtype_code(d["b"]) if "b" in d else 0)
+    nb = L.linear_workspace_size(*args)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    y = L.linear(d["x"], d["w"], d.get("b"), workspace=ws)
     torch.cuda.synchronize()
-    return y.cpu(), None, None
+    fo = L.linear_workspace_layout(*args)
+    flagged = int(ws[fo: fo + 4].cpu().view(torch.int32).item()) if nb > 0 else None
+    return y.cpu(), None, flagged
 
 
 def oracle_forward(inputs: Dict[str, torch.Tensor], wl: WL.Workload, rows=None, scale: Optional[float] = None):

@@ -137,5 +137,7 @@ def test_workspace_sizes():
     assert L.linear_workspace_size(64, 64, 64, 1, 1) >= 64 * 16
     assert L.linear_workspace_size(64, 32, 64, 2, 3) >= 32 * 64 * 2 + 32 * 16
     assert L.lora_workspace_size(8, 8, 8, 0, 1, 1, 0, 1, 1) == 0        # rank 0: no bypass
-    for r, pad in ((1, 32), (32, 32), (33, 64), (64, 64), (65, 128), (129, 256), (256, 256)):
+    for r, pad in ((1, 16), (16, 16), (17, 32), (32, 32), (33, 64), (64, 64), (65, 128), (129, 256), (256, 256)):
         assert L.lora_workspace_layout(16, 16, 16, r, 2, 2, 0, 2, 2)[1] == pad
+    # fp32 compute pads small ranks to 32
+    assert L.lora_workspace_layout(16, 16, 16, 8, 3, 3, 0, 3, 3)[1] == 32
