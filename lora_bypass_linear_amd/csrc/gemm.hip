@@ -315,13 +315,12 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
                         if (nb + e < p.N) y[base + e] = v[e];
                 }
             } else {
-                uint16_t o[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = p.y_dt == DT_F16 ? f32_to_f16(v[e]) : f32_to_bf16(v[e]);
+                const uint32_t lo = p.y_dt == DT_F16 ? pack_f16x2(v[0], v[1]) : pack_bf16x2(v[0], v[1]);
+                const uint32_t hi = p.y_dt == DT_F16 ? pack_f16x2(v[2], v[3]) : pack_bf16x2(v[2], v[3]);
+                const uint16_t o[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
                 uint16_t* y = (uint16_t*)p.y;
                 if (p.vec_store && nb + 3 < p.N) {
-                    *(i32x2*)(y + base) = i32x2{(int)(o[0] | ((uint32_t)o[1] << 16)),
-                                                (int)(o[2] | ((uint32_t)o[3] << 16))};
+                    *(i32x2*)(y + base) = i32x2{(int)lo, (int)hi};
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)

@@ -307,10 +307,10 @@ __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB]
 // row groups of a workgroup with KS k groups: 4 / KS (16 rows per group), at least 1
 constexpr int xr_row_groups(int KS) { return KS >= 4 ? 1 : 4 / KS; }
 
-template <int JB, int KS, int CG, bool SPLIT>
+template <int JB, int KS, int CG, int RW_, bool SPLIT>
 struct XrStage {
     static constexpr int NB = SPLIT ? 2 : 1;
-    static constexpr int RW = xr_row_groups(KS), RP = JB * 16 * CG, NW = RW * KS * CG;
+    static constexpr int RW = RW_, RP = JB * 16 * CG, NW = RW * KS * CG;
     static constexpr int TILE = RP * 128, XT = RW * 16 * 128;
     static constexpr int BYTES = KS * (NB * TILE + XT);
     static constexpr int NBB = KS * NB * RP / 8;      // 1 KiB wave loads of b per round
@@ -321,11 +321,11 @@ struct XrStage {
     static_assert(NS * BYTES <= 160 * 1024 && (NS - 1) * Q < 64, "LDS stages");
 };
 
-template <class CT, int JB, int KS, int CG>
-__global__ __launch_bounds__(64 * xr_row_groups(KS) * KS * CG) __attribute__((amdgpu_num_vgpr(256)))
+template <class CT, int JB, int KS, int CG, int RW_>
+__global__ __launch_bounds__(64 * RW_ * KS * CG) __attribute__((amdgpu_num_vgpr(256)))
 void xr_kernel(XrParams p) {
     constexpr bool SPLIT = CT::dt != DT_F32;     // 16-bit compute: hi/lo split and guard
-    using ST = XrStage<JB, KS, CG, SPLIT>;
+    using ST = XrStage<JB, KS, CG, RW_, SPLIT>;
     constexpr int NB = ST::NB, RW = ST::RW, RP = ST::RP, TILE = ST::TILE, NS = ST::NS, Q = ST::Q, NW = ST::NW;
     __shared__ __attribute__((aligned(16))) char sd[NS * ST::BYTES];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -566,11 +566,11 @@ void xr_kernel(XrParams p) {
     }
 }
 
-template <class CT, int JB, int KS, int CG>
+template <class CT, int JB, int KS, int CG, int RW = xr_row_groups(KS)>
 static hipError_t run_xr(const XrParams& p, hipStream_t s) {
-    constexpr int RP = JB * 16 * CG, RW = xr_row_groups(KS);
+    constexpr int RP = JB * 16 * CG;
     const dim3 grid((unsigned)((p.M + RW * 16 - 1) / (RW * 16)), (unsigned)((p.Nc + RP - 1) / RP));
-    hipLaunchKernelGGL((xr_kernel<CT, JB, KS, CG>), grid, dim3(64 * RW * KS * CG), 0, s, p);
+    hipLaunchKernelGGL((xr_kernel<CT, JB, KS, CG, RW>), grid, dim3(64 * RW * KS * CG), 0, s, p);
     return hipGetLastError();
 }
 
@@ -592,8 +592,10 @@ static hipError_t run_xr_jb(const XrParams& p, hipStream_t s) {
     return run_xr<CT, JB, (KSMAX >= 4 ? KSMAX : 1), CG>(p, s);
 }
 
-// Columns per wave (JB blocks of 16) and column groups per workgroup (CG):
-// eight waves of 16 x 64 for the wider ranks keep two waves per SIMD.
+// Columns per wave (JB blocks of 16), column groups (CG), k groups (KS) and
+// row groups (RW) per workgroup: at least 256 workgroups where M allows,
+// eight waves (two per SIMD) for the wider ranks, and one wave over all
+// columns of its rows where that fits, so that each x fragment is split once.
 template <class CT>
 static hipError_t run_xr_ct(const XrParams& p, hipStream_t s) {
     if (p.mode == XR_AFFINE) return run_xr_jb<CT, 4, 1, 4>(p, s);
@@ -602,8 +604,15 @@ static hipError_t run_xr_ct(const XrParams& p, hipStream_t s) {
         if (CT::dt == DT_F32) return hipErrorInvalidValue;
         return run_xr_jb<CT, (CT::dt == DT_F32 ? 2 : 1), 1, LYC_R16_KS>(p, s);
     case 32: return run_xr_jb<CT, 2, 1, 4>(p, s);
-    case 64: return run_xr_jb<CT, 2, 2, 4>(p, s);
-    case 128: return run_xr_jb<CT, 4, 2, 2>(p, s);
+    case 64:
+        // one wave per 16 rows x all 64 columns where M fills the GPU with
+        // 32- or 64-row workgroups (the x split is done once per row)
+        if (p.M >= 256 * 64) return run_xr<CT, 4, 2, 1, 4>(p, s);
+        if (p.M >= 256 * 32) return run_xr<CT, 4, 4, 1, 2>(p, s);
+        return run_xr_jb<CT, 2, 2, 4>(p, s);
+    case 128:
+        if (p.M >= 256 * 64) return run_xr<CT, 8, 2, 1, 4>(p, s);
+        return run_xr_jb<CT, 4, 2, 2>(p, s);
     case 256: return run_xr<CT, 8, 1, 2>(p, s);
     default: return hipErrorInvalidValue;
     }

@@ -213,12 +213,8 @@ __global__ __launch_bounds__(256) void cast_kernel(const float* __restrict__ src
         uint32_t o[4];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            const uint16_t a0 = c_dt == DT_F16 ? f32_to_f16(a[2 * e]) : f32_to_bf16(a[2 * e]);
-            const uint16_t a1 = c_dt == DT_F16 ? f32_to_f16(a[2 * e + 1]) : f32_to_bf16(a[2 * e + 1]);
-            const uint16_t b0 = c_dt == DT_F16 ? f32_to_f16(b[2 * e]) : f32_to_bf16(b[2 * e]);
-            const uint16_t b1 = c_dt == DT_F16 ? f32_to_f16(b[2 * e + 1]) : f32_to_bf16(b[2 * e + 1]);
-            o[e] = a0 | ((uint32_t)a1 << 16);
-            o[2 + e] = b0 | ((uint32_t)b1 << 16);
+            o[e] = c_dt == DT_F16 ? pack_f16x2(a[2 * e], a[2 * e + 1]) : pack_bf16x2(a[2 * e], a[2 * e + 1]);
+            o[2 + e] = c_dt == DT_F16 ? pack_f16x2(b[2 * e], b[2 * e + 1]) : pack_bf16x2(b[2 * e], b[2 * e + 1]);
         }
         ((i32x4*)dst)[i] = i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
     }

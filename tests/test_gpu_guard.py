@@ -54,11 +54,12 @@ def _expected_flags(inputs, ct, b_name="down") -> int:
     return int((r16(h - E) != r16(h + E)).sum())
 
 
-@pytest.mark.parametrize("name,M", [("lora_f16_4096x3072x3072_r16", 4096),
-                                    ("lora_bf16x_f32w_8192x4096x4096_r64", 1024),
-                                    ("lora_bf16_16384x8192x8192_r128", 512)])
-def test_guard_flag_count_matches_its_bound(name, M):
-    wl = WL.WORKLOADS[name].resized(M=M)
+# sizes that run the h pass in the work split of the full workload
+@pytest.mark.parametrize("name,M,K", [("lora_f16_4096x3072x3072_r16", 4096, 3072),
+                                      ("lora_bf16x_f32w_8192x4096x4096_r64", 8192, 1024),
+                                      ("lora_bf16_16384x8192x8192_r128", 16384, 512)])
+def test_guard_flag_count_matches_its_bound(name, M, K):
+    wl = WL.WORKLOADS[name].resized(M=M, K=K)
     inputs = WL.generate(wl)
     ct = torch.float16 if torch.float16 in (inputs["x"].dtype, inputs["w"].dtype) else torch.bfloat16
     _, _, flagged = gpu_forward(inputs, wl)

@@ -95,6 +95,14 @@ def test_tiles_sampled_rows(name, M, N, K):
     _check(wl, rows=sample_rows(M, 24, seed=M))
 
 
+# every h-pass work split: large M selects the wide-wave splits for ranks 64 and 128
+@pytest.mark.parametrize("r", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("M", [8192, 16384])
+def test_h_pass_splits_large_m(M, r):
+    wl = BASE["lora_bf16_16384x8192x8192_r128"].resized(M=M, N=72, K=200, r=r)
+    _check(wl, rows=sample_rows(M, 24, seed=r))
+
+
 def test_every_tile_configuration_is_covered():
     tiles = {L.gemm_tile(M, N, L.F16) for M, N, _ in TILE_SHAPES}
     assert tiles == {(64, 64), (128, 128), (192, 256), (256, 256)}
