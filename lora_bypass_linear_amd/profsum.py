@@ -3,6 +3,9 @@
     # per-kernel durations (from a --kernel-trace --stats run)
     python -m lora_bypass_linear_amd.profsum stats DIR --cmd "<command>" --out profiles/NAME.txt
 
+    # MFMA busy fraction and MFMA flops of one kernel (one --pmc run)
+    python -m lora_bypass_linear_amd.profsum mfma DIR --kernel SUBSTR --cmd "<command>" --out profiles/NAME.txt
+
     # HBM traffic of one kernel (from one --pmc FETCH_SIZE run and one --pmc
     # WRITE_SIZE run of a command that also performs a plain copy of a known size)
     python -m lora_bypass_linear_amd.profsum traffic --fetch DIR_F --write DIR_W --kernel SUBSTR \\
@@ -96,6 +99,36 @@ def traffic(args) -> str:
     return "\n".join(lines) + "\n"
 
 
+def mfma(args) -> str:
+    """MFMA activity of one kernel from a --pmc run of SQ_VALU_MFMA_BUSY_CYCLES,
+    SQ_INSTS_VALU_MFMA_MOPS_F16, SQ_INSTS_VALU_MFMA_MOPS_BF16 and GRBM_GUI_ACTIVE:
+    the fraction of SIMD cycles in which the matrix pipe was busy while the
+    GPU was active, and the MFMA flops the counters saw (MOPS count units of
+    512 flops).  GRBM_GUI_ACTIVE is counted once per XCD (the value is the
+    sum over the XCDs' instances), SQ_VALU_MFMA_BUSY_CYCLES once per SIMD."""
+    path = _find(args.dir, "counter_collection.csv")
+    vals = {}
+    for c in ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+              "GRBM_GUI_ACTIVE"):
+        per = _per_dispatch(path, c)
+        ker = [v for n, v in per.values() if args.kernel in n]
+        if not ker:
+            raise SystemExit(f"{c}: kernel not found in {args.dir}")
+        vals[c] = statistics.median(ker)
+    busy, active = vals["SQ_VALU_MFMA_BUSY_CYCLES"], vals["GRBM_GUI_ACTIVE"] / args.xcds
+    flops = (vals["SQ_INSTS_VALU_MFMA_MOPS_F16"] + vals["SQ_INSTS_VALU_MFMA_MOPS_BF16"]) * 512.0
+    lines = ["# MFMA activity per launch (rocprofv3 --pmc, median over dispatches)",
+             f"command: {args.cmd}",
+             f"kernel: {args.kernel}",
+             f"simds: {args.simds}",
+             f"xcds: {args.xcds}",
+             f"mfma_busy_cycles: {busy:.0f}",
+             f"gui_active_cycles_per_xcd: {active:.0f}",
+             f"mfma_busy_fraction: {busy / max(active * args.simds, 1.0):.4f}",
+             f"mfma_flops_per_launch: {flops:.6g}"]
+    return "\n".join(lines) + "\n"
+
+
 def read_traffic(path: str, kind: str):
     """traffic bytes per launch from a summary, or None if it is missing or stale."""
     if not os.path.exists(path):
@@ -129,8 +162,15 @@ def main(argv=None):
     t.add_argument("--calib-bytes", type=float, required=True)
     t.add_argument("--cmd", required=True)
     t.add_argument("--out", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("dir")
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--simds", type=int, default=1024)
+    m.add_argument("--xcds", type=int, default=8)
+    m.add_argument("--cmd", required=True)
+    m.add_argument("--out", required=True)
     args = ap.parse_args(argv)
-    text = stats(args) if args.mode == "stats" else traffic(args)
+    text = {"stats": stats, "traffic": traffic, "mfma": mfma}[args.mode](args)
     os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
     with open(args.out, "w") as f:
         f.write(text)
