@@ -598,7 +598,13 @@ static hipError_t run_xr_jb(const XrParams& p, hipStream_t s) {
 // columns of its rows where that fits, so that each x fragment is split once.
 template <class CT>
 static hipError_t run_xr_ct(const XrParams& p, hipStream_t s) {
-    if (p.mode == XR_AFFINE) return run_xr_jb<CT, 4, 1, 4>(p, s);
+    if (p.mode == XR_AFFINE) {
+        // few rows: 16 columns per workgroup and 8 k groups, so that more CUs
+        // share the rows of W (16-bit compute; fp32 keeps the 64-column split)
+        if (CT::dt != DT_F32 && ((p.M + 63) / 64) * ((p.Nc + 63) / 64) < 256)
+            return run_xr_jb<CT, (CT::dt == DT_F32 ? 4 : 1), 1, 8>(p, s);
+        return run_xr_jb<CT, 4, 1, 4>(p, s);
+    }
     switch (p.Nc) {
     case 16:   // 16-bit compute only (fp32 compute pads the rank to 32)
         if (CT::dt == DT_F32) return hipErrorInvalidValue;

@@ -69,10 +69,11 @@ def test_guard_flag_count_matches_its_bound(name, M, K):
     assert abs(flagged - want) <= max(5, 0.05 * want), (flagged, want)
 
 
-def test_affine_guard_flag_count_matches_its_bound():
+@pytest.mark.parametrize("M", [1024, 128])
+def test_affine_guard_flag_count_matches_its_bound(M):
     """The plain affine form guards the rounding of p = x.W^T to the fp16 output
-    with the same bound (b = W)."""
-    wl = WL.WORKLOADS["affine_f16_1024x768x1024"]
+    with the same bound (b = W); M = 128 runs the narrow-column split."""
+    wl = WL.WORKLOADS["affine_f16_1024x768x1024"].resized(M=M)
     inputs = WL.generate(wl)
     _, _, flagged = gpu_forward(inputs, wl)
     want = _expected_flags(inputs, torch.float16, b_name="w")

@@ -103,6 +103,13 @@ def test_h_pass_splits_large_m(M, r):
     _check(wl, rows=sample_rows(M, 24, seed=r))
 
 
+# decode-sized M: the shapes of the bench's small-M timings, every output row
+@pytest.mark.parametrize("M", [16, 128])
+@pytest.mark.parametrize("name", ["affine_f16_1024x768x1024", "lora_f16_4096x3072x3072_r16"])
+def test_small_m_full_output(name, M):
+    _check(BASE[name].resized(M=M))
+
+
 def test_every_tile_configuration_is_covered():
     tiles = {L.gemm_tile(M, N, L.F16) for M, N, _ in TILE_SHAPES}
     assert tiles == {(64, 64), (128, 128), (192, 256), (256, 256)}
