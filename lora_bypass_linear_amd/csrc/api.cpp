@@ -74,7 +74,8 @@ int check_problem(Problem& P) {
 
 struct Layout {
     size_t xc = 0, wc = 0, dc = 0, dh = 0, dl = 0, uc = 0, h = 0, dnorm = 0, wh = 0, wl = 0, wnorm = 0, flagged = 0,
-           total = 0;
+           partial = 0, total = 0;
+    int ksplit = 1;
     bool cast_x = false, cast_w = false;
 };
 
@@ -97,6 +98,11 @@ Layout layout(const Problem& P) {
         L.h = off; off = align256(off + (size_t)P.M * (size_t)P.r_pad * ce);
         L.dnorm = off; off = align256(off + (size_t)P.r_pad * 2 * sizeof(double));
         L.flagged = off; off = align256(off + sizeof(unsigned));
+    }
+    if (P.lora) {
+        // fp32 partial sums of a K-split GEMM (few output tiles)
+        L.ksplit = lyc::gemm_ksplit(P.M, P.N, P.K, P.c_dt);
+        if (L.ksplit > 1) { L.partial = off; off = align256(off + (size_t)L.ksplit * (size_t)(P.M * P.N) * 4); }
     }
     if (!P.lora) {
         // the projection's rounding guard: hi/lo split and row norms of W_c, a counter
@@ -223,6 +229,8 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
     g.y_dt = y_dt;
     g.scale = (float)scale;
     g.rf = 0;
+    g.ksplit = L.ksplit;
+    g.partial = L.ksplit > 1 ? (float*)(W + L.partial) : nullptr;
     const uintptr_t vec_align = y_dt == LYC_F32 ? 16 : 8;
     g.vec_store = (P.N % 4 == 0) && aligned(y, vec_align);
 

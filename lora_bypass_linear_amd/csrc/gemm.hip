@@ -160,6 +160,7 @@ struct Steps {
     uint32_t nfa, nfb, nma, nmb;     // their byte extents (buffer range)
     uint32_t fbytes, kbytes;
     int RF, KT;
+    int k0;                          // first main step of this workgroup's K split
     __device__ __forceinline__ void issue(char* smem, int s, int wave, int lane) const {
         char* st = smem + (s % TL::NS) * TL::STAGE;
         const bool fold = s < RF;
@@ -173,7 +174,7 @@ struct Steps {
         l.sa = fold ? lf.sa : lm.sa;
         l.sb = fold ? lf.sb : lm.sb;
         const uint32_t row_bytes = s < KT ? (fold ? fbytes : kbytes) : 0u;   // 0: all out of range
-        l.issue(st, ra, rb, row_bytes, (uint32_t)(fold ? s : s - RF) * TL::BKB, wave, lane);
+        l.issue(st, ra, rb, row_bytes, (uint32_t)(fold ? s : s - RF + k0) * TL::BKB, wave, lane);
     }
 };
 
@@ -247,8 +248,14 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
     Steps<TL> S;
     S.fbytes = (uint32_t)(p.rf * CT::es);
     S.kbytes = (uint32_t)(p.K * CT::es);
-    S.RF = (int)((S.fbytes + TL::BKB - 1) / TL::BKB);
-    S.KT = S.RF + (int)((S.kbytes + TL::BKB - 1) / TL::BKB);
+    // K split (blockIdx.y of gridDim.y): a contiguous range of the main steps;
+    // the fold steps go with split 0
+    const int KM = (int)((S.kbytes + TL::BKB - 1) / TL::BKB);
+    const int per = (KM + (int)gridDim.y - 1) / (int)gridDim.y;
+    S.k0 = (int)blockIdx.y * per;
+    const int nmain = KM - S.k0 < per ? (KM - S.k0 > 0 ? KM - S.k0 : 0) : per;
+    S.RF = blockIdx.y == 0 ? (int)((S.fbytes + TL::BKB - 1) / TL::BKB) : 0;
+    S.KT = S.RF + nmain;
     S.fa = (const char*)p.af + n0 * S.fbytes;
     S.fb = (const char*)p.bf + m0 * S.fbytes;
     S.ma = (const char*)p.a + n0 * S.kbytes;
@@ -282,6 +289,28 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
     }
 
     // 3. epilogue: lane holds, per 16x16 block, 4 consecutive n for one m.
+    if (p.ksplit > 1) {
+        // this split's fp32 sums; the reduction adds the bias and rounds
+        float* part = p.partial + (int64_t)blockIdx.y * p.M * p.N;
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            const int64_t nb = n0 + wn * TL::WN + i * 16 + 4 * (lane >> 4);
+#pragma unroll
+            for (int j = 0; j < FM; ++j) {
+                const int64_t m = m0 + wm * TL::WM + j * 16 + (lane & 15);
+                if (m >= p.M) continue;
+                float* dst = part + m * p.N + nb;
+                if (p.vec_store && nb + 3 < p.N) {
+                    *(f32x4*)dst = acc[i][j];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (nb + e < p.N) dst[e] = acc[i][j][e];
+                }
+            }
+        }
+        return;
+    }
     //    The bias of every block is loaded before the first store.
     float biasv[FN * 4] = {};
     if (p.bias != nullptr) {
@@ -331,12 +360,31 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
     }
 }
 
+// y = round_out(sum of the K splits' partial sums, in split order, + b)
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmParams p) {
+    const int64_t MN = p.M * p.N;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < MN; i += stride) {
+        float v = p.partial[i];
+        for (int k = 1; k < p.ksplit; ++k) v += p.partial[(int64_t)k * MN + i];
+        const int64_t n = i % p.N;
+        if (p.bias != nullptr) v += load_as_f32(p.bias, p.bias_dt, n);
+        if (p.y_dt == DT_F32) ((float*)p.y)[i] = v;
+        else ((uint16_t*)p.y)[i] = p.y_dt == DT_F16 ? f32_to_f16(v) : f32_to_bf16(v);
+    }
+}
+
 template <class CT, class TL>
 static hipError_t run(const GemmParams& p, hipStream_t s) {
     const int tiles_n = (int)((p.N + TL::TN - 1) / TL::TN);
     const int tiles_m = (int)((p.M + TL::TM - 1) / TL::TM);
     const int nblk = tiles_n * tiles_m;
-    hipLaunchKernelGGL((gemm_kernel<CT, TL>), dim3(nblk), dim3(TL::NT), 0, s, p, tiles_n, tiles_m, 4);
+    const int ks = p.ksplit > 1 ? p.ksplit : 1;
+    hipLaunchKernelGGL((gemm_kernel<CT, TL>), dim3(nblk, ks), dim3(TL::NT), 0, s, p, tiles_n, tiles_m, 4);
+    if (ks > 1) {
+        const int64_t blocks = (p.M * p.N + 255) / 256;
+        hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, p);
+    }
     return hipGetLastError();
 }
 
@@ -358,6 +406,19 @@ static int pick_tile(int64_t M, int64_t N, bool f32) {
         if (cost < best_cost) { best_cost = cost; best = c[i].id; }
     }
     return best;
+}
+
+int gemm_ksplit(int64_t M, int64_t N, int64_t K, int c_dt) {
+    int tn, tm;
+    gemm_tile_shape(M, N, c_dt, &tn, &tm);
+    const int64_t tiles = ((N + tn - 1) / tn) * ((M + tm - 1) / tm);
+    const int64_t ksteps = (K * (c_dt == DT_F32 ? 4 : 2) + 127) / 128;
+    if (tiles >= 128 || tiles == 0) return 1;
+    // about 256 workgroups, at least 4 K steps each, at most 8 splits
+    int64_t ks = 256 / tiles;
+    if (ks > ksteps / 4) ks = ksteps / 4;
+    if (ks > 8) ks = 8;
+    return ks > 1 ? (int)ks : 1;
 }
 
 void gemm_tile_shape(int64_t M, int64_t N, int c_dt, int* tn, int* tm) {

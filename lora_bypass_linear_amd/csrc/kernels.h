@@ -22,6 +22,12 @@ struct GemmParams {
     void* y;
     int y_dt;
     int vec_store;     // 1: y rows allow 4-element vector stores
+    // ksplit > 1: the main K steps of every tile are split over ksplit
+    // workgroups (the fold goes with the first); each writes its fp32 sums to
+    // partial [ksplit][M][N] and a second kernel adds them in split order,
+    // adds the bias and rounds once
+    int ksplit;
+    float* partial;
 };
 
 // Exact-rounding contraction (h pass and plain affine projection):
@@ -68,6 +74,9 @@ struct PrepParams {
 };
 
 hipError_t launch_gemm(int c_dt, const GemmParams& p, hipStream_t s);
+// K splits launch_gemm uses for this shape (1: none; the partial sums then
+// need ksplit * M * N * 4 bytes of workspace)
+int gemm_ksplit(int64_t M, int64_t N, int64_t K, int c_dt);
 // the output tile launch_gemm uses for this shape
 void gemm_tile_shape(int64_t M, int64_t N, int c_dt, int* tn, int* tm);
 hipError_t launch_xr(int c_dt, const XrParams& p, hipStream_t s);

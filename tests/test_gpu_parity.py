@@ -104,10 +104,20 @@ def test_h_pass_splits_large_m(M, r):
 
 
 # decode-sized M: the shapes of the bench's small-M timings, every output row
+# (the LoRA GEMM splits K over several workgroups there)
 @pytest.mark.parametrize("M", [16, 128])
 @pytest.mark.parametrize("name", ["affine_f16_1024x768x1024", "lora_f16_4096x3072x3072_r16"])
 def test_small_m_full_output(name, M):
     _check(BASE[name].resized(M=M))
+
+
+# K-split GEMM with a bias (bf16), with fp32 weights and fp32 output, and a ragged N
+@pytest.mark.parametrize("name,dims", [("lora_bf16_16384x8192x8192_r128", dict(M=16, N=2048, K=1024)),
+                                       ("lora_bf16x_f32w_8192x4096x4096_r64", dict(M=16, N=4096, K=1024)),
+                                       ("lora_f16_4096x3072x3072_r16", dict(M=5, N=1003, K=1040))])
+def test_k_split_gemm(name, dims):
+    assert L.lora_workspace_size(dims["M"], dims["N"], dims["K"], 16, 1, 1, 0, 1, 1) > 0
+    _check(BASE[name].resized(**dims))
 
 
 def test_every_tile_configuration_is_covered():
