@@ -34,8 +34,10 @@ DEFAULT = "lora_f16_4096x3072x3072_r16"
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # the GPU's clocks take a few hundred steps of the fp16 r16 problem to settle
+    # (10 warm-up steps measure ~15% below the steady state)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=DEFAULT)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -162,16 +164,24 @@ def main():
         cores = oracle.default_threads()
         row_flops = wl.flops / wl.M
         rng = np.random.default_rng(wl.seed)
-        # size the sample from a second, timed probe (the first one pays one-time costs)
+        # size the sample from two timed probes of different sizes (after one
+        # warm call): a call costs a fixed part (widening every operand) plus a
+        # part per output row
         probe_rows = np.sort(rng.choice(wl.M, size=min(wl.M, 4 * cores), replace=False))
-        oracle_forward(inputs, wl, rows=probe_rows[: cores])
+        small = probe_rows[: max(1, probe_rows.size // 4)]
+        oracle_forward(inputs, wl, rows=small)
+        t1 = time.perf_counter()
+        oracle_forward(inputs, wl, rows=small)
+        t_small = time.perf_counter() - t1
         t1 = time.perf_counter()
         oracle_forward(inputs, wl, rows=probe_rows)
-        t_probe = time.perf_counter() - t1
-        want_rows = probe_rows.size * args.cpu_seconds / max(t_probe, 1e-3)
+        t_big = time.perf_counter() - t1
+        per_row = max((t_big - t_small) / max(probe_rows.size - small.size, 1), 1e-6)
+        fixed = max(t_small - per_row * small.size, 0.0)
+        want_rows = max(args.cpu_seconds - fixed, per_row) / per_row
         n_rows = int(min(wl.M, max(cores, want_rows)))
         # a workload whose every row fits in the budget is passed over whole, several times
-        passes = int(max(1, min(20, round(want_rows / wl.M)))) if n_rows == wl.M else 1
+        passes = int(max(1, min(20, round(args.cpu_seconds / (fixed + per_row * wl.M))))) if n_rows == wl.M else 1
         rows = np.sort(rng.choice(wl.M, size=n_rows, replace=False))
         print(f"[bench] oracle on {n_rows} rows x {passes}, {cores} threads", file=sys.stderr, flush=True)
         t1 = time.perf_counter()
