@@ -112,6 +112,24 @@ __device__ __forceinline__ void split16(i32x4 v, float magic, i32x4& hi, i32x4& 
     }
 }
 
+// The same split for fp16 in packed fp16 arithmetic (three v_pk_add_f16 per
+// 4 bytes instead of the unpack / fp32 / repack sequence): with
+// M = 1.5 * 2^(g+10), v + M lies in [1.25, 1.75] * 2^(g+10) for |v| < 2^(g+8)
+// and rounds to a multiple of 2^g (ties to even), t - M is exact, and so is
+// v - hi (hi is a multiple of the ulp of v, and hi = 0 wherever |v| < 2^(g-2)).
+// M must be a normal fp16 value: g <= 5 (callers check), and a grid finer
+// than fp16's smallest subnormal 2^-24 is taken as 2^-24 (every value of such
+// a block is on it: hi = v, lo = 0).
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ void split16_pk(i32x4 v, int g, i32x4& hi, i32x4& lo) {
+    const int gc = g < -24 ? -24 : g;
+    const _Float16 M = __builtin_bit_cast(_Float16, (uint16_t)(((gc + 25) << 10) | 0x200));
+    const f16x8_t vv = __builtin_bit_cast(f16x8_t, v);
+    const f16x8_t h = (vv + M) - M;
+    hi = __builtin_bit_cast(i32x4, h);
+    lo = __builtin_bit_cast(i32x4, vv - h);
+}
+
 // exact products of two 16-byte fragments, summed in fp64 (two chains)
 template <class CT>
 __device__ __forceinline__ double dot16_f64(i32x4 a, i32x4 b) {
@@ -211,35 +229,45 @@ __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB]
 
     // guard: flag the elements whose error interval straddles a rounding
     // boundary (bit jb*4+e of `flags`); they are re-evaluated after the
-    // outputs are written, so the accumulators are only ever indexed statically
+    // outputs are written, so the accumulators are only ever indexed statically.
+    // r16 = round16(h - E) is the rounded value wherever the element is not
+    // flagged (rounding is monotone: round(h - E) <= round(h) <= round(h + E)).
     uint32_t flags = 0;
-    if (SPLIT && p.guard) {
-        const double xn2 = __builtin_sqrt(xm2) * (1.0 + 0x1p-20);
-        const double xln = __builtin_sqrt(xl2) * (1.0 + 0x1p-20);
+    uint16_t r16[JB][4];
+    if (SPLIT) {
+        const bool guard = p.guard != 0;
+        const double slack = 1.0 + 0x1p-20;
+        const double xn2 = __builtin_sqrt(xm2) * slack;
+        const double xln = __builtin_sqrt(xl2) * slack;
+        const double A = 0x1p-24 * GUARD_CROSS * xn2 * slack, B = 0x1p-24 * GUARD_CROSS * xln * slack;
+        const double C = 0x1p-37 * xn2 * slack;
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) {
+            double2 b2[4];   // {|b|, |b_lo|} of the lane's 4 columns of this block
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int jl = c0 + jb * 16 + 4 * (lane >> 4) + e;
-                const bool col_ok = jl < cols_wg;
-                const double2 b2 = col_ok ? p.bnorm[j0 + jl] : double2{0.0, 0.0};   // {|b|, |b_lo|}
-                const double E = (0x1p-24 * GUARD_CROSS * (xn2 * b2.y + xln * (b2.x + b2.y)) + 0x1p-37 * xn2 * b2.x) *
-                                 (1.0 + 0x1p-20);
+                b2[e] = (guard && jl < cols_wg) ? p.bnorm[j0 + jl] : double2{0.0, 0.0};
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int jl = c0 + jb * 16 + 4 * (lane >> 4) + e;
                 const double h = acc[jb][e];
-                const bool bwide = !(b2.y < 1e300);   // a block of b could not be split
-                const bool flag = row_ok && col_ok && (wide || bwide || round16<CT>(h - E) != round16<CT>(h + E));
+                const double E = A * b2[e].y + B * (b2[e].x + b2[e].y) + C * b2[e].x;
+                const uint16_t lo = round16<CT>(h - E);
+                r16[jb][e] = lo;
+                const bool bwide = !(b2[e].y < 1e300);   // a block of b could not be split
+                const bool flag =
+                    guard && row_ok && jl < cols_wg && (wide || bwide || lo != round16<CT>(h + E));
                 flags |= flag ? (1u << (jb * 4 + e)) : 0u;
             }
         }
-        // guarded elements go to the workgroup's work list
-#pragma unroll
-        for (int jb = 0; jb < JB; ++jb) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if ((flags >> (jb * 4 + e)) & 1u) {
-                    const unsigned at = atomicAdd(lcount, 1u);
-                    list[at] = ((uint32_t)my_row << 16) | (uint32_t)(c0 + jb * 16 + 4 * (lane >> 4) + e);
-                }
+        // guarded elements go to the workgroup's work list: one LDS atomic per lane
+        if (flags != 0u) {
+            unsigned at = atomicAdd(lcount, (unsigned)__builtin_popcount(flags));
+            for (uint32_t f = flags; f != 0u; f &= f - 1u) {
+                const int bit = __builtin_ctz(f);
+                list[at++] = ((uint32_t)my_row << 16) | (uint32_t)(c0 + (bit >> 2) * 16 + 4 * (lane >> 4) + (bit & 3));
             }
         }
     }
@@ -254,22 +282,26 @@ __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB]
                     float* hp = (float*)p.out + m * p.ld_out + jg;
                     *(f32x4*)hp = f32x4{(float)acc[jb][0], (float)acc[jb][1], (float)acc[jb][2], (float)acc[jb][3]};
                 } else {
-                    uint16_t o[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) o[e] = round16<CT>(acc[jb][e]);
                     uint16_t* hp = (uint16_t*)p.out + m * p.ld_out + jg;
-                    *(i32x2*)hp = i32x2{(int)(o[0] | ((uint32_t)o[1] << 16)), (int)(o[2] | ((uint32_t)o[3] << 16))};
+                    *(i32x2*)hp = i32x2{(int)(r16[jb][0] | ((uint32_t)r16[jb][1] << 16)),
+                                        (int)(r16[jb][2] | ((uint32_t)r16[jb][3] << 16))};
                 }
             }
         } else {
-            // plain affine: y = round_out(round_out(p) + b)
+            // plain affine: y = round_out(round_out(p) + b); the projection
+            // rounds to fp32 for an fp32 output, else to the compute dtype (= output)
 #pragma unroll
             for (int jb = 0; jb < JB; ++jb) {
                 const int jl0 = c0 + jb * 16 + 4 * (lane >> 4);
                 const int64_t n0 = j0 + jl0;
                 float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = affine_value<CT>(acc[jb][e], p.out_dt) + bias[jb][e];
+                for (int e = 0; e < 4; ++e) {
+                    float pr;
+                    if (!SPLIT || p.out_dt == DT_F32) pr = (float)acc[jb][e];
+                    else pr = CT::dt == DT_F16 ? f16_to_f32(r16[jb][e]) : bf16_to_f32(r16[jb][e]);
+                    v[e] = pr + bias[jb][e];
+                }
                 const int64_t base = m * p.ld_out + n0;
                 if (p.out_dt == DT_F32) {
                     float* y = (float*)p.out;
@@ -281,14 +313,13 @@ __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB]
                             if (jl0 + e < cols_wg) y[base + e] = v[e];
                     }
                 } else {
-                    uint16_t o[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) o[e] = p.out_dt == DT_F16 ? f32_to_f16(v[e]) : f32_to_bf16(v[e]);
+                    const uint32_t lo = p.out_dt == DT_F16 ? pack_f16x2(v[0], v[1]) : pack_bf16x2(v[0], v[1]);
+                    const uint32_t hi = p.out_dt == DT_F16 ? pack_f16x2(v[2], v[3]) : pack_bf16x2(v[2], v[3]);
                     uint16_t* y = (uint16_t*)p.out;
                     if (p.vec_store && jl0 + 3 < cols_wg) {
-                        *(i32x2*)(y + base) =
-                            i32x2{(int)(o[0] | ((uint32_t)o[1] << 16)), (int)(o[2] | ((uint32_t)o[3] << 16))};
+                        *(i32x2*)(y + base) = i32x2{(int)lo, (int)hi};
                     } else {
+                        const uint16_t o[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             if (jl0 + e < cols_wg) y[base + e] = o[e];
@@ -420,10 +451,15 @@ void xr_kernel(XrParams p) {
             mb = mb > o2 ? mb : o2;
             const int g = grid_exp<CT>(mb);
             wide |= (g > 100);
-            const float magic = __builtin_ldexpf(1.5f, (g > 100 ? 100 : g) + 23);
             i32x4 xh[2], xlo[2];
-            split16<CT>(xr[0], magic, xh[0], xlo[0]);
-            split16<CT>(xr[1], magic, xh[1], xlo[1]);
+            if (CT::dt == DT_F16 && __all(g <= 5)) {
+                split16_pk(xr[0], g, xh[0], xlo[0]);
+                split16_pk(xr[1], g, xh[1], xlo[1]);
+            } else {
+                const float magic = __builtin_ldexpf(1.5f, (g > 100 ? 100 : g) + 23);
+                split16<CT>(xr[0], magic, xh[0], xlo[0]);
+                split16<CT>(xr[1], magic, xh[1], xlo[1]);
+            }
             // squared norms of the wave's rows of x and x_lo: the diagonals of
             // their 16 x 16 Gram matrices, accumulated by the MFMA
 #pragma unroll
@@ -599,10 +635,14 @@ static hipError_t run_xr_jb(const XrParams& p, hipStream_t s) {
 template <class CT>
 static hipError_t run_xr_ct(const XrParams& p, hipStream_t s) {
     if (p.mode == XR_AFFINE) {
-        // few rows: 16 columns per workgroup and 8 k groups, so that more CUs
-        // share the rows of W (16-bit compute; fp32 keeps the 64-column split)
-        if (CT::dt != DT_F32 && ((p.M + 63) / 64) * ((p.Nc + 63) / 64) < 256)
-            return run_xr_jb<CT, (CT::dt == DT_F32 ? 4 : 1), 1, 8>(p, s);
+        // 16-bit compute: with at least 256 tiles of 64 x 64, 8 waves (two
+        // k groups) per tile; with fewer, 16 columns per workgroup and 8 k
+        // groups, so that more CUs share the rows of W.  fp32 compute keeps the
+        // 4-wave 64-column split.
+        if constexpr (CT::dt != DT_F32) {
+            if (((p.M + 63) / 64) * ((p.Nc + 63) / 64) >= 256) return run_xr<CT, 4, 2, 1, 4>(p, s);
+            return run_xr_jb<CT, 1, 1, 8>(p, s);
+        }
         return run_xr_jb<CT, 4, 1, 4>(p, s);
     }
     switch (p.Nc) {
