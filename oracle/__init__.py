@@ -61,6 +61,10 @@ def lib():
         L.oracle_resolve.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int,
                                      ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
         L.oracle_forward.restype = ctypes.c_int
+        L.oracle_merge.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                   ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
         L.oracle_forward.argtypes = [ctypes.c_int,
                                      ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
                                      ctypes.c_void_p, ctypes.c_int,
@@ -186,6 +190,35 @@ def forward(x, x_dt, w, w_dt, b=None, b_dt=None, down=None, down_dt=None, up=Non
     if st != OK:
         raise OracleError(st)
     return {"compute": c_out.value, "output": o_out.value, "y": y, "ref": ref, "h": h}
+
+
+def merge(w, w_dt, down, down_dt, up, up_dt, scale: float = 1.0, rows=None, nthreads: Optional[int] = None):
+    """The LoRA merge W' = round_out(W + scale * up_c . down_c) for the rows of
+    W in ``rows`` (default: all).  Storage arrays as in ``forward``: w [N,K],
+    down [r,K], up [N,r].  Returns a dict with the resolved ``compute`` /
+    ``output`` dtypes, ``y`` (storage of the output dtype, [len(rows), K]) and
+    ``ref`` (float64 value before the rounding)."""
+    w = np.ascontiguousarray(w, dtype=storage_np(w_dt))
+    down = np.ascontiguousarray(down, dtype=storage_np(down_dt))
+    up = np.ascontiguousarray(up, dtype=storage_np(up_dt))
+    N, K = w.shape
+    r = down.shape[0]
+    assert down.shape == (r, K) and up.shape == (N, r)
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nrows = N if rows is None else rows_arr.size
+    st, c_dt, o_dt = resolve([w_dt, down_dt, up_dt])
+    if st != OK:
+        raise OracleError(st)
+    y = np.zeros((nrows, K), dtype=storage_np(o_dt))
+    ref = np.zeros((nrows, K), dtype=np.float64)
+    c_out, o_out = ctypes.c_int(0), ctypes.c_int(0)
+    st = lib().oracle_merge(_ptr(w), w_dt, _ptr(down), down_dt, _ptr(up), up_dt, r, float(scale), N, K,
+                            _ptr(rows_arr), nrows, _ptr(y), _ptr(ref),
+                            int(default_threads() if nthreads is None else nthreads),
+                            ctypes.byref(c_out), ctypes.byref(o_out))
+    if st != OK:
+        raise OracleError(st)
+    return {"compute": c_out.value, "output": o_out.value, "y": y, "ref": ref}
 
 
 # ---- scoring ----------------------------------------------------------------

@@ -26,6 +26,12 @@
  *               p = x.W^T (fp32 compute) is rounded to the output dtype,
  *               then the bias is added and the sum rounded again; the bias is
  *               never fused across the projection's rounding boundary.
+ *   merge    -- the LoRA merge W' = round_out( W + scale * up_c . down_c ):
+ *               the original weight is the "input" of the same dtype policy
+ *               and, like the bias, not a matmul operand (it keeps its stored
+ *               value); up and down are cast to the compute dtype; one
+ *               rounding (LyCORIS "Precision" page, "Dtype policy" and the
+ *               merge figure of "Measured accuracy").
  *   rounding -- IEEE round-to-nearest, ties-to-even, directly from fp64 (never
  *               via fp32), gradual underflow, overflow to +-inf at or beyond
  *               max + half an ulp, NaN propagated.
@@ -285,6 +291,85 @@ int oracle_forward(int lora,
     free(jobs);
     free(th);
     free(wc);
+    free(dc);
+    free(uc);
+    return OR_OK;
+}
+
+/* ---- the merge ------------------------------------------------------------ */
+
+typedef struct {
+    const void* w;
+    int w_dt, o_dt;
+    int64_t N, K, r;
+    double scale;
+    const double *dc, *uc;       /* [r,K], [N,r] cast to compute, binary64 */
+    const int64_t* rows;
+    void* out;                   /* [nrows][K], o_dt storage */
+    double* ref;                 /* [nrows][K] before the rounding */
+    int64_t lo, hi;
+} merge_job_t;
+
+static void* merge_rows(void* arg) {
+    merge_job_t* J = (merge_job_t*)arg;
+    const int64_t K = J->K, r = J->r;
+    for (int64_t i = J->lo; i < J->hi; ++i) {
+        const int64_t n = J->rows ? J->rows[i] : i;
+        for (int64_t k = 0; k < K; ++k) {
+            double d = 0.0;
+            for (int64_t j = 0; j < r; ++j) d += J->uc[n * r + j] * J->dc[j * K + k];
+            const double v = widen(J->w, J->w_dt, n * K + k) + J->scale * d;
+            if (J->ref) J->ref[i * K + k] = v;
+            if (J->out) store(J->out, J->o_dt, i * K + k, oracle_round(v, J->o_dt));
+        }
+    }
+    return NULL;
+}
+
+/*
+ * The LoRA merge for the given rows n of W [N,K]: down [r,K], up [N,r].
+ *   rows = NULL evaluates rows 0..nrows-1; out / ref are [nrows][K], either
+ *   may be NULL.  Returns OR_OK, OR_MIXED_HALF or OR_INVALID and the
+ *   resolved dtypes (over W, down, up) in *c_out / *o_out.
+ */
+int oracle_merge(const void* w, int w_dt, const void* down, int down_dt, const void* up, int up_dt, int64_t r,
+                 double scale, int64_t N, int64_t K, const int64_t* rows, int64_t nrows, void* out, double* ref,
+                 int nthreads, int* c_out, int* o_out) {
+    int dts[3] = {w_dt, down_dt, up_dt};
+    int c_dt, o_dt;
+    int st = oracle_resolve(dts, 3, &c_dt, &o_dt);
+    if (st != OR_OK) return st;
+    if (c_out) *c_out = c_dt;
+    if (o_out) *o_out = o_dt;
+    if (N < 0 || K < 0 || r < 0 || nrows < 0) return OR_INVALID;
+    for (int64_t i = 0; rows && i < nrows; ++i)
+        if (rows[i] < 0 || rows[i] >= N) return OR_INVALID;
+    if (!rows && nrows > N) return OR_INVALID;
+    double* dc = cast_all(down, down_dt, c_dt, r * K);
+    double* uc = cast_all(up, up_dt, c_dt, N * r);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > nrows) nthreads = nrows > 0 ? (int)nrows : 1;
+    merge_job_t* jobs = (merge_job_t*)calloc((size_t)nthreads, sizeof(merge_job_t));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    int* started = (int*)calloc((size_t)nthreads, sizeof(int));
+    for (int t = 0; t < nthreads; ++t) {
+        merge_job_t* J = &jobs[t];
+        J->w = w; J->w_dt = w_dt; J->o_dt = o_dt;
+        J->N = N; J->K = K; J->r = r; J->scale = scale;
+        J->dc = dc; J->uc = uc; J->rows = rows; J->out = out; J->ref = ref;
+        J->lo = nrows * t / nthreads;
+        J->hi = nrows * (t + 1) / nthreads;
+    }
+    for (int t = 1; t < nthreads; ++t)
+        started[t] = pthread_create(&th[t], NULL, merge_rows, &jobs[t]) == 0;
+    merge_rows(&jobs[0]);
+    for (int t = 1; t < nthreads; ++t) {
+        if (started[t]) pthread_join(th[t], NULL);
+        else merge_rows(&jobs[t]);
+    }
+    free(started);
+    free(jobs);
+    free(th);
     free(dc);
     free(uc);
     return OR_OK;

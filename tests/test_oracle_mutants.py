@@ -31,6 +31,13 @@ MUTANTS = [
     ("scale-ignored", "v = acc + J->scale * f + bias;", "v = acc + f + bias;"),
     ("down-index", "s += xc[k] * J->dc[j * K + k];", "s += xc[k] * J->dc[k];"),
     ("fp16-exponent-bias", "else v = ldexp((double)(1024 + m), e - 25);", "else v = ldexp((double)(1024 + m), e - 24);"),
+    ("merge-delta-rounded-first", "const double v = widen(J->w, J->w_dt, n * K + k) + J->scale * d;",
+     "const double v = widen(J->w, J->w_dt, n * K + k) + J->scale * oracle_round(d, J->o_dt);"),
+    ("merge-weight-cast", "const double v = widen(J->w, J->w_dt, n * K + k) + J->scale * d;",
+     "const double v = oracle_round(widen(J->w, J->w_dt, n * K + k), J->o_dt == OR_F32 ? OR_F16 : J->o_dt) + J->scale * d;"),
+    ("merge-scale-ignored", "const double v = widen(J->w, J->w_dt, n * K + k) + J->scale * d;",
+     "const double v = widen(J->w, J->w_dt, n * K + k) + d;"),
+    ("merge-down-transposed", "d += J->uc[n * r + j] * J->dc[j * K + k];", "d += J->uc[n * r + j] * J->dc[k * r + j];"),
 ]
 
 

@@ -337,6 +337,95 @@ def test_mixed_half_rejected_by_forward():
         oracle.forward(x, F16, w, BF16, None, None, down, BF16, up, BF16)
 
 
+# ---- the LoRA merge W' = round_out(W + scale * up_c . down_c) ------------------------
+
+def _exact_merge(w, w_dt, down, up, m_dt, c_dt, o_dt, scale):
+    """The merge in exact rational arithmetic: W keeps its stored value, up and
+    down are rounded to the compute dtype, one rounding at the end."""
+    N, K = w.shape
+    r = down.shape[0]
+    W = exact.to_fraction_array(w, w_dt)
+    D = [exact.exact_round(v, c_dt) for v in exact.to_fraction_array(down, m_dt)]
+    U = [exact.exact_round(v, c_dt) for v in exact.to_fraction_array(up, m_dt)]
+    return [[exact.exact_round(W[n * K + k] + scale * sum(U[n * r + j] * D[j * K + k] for j in range(r)), o_dt)
+             for k in range(K)] for n in range(N)]
+
+
+MERGE_CASES = [  # (W dtype, module dtype, N, K, r)
+    (F16, F16, 4, 8, 1), (F16, F16, 3, 7, 4), (BF16, BF16, 4, 6, 2), (F32, F32, 3, 5, 3),
+    (F32, F16, 4, 5, 2), (F32, BF16, 3, 6, 4), (F16, F32, 3, 5, 2),
+]
+
+
+@pytest.mark.parametrize("case", MERGE_CASES)
+@pytest.mark.parametrize("seed", [0, 1])
+def test_bruteforce_merge_exact(case, seed):
+    w_dt, m_dt, N, K, r = case
+    rng = np.random.default_rng(300 + seed)
+    w = _draw(rng, (N, K), w_dt, 0.5)
+    down = _draw(rng, (r, K), m_dt, 0.5)
+    up = _draw(rng, (N, r), m_dt, 0.5)
+    scale = [1.0, 0.75][seed]
+    res = oracle.merge(w, w_dt, down, m_dt, up, m_dt, scale=scale, nthreads=2)
+    want = _exact_merge(w, w_dt, down, up, m_dt, res["compute"], res["output"], Fraction(scale))
+    got = oracle.as_float64(res["y"], res["output"])
+    for n in range(N):
+        for k in range(K):
+            assert Fraction(float(got[n, k])) == want[n][k], (n, k)
+
+
+def test_merge_policy():
+    w = _draw(np.random.default_rng(1), (2, 3), F16)
+    d = _draw(np.random.default_rng(2), (1, 3), BF16)
+    u = _draw(np.random.default_rng(3), (2, 1), BF16)
+    with pytest.raises(oracle.OracleError):
+        oracle.merge(w, F16, d, BF16, u, BF16)
+    # an fp32 master weight with fp16 modules: fp16 compute, fp32 result
+    w32 = _draw(np.random.default_rng(4), (2, 3), F32)
+    d16, u16 = _draw(np.random.default_rng(5), (1, 3), F16), _draw(np.random.default_rng(6), (2, 1), F16)
+    res = oracle.merge(w32, F32, d16, F16, u16, F16)
+    assert (res["compute"], res["output"]) == (F16, F32)
+
+
+@pytest.mark.parametrize("w_dt,m_dt", [(F16, F16), (BF16, BF16), (F32, F16), (F32, F32)])
+def test_merge_closed_form_zero_bypass(w_dt, m_dt):
+    rng = np.random.default_rng(11)
+    w = _draw(rng, (6, 10), w_dt)
+    down = _draw(rng, (3, 10), m_dt)
+    up = _draw(rng, (6, 3), m_dt)
+    zero_up = np.zeros_like(up)
+    for args in ((down, up, 0.0), (down, zero_up, 1.5)):
+        res = oracle.merge(w, w_dt, args[0], m_dt, args[1], m_dt, scale=args[2])
+        # the weight is returned unchanged (it is exactly representable in the result dtype)
+        np.testing.assert_array_equal(oracle.as_float64(res["y"], res["output"]), oracle.as_float64(w, w_dt))
+
+
+def test_merge_fixture_single_rounding():
+    # W = 1, up . down = 2^-11 + 2^-22 exactly: the sum lies just above the fp16
+    # midpoint 1 + 2^-11 and rounds up; rounding the product to fp16 first
+    # (2^-11 + 2^-22 is itself a tie and goes to 2^-11) would land on the tie and give 1
+    w = oracle.encode([1.0], F16).reshape(1, 1)
+    down = oracle.encode([2.0 ** -11, 2.0 ** -22], F16).reshape(2, 1)
+    up = oracle.encode([1.0, 1.0], F16).reshape(1, 2)
+    res = oracle.merge(w, F16, down, F16, up, F16)
+    assert float(oracle.as_float64(res["y"], F16)[0, 0]) == 1.0 + 2.0 ** -10
+    early = oracle.round_to(1.0 + oracle.round_to(2.0 ** -11 + 2.0 ** -22, F16), F16)
+    assert early == 1.0
+
+
+def test_merge_invariants():
+    rng = np.random.default_rng(12)
+    w, down, up = _draw(rng, (8, 12), BF16), _draw(rng, (5, 12), BF16, 0.3), _draw(rng, (8, 5), BF16, 0.3)
+    full = oracle.merge(w, BF16, down, BF16, up, BF16, scale=2.0)
+    perm = np.array([3, 0, 4, 1, 2])
+    # the rank index permuted consistently in up and down (random non-tie inputs)
+    pm = oracle.merge(w, BF16, down[perm], BF16, up[:, perm], BF16, scale=2.0)
+    np.testing.assert_array_equal(pm["y"], full["y"])
+    rows = np.array([7, 2, 2, 0])
+    part = oracle.merge(w, BF16, down, BF16, up, BF16, scale=2.0, rows=rows)
+    np.testing.assert_array_equal(part["y"], full["y"][rows])
+
+
 # ---- scoring --------------------------------------------------------------------
 
 def test_tolerance_constants_from_pages():
