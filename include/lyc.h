@@ -97,8 +97,8 @@ int lyc_linear_fwd(const void* x, int x_dt, const void* w, int w_dt, const void*
 
 /*
  * Workspace bytes lyc_lora_linear_fwd needs.  It holds the rounded h
- * [M, r_pad] in the compute dtype (r_pad: the rank rounded up to 32, 64, 128
- * or 256), compute-dtype copies of down and up (rank padded with zeros), for
+ * [M, r_pad] in the compute dtype (r_pad: the rank rounded up to 16 -- under
+ * 16-bit compute only --, 32, 64, 128 or 256), compute-dtype copies of down and up (rank padded with zeros), for
  * 16-bit compute the hi/lo split of down_c and its row norms used by the h
  * guard, a counter, and compute-dtype copies of fp32 x/W when they feed a
  * 16-bit contraction.  Returns the same argument errors as
@@ -150,6 +150,36 @@ int lyc_lora_workspace_layout(int64_t M, int64_t N, int64_t K, int64_t rank, int
  */
 int lyc_linear_workspace_layout(int64_t M, int64_t N, int64_t K, int x_dt, int w_dt, int bias_dt,
                                 size_t* flagged_offset);
+
+/*
+ * LoRA merge (LyCORIS "Precision" page: "Dtype policy", whose "input" is here
+ * the original weight, and the merge figure of "Measured accuracy"):
+ *   W' = round_out( W + scale * up_c . down_c )
+ * with W [N,K] (the nn.Linear layout), down [rank,K], up [N,rank], all
+ * row-major and contiguous, W' [N,K].  The compute dtype c and the output
+ * dtype are resolved over (W, down, up) by the dtype policy; up and down are
+ * rounded to c, W keeps its stored value (it is not a matmul operand, like
+ * the bias of the forward).  The rank-sum runs in fp32 (exact products of
+ * 16-bit factors), scale * sum + W is one fp32 fused multiply-add, and that
+ * is rounded once to the output dtype (round to nearest even).
+ * rank == 0 gives W' = round_out(W) (down/up may be NULL).
+ *  - out_dt must equal the resolved output dtype (LYC_ERR_DTYPE_MISMATCH).
+ *  - out may be w itself (in-place merge; then out_dt == w_dt, else
+ *    LYC_ERR_INVALID_ARG); any other overlap of out with w is
+ *    LYC_ERR_INVALID_ARG.  out must not overlap down, up or the workspace.
+ *  - Pointers need element alignment only; 16-byte-aligned rows with K a
+ *    multiple of 4 take the vector path.  N, K <= 2^30 and N*K <= 2^38,
+ *    rank <= 256, else LYC_ERR_UNSUPPORTED.  N == 0 or K == 0 launches
+ *    nothing.  scale must be finite and within the fp32 range.
+ *  - The workspace (256-byte aligned, lyc_lora_merge_workspace_size bytes,
+ *    0 when rank == 0) receives compute-dtype copies of down^T and up.
+ * The same stream, ownership and error conventions as the forward calls.
+ */
+int lyc_lora_merge_workspace_size(int64_t N, int64_t K, int64_t rank, int w_dt, int down_dt, int up_dt,
+                                  size_t* bytes);
+int lyc_lora_merge_fwd(const void* w, int w_dt, const void* down, int down_dt, const void* up, int up_dt,
+                       int64_t rank, double scale, void* out, int out_dt, int64_t N, int64_t K,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Output tile (rows of W x rows of x) that the forward calls use for an

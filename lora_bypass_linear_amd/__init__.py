@@ -14,8 +14,9 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 __all__ = ["F16", "BF16", "F32", "LycError", "MixedHalfError", "lib", "resolve_dtypes", "linear", "lora_linear",
-           "linear_workspace_size", "lora_workspace_size", "lora_workspace_layout", "linear_workspace_layout", "gemm_tile", "profile_begin", "profile_end", "dtype_code",
-           "torch_dtype"]
+           "lora_merge", "linear_workspace_size", "lora_workspace_size", "lora_workspace_layout",
+           "linear_workspace_layout", "lora_merge_workspace_size", "gemm_tile", "profile_begin", "profile_end",
+           "dtype_code", "torch_dtype"]
 
 F16, BF16, F32 = 1, 2, 3
 OK, ERR_MIXED_HALF, ERR_INVALID_ARG, ERR_DTYPE_MISMATCH, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = range(7)
@@ -57,6 +58,9 @@ def lib():
         L.lyc_lora_workspace_layout.argtypes = [c_i64, c_i64, c_i64, c_i64, c_int, c_int, c_int, c_int, c_int,
                                                 ctypes.POINTER(c_sz), ctypes.POINTER(c_i64), ctypes.POINTER(c_sz)]
         L.lyc_linear_workspace_layout.argtypes = [c_i64, c_i64, c_i64, c_int, c_int, c_int, ctypes.POINTER(c_sz)]
+        L.lyc_lora_merge_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_int, c_int, c_int, ctypes.POINTER(c_sz)]
+        L.lyc_lora_merge_fwd.argtypes = [c_vp, c_int, c_vp, c_int, c_vp, c_int, c_i64, ctypes.c_double, c_vp, c_int,
+                                         c_i64, c_i64, c_vp, c_sz, c_vp]
         L.lyc_gemm_tile.argtypes = [c_i64, c_i64, c_int, ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
         L.lyc_profile_begin.argtypes = [c_int]
         L.lyc_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_int)]
@@ -64,7 +68,7 @@ def lib():
         L.lyc_status_str.restype = ctypes.c_char_p
         for fn in (L.lyc_resolve_dtypes, L.lyc_linear_workspace_size, L.lyc_linear_fwd,
                    L.lyc_lora_linear_workspace_size, L.lyc_lora_linear_fwd, L.lyc_lora_workspace_layout,
-                   L.lyc_linear_workspace_layout,
+                   L.lyc_linear_workspace_layout, L.lyc_lora_merge_workspace_size, L.lyc_lora_merge_fwd,
                    L.lyc_gemm_tile, L.lyc_profile_begin, L.lyc_profile_end):
             fn.restype = c_int
         _lib = L
@@ -147,6 +151,12 @@ def linear_workspace_layout(M, N, K, x_dt, w_dt, b_dt=0) -> int:
     return fo.value
 
 
+def lora_merge_workspace_size(N, K, r, w_dt, d_dt, u_dt) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().lyc_lora_merge_workspace_size(N, K, r, w_dt, d_dt, u_dt, ctypes.byref(n)))
+    return n.value
+
+
 def gemm_tile(M: int, N: int, compute_dt: int) -> Tuple[int, int]:
     """(tile_n, tile_m) of the output tile one workgroup computes for this shape."""
     tn, tm = ctypes.c_int(0), ctypes.c_int(0)
@@ -219,3 +229,23 @@ def lora_linear(x: torch.Tensor, w: torch.Tensor, down: torch.Tensor, up: torch.
                                      u_dt, r, float(scale), _ptr(out), dtype_code(out), M, N, K, _ptr(ws), nbytes,
                                      _stream(dev)))
     return (out, ws) if return_workspace else out
+
+
+def lora_merge(w: torch.Tensor, down: torch.Tensor, up: torch.Tensor, scale: float,
+               out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """W' = round_out(W + scale * up_c.down_c) on the GPU.
+
+    w [N,K], down [r,K], up [N,r].  ``out`` may be ``w`` itself (in-place
+    merge, when W already has the output dtype)."""
+    dev = _need_device(w, down, up, out)
+    N, K = w.shape
+    r = down.shape[0]
+    w_dt, d_dt, u_dt = dtype_code(w), dtype_code(down), dtype_code(up)
+    _, o_dt = resolve_dtypes([w_dt, d_dt, u_dt])
+    if out is None:
+        out = torch.empty((N, K), dtype=_TORCH[o_dt], device=dev)
+    ws = _workspace(lora_merge_workspace_size(N, K, r, w_dt, d_dt, u_dt), dev, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().lyc_lora_merge_fwd(_ptr(w), w_dt, _ptr(down), d_dt, _ptr(up), u_dt, r, float(scale), _ptr(out),
+                                    dtype_code(out), N, K, _ptr(ws), nbytes, _stream(dev)))
+    return out

@@ -280,9 +280,109 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
     return LYC_OK;
 }
 
+// ---- LoRA merge: W' = round_out(W + scale * up_c . down_c) ------------------
+struct Merge {
+    int64_t N, K, rank;
+    int w_dt, d_dt, u_dt;
+    int c_dt, o_dt;
+    int r_pad;
+    size_t dt_c, uc, total;   // workspace: down^T_c [K][r_pad], up_c [N][r_pad]
+};
+
+int check_merge(Merge& G) {
+    if (G.N < 0 || G.K < 0 || G.rank < 0) return LYC_ERR_INVALID_ARG;
+    if (!valid_dt(G.w_dt) || !valid_dt(G.d_dt) || !valid_dt(G.u_dt)) return LYC_ERR_INVALID_ARG;
+    const int dts[3] = {G.w_dt, G.d_dt, G.u_dt};
+    const int st = resolve(dts, 3, &G.c_dt, &G.o_dt);
+    if (st != LYC_OK) return st;
+    if (G.N > MAX_DIM || G.K > MAX_DIM || G.N * G.K > ((int64_t)1 << 38)) return LYC_ERR_UNSUPPORTED;
+    if (G.rank > MAX_RANK) return LYC_ERR_UNSUPPORTED;
+    G.r_pad = G.rank == 0 ? 0 : G.rank <= 16 ? 16 : G.rank <= 32 ? 32 : G.rank <= 64 ? 64 : G.rank <= 128 ? 128 : 256;
+    const size_t ce = esize(G.c_dt);
+    size_t off = 0;
+    G.dt_c = off; off = align256(off + (size_t)G.K * (size_t)G.r_pad * ce);
+    G.uc = off; off = align256(off + (size_t)G.N * (size_t)G.r_pad * ce);
+    G.total = G.r_pad > 0 ? off : 0;
+    return LYC_OK;
+}
+
+int merge(const Merge& G, const void* w, const void* down, const void* up, double scale, void* out, int out_dt,
+          void* ws, size_t ws_bytes, void* stream) {
+    if (out_dt != G.o_dt) return LYC_ERR_DTYPE_MISMATCH;
+    if (!(scale == scale) || scale > 3.4e38 || scale < -3.4e38) return LYC_ERR_INVALID_ARG;
+    if (G.N == 0 || G.K == 0) return LYC_OK;
+    if (w == nullptr || out == nullptr) return LYC_ERR_INVALID_ARG;
+    if (G.rank > 0 && (down == nullptr || up == nullptr)) return LYC_ERR_INVALID_ARG;
+    // out may be w itself (each element's W is read before it is written),
+    // but no other overlap
+    const uintptr_t wb = (uintptr_t)w, we = wb + (uintptr_t)(G.N * G.K) * esize(G.w_dt);
+    const uintptr_t ob = (uintptr_t)out, oe = ob + (uintptr_t)(G.N * G.K) * esize(out_dt);
+    if (ob != wb && ob < we && wb < oe) return LYC_ERR_INVALID_ARG;
+    if (ob == wb && G.w_dt != out_dt) return LYC_ERR_INVALID_ARG;
+    if (!aligned(w, esize(G.w_dt)) || !aligned(out, esize(out_dt))) return LYC_ERR_UNSUPPORTED;
+    if (G.rank > 0 && (!aligned(down, esize(G.d_dt)) || !aligned(up, esize(G.u_dt)))) return LYC_ERR_UNSUPPORTED;
+    if (G.total > 0 && (ws == nullptr || ws_bytes < G.total || !aligned(ws, 256))) return LYC_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    char* W = (char*)ws;
+    (void)hipGetLastError();
+    if (G.r_pad > 0) {
+        lyc::MergePrepParams mp{};
+        mp.down = down;
+        mp.down_dt = G.d_dt;
+        mp.up = up;
+        mp.up_dt = G.u_dt;
+        mp.dt_c = W + G.dt_c;
+        mp.uc = W + G.uc;
+        mp.N = G.N;
+        mp.K = G.K;
+        mp.rank = G.rank;
+        mp.r_pad = G.r_pad;
+        mp.c_dt = G.c_dt;
+        if (timed(LYC_KERNEL_PREP, s, [&] { return lyc::launch_merge_prep(mp, s); }) != hipSuccess) return LYC_ERR_HIP;
+    }
+    // output rows are the rows of W (GEMM m = n of W), columns its k:
+    // acc[n][k] = sum_j up_c[n][j] down^T_c[k][j]
+    lyc::GemmParams g{};
+    g.a = W + G.dt_c;
+    g.b = W + G.uc;
+    g.M = G.N;
+    g.N = G.K;
+    g.K = G.r_pad;
+    g.rf = 0;
+    g.scale = (float)scale;
+    g.y = out;
+    g.y_dt = out_dt;
+    g.ksplit = 1;
+    g.resid = w;
+    g.resid_dt = G.w_dt;
+    const uintptr_t va = out_dt == LYC_F32 ? 16 : 8, wa = G.w_dt == LYC_F32 ? 16 : 8;
+    g.vec_store = (G.K % 4 == 0) && aligned(out, va) && aligned(w, wa);
+    if (timed(LYC_KERNEL_GEMM, s, [&] { return lyc::launch_gemm(G.c_dt, g, s); }) != hipSuccess) return LYC_ERR_HIP;
+    return LYC_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int lyc_lora_merge_workspace_size(int64_t N, int64_t K, int64_t rank, int w_dt, int down_dt, int up_dt,
+                                  size_t* bytes) {
+    Merge G{N, K, rank, w_dt, down_dt, up_dt, 0, 0, 0, 0, 0, 0};
+    const int st = check_merge(G);
+    if (st != LYC_OK) return st;
+    if (bytes) *bytes = G.total;
+    return LYC_OK;
+}
+
+int lyc_lora_merge_fwd(const void* w, int w_dt, const void* down, int down_dt, const void* up, int up_dt,
+                       int64_t rank, double scale, void* out, int out_dt, int64_t N, int64_t K, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    Merge G{N, K, rank, w_dt, down_dt, up_dt, 0, 0, 0, 0, 0, 0};
+    const int st = check_merge(G);
+    if (st != LYC_OK) return st;
+    if (!valid_dt(out_dt)) return LYC_ERR_INVALID_ARG;
+    return merge(G, w, down, up, scale, out, out_dt, workspace, workspace_bytes, stream);
+}
 
 int lyc_resolve_dtypes(const int* operand_dtypes, int n, int* compute, int* output) {
     return resolve(operand_dtypes, n, compute, output);

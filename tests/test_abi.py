@@ -141,3 +141,52 @@ def test_workspace_sizes():
         assert L.lora_workspace_layout(16, 16, 16, r, 2, 2, 0, 2, 2)[1] == pad
     # fp32 compute pads small ranks to 32
     assert L.lora_workspace_layout(16, 16, 16, 8, 3, 3, 0, 3, 3)[1] == 32
+
+
+def _merge(allow_ok=False, **kw):
+    a = dict(w=P, w_dt=1, d=P, d_dt=1, u=P, u_dt=1, r=4, scale=1.0, o=V(1 << 30), o_dt=1, N=64, K=64, ws=None,
+             nws=0, s=None)
+    a.update(kw)
+    return _refused(L.lib().lyc_lora_merge_fwd(a["w"], a["w_dt"], a["d"], a["d_dt"], a["u"], a["u_dt"], a["r"],
+                                               ctypes.c_double(a["scale"]), a["o"], a["o_dt"], a["N"], a["K"],
+                                               a["ws"], a["nws"], a["s"]), allow_ok)
+
+
+def test_merge_argument_errors():
+    assert _merge(d_dt=2) == L.ERR_MIXED_HALF
+    assert _merge(w_dt=2) == L.ERR_MIXED_HALF
+    assert _merge(o_dt=2) == L.ERR_DTYPE_MISMATCH
+    assert _merge(w_dt=3, o_dt=1) == L.ERR_DTYPE_MISMATCH     # an fp32 W promotes W' to fp32
+    assert _merge(r=257) == L.ERR_UNSUPPORTED
+    assert _merge(r=-1) == L.ERR_INVALID_ARG
+    assert _merge(N=-1) == L.ERR_INVALID_ARG
+    assert _merge(N=1 << 20, K=1 << 20) == L.ERR_UNSUPPORTED  # more elements than one GPU holds
+    assert _merge(w_dt=9) == L.ERR_INVALID_ARG
+    assert _merge(scale=float("nan")) == L.ERR_INVALID_ARG
+    assert _merge(scale=1e39) == L.ERR_INVALID_ARG
+    assert _merge(w=None) == L.ERR_INVALID_ARG
+    assert _merge(o=None) == L.ERR_INVALID_ARG
+    assert _merge(u=None) == L.ERR_INVALID_ARG
+    assert _merge(d=None) == L.ERR_INVALID_ARG
+    # W' may be W itself, but may not overlap it otherwise
+    assert _merge(o=V(4096 + 128)) == L.ERR_INVALID_ARG
+    assert _merge(w=V(1 << 20), o=V((1 << 20) - 64 * 64 * 2 + 2)) == L.ERR_INVALID_ARG
+    assert _merge(w_dt=3, d_dt=3, u_dt=1, o=P, o_dt=3) == L.ERR_WORKSPACE   # in place passes the overlap check
+    assert _merge(w=V(4097)) == L.ERR_UNSUPPORTED             # W not element-aligned
+    assert _merge(o=V((1 << 30) + 1)) == L.ERR_UNSUPPORTED
+    assert _merge() == L.ERR_WORKSPACE
+    assert _merge(ws=V(4100), nws=1 << 20) == L.ERR_WORKSPACE
+    assert _merge(ws=P, nws=16) == L.ERR_WORKSPACE
+    # empty merges launch nothing
+    assert _merge(N=0, w=None, o=None, allow_ok=True) == L.OK
+    assert _merge(K=0, w=None, o=None, allow_ok=True) == L.OK
+
+
+def test_merge_workspace_sizes():
+    # down^T_c [K][r_pad] + up_c [N][r_pad], each 256-aligned; none without a rank
+    assert L.lora_merge_workspace_size(300, 64, 17, 1, 1, 1) == 64 * 32 * 2 + 300 * 32 * 2 + (-(300 * 32 * 2) % 256)
+    assert L.lora_merge_workspace_size(64, 64, 8, 3, 3, 3) == 64 * 16 * 4 * 2
+    assert L.lora_merge_workspace_size(64, 64, 8, 3, 2, 3) == 64 * 16 * 2 * 2   # bf16 compute copies
+    assert L.lora_merge_workspace_size(64, 64, 0, 1, 1, 1) == 0
+    with pytest.raises(L.MixedHalfError):
+        L.lora_merge_workspace_size(64, 64, 4, 1, 2, 1)
