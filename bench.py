@@ -43,6 +43,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-eager", action="store_true")
     ap.add_argument("--no-small-m", action="store_true", help="skip the small-M (decode-like) timings")
+    ap.add_argument("--no-merge", action="store_true", help="skip the LoRA merge timing")
+    ap.add_argument("--merge-only", action="store_true",
+                    help="time only the LoRA merge of the workload's weights (profiling runs)")
+    ap.add_argument("--merge-steps", type=int, default=100)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (HBM counter calibration)")
     args = ap.parse_args()
@@ -73,6 +77,13 @@ def main():
         nws = L.linear_workspace_size(wl.M, wl.N, wl.K, dts[0], dts[1], L.dtype_code(d["b"]) if "b" in d else 0)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
 
+    if args.merge_only:
+        if args.copy_calibration_mib > 0:
+            _copy_calibration(dev, args.copy_calibration_mib)
+        print(json.dumps({"workload": wl.name, "merge": _merge(dev, wl, inputs, args.merge_steps, args.merge_steps,
+                                                                 not args.no_cpu_baseline)}))
+        return
+
     def step():
         if lora:
             L.lora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, d.get("b"), out=y, workspace=ws)
@@ -80,11 +91,7 @@ def main():
             L.linear(d["x"], d["w"], d.get("b"), out=y, workspace=ws)
 
     if args.copy_calibration_mib > 0:
-        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        _copy_calibration(dev, args.copy_calibration_mib)
 
     print(f"[bench] {wl.name}: warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -154,6 +161,8 @@ def main():
 
     if not args.no_small_m:
         out["small_m"] = _small_m(dev)
+    if lora and wl.r > 0 and not args.no_merge:
+        out["merge"] = _merge(dev, wl, inputs, args.merge_steps, 20, not args.no_cpu_baseline)
 
     # accuracy on sampled rows against the fp64 oracle (this is also the CPU-baseline leg)
     if not args.no_cpu_baseline:
@@ -201,6 +210,85 @@ def main():
         if not args.no_eager:
             out["eager_baseline"] = _eager(d, wl, c_dt, o_dt, rows, res, args.steps, score)
     print(json.dumps(out))
+
+
+def _copy_calibration(dev, mib):
+    """One plain device copy of a known size (scales the HBM byte counters)."""
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def _merge(dev, wl, inputs, reps, warm, accuracy):
+    """The LoRA merge W' = round_out(W + scale * up_c.down_c) of the workload's
+    weights (out of place): wall and device time per call, algorithmic HBM
+    bytes (read W, down, up; write W') over the merge contraction's device time
+    against the 8 TB/s peak, and, on sampled rows, ULP against the fp64 oracle
+    next to the eager torch chain (up.down rounded to the compute dtype, then
+    scaled and added to W, each step rounding)."""
+    import numpy as np
+    import torch
+
+    import lora_bypass_linear_amd as L
+    import workloads as WL
+
+    w, dn, up = (inputs[k].to(dev) for k in ("w", "down", "up"))
+    dts = [L.dtype_code(w), L.dtype_code(dn), L.dtype_code(up)]
+    c_dt, o_dt = L.resolve_dtypes(dts)
+    out = torch.empty((wl.N, wl.K), dtype=L.torch_dtype(o_dt), device=dev)
+    nws = L.lora_merge_workspace_size(wl.N, wl.K, wl.r, *dts)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    call = lambda: L.lora_merge(w, dn, up, wl.scale, out=out, workspace=ws)
+    print(f"[bench] merge {wl.name}: {warm} + {reps} calls", file=sys.stderr, flush=True)
+    for _ in range(warm):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        call()
+    torch.cuda.synchronize()
+    wall_us = (time.perf_counter() - t0) * 1e6 / reps
+    L.profile_begin(4 * reps)
+    for _ in range(reps):
+        call()
+    torch.cuda.synchronize()
+    prof = L.profile_end()
+    es = {L.F16: 2, L.BF16: 2, L.F32: 4}
+    nbytes = wl.N * wl.K * (es[dts[0]] + es[o_dt]) + wl.r * wl.K * es[dts[1]] + wl.N * wl.r * es[dts[2]]
+    n_g, t_g = prof["gemm"]
+    g_us = t_g * 1e3 / max(n_g, 1)
+    dev_us = sum(ms for _, ms in prof.values()) * 1e3 / reps
+    from lora_bypass_linear_amd.profsum import read_traffic
+    traffic = read_traffic(os.path.join(ROOT, "profiles", f"traffic_merge_{wl.name}.txt"), "merge")
+    r = {"shape": f"W [{wl.N},{wl.K}] {WL.NAME[wl.w_dt]}, rank {wl.r}, scale {wl.scale}",
+         "wall_us_per_call": round(wall_us, 2), "device_us_per_call": round(dev_us, 2),
+         "kernels": {k: {"launches": n, "avg_us": round(ms * 1e3 / n, 3)} for k, (n, ms) in prof.items() if n},
+         "hbm_gbs_call": round(nbytes / (dev_us * 1e-6) / 1e9, 1),
+         "roofline": {"bound": "hbm", "kernel": "merge_kernel",
+                      "achieved": round(nbytes / (g_us * 1e-6) / 1e9, 1), "peak": HBM_GBS, "unit": "GB/s",
+                      "frac": round(nbytes / (g_us * 1e-6) / 1e9 / HBM_GBS, 4),
+                      "traffic": None if traffic is None else int(traffic), "bytes_per_launch": nbytes,
+                      "avg_us": round(g_us, 3)}}
+    if accuracy:
+        import oracle
+        from tests.gpu_cases import sample_rows, score
+        rows = sample_rows(wl.N, 32, seed=wl.seed, tile=128)
+        res = oracle.merge(WL.raw_bits(inputs["w"]), dts[0], WL.raw_bits(inputs["down"]), dts[1],
+                           WL.raw_bits(inputs["up"]), dts[2], scale=wl.scale, rows=rows)
+        s = score(out.cpu(), res, rows, wl.r, 0)
+        ct, ot = L.torch_dtype(c_dt), L.torch_dtype(o_dt)
+        delta = torch.matmul(up.to(ct), dn.to(ct).contiguous())
+        eager = (w.to(ot) + (delta * wl.scale).to(ot)).to(ot) if o_dt == L.F32 else (w + delta * wl.scale).to(ot)
+        torch.cuda.synchronize()
+        se = score(eager.cpu(), res, rows, wl.r, 0)
+        r.update({"rows_checked": int(np.asarray(rows).size), "max_ulp": round(s["ulp_max"], 4),
+                  "rms_ulp": round(s["ulp_rms"], 4), "tol_fail": s["fail"],
+                  "eager": {"max_ulp": round(se["ulp_max"], 4), "rms_ulp": round(se["ulp_rms"], 4),
+                            "tol_fail": se["fail"]}})
+    return r
 
 
 def _small_m(dev, reps=50):

@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "kernels.h"
+#include "merge.h"
 
 namespace {
 
@@ -340,24 +341,21 @@ int merge(const Merge& G, const void* w, const void* down, const void* up, doubl
         mp.c_dt = G.c_dt;
         if (timed(LYC_KERNEL_PREP, s, [&] { return lyc::launch_merge_prep(mp, s); }) != hipSuccess) return LYC_ERR_HIP;
     }
-    // output rows are the rows of W (GEMM m = n of W), columns its k:
-    // acc[n][k] = sum_j up_c[n][j] down^T_c[k][j]
-    lyc::GemmParams g{};
-    g.a = W + G.dt_c;
-    g.b = W + G.uc;
-    g.M = G.N;
-    g.N = G.K;
-    g.K = G.r_pad;
-    g.rf = 0;
-    g.scale = (float)scale;
-    g.y = out;
-    g.y_dt = out_dt;
-    g.ksplit = 1;
-    g.resid = w;
-    g.resid_dt = G.w_dt;
-    const uintptr_t va = out_dt == LYC_F32 ? 16 : 8, wa = G.w_dt == LYC_F32 ? 16 : 8;
-    g.vec_store = (G.K % 4 == 0) && aligned(out, va) && aligned(w, wa);
-    if (timed(LYC_KERNEL_GEMM, s, [&] { return lyc::launch_gemm(G.c_dt, g, s); }) != hipSuccess) return LYC_ERR_HIP;
+    lyc::MergeParams mg{};
+    mg.w = w;
+    mg.w_dt = G.w_dt;
+    mg.dt_c = W + G.dt_c;
+    mg.uc = W + G.uc;
+    mg.out = out;
+    mg.out_dt = out_dt;
+    mg.N = G.N;
+    mg.K = G.K;
+    mg.r_pad = G.r_pad;
+    mg.scale = (float)scale;
+    // 8 elements per lane chunk when W and W' are both 16-bit, else 4
+    const int E = (G.w_dt == LYC_F32 || out_dt == LYC_F32) ? 4 : 8;
+    mg.vec = (G.K % E == 0) && aligned(w, E * esize(G.w_dt)) && aligned(out, E * esize(out_dt));
+    if (timed(LYC_KERNEL_GEMM, s, [&] { return lyc::launch_merge(G.c_dt, mg, s); }) != hipSuccess) return LYC_ERR_HIP;
     return LYC_OK;
 }
 

@@ -311,57 +311,6 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
         }
         return;
     }
-    //    The LoRA merge (4-wave tiles only): every value of resid this wave
-    //    needs is loaded before the first store, since y may be resid.
-    constexpr bool RES = TL::NW == 4;
-    float resv[RES ? FN : 1][RES ? FM : 1][4] = {};
-    const bool merge = RES && p.resid != nullptr;
-    if (merge) {
-        if (p.resid_dt == DT_F32) {
-            const float* R = (const float*)p.resid;
-#pragma unroll
-            for (int i = 0; i < (RES ? FN : 1); ++i) {
-                const int64_t nb = n0 + wn * TL::WN + i * 16 + 4 * (lane >> 4);
-#pragma unroll
-                for (int j = 0; j < (RES ? FM : 1); ++j) {
-                    const int64_t m = m0 + wm * TL::WM + j * 16 + (lane & 15);
-                    if (m < p.M && p.vec_store && nb + 3 < p.N) {
-                        const f32x4 w = *(const f32x4*)(R + m * p.N + nb);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) resv[i][j][e] = w[e];
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) resv[i][j][e] = (m < p.M && nb + e < p.N) ? R[m * p.N + nb + e] : 0.f;
-                    }
-                }
-            }
-        } else {
-            const uint16_t* R = (const uint16_t*)p.resid;
-            const bool f16 = p.resid_dt == DT_F16;
-#pragma unroll
-            for (int i = 0; i < (RES ? FN : 1); ++i) {
-                const int64_t nb = n0 + wn * TL::WN + i * 16 + 4 * (lane >> 4);
-#pragma unroll
-                for (int j = 0; j < (RES ? FM : 1); ++j) {
-                    const int64_t m = m0 + wm * TL::WM + j * 16 + (lane & 15);
-                    uint32_t u[4];
-                    if (m < p.M && p.vec_store && nb + 3 < p.N) {
-                        const i32x2 w = *(const i32x2*)(R + m * p.N + nb);
-                        u[0] = (uint32_t)w[0] & 0xffffu;
-                        u[1] = (uint32_t)w[0] >> 16;
-                        u[2] = (uint32_t)w[1] & 0xffffu;
-                        u[3] = (uint32_t)w[1] >> 16;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) u[e] = (m < p.M && nb + e < p.N) ? R[m * p.N + nb + e] : 0u;
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        resv[i][j][e] = f16 ? f16_to_f32((uint16_t)u[e]) : bf16_to_f32((uint16_t)u[e]);
-                }
-            }
-        }
-    }
     //    The bias of every block is loaded before the first store.
     float biasv[FN * 4] = {};
     if (p.bias != nullptr) {
@@ -382,7 +331,7 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float a = acc[i][j][e];
-                v[e] = merge ? __builtin_fmaf(p.scale, a, resv[RES ? i : 0][RES ? j : 0][e]) : a + bias[e];
+                v[e] = a + bias[e];
             }
             const int64_t base = m * p.N + nb;
             if (p.y_dt == DT_F32) {
@@ -480,8 +429,7 @@ void gemm_tile_shape(int64_t M, int64_t N, int c_dt, int* tn, int* tm) {
 }
 
 hipError_t launch_gemm(int c_dt, const GemmParams& p, hipStream_t s) {
-    // the merge's epilogue reads a whole output-sized operand: the 4-wave tile
-    const int t = p.resid != nullptr ? T_M : pick_tile(p.M, p.N, c_dt == DT_F32);
+    const int t = pick_tile(p.M, p.N, c_dt == DT_F32);
     if (c_dt == DT_F16) {
         switch (t) {
         case T_L: return run<CF16, TileL>(p, s);

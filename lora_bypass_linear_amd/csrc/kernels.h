@@ -28,27 +28,7 @@ struct GemmParams {
     // adds the bias and rounds once
     int ksplit;
     float* partial;
-    // resid != nullptr (the LoRA merge): y = round_out(fma(scale, acc, resid)),
-    // resid [M][N] in resid_dt, read before y is written (y may be resid);
-    // no fold, no bias, no K split
-    const void* resid;
-    int resid_dt;
 };
-
-// LoRA merge operands: down^T_c [K][r_pad] and up_c [N][r_pad] in the compute
-// dtype, the rank padded with zeros
-struct MergePrepParams {
-    const void* down;
-    int down_dt;
-    const void* up;
-    int up_dt;
-    void* dt_c;
-    void* uc;
-    int64_t N, K, rank;
-    int r_pad;
-    int c_dt;
-};
-hipError_t launch_merge_prep(const MergePrepParams& p, hipStream_t s);
 
 // Exact-rounding contraction (h pass and plain affine projection):
 // C = x_c . b^T with fp64-folded MFMA steps, a rounding guard and in-kernel

@@ -1,0 +1,305 @@
+// merge.hip -- the LoRA merge W' = round_out(W + scale * up_c . down_c)
+// (LyCORIS "Precision" page: "Dtype policy" with the original weight as the
+// input operand, and the merge figure of "Measured accuracy").
+//
+// The merge streams W in and W' out once: 4-6 bytes per element against
+// 2 r flops, so it is bound by HBM for every rank the library takes.  One
+// workgroup owns a 128 x 128 tile of W:
+//   1. the first rank chunk of up_c and down^T_c is requested, then the whole
+//      W tile, 16 bytes per lane in row order (coalesced), into registers;
+//   2. while W is in flight, the rank contraction runs on MFMA from LDS
+//      (chunks of 128 bytes of every operand row, 16-byte slots swizzled);
+//   3. the fp32 accumulators go through LDS once more, so that
+//   4. each lane meets the W elements it loaded: W' = fma(scale, acc, W),
+//      rounded once, stored 16 bytes per lane in row order.
+// 67.5 KiB of LDS and at most 256 VGPRs: two workgroups per CU.
+#include "lyc_device.h"
+#include "merge.h"
+
+namespace lyc {
+
+namespace {
+constexpr int MT = 128;                 // W rows (n) per workgroup
+constexpr int MC = 128;                 // W columns (k) per workgroup
+constexpr int XS = MC + 4;              // exchange row stride in floats (conflict-free 16-byte writes)
+constexpr int LDS = MT * XS * 4;        // 67584 bytes; the operand chunk needs (MT + MC) * 128 = 32768
+constexpr int BOFF = MC * 128;          // byte offset of the up_c chunk behind the down^T_c chunk
+static_assert((MT + MC) * 128 <= LDS, "operand chunk fits the exchange buffer");
+}  // namespace
+
+// A buffer resource from values the compiler may hold in vector registers:
+// each piece is taken from the first lane (they are uniform), so that the
+// loads through it need no per-lane loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_uniform(const void* base, uint32_t bytes) {
+    const uint64_t b = (uint64_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    return make_rsrc((const void*)(((uint64_t)hi << 32) | lo), __builtin_amdgcn_readfirstlane(bytes));
+}
+
+// One rank chunk (128 bytes of every row) of the 128 down^T_c rows (ra) and
+// the 128 up_c rows (rb) of a tile: 8 rows per 32-thread group, one 16-byte
+// slot per thread.
+__device__ __forceinline__ void merge_chunk_loads(i32x4 (&st)[8], __amdgpu_buffer_rsrc_t ra,
+                                                  __amdgpu_buffer_rsrc_t rb, int c, uint32_t rowb, int orow,
+                                                  int okc) {
+    const uint32_t byte = (uint32_t)c * 128 + okc * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) st[q] = buf_load16(ra, byte < rowb ? (uint32_t)(q * 32 + orow) * rowb + byte : OOB);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        st[4 + q] = buf_load16(rb, byte < rowb ? (uint32_t)(q * 32 + orow) * rowb + byte : OOB);
+}
+
+// Chunk c to LDS (16-byte slots swizzled per row), then its one or two
+// 64-byte MFMA substeps: this wave's 64 k x 64 n quadrant.
+template <class CT>
+__device__ __forceinline__ void merge_chunk_mma(char* smem, const i32x4 (&st)[8], f32x4 (&acc)[4][4], int c,
+                                                uint32_t rowb, int orow, int okc, int lane, int wn, int wk) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) *(i32x4*)(smem + (q < 4 ? 0 : BOFF) + lds_off((q & 3) * 32 + orow, okc)) = st[q];
+    lds_barrier();
+    const int nsub = (uint32_t)c * 128 + 64 < rowb ? 2 : 1;
+    for (int s = 0; s < nsub; ++s) {
+        i32x4 fa[4], fb[4];
+        const int kc = 4 * s + (lane >> 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = *(const i32x4*)(smem + lds_off(64 * wk + 16 * i + (lane & 15), kc));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fb[j] = *(const i32x4*)(smem + BOFF + lds_off(64 * wn + 16 * j + (lane & 15), kc));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = CT::step(fa[i], fb[j], acc[i][j]);
+    }
+}
+
+template <class CT, bool WF, bool OF, bool VEC>
+__global__ __launch_bounds__(256, 2) void merge_kernel(MergeParams p, int tiles_k) {
+    __shared__ __attribute__((aligned(16))) char smem[LDS];
+    // a thread's share of the tile: E consecutive elements of one row per pass
+    constexpr int E = (WF || OF) ? 4 : 8;
+    constexpr int CPR = MC / E, RPP = 256 / CPR, P = MT / RPP;
+    constexpr int WES = WF ? 4 : 2;
+    constexpr int WW = E * WES / 4;     // 32-bit words of W per pass
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wn = wave >> 1, wk = wave & 1;
+
+    // workgroups are dealt round-robin over the 8 XCDs: give each XCD a
+    // contiguous row-major range of tiles (they share up_c rows in its L2)
+    const int nblk = gridDim.x, per = nblk >> 3, rem = nblk & 7;
+    const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+    const int l = xcd * per + (xcd < rem ? xcd : rem) + loc;
+    const int64_t n0 = (int64_t)(l / tiles_k) * MT, k0 = (int64_t)(l % tiles_k) * MC;
+
+    // 1a. the first rank chunk of the operands (range-checked buffer loads:
+    //     rows past N or K and bytes past the padded rank read 0)
+    const uint32_t rowb = (uint32_t)p.r_pad * CT::es;
+    const int nchunk = (int)((rowb + 127) / 128);
+    const int64_t ka = p.K - k0 < MC ? p.K - k0 : MC, nb_ = p.N - n0 < MT ? p.N - n0 : MT;
+    const auto ra = make_rsrc_uniform((const char*)p.dt_c + k0 * rowb, (uint32_t)ka * rowb);
+    const auto rb = make_rsrc_uniform((const char*)p.uc + n0 * rowb, (uint32_t)nb_ * rowb);
+    const int orow = tid >> 3, okc = tid & 7;   // operand row (of 32 per load) and 16-byte slot
+    // (unconditional: without a rank every offset is out of range and reads 0;
+    // a branch here would cost the exact wait counts below)
+    i32x4 st[8];
+    merge_chunk_loads(st, ra, rb, 0, rowb, orow, okc);
+
+    // 1b. the W tile, behind the operand chunk in the memory queue.  VEC: K
+    //     is a multiple of E and the rows are aligned, so a lane's chunk is
+    //     either wholly inside W or wholly outside (then it reads a valid
+    //     chunk and stores nothing).  Otherwise, element loads at clamped
+    //     indices.  (No branch between the two: a join here would make the
+    //     compiler's wait before the first LDS write cover the W loads too.)
+    const int prow = tid / CPR, pcol = (tid % CPR) * E;
+    uint32_t wv[P][WW];
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        const int64_t n = n0 + q * RPP + prow;
+        if constexpr (VEC) {
+            const int64_t k = k0 + pcol;
+            const char* src = (const char*)p.w + ((n < p.N && k < p.K) ? n * p.K + k : 0) * WES;
+            if constexpr (WW == 4) {
+                const i32x4 t = *(const i32x4*)src;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) wv[q][e] = (uint32_t)t[e];
+            } else {
+                const i32x2 t = *(const i32x2*)src;
+                wv[q][0] = (uint32_t)t[0];
+                wv[q][1] = (uint32_t)t[1];
+            }
+        } else {
+            uint32_t raw[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int64_t k = k0 + pcol + e;
+                const int64_t idx = (n < p.N && k < p.K) ? n * p.K + k : 0;
+                raw[e] = WF ? ((const uint32_t*)p.w)[idx] : (uint32_t)((const uint16_t*)p.w)[idx];
+            }
+#pragma unroll
+            for (int t = 0; t < WW; ++t) wv[q][t] = WF ? raw[t] : (raw[2 * t] | (raw[2 * t + 1] << 16));
+        }
+    }
+
+    // 2. rank contraction: acc[i][j] holds, per 16 x 16 block, k rows of
+    //    down^T_c (A side) by n columns of up_c (B side).  Chunk 0 is peeled
+    //    off the loop so that its wait covers its own loads only, not the W
+    //    loads issued after them.
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    merge_chunk_mma<CT>(smem, st, acc, 0, rowb, orow, okc, lane, wn, wk);
+    for (int c = 1; c < nchunk; ++c) {
+        merge_chunk_loads(st, ra, rb, c, rowb, orow, okc);
+        lds_barrier();   // every wave is done reading the previous chunk
+        merge_chunk_mma<CT>(smem, st, acc, c, rowb, orow, okc, lane, wn, wk);
+    }
+
+    // 3. accumulators to LDS as X[n][k] (lane: 4 consecutive k of one n)
+    lds_barrier();
+    float* X = (float*)smem;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *(f32x4*)(X + (64 * wn + 16 * j + (lane & 15)) * XS + 64 * wk + 16 * i + 4 * (lane >> 4)) = acc[i][j];
+    lds_barrier();
+
+    // 4. W' = round_out(fma(scale, acc, W)) for the elements this lane loaded
+    constexpr int OES = OF ? 4 : 2;
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        const int rl = q * RPP + prow;
+        float a[E];
+#pragma unroll
+        for (int h = 0; h < E / 4; ++h) {
+            const f32x4 t = *(const f32x4*)(X + rl * XS + pcol + 4 * h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[4 * h + e] = t[e];
+        }
+        float v[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            float w;
+            if constexpr (WF) {
+                w = __builtin_bit_cast(float, wv[q][e]);
+            } else {
+                const uint16_t b = (uint16_t)(wv[q][e >> 1] >> ((e & 1) * 16));
+                w = CT::dt == DT_F16 ? f16_to_f32(b) : bf16_to_f32(b);
+            }
+            v[e] = __builtin_fmaf(p.scale, a[e], w);
+        }
+        uint32_t o[E * OES / 4];
+        if constexpr (OF) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[e] = __builtin_bit_cast(uint32_t, v[e]);
+        } else {
+#pragma unroll
+            for (int t = 0; t < E / 2; ++t)
+                o[t] = CT::dt == DT_F16 ? pack_f16x2(v[2 * t], v[2 * t + 1]) : pack_bf16x2(v[2 * t], v[2 * t + 1]);
+        }
+        const int64_t n = n0 + rl;
+        if constexpr (VEC) {
+            if (n < p.N && k0 + pcol < p.K)
+                *(i32x4*)((char*)p.out + (n * p.K + k0 + pcol) * OES) = i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+        } else if (n < p.N) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int64_t k = k0 + pcol + e;
+                if (k >= p.K) continue;
+                if constexpr (OF) ((uint32_t*)p.out)[n * p.K + k] = o[e];
+                else ((uint16_t*)p.out)[n * p.K + k] = (uint16_t)(o[e >> 1] >> ((e & 1) * 16));
+            }
+        }
+    }
+}
+
+// down [rank][K] -> down^T_c [K][r_pad] (rounded to the compute dtype, zero
+// columns from rank on), 32 columns of down per workgroup through LDS so that
+// both the reads and the writes run along rows; the remaining workgroups copy
+// up [N][rank] -> up_c [N][r_pad], one element per thread.
+template <class T>
+__device__ __forceinline__ float widen(T v, int dt) {
+    if constexpr (sizeof(T) == 4) return __builtin_bit_cast(float, v);
+    else return dt == DT_F16 ? f16_to_f32(v) : bf16_to_f32(v);
+}
+__device__ __forceinline__ void put_c(void* dst, int64_t i, float v, int c_dt) {
+    if (c_dt == DT_F32) ((float*)dst)[i] = v;
+    else ((uint16_t*)dst)[i] = c_dt == DT_F16 ? f32_to_f16(v) : f32_to_bf16(v);
+}
+
+template <class TD, class TU>
+__global__ __launch_bounds__(256) void merge_prep_kernel(MergePrepParams p, int down_blocks) {
+    __shared__ float T[32][257];
+    const int tid = threadIdx.x;
+    if ((int)blockIdx.x < down_blocks) {
+        const int64_t k0 = (int64_t)blockIdx.x * 32;
+        const int kk = tid & 31, jg = tid >> 5;
+        const int64_t k = k0 + kk;
+        const TD* d = (const TD*)p.down;
+        const int64_t kc = k < p.K ? k : p.K - 1;   // clamped: every load is issued unmasked
+#pragma unroll 8
+        for (int j = jg; j < p.rank; j += 8) {
+            const float v = widen(d[(int64_t)j * p.K + kc], p.down_dt);
+            T[kk][j] = k < p.K ? v : 0.f;
+        }
+        __syncthreads();
+        const int sh = __builtin_ctz((unsigned)p.r_pad);
+        for (int i = tid; i < 32 * p.r_pad; i += 256) {
+            const int r = i >> sh, j = i & (p.r_pad - 1);
+            if (k0 + r < p.K) put_c(p.dt_c, (k0 + r) * p.r_pad + j, j < p.rank ? T[r][j] : 0.f, p.c_dt);
+        }
+        return;
+    }
+    const int sh = __builtin_ctz((unsigned)p.r_pad);
+    const int64_t total = p.N * (int64_t)p.r_pad;
+    const int64_t stride = (int64_t)(gridDim.x - down_blocks) * 256;
+    const TU* u = (const TU*)p.up;
+    for (int64_t i = (int64_t)(blockIdx.x - down_blocks) * 256 + tid; i < total; i += stride) {
+        const int64_t n = i >> sh;
+        const int j = (int)(i & (p.r_pad - 1));
+        const float v = widen(u[n * p.rank + (j < p.rank ? j : 0)], p.up_dt);
+        put_c(p.uc, i, j < p.rank ? v : 0.f, p.c_dt);
+    }
+}
+
+hipError_t launch_merge_prep(const MergePrepParams& p, hipStream_t s) {
+    const int down_blocks = (int)((p.K + 31) / 32);
+    int64_t up_blocks = (p.N * (int64_t)p.r_pad + 255) / 256;
+    if (up_blocks > 8192) up_blocks = 8192;
+    if (up_blocks < 1) up_blocks = 1;
+    const dim3 g((unsigned)(down_blocks + up_blocks));
+    const bool d32 = p.down_dt == DT_F32, u32 = p.up_dt == DT_F32;
+    if (d32 && u32) hipLaunchKernelGGL((merge_prep_kernel<uint32_t, uint32_t>), g, dim3(256), 0, s, p, down_blocks);
+    else if (d32) hipLaunchKernelGGL((merge_prep_kernel<uint32_t, uint16_t>), g, dim3(256), 0, s, p, down_blocks);
+    else if (u32) hipLaunchKernelGGL((merge_prep_kernel<uint16_t, uint32_t>), g, dim3(256), 0, s, p, down_blocks);
+    else hipLaunchKernelGGL((merge_prep_kernel<uint16_t, uint16_t>), g, dim3(256), 0, s, p, down_blocks);
+    return hipGetLastError();
+}
+
+template <class CT, bool WF, bool OF>
+static hipError_t run_merge(const MergeParams& p, hipStream_t s) {
+    const int tiles_n = (int)((p.N + MT - 1) / MT), tiles_k = (int)((p.K + MC - 1) / MC);
+    const dim3 g((unsigned)(tiles_n * tiles_k));
+    if (p.vec) hipLaunchKernelGGL((merge_kernel<CT, WF, OF, true>), g, dim3(256), 0, s, p, tiles_k);
+    else hipLaunchKernelGGL((merge_kernel<CT, WF, OF, false>), g, dim3(256), 0, s, p, tiles_k);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(int c_dt, const MergeParams& p, hipStream_t s) {
+    const bool wf = p.w_dt == DT_F32, of = p.out_dt == DT_F32;
+    if (wf && !of) return hipErrorInvalidValue;   // the policy promotes an fp32 W to an fp32 W'
+    switch (c_dt) {
+    case DT_F16: return wf ? run_merge<CF16, true, true>(p, s) : of ? run_merge<CF16, false, true>(p, s)
+                                                                   : run_merge<CF16, false, false>(p, s);
+    case DT_BF16: return wf ? run_merge<CBF16, true, true>(p, s) : of ? run_merge<CBF16, false, true>(p, s)
+                                                                     : run_merge<CBF16, false, false>(p, s);
+    case DT_F32: return (wf && of) ? run_merge<CF32, true, true>(p, s) : hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace lyc

@@ -200,44 +200,6 @@ hipError_t launch_prep(const PrepParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-// The LoRA merge's operands: down^T_c [K][r_pad] (the transpose of down,
-// rounded to the compute dtype, zero columns past the rank) and up_c
-// [N][r_pad], grid-stride over both.
-__global__ __launch_bounds__(256) void merge_prep_kernel(MergePrepParams p) {
-    const int sh = __builtin_ctz((unsigned)p.r_pad);
-    const int64_t nd = p.K * (int64_t)p.r_pad, total = nd + p.N * (int64_t)p.r_pad;
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += stride) {
-        float v;
-        void* dst;
-        int64_t at;
-        if (i < nd) {
-            const int64_t k = i >> sh;
-            const int j = (int)(i & (p.r_pad - 1));
-            v = j < p.rank ? load_as_f32(p.down, p.down_dt, (int64_t)j * p.K + k) : 0.f;
-            dst = p.dt_c;
-            at = i;
-        } else {
-            const int64_t i2 = i - nd, n = i2 >> sh;
-            const int j = (int)(i2 & (p.r_pad - 1));
-            v = j < p.rank ? load_as_f32(p.up, p.up_dt, n * p.rank + j) : 0.f;
-            dst = p.uc;
-            at = i2;
-        }
-        if (p.c_dt == DT_F32) ((float*)dst)[at] = v;
-        else ((uint16_t*)dst)[at] = p.c_dt == DT_F16 ? f32_to_f16(v) : f32_to_bf16(v);
-    }
-}
-
-hipError_t launch_merge_prep(const MergePrepParams& p, hipStream_t s) {
-    const int64_t total = (p.K + p.N) * (int64_t)p.r_pad;
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
-    if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(merge_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
-    return hipGetLastError();
-}
-
 // fp32 -> 16-bit compute copy (x or W stored in fp32 under a 16-bit policy):
 // 8 elements per thread and iteration, two 16-byte loads and one 16-byte
 // store (src is 16-byte aligned and dst 256-byte aligned).

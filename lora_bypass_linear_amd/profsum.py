@@ -9,7 +9,7 @@
     # HBM traffic of one kernel (from one --pmc FETCH_SIZE run and one --pmc
     # WRITE_SIZE run of a command that also performs a plain copy of a known size)
     python -m lora_bypass_linear_amd.profsum traffic --fetch DIR_F --write DIR_W --kernel SUBSTR \\
-        --sources gemm|hpass --calib-kernel copyBuffer --calib-bytes N --cmd "<commands>" --out profiles/NAME.txt
+        --sources gemm|hpass|merge --calib-kernel copyBuffer --calib-bytes N --cmd "<commands>" --out profiles/NAME.txt
 
 FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch.  Each is scaled by
 the ratio (known bytes of the copy) / (what the same counter reports for the
@@ -30,7 +30,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 # the sources each profiled kernel is built from
 SOURCES = {"gemm": ("csrc/gemm.hip", "csrc/kernels.h", "csrc/lyc_device.h"),
-           "hpass": ("csrc/hpass.hip", "csrc/kernels.h", "csrc/lyc_device.h")}
+           "hpass": ("csrc/hpass.hip", "csrc/kernels.h", "csrc/lyc_device.h"),
+           "merge": ("csrc/merge.hip", "csrc/merge.h", "csrc/lyc_device.h")}
 
 
 def source_hash(kind: str) -> str:
