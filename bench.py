@@ -265,7 +265,8 @@ def _merge(dev, wl, inputs, reps, warm, accuracy):
     traffic = read_traffic(os.path.join(ROOT, "profiles", f"traffic_merge_{wl.name}.txt"), "merge")
     r = {"shape": f"W [{wl.N},{wl.K}] {WL.NAME[wl.w_dt]}, rank {wl.r}, scale {wl.scale}",
          "wall_us_per_call": round(wall_us, 2), "device_us_per_call": round(dev_us, 2),
-         "kernels": {k: {"launches": n, "avg_us": round(ms * 1e3 / n, 3)} for k, (n, ms) in prof.items() if n},
+         "kernels": {{"prep": "merge_prep_kernel", "gemm": "merge_kernel"}.get(k, k):
+                     {"launches": n, "avg_us": round(ms * 1e3 / n, 3)} for k, (n, ms) in prof.items() if n},
          "hbm_gbs_call": round(nbytes / (dev_us * 1e-6) / 1e9, 1),
          "roofline": {"bound": "hbm", "kernel": "merge_kernel",
                       "achieved": round(nbytes / (g_us * 1e-6) / 1e9, 1), "peak": HBM_GBS, "unit": "GB/s",

@@ -207,9 +207,10 @@ int lyc_gemm_tile(int64_t M, int64_t N, int compute_dt, int* tile_n, int* tile_m
  */
 enum {
     LYC_KERNEL_CAST = 0,   /* fp32 operand -> 16-bit compute copy */
-    LYC_KERNEL_PREP = 1,   /* low-rank factor / W preparation (copies, split, norms) */
+    LYC_KERNEL_PREP = 1,   /* low-rank factor / W preparation (copies, split, norms; the merge's down^T/up copies) */
     LYC_KERNEL_HPASS = 2,  /* h = x.down^T, its rounding guard and fp64 re-evaluations */
-    LYC_KERNEL_GEMM = 3,   /* the main contraction and epilogue (plain affine: the exactly rounded projection) */
+    LYC_KERNEL_GEMM = 3,   /* the main contraction and epilogue (plain affine: the exactly rounded projection;
+                              merge: the merge kernel) */
     LYC_KERNEL_KINDS = 4
 };
 int lyc_profile_begin(int capacity);

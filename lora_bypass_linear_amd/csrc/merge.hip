@@ -6,7 +6,9 @@
 // 2 r flops, so it is bound by HBM for every rank the library takes.  One
 // workgroup owns a 128 x 128 tile of W:
 //   1. the first rank chunk of up_c and down^T_c is requested, then the whole
-//      W tile, 16 bytes per lane in row order (coalesced), into registers;
+//      W tile, 16 bytes per lane in row order (coalesced), into registers,
+//      non-temporally (W and W' pass through once; the rank operands, re-read
+//      by every tile, stay in L2);
 //   2. while W is in flight, the rank contraction runs on MFMA from LDS
 //      (chunks of 128 bytes of every operand row, 16-byte slots swizzled);
 //   3. the fp32 accumulators go through LDS once more, so that
@@ -22,7 +24,7 @@ namespace {
 constexpr int MT = 128;                 // W rows (n) per workgroup
 constexpr int MC = 128;                 // W columns (k) per workgroup
 constexpr int XS = MC + 4;              // exchange row stride in floats (conflict-free 16-byte writes)
-constexpr int LDS = MT * XS * 4;        // 67584 bytes; the operand chunk needs (MT + MC) * 128 = 32768
+constexpr int LDS = MT / 2 * XS * 4;    // 33792 bytes; the operand chunk needs (MT + MC) * 128 = 32768
 constexpr int BOFF = MC * 128;          // byte offset of the up_c chunk behind the down^T_c chunk
 static_assert((MT + MC) * 128 <= LDS, "operand chunk fits the exchange buffer");
 }  // namespace
@@ -75,7 +77,7 @@ __device__ __forceinline__ void merge_chunk_mma(char* smem, const i32x4 (&st)[8]
 }
 
 template <class CT, bool WF, bool OF, bool VEC>
-__global__ __launch_bounds__(256, 2) void merge_kernel(MergeParams p, int tiles_k) {
+__global__ __launch_bounds__(256, (WF || !VEC) ? 2 : 3) void merge_kernel(MergeParams p, int tiles_k) {
     __shared__ __attribute__((aligned(16))) char smem[LDS];
     // a thread's share of the tile: E consecutive elements of one row per pass
     constexpr int E = (WF || OF) ? 4 : 8;
@@ -121,11 +123,11 @@ __global__ __launch_bounds__(256, 2) void merge_kernel(MergeParams p, int tiles_
             const int64_t k = k0 + pcol;
             const char* src = (const char*)p.w + ((n < p.N && k < p.K) ? n * p.K + k : 0) * WES;
             if constexpr (WW == 4) {
-                const i32x4 t = *(const i32x4*)src;
+                const i32x4 t = __builtin_nontemporal_load((const i32x4*)src);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) wv[q][e] = (uint32_t)t[e];
             } else {
-                const i32x2 t = *(const i32x2*)src;
+                const i32x2 t = __builtin_nontemporal_load((const i32x2*)src);
                 wv[q][0] = (uint32_t)t[0];
                 wv[q][1] = (uint32_t)t[1];
             }
@@ -158,25 +160,32 @@ __global__ __launch_bounds__(256, 2) void merge_kernel(MergeParams p, int tiles_
         merge_chunk_mma<CT>(smem, st, acc, c, rowb, orow, okc, lane, wn, wk);
     }
 
-    // 3. accumulators to LDS as X[n][k] (lane: 4 consecutive k of one n)
-    lds_barrier();
+    // 3-4. in two halves of 64 rows: the accumulators of the waves that own
+    //      the half go to LDS as X[n][k] (lane: 4 consecutive k of one n), then
+    //      every lane finishes the elements of that half it loaded:
+    //      W' = round_out(fma(scale, acc, W))
     float* X = (float*)smem;
+    constexpr int OES = OF ? 4 : 2;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+    lds_barrier();
+    if (wn == half) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            *(f32x4*)(X + (64 * wn + 16 * j + (lane & 15)) * XS + 64 * wk + 16 * i + 4 * (lane >> 4)) = acc[i][j];
+            *(f32x4*)(X + (16 * j + (lane & 15)) * XS + 64 * wk + 16 * i + 4 * (lane >> 4)) = acc[i][j];
+    }
     lds_barrier();
-
-    // 4. W' = round_out(fma(scale, acc, W)) for the elements this lane loaded
-    constexpr int OES = OF ? 4 : 2;
 #pragma unroll
-    for (int q = 0; q < P; ++q) {
+    for (int qq = 0; qq < P / 2; ++qq) {
+        const int q = half * (P / 2) + qq;
         const int rl = q * RPP + prow;
+        const int rx = qq * RPP + prow;
         float a[E];
 #pragma unroll
         for (int h = 0; h < E / 4; ++h) {
-            const f32x4 t = *(const f32x4*)(X + rl * XS + pcol + 4 * h);
+            const f32x4 t = *(const f32x4*)(X + rx * XS + pcol + 4 * h);
 #pragma unroll
             for (int e = 0; e < 4; ++e) a[4 * h + e] = t[e];
         }
@@ -204,7 +213,7 @@ __global__ __launch_bounds__(256, 2) void merge_kernel(MergeParams p, int tiles_
         const int64_t n = n0 + rl;
         if constexpr (VEC) {
             if (n < p.N && k0 + pcol < p.K)
-                *(i32x4*)((char*)p.out + (n * p.K + k0 + pcol) * OES) = i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+                __builtin_nontemporal_store(i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]}, (i32x4*)((char*)p.out + (n * p.K + k0 + pcol) * OES));
         } else if (n < p.N) {
 #pragma unroll
             for (int e = 0; e < E; ++e) {
@@ -214,6 +223,7 @@ __global__ __launch_bounds__(256, 2) void merge_kernel(MergeParams p, int tiles_
                 else ((uint16_t*)p.out)[n * p.K + k] = (uint16_t)(o[e >> 1] >> ((e & 1) * 16));
             }
         }
+    }
     }
 }
 
