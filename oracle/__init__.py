@@ -74,6 +74,11 @@ def lib():
                                      ctypes.c_void_p, ctypes.c_int64,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                      ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
+        vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.oracle_backward.restype = ctypes.c_int
+        L.oracle_backward.argtypes = [vp, ci, vp, ci, ci, vp, ci, vp, ci, i64, ctypes.c_double, vp, ci,
+                                      i64, i64, i64, vp, i64, vp, vp, vp, vp, i64, vp, i64, vp, vp, vp, i64,
+                                      vp, vp, ci, ctypes.POINTER(ctypes.c_int)]
         _lib = L
     return _lib
 
@@ -219,6 +224,53 @@ def merge(w, w_dt, down, down_dt, up, up_dt, scale: float = 1.0, rows=None, nthr
     if st != OK:
         raise OracleError(st)
     return {"compute": c_out.value, "output": o_out.value, "y": y, "ref": ref}
+
+
+def backward(x, x_dt, w, w_dt, down, down_dt, up, up_dt, dy, dy_dt, scale: float = 1.0, b_dt: int = 0,
+             dx_rows=None, js=None, dd_cols=None, du_rows=None, nthreads: Optional[int] = None):
+    """The LoRA-bypass backward for a given dy: dx = round_x(dy_c.W_c + gh_r.down_c),
+    dDown = round_down(gh_r^T.x_c), dUp = round_up(scale * dy_c^T.h_r), with
+    gh_r = round_c(scale * dy_c.up_c) and h_r the forward's rounded h.
+
+    Storage arrays: x [M,K], w [N,K], down [r,K], up [N,r], dy [M,N]; b_dt is
+    the forward's bias dtype (0: none; it only enters the dtype policy).
+    Index sets (default: all) select the rows of dx (tokens), the rank
+    indices js, the columns of dDown (k) and the rows of dUp (n).  Returns a
+    dict with ``compute``, ``dx`` / ``dx_ref`` [len(dx_rows), K], ``gh``
+    [len(dx_rows), r] (the rounded gh of those rows, float64), ``d_down`` /
+    ``dd_ref`` [len(js), len(dd_cols)] and ``d_up`` / ``du_ref``
+    [len(du_rows), len(js)]; gradients in storage of their leaf's dtype."""
+    x = np.ascontiguousarray(x, dtype=storage_np(x_dt))
+    w = np.ascontiguousarray(w, dtype=storage_np(w_dt))
+    down = np.ascontiguousarray(down, dtype=storage_np(down_dt))
+    up = np.ascontiguousarray(up, dtype=storage_np(up_dt))
+    dy = np.ascontiguousarray(dy, dtype=storage_np(dy_dt))
+    M, K = x.shape
+    N = w.shape[0]
+    r = down.shape[0]
+    assert w.shape == (N, K) and down.shape == (r, K) and up.shape == (N, r) and dy.shape == (M, N)
+
+    def idx(v, n):
+        return np.arange(n, dtype=np.int64) if v is None else np.ascontiguousarray(v, dtype=np.int64)
+
+    dx_rows, js, dd_cols, du_rows = idx(dx_rows, M), idx(js, r), idx(dd_cols, K), idx(du_rows, N)
+    dx = np.zeros((dx_rows.size, K), dtype=storage_np(x_dt))
+    dx_ref = np.zeros((dx_rows.size, K))
+    gh = np.zeros((dx_rows.size, r))
+    d_down = np.zeros((js.size, dd_cols.size), dtype=storage_np(down_dt))
+    dd_ref = np.zeros((js.size, dd_cols.size))
+    d_up = np.zeros((du_rows.size, js.size), dtype=storage_np(up_dt))
+    du_ref = np.zeros((du_rows.size, js.size))
+    c_out = ctypes.c_int(0)
+    st = lib().oracle_backward(_ptr(x), x_dt, _ptr(w), w_dt, int(b_dt or 0), _ptr(down), down_dt, _ptr(up), up_dt,
+                               r, float(scale), _ptr(dy), dy_dt, M, N, K, _ptr(dx_rows), dx_rows.size, _ptr(dx),
+                               _ptr(dx_ref), _ptr(gh), _ptr(js), js.size, _ptr(dd_cols), dd_cols.size, _ptr(d_down),
+                               _ptr(dd_ref), _ptr(du_rows), du_rows.size, _ptr(d_up), _ptr(du_ref),
+                               int(default_threads() if nthreads is None else nthreads), ctypes.byref(c_out))
+    if st != OK:
+        raise OracleError(st)
+    return {"compute": c_out.value, "dx": dx, "dx_ref": dx_ref, "gh": gh, "d_down": d_down, "dd_ref": dd_ref,
+            "d_up": d_up, "du_ref": du_ref}
 
 
 # ---- scoring ----------------------------------------------------------------

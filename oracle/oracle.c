@@ -32,6 +32,13 @@
  *               value); up and down are cast to the compute dtype; one
  *               rounding (LyCORIS "Precision" page, "Dtype policy" and the
  *               merge figure of "Measured accuracy").
+ *   backward -- the gradients of x, down and up for a given dy (LyCORIS
+ *               "Precision" page, "Dtype policy": each gradient in its own
+ *               leaf's dtype; "VRAM": h recomputed, up.down and its gradient
+ *               never formed).  W and the bias are the frozen base layer.
+ *               h and the gradient at h, gh = scale * dy_c . up_c, are each
+ *               rounded once to the storage dtype before their second dots,
+ *               as the forward rounds h; dx, dDown and dUp round once.
  *   rounding -- IEEE round-to-nearest, ties-to-even, directly from fp64 (never
  *               via fp32), gradual underflow, overflow to +-inf at or beyond
  *               max + half an ulp, NaN propagated.
@@ -372,5 +379,219 @@ int oracle_merge(const void* w, int w_dt, const void* down, int down_dt, const v
     free(th);
     free(dc);
     free(uc);
+    return OR_OK;
+}
+
+/* ---- the backward ---------------------------------------------------------- */
+
+/* Run fn(ctx, lo, hi) over [0, n) split into nthreads contiguous shares. */
+typedef void (*range_fn)(void* ctx, int64_t lo, int64_t hi);
+typedef struct {
+    range_fn fn;
+    void* ctx;
+    int64_t lo, hi;
+} range_job_t;
+
+static void* run_range(void* arg) {
+    range_job_t* J = (range_job_t*)arg;
+    J->fn(J->ctx, J->lo, J->hi);
+    return NULL;
+}
+
+static void par_for(int64_t n, int nthreads, range_fn fn, void* ctx) {
+    if (n <= 0) return;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > n) nthreads = (int)n;
+    range_job_t* jobs = (range_job_t*)calloc((size_t)nthreads, sizeof(range_job_t));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    int* started = (int*)calloc((size_t)nthreads, sizeof(int));
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t].fn = fn;
+        jobs[t].ctx = ctx;
+        jobs[t].lo = n * t / nthreads;
+        jobs[t].hi = n * (t + 1) / nthreads;
+    }
+    for (int t = 1; t < nthreads; ++t) started[t] = pthread_create(&th[t], NULL, run_range, &jobs[t]) == 0;
+    run_range(&jobs[0]);
+    for (int t = 1; t < nthreads; ++t) {
+        if (started[t]) pthread_join(th[t], NULL);
+        else run_range(&jobs[t]);
+    }
+    free(started);
+    free(jobs);
+    free(th);
+}
+
+typedef struct {
+    int64_t M, N, K, r;
+    double scale;
+    int c_dt, x_dt, down_dt, up_dt;
+    /* operands rounded to the compute dtype, binary64 */
+    const double *xc, *wc, *dc, *uc, *gc;   /* [M,K], [N,K], [r,K], [N,r], [M,N] */
+    /* rank columns evaluated for d_down and d_up */
+    const int64_t* js;
+    int64_t nj;
+    /* h_r and gh_r for every token, columns js: [M][nj] */
+    double *hj, *ghj;
+    /* dx rows */
+    const int64_t* dx_rows;
+    double* ghrow;                           /* [n_dx][r] gh_r of the dx rows */
+    void* dx;
+    double* dx_ref;
+    /* d_down[js][dd_cols], d_up[du_rows][js] */
+    const int64_t *dd_cols, *du_rows;
+    int64_t n_dd, n_du;
+    void *d_down, *d_up;
+    double *dd_ref, *du_ref;
+} bwd_t;
+
+/* h_r[m][j] = round_c(sum_k x_c[m,k] down_c[j,k]) -- the forward's h, recomputed */
+static double bwd_h(const bwd_t* B, int64_t m, int64_t j) {
+    double s = 0.0;
+    for (int64_t k = 0; k < B->K; ++k) s += B->xc[m * B->K + k] * B->dc[j * B->K + k];
+    return oracle_round(s, B->c_dt);
+}
+
+/* gh_r[m][j] = round_c(scale * sum_n dy_c[m,n] up_c[n,j]): the gradient at h,
+ * rounded to the storage dtype before its own second dots */
+static double bwd_gh(const bwd_t* B, int64_t m, int64_t j) {
+    double s = 0.0;
+    for (int64_t n = 0; n < B->N; ++n) s += B->gc[m * B->N + n] * B->uc[n * B->r + j];
+    return oracle_round(B->scale * s, B->c_dt);
+}
+
+static void bwd_tokens(void* ctx, int64_t lo, int64_t hi) {
+    bwd_t* B = (bwd_t*)ctx;
+    for (int64_t m = lo; m < hi; ++m)
+        for (int64_t t = 0; t < B->nj; ++t) {
+            if (B->hj) B->hj[m * B->nj + t] = bwd_h(B, m, B->js[t]);
+            if (B->ghj) B->ghj[m * B->nj + t] = bwd_gh(B, m, B->js[t]);
+        }
+}
+
+/* dx[m,k] = round_x( sum_n dy_c[m,n] W_c[n,k] + sum_j gh_r[m,j] down_c[j,k] ) */
+static void bwd_dx(void* ctx, int64_t lo, int64_t hi) {
+    bwd_t* B = (bwd_t*)ctx;
+    const int64_t N = B->N, K = B->K, r = B->r;
+    for (int64_t i = lo; i < hi; ++i) {
+        const int64_t m = B->dx_rows[i];
+        double* gh = B->ghrow + i * r;
+        for (int64_t j = 0; j < r; ++j) gh[j] = bwd_gh(B, m, j);
+        for (int64_t k = 0; k < K; ++k) {
+            double s = 0.0;
+            for (int64_t n = 0; n < N; ++n) s += B->gc[m * N + n] * B->wc[n * K + k];
+            double f = 0.0;
+            for (int64_t j = 0; j < r; ++j) f += gh[j] * B->dc[j * K + k];
+            const double v = s + f;
+            if (B->dx_ref) B->dx_ref[i * K + k] = v;
+            if (B->dx) store(B->dx, B->x_dt, i * K + k, oracle_round(v, B->x_dt));
+        }
+    }
+}
+
+/* d_down[j,k] = round_down( sum_m gh_r[m,j] x_c[m,k] ), over the columns k listed */
+static void bwd_ddown(void* ctx, int64_t lo, int64_t hi) {
+    bwd_t* B = (bwd_t*)ctx;
+    for (int64_t c = lo; c < hi; ++c) {
+        const int64_t k = B->dd_cols[c];
+        for (int64_t t = 0; t < B->nj; ++t) {
+            double s = 0.0;
+            for (int64_t m = 0; m < B->M; ++m) s += B->ghj[m * B->nj + t] * B->xc[m * B->K + k];
+            if (B->dd_ref) B->dd_ref[t * B->n_dd + c] = s;
+            if (B->d_down) store(B->d_down, B->down_dt, t * B->n_dd + c, oracle_round(s, B->down_dt));
+        }
+    }
+}
+
+/* d_up[n,j] = round_up( scale * sum_m dy_c[m,n] h_r[m,j] ), over the rows n listed */
+static void bwd_dup(void* ctx, int64_t lo, int64_t hi) {
+    bwd_t* B = (bwd_t*)ctx;
+    for (int64_t i = lo; i < hi; ++i) {
+        const int64_t n = B->du_rows[i];
+        for (int64_t t = 0; t < B->nj; ++t) {
+            double s = 0.0;
+            for (int64_t m = 0; m < B->M; ++m) s += B->gc[m * B->N + n] * B->hj[m * B->nj + t];
+            const double v = B->scale * s;
+            if (B->du_ref) B->du_ref[i * B->nj + t] = v;
+            if (B->d_up) store(B->d_up, B->up_dt, i * B->nj + t, oracle_round(v, B->up_dt));
+        }
+    }
+}
+
+/*
+ * The LoRA-bypass backward: the gradients of x, down and up given dy, the
+ * gradient of y (LyCORIS "Precision" page: "Dtype policy" -- each gradient
+ * comes back in its own leaf's dtype -- and "VRAM" -- h is recomputed, the
+ * product up.down and its gradient are never formed).  W and the bias are the
+ * frozen base layer: they get no gradient; the bias dtype (0: none) only
+ * takes part in the policy, so that the compute dtype is the forward's.
+ * The policy runs over (x, W, b, down, up, dy); with c the compute dtype:
+ *
+ *   h_r   = round_c( x_c . down_c^T )                  as in the forward
+ *   gh_r  = round_c( scale * dy_c . up_c )             [M, r], rounded once
+ *   dx    = round_x( dy_c . W_c + gh_r . down_c )      [M, K]
+ *   dDown = round_down( gh_r^T . x_c )                 [r, K]
+ *   dUp   = round_up( scale * dy_c^T . h_r )           [N, r]
+ *
+ * every sum in binary64, rounding only where written.  Outputs, each
+ * optional (NULL):
+ *   dx / dx_ref      [n_dx][K]  for the token rows dx_rows
+ *   gh_rows          [n_dx][r]  gh_r of those rows
+ *   d_down / dd_ref  [nj][n_dd] for the rank rows js and the columns dd_cols
+ *   d_up / du_ref    [n_du][nj] for the rows du_rows and the rank columns js
+ * Returns OR_OK, OR_MIXED_HALF or OR_INVALID, and the compute dtype.
+ */
+int oracle_backward(const void* x, int x_dt, const void* w, int w_dt, int b_dt, const void* down, int down_dt,
+                    const void* up, int up_dt, int64_t r, double scale, const void* dy, int dy_dt, int64_t M,
+                    int64_t N, int64_t K, const int64_t* dx_rows, int64_t n_dx, void* dx, double* dx_ref,
+                    double* gh_rows, const int64_t* js, int64_t nj, const int64_t* dd_cols, int64_t n_dd,
+                    void* d_down, double* dd_ref, const int64_t* du_rows, int64_t n_du, void* d_up,
+                    double* du_ref, int nthreads, int* c_out) {
+    int dts[6], nd = 0;
+    dts[nd++] = x_dt;
+    dts[nd++] = w_dt;
+    if (b_dt) dts[nd++] = b_dt;
+    dts[nd++] = down_dt;
+    dts[nd++] = up_dt;
+    dts[nd++] = dy_dt;
+    int c_dt, o_dt;
+    int st = oracle_resolve(dts, nd, &c_dt, &o_dt);
+    if (st != OR_OK) return st;
+    if (c_out) *c_out = c_dt;
+    if (M < 0 || N < 0 || K < 0 || r < 0 || n_dx < 0 || nj < 0 || n_dd < 0 || n_du < 0) return OR_INVALID;
+    for (int64_t i = 0; i < n_dx; ++i) if (dx_rows[i] < 0 || dx_rows[i] >= M) return OR_INVALID;
+    for (int64_t i = 0; i < nj; ++i) if (js[i] < 0 || js[i] >= r) return OR_INVALID;
+    for (int64_t i = 0; i < n_dd; ++i) if (dd_cols[i] < 0 || dd_cols[i] >= K) return OR_INVALID;
+    for (int64_t i = 0; i < n_du; ++i) if (du_rows[i] < 0 || du_rows[i] >= N) return OR_INVALID;
+
+    bwd_t B;
+    memset(&B, 0, sizeof(B));
+    B.M = M; B.N = N; B.K = K; B.r = r; B.scale = scale;
+    B.c_dt = c_dt; B.x_dt = x_dt; B.down_dt = down_dt; B.up_dt = up_dt;
+    double* xc = cast_all(x, x_dt, c_dt, M * K);
+    double* wc = cast_all(w, w_dt, c_dt, N * K);
+    double* dc = cast_all(down, down_dt, c_dt, r * K);
+    double* uc = cast_all(up, up_dt, c_dt, N * r);
+    double* gc = cast_all(dy, dy_dt, c_dt, M * N);
+    B.xc = xc; B.wc = wc; B.dc = dc; B.uc = uc; B.gc = gc;
+    B.js = js; B.nj = nj;
+    const int need_tokens = nj > 0 && (n_dd > 0 || n_du > 0);
+    double* hj = need_tokens && n_du > 0 ? (double*)malloc(sizeof(double) * (size_t)(M * nj > 0 ? M * nj : 1)) : NULL;
+    double* ghj = need_tokens && n_dd > 0 ? (double*)malloc(sizeof(double) * (size_t)(M * nj > 0 ? M * nj : 1)) : NULL;
+    B.hj = hj; B.ghj = ghj;
+    if (need_tokens) par_for(M, nthreads, bwd_tokens, &B);
+
+    double* ghr = (double*)malloc(sizeof(double) * (size_t)(n_dx * r > 0 ? n_dx * r : 1));
+    B.dx_rows = dx_rows; B.ghrow = ghr; B.dx = dx; B.dx_ref = dx_ref;
+    par_for(n_dx, nthreads, bwd_dx, &B);
+    if (gh_rows) memcpy(gh_rows, ghr, sizeof(double) * (size_t)(n_dx * r));
+
+    B.dd_cols = dd_cols; B.n_dd = n_dd; B.d_down = d_down; B.dd_ref = dd_ref;
+    if (ghj) par_for(n_dd, nthreads, bwd_ddown, &B);
+    B.du_rows = du_rows; B.n_du = n_du; B.d_up = d_up; B.du_ref = du_ref;
+    if (hj) par_for(n_du, nthreads, bwd_dup, &B);
+
+    free(xc); free(wc); free(dc); free(uc); free(gc);
+    free(hj); free(ghj); free(ghr);
     return OR_OK;
 }

@@ -38,6 +38,16 @@ MUTANTS = [
     ("merge-scale-ignored", "const double v = widen(J->w, J->w_dt, n * K + k) + J->scale * d;",
      "const double v = widen(J->w, J->w_dt, n * K + k) + d;"),
     ("merge-down-transposed", "d += J->uc[n * r + j] * J->dc[j * K + k];", "d += J->uc[n * r + j] * J->dc[k * r + j];"),
+    ("bwd-gh-not-rounded", "return oracle_round(B->scale * s, B->c_dt);", "return B->scale * s;"),
+    ("bwd-gh-scale-missing", "return oracle_round(B->scale * s, B->c_dt);", "return oracle_round(s, B->c_dt);"),
+    ("bwd-gh-up-transposed", "s += B->gc[m * B->N + n] * B->uc[n * B->r + j];",
+     "s += B->gc[m * B->N + n] * B->uc[(j * B->N + n) % (B->N * B->r)];"),
+    ("bwd-dx-fold-dropped", "const double v = s + f;", "const double v = s;"),
+    ("bwd-dup-scale-missing", "const double v = B->scale * s;", "const double v = s;"),
+    ("bwd-ddown-uses-x-not-cast", "double* xc = cast_all(x, x_dt, c_dt, M * K);\n    double* wc = cast_all(w, w_dt, c_dt, N * K);\n    double* dc = cast_all(down, down_dt, c_dt, r * K);\n    double* uc = cast_all(up, up_dt, c_dt, N * r);\n    double* gc",
+     "double* xc = cast_all(x, x_dt, x_dt, M * K);\n    double* wc = cast_all(w, w_dt, c_dt, N * K);\n    double* dc = cast_all(down, down_dt, c_dt, r * K);\n    double* uc = cast_all(up, up_dt, c_dt, N * r);\n    double* gc"),
+    ("bwd-dx-rounded-to-compute", "if (B->dx) store(B->dx, B->x_dt, i * K + k, oracle_round(v, B->x_dt));",
+     "if (B->dx) store(B->dx, B->x_dt, i * K + k, oracle_round(oracle_round(v, B->c_dt), B->x_dt));"),
 ]
 
 

@@ -440,3 +440,174 @@ def test_ulp_report():
     assert mx == 1.0 and rms == pytest.approx(np.sqrt((1 + 0.25) / 4))
     assert oracle.ulp_of(1.0, BF16) == 2.0 ** -7
     assert oracle.ulp_of(1.0, F32) == 2.0 ** -23
+
+
+# ---- the backward ------------------------------------------------------------------
+#
+# Pinned against the forward map itself: for y = x W^T + scale (x down^T) up^T
+# the loss L = sum(dy * y) is linear in each of x, down and up when the other
+# two are held, so every partial derivative is exactly L(theta + e_i) - L(theta).
+# With small-integer inputs nothing rounds anywhere (h, gh and every gradient
+# are exact in the storage dtype), so the oracle's gradients must equal these
+# exact differences bit for bit.  That pins which operand meets which, every
+# transpose and where scale enters, independently of the backward formula.
+
+
+def _int_draw(rng, shape, lim, dt):
+    v = rng.integers(-lim, lim + 1, size=shape).astype(np.float64)
+    return oracle.encode(v.ravel(), dt).reshape(shape), v
+
+
+def _loss(x, w, down, up, dy, scale):
+    """sum(dy * y) of the unrounded forward, in exact rationals."""
+    M, K = x.shape
+    N, r = up.shape
+    L = Fraction(0)
+    for m in range(M):
+        h = [sum(Fraction(x[m, k]) * Fraction(down[j, k]) for k in range(K)) for j in range(r)]
+        for n in range(N):
+            y = sum(Fraction(x[m, k]) * Fraction(w[n, k]) for k in range(K))
+            y += scale * sum(h[j] * Fraction(up[n, j]) for j in range(r))
+            L += Fraction(dy[m, n]) * y
+    return L
+
+
+def _exact_grad(theta, bump):
+    """Partial derivatives of a function linear in theta: f(theta + e_i) - f(theta)."""
+    base = bump(theta)
+    g = np.zeros(theta.shape)
+    for idx in np.ndindex(*theta.shape):
+        t = theta.copy()
+        t[idx] += 1
+        g[idx] = float(bump(t) - base)
+    return g
+
+
+BWD_EXACT = [  # (dtype, lim, scale, M, N, K, r)
+    (F16, 3, Fraction(1, 2), 3, 4, 5, 2), (F16, 2, Fraction(2), 2, 3, 4, 3),
+    (BF16, 1, Fraction(1, 2), 3, 4, 5, 2), (F32, 3, Fraction(3, 4), 3, 3, 4, 2),
+]
+
+
+@pytest.mark.parametrize("case", BWD_EXACT)
+def test_backward_is_the_exact_gradient_of_the_forward(case):
+    dt, lim, scale, M, N, K, r = case
+    rng = np.random.default_rng(M * 7 + r)
+    xs, x = _int_draw(rng, (M, K), lim, dt)
+    ws, w = _int_draw(rng, (N, K), lim, dt)
+    ds, d = _int_draw(rng, (r, K), lim, dt)
+    us, u = _int_draw(rng, (N, r), lim, dt)
+    gs, g = _int_draw(rng, (M, N), lim, dt)
+    res = oracle.backward(xs, dt, ws, dt, ds, dt, us, dt, gs, dt, scale=float(scale))
+    want_dx = _exact_grad(x, lambda t: _loss(t, w, d, u, g, scale))
+    want_dd = _exact_grad(d, lambda t: _loss(x, w, t, u, g, scale))
+    want_du = _exact_grad(u, lambda t: _loss(x, w, d, t, g, scale))
+    np.testing.assert_array_equal(oracle.as_float64(res["dx"], dt), want_dx)
+    np.testing.assert_array_equal(oracle.as_float64(res["d_down"], dt), want_dd)
+    np.testing.assert_array_equal(oracle.as_float64(res["d_up"], dt), want_du)
+    assert np.any(want_dd != 0) and np.any(want_du != 0)
+
+
+def test_backward_gh_rounded_once_fixture():
+    """fp16, M = K = r = 1, N = 2.  gh = scale * dy.up = 1 + 2^-11 + 2^-20 lies
+    just above the midpoint 1 + 2^-11 and rounds to gh_r = 1 + 2^-10; then
+    dx = dy.W + gh_r.down = (-1 - 2^-10) + (1 + 2^-10) = 0 exactly.  Without
+    the rounding of gh, dx would be -2^-11 + 2^-20 (-4.87e-4, beyond the fp16
+    bound 2e-4 of the Luminal page); with gh truncated, -2^-10."""
+    enc = lambda v, s: oracle.encode(np.array(v, dtype=np.float64).ravel(), F16).reshape(s)
+    x, w = enc([1.0], (1, 1)), enc([-1.0, -(2.0 ** -10)], (2, 1))
+    down, up = enc([1.0], (1, 1)), enc([1.0, 2.0 ** -11 + 2.0 ** -20], (2, 1))
+    dy = enc([1.0, 1.0], (1, 2))
+    res = oracle.backward(x, F16, w, F16, down, F16, up, F16, dy, F16, scale=1.0)
+    assert res["gh"][0, 0] == 1.0 + 2.0 ** -10
+    assert oracle.as_float64(res["dx"], F16)[0, 0] == 0.0
+    assert oracle.as_float64(res["d_down"], F16)[0, 0] == 1.0 + 2.0 ** -10     # gh_r . x
+    assert oracle.as_float64(res["d_up"], F16)[:, 0].tolist() == [1.0, 1.0]     # dy^T . h_r, h_r = 1
+    unrounded = -1.0 - 2.0 ** -10 + 1.0 + 2.0 ** -11 + 2.0 ** -20
+    assert abs(unrounded) > oracle.tolerance(np.array([0.0]), F16, 2, 1)[0]
+
+
+@pytest.mark.parametrize("dt", [F16, BF16, F32])
+def test_backward_closed_forms(dt):
+    rng = np.random.default_rng(21)
+    M, N, K, r = 5, 6, 8, 3
+    x, w, d, u, g = (_draw(rng, s, dt, 0.5) for s in ((M, K), (N, K), (r, K), (N, r), (M, N)))
+    # dx with no bypass is the plain product dy . W: the (pinned) forward of dy with W^T
+    wt = np.ascontiguousarray(w.reshape(N, K).T)
+    plain = oracle.forward(g, dt, wt, dt, None, None, None, None, None, None, lora=False)["y"]
+    for kw in (dict(scale=0.0, up=np.zeros_like(u)), dict(scale=1.5, up=np.zeros_like(u))):
+        res = oracle.backward(x, dt, w, dt, d, dt, kw["up"], dt, g, dt, scale=kw["scale"])
+        np.testing.assert_array_equal(res["dx"], plain)
+        assert not np.any(oracle.as_float64(res["d_down"], dt))
+    res = oracle.backward(x, dt, w, dt, d, dt, u, dt, g, dt, scale=0.0)
+    np.testing.assert_array_equal(res["dx"], plain)
+    assert not np.any(oracle.as_float64(res["d_up"], dt)) and not np.any(oracle.as_float64(res["d_down"], dt))
+    res = oracle.backward(x, dt, w, dt, np.zeros_like(d), dt, u, dt, g, dt, scale=1.5)   # h = 0
+    assert not np.any(oracle.as_float64(res["d_up"], dt))
+
+
+def test_backward_recomputes_the_forward_h():
+    """With dy = e_(m,n) and scale 1, dUp[n, :] = h_r[m, :]: the forward's rounded h."""
+    rng = np.random.default_rng(22)
+    M, N, K, r = 4, 3, 16, 4
+    x, w, d, u = (_draw(rng, s, BF16) for s in ((M, K), (N, K), (r, K), (N, r)))
+    h = oracle.forward(x, BF16, w, BF16, None, None, d, BF16, u, BF16, scale=1.0)["h"]
+    for m, n in ((0, 0), (3, 2), (2, 1)):
+        g = np.zeros((M, N))
+        g[m, n] = 1.0
+        res = oracle.backward(x, BF16, w, BF16, d, BF16, u, BF16, oracle.encode(g.ravel(), BF16).reshape(M, N),
+                              BF16, scale=1.0)
+        np.testing.assert_array_equal(oracle.as_float64(res["d_up"], BF16)[n], h[m])
+
+
+def test_backward_invariants_and_subsets():
+    rng = np.random.default_rng(23)
+    M, N, K, r = 6, 5, 16, 3
+    dt = F16
+    x, w, d, u, g = (_draw(rng, s, dt, 0.5) for s in ((M, K), (N, K), (r, K), (N, r), (M, N)))
+    full = oracle.backward(x, dt, w, dt, d, dt, u, dt, g, dt, scale=0.75)
+    # dy doubled: every gradient doubles exactly (no overflow or underflow here)
+    g2 = oracle.encode(2 * oracle.as_float64(g, dt).ravel(), dt).reshape(M, N)
+    dbl = oracle.backward(x, dt, w, dt, d, dt, u, dt, g2, dt, scale=0.75)
+    for key in ("dx", "d_down", "d_up"):
+        np.testing.assert_array_equal(oracle.as_float64(dbl[key], dt), 2 * oracle.as_float64(full[key], dt))
+    # index subsets select the same values
+    sub = oracle.backward(x, dt, w, dt, d, dt, u, dt, g, dt, scale=0.75, dx_rows=[5, 0, 0], js=[2, 0],
+                          dd_cols=[15, 3], du_rows=[4, 1])
+    np.testing.assert_array_equal(sub["dx"], full["dx"][[5, 0, 0]])
+    np.testing.assert_array_equal(sub["d_down"], full["d_down"][np.ix_([2, 0], [15, 3])])
+    np.testing.assert_array_equal(sub["d_up"], full["d_up"][np.ix_([4, 1], [2, 0])])
+
+
+def test_backward_policy():
+    rng = np.random.default_rng(24)
+    M, N, K, r = 2, 3, 4, 2
+    x, w = _draw(rng, (M, K), F32), _draw(rng, (N, K), F32)
+    d, u = _draw(rng, (r, K), BF16), _draw(rng, (N, r), BF16)
+    g = _draw(rng, (M, N), F32)
+    res = oracle.backward(x, F32, w, F32, d, BF16, u, BF16, g, F32)
+    assert res["compute"] == BF16
+    assert res["dx"].dtype == np.float32 and res["d_down"].dtype == np.uint16 and res["d_up"].dtype == np.uint16
+    assert oracle.backward(x, F32, w, F32, d, F32, u, F32, g, F32, b_dt=F16)["compute"] == F16   # the bias counts
+    with pytest.raises(oracle.OracleError):
+        oracle.backward(x, F32, w, F32, d, BF16, u, BF16, _draw(rng, (M, N), F16), F16)
+
+
+def test_backward_mixed_dtype_fixture():
+    """x, W, dy and down in fp32, up in fp16: the compute dtype is fp16.
+    x = 1 + 2^-12 rounds to x_c = 1; dy = [1, 2^-12] is exact in fp16; up =
+    [1, 0] gives gh_r = 1 and h_r = x_c . down_c = 1.  Then
+      dx    = dy_c.W_c + gh_r.down_c = (1 + 2^-12) + 1 = 2 + 2^-12, kept in
+              fp32 (x's dtype), not rounded through fp16 (which gives 2);
+      dDown = gh_r . x_c = 1 (with the uncast x it would be 1 + 2^-12, and
+              down's dtype fp32 would keep that);
+      dUp   = dy_c^T . h_r = [1, 2^-12] in fp16."""
+    f32 = lambda v, s: np.array(v, dtype=np.float32).reshape(s)
+    x, w, down, dy = f32([1 + 2.0 ** -12], (1, 1)), f32([1.0, 1.0], (2, 1)), f32([1.0], (1, 1)), f32([1.0, 2.0 ** -12], (1, 2))
+    up = oracle.encode(np.array([1.0, 0.0]), F16).reshape(2, 1)
+    res = oracle.backward(x, F32, w, F32, down, F32, up, F16, dy, F32, scale=1.0)
+    assert res["compute"] == F16
+    assert res["gh"][0, 0] == 1.0
+    assert float(res["dx"][0, 0]) == 2.0 + 2.0 ** -12
+    assert float(res["d_down"][0, 0]) == 1.0
+    assert oracle.as_float64(res["d_up"], F16)[:, 0].tolist() == [1.0, 2.0 ** -12]
