@@ -182,6 +182,53 @@ int lyc_lora_merge_fwd(const void* w, int w_dt, const void* down, int down_dt, c
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * LoRA-bypass backward (LyCORIS "Precision" page: "Dtype policy" -- each
+ * gradient comes back in its own leaf's dtype -- and "VRAM" -- h is
+ * recomputed, up.down and its gradient are never formed).  Given dy [M,N],
+ * the gradient of y, with c the compute dtype of the dtype policy over
+ * (x, W, b, down, up, dy):
+ *   h_r   = round_c( x_c . down_c^T )                 recomputed as the forward computes it
+ *   gh_r  = round_c( scale * dy_c . up_c )            [M, rank], rounded once from its exact
+ *                                                     value (the same guard as h)
+ *   dx    = round_x( dy_c . W_c + gh_r . down_c )     [M, K] in x's dtype
+ *   dDown = round_down( gh_r^T . x_c )                [rank, K] in down's dtype
+ *   dUp   = round_up( scale * dy_c^T . h_r )          [N, rank] in up's dtype
+ * fp32 accumulation, one final rounding each (dUp: the fp32 sum times scale
+ * in fp32, then rounded).  W and the bias are the frozen base layer: no
+ * gradient; bias_dt (0: none) only enters the policy, so that c is the
+ * forward's.  Layouts as in the forward; dy row-major [M,N].
+ *  - dx, d_down, d_up: device outputs; a NULL one is not computed (and what
+ *    only it needs is skipped).  They must not overlap any input or each
+ *    other (LYC_ERR_INVALID_ARG).  Element alignment suffices.
+ *  - K and N multiples of 8; M, N, K <= 2^20, rank <= 256
+ *    (LYC_ERR_UNSUPPORTED).  x (when it is read in the compute dtype, i.e.
+ *    x_dt == c) and dy (likewise) must be 16-byte aligned; W, down, up need
+ *    element alignment.  M == 0 gives zero dDown and dUp.
+ *  - The workspace (256-byte aligned) holds h_r, gh_r, the guard's splits and
+ *    norms, compute-dtype copies of fp32 x/dy, and transposed compute-dtype
+ *    copies of W, down, up, x, dy, h_r and gh_r (the token contractions read
+ *    both operands along the token index); its size comes from
+ *    lyc_lora_linear_bwd_workspace_size with `want` = 1 (dx) | 2 (dDown) |
+ *    4 (dUp), the set of non-NULL outputs of the call.
+ * Same stream, ownership and error conventions as the forward.
+ */
+int lyc_lora_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt,
+                                       int bias_dt, int down_dt, int up_dt, int dy_dt, int want, size_t* bytes);
+int lyc_lora_linear_bwd(const void* x, int x_dt, const void* w, int w_dt, int bias_dt, const void* down,
+                        int down_dt, const void* up, int up_dt, int64_t rank, double scale, const void* dy,
+                        int dy_dt, void* dx, void* d_down, void* d_up, int64_t M, int64_t N, int64_t K,
+                        void* workspace, size_t workspace_bytes, void* stream);
+/*
+ * Where lyc_lora_linear_bwd leaves h_r and gh_r in its workspace (both
+ * [M][ld] in the compute dtype; SIZE_MAX when the call set `want` does not
+ * compute them) and the uint32 count of gh elements its guard re-evaluated
+ * in fp64 (16-bit compute; else SIZE_MAX).  Same argument errors as the size query.
+ */
+int lyc_lora_linear_bwd_workspace_layout(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt,
+                                         int bias_dt, int down_dt, int up_dt, int dy_dt, int want,
+                                         size_t* h_offset, size_t* gh_offset, int64_t* ld, size_t* flagged_offset);
+
+/*
  * Output tile (rows of W x rows of x) that the forward calls use for an
  * M x N problem in compute dtype compute_dt; one workgroup computes one tile.
  * Host only.  Returns LYC_ERR_INVALID_ARG for negative sizes or an unknown

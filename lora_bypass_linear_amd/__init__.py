@@ -14,8 +14,9 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 __all__ = ["F16", "BF16", "F32", "LycError", "MixedHalfError", "lib", "resolve_dtypes", "linear", "lora_linear",
-           "lora_merge", "linear_workspace_size", "lora_workspace_size", "lora_workspace_layout",
-           "linear_workspace_layout", "lora_merge_workspace_size", "gemm_tile", "profile_begin", "profile_end",
+           "lora_merge", "lora_linear_backward", "linear_workspace_size", "lora_workspace_size", "lora_workspace_layout",
+           "linear_workspace_layout", "lora_merge_workspace_size", "lora_bwd_workspace_size",
+           "lora_bwd_workspace_layout", "gemm_tile", "profile_begin", "profile_end",
            "dtype_code", "torch_dtype"]
 
 F16, BF16, F32 = 1, 2, 3
@@ -61,6 +62,15 @@ def lib():
         L.lyc_lora_merge_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_int, c_int, c_int, ctypes.POINTER(c_sz)]
         L.lyc_lora_merge_fwd.argtypes = [c_vp, c_int, c_vp, c_int, c_vp, c_int, c_i64, ctypes.c_double, c_vp, c_int,
                                          c_i64, c_i64, c_vp, c_sz, c_vp]
+        L.lyc_lora_linear_bwd_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_i64, c_int, c_int, c_int, c_int,
+                                                         c_int, c_int, c_int, ctypes.POINTER(c_sz)]
+        L.lyc_lora_linear_bwd.argtypes = [c_vp, c_int, c_vp, c_int, c_int, c_vp, c_int, c_vp, c_int, c_i64,
+                                          ctypes.c_double, c_vp, c_int, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64,
+                                          c_vp, c_sz, c_vp]
+        L.lyc_lora_linear_bwd_workspace_layout.argtypes = [c_i64, c_i64, c_i64, c_i64, c_int, c_int, c_int, c_int,
+                                                           c_int, c_int, c_int, ctypes.POINTER(c_sz),
+                                                           ctypes.POINTER(c_sz), ctypes.POINTER(c_i64),
+                                                           ctypes.POINTER(c_sz)]
         L.lyc_gemm_tile.argtypes = [c_i64, c_i64, c_int, ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
         L.lyc_profile_begin.argtypes = [c_int]
         L.lyc_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_int)]
@@ -69,6 +79,7 @@ def lib():
         for fn in (L.lyc_resolve_dtypes, L.lyc_linear_workspace_size, L.lyc_linear_fwd,
                    L.lyc_lora_linear_workspace_size, L.lyc_lora_linear_fwd, L.lyc_lora_workspace_layout,
                    L.lyc_linear_workspace_layout, L.lyc_lora_merge_workspace_size, L.lyc_lora_merge_fwd,
+                   L.lyc_lora_linear_bwd_workspace_size, L.lyc_lora_linear_bwd, L.lyc_lora_linear_bwd_workspace_layout,
                    L.lyc_gemm_tile, L.lyc_profile_begin, L.lyc_profile_end):
             fn.restype = c_int
         _lib = L
@@ -155,6 +166,26 @@ def lora_merge_workspace_size(N, K, r, w_dt, d_dt, u_dt) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().lyc_lora_merge_workspace_size(N, K, r, w_dt, d_dt, u_dt, ctypes.byref(n)))
     return n.value
+
+
+BWD_DX, BWD_DDOWN, BWD_DUP = 1, 2, 4
+
+
+def lora_bwd_workspace_size(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt, dy_dt, want=7) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().lyc_lora_linear_bwd_workspace_size(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt, dy_dt, want,
+                                                    ctypes.byref(n)))
+    return n.value
+
+
+def lora_bwd_workspace_layout(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt, dy_dt, want=7):
+    """(h_offset, gh_offset, ld, flagged_offset) inside the backward's workspace
+    (an offset of 2^64-1: not computed for this `want`)."""
+    ho, go, ld, fo = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_int64(0), ctypes.c_size_t(0)
+    _check(lib().lyc_lora_linear_bwd_workspace_layout(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt, dy_dt, want,
+                                                      ctypes.byref(ho), ctypes.byref(go), ctypes.byref(ld),
+                                                      ctypes.byref(fo)))
+    return ho.value, go.value, ld.value, fo.value
 
 
 def gemm_tile(M: int, N: int, compute_dt: int) -> Tuple[int, int]:
@@ -249,3 +280,31 @@ def lora_merge(w: torch.Tensor, down: torch.Tensor, up: torch.Tensor, scale: flo
     _check(lib().lyc_lora_merge_fwd(_ptr(w), w_dt, _ptr(down), d_dt, _ptr(up), u_dt, r, float(scale), _ptr(out),
                                     dtype_code(out), N, K, _ptr(ws), nbytes, _stream(dev)))
     return out
+
+
+def lora_linear_backward(x: torch.Tensor, w: torch.Tensor, down: torch.Tensor, up: torch.Tensor, scale: float,
+                         dy: torch.Tensor, bias_dtype: Optional[torch.dtype] = None, want_dx: bool = True,
+                         want_ddown: bool = True, want_dup: bool = True, workspace: Optional[torch.Tensor] = None,
+                         return_workspace: bool = False):
+    """Gradients (dx, d_down, d_up) of the LoRA-bypass linear for dy, each in
+    its leaf's dtype (None where not wanted).  W and the bias are frozen;
+    ``bias_dtype`` is the forward's bias dtype (it enters the dtype policy)."""
+    dev = _need_device(x, w, down, up, dy)
+    M, K = x.shape
+    N = w.shape[0]
+    r = down.shape[0]
+    x_dt, w_dt, d_dt, u_dt, g_dt = (dtype_code(t) for t in (x, w, down, up, dy))
+    b_dt = dtype_code(torch.empty(0, dtype=bias_dtype)) if bias_dtype is not None else 0
+    want = (BWD_DX if want_dx else 0) | (BWD_DDOWN if want_ddown else 0) | (BWD_DUP if want_dup else 0)
+    dx = torch.empty((M, K), dtype=x.dtype, device=dev) if want_dx else None
+    dd = torch.empty((r, K), dtype=down.dtype, device=dev) if want_ddown else None
+    du = torch.empty((N, r), dtype=up.dtype, device=dev) if want_dup else None
+    ws = _workspace(lora_bwd_workspace_size(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt, g_dt, want), dev, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    # an empty output still has to be passed (non-NULL) to be "wanted"
+    p = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr() if t.numel() else 256)
+    _check(lib().lyc_lora_linear_bwd(_ptr(x), x_dt, _ptr(w), w_dt, b_dt, _ptr(down), d_dt, _ptr(up), u_dt, r,
+                                     float(scale), _ptr(dy), g_dt, p(dx), p(dd), p(du), M, N, K, _ptr(ws), nbytes,
+                                     _stream(dev)))
+    out = (dx, dd, du)
+    return (out, ws) if return_workspace else out

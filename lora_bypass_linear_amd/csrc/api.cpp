@@ -6,9 +6,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
+#include "bwd.h"
 #include "kernels.h"
 #include "merge.h"
 
@@ -214,6 +216,7 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
         xp.bias = bias;
         xp.bias_dt = P.b_dt;
         xp.vec_store = (P.N % 4 == 0) && aligned(y, y_dt == LYC_F32 ? 16 : 8);
+        xp.scale = 1.0;
         if (timed(LYC_KERNEL_GEMM, s, [&] { return lyc::launch_xr(P.c_dt, xp, s); }) != hipSuccess) return LYC_ERR_HIP;
         return LYC_OK;
     }
@@ -231,6 +234,7 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
     g.scale = (float)scale;
     g.rf = 0;
     g.ksplit = L.ksplit;
+    g.post = 1.0f;
     g.partial = L.ksplit > 1 ? (float*)(W + L.partial) : nullptr;
     const uintptr_t vec_align = y_dt == LYC_F32 ? 16 : 8;
     g.vec_store = (P.N % 4 == 0) && aligned(y, vec_align);
@@ -270,6 +274,7 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
         hp.mode = lyc::XR_H;
         hp.out = W + L.h;
         hp.ld_out = P.r_pad;
+        hp.scale = 1.0;
         if (timed(LYC_KERNEL_HPASS, s, [&] { return lyc::launch_xr(P.c_dt, hp, s); }) != hipSuccess)
             return LYC_ERR_HIP;
 
@@ -359,9 +364,355 @@ int merge(const Merge& G, const void* w, const void* down, const void* up, doubl
     return LYC_OK;
 }
 
+// ---- LoRA-bypass backward ------------------------------------------------------
+enum { BWD_DX = 1, BWD_DDOWN = 2, BWD_DUP = 4 };
+
+struct Bwd {
+    Problem P;       // the forward's problem; c_dt resolved over (x, W, b, down, up, dy)
+    int dy_dt;
+    int want;        // BWD_* bits
+    int64_t M8;      // tokens rounded up to 8: row length of the transposed token-major copies
+};
+
+struct BwdLayout {
+    size_t xc = 0, gc = 0, dc = 0, dh = 0, dl = 0, uc = 0, dnorm = 0, flag_h = 0, h = 0, ut = 0, uth = 0, utl = 0,
+           unorm = 0, flag_g = 0, gh = 0, wt = 0, dt = 0, xt = 0, ght = 0, dyt = 0, ht = 0, partial = 0, total = 0;
+    bool cast_x = false, cast_g = false, need_h = false, need_gh = false;
+    int ks_dx = 1, ks_dd = 1, ks_du = 1;
+};
+
+int check_bwd(Bwd& B) {
+    Problem& P = B.P;
+    if (P.M < 0 || P.N < 0 || P.K < 0 || P.rank < 0 || B.want < 0 || B.want > 7) return LYC_ERR_INVALID_ARG;
+    if (!valid_dt(P.x_dt) || !valid_dt(P.w_dt) || !valid_dt(P.d_dt) || !valid_dt(P.u_dt) || !valid_dt(B.dy_dt))
+        return LYC_ERR_INVALID_ARG;
+    if (P.b_dt != 0 && !valid_dt(P.b_dt)) return LYC_ERR_INVALID_ARG;
+    int dts[6], n = 0;
+    dts[n++] = P.x_dt;
+    dts[n++] = P.w_dt;
+    if (P.b_dt != 0) dts[n++] = P.b_dt;
+    dts[n++] = P.d_dt;
+    dts[n++] = P.u_dt;
+    dts[n++] = B.dy_dt;
+    const int st = resolve(dts, n, &P.c_dt, &P.o_dt);
+    if (st != LYC_OK) return st;
+    // every dimension is the contraction length of one of the products (M of
+    // dDown and dUp, N of dx and gh, K of h): the limit of K in the forward
+    if (P.M > MAX_K || P.N > MAX_K || P.K > MAX_K) return LYC_ERR_UNSUPPORTED;
+    if (P.K % 8 != 0 || P.N % 8 != 0) return LYC_ERR_UNSUPPORTED;
+    if (P.rank > MAX_RANK) return LYC_ERR_UNSUPPORTED;
+    P.r_pad = P.rank == 0 ? 0 : (P.rank <= 16 && P.c_dt != LYC_F32) ? 16 : (P.rank <= 32 ? 32 : P.rank <= 64 ? 64 : P.rank <= 128 ? 128 : 256);
+    B.M8 = (P.M + 7) & ~(int64_t)7;
+    return LYC_OK;
+}
+
+BwdLayout bwd_layout(const Bwd& B) {
+    const Problem& P = B.P;
+    BwdLayout L;
+    size_t off = 0;
+    const size_t ce = esize(P.c_dt);
+    const bool split = P.c_dt != LYC_F32;
+    const bool dx = B.want & BWD_DX, dd = (B.want & BWD_DDOWN) && P.rank > 0, du = (B.want & BWD_DUP) && P.rank > 0;
+    L.need_h = du;                          // h_r feeds dUp only
+    L.need_gh = P.rank > 0 && (dx || dd);   // gh_r feeds dx's fold and dDown
+    L.cast_x = P.x_dt == LYC_F32 && P.c_dt != LYC_F32 && L.need_h;
+    L.cast_g = B.dy_dt == LYC_F32 && P.c_dt != LYC_F32 && (L.need_gh || dx);
+    auto take = [&](size_t& at, size_t bytes) { at = off; off = align256(off + bytes); };
+    const size_t M = (size_t)P.M, N = (size_t)P.N, K = (size_t)P.K, R = (size_t)P.r_pad, M8 = (size_t)B.M8;
+    if (L.cast_x) take(L.xc, M * K * 2);
+    if (L.cast_g) take(L.gc, M * N * 2);
+    if (L.need_h) {
+        take(L.dc, R * K * ce);
+        if (split) { take(L.dh, R * K * ce); take(L.dl, R * K * ce); }
+        take(L.uc, N * R * ce);
+        take(L.dnorm, R * 2 * sizeof(double));
+        take(L.flag_h, sizeof(unsigned));
+        take(L.h, M * R * ce);
+    }
+    if (L.need_gh) {
+        take(L.ut, R * N * ce);
+        if (split) { take(L.uth, R * N * ce); take(L.utl, R * N * ce); }
+        take(L.unorm, R * 2 * sizeof(double));
+        take(L.flag_g, sizeof(unsigned));
+        take(L.gh, M * R * ce);
+    }
+    size_t part = 0;
+    if (dx) {
+        take(L.wt, K * N * ce);
+        if (P.rank > 0) take(L.dt, K * R * ce);
+        L.ks_dx = lyc::gemm_ksplit(P.M, P.K, P.N, P.c_dt);
+        if (L.ks_dx > 1) part = std::max(part, (size_t)L.ks_dx * M * K * 4);
+    }
+    if (dd) {
+        take(L.xt, K * M8 * ce);
+        take(L.ght, R * M8 * ce);
+        L.ks_dd = lyc::gemm_ksplit(P.rank, P.K, B.M8, P.c_dt);
+        if (L.ks_dd > 1) part = std::max(part, (size_t)L.ks_dd * (size_t)P.rank * K * 4);
+    }
+    if (du) {
+        take(L.dyt, N * M8 * ce);
+        take(L.ht, R * M8 * ce);
+        L.ks_du = lyc::gemm_ksplit(P.N, P.rank, B.M8, P.c_dt);
+        if (L.ks_du > 1) part = std::max(part, (size_t)L.ks_du * N * (size_t)P.rank * 4);
+    }
+    if (part > 0) take(L.partial, part);
+    L.total = off;
+    return L;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+int backward(const Bwd& B, const void* x, const void* w, const void* down, const void* up, double scale,
+             const void* dy, void* dx, void* d_down, void* d_up, void* ws, size_t ws_bytes, void* stream) {
+    const Problem& P = B.P;
+    if (!(scale == scale) || scale > 3.4e38 || scale < -3.4e38) return LYC_ERR_INVALID_ARG;
+    const bool wdx = B.want & BWD_DX, wdd = B.want & BWD_DDOWN, wdu = B.want & BWD_DUP;
+    const int64_t M = P.M, N = P.N, K = P.K, r = P.rank;
+    // which inputs the wanted gradients read
+    const bool use_x = (wdd || wdu) && r > 0 && M > 0 && K > 0;
+    const bool use_dy = M > 0 && N > 0 && (wdx || r > 0);
+    const bool use_w = wdx && M > 0 && N > 0 && K > 0;
+    const bool use_f = r > 0 && M > 0;
+    if ((use_x && x == nullptr) || (use_dy && dy == nullptr) || (use_w && w == nullptr) ||
+        (use_f && (down == nullptr || up == nullptr)))
+        return LYC_ERR_INVALID_ARG;
+    const size_t ndx = (size_t)(M * K) * esize(P.x_dt), ndd = (size_t)(r * K) * esize(P.d_dt),
+                 ndu = (size_t)(N * r) * esize(P.u_dt);
+    if ((wdx && ndx > 0 && dx == nullptr) || (wdd && ndd > 0 && d_down == nullptr) || (wdu && ndu > 0 && d_up == nullptr))
+        return LYC_ERR_INVALID_ARG;
+    // alignment: rows read in place by the contractions need 16 bytes
+    const bool x_in_place = use_x && P.x_dt == P.c_dt, dy_in_place = use_dy && B.dy_dt == P.c_dt;
+    if ((x_in_place && !aligned(x, 16)) || (dy_in_place && !aligned(dy, 16))) return LYC_ERR_UNSUPPORTED;
+    if ((w && !aligned(w, esize(P.w_dt))) || (down && !aligned(down, esize(P.d_dt))) ||
+        (up && !aligned(up, esize(P.u_dt))) || (x && !aligned(x, esize(P.x_dt))) ||
+        (dy && !aligned(dy, esize(B.dy_dt))))
+        return LYC_ERR_UNSUPPORTED;
+    if ((wdx && dx && !aligned(dx, esize(P.x_dt))) || (wdd && d_down && !aligned(d_down, esize(P.d_dt))) ||
+        (wdu && d_up && !aligned(d_up, esize(P.u_dt))))
+        return LYC_ERR_UNSUPPORTED;
+    // the gradients overlap neither the inputs nor each other
+    const void* ins[5] = {x, w, down, up, dy};
+    const size_t nin[5] = {(size_t)(M * K) * esize(P.x_dt), (size_t)(N * K) * esize(P.w_dt),
+                           (size_t)(r * K) * esize(P.d_dt), (size_t)(N * r) * esize(P.u_dt),
+                           (size_t)(M * N) * esize(B.dy_dt)};
+    void* outs[3] = {wdx ? dx : nullptr, wdd ? d_down : nullptr, wdu ? d_up : nullptr};
+    const size_t nout[3] = {ndx, ndd, ndu};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 5; ++j)
+            if (overlaps(outs[i], nout[i], ins[j], nin[j])) return LYC_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(outs[i], nout[i], outs[j], nout[j])) return LYC_ERR_INVALID_ARG;
+    }
+    const BwdLayout L = bwd_layout(B);
+    if (L.total > 0 && (ws == nullptr || ws_bytes < L.total || !aligned(ws, 256))) return LYC_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    char* W = (char*)ws;
+    (void)hipGetLastError();
+    const bool split = P.c_dt != LYC_F32;
+    auto transpose = [&](const void* src, int src_dt, int64_t rows, int64_t cols, void* dst, int64_t rows_pad,
+                         int64_t cols_pad) {
+        lyc::TransposeParams tp{src, src_dt, rows, cols, dst, P.c_dt, rows_pad, cols_pad};
+        return timed(LYC_KERNEL_CAST, s, [&] { return lyc::launch_transpose(tp, s); }) == hipSuccess;
+    };
+    auto gemm = [&](lyc::GemmParams& g) {
+        return timed(LYC_KERNEL_GEMM, s, [&] { return lyc::launch_gemm(P.c_dt, g, s); }) == hipSuccess;
+    };
+
+    // compute-dtype copies of fp32 operands that are read in place
+    const void* xa = x;
+    const void* ga = dy;
+    if (L.cast_x && M * K > 0) {
+        if (timed(LYC_KERNEL_CAST, s, [&] { return lyc::launch_cast((const float*)x, W + L.xc, M * K, P.c_dt, s); }) !=
+            hipSuccess)
+            return LYC_ERR_HIP;
+        xa = W + L.xc;
+    }
+    if (L.cast_g && M * N > 0) {
+        if (timed(LYC_KERNEL_CAST, s, [&] { return lyc::launch_cast((const float*)dy, W + L.gc, M * N, P.c_dt, s); }) !=
+            hipSuccess)
+            return LYC_ERR_HIP;
+        ga = W + L.gc;
+    }
+
+    // h_r, recomputed exactly as the forward computes it (only dUp reads it)
+    if (L.need_h && M > 0) {
+        lyc::PrepParams pp{};
+        pp.down = down;
+        pp.down_dt = P.d_dt;
+        pp.up = up;
+        pp.up_dt = P.u_dt;
+        pp.dc = W + L.dc;
+        pp.dh = W + L.dh;
+        pp.dl = W + L.dl;
+        pp.uc = W + L.uc;
+        pp.dnorm = (double2*)(W + L.dnorm);
+        pp.flagged = (unsigned*)(W + L.flag_h);
+        pp.N = N;
+        pp.K = K;
+        pp.rank = r;
+        pp.r_pad = P.r_pad;
+        pp.c_dt = P.c_dt;
+        pp.vec = aligned(down, 16) ? 1 : 0;
+        if (timed(LYC_KERNEL_PREP, s, [&] { return lyc::launch_prep(pp, s); }) != hipSuccess) return LYC_ERR_HIP;
+        lyc::XrParams hp{};
+        hp.x = xa;
+        hp.b = W + (split ? L.dh : L.dc);
+        hp.b_lo = split ? (const void*)(W + L.dl) : nullptr;
+        hp.b_full = W + L.dc;
+        hp.bnorm = (const double2*)(W + L.dnorm);
+        hp.M = M;
+        hp.Nc = P.r_pad;
+        hp.K = K;
+        hp.guard = split ? 1 : 0;
+        hp.flagged = (unsigned*)(W + L.flag_h);
+        hp.mode = lyc::XR_H;
+        hp.out = W + L.h;
+        hp.ld_out = P.r_pad;
+        hp.scale = 1.0;
+        if (timed(LYC_KERNEL_HPASS, s, [&] { return lyc::launch_xr(P.c_dt, hp, s); }) != hipSuccess) return LYC_ERR_HIP;
+    }
+
+    // gh_r = round_c(scale * dy_c . up_c): the h pass over dy with b = up_c^T
+    if (L.need_gh && M > 0 && N == 0) {
+        // no outputs: gh = 0 (a transpose of an empty source writes only its zero padding)
+        if (!transpose(W, P.c_dt, 0, 0, W + L.gh, P.r_pad, M)) return LYC_ERR_HIP;
+    } else if (L.need_gh && M > 0) {
+        if (!transpose(up, P.u_dt, N, r, W + L.ut, N, P.r_pad)) return LYC_ERR_HIP;
+        if (split && timed(LYC_KERNEL_PREP, s, [&] {
+                return lyc::launch_rownorm(W + L.ut, P.c_dt, P.r_pad, N, W + L.uth, W + L.utl,
+                                           (double2*)(W + L.unorm), (unsigned*)(W + L.flag_g), s);
+            }) != hipSuccess)
+            return LYC_ERR_HIP;
+        lyc::XrParams gp{};
+        gp.x = ga;
+        gp.b = W + (split ? L.uth : L.ut);
+        gp.b_lo = split ? (const void*)(W + L.utl) : nullptr;
+        gp.b_full = W + L.ut;
+        gp.bnorm = (const double2*)(W + L.unorm);
+        gp.M = M;
+        gp.Nc = P.r_pad;
+        gp.K = N;
+        gp.guard = split ? 1 : 0;
+        gp.flagged = (unsigned*)(W + L.flag_g);
+        gp.mode = lyc::XR_H;
+        gp.out = W + L.gh;
+        gp.ld_out = P.r_pad;
+        gp.scale = scale;
+        if (timed(LYC_KERNEL_HPASS, s, [&] { return lyc::launch_xr(P.c_dt, gp, s); }) != hipSuccess) return LYC_ERR_HIP;
+    }
+
+    // dx = round_x(dy_c . W_c + gh_r . down_c): the forward's GEMM with W^T, the fold over down^T
+    if (wdx && M > 0 && K > 0) {
+        if (N > 0 && !transpose(w, P.w_dt, N, K, W + L.wt, N, K)) return LYC_ERR_HIP;
+        if (r > 0 && !transpose(down, P.d_dt, r, K, W + L.dt, P.r_pad, K)) return LYC_ERR_HIP;
+        lyc::GemmParams g{};
+        g.a = W + L.wt;
+        g.b = ga;
+        g.M = M;
+        g.N = K;
+        g.K = N;
+        g.af = r > 0 ? (const void*)(W + L.dt) : nullptr;
+        g.bf = r > 0 ? (const void*)(W + L.gh) : nullptr;
+        g.rf = r > 0 ? P.r_pad : 0;
+        g.scale = 1.0f;
+        g.post = 1.0f;
+        g.y = dx;
+        g.y_dt = P.x_dt;
+        g.ksplit = L.ks_dx;
+        g.partial = L.ks_dx > 1 ? (float*)(W + L.partial) : nullptr;
+        g.vec_store = (K % 4 == 0) && aligned(dx, P.x_dt == LYC_F32 ? 16 : 8);
+        if (!gemm(g)) return LYC_ERR_HIP;
+    }
+
+    // dDown = round_down(gh_r^T . x_c), over the tokens
+    if (wdd && r > 0 && K > 0) {
+        if (M > 0) {
+            if (!transpose(x, P.x_dt, M, K, W + L.xt, B.M8, K)) return LYC_ERR_HIP;
+            if (!transpose(W + L.gh, P.c_dt, M, P.r_pad, W + L.ght, B.M8, P.r_pad)) return LYC_ERR_HIP;
+        }
+        lyc::GemmParams g{};
+        g.a = W + L.xt;
+        g.b = W + L.ght;
+        g.M = r;
+        g.N = K;
+        g.K = B.M8;
+        g.rf = 0;
+        g.scale = 1.0f;
+        g.post = 1.0f;
+        g.y = d_down;
+        g.y_dt = P.d_dt;
+        g.ksplit = L.ks_dd;
+        g.partial = L.ks_dd > 1 ? (float*)(W + L.partial) : nullptr;
+        g.vec_store = (K % 4 == 0) && aligned(d_down, P.d_dt == LYC_F32 ? 16 : 8);
+        if (!gemm(g)) return LYC_ERR_HIP;
+    }
+
+    // dUp = round_up(scale * dy_c^T . h_r), over the tokens
+    if (wdu && r > 0 && N > 0) {
+        if (M > 0) {
+            if (!transpose(dy, B.dy_dt, M, N, W + L.dyt, B.M8, N)) return LYC_ERR_HIP;
+            if (!transpose(W + L.h, P.c_dt, M, P.r_pad, W + L.ht, B.M8, P.r_pad)) return LYC_ERR_HIP;
+        }
+        lyc::GemmParams g{};
+        g.a = W + L.ht;
+        g.b = W + L.dyt;
+        g.M = N;
+        g.N = r;
+        g.K = B.M8;
+        g.rf = 0;
+        g.scale = 1.0f;
+        g.post = (float)scale;
+        g.y = d_up;
+        g.y_dt = P.u_dt;
+        g.ksplit = L.ks_du;
+        g.partial = L.ks_du > 1 ? (float*)(W + L.partial) : nullptr;
+        g.vec_store = (r % 4 == 0) && aligned(d_up, P.u_dt == LYC_F32 ? 16 : 8);
+        if (!gemm(g)) return LYC_ERR_HIP;
+    }
+    return LYC_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int lyc_lora_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt,
+                                       int bias_dt, int down_dt, int up_dt, int dy_dt, int want, size_t* bytes) {
+    Bwd B{Problem{true, M, N, K, rank, x_dt, w_dt, bias_dt, down_dt, up_dt, 0, 0, 0}, dy_dt, want, 0};
+    const int st = check_bwd(B);
+    if (st != LYC_OK) return st;
+    if (bytes) *bytes = bwd_layout(B).total;
+    return LYC_OK;
+}
+
+int lyc_lora_linear_bwd(const void* x, int x_dt, const void* w, int w_dt, int bias_dt, const void* down,
+                        int down_dt, const void* up, int up_dt, int64_t rank, double scale, const void* dy,
+                        int dy_dt, void* dx, void* d_down, void* d_up, int64_t M, int64_t N, int64_t K,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    const int want = (dx ? BWD_DX : 0) | (d_down ? BWD_DDOWN : 0) | (d_up ? BWD_DUP : 0);
+    Bwd B{Problem{true, M, N, K, rank, x_dt, w_dt, bias_dt, down_dt, up_dt, 0, 0, 0}, dy_dt, want, 0};
+    const int st = check_bwd(B);
+    if (st != LYC_OK) return st;
+    return backward(B, x, w, down, up, scale, dy, dx, d_down, d_up, workspace, workspace_bytes, stream);
+}
+
+int lyc_lora_linear_bwd_workspace_layout(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt,
+                                         int bias_dt, int down_dt, int up_dt, int dy_dt, int want,
+                                         size_t* h_offset, size_t* gh_offset, int64_t* ld, size_t* flagged_offset) {
+    Bwd B{Problem{true, M, N, K, rank, x_dt, w_dt, bias_dt, down_dt, up_dt, 0, 0, 0}, dy_dt, want, 0};
+    const int st = check_bwd(B);
+    if (st != LYC_OK) return st;
+    const BwdLayout L = bwd_layout(B);
+    if (h_offset) *h_offset = L.need_h ? L.h : (size_t)-1;
+    if (gh_offset) *gh_offset = L.need_gh ? L.gh : (size_t)-1;
+    if (ld) *ld = B.P.r_pad;
+    if (flagged_offset) *flagged_offset = L.need_gh && B.P.c_dt != LYC_F32 ? L.flag_g : (size_t)-1;
+    return LYC_OK;
+}
 
 int lyc_lora_merge_workspace_size(int64_t N, int64_t K, int64_t rank, int w_dt, int down_dt, int up_dt,
                                   size_t* bytes) {

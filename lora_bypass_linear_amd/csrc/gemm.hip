@@ -331,7 +331,7 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float a = acc[i][j][e];
-                v[e] = a + bias[e];
+                v[e] = a * p.post + bias[e];
             }
             const int64_t base = m * p.N + nb;
             if (p.y_dt == DT_F32) {
@@ -360,13 +360,14 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
     }
 }
 
-// y = round_out(sum of the K splits' partial sums, in split order, + b)
+// y = round_out(post * (sum of the K splits' partial sums, in split order) + b)
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmParams p) {
     const int64_t MN = p.M * p.N;
     const int64_t stride = (int64_t)gridDim.x * 256;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < MN; i += stride) {
         float v = p.partial[i];
         for (int k = 1; k < p.ksplit; ++k) v += p.partial[(int64_t)k * MN + i];
+        v *= p.post;
         const int64_t n = i % p.N;
         if (p.bias != nullptr) v += load_as_f32(p.bias, p.bias_dt, n);
         if (p.y_dt == DT_F32) ((float*)p.y)[i] = v;

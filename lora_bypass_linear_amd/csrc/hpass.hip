@@ -239,8 +239,11 @@ __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB]
         const double slack = 1.0 + 0x1p-20;
         const double xn2 = __builtin_sqrt(xm2) * slack;
         const double xln = __builtin_sqrt(xl2) * slack;
-        const double A = 0x1p-24 * GUARD_CROSS * xn2 * slack, B = 0x1p-24 * GUARD_CROSS * xln * slack;
-        const double C = 0x1p-37 * xn2 * slack;
+        // h = scale * C: the bound scales with |scale| (the fp64 product's own
+        // rounding, 2^-53 relative, lies far inside the 2^-37 slack term)
+        const double as = __builtin_fabs(p.scale);
+        const double A = 0x1p-24 * GUARD_CROSS * xn2 * slack * as, B = 0x1p-24 * GUARD_CROSS * xln * slack * as;
+        const double C = 0x1p-37 * xn2 * slack * as;
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) {
             double2 b2[4];   // {|b|, |b_lo|} of the lane's 4 columns of this block
@@ -252,7 +255,7 @@ __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB]
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int jl = c0 + jb * 16 + 4 * (lane >> 4) + e;
-                const double h = acc[jb][e];
+                const double h = acc[jb][e] * p.scale;
                 const double E = A * b2[e].y + B * (b2[e].x + b2[e].y) + C * b2[e].x;
                 const uint16_t lo = round16<CT>(h - E);
                 r16[jb][e] = lo;
@@ -280,7 +283,8 @@ __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB]
                 const int64_t jg = j0 + c0 + jb * 16 + 4 * (lane >> 4);
                 if (CT::dt == DT_F32) {
                     float* hp = (float*)p.out + m * p.ld_out + jg;
-                    *(f32x4*)hp = f32x4{(float)acc[jb][0], (float)acc[jb][1], (float)acc[jb][2], (float)acc[jb][3]};
+                    *(f32x4*)hp = f32x4{(float)(acc[jb][0] * p.scale), (float)(acc[jb][1] * p.scale),
+                                        (float)(acc[jb][2] * p.scale), (float)(acc[jb][3] * p.scale)};
                 } else {
                     uint16_t* hp = (uint16_t*)p.out + m * p.ld_out + jg;
                     *(i32x2*)hp = i32x2{(int)(r16[jb][0] | ((uint32_t)r16[jb][1] << 16)),
@@ -589,7 +593,7 @@ void xr_kernel(XrParams p) {
             if (mine && j == 0) {
                 const int64_t m = wg_m0 + row, j = j0 + col;
                 if (p.mode == XR_H) {
-                    ((uint16_t*)p.out)[m * p.ld_out + j] = round16<CT>(d);
+                    ((uint16_t*)p.out)[m * p.ld_out + j] = round16<CT>(d * p.scale);
                 } else {
                     const float bias = p.bias != nullptr ? load_as_f32(p.bias, p.bias_dt, j) : 0.f;
                     const float v = affine_value<CT>(d, p.out_dt) + bias;

@@ -28,6 +28,9 @@ struct GemmParams {
     // adds the bias and rounds once
     int ksplit;
     float* partial;
+    // y = round_out(post * acc + b): 1 in the forward; the scale of a weight
+    // gradient whose product has no fold
+    float post;
 };
 
 // Exact-rounding contraction (h pass and plain affine projection):
@@ -51,6 +54,7 @@ struct XrParams {
     const void* bias;       // XR_AFFINE, nullptr: none
     int bias_dt;
     int vec_store;          // XR_AFFINE: rows allow 4-element vector stores
+    double scale;           // XR_H: the value rounded is scale * C (1 in the forward)
 };
 
 // Compute-dtype copies of down [rank,K] -> [r_pad,K] (+ its hi/lo split per

@@ -78,7 +78,7 @@ def lib():
         L.oracle_backward.restype = ctypes.c_int
         L.oracle_backward.argtypes = [vp, ci, vp, ci, ci, vp, ci, vp, ci, i64, ctypes.c_double, vp, ci,
                                       i64, i64, i64, vp, i64, vp, vp, vp, vp, i64, vp, i64, vp, vp, vp, i64,
-                                      vp, vp, ci, ctypes.POINTER(ctypes.c_int)]
+                                      vp, vp, vp, vp, vp, ci, ctypes.POINTER(ctypes.c_int)]
         _lib = L
     return _lib
 
@@ -239,7 +239,9 @@ def backward(x, x_dt, w, w_dt, down, down_dt, up, up_dt, dy, dy_dt, scale: float
     dict with ``compute``, ``dx`` / ``dx_ref`` [len(dx_rows), K], ``gh``
     [len(dx_rows), r] (the rounded gh of those rows, float64), ``d_down`` /
     ``dd_ref`` [len(js), len(dd_cols)] and ``d_up`` / ``du_ref``
-    [len(du_rows), len(js)]; gradients in storage of their leaf's dtype."""
+    [len(du_rows), len(js)]; gradients in storage of their leaf's dtype;
+    ``dx_rss`` / ``dd_rss`` / ``du_rss``: the root-sum-square of the terms of
+    each output's final sum (for ``tolerance_sum``)."""
     x = np.ascontiguousarray(x, dtype=storage_np(x_dt))
     w = np.ascontiguousarray(w, dtype=storage_np(w_dt))
     down = np.ascontiguousarray(down, dtype=storage_np(down_dt))
@@ -261,16 +263,18 @@ def backward(x, x_dt, w, w_dt, down, down_dt, up, up_dt, dy, dy_dt, scale: float
     dd_ref = np.zeros((js.size, dd_cols.size))
     d_up = np.zeros((du_rows.size, js.size), dtype=storage_np(up_dt))
     du_ref = np.zeros((du_rows.size, js.size))
+    dx_rss, dd_rss, du_rss = np.zeros_like(dx_ref), np.zeros_like(dd_ref), np.zeros_like(du_ref)
     c_out = ctypes.c_int(0)
     st = lib().oracle_backward(_ptr(x), x_dt, _ptr(w), w_dt, int(b_dt or 0), _ptr(down), down_dt, _ptr(up), up_dt,
                                r, float(scale), _ptr(dy), dy_dt, M, N, K, _ptr(dx_rows), dx_rows.size, _ptr(dx),
                                _ptr(dx_ref), _ptr(gh), _ptr(js), js.size, _ptr(dd_cols), dd_cols.size, _ptr(d_down),
-                               _ptr(dd_ref), _ptr(du_rows), du_rows.size, _ptr(d_up), _ptr(du_ref),
-                               int(default_threads() if nthreads is None else nthreads), ctypes.byref(c_out))
+                               _ptr(dd_ref), _ptr(du_rows), du_rows.size, _ptr(d_up), _ptr(du_ref), _ptr(dx_rss),
+                               _ptr(dd_rss), _ptr(du_rss), int(default_threads() if nthreads is None else nthreads),
+                               ctypes.byref(c_out))
     if st != OK:
         raise OracleError(st)
     return {"compute": c_out.value, "dx": dx, "dx_ref": dx_ref, "gh": gh, "d_down": d_down, "dd_ref": dd_ref,
-            "d_up": d_up, "du_ref": du_ref}
+            "d_up": d_up, "du_ref": du_ref, "dx_rss": dx_rss, "dd_rss": dd_rss, "du_rss": du_rss}
 
 
 # ---- scoring ----------------------------------------------------------------
@@ -294,6 +298,22 @@ def tolerance(ref: np.ndarray, compute: int, K: int, r: int) -> np.ndarray:
         atol, rtol = TOL[compute]
         return atol + rtol * a
     return 8.0 * 2.0 ** -24 * np.sqrt(max(K + r, 1)) * (1.0 + a)
+
+
+def tolerance_sum(ref: np.ndarray, rss: np.ndarray, compute: int, L: int) -> np.ndarray:
+    """Per-element bound for |gpu - ref| of a result summed over L terms whose
+    root-sum-square is rss (the gradients).  The fp32 accumulation a GPU does
+    errs by about 2^-24 * sqrt(L) times the size of its partial sums, which
+    for terms of random sign is rss, not |ref|: 8 * 2^-24 * sqrt(L) * rss.
+    16-bit compute: the forward's bound plus that term; fp32 compute:
+    8 * 2^-24 * sqrt(L) * (|ref| + rss) (the forward's (1 + |ref|) with the
+    terms' own scale in place of the 1)."""
+    a = np.abs(ref)
+    acc = 8.0 * 2.0 ** -24 * np.sqrt(max(L, 1)) * rss
+    if compute in TOL:
+        atol, rtol = TOL[compute]
+        return atol + rtol * a + acc
+    return 8.0 * 2.0 ** -24 * np.sqrt(max(L, 1)) * a + acc
 
 
 def ulp_of(v: float, dt: int) -> float:

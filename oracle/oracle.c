@@ -437,12 +437,12 @@ typedef struct {
     const int64_t* dx_rows;
     double* ghrow;                           /* [n_dx][r] gh_r of the dx rows */
     void* dx;
-    double* dx_ref;
+    double *dx_ref, *dx_rss;
     /* d_down[js][dd_cols], d_up[du_rows][js] */
     const int64_t *dd_cols, *du_rows;
     int64_t n_dd, n_du;
     void *d_down, *d_up;
-    double *dd_ref, *du_ref;
+    double *dd_ref, *du_ref, *dd_rss, *du_rss;
 } bwd_t;
 
 /* h_r[m][j] = round_c(sum_k x_c[m,k] down_c[j,k]) -- the forward's h, recomputed */
@@ -478,12 +478,21 @@ static void bwd_dx(void* ctx, int64_t lo, int64_t hi) {
         double* gh = B->ghrow + i * r;
         for (int64_t j = 0; j < r; ++j) gh[j] = bwd_gh(B, m, j);
         for (int64_t k = 0; k < K; ++k) {
-            double s = 0.0;
-            for (int64_t n = 0; n < N; ++n) s += B->gc[m * N + n] * B->wc[n * K + k];
+            double s = 0.0, q = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                const double t = B->gc[m * N + n] * B->wc[n * K + k];
+                s += t;
+                q += t * t;
+            }
             double f = 0.0;
-            for (int64_t j = 0; j < r; ++j) f += gh[j] * B->dc[j * K + k];
+            for (int64_t j = 0; j < r; ++j) {
+                const double t = gh[j] * B->dc[j * K + k];
+                f += t;
+                q += t * t;
+            }
             const double v = s + f;
             if (B->dx_ref) B->dx_ref[i * K + k] = v;
+            if (B->dx_rss) B->dx_rss[i * K + k] = sqrt(q);
             if (B->dx) store(B->dx, B->x_dt, i * K + k, oracle_round(v, B->x_dt));
         }
     }
@@ -495,9 +504,14 @@ static void bwd_ddown(void* ctx, int64_t lo, int64_t hi) {
     for (int64_t c = lo; c < hi; ++c) {
         const int64_t k = B->dd_cols[c];
         for (int64_t t = 0; t < B->nj; ++t) {
-            double s = 0.0;
-            for (int64_t m = 0; m < B->M; ++m) s += B->ghj[m * B->nj + t] * B->xc[m * B->K + k];
+            double s = 0.0, q = 0.0;
+            for (int64_t m = 0; m < B->M; ++m) {
+                const double u = B->ghj[m * B->nj + t] * B->xc[m * B->K + k];
+                s += u;
+                q += u * u;
+            }
             if (B->dd_ref) B->dd_ref[t * B->n_dd + c] = s;
+            if (B->dd_rss) B->dd_rss[t * B->n_dd + c] = sqrt(q);
             if (B->d_down) store(B->d_down, B->down_dt, t * B->n_dd + c, oracle_round(s, B->down_dt));
         }
     }
@@ -509,10 +523,15 @@ static void bwd_dup(void* ctx, int64_t lo, int64_t hi) {
     for (int64_t i = lo; i < hi; ++i) {
         const int64_t n = B->du_rows[i];
         for (int64_t t = 0; t < B->nj; ++t) {
-            double s = 0.0;
-            for (int64_t m = 0; m < B->M; ++m) s += B->gc[m * B->N + n] * B->hj[m * B->nj + t];
+            double s = 0.0, q = 0.0;
+            for (int64_t m = 0; m < B->M; ++m) {
+                const double u = B->gc[m * B->N + n] * B->hj[m * B->nj + t];
+                s += u;
+                q += u * u;
+            }
             const double v = B->scale * s;
             if (B->du_ref) B->du_ref[i * B->nj + t] = v;
+            if (B->du_rss) B->du_rss[i * B->nj + t] = fabs(B->scale) * sqrt(q);
             if (B->d_up) store(B->d_up, B->up_dt, i * B->nj + t, oracle_round(v, B->up_dt));
         }
     }
@@ -539,6 +558,8 @@ static void bwd_dup(void* ctx, int64_t lo, int64_t hi) {
  *   gh_rows          [n_dx][r]  gh_r of those rows
  *   d_down / dd_ref  [nj][n_dd] for the rank rows js and the columns dd_cols
  *   d_up / du_ref    [n_du][nj] for the rows du_rows and the rank columns js
+ * With each *_ref goes *_rss, the root-sum-square of the terms of that
+ * output's final sum (for error bounds of an fp32 evaluation; NULL: skipped).
  * Returns OR_OK, OR_MIXED_HALF or OR_INVALID, and the compute dtype.
  */
 int oracle_backward(const void* x, int x_dt, const void* w, int w_dt, int b_dt, const void* down, int down_dt,
@@ -546,7 +567,7 @@ int oracle_backward(const void* x, int x_dt, const void* w, int w_dt, int b_dt, 
                     int64_t N, int64_t K, const int64_t* dx_rows, int64_t n_dx, void* dx, double* dx_ref,
                     double* gh_rows, const int64_t* js, int64_t nj, const int64_t* dd_cols, int64_t n_dd,
                     void* d_down, double* dd_ref, const int64_t* du_rows, int64_t n_du, void* d_up,
-                    double* du_ref, int nthreads, int* c_out) {
+                    double* du_ref, double* dx_rss, double* dd_rss, double* du_rss, int nthreads, int* c_out) {
     int dts[6], nd = 0;
     dts[nd++] = x_dt;
     dts[nd++] = w_dt;
@@ -582,13 +603,13 @@ int oracle_backward(const void* x, int x_dt, const void* w, int w_dt, int b_dt, 
     if (need_tokens) par_for(M, nthreads, bwd_tokens, &B);
 
     double* ghr = (double*)malloc(sizeof(double) * (size_t)(n_dx * r > 0 ? n_dx * r : 1));
-    B.dx_rows = dx_rows; B.ghrow = ghr; B.dx = dx; B.dx_ref = dx_ref;
+    B.dx_rows = dx_rows; B.ghrow = ghr; B.dx = dx; B.dx_ref = dx_ref; B.dx_rss = dx_rss;
     par_for(n_dx, nthreads, bwd_dx, &B);
     if (gh_rows) memcpy(gh_rows, ghr, sizeof(double) * (size_t)(n_dx * r));
 
-    B.dd_cols = dd_cols; B.n_dd = n_dd; B.d_down = d_down; B.dd_ref = dd_ref;
+    B.dd_cols = dd_cols; B.n_dd = n_dd; B.d_down = d_down; B.dd_ref = dd_ref; B.dd_rss = dd_rss;
     if (ghj) par_for(n_dd, nthreads, bwd_ddown, &B);
-    B.du_rows = du_rows; B.n_du = n_du; B.d_up = d_up; B.du_ref = du_ref;
+    B.du_rows = du_rows; B.n_du = n_du; B.d_up = d_up; B.du_ref = du_ref; B.du_rss = du_rss;
     if (hj) par_for(n_du, nthreads, bwd_dup, &B);
 
     free(xc); free(wc); free(dc); free(uc); free(gc);

@@ -190,3 +190,50 @@ def test_merge_workspace_sizes():
     assert L.lora_merge_workspace_size(64, 64, 0, 1, 1, 1) == 0
     with pytest.raises(L.MixedHalfError):
         L.lora_merge_workspace_size(64, 64, 4, 1, 2, 1)
+
+
+def _bwd(allow_ok=False, **kw):
+    a = dict(x=P, x_dt=1, w=P, w_dt=1, b_dt=0, d=P, d_dt=1, u=P, u_dt=1, r=4, scale=1.0, g=P, g_dt=1,
+             dx=V(1 << 30), dd=V(1 << 31), du=V(1 << 32), M=16, N=16, K=16, ws=None, nws=0, s=None)
+    a.update(kw)
+    return _refused(L.lib().lyc_lora_linear_bwd(a["x"], a["x_dt"], a["w"], a["w_dt"], a["b_dt"], a["d"], a["d_dt"],
+                                                a["u"], a["u_dt"], a["r"], ctypes.c_double(a["scale"]), a["g"],
+                                                a["g_dt"], a["dx"], a["dd"], a["du"], a["M"], a["N"], a["K"],
+                                                a["ws"], a["nws"], a["s"]), allow_ok)
+
+
+def test_backward_argument_errors():
+    assert _bwd(g_dt=2) == L.ERR_MIXED_HALF                  # dy is a policy operand
+    assert _bwd(b_dt=2) == L.ERR_MIXED_HALF                  # so is the forward's bias dtype
+    assert _bwd(K=12) == L.ERR_UNSUPPORTED
+    assert _bwd(N=12) == L.ERR_UNSUPPORTED                   # N is a contraction length here
+    assert _bwd(M=(1 << 20) + 8) == L.ERR_UNSUPPORTED
+    assert _bwd(r=257) == L.ERR_UNSUPPORTED
+    assert _bwd(r=-1) == L.ERR_INVALID_ARG
+    assert _bwd(x_dt=5) == L.ERR_INVALID_ARG
+    assert _bwd(scale=float("nan")) == L.ERR_INVALID_ARG
+    assert _bwd(g=None) == L.ERR_INVALID_ARG
+    assert _bwd(x=None) == L.ERR_INVALID_ARG
+    assert _bwd(u=None) == L.ERR_INVALID_ARG
+    assert _bwd(x=V(4096 + 2)) == L.ERR_UNSUPPORTED           # x read in place: 16-byte rows
+    assert _bwd(g=V(4096 + 2)) == L.ERR_UNSUPPORTED
+    assert _bwd(dx=V(4096 + 256)) == L.ERR_INVALID_ARG        # dx overlaps the inputs
+    assert _bwd(dd=V(1 << 30)) == L.ERR_INVALID_ARG           # two gradients overlap
+    assert _bwd(dx=V((1 << 30) + 1)) == L.ERR_UNSUPPORTED      # element alignment
+    assert _bwd() == L.ERR_WORKSPACE
+    assert _bwd(ws=V(4100), nws=1 << 30) == L.ERR_WORKSPACE
+
+
+def test_backward_workspace_sizes():
+    n_all = L.lora_bwd_workspace_size(300, 64, 128, 17, 1, 1, 0, 1, 1, 1, 7)
+    n_dx = L.lora_bwd_workspace_size(300, 64, 128, 17, 1, 1, 0, 1, 1, 1, 1)
+    n_du = L.lora_bwd_workspace_size(300, 64, 128, 17, 1, 1, 0, 1, 1, 1, 4)
+    # dx needs W^T [K][N] and gh; dUp needs dy^T [N][M8] and h^T; all of it for the three
+    assert n_dx >= 128 * 64 * 2 + 300 * 32 * 2 and n_du >= 64 * 304 * 2 + 32 * 304 * 2
+    assert n_all >= max(n_dx, n_du)
+    ho, go, ld, fo = L.lora_bwd_workspace_layout(300, 64, 128, 17, 1, 1, 0, 1, 1, 1, 1)
+    assert ho == 2 ** 64 - 1 and go % 256 == 0 and ld == 32      # dx alone recomputes no h
+    ho, go, ld, fo = L.lora_bwd_workspace_layout(300, 64, 128, 17, 3, 3, 0, 3, 3, 3, 7)
+    assert ho % 256 == 0 and fo == 2 ** 64 - 1                    # fp32 compute: no guard
+    with pytest.raises(L.MixedHalfError):
+        L.lora_bwd_workspace_size(8, 8, 8, 2, 1, 1, 0, 1, 1, 2, 7)

@@ -611,3 +611,13 @@ def test_backward_mixed_dtype_fixture():
     assert float(res["dx"][0, 0]) == 2.0 + 2.0 ** -12
     assert float(res["d_down"][0, 0]) == 1.0
     assert oracle.as_float64(res["d_up"], F16)[:, 0].tolist() == [1.0, 2.0 ** -12]
+
+
+def test_tolerance_sum_forms():
+    # 16-bit: the forward's bound plus the fp32 accumulation term; fp32: terms' scale in place of 1
+    ref, rss = np.array([0.0, 2.0]), np.array([0.0, 8.0])
+    acc = 8.0 * 2.0 ** -24 * 10.0 * rss                         # sqrt(L) = 10
+    np.testing.assert_allclose(oracle.tolerance_sum(ref, rss, F16, 100), 2e-4 + 2e-3 * ref + acc)
+    np.testing.assert_allclose(oracle.tolerance_sum(ref, rss, F32, 100), 8.0 * 2.0 ** -24 * 10.0 * ref + acc)
+    # the forward's fp32 bound is the special case rss = 1
+    np.testing.assert_allclose(oracle.tolerance_sum(ref, np.ones(2), F32, 100), oracle.tolerance(ref, F32, 100, 0))

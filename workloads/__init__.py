@@ -31,7 +31,7 @@ NAME = {F16: "f16", BF16: "bf16", F32: "f32"}
 BYTES = {F16: 2, BF16: 2, F32: 4}
 
 # tensor ids used to key the per-tensor Philox streams
-_TID = {"x": 1, "w": 2, "b": 3, "down": 4, "up": 5, "rowscale": 6}
+_TID = {"x": 1, "w": 2, "b": 3, "down": 4, "up": 5, "rowscale": 6, "dy": 7}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -157,6 +157,12 @@ def generate(w: Workload) -> Dict[str, torch.Tensor]:
         out["down"] = _draw(w.seed, "down", (w.r, w.K), w.down_std, w.w_dt)
         out["up"] = _draw(w.seed, "up", (w.N, w.r), w.up_std, w.w_dt)
     return out
+
+
+def generate_dy(w: Workload, dt: int, std: float = 1.0) -> torch.Tensor:
+    """The upstream gradient dy [M,N] for the backward: N(0, std^2) in dtype dt
+    (the forward's output dtype), from its own Philox stream."""
+    return _draw(w.seed, "dy", (w.M, w.N), std, dt)
 
 
 def raw_bits(t: torch.Tensor) -> np.ndarray:
