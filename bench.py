@@ -47,6 +47,10 @@ def main():
     ap.add_argument("--merge-only", action="store_true",
                     help="time only the LoRA merge of the workload's weights (profiling runs)")
     ap.add_argument("--merge-steps", type=int, default=100)
+    ap.add_argument("--no-backward", action="store_true", help="skip the LoRA-bypass backward timing")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the backward of the workload (profiling runs)")
+    ap.add_argument("--backward-steps", type=int, default=50)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (HBM counter calibration)")
     args = ap.parse_args()
@@ -82,6 +86,14 @@ def main():
             _copy_calibration(dev, args.copy_calibration_mib)
         print(json.dumps({"workload": wl.name, "merge": _merge(dev, wl, inputs, args.merge_steps, args.merge_steps,
                                                                  not args.no_cpu_baseline)}))
+        return
+
+    if args.backward_only:
+        if args.copy_calibration_mib > 0:
+            _copy_calibration(dev, args.copy_calibration_mib)
+        print(json.dumps({"workload": wl.name, "backward": _backward(dev, wl, inputs, args.backward_steps,
+                                                                       args.backward_steps, not args.no_cpu_baseline,
+                                                                       not args.no_eager)}))
         return
 
     def step():
@@ -163,6 +175,9 @@ def main():
         out["small_m"] = _small_m(dev)
     if lora and wl.r > 0 and not args.no_merge:
         out["merge"] = _merge(dev, wl, inputs, args.merge_steps, 20, not args.no_cpu_baseline)
+    if lora and wl.r > 0 and not args.no_backward:
+        out["backward"] = _backward(dev, wl, inputs, args.backward_steps, 20, not args.no_cpu_baseline,
+                                    not args.no_eager)
 
     # accuracy on sampled rows against the fp64 oracle (this is also the CPU-baseline leg)
     if not args.no_cpu_baseline:
@@ -290,6 +305,125 @@ def _merge(dev, wl, inputs, reps, warm, accuracy):
                   "eager": {"max_ulp": round(se["ulp_max"], 4), "rms_ulp": round(se["ulp_rms"], 4),
                             "tol_fail": se["fail"]}})
     return r
+
+
+def _backward(dev, wl, inputs, reps, warm, accuracy, eager):
+    """The LoRA-bypass backward for a seeded dy (N(0,1) in the forward's output
+    dtype): wall time per call with all three gradients, the device time of
+    each kernel kind, algorithmic TFLOP/s, and the dx GEMM's roofline from a
+    dx-only call (its GEMM launch alone); on sampled rows / columns / rank
+    indices, ULP against the fp64 oracle next to the eager torch autograd
+    chain."""
+    import numpy as np
+    import torch
+
+    import lora_bypass_linear_amd as L
+    import workloads as WL
+
+    M, N, K, r = wl.M, wl.N, wl.K, wl.r
+    d = {k: v.to(dev) for k, v in inputs.items()}
+    codes = [WL.dtype_code(inputs[k]) for k in ("x", "w", "down", "up")] + \
+            ([WL.dtype_code(inputs["b"])] if "b" in inputs else [])
+    c_dt, o_dt = L.resolve_dtypes(codes)
+    dy_cpu = WL.generate_dy(wl, o_dt)
+    dy = dy_cpu.to(dev)
+    b_dtype = inputs["b"].dtype if "b" in inputs else None
+    ws = torch.empty(max(L.lora_bwd_workspace_size(M, N, K, r, codes[0], codes[1], WL.dtype_code(inputs["b"])
+                                                   if "b" in inputs else 0, codes[2], codes[3],
+                                                   WL.dtype_code(dy_cpu), 7), 1), dtype=torch.uint8, device=dev)
+    call = lambda **kw: L.lora_linear_backward(d["x"], d["w"], d["down"], d["up"], wl.scale, dy, bias_dtype=b_dtype,
+                                               workspace=ws, **kw)
+    print(f"[bench] backward {wl.name}: {warm} + {reps} calls", file=sys.stderr, flush=True)
+    for _ in range(warm):
+        grads = call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        grads = call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / reps
+    L.profile_begin(32 * reps)
+    for _ in range(reps):
+        call()
+    torch.cuda.synchronize()
+    prof = L.profile_end()
+    # dx alone: its one GEMM launch is the dominant kernel of the backward
+    for _ in range(5):
+        call(want_ddown=False, want_dup=False)
+    L.profile_begin(16 * reps)
+    for _ in range(reps):
+        call(want_ddown=False, want_dup=False)
+    torch.cuda.synchronize()
+    pdx = L.profile_end()
+    n_g, t_g = pdx["gemm"]
+    g_us = t_g * 1e3 / max(n_g, 1)
+    dx_flops = 2.0 * M * N * K + 2.0 * M * r * K
+    flops = 2.0 * M * K * r + 2.0 * M * N * r + dx_flops + 2.0 * M * r * K + 2.0 * M * N * r
+    peak = PEAK_TFLOPS[c_dt]
+    names = {"cast": "transposes + casts", "prep": "prep + row norms", "hpass": "h and gh passes",
+             "gemm": "dx, dDown, dUp GEMMs"}
+    out = {"shape": f"M {M}, N {N}, K {K}, rank {r}, dy {WL.NAME[WL.dtype_code(dy_cpu)]}",
+           "ms_per_call": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+           "flops_per_call": flops,
+           "kernels": {names[k]: {"launches": n // reps, "us_per_call": round(t * 1e3 / reps, 2)}
+                       for k, (n, t) in prof.items() if n},
+           "roofline": {"bound": "mfma", "kernel": "gemm_kernel (dx = dy_c.W_c + gh_r.down_c)",
+                        "achieved": round(dx_flops / (g_us * 1e-6) / 1e12, 2), "peak": peak, "unit": "TFLOP/s",
+                        "frac": round(dx_flops / (g_us * 1e-6) / 1e12 / peak, 4), "traffic": None,
+                        "flops_per_launch": dx_flops, "avg_us": round(g_us, 3)}}
+    if accuracy:
+        import oracle
+        from tests.gpu_cases import sample_rows
+        rng = np.random.default_rng(wl.seed)
+        rows = sample_rows(M, 16, seed=wl.seed)
+        js = np.sort(rng.choice(r, min(r, 4), replace=False))
+        kk = sample_rows(K, 24, seed=wl.seed + 1)
+        nn = sample_rows(N, 24, seed=wl.seed + 2)
+        bits = {k: WL.raw_bits(v) for k, v in inputs.items()}
+        res = oracle.backward(bits["x"], codes[0], bits["w"], codes[1], bits["down"], codes[2], bits["up"], codes[3],
+                              WL.raw_bits(dy_cpu), WL.dtype_code(dy_cpu), scale=wl.scale,
+                              b_dt=WL.dtype_code(inputs["b"]) if "b" in inputs else 0, dx_rows=rows, js=js,
+                              dd_cols=kk, du_rows=nn)
+
+        def score(gx, gd, gu):
+            o = {}
+            for name, g, want, ref, rss, dt, length in (
+                    ("dx", WL.raw_bits(gx.cpu())[rows], res["dx"], res["dx_ref"], res["dx_rss"], codes[0], N + r),
+                    ("d_down", WL.raw_bits(gd.cpu())[np.ix_(js, kk)], res["d_down"], res["dd_ref"], res["dd_rss"],
+                     codes[2], M),
+                    ("d_up", WL.raw_bits(gu.cpu())[np.ix_(nn, js)], res["d_up"], res["du_ref"], res["du_rss"],
+                     codes[3], M)):
+                gv, wv = oracle.as_float64(g, dt), oracle.as_float64(want, dt)
+                tol = oracle.tolerance_sum(wv, rss, c_dt, length)
+                umax, urms = oracle.ulp_report(gv, ref, c_dt)
+                o[name] = {"max_ulp": round(umax, 3), "rms_ulp": round(urms, 3),
+                           "tol_fail": int((~((gv == wv) | (np.abs(gv - wv) <= tol))).sum()), "n": int(gv.size)}
+            return o
+
+        out["accuracy"] = score(*grads)
+        if eager:
+            ct = L.torch_dtype(c_dt)
+            xe = d["x"].detach().clone().requires_grad_(True)
+            de = d["down"].detach().clone().requires_grad_(True)
+            ue = d["up"].detach().clone().requires_grad_(True)
+            import torch.nn.functional as F
+
+            def run():
+                h = F.linear(xe.to(ct), de.to(ct))
+                y = F.linear(xe.to(ct), d["w"].to(ct)) + wl.scale * F.linear(h, ue.to(ct))
+                return torch.autograd.grad(y, (xe, de, ue), dy.to(ct))
+
+            run()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            n = max(5, reps // 2)
+            for _ in range(n):
+                ge = run()
+            torch.cuda.synchronize()
+            ems = (time.perf_counter() - t0) * 1e3 / n
+            out["eager"] = {"ms_per_call": round(ems, 4), "tflops": round(flops / (ems * 1e-3) / 1e12, 2),
+                            "accuracy": score(*ge)}
+    return out
 
 
 def _small_m(dev, reps=50):
