@@ -60,7 +60,8 @@ enum {
     LYC_ERR_DTYPE_MISMATCH = 3, /* y_dt is not the resolved output dtype */
     LYC_ERR_UNSUPPORTED = 4,    /* K not a multiple of 8, misaligned x/W, rank > 256, sizes too large */
     LYC_ERR_HIP = 5,            /* the HIP runtime refused a launch */
-    LYC_ERR_WORKSPACE = 6       /* workspace missing, too small or not 256-byte aligned */
+    LYC_ERR_WORKSPACE = 6,      /* workspace missing, too small or not 256-byte aligned */
+    LYC_ERR_IO = 7              /* tuning table file could not be read, parsed or written */
 };
 
 /*
@@ -227,6 +228,65 @@ int lyc_lora_linear_bwd(const void* x, int x_dt, const void* w, int w_dt, int bi
 int lyc_lora_linear_bwd_workspace_layout(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt,
                                          int bias_dt, int down_dt, int up_dt, int dy_dt, int want,
                                          size_t* h_offset, size_t* gh_offset, int64_t* ld, size_t* flagged_offset);
+
+/*
+ * Tile planner and measured pick for the LoRA forward's main contraction
+ * (LyCORIS "Backend Selection" page, "Tile selection": an analytic model
+ * shortlists candidates, the shortlist is timed once, best of three, and the
+ * winner is kept in memory and in a table file keyed by device, op, bucketed
+ * shape and dtype).
+ *
+ * lyc_gemm_plan: the shortlist for an M x N x K product with a fold of rf
+ *   (padded rank) steps in compute dtype compute_dt, best first -- first the
+ *   pick the forward makes on its own, then the other (tile, K split) pairs
+ *   in the order of the model's time, which counts rounds of workgroups over
+ *   256 CUs at the MFMA peak, a per-tile re-read penalty, and the partial
+ *   sums' HBM round trip of a K split.  Writes up to max_out (at most 7)
+ *   entries into the host arrays tile_n, tile_m (output tile: rows of W x rows
+ *   of x), ksplit, cost_us (any may be NULL) and their number into *count.
+ *   Host only.
+ * lyc_lora_linear_tune: the same arguments as lyc_lora_linear_fwd (whose
+ *   output y it overwrites), plus the winner's tile, split and time (any
+ *   may be NULL) and, in cand_ms (NULL or 7 doubles), the best time of
+ *   each shortlisted candidate in lyc_gemm_plan's order.  Runs the whole
+ *   forward once and then three times timed
+ *   with each shortlisted configuration on `stream`, and stores the fastest
+ *   under the key of this device and shape; later lyc_lora_linear_fwd calls
+ *   with that key use it.  BLOCKS the host until the timed runs end (the one
+ *   call of the library that synchronises).  With the environment variable
+ *   LYC_KERNEL_TUNE=off (or 0) it times nothing and stores the planner's
+ *   first candidate.  The workspace is the forward's (its size covers every
+ *   shortlisted K split).
+ * lyc_tuning_key: the key of a forward call on the current device into buf
+ *   (e.g. "gfx950-256cu|lora_fwd|M4096|N3072|K3072|r16|c1|o1": device, op, M
+ *   rounded up to a power of two (at least 16), N, K, padded rank, compute
+ *   and output dtypes).  LYC_ERR_HIP without a current device,
+ *   LYC_ERR_INVALID_ARG if buf is NULL or shorter than the key + 1.
+ * lyc_tuning_lookup: *found = 1 and the stored pick if the table holds one
+ *   for that call on the current device, else *found = 0.
+ * lyc_tuning_save / lyc_tuning_load: the table as JSON, one entry per line
+ *   ({"key": ..., "tile_n": ..., "tile_m": ..., "ksplit": ..., "ms": ...}).
+ *   Loading merges into the table (*entries = the number read) and takes
+ *   nothing from a file with a malformed entry (LYC_ERR_IO).  A stored pick
+ *   the forward cannot run (a tile without an instance for the compute dtype,
+ *   a split beyond its workspace) is ignored by the forward.
+ * lyc_tuning_clear / lyc_tuning_count: empty the table / its size.
+ * The table is process-wide and guarded by a mutex.
+ */
+int lyc_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t rf, int compute_dt, int max_out, int* count, int* tile_n,
+                  int* tile_m, int* ksplit, double* cost_us);
+int lyc_lora_linear_tune(const void* x, int x_dt, const void* w, int w_dt, const void* bias, int bias_dt,
+                         const void* down, int down_dt, const void* up, int up_dt, int64_t rank, double scale,
+                         void* y, int y_dt, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                         void* stream, int* tile_n, int* tile_m, int* ksplit, double* best_ms, double* cand_ms);
+int lyc_tuning_key(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt, int bias_dt, int down_dt,
+                   int up_dt, char* buf, size_t len);
+int lyc_tuning_lookup(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt, int bias_dt, int down_dt,
+                      int up_dt, int* found, int* tile_n, int* tile_m, int* ksplit);
+int lyc_tuning_save(const char* path);
+int lyc_tuning_load(const char* path, int* entries);
+int lyc_tuning_clear(void);
+int lyc_tuning_count(void);
 
 /*
  * Output tile (rows of W x rows of x) that the forward calls use for an

@@ -16,11 +16,12 @@ import torch
 __all__ = ["F16", "BF16", "F32", "LycError", "MixedHalfError", "lib", "resolve_dtypes", "linear", "lora_linear",
            "lora_merge", "lora_linear_backward", "linear_workspace_size", "lora_workspace_size", "lora_workspace_layout",
            "linear_workspace_layout", "lora_merge_workspace_size", "lora_bwd_workspace_size",
-           "lora_bwd_workspace_layout", "gemm_tile", "profile_begin", "profile_end",
+           "lora_bwd_workspace_layout", "gemm_tile", "gemm_plan", "lora_linear_tune", "tuning_save",
+           "tuning_load", "tuning_clear", "tuning_count", "tuning_key", "tuning_lookup", "tuning_cache_path", "profile_begin", "profile_end",
            "dtype_code", "torch_dtype"]
 
 F16, BF16, F32 = 1, 2, 3
-OK, ERR_MIXED_HALF, ERR_INVALID_ARG, ERR_DTYPE_MISMATCH, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = range(7)
+OK, ERR_MIXED_HALF, ERR_INVALID_ARG, ERR_DTYPE_MISMATCH, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE, ERR_IO = range(8)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblyc.so")
@@ -71,6 +72,18 @@ def lib():
                                                            c_int, c_int, c_int, ctypes.POINTER(c_sz),
                                                            ctypes.POINTER(c_sz), ctypes.POINTER(c_i64),
                                                            ctypes.POINTER(c_sz)]
+        pi, pd = ctypes.POINTER(c_int), ctypes.POINTER(ctypes.c_double)
+        L.lyc_gemm_plan.argtypes = [c_i64, c_i64, c_i64, c_i64, c_int, c_int, pi, pi, pi, pi, pd]
+        L.lyc_lora_linear_tune.argtypes = [c_vp, c_int, c_vp, c_int, c_vp, c_int, c_vp, c_int, c_vp, c_int, c_i64,
+                                           ctypes.c_double, c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_sz, c_vp,
+                                           pi, pi, pi, pd, pd]
+        L.lyc_tuning_key.argtypes = [c_i64, c_i64, c_i64, c_i64, c_int, c_int, c_int, c_int, c_int, ctypes.c_char_p,
+                                     c_sz]
+        L.lyc_tuning_lookup.argtypes = [c_i64, c_i64, c_i64, c_i64, c_int, c_int, c_int, c_int, c_int, pi, pi, pi, pi]
+        L.lyc_tuning_save.argtypes = [ctypes.c_char_p]
+        L.lyc_tuning_load.argtypes = [ctypes.c_char_p, pi]
+        L.lyc_tuning_clear.argtypes = []
+        L.lyc_tuning_count.argtypes = []
         L.lyc_gemm_tile.argtypes = [c_i64, c_i64, c_int, ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
         L.lyc_profile_begin.argtypes = [c_int]
         L.lyc_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_int)]
@@ -80,6 +93,8 @@ def lib():
                    L.lyc_lora_linear_workspace_size, L.lyc_lora_linear_fwd, L.lyc_lora_workspace_layout,
                    L.lyc_linear_workspace_layout, L.lyc_lora_merge_workspace_size, L.lyc_lora_merge_fwd,
                    L.lyc_lora_linear_bwd_workspace_size, L.lyc_lora_linear_bwd, L.lyc_lora_linear_bwd_workspace_layout,
+                   L.lyc_gemm_plan, L.lyc_lora_linear_tune, L.lyc_tuning_key, L.lyc_tuning_lookup, L.lyc_tuning_save,
+                   L.lyc_tuning_load, L.lyc_tuning_clear, L.lyc_tuning_count,
                    L.lyc_gemm_tile, L.lyc_profile_begin, L.lyc_profile_end):
             fn.restype = c_int
         _lib = L
@@ -186,6 +201,61 @@ def lora_bwd_workspace_layout(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt, dy_dt, w
                                                       ctypes.byref(ho), ctypes.byref(go), ctypes.byref(ld),
                                                       ctypes.byref(fo)))
     return ho.value, go.value, ld.value, fo.value
+
+
+def gemm_plan(M: int, N: int, K: int, rf: int, compute_dt: int, max_out: int = 7):
+    """The tile planner's shortlist, best first: [(tile_n, tile_m, ksplit, modelled_us)]."""
+    tn, tm, ks = (ctypes.c_int * 8)(), (ctypes.c_int * 8)(), (ctypes.c_int * 8)()
+    cost = (ctypes.c_double * 8)()
+    n = ctypes.c_int(0)
+    _check(lib().lyc_gemm_plan(M, N, K, rf, compute_dt, max_out, ctypes.byref(n), tn, tm, ks, cost))
+    return [(tn[i], tm[i], ks[i], cost[i]) for i in range(n.value)]
+
+
+def tuning_cache_path() -> str:
+    """Where the tuning table file lives: $LYC_KERNEL_CACHE_DIR/tuning.json
+    (default ~/.cache/lyc_kernels)."""
+    d = os.environ.get("LYC_KERNEL_CACHE_DIR", os.path.join(os.path.expanduser("~"), ".cache", "lyc_kernels"))
+    return os.path.join(d, "tuning.json")
+
+
+def tuning_save(path: Optional[str] = None) -> str:
+    path = path or tuning_cache_path()
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    _check(lib().lyc_tuning_save(path.encode()))
+    return path
+
+
+def tuning_load(path: Optional[str] = None) -> int:
+    """Merge a saved table into the process's table; returns the entries read (0 if no file)."""
+    path = path or tuning_cache_path()
+    if not os.path.exists(path):
+        return 0
+    n = ctypes.c_int(0)
+    _check(lib().lyc_tuning_load(path.encode(), ctypes.byref(n)))
+    return n.value
+
+
+def tuning_clear() -> None:
+    _check(lib().lyc_tuning_clear())
+
+
+def tuning_count() -> int:
+    return int(lib().lyc_tuning_count())
+
+
+def tuning_key(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().lyc_tuning_key(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt, buf, 256))
+    return buf.value.decode()
+
+
+def tuning_lookup(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt):
+    """(tile_n, tile_m, ksplit) stored for this call on the current device, or None."""
+    f, tn, tm, ks = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().lyc_tuning_lookup(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt, ctypes.byref(f), ctypes.byref(tn),
+                                   ctypes.byref(tm), ctypes.byref(ks)))
+    return (tn.value, tm.value, ks.value) if f.value else None
 
 
 def gemm_tile(M: int, N: int, compute_dt: int) -> Tuple[int, int]:
@@ -308,3 +378,31 @@ def lora_linear_backward(x: torch.Tensor, w: torch.Tensor, down: torch.Tensor, u
                                      _stream(dev)))
     out = (dx, dd, du)
     return (out, ws) if return_workspace else out
+
+
+def lora_linear_tune(x: torch.Tensor, w: torch.Tensor, down: torch.Tensor, up: torch.Tensor, scale: float,
+                     bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None):
+    """Time the planner's shortlist for this forward (blocking) and keep the
+    fastest for later calls of the same shape.  Returns (tile_n, tile_m,
+    ksplit, ms, [ms of each shortlisted candidate, in gemm_plan order])."""
+    dev = _need_device(x, w, down, up, bias, out)
+    M, K = x.shape
+    N = w.shape[0]
+    r = down.shape[0]
+    x_dt, w_dt, d_dt, u_dt = dtype_code(x), dtype_code(w), dtype_code(down), dtype_code(up)
+    b_dt = dtype_code(bias) if bias is not None else 0
+    _, o_dt = resolve_dtypes([x_dt, w_dt] + ([b_dt] if b_dt else []) + [d_dt, u_dt])
+    if out is None:
+        out = torch.empty((M, N), dtype=_TORCH[o_dt], device=dev)
+    ws = _workspace(lora_workspace_size(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt), dev, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    tn, tm, ks, ms = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0), ctypes.c_double(0)
+    cand = (ctypes.c_double * 7)(*([-1.0] * 7))
+    _check(lib().lyc_lora_linear_tune(_ptr(x), x_dt, _ptr(w), w_dt, _ptr(bias), b_dt, _ptr(down), d_dt, _ptr(up),
+                                      u_dt, r, float(scale), _ptr(out), dtype_code(out), M, N, K, _ptr(ws), nbytes,
+                                      _stream(dev), ctypes.byref(tn), ctypes.byref(tm), ctypes.byref(ks),
+                                      ctypes.byref(ms), cand))
+    n = len(gemm_plan(M, N, K, lora_workspace_layout(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt)[1] if r else 0,
+                      resolve_dtypes([x_dt, w_dt] + ([b_dt] if b_dt else []) + [d_dt, u_dt])[0]))
+    return tn.value, tm.value, ks.value, ms.value, [cand[i] for i in range(n)]

@@ -7,12 +7,16 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <string>
 #include <mutex>
 #include <vector>
 
 #include "bwd.h"
 #include "kernels.h"
 #include "merge.h"
+#include "tune.h"
 
 namespace {
 
@@ -78,7 +82,7 @@ int check_problem(Problem& P) {
 struct Layout {
     size_t xc = 0, wc = 0, dc = 0, dh = 0, dl = 0, uc = 0, h = 0, dnorm = 0, wh = 0, wl = 0, wnorm = 0, flagged = 0,
            partial = 0, total = 0;
-    int ksplit = 1;
+    int ksplit = 1, ks_max = 1;
     bool cast_x = false, cast_w = false;
 };
 
@@ -103,9 +107,15 @@ Layout layout(const Problem& P) {
         L.flagged = off; off = align256(off + sizeof(unsigned));
     }
     if (P.lora) {
-        // fp32 partial sums of a K-split GEMM (few output tiles)
+        // fp32 partial sums of a K-split GEMM (few output tiles), sized for
+        // the largest split of the planner's shortlist (a tuned pick may take it)
         L.ksplit = lyc::gemm_ksplit(P.M, P.N, P.K, P.c_dt);
-        if (L.ksplit > 1) { L.partial = off; off = align256(off + (size_t)L.ksplit * (size_t)(P.M * P.N) * 4); }
+        lyc::GemmCand plan[8];
+        const int np = lyc::gemm_plan(P.M, P.N, P.K, P.r_pad, P.c_dt, plan, 8);
+        int ks_max = L.ksplit;
+        for (int i = 0; i < np; ++i) ks_max = std::max(ks_max, plan[i].ksplit);
+        L.ks_max = ks_max;
+        if (ks_max > 1) { L.partial = off; off = align256(off + (size_t)ks_max * (size_t)(P.M * P.N) * 4); }
     }
     if (!P.lora) {
         // the projection's rounding guard: hi/lo split and row norms of W_c, a counter
@@ -149,8 +159,11 @@ hipError_t timed(int kind, hipStream_t s, F fn) {
     return e;
 }
 
+// The GEMM configuration a LoRA forward runs with: `force` (while tuning),
+// else a measured pick for this device and shape, else the analytic one.
 int forward(const Problem& P, const void* x, const void* w, const void* bias, const void* down, const void* up,
-            double scale, void* y, int y_dt, void* ws, size_t ws_bytes, void* stream) {
+            double scale, void* y, int y_dt, void* ws, size_t ws_bytes, void* stream,
+            const lyc::TuneChoice* force = nullptr) {
     if (y_dt != P.o_dt) return LYC_ERR_DTYPE_MISMATCH;
     if ((bias == nullptr) != (P.b_dt == 0)) return LYC_ERR_INVALID_ARG;
     if (P.M == 0 || P.N == 0) return LYC_OK;
@@ -235,7 +248,17 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
     g.rf = 0;
     g.ksplit = L.ksplit;
     g.post = 1.0f;
-    g.partial = L.ksplit > 1 ? (float*)(W + L.partial) : nullptr;
+    lyc::TuneChoice tc{};
+    const bool have = force ? (tc = *force, true)
+                            : lyc::tune_count() > 0 &&
+                                  lyc::tune_lookup(lyc::tune_key("lora_fwd", P.M, P.N, P.K, P.r_pad, P.c_dt, P.o_dt), &tc);
+    // a pick is taken only if this build can run it in this workspace
+    if (have && tc.ksplit >= 1 && tc.ksplit <= L.ks_max && tc.tile >= 0 && tc.tile <= 3 &&
+        (P.c_dt != LYC_F32 || tc.tile == lyc::GEMM_TILE_128x128 || tc.tile == lyc::GEMM_TILE_64x64)) {
+        g.tile = tc.tile;
+        g.ksplit = tc.ksplit;
+    }
+    g.partial = g.ksplit > 1 ? (float*)(W + L.partial) : nullptr;
     const uintptr_t vec_align = y_dt == LYC_F32 ? 16 : 8;
     g.vec_store = (P.N % 4 == 0) && aligned(y, vec_align);
 
@@ -680,6 +703,122 @@ int backward(const Bwd& B, const void* x, const void* w, const void* down, const
 
 extern "C" {
 
+int lyc_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t rf, int compute_dt, int max_out, int* count, int* tile_n,
+                  int* tile_m, int* ksplit, double* cost_us) {
+    if (M < 0 || N < 0 || K < 0 || rf < 0 || !valid_dt(compute_dt) || max_out < 0) return LYC_ERR_INVALID_ARG;
+    lyc::GemmCand c[8];
+    const int n = lyc::gemm_plan(M, N, K, rf, compute_dt, c, max_out < 8 ? max_out : 8);
+    if (count) *count = n;
+    for (int i = 0; i < n; ++i) {
+        int tn, tm;
+        lyc::gemm_tile_dims(c[i].tile, &tn, &tm);
+        if (tile_n) tile_n[i] = tn;
+        if (tile_m) tile_m[i] = tm;
+        if (ksplit) ksplit[i] = c[i].ksplit;
+        if (cost_us) cost_us[i] = c[i].cost;
+    }
+    return LYC_OK;
+}
+
+int lyc_lora_linear_tune(const void* x, int x_dt, const void* w, int w_dt, const void* bias, int bias_dt,
+                         const void* down, int down_dt, const void* up, int up_dt, int64_t rank, double scale,
+                         void* y, int y_dt, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                         void* stream, int* tile_n, int* tile_m, int* ksplit, double* best_ms, double* cand_ms) {
+    Problem P{true, M, N, K, rank, x_dt, w_dt, bias_dt, down_dt, up_dt, 0, 0, 0};
+    int st = check_problem(P);
+    if (st != LYC_OK) return st;
+    if (!valid_dt(y_dt)) return LYC_ERR_INVALID_ARG;
+    if (!(scale == scale) || scale > 3.4e38 || scale < -3.4e38) return LYC_ERR_INVALID_ARG;
+    const std::string key = lyc::tune_key("lora_fwd", M, N, K, P.r_pad, P.c_dt, P.o_dt);
+    if (key.empty()) return LYC_ERR_HIP;
+    lyc::GemmCand plan[8];
+    const int np = lyc::gemm_plan(M, N, K, P.r_pad, P.c_dt, plan, 7);
+    lyc::TuneChoice best{plan[0].tile, plan[0].ksplit, 0.0};
+    const char* env = std::getenv("LYC_KERNEL_TUNE");
+    const bool timing = !(env && (std::strcmp(env, "off") == 0 || std::strcmp(env, "0") == 0));
+    if (timing && M > 0 && N > 0) {
+        hipStream_t s = (hipStream_t)stream;
+        hipEvent_t a, b;
+        if (hipEventCreate(&a) != hipSuccess) return LYC_ERR_HIP;
+        if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return LYC_ERR_HIP; }
+        double best_t = 1e300;
+        for (int i = 0; i < np && st == LYC_OK; ++i) {
+            const lyc::TuneChoice c{plan[i].tile, plan[i].ksplit, 0.0};
+            st = forward(P, x, w, bias, down, up, scale, y, y_dt, workspace, workspace_bytes, stream, &c);   // warm
+            double t_min = 1e300;
+            for (int rep = 0; rep < 3 && st == LYC_OK; ++rep) {
+                float ms = 0.f;
+                if (hipEventRecord(a, s) != hipSuccess) { st = LYC_ERR_HIP; break; }
+                st = forward(P, x, w, bias, down, up, scale, y, y_dt, workspace, workspace_bytes, stream, &c);
+                if (st != LYC_OK) break;
+                if (hipEventRecord(b, s) != hipSuccess || hipEventSynchronize(b) != hipSuccess ||
+                    hipEventElapsedTime(&ms, a, b) != hipSuccess) { st = LYC_ERR_HIP; break; }
+                t_min = std::min(t_min, (double)ms);
+            }
+            if (cand_ms) cand_ms[i] = t_min;
+            if (st == LYC_OK && t_min < best_t) { best_t = t_min; best = c; best.ms = t_min; }
+        }
+        (void)hipEventDestroy(a);
+        (void)hipEventDestroy(b);
+        if (st != LYC_OK) return st;
+    }
+    lyc::tune_store(key, best);
+    int tn, tm;
+    lyc::gemm_tile_dims(best.tile, &tn, &tm);
+    if (tile_n) *tile_n = tn;
+    if (tile_m) *tile_m = tm;
+    if (ksplit) *ksplit = best.ksplit;
+    if (best_ms) *best_ms = best.ms;
+    return LYC_OK;
+}
+
+int lyc_tuning_key(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt, int bias_dt, int down_dt,
+                   int up_dt, char* buf, size_t len) {
+    Problem P{true, M, N, K, rank, x_dt, w_dt, bias_dt, down_dt, up_dt, 0, 0, 0};
+    const int st = check_problem(P);
+    if (st != LYC_OK) return st;
+    const std::string key = lyc::tune_key("lora_fwd", M, N, K, P.r_pad, P.c_dt, P.o_dt);
+    if (key.empty()) return LYC_ERR_HIP;
+    if (buf == nullptr || len < key.size() + 1) return LYC_ERR_INVALID_ARG;
+    std::memcpy(buf, key.c_str(), key.size() + 1);
+    return LYC_OK;
+}
+
+int lyc_tuning_lookup(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt, int bias_dt, int down_dt,
+                      int up_dt, int* found, int* tile_n, int* tile_m, int* ksplit) {
+    Problem P{true, M, N, K, rank, x_dt, w_dt, bias_dt, down_dt, up_dt, 0, 0, 0};
+    const int st = check_problem(P);
+    if (st != LYC_OK) return st;
+    lyc::TuneChoice c{};
+    const bool f = lyc::tune_lookup(lyc::tune_key("lora_fwd", M, N, K, P.r_pad, P.c_dt, P.o_dt), &c);
+    if (found) *found = f ? 1 : 0;
+    if (f) {
+        int tn, tm;
+        lyc::gemm_tile_dims(c.tile, &tn, &tm);
+        if (tile_n) *tile_n = tn;
+        if (tile_m) *tile_m = tm;
+        if (ksplit) *ksplit = c.ksplit;
+    }
+    return LYC_OK;
+}
+
+int lyc_tuning_save(const char* path) {
+    if (path == nullptr) return LYC_ERR_INVALID_ARG;
+    return lyc::tune_save(path) == 0 ? LYC_OK : LYC_ERR_IO;
+}
+
+int lyc_tuning_load(const char* path, int* entries) {
+    if (path == nullptr) return LYC_ERR_INVALID_ARG;
+    return lyc::tune_load(path, entries) == 0 ? LYC_OK : LYC_ERR_IO;
+}
+
+int lyc_tuning_clear(void) {
+    lyc::tune_clear();
+    return LYC_OK;
+}
+
+int lyc_tuning_count(void) { return lyc::tune_count(); }
+
 int lyc_lora_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt,
                                        int bias_dt, int down_dt, int up_dt, int dy_dt, int want, size_t* bytes) {
     Bwd B{Problem{true, M, N, K, rank, x_dt, w_dt, bias_dt, down_dt, up_dt, 0, 0, 0}, dy_dt, want, 0};
@@ -867,6 +1006,7 @@ const char* lyc_status_str(int status) {
     case LYC_ERR_UNSUPPORTED: return "unsupported shape, alignment or rank";
     case LYC_ERR_HIP: return "HIP runtime error while launching";
     case LYC_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case LYC_ERR_IO: return "tuning table file could not be read, parsed or written";
     default: return "unknown status";
     }
 }

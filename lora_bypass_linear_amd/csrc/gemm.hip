@@ -14,6 +14,9 @@
 // Accumulation is fp32 throughout (LyCORIS "Precision" page, "Dtype policy");
 // the bypass lands in the same accumulators as x.W^T, so Delta W = up.down is
 // never formed ("VRAM" section).
+#include <algorithm>
+#include <cmath>
+
 #include "kernels.h"
 #include "lyc_device.h"
 
@@ -429,8 +432,70 @@ void gemm_tile_shape(int64_t M, int64_t N, int c_dt, int* tn, int* tm) {
     *tm = shape[t][1];
 }
 
+void gemm_tile_dims(int tile, int* tn, int* tm) {
+    static const int shape[4][2] = {{256, 256}, {192, 256}, {128, 128}, {64, 64}};
+    const int t = tile < 0 || tile > 3 ? 3 : tile;
+    *tn = shape[t][0];
+    *tm = shape[t][1];
+}
+
+// The cost model: every workgroup of a tile runs its share of the K steps on
+// one CU (one workgroup per CU for every tile); the MFMA rate of a CU falls
+// with the tile's operand re-reads (the penalties of pick_tile); a K split
+// adds the fp32 partial sums' round trip through HBM and a second launch.
+int gemm_plan(int64_t M, int64_t N, int64_t K, int64_t rf, int c_dt, GemmCand* out, int max_out) {
+    if (max_out <= 0) return 0;
+    const bool f32 = c_dt == DT_F32;
+    const double es = f32 ? 4.0 : 2.0;
+    const double cu_rate = (f32 ? 157.3e12 : 2500e12) / 256.0;   // flop/s per CU at the published peak
+    const double hbm = 8.0e12;
+    struct T { int id; double pen; };
+    const T t16[] = {{T_L, 1.0}, {T_G, 1.0}, {T_M, 1.3}, {T_S, 2.0}};
+    const T t32[] = {{T_M, 1.0}, {T_S, 1.5}};
+    const T* ts = f32 ? t32 : t16;
+    const int nt = f32 ? 2 : 4;
+    const int64_t ksteps = (int64_t)((K * es + 127) / 128);
+    auto cost = [&](int tile, int ks, double pen) {
+        int tn, tm;
+        gemm_tile_dims(tile, &tn, &tm);
+        const double tiles = (double)((N + tn - 1) / tn) * (double)((M + tm - 1) / tm);
+        const double rounds = std::ceil(tiles * ks / 256.0);
+        const double steps = std::ceil((double)ksteps / ks) + (double)((rf * (int64_t)es + 127) / 128);
+        const double step_s = 2.0 * tn * tm * (128.0 / es) / cu_rate * pen;
+        double t = rounds * steps * step_s + 2e-6;
+        if (ks > 1) t += (double)M * N * 4.0 * (ks + 1) / hbm + 3e-6;
+        return t * 1e6;
+    };
+    GemmCand all[4 * 4];
+    int n = 0;   // at most 4 tiles x 4 K splits
+    double pen0 = 1.0;
+    const int t0 = pick_tile(M, N, f32), k0 = gemm_ksplit(M, N, K, c_dt);
+    for (int i = 0; i < nt; ++i) {
+        int tn, tm;
+        gemm_tile_dims(ts[i].id, &tn, &tm);
+        if (ts[i].id == t0) pen0 = ts[i].pen;
+        const double tiles = (double)((N + tn - 1) / tn) * (double)((M + tm - 1) / tm);
+        for (int ks = 1; ks <= 8; ks *= 2) {
+            if (ks > 1 && (tiles >= 256 || ks > ksteps / 4)) continue;
+            all[n++] = GemmCand{ts[i].id, ks, cost(ts[i].id, ks, ts[i].pen)};
+        }
+    }
+    // the analytic pick first, then the rest by modelled time
+    const GemmCand head{t0, k0, cost(t0, k0, pen0)};
+    int w = 0;
+    GemmCand rest[4 * 4];
+    for (int i = 0; i < n; ++i)
+        if (!(all[i].tile == t0 && all[i].ksplit == k0)) rest[w++] = all[i];
+    std::sort(rest, rest + w, [](const GemmCand& a, const GemmCand& b) { return a.cost < b.cost; });
+    int m = 0;
+    out[m++] = head;
+    for (int i = 0; i < w && m < max_out && m < 7; ++i) out[m++] = rest[i];
+    return m;
+}
+
 hipError_t launch_gemm(int c_dt, const GemmParams& p, hipStream_t s) {
-    const int t = pick_tile(p.M, p.N, c_dt == DT_F32);
+    int t = p.tile >= 0 ? p.tile : pick_tile(p.M, p.N, c_dt == DT_F32);
+    if (c_dt == DT_F32 && t != T_M && t != T_S) return hipErrorInvalidValue;   // no fp32 instance
     if (c_dt == DT_F16) {
         switch (t) {
         case T_L: return run<CF16, TileL>(p, s);

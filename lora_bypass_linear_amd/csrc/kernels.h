@@ -7,6 +7,11 @@
 
 namespace lyc {
 
+// Output tiles (rows of a x rows of b per workgroup); fp32 compute has 128x128
+// and 64x64 only.
+enum { GEMM_TILE_AUTO = -1, GEMM_TILE_256x256 = 0, GEMM_TILE_192x256 = 1, GEMM_TILE_128x128 = 2,
+       GEMM_TILE_64x64 = 3 };
+
 // y = epilogue( [scale * (af . bf^T)] + a . b^T ) for one output tile per
 // workgroup.  a = W_c [N,K], b = x_c [M,K], af = up_c [N,rf], bf = h_r [M,rf],
 // all in the compute dtype, rows 16-byte aligned.
@@ -30,8 +35,21 @@ struct GemmParams {
     float* partial;
     // y = round_out(post * acc + b): 1 in the forward; the scale of a weight
     // gradient whose product has no fold
-    float post;
+    float post = 1.0f;
+    // output tile: GEMM_TILE_AUTO (the analytic pick) or one of GEMM_TILE_*
+    int tile = GEMM_TILE_AUTO;
 };
+
+struct GemmCand {
+    int tile, ksplit;
+    double cost;   // the model's estimate, microseconds
+};
+// The planner's shortlist for an M x N x K product (+ rf fold steps), best
+// first: the analytic pick (the tile and K split launch_gemm takes by
+// itself), then the other tile / K-split pairs by modelled time.  Returns
+// the number written (at most max_out, at most 7).
+int gemm_plan(int64_t M, int64_t N, int64_t K, int64_t rf, int c_dt, GemmCand* out, int max_out);
+void gemm_tile_dims(int tile, int* tn, int* tm);
 
 // Exact-rounding contraction (h pass and plain affine projection):
 // C = x_c . b^T with fp64-folded MFMA steps, a rounding guard and in-kernel
