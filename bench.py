@@ -465,11 +465,29 @@ def _small_m(dev, reps=50):
             torch.cuda.synchronize()
             prof = L.profile_end()
             dev_us = sum(ms for _, ms in prof.values()) * 1e3 / reps
-            res.append({"workload": f"{base} at M={M}", "wall_us_per_call": round(wall_us, 2),
-                        "device_us_per_call": round(dev_us, 2),
-                        "kernels": {k: round(ms * 1e3 / reps, 2) for k, (n, ms) in prof.items() if n},
-                        "hbm_gbs": round(wl.bytes / (dev_us * 1e-6) / 1e9, 1),
-                        "tflops": round(wl.flops / (dev_us * 1e-6) / 1e12, 3)})
+            entry = {"workload": f"{base} at M={M}", "wall_us_per_call": round(wall_us, 2),
+                     "device_us_per_call": round(dev_us, 2),
+                     "kernels": {k: round(ms * 1e3 / reps, 2) for k, (n, ms) in prof.items() if n},
+                     "hbm_gbs": round(wl.bytes / (dev_us * 1e-6) / 1e9, 1),
+                     "tflops": round(wl.flops / (dev_us * 1e-6) / 1e12, 3)}
+            if wl.kind == "lora":
+                # the measured tile pick: the planner's shortlist timed, then the same calls again
+                c_dt = L.resolve_dtypes([L.dtype_code(d[k]) for k in ("x", "w", "down", "up")])[0]
+                plan = L.gemm_plan(wl.M, wl.N, wl.K, 16, c_dt)
+                tn, tm, ks, _, cand = L.lora_linear_tune(d["x"], d["w"], d["down"], d["up"], wl.scale, d.get("b"),
+                                                         out=y, workspace=ws)
+                L.profile_begin(8 * reps)
+                for _ in range(reps):
+                    call()
+                torch.cuda.synchronize()
+                tuned_us = sum(ms for _, ms in L.profile_end().values()) * 1e3 / reps
+                entry["tuned"] = {"analytic_pick": list(plan[0][:3]), "pick": [tn, tm, ks],
+                                  "device_us_per_call": round(tuned_us, 2),
+                                  "shortlist": [{"tile": f"{p[0]}x{p[1]}", "ksplit": p[2],
+                                                 "model_us": round(p[3], 2), "measured_us": round(c * 1e3, 2)}
+                                                for p, c in zip(plan, cand)]}
+                L.tuning_clear()
+            res.append(entry)
     return res
 
 
