@@ -79,6 +79,13 @@ def lib():
         L.oracle_backward.argtypes = [vp, ci, vp, ci, ci, vp, ci, vp, ci, i64, ctypes.c_double, vp, ci,
                                       i64, i64, i64, vp, i64, vp, vp, vp, vp, i64, vp, i64, vp, vp, vp, i64,
                                       vp, vp, vp, vp, vp, ci, ctypes.POINTER(ctypes.c_int)]
+        L.oracle_dora_norms.restype = ctypes.c_int
+        L.oracle_dora_norms.argtypes = [vp, ci, vp, ci, vp, ci, i64, ctypes.c_double, i64, i64, vp, i64, vp, vp, ci,
+                                        ctypes.POINTER(ctypes.c_int)]
+        L.oracle_dora_forward.restype = ctypes.c_int
+        L.oracle_dora_forward.argtypes = [vp, ci, vp, ci, vp, ci, vp, ci, vp, ci, vp, ci, i64, ctypes.c_double, i64,
+                                          i64, i64, vp, i64, vp, vp, vp, ci, ctypes.POINTER(ctypes.c_int),
+                                          ctypes.POINTER(ctypes.c_int)]
         _lib = L
     return _lib
 
@@ -275,6 +282,62 @@ def backward(x, x_dt, w, w_dt, down, down_dt, up, up_dt, dy, dy_dt, scale: float
         raise OracleError(st)
     return {"compute": c_out.value, "dx": dx, "dx_ref": dx_ref, "gh": gh, "d_down": d_down, "dd_ref": dd_ref,
             "d_up": d_up, "du_ref": du_ref, "dx_rss": dx_rss, "dd_rss": dd_rss, "du_rss": du_rss}
+
+
+def dora_norms(w, w_dt, down, down_dt, up, up_dt, scale: float = 1.0, rows=None, nthreads: Optional[int] = None):
+    """DoRA row norms RN_fp32(||W + scale * up_c.down_c||_2) for the rows of W
+    in ``rows`` (default all).  Returns (norms float32, exact float64, compute)."""
+    w = np.ascontiguousarray(w, dtype=storage_np(w_dt))
+    down = np.ascontiguousarray(down, dtype=storage_np(down_dt))
+    up = np.ascontiguousarray(up, dtype=storage_np(up_dt))
+    N, K = w.shape
+    r = down.shape[0]
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nrows = N if rows is None else rows_arr.size
+    norms = np.zeros(nrows, dtype=np.float32)
+    exact = np.zeros(nrows)
+    c_out = ctypes.c_int(0)
+    st = lib().oracle_dora_norms(_ptr(w), w_dt, _ptr(down), down_dt, _ptr(up), up_dt, r, float(scale), N, K,
+                                 _ptr(rows_arr), nrows, _ptr(norms), _ptr(exact),
+                                 int(default_threads() if nthreads is None else nthreads), ctypes.byref(c_out))
+    if st != OK:
+        raise OracleError(st)
+    return norms, exact, c_out.value
+
+
+def dora_forward(x, x_dt, w, w_dt, b, b_dt, down, down_dt, up, up_dt, mag, m_dt, scale: float = 1.0, rows=None,
+                 nthreads: Optional[int] = None):
+    """The DoRA forward y = round_out((m/norm) * (x_c.W_c^T + scale h_r.up_c^T) + b)
+    with the fp32 row norms computed here.  Returns a dict like ``forward`` plus
+    ``norms`` (float32 [N])."""
+    x = np.ascontiguousarray(x, dtype=storage_np(x_dt))
+    w = np.ascontiguousarray(w, dtype=storage_np(w_dt))
+    down = np.ascontiguousarray(down, dtype=storage_np(down_dt))
+    up = np.ascontiguousarray(up, dtype=storage_np(up_dt))
+    mag = np.ascontiguousarray(mag, dtype=storage_np(m_dt))
+    if b is not None:
+        b = np.ascontiguousarray(b, dtype=storage_np(b_dt))
+    M, K = x.shape
+    N = w.shape[0]
+    r = down.shape[0]
+    assert mag.shape == (N,) and up.shape == (N, r) and down.shape == (r, K)
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nrows = M if rows is None else rows_arr.size
+    dts = [x_dt, w_dt] + ([b_dt] if b is not None else []) + [down_dt, up_dt, m_dt]
+    st, c_dt, o_dt = resolve(dts)
+    if st != OK:
+        raise OracleError(st)
+    y = np.zeros((nrows, N), dtype=storage_np(o_dt))
+    ref = np.zeros((nrows, N))
+    norms = np.zeros(N, dtype=np.float32)
+    c_out, o_out = ctypes.c_int(0), ctypes.c_int(0)
+    st = lib().oracle_dora_forward(_ptr(x), x_dt, _ptr(w), w_dt, _ptr(b), b_dt or 0, _ptr(down), down_dt, _ptr(up),
+                                   up_dt, _ptr(mag), m_dt, r, float(scale), M, N, K, _ptr(rows_arr), nrows, _ptr(y),
+                                   _ptr(ref), _ptr(norms), int(default_threads() if nthreads is None else nthreads),
+                                   ctypes.byref(c_out), ctypes.byref(o_out))
+    if st != OK:
+        raise OracleError(st)
+    return {"compute": c_out.value, "output": o_out.value, "y": y, "ref": ref, "norms": norms}
 
 
 # ---- scoring ----------------------------------------------------------------

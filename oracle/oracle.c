@@ -39,6 +39,11 @@
  *               h and the gradient at h, gh = scale * dy_c . up_c, are each
  *               rounded once to the storage dtype before their second dots,
  *               as the forward rounds h; dx, dDown and dUp round once.
+ *   dora     -- the row norms of the merged weight, RN_fp32(||W + scale up_c.down_c||_2)
+ *               per row (the cached DoRA state of the "VRAM" section), and
+ *               the DoRA forward y = round_out((m/norm) (x_c.W_c^T +
+ *               scale h_r.up_c^T) + b): the magnitude vector m scales the
+ *               LoRA product of each output feature, the bias is added after.
  *   rounding -- IEEE round-to-nearest, ties-to-even, directly from fp64 (never
  *               via fp32), gradual underflow, overflow to +-inf at or beyond
  *               max + half an ulp, NaN propagated.
@@ -614,5 +619,149 @@ int oracle_backward(const void* x, int x_dt, const void* w, int w_dt, int b_dt, 
 
     free(xc); free(wc); free(dc); free(uc); free(gc);
     free(hj); free(ghj); free(ghr);
+    return OR_OK;
+}
+
+/* ---- DoRA ------------------------------------------------------------------- */
+
+/* The row norms of the merged weight, before its rounding: for each row n,
+ *   norm_n = RN_fp32( || W[n,:] + scale * (up_c . down_c)[n,:] ||_2 )
+ * with the merge's policy over (W, down, up): W keeps its stored value, up and
+ * down are rounded to the compute dtype (LyCORIS "Precision" page, "VRAM": the
+ * DoRA row norms are the small cached state, one fp32 value per row).  The sum
+ * of squares is binary64 in k order and its square root the binary64 one. */
+typedef struct {
+    const void* w;
+    int w_dt;
+    int64_t N, K, r;
+    double scale;
+    const double *dc, *uc;
+    const int64_t* rows;
+    float* norms;
+    double* exact;
+} dnorm_t;
+
+static void dora_norm_rows(void* ctx, int64_t lo, int64_t hi) {
+    dnorm_t* D = (dnorm_t*)ctx;
+    const int64_t K = D->K, r = D->r;
+    for (int64_t i = lo; i < hi; ++i) {
+        const int64_t n = D->rows ? D->rows[i] : i;
+        double q = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double d = 0.0;
+            for (int64_t j = 0; j < r; ++j) d += D->uc[n * r + j] * D->dc[j * K + k];
+            const double v = widen(D->w, D->w_dt, n * K + k) + D->scale * d;
+            q += v * v;
+        }
+        const double s = sqrt(q);
+        if (D->exact) D->exact[i] = s;
+        if (D->norms) D->norms[i] = (float)oracle_round(s, OR_F32);
+    }
+}
+
+int oracle_dora_norms(const void* w, int w_dt, const void* down, int down_dt, const void* up, int up_dt, int64_t r,
+                      double scale, int64_t N, int64_t K, const int64_t* rows, int64_t nrows, float* norms,
+                      double* exact, int nthreads, int* c_out) {
+    int dts[3] = {w_dt, down_dt, up_dt};
+    int c_dt, o_dt;
+    int st = oracle_resolve(dts, 3, &c_dt, &o_dt);
+    if (st != OR_OK) return st;
+    if (c_out) *c_out = c_dt;
+    if (N < 0 || K < 0 || r < 0 || nrows < 0) return OR_INVALID;
+    for (int64_t i = 0; rows && i < nrows; ++i)
+        if (rows[i] < 0 || rows[i] >= N) return OR_INVALID;
+    if (!rows && nrows > N) return OR_INVALID;
+    dnorm_t D;
+    memset(&D, 0, sizeof D);
+    D.w = w; D.w_dt = w_dt; D.N = N; D.K = K; D.r = r; D.scale = scale;
+    double* dc = cast_all(down, down_dt, c_dt, r * K);
+    double* uc = cast_all(up, up_dt, c_dt, N * r);
+    D.dc = dc; D.uc = uc; D.rows = rows; D.norms = norms; D.exact = exact;
+    par_for(nrows, nthreads, dora_norm_rows, &D);
+    free(dc);
+    free(uc);
+    return OR_OK;
+}
+
+/* The DoRA forward for the given rows of x, with norms = the fp32 row norms
+ * above (computed here from W, down and up):
+ *   y = round_out( (m_n / norm_n) * (x_c . W_c^T + scale * h_r . up_c^T)_n + b_n )
+ * The policy runs over (x, W, b, down, up, m); h_r is the LoRA forward's;
+ * m_n / norm_n is one binary64 division, the bias is added after the
+ * magnitude scaling, one final rounding. */
+typedef struct {
+    const void *x, *b, *m;
+    int x_dt, b_dt, m_dt, c_dt, o_dt;
+    int64_t N, K, r;
+    double scale;
+    const double *wc, *dc, *uc;
+    const float* norms;          /* [N] */
+    const int64_t* rows;
+    void* y;
+    double* ref;
+} dfwd_t;
+
+static void dora_fwd_rows(void* ctx, int64_t lo, int64_t hi) {
+    dfwd_t* D = (dfwd_t*)ctx;
+    const int64_t N = D->N, K = D->K, r = D->r;
+    double* xc = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    double* h = (double*)malloc(sizeof(double) * (size_t)(r > 0 ? r : 1));
+    for (int64_t i = lo; i < hi; ++i) {
+        const int64_t m = D->rows ? D->rows[i] : i;
+        for (int64_t k = 0; k < K; ++k) xc[k] = oracle_round(widen(D->x, D->x_dt, m * K + k), D->c_dt);
+        for (int64_t j = 0; j < r; ++j) {
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k) s += xc[k] * D->dc[j * K + k];
+            h[j] = oracle_round(s, D->c_dt);
+        }
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0, f = 0.0;
+            for (int64_t k = 0; k < K; ++k) acc += xc[k] * D->wc[n * K + k];
+            for (int64_t j = 0; j < r; ++j) f += h[j] * D->uc[n * r + j];
+            const double g = widen(D->m, D->m_dt, n) / (double)D->norms[n];
+            const double bias = D->b ? widen(D->b, D->b_dt, n) : 0.0;
+            const double v = g * (acc + D->scale * f) + bias;
+            if (D->ref) D->ref[i * N + n] = v;
+            if (D->y) store(D->y, D->o_dt, i * N + n, oracle_round(v, D->o_dt));
+        }
+    }
+    free(xc);
+    free(h);
+}
+
+int oracle_dora_forward(const void* x, int x_dt, const void* w, int w_dt, const void* b, int b_dt, const void* down,
+                        int down_dt, const void* up, int up_dt, const void* mag, int m_dt, int64_t r, double scale,
+                        int64_t M, int64_t N, int64_t K, const int64_t* rows, int64_t nrows, void* y, double* ref,
+                        float* norms_out, int nthreads, int* c_out, int* o_out) {
+    int dts[6], nd = 0;
+    dts[nd++] = x_dt;
+    dts[nd++] = w_dt;
+    if (b) dts[nd++] = b_dt;
+    dts[nd++] = down_dt;
+    dts[nd++] = up_dt;
+    dts[nd++] = m_dt;
+    int c_dt, o_dt;
+    int st = oracle_resolve(dts, nd, &c_dt, &o_dt);
+    if (st != OR_OK) return st;
+    if (c_out) *c_out = c_dt;
+    if (o_out) *o_out = o_dt;
+    if (M < 0 || N < 0 || K < 0 || r < 0 || nrows < 0) return OR_INVALID;
+    for (int64_t i = 0; rows && i < nrows; ++i)
+        if (rows[i] < 0 || rows[i] >= M) return OR_INVALID;
+    if (!rows && nrows > M) return OR_INVALID;
+    float* norms = (float*)malloc(sizeof(float) * (size_t)(N > 0 ? N : 1));
+    st = oracle_dora_norms(w, w_dt, down, down_dt, up, up_dt, r, scale, N, K, NULL, N, norms, NULL, nthreads, NULL);
+    if (st != OR_OK) { free(norms); return st; }
+    if (norms_out) memcpy(norms_out, norms, sizeof(float) * (size_t)N);
+    dfwd_t D;
+    memset(&D, 0, sizeof D);
+    D.x = x; D.b = b; D.m = mag; D.x_dt = x_dt; D.b_dt = b_dt; D.m_dt = m_dt; D.c_dt = c_dt; D.o_dt = o_dt;
+    D.N = N; D.K = K; D.r = r; D.scale = scale;
+    double* wc = cast_all(w, w_dt, c_dt, N * K);
+    double* dc = cast_all(down, down_dt, c_dt, r * K);
+    double* uc = cast_all(up, up_dt, c_dt, N * r);
+    D.wc = wc; D.dc = dc; D.uc = uc; D.norms = norms; D.rows = rows; D.y = y; D.ref = ref;
+    par_for(nrows, nthreads, dora_fwd_rows, &D);
+    free(wc); free(dc); free(uc); free(norms);
     return OR_OK;
 }

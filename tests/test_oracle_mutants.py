@@ -46,6 +46,13 @@ MUTANTS = [
     ("bwd-dup-scale-missing", "const double v = B->scale * s;", "const double v = s;"),
     ("bwd-ddown-uses-x-not-cast", "double* xc = cast_all(x, x_dt, c_dt, M * K);\n    double* wc = cast_all(w, w_dt, c_dt, N * K);\n    double* dc = cast_all(down, down_dt, c_dt, r * K);\n    double* uc = cast_all(up, up_dt, c_dt, N * r);\n    double* gc",
      "double* xc = cast_all(x, x_dt, x_dt, M * K);\n    double* wc = cast_all(w, w_dt, c_dt, N * K);\n    double* dc = cast_all(down, down_dt, c_dt, r * K);\n    double* uc = cast_all(up, up_dt, c_dt, N * r);\n    double* gc"),
+    ("dora-norm-without-delta", "const double v = widen(D->w, D->w_dt, n * K + k) + D->scale * d;",
+     "const double v = widen(D->w, D->w_dt, n * K + k);"),
+    ("dora-norm-not-rooted", "const double s = sqrt(q);", "const double s = q;"),
+    ("dora-gain-inverted", "const double g = widen(D->m, D->m_dt, n) / (double)D->norms[n];",
+     "const double g = (double)D->norms[n] / widen(D->m, D->m_dt, n);"),
+    ("dora-bias-scaled", "const double v = g * (acc + D->scale * f) + bias;", "const double v = g * (acc + D->scale * f + bias);"),
+    ("dora-gain-on-base-only", "const double v = g * (acc + D->scale * f) + bias;", "const double v = g * acc + D->scale * f + bias;"),
     ("bwd-dx-rounded-to-compute", "if (B->dx) store(B->dx, B->x_dt, i * K + k, oracle_round(v, B->x_dt));",
      "if (B->dx) store(B->dx, B->x_dt, i * K + k, oracle_round(oracle_round(v, B->c_dt), B->x_dt));"),
 ]

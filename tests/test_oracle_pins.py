@@ -621,3 +621,80 @@ def test_tolerance_sum_forms():
     np.testing.assert_allclose(oracle.tolerance_sum(ref, rss, F32, 100), 8.0 * 2.0 ** -24 * 10.0 * ref + acc)
     # the forward's fp32 bound is the special case rss = 1
     np.testing.assert_allclose(oracle.tolerance_sum(ref, np.ones(2), F32, 100), oracle.tolerance(ref, F32, 100, 0))
+
+
+# ---- DoRA ----------------------------------------------------------------------------
+
+def test_dora_norms_exact_and_correctly_rounded():
+    """Integer rows whose merged norms are exact (3, 7, 9) or irrational (sqrt 18):
+    the fp32 norm is the exact square root rounded once to fp32."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 60
+    enc = lambda v, dt, s: oracle.encode(np.array(v, dtype=np.float64).ravel(), dt).reshape(s)
+    # W + up.down: up = [0, 0, 1, 1]^T, down = [[1, 0, 0, 0]]
+    W = [[1, 2, 2, 0], [2, 3, 6, 0], [0, 4, 8, 0], [2, 3, 0, 0]]
+    w, down, up = enc(W, F16, (4, 4)), enc([1, 0, 0, 0], F16, (1, 4)), enc([0, 0, 1, 1], F16, (4, 1))
+    norms, exact, c = oracle.dora_norms(w, F16, down, F16, up, F16, scale=1.0)
+    merged = np.array(W, dtype=np.float64) + np.outer([0, 0, 1, 1], [1, 0, 0, 0])
+    for n in range(4):
+        q = sum(Decimal(int(v)) ** 2 for v in merged[n])
+        want = oracle.round_to(float(q.sqrt()), F32)
+        assert float(norms[n]) == want, (n, norms[n], want)
+    assert norms[:3].tolist() == [3.0, 7.0, 9.0] and abs(float(norms[3]) - 18 ** 0.5) < 3e-7   # [3, 3, 0, 0]
+
+
+def _dora_case(dt, rng, M=5, K=8, with_bias=True):
+    enc = lambda v: oracle.encode(np.asarray(v, dtype=np.float64).ravel(), dt).reshape(np.shape(v))
+    rows = np.zeros((4, K))
+    rows[0, :3] = [1, 2, 2]
+    rows[1, :3] = [2, 3, 6]
+    rows[2, :3] = [1, 4, 8]
+    rows[3, :3] = [4, 4, 7]                                   # norms 3, 7, 9, 9
+    x = enc(np.round(rng.standard_normal((M, K)) * 4) / 4)
+    b = enc(np.round(rng.standard_normal(4) * 8) / 8) if with_bias else None
+    down = enc(np.round(rng.standard_normal((2, K)) * 4) / 4)
+    return x, enc(rows), b, down, enc(np.zeros((4, 2)))
+
+
+@pytest.mark.parametrize("dt", [F16, BF16, F32])
+def test_dora_unit_gain_is_the_lora_forward(dt):
+    """With up = 0 the merged weight is W; a magnitude equal to each row's norm
+    gives gain 1, so y is the LoRA forward (bias added unscaled); a magnitude
+    of twice the norm gives the forward of 2W."""
+    rng = np.random.default_rng(31)
+    x, w, b, down, up = _dora_case(dt, rng)
+    m1 = oracle.encode(np.array([3.0, 7.0, 9.0, 9.0]), dt)
+    got = oracle.dora_forward(x, dt, w, dt, b, dt, down, dt, up, dt, m1, dt, scale=1.5)
+    lora = oracle.forward(x, dt, w, dt, b, dt, down, dt, up, dt, scale=1.5)
+    np.testing.assert_array_equal(got["y"], lora["y"])
+    assert got["norms"].tolist() == [3.0, 7.0, 9.0, 9.0]
+    m2 = oracle.encode(np.array([6.0, 14.0, 18.0, 18.0]), dt)
+    w2 = oracle.encode(2 * oracle.as_float64(w, dt).ravel(), dt).reshape(w.shape)
+    got2 = oracle.dora_forward(x, dt, w, dt, b, dt, down, dt, up, dt, m2, dt, scale=1.5)
+    np.testing.assert_array_equal(got2["y"], oracle.forward(x, dt, w2, dt, b, dt, down, dt, up, dt, scale=1.5)["y"])
+
+
+def test_dora_is_invariant_to_the_scale_of_the_merged_weight():
+    """Doubling W and up doubles the merged weight and its norms: y is unchanged."""
+    rng = np.random.default_rng(32)
+    dt = BF16
+    M, N, K, r = 6, 5, 16, 3
+    x, w, d, u = (_draw(rng, s, dt, 0.5) for s in ((M, K), (N, K), (r, K), (N, r)))
+    b, mag = _draw(rng, (N,), dt, 0.5), _draw(rng, (N,), dt)
+    dbl = lambda a: oracle.encode(2 * oracle.as_float64(a, dt).ravel(), dt).reshape(a.shape)
+    y1 = oracle.dora_forward(x, dt, w, dt, b, dt, d, dt, u, dt, mag, dt, scale=0.75)
+    y2 = oracle.dora_forward(x, dt, dbl(w), dt, b, dt, d, dt, dbl(u), dt, mag, dt, scale=0.75)
+    np.testing.assert_array_equal(y1["y"], y2["y"])
+    np.testing.assert_array_equal(y2["norms"], 2 * y1["norms"])
+    # a row subset is the same rows of the full evaluation
+    part = oracle.dora_forward(x, dt, w, dt, b, dt, d, dt, u, dt, mag, dt, scale=0.75, rows=[4, 1])
+    np.testing.assert_array_equal(part["y"], y1["y"][[4, 1]])
+
+
+def test_dora_policy():
+    rng = np.random.default_rng(33)
+    x, w, d, u = (_draw(rng, s, F16) for s in ((2, 8), (3, 8), (1, 8), (3, 1)))
+    got = oracle.dora_forward(x, F16, w, F16, None, None, d, F16, u, F16, _draw(rng, (3,), F32), F32)
+    assert got["compute"] == F16 and got["output"] == F32             # an fp32 magnitude promotes y
+    with pytest.raises(oracle.OracleError):
+        oracle.dora_forward(x, F16, w, F16, None, None, d, F16, u, F16, _draw(rng, (3,), BF16), BF16)
