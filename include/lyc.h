@@ -230,6 +230,39 @@ int lyc_lora_linear_bwd_workspace_layout(int64_t M, int64_t N, int64_t K, int64_
                                          size_t* h_offset, size_t* gh_offset, int64_t* ld, size_t* flagged_offset);
 
 /*
+ * DoRA (the LyCORIS "Precision" page, "VRAM": the DoRA row norms are the small
+ * state the kernels cache, one fp32 value per row).  The merged weight
+ * V = W + scale * up_c . down_c (the merge's definition and dtype policy over
+ * (W, down, up), never stored) and its row norms
+ *   norm_n = || V[n, :] ||_2 ,
+ * then the DoRA forward, with the magnitude vector m [N]:
+ *   y = round_out( (m_n / norm_n) * (x_c.W_c^T + scale * round_c(x_c.down_c^T).up_c^T)_n + b_n )
+ * -- the LoRA forward with each output feature's sum scaled before the bias
+ * is added.  The dtype policy runs over (x, W, b, down, up, m).
+ * lyc_dora_norms: norms [N] fp32 (device), computed tile by tile from W and
+ *   the factors (fp32 sums of squares per tile, added in tile order, square
+ *   root); the workspace (256-byte aligned, lyc_dora_norms_workspace_size
+ *   bytes) holds the factors' compute-dtype copies and the per-tile sums.
+ *   norms must not overlap W.  Argument errors as lyc_lora_merge_fwd.
+ * lyc_dora_linear_fwd: the arguments of lyc_lora_linear_fwd plus magnitude
+ *   (m_dt, element-aligned) and norms (fp32, as lyc_dora_norms writes them);
+ *   the gain m_n / norm_n is one fp32 division, applied to the fp32 sum.
+ *   Workspace: lyc_dora_linear_workspace_size (the LoRA forward's plus the
+ *   gain vector).  Errors as lyc_lora_linear_fwd.
+ */
+int lyc_dora_norms_workspace_size(int64_t N, int64_t K, int64_t rank, int w_dt, int down_dt, int up_dt,
+                                  size_t* bytes);
+int lyc_dora_norms(const void* w, int w_dt, const void* down, int down_dt, const void* up, int up_dt, int64_t rank,
+                   double scale, float* norms, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                   void* stream);
+int lyc_dora_linear_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt, int bias_dt,
+                                   int down_dt, int up_dt, int m_dt, size_t* bytes);
+int lyc_dora_linear_fwd(const void* x, int x_dt, const void* w, int w_dt, const void* bias, int bias_dt,
+                        const void* down, int down_dt, const void* up, int up_dt, const void* magnitude, int m_dt,
+                        const float* norms, int64_t rank, double scale, void* y, int y_dt, int64_t M, int64_t N,
+                        int64_t K, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Tile planner and measured pick for the LoRA forward's main contraction
  * (LyCORIS "Backend Selection" page, "Tile selection": an analytic model
  * shortlists candidates, the shortlist is timed once, best of three, and the

@@ -14,7 +14,7 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 __all__ = ["F16", "BF16", "F32", "LycError", "MixedHalfError", "lib", "resolve_dtypes", "linear", "lora_linear",
-           "lora_merge", "lora_linear_backward", "linear_workspace_size", "lora_workspace_size", "lora_workspace_layout",
+           "lora_merge", "lora_linear_backward", "dora_norms", "dora_linear", "linear_workspace_size", "lora_workspace_size", "lora_workspace_layout",
            "linear_workspace_layout", "lora_merge_workspace_size", "lora_bwd_workspace_size",
            "lora_bwd_workspace_layout", "gemm_tile", "gemm_plan", "lora_linear_tune", "tuning_save",
            "tuning_load", "tuning_clear", "tuning_count", "tuning_key", "tuning_lookup", "tuning_cache_path", "profile_begin", "profile_end",
@@ -84,6 +84,14 @@ def lib():
         L.lyc_tuning_load.argtypes = [ctypes.c_char_p, pi]
         L.lyc_tuning_clear.argtypes = []
         L.lyc_tuning_count.argtypes = []
+        L.lyc_dora_norms_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_int, c_int, c_int, ctypes.POINTER(c_sz)]
+        L.lyc_dora_norms.argtypes = [c_vp, c_int, c_vp, c_int, c_vp, c_int, c_i64, ctypes.c_double, c_vp, c_i64,
+                                     c_i64, c_vp, c_sz, c_vp]
+        L.lyc_dora_linear_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_i64, c_int, c_int, c_int, c_int, c_int,
+                                                     c_int, ctypes.POINTER(c_sz)]
+        L.lyc_dora_linear_fwd.argtypes = [c_vp, c_int, c_vp, c_int, c_vp, c_int, c_vp, c_int, c_vp, c_int, c_vp,
+                                          c_int, c_vp, c_i64, ctypes.c_double, c_vp, c_int, c_i64, c_i64, c_i64,
+                                          c_vp, c_sz, c_vp]
         L.lyc_gemm_tile.argtypes = [c_i64, c_i64, c_int, ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
         L.lyc_profile_begin.argtypes = [c_int]
         L.lyc_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_int)]
@@ -94,7 +102,8 @@ def lib():
                    L.lyc_linear_workspace_layout, L.lyc_lora_merge_workspace_size, L.lyc_lora_merge_fwd,
                    L.lyc_lora_linear_bwd_workspace_size, L.lyc_lora_linear_bwd, L.lyc_lora_linear_bwd_workspace_layout,
                    L.lyc_gemm_plan, L.lyc_lora_linear_tune, L.lyc_tuning_key, L.lyc_tuning_lookup, L.lyc_tuning_save,
-                   L.lyc_tuning_load, L.lyc_tuning_clear, L.lyc_tuning_count,
+                   L.lyc_tuning_load, L.lyc_tuning_clear, L.lyc_tuning_count, L.lyc_dora_norms_workspace_size,
+                   L.lyc_dora_norms, L.lyc_dora_linear_workspace_size, L.lyc_dora_linear_fwd,
                    L.lyc_gemm_tile, L.lyc_profile_begin, L.lyc_profile_end):
             fn.restype = c_int
         _lib = L
@@ -406,3 +415,46 @@ def lora_linear_tune(x: torch.Tensor, w: torch.Tensor, down: torch.Tensor, up: t
     n = len(gemm_plan(M, N, K, lora_workspace_layout(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt)[1] if r else 0,
                       resolve_dtypes([x_dt, w_dt] + ([b_dt] if b_dt else []) + [d_dt, u_dt])[0]))
     return tn.value, tm.value, ks.value, ms.value, [cand[i] for i in range(n)]
+
+
+def dora_norms(w: torch.Tensor, down: torch.Tensor, up: torch.Tensor, scale: float,
+               out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """DoRA row norms ||W + scale * up_c.down_c||_2 per row of W [N,K], fp32 [N]."""
+    dev = _need_device(w, down, up, out)
+    N, K = w.shape
+    r = down.shape[0]
+    w_dt, d_dt, u_dt = dtype_code(w), dtype_code(down), dtype_code(up)
+    if out is None:
+        out = torch.empty(N, dtype=torch.float32, device=dev)
+    n = ctypes.c_size_t(0)
+    _check(lib().lyc_dora_norms_workspace_size(N, K, r, w_dt, d_dt, u_dt, ctypes.byref(n)))
+    ws = _workspace(n.value, dev, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().lyc_dora_norms(_ptr(w), w_dt, _ptr(down), d_dt, _ptr(up), u_dt, r, float(scale), _ptr(out), N, K,
+                                _ptr(ws), nbytes, _stream(dev)))
+    return out
+
+
+def dora_linear(x: torch.Tensor, w: torch.Tensor, down: torch.Tensor, up: torch.Tensor, scale: float,
+                magnitude: torch.Tensor, norms: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = round_out((m/norm) * (x.W^T + scale * round_c(x.down^T).up^T) + b) on the GPU."""
+    dev = _need_device(x, w, down, up, magnitude, norms, bias, out)
+    if norms.dtype != torch.float32:
+        raise ValueError("DoRA norms are fp32")
+    M, K = x.shape
+    N = w.shape[0]
+    r = down.shape[0]
+    x_dt, w_dt, d_dt, u_dt, m_dt = (dtype_code(t) for t in (x, w, down, up, magnitude))
+    b_dt = dtype_code(bias) if bias is not None else 0
+    _, o_dt = resolve_dtypes([x_dt, w_dt] + ([b_dt] if b_dt else []) + [d_dt, u_dt, m_dt])
+    if out is None:
+        out = torch.empty((M, N), dtype=_TORCH[o_dt], device=dev)
+    n = ctypes.c_size_t(0)
+    _check(lib().lyc_dora_linear_workspace_size(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt, m_dt, ctypes.byref(n)))
+    ws = _workspace(n.value, dev, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().lyc_dora_linear_fwd(_ptr(x), x_dt, _ptr(w), w_dt, _ptr(bias), b_dt, _ptr(down), d_dt, _ptr(up), u_dt,
+                                     _ptr(magnitude), m_dt, _ptr(norms), r, float(scale), _ptr(out), dtype_code(out),
+                                     M, N, K, _ptr(ws), nbytes, _stream(dev)))
+    return out

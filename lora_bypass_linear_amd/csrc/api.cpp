@@ -53,6 +53,7 @@ struct Problem {
     int x_dt, w_dt, b_dt, d_dt, u_dt;
     int c_dt, o_dt;
     int r_pad;
+    int m_dt = 0;    // DoRA: the magnitude vector's dtype (a policy operand); 0 otherwise
 };
 
 // Shape and dtype checks shared by the size queries and the forward calls.
@@ -60,7 +61,7 @@ int check_problem(Problem& P) {
     if (P.M < 0 || P.N < 0 || P.K < 0 || P.rank < 0) return LYC_ERR_INVALID_ARG;
     if (!valid_dt(P.x_dt) || !valid_dt(P.w_dt)) return LYC_ERR_INVALID_ARG;
     if (P.b_dt != 0 && !valid_dt(P.b_dt)) return LYC_ERR_INVALID_ARG;
-    int dts[5], n = 0;
+    int dts[6], n = 0;
     dts[n++] = P.x_dt;
     dts[n++] = P.w_dt;
     if (P.b_dt != 0) dts[n++] = P.b_dt;
@@ -68,6 +69,10 @@ int check_problem(Problem& P) {
         if (!valid_dt(P.d_dt) || !valid_dt(P.u_dt)) return LYC_ERR_INVALID_ARG;
         dts[n++] = P.d_dt;
         dts[n++] = P.u_dt;
+    }
+    if (P.m_dt != 0) {
+        if (!P.lora || !valid_dt(P.m_dt)) return LYC_ERR_INVALID_ARG;
+        dts[n++] = P.m_dt;
     }
     const int st = resolve(dts, n, &P.c_dt, &P.o_dt);
     if (st != LYC_OK) return st;
@@ -81,7 +86,7 @@ int check_problem(Problem& P) {
 
 struct Layout {
     size_t xc = 0, wc = 0, dc = 0, dh = 0, dl = 0, uc = 0, h = 0, dnorm = 0, wh = 0, wl = 0, wnorm = 0, flagged = 0,
-           partial = 0, total = 0;
+           partial = 0, gain = 0, total = 0;
     int ksplit = 1, ks_max = 1;
     bool cast_x = false, cast_w = false;
 };
@@ -116,6 +121,8 @@ Layout layout(const Problem& P) {
         for (int i = 0; i < np; ++i) ks_max = std::max(ks_max, plan[i].ksplit);
         L.ks_max = ks_max;
         if (ks_max > 1) { L.partial = off; off = align256(off + (size_t)ks_max * (size_t)(P.M * P.N) * 4); }
+        // DoRA: the per-feature gain m / norm in fp32
+        if (P.m_dt != 0) { L.gain = off; off = align256(off + (size_t)P.N * 4); }
     }
     if (!P.lora) {
         // the projection's rounding guard: hi/lo split and row norms of W_c, a counter
@@ -163,7 +170,7 @@ hipError_t timed(int kind, hipStream_t s, F fn) {
 // else a measured pick for this device and shape, else the analytic one.
 int forward(const Problem& P, const void* x, const void* w, const void* bias, const void* down, const void* up,
             double scale, void* y, int y_dt, void* ws, size_t ws_bytes, void* stream,
-            const lyc::TuneChoice* force = nullptr) {
+            const lyc::TuneChoice* force = nullptr, const void* mag = nullptr, const float* norms = nullptr) {
     if (y_dt != P.o_dt) return LYC_ERR_DTYPE_MISMATCH;
     if ((bias == nullptr) != (P.b_dt == 0)) return LYC_ERR_INVALID_ARG;
     if (P.M == 0 || P.N == 0) return LYC_OK;
@@ -259,6 +266,13 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
         g.ksplit = tc.ksplit;
     }
     g.partial = g.ksplit > 1 ? (float*)(W + L.partial) : nullptr;
+    if (P.m_dt != 0) {
+        float* gain = (float*)(W + L.gain);
+        if (timed(LYC_KERNEL_PREP, s, [&] { return lyc::launch_dora_gain(mag, P.m_dt, norms, P.N, gain, s); }) !=
+            hipSuccess)
+            return LYC_ERR_HIP;
+        g.gain = gain;
+    }
     const uintptr_t vec_align = y_dt == LYC_F32 ? 16 : 8;
     g.vec_store = (P.N % 4 == 0) && aligned(y, vec_align);
 
@@ -851,6 +865,98 @@ int lyc_lora_linear_bwd_workspace_layout(int64_t M, int64_t N, int64_t K, int64_
     if (ld) *ld = B.P.r_pad;
     if (flagged_offset) *flagged_offset = L.need_gh && B.P.c_dt != LYC_F32 ? L.flag_g : (size_t)-1;
     return LYC_OK;
+}
+
+// ---- DoRA -------------------------------------------------------------------------
+
+int lyc_dora_norms_workspace_size(int64_t N, int64_t K, int64_t rank, int w_dt, int down_dt, int up_dt,
+                                  size_t* bytes) {
+    Merge G{N, K, rank, w_dt, down_dt, up_dt, 0, 0, 0, 0, 0, 0};
+    const int st = check_merge(G);
+    if (st != LYC_OK) return st;
+    if (bytes) *bytes = align256(G.total) + align256((size_t)((K + 127) / 128) * (size_t)N * 4);
+    return LYC_OK;
+}
+
+int lyc_dora_norms(const void* w, int w_dt, const void* down, int down_dt, const void* up, int up_dt, int64_t rank,
+                   double scale, float* norms, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+    Merge G{N, K, rank, w_dt, down_dt, up_dt, 0, 0, 0, 0, 0, 0};
+    int st = check_merge(G);
+    if (st != LYC_OK) return st;
+    if (!(scale == scale) || scale > 3.4e38 || scale < -3.4e38) return LYC_ERR_INVALID_ARG;
+    if (N == 0) return LYC_OK;
+    if (norms == nullptr || (K > 0 && w == nullptr)) return LYC_ERR_INVALID_ARG;
+    if (rank > 0 && K > 0 && (down == nullptr || up == nullptr)) return LYC_ERR_INVALID_ARG;
+    if (!aligned(norms, 4) || (w && !aligned(w, esize(w_dt)))) return LYC_ERR_UNSUPPORTED;
+    if (rank > 0 && (!aligned(down, esize(down_dt)) || !aligned(up, esize(up_dt)))) return LYC_ERR_UNSUPPORTED;
+    if (overlaps(norms, (size_t)N * 4, w, (size_t)(N * K) * esize(w_dt))) return LYC_ERR_INVALID_ARG;
+    const size_t part = align256(G.total), need = part + align256((size_t)((K + 127) / 128) * (size_t)N * 4);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))) return LYC_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    char* W = (char*)workspace;
+    (void)hipGetLastError();
+    if (K == 0) {
+        // no columns: every norm is 0 (a transpose of an empty source writes only zeros)
+        lyc::TransposeParams tp{norms, LYC_F32, 0, 0, norms, LYC_F32, N, 1};
+        return lyc::launch_transpose(tp, s) == hipSuccess ? LYC_OK : LYC_ERR_HIP;
+    }
+    if (G.r_pad > 0) {
+        lyc::MergePrepParams mp{};
+        mp.down = down;
+        mp.down_dt = down_dt;
+        mp.up = up;
+        mp.up_dt = up_dt;
+        mp.dt_c = W + G.dt_c;
+        mp.uc = W + G.uc;
+        mp.N = N;
+        mp.K = K;
+        mp.rank = rank;
+        mp.r_pad = G.r_pad;
+        mp.c_dt = G.c_dt;
+        if (timed(LYC_KERNEL_PREP, s, [&] { return lyc::launch_merge_prep(mp, s); }) != hipSuccess) return LYC_ERR_HIP;
+    }
+    lyc::MergeParams mg{};
+    mg.w = w;
+    mg.w_dt = w_dt;
+    mg.dt_c = W + G.dt_c;
+    mg.uc = W + G.uc;
+    mg.out = nullptr;
+    mg.out_dt = G.o_dt;
+    mg.N = N;
+    mg.K = K;
+    mg.r_pad = G.r_pad;
+    mg.scale = (float)scale;
+    const int E = (w_dt == LYC_F32 || G.o_dt == LYC_F32) ? 4 : 8;
+    mg.vec = (K % E == 0) && aligned(w, E * esize(w_dt));
+    mg.norm_partial = (float*)(W + part);
+    mg.norms = norms;
+    if (timed(LYC_KERNEL_GEMM, s, [&] { return lyc::launch_merge(G.c_dt, mg, s); }) != hipSuccess) return LYC_ERR_HIP;
+    return LYC_OK;
+}
+
+int lyc_dora_linear_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt, int bias_dt,
+                                   int down_dt, int up_dt, int m_dt, size_t* bytes) {
+    Problem P{true, M, N, K, rank, x_dt, w_dt, bias_dt, down_dt, up_dt, 0, 0, 0, m_dt == 0 ? -1 : m_dt};
+    const int st = check_problem(P);
+    if (st != LYC_OK) return st;
+    if (bytes) *bytes = layout(P).total;
+    return LYC_OK;
+}
+
+int lyc_dora_linear_fwd(const void* x, int x_dt, const void* w, int w_dt, const void* bias, int bias_dt,
+                        const void* down, int down_dt, const void* up, int up_dt, const void* magnitude, int m_dt,
+                        const float* norms, int64_t rank, double scale, void* y, int y_dt, int64_t M, int64_t N,
+                        int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+    Problem P{true, M, N, K, rank, x_dt, w_dt, bias_dt, down_dt, up_dt, 0, 0, 0, m_dt == 0 ? -1 : m_dt};
+    const int st = check_problem(P);
+    if (st != LYC_OK) return st;
+    if (!valid_dt(y_dt)) return LYC_ERR_INVALID_ARG;
+    if (!(scale == scale) || scale > 3.4e38 || scale < -3.4e38) return LYC_ERR_INVALID_ARG;
+    if (M > 0 && N > 0 && (magnitude == nullptr || norms == nullptr)) return LYC_ERR_INVALID_ARG;
+    if ((magnitude && !aligned(magnitude, esize(m_dt))) || (norms && !aligned(norms, 4))) return LYC_ERR_UNSUPPORTED;
+    return forward(P, x, w, bias, down, up, scale, y, y_dt, workspace, workspace_bytes, stream, nullptr, magnitude,
+                   norms);
 }
 
 int lyc_lora_merge_workspace_size(int64_t N, int64_t K, int64_t rank, int w_dt, int down_dt, int up_dt,

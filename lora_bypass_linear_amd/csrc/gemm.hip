@@ -224,7 +224,9 @@ __device__ __forceinline__ void k_step(const Steps<TL>& S, char* smem, int kt, i
     mma_spread<CT, TL, TL::Q, TL::FN + TL::FM>(f1a, f1b, acc);
 }
 
-template <class CT, class TL>
+// GAIN: a per-output-feature factor gain[n] in place of post (an instance of
+// its own, so the others carry no registers for it)
+template <class CT, class TL, bool GAIN>
 __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles_n, int tiles_m, int group_m) {
     __shared__ __attribute__((aligned(16))) char smem[TL::NS * TL::STAGE];
     constexpr int FN = TL::FN, FM = TL::FM;
@@ -314,7 +316,7 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
         }
         return;
     }
-    //    The bias of every block is loaded before the first store.
+    //    The bias (and a per-feature gain) of every block is loaded before the first store.
     float biasv[FN * 4] = {};
     if (p.bias != nullptr) {
         int64_t idx[FN * 4];
@@ -322,10 +324,18 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
         for (int i = 0; i < FN * 4; ++i) idx[i] = n0 + wn * TL::WN + (i >> 2) * 16 + 4 * (lane >> 4) + (i & 3);
         load_n_as_f32<FN * 4>(p.bias, p.bias_dt, idx, p.N, biasv);
     }
+    float gainv[GAIN ? FN * 4 : 1];
+    if constexpr (GAIN) {
+        int64_t idx[FN * 4];
+#pragma unroll
+        for (int i = 0; i < FN * 4; ++i) idx[i] = n0 + wn * TL::WN + (i >> 2) * 16 + 4 * (lane >> 4) + (i & 3);
+        load_n_as_f32<FN * 4>(p.gain, DT_F32, idx, p.N, gainv);
+    }
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
         const int64_t nb = n0 + wn * TL::WN + i * 16 + 4 * (lane >> 4);
         const float* bias = biasv + 4 * i;
+        const float* gain = gainv + (GAIN ? 4 * i : 0);
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
             const int64_t m = m0 + wm * TL::WM + j * 16 + (lane & 15);
@@ -334,7 +344,7 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float a = acc[i][j][e];
-                v[e] = a * p.post + bias[e];
+                v[e] = a * (GAIN ? gain[e] : p.post) + bias[e];
             }
             const int64_t base = m * p.N + nb;
             if (p.y_dt == DT_F32) {
@@ -363,15 +373,15 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
     }
 }
 
-// y = round_out(post * (sum of the K splits' partial sums, in split order) + b)
+// y = round_out(gain or post * (sum of the K splits' partial sums, in split order) + b)
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmParams p) {
     const int64_t MN = p.M * p.N;
     const int64_t stride = (int64_t)gridDim.x * 256;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < MN; i += stride) {
         float v = p.partial[i];
         for (int k = 1; k < p.ksplit; ++k) v += p.partial[(int64_t)k * MN + i];
-        v *= p.post;
         const int64_t n = i % p.N;
+        v *= p.gain != nullptr ? p.gain[n] : p.post;
         if (p.bias != nullptr) v += load_as_f32(p.bias, p.bias_dt, n);
         if (p.y_dt == DT_F32) ((float*)p.y)[i] = v;
         else ((uint16_t*)p.y)[i] = p.y_dt == DT_F16 ? f32_to_f16(v) : f32_to_bf16(v);
@@ -384,7 +394,11 @@ static hipError_t run(const GemmParams& p, hipStream_t s) {
     const int tiles_m = (int)((p.M + TL::TM - 1) / TL::TM);
     const int nblk = tiles_n * tiles_m;
     const int ks = p.ksplit > 1 ? p.ksplit : 1;
-    hipLaunchKernelGGL((gemm_kernel<CT, TL>), dim3(nblk, ks), dim3(TL::NT), 0, s, p, tiles_n, tiles_m, 4);
+    // (a K split applies the gain in its reduction)
+    if (p.gain != nullptr && ks == 1)
+        hipLaunchKernelGGL((gemm_kernel<CT, TL, true>), dim3(nblk, ks), dim3(TL::NT), 0, s, p, tiles_n, tiles_m, 4);
+    else
+        hipLaunchKernelGGL((gemm_kernel<CT, TL, false>), dim3(nblk, ks), dim3(TL::NT), 0, s, p, tiles_n, tiles_m, 4);
     if (ks > 1) {
         const int64_t blocks = (p.M * p.N + 255) / 256;
         hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, p);

@@ -38,6 +38,9 @@ struct GemmParams {
     float post = 1.0f;
     // output tile: GEMM_TILE_AUTO (the analytic pick) or one of GEMM_TILE_*
     int tile = GEMM_TILE_AUTO;
+    // per output feature n: y = round_out(gain[n] * acc + b) in place of post
+    // (the DoRA forward's m_n / norm_n; nullptr: none)
+    const float* gain = nullptr;
 };
 
 struct GemmCand {

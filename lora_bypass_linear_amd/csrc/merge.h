@@ -35,7 +35,13 @@ struct MergeParams {
     float scale;
     int vec;            // K a multiple of the lane chunk (8 elements when W and W' are 16-bit, else 4)
                         // and W, W' aligned to one chunk: 16-byte (8-byte for 16-bit W under fp32 W') accesses
+    // DoRA row norms instead of W' (norm_partial != nullptr): per-tile sums of
+    // squares [K tiles][N] fp32, then norms[n] = sqrt of their sum in tile order
+    float* norm_partial = nullptr;
+    float* norms = nullptr;
 };
 hipError_t launch_merge(int c_dt, const MergeParams& p, hipStream_t s);
+// gain[n] = m[n] / norms[n] in fp32 (the DoRA forward's per-feature factor)
+hipError_t launch_dora_gain(const void* m, int m_dt, const float* norms, int64_t N, float* gain, hipStream_t s);
 
 }  // namespace lyc

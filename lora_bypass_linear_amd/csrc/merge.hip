@@ -76,7 +76,10 @@ __device__ __forceinline__ void merge_chunk_mma(char* smem, const i32x4 (&st)[8]
     }
 }
 
-template <class CT, bool WF, bool OF, bool VEC>
+// NORM: instead of storing W', each tile adds up v^2 over its columns for
+// every row and writes that partial sum to norm_partial[tile column][n] (the
+// DoRA row norms of the merged weight, which is never stored).
+template <class CT, bool WF, bool OF, bool VEC, bool NORM>
 __global__ __launch_bounds__(256, (WF || !VEC) ? 2 : 3) void merge_kernel(MergeParams p, int tiles_k) {
     __shared__ __attribute__((aligned(16))) char smem[LDS];
     // a thread's share of the tile: E consecutive elements of one row per pass
@@ -201,6 +204,21 @@ __global__ __launch_bounds__(256, (WF || !VEC) ? 2 : 3) void merge_kernel(MergeP
             }
             v[e] = __builtin_fmaf(p.scale, a[e], w);
         }
+        const int64_t n = n0 + rl;
+        if constexpr (NORM) {
+            // squares of this lane's in-range elements, then the sum over the
+            // CPR lanes of the row (a fixed butterfly: deterministic)
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const bool in = n < p.N && k0 + pcol + e < p.K;
+                ss = __builtin_fmaf(in ? v[e] : 0.f, in ? v[e] : 0.f, ss);
+            }
+#pragma unroll
+            for (int o = CPR / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+            if (tid % CPR == 0 && n < p.N) p.norm_partial[(int64_t)(l % tiles_k) * p.N + n] = ss;
+            continue;
+        }
         uint32_t o[E * OES / 4];
         if constexpr (OF) {
 #pragma unroll
@@ -210,7 +228,6 @@ __global__ __launch_bounds__(256, (WF || !VEC) ? 2 : 3) void merge_kernel(MergeP
             for (int t = 0; t < E / 2; ++t)
                 o[t] = CT::dt == DT_F16 ? pack_f16x2(v[2 * t], v[2 * t + 1]) : pack_bf16x2(v[2 * t], v[2 * t + 1]);
         }
-        const int64_t n = n0 + rl;
         if constexpr (VEC) {
             if (n < p.N && k0 + pcol < p.K)
                 __builtin_nontemporal_store(i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]}, (i32x4*)((char*)p.out + (n * p.K + k0 + pcol) * OES));
@@ -225,6 +242,29 @@ __global__ __launch_bounds__(256, (WF || !VEC) ? 2 : 3) void merge_kernel(MergeP
         }
     }
     }
+}
+
+// DoRA row norms: the tiles' partial sums of squares of each row, added in
+// tile order, then the square root (fp32)
+__global__ __launch_bounds__(256) void norm_finish_kernel(const float* partial, int tiles_k, int64_t N, float* norms) {
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (n >= N) return;
+    float s = 0.f;
+    for (int t = 0; t < tiles_k; ++t) s += partial[(int64_t)t * N + n];
+    norms[n] = (float)__builtin_sqrt((double)s);
+}
+
+// DoRA gain g_n = m_n / norm_n (fp32)
+__global__ __launch_bounds__(256) void dora_gain_kernel(const void* m, int m_dt, const float* norms, int64_t N,
+                                                        float* gain) {
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (n < N) gain[n] = load_as_f32(m, m_dt, n) / norms[n];
+}
+
+hipError_t launch_dora_gain(const void* m, int m_dt, const float* norms, int64_t N, float* gain, hipStream_t s) {
+    if (N <= 0) return hipSuccess;
+    hipLaunchKernelGGL(dora_gain_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, m, m_dt, norms, N, gain);
+    return hipGetLastError();
 }
 
 // down [rank][K] -> down^T_c [K][r_pad] (rounded to the compute dtype, zero
@@ -294,8 +334,17 @@ template <class CT, bool WF, bool OF>
 static hipError_t run_merge(const MergeParams& p, hipStream_t s) {
     const int tiles_n = (int)((p.N + MT - 1) / MT), tiles_k = (int)((p.K + MC - 1) / MC);
     const dim3 g((unsigned)(tiles_n * tiles_k));
-    if (p.vec) hipLaunchKernelGGL((merge_kernel<CT, WF, OF, true>), g, dim3(256), 0, s, p, tiles_k);
-    else hipLaunchKernelGGL((merge_kernel<CT, WF, OF, false>), g, dim3(256), 0, s, p, tiles_k);
+    if (p.norm_partial != nullptr) {
+        if (p.vec) hipLaunchKernelGGL((merge_kernel<CT, WF, OF, true, true>), g, dim3(256), 0, s, p, tiles_k);
+        else hipLaunchKernelGGL((merge_kernel<CT, WF, OF, false, true>), g, dim3(256), 0, s, p, tiles_k);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+        const int64_t blocks = (p.N + 255) / 256;
+        hipLaunchKernelGGL(norm_finish_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p.norm_partial, tiles_k, p.N,
+                           p.norms);
+        return hipGetLastError();
+    }
+    if (p.vec) hipLaunchKernelGGL((merge_kernel<CT, WF, OF, true, false>), g, dim3(256), 0, s, p, tiles_k);
+    else hipLaunchKernelGGL((merge_kernel<CT, WF, OF, false, false>), g, dim3(256), 0, s, p, tiles_k);
     return hipGetLastError();
 }
 

@@ -237,3 +237,32 @@ def test_backward_workspace_sizes():
     assert ho % 256 == 0 and fo == 2 ** 64 - 1                    # fp32 compute: no guard
     with pytest.raises(L.MixedHalfError):
         L.lora_bwd_workspace_size(8, 8, 8, 2, 1, 1, 0, 1, 1, 2, 7)
+
+
+def test_dora_argument_errors():
+    lib = L.lib()
+    n = ctypes.c_size_t(0)
+    assert lib.lyc_dora_norms_workspace_size(64, 64, 4, 1, 1, 1, ctypes.byref(n)) == L.OK and n.value > 0
+    assert lib.lyc_dora_norms_workspace_size(64, 64, 4, 1, 2, 1, ctypes.byref(n)) == L.ERR_MIXED_HALF
+    args = lambda **kw: {**dict(w=P, w_dt=1, d=P, d_dt=1, u=P, u_dt=1, r=4, s=ctypes.c_double(1.0),
+                                o=V(1 << 30), N=64, K=64, ws=None, nws=0, st=None), **kw}
+    call = lambda a: _refused(lib.lyc_dora_norms(a["w"], a["w_dt"], a["d"], a["d_dt"], a["u"], a["u_dt"], a["r"],
+                                                 a["s"], a["o"], a["N"], a["K"], a["ws"], a["nws"], a["st"]))
+    assert call(args()) == L.ERR_WORKSPACE
+    assert call(args(o=None)) == L.ERR_INVALID_ARG
+    assert call(args(o=V(4096 + 64))) == L.ERR_INVALID_ARG           # norms overlap W
+    assert call(args(r=300)) == L.ERR_UNSUPPORTED
+    assert call(args(s=ctypes.c_double(float("inf")))) == L.ERR_INVALID_ARG
+    # the forward: the magnitude's dtype is a policy operand and is required
+    assert lib.lyc_dora_linear_workspace_size(8, 8, 8, 2, 1, 1, 0, 1, 1, 2, ctypes.byref(n)) == L.ERR_MIXED_HALF
+    assert lib.lyc_dora_linear_workspace_size(8, 8, 8, 2, 1, 1, 0, 1, 1, 0, ctypes.byref(n)) == L.ERR_INVALID_ARG
+    base = L.lora_workspace_size(8, 8, 8, 2, 1, 1, 0, 1, 1)
+    assert lib.lyc_dora_linear_workspace_size(8, 8, 8, 2, 1, 1, 0, 1, 1, 1, ctypes.byref(n)) == L.OK
+    assert n.value >= base + 8 * 4                                     # plus the gain vector
+    f = lambda **kw: _refused(lib.lyc_dora_linear_fwd(
+        P, 1, P, 1, None, 0, P, 1, P, 1, kw.get("m", P), 1, kw.get("nm", P), 2, ctypes.c_double(1.0),
+        V(1 << 30), kw.get("y_dt", 1), 8, 8, 8, None, 0, None))
+    assert f(m=None) == L.ERR_INVALID_ARG and f(nm=None) == L.ERR_INVALID_ARG
+    assert f(y_dt=3) == L.ERR_DTYPE_MISMATCH
+    assert f(nm=V(4098)) == L.ERR_UNSUPPORTED
+    assert f() == L.ERR_WORKSPACE

@@ -31,7 +31,7 @@ NAME = {F16: "f16", BF16: "bf16", F32: "f32"}
 BYTES = {F16: 2, BF16: 2, F32: 4}
 
 # tensor ids used to key the per-tensor Philox streams
-_TID = {"x": 1, "w": 2, "b": 3, "down": 4, "up": 5, "rowscale": 6, "dy": 7}
+_TID = {"x": 1, "w": 2, "b": 3, "down": 4, "up": 5, "rowscale": 6, "dy": 7, "magnitude": 8}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -163,6 +163,13 @@ def generate_dy(w: Workload, dt: int, std: float = 1.0) -> torch.Tensor:
     """The upstream gradient dy [M,N] for the backward: N(0, std^2) in dtype dt
     (the forward's output dtype), from its own Philox stream."""
     return _draw(w.seed, "dy", (w.M, w.N), std, dt)
+
+
+def generate_magnitude(w: Workload) -> torch.Tensor:
+    """A DoRA magnitude vector m [N]: N(1, 0.1^2) in the module weights' dtype
+    (the row norms of a 1/fan_in-initialised W are close to 1)."""
+    a = 1.0 + 0.1 * _stream(w.seed, "magnitude").standard_normal(w.N)
+    return torch.from_numpy(a.astype(np.float32)).to(TORCH_DTYPE[w.w_dt]).contiguous()
 
 
 def raw_bits(t: torch.Tensor) -> np.ndarray:
