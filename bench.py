@@ -51,6 +51,9 @@ def main():
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the backward of the workload (profiling runs)")
     ap.add_argument("--backward-steps", type=int, default=50)
+    ap.add_argument("--no-dora", action="store_true", help="skip the DoRA timing")
+    ap.add_argument("--dora-only", action="store_true", help="time only DoRA's norms and forward (profiling runs)")
+    ap.add_argument("--dora-steps", type=int, default=100)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (HBM counter calibration)")
     args = ap.parse_args()
@@ -86,6 +89,13 @@ def main():
             _copy_calibration(dev, args.copy_calibration_mib)
         print(json.dumps({"workload": wl.name, "merge": _merge(dev, wl, inputs, args.merge_steps, args.merge_steps,
                                                                  not args.no_cpu_baseline)}))
+        return
+
+    if args.dora_only:
+        if args.copy_calibration_mib > 0:
+            _copy_calibration(dev, args.copy_calibration_mib)
+        print(json.dumps({"workload": wl.name, "dora": _dora(dev, wl, inputs, args.dora_steps, args.dora_steps,
+                                                               not args.no_cpu_baseline)}))
         return
 
     if args.backward_only:
@@ -175,6 +185,8 @@ def main():
         out["small_m"] = _small_m(dev)
     if lora and wl.r > 0 and not args.no_merge:
         out["merge"] = _merge(dev, wl, inputs, args.merge_steps, 20, not args.no_cpu_baseline)
+    if lora and wl.r > 0 and not args.no_dora:
+        out["dora"] = _dora(dev, wl, inputs, args.dora_steps, 20, not args.no_cpu_baseline)
     if lora and wl.r > 0 and not args.no_backward:
         out["backward"] = _backward(dev, wl, inputs, args.backward_steps, 20, not args.no_cpu_baseline,
                                     not args.no_eager)
@@ -305,6 +317,78 @@ def _merge(dev, wl, inputs, reps, warm, accuracy):
                   "eager": {"max_ulp": round(se["ulp_max"], 4), "rms_ulp": round(se["ulp_rms"], 4),
                             "tol_fail": se["fail"]}})
     return r
+
+
+def _dora(dev, wl, inputs, reps, warm, accuracy):
+    """DoRA: the row norms of the merged weight (device time, HBM bytes of W,
+    down and up read and the norms written, against 8 TB/s) and the DoRA
+    forward beside the plain LoRA forward of the same shape (the gain's
+    cost), with ULP against the fp64 oracle on sampled rows."""
+    import numpy as np
+    import torch
+
+    import lora_bypass_linear_amd as L
+    import workloads as WL
+
+    d = {k: v.to(dev) for k, v in inputs.items()}
+    mag = WL.generate_magnitude(wl)
+    m = mag.to(dev)
+    norms = torch.empty(wl.N, dtype=torch.float32, device=dev)
+    print(f"[bench] dora {wl.name}: {warm} + {reps} calls", file=sys.stderr, flush=True)
+
+    def timed_calls(fn):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e6 / reps
+        L.profile_begin(8 * reps)
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return wall, L.profile_end()
+
+    nfn = lambda: L.dora_norms(d["w"], d["down"], d["up"], wl.scale, out=norms)
+    wall_n, prof_n = timed_calls(nfn)
+    es = {L.F16: 2, L.BF16: 2, L.F32: 4}
+    w_dt, d_dt, u_dt = (L.dtype_code(d[k]) for k in ("w", "down", "up"))
+    nbytes = wl.N * wl.K * es[w_dt] + wl.r * wl.K * es[d_dt] + wl.N * wl.r * es[u_dt] + wl.N * 4
+    n_g, t_g = prof_n["gemm"]
+    g_us = t_g * 1e3 / max(n_g, 1)
+    y = L.dora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, m, norms, d.get("b"))
+    wall_f, prof_f = timed_calls(lambda: L.dora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, m, norms,
+                                                       d.get("b"), out=y))
+    yl = L.lora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, d.get("b"))
+    wall_l, prof_l = timed_calls(lambda: L.lora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, d.get("b"),
+                                                       out=yl))
+    dev_us = lambda prof: round(sum(ms for _, ms in prof.values()) * 1e3 / reps, 2)
+    out = {"shape": f"M {wl.M}, N {wl.N}, K {wl.K}, rank {wl.r}, magnitude {WL.NAME[L.dtype_code(m)]}",
+           "norms": {"wall_us_per_call": round(wall_n, 2), "device_us_per_call": dev_us(prof_n),
+                     "roofline": {"bound": "hbm", "kernel": "merge_kernel (row norms)",
+                                  "achieved": round(nbytes / (g_us * 1e-6) / 1e9, 1), "peak": HBM_GBS,
+                                  "unit": "GB/s", "frac": round(nbytes / (g_us * 1e-6) / 1e9 / HBM_GBS, 4),
+                                  "traffic": None, "bytes_per_launch": nbytes, "avg_us": round(g_us, 3)}},
+           "forward": {"wall_us_per_call": round(wall_f, 2), "device_us_per_call": dev_us(prof_f),
+                       "tflops": round(wl.flops / (dev_us(prof_f) * 1e-6) / 1e12, 2),
+                       "lora_forward_device_us": dev_us(prof_l)}}
+    if accuracy:
+        import oracle
+        from tests.gpu_cases import sample_rows, score
+        rows = sample_rows(wl.M, 24, seed=wl.seed)
+        bits = {k: WL.raw_bits(v) for k, v in inputs.items()}
+        dt = {k: WL.dtype_code(v) for k, v in inputs.items()}
+        res = oracle.dora_forward(bits["x"], dt["x"], bits["w"], dt["w"], bits.get("b"), dt.get("b"), bits["down"],
+                                  dt["down"], bits["up"], dt["up"], WL.raw_bits(mag), WL.dtype_code(mag),
+                                  scale=wl.scale, rows=rows)
+        sc = score(y.cpu(), res, rows, wl.K, wl.r)
+        nrel = np.abs(norms.cpu().numpy().astype(np.float64) - res["norms"].astype(np.float64)) / res["norms"]
+        out["forward"].update({"max_ulp": round(sc["ulp_max"], 4), "rms_ulp": round(sc["ulp_rms"], 4),
+                               "tol_fail": sc["fail"], "rows_checked": int(len(rows))})
+        out["norms"]["max_rel_err_vs_oracle"] = float(nrel.max())
+    return out
 
 
 def _backward(dev, wl, inputs, reps, warm, accuracy, eager):

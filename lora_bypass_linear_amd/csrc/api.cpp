@@ -932,6 +932,7 @@ int lyc_dora_norms(const void* w, int w_dt, const void* down, int down_dt, const
     mg.norm_partial = (float*)(W + part);
     mg.norms = norms;
     if (timed(LYC_KERNEL_GEMM, s, [&] { return lyc::launch_merge(G.c_dt, mg, s); }) != hipSuccess) return LYC_ERR_HIP;
+    if (timed(LYC_KERNEL_PREP, s, [&] { return lyc::launch_norm_finish(mg, s); }) != hipSuccess) return LYC_ERR_HIP;
     return LYC_OK;
 }
 

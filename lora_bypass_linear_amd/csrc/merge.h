@@ -41,6 +41,8 @@ struct MergeParams {
     float* norms = nullptr;
 };
 hipError_t launch_merge(int c_dt, const MergeParams& p, hipStream_t s);
+// after launch_merge in the norm mode: norms[n] = sqrt(sum of the tiles' partials, in tile order)
+hipError_t launch_norm_finish(const MergeParams& p, hipStream_t s);
 // gain[n] = m[n] / norms[n] in fp32 (the DoRA forward's per-feature factor)
 hipError_t launch_dora_gain(const void* m, int m_dt, const float* norms, int64_t N, float* gain, hipStream_t s);
 

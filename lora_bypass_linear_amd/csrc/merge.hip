@@ -249,9 +249,24 @@ __global__ __launch_bounds__(256, (WF || !VEC) ? 2 : 3) void merge_kernel(MergeP
 __global__ __launch_bounds__(256) void norm_finish_kernel(const float* partial, int tiles_k, int64_t N, float* norms) {
     const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (n >= N) return;
+    // 16 loads in flight at a time, the adds still in tile order
     float s = 0.f;
-    for (int t = 0; t < tiles_k; ++t) s += partial[(int64_t)t * N + n];
+    for (int t0 = 0; t0 < tiles_k; t0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = partial[(int64_t)(t0 + i < tiles_k ? t0 + i : 0) * N + n];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s += t0 + i < tiles_k ? v[i] : 0.f;
+    }
     norms[n] = (float)__builtin_sqrt((double)s);
+}
+
+hipError_t launch_norm_finish(const MergeParams& p, hipStream_t s) {
+    if (p.N <= 0) return hipSuccess;
+    const int tiles_k = (int)((p.K + MC - 1) / MC);
+    hipLaunchKernelGGL(norm_finish_kernel, dim3((unsigned)((p.N + 255) / 256)), dim3(256), 0, s, p.norm_partial,
+                       tiles_k, p.N, p.norms);
+    return hipGetLastError();
 }
 
 // DoRA gain g_n = m_n / norm_n (fp32)
@@ -337,10 +352,6 @@ static hipError_t run_merge(const MergeParams& p, hipStream_t s) {
     if (p.norm_partial != nullptr) {
         if (p.vec) hipLaunchKernelGGL((merge_kernel<CT, WF, OF, true, true>), g, dim3(256), 0, s, p, tiles_k);
         else hipLaunchKernelGGL((merge_kernel<CT, WF, OF, false, true>), g, dim3(256), 0, s, p, tiles_k);
-        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-        const int64_t blocks = (p.N + 255) / 256;
-        hipLaunchKernelGGL(norm_finish_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p.norm_partial, tiles_k, p.N,
-                           p.norms);
         return hipGetLastError();
     }
     if (p.vec) hipLaunchKernelGGL((merge_kernel<CT, WF, OF, true, false>), g, dim3(256), 0, s, p, tiles_k);
