@@ -207,8 +207,11 @@ int lyc_lora_merge_fwd(const void* w, int w_dt, const void* down, int down_dt, c
  *    element alignment.  M == 0 gives zero dDown and dUp.
  *  - The workspace (256-byte aligned) holds h_r, gh_r, the guard's splits and
  *    norms, compute-dtype copies of fp32 x/dy, and transposed compute-dtype
- *    copies of W, down, up, x, dy, h_r and gh_r (the token contractions read
- *    both operands along the token index); its size comes from
+ *    copies of W and down (for dx).  Under 16-bit compute the token
+ *    contractions (dDown, dUp) read x, dy, h_r and gh_r as stored, the token
+ *    index as their contraction rows (each of them below 1 GiB); under fp32
+ *    compute (or larger operands) transposed copies of those are made in the
+ *    workspace too.  Its size comes from
  *    lyc_lora_linear_bwd_workspace_size with `want` = 1 (dx) | 2 (dDown) |
  *    4 (dUp), the set of non-NULL outputs of the call.
  * Same stream, ownership and error conventions as the forward.

@@ -415,6 +415,10 @@ struct BwdLayout {
     size_t xc = 0, gc = 0, dc = 0, dh = 0, dl = 0, uc = 0, dnorm = 0, flag_h = 0, h = 0, ut = 0, uth = 0, utl = 0,
            unorm = 0, flag_g = 0, gh = 0, wt = 0, dt = 0, xt = 0, ght = 0, dyt = 0, ht = 0, partial = 0, total = 0;
     bool cast_x = false, cast_g = false, need_h = false, need_gh = false;
+    // tr_tok: dDown and dUp read x, dy, h_r and gh_r as stored, the token
+    // index as their contraction rows (16-bit compute, each operand below
+    // 1 GiB); else they read transposed copies.  dx reads W^T and down^T copies.
+    bool tr_tok = false, need_prep = false;
     int ks_dx = 1, ks_dd = 1, ks_du = 1;
 };
 
@@ -443,6 +447,21 @@ int check_bwd(Bwd& B) {
     return LYC_OK;
 }
 
+// K split of a token contraction read in place (dDown, dUp): the token
+// count against few output tiles; about two workgroups per compute unit (512),
+// at least 4 K steps each, at most 8 splits
+int tok_ksplit(int64_t M, int64_t N, int64_t K, int c_dt) {
+    int tn, tm;
+    lyc::gemm_tile_shape(M, N, c_dt, &tn, &tm);
+    const int64_t tiles = ((N + tn - 1) / tn) * ((M + tm - 1) / tm);
+    const int64_t ksteps = (K * 2 + 127) / 128;
+    if (tiles == 0) return 1;
+    int64_t ks = (512 + tiles - 1) / tiles;
+    if (ks > ksteps / 4) ks = ksteps / 4;
+    if (ks > 8) ks = 8;
+    return ks > 1 ? (int)ks : 1;
+}
+
 BwdLayout bwd_layout(const Bwd& B) {
     const Problem& P = B.P;
     BwdLayout L;
@@ -452,20 +471,23 @@ BwdLayout bwd_layout(const Bwd& B) {
     const bool dx = B.want & BWD_DX, dd = (B.want & BWD_DDOWN) && P.rank > 0, du = (B.want & BWD_DUP) && P.rank > 0;
     L.need_h = du;                          // h_r feeds dUp only
     L.need_gh = P.rank > 0 && (dx || dd);   // gh_r feeds dx's fold and dDown
-    L.cast_x = P.x_dt == LYC_F32 && P.c_dt != LYC_F32 && L.need_h;
-    L.cast_g = B.dy_dt == LYC_F32 && P.c_dt != LYC_F32 && (L.need_gh || dx);
+    const size_t G1 = (size_t)1 << 30;
+    L.tr_tok = split && (size_t)P.M * (size_t)P.K * 2 < G1 && (size_t)P.M * (size_t)P.N * 2 < G1;
+    L.need_prep = L.need_h;
+    L.cast_x = P.x_dt == LYC_F32 && P.c_dt != LYC_F32 && (L.need_h || (L.tr_tok && dd));
+    L.cast_g = B.dy_dt == LYC_F32 && P.c_dt != LYC_F32 && (L.need_gh || dx || (L.tr_tok && du));
     auto take = [&](size_t& at, size_t bytes) { at = off; off = align256(off + bytes); };
     const size_t M = (size_t)P.M, N = (size_t)P.N, K = (size_t)P.K, R = (size_t)P.r_pad, M8 = (size_t)B.M8;
     if (L.cast_x) take(L.xc, M * K * 2);
     if (L.cast_g) take(L.gc, M * N * 2);
-    if (L.need_h) {
+    if (L.need_prep) {
         take(L.dc, R * K * ce);
         if (split) { take(L.dh, R * K * ce); take(L.dl, R * K * ce); }
         take(L.uc, N * R * ce);
         take(L.dnorm, R * 2 * sizeof(double));
         take(L.flag_h, sizeof(unsigned));
-        take(L.h, M * R * ce);
     }
+    if (L.need_h) take(L.h, M * R * ce);
     if (L.need_gh) {
         take(L.ut, R * N * ce);
         if (split) { take(L.uth, R * N * ce); take(L.utl, R * N * ce); }
@@ -474,6 +496,7 @@ BwdLayout bwd_layout(const Bwd& B) {
         take(L.gh, M * R * ce);
     }
     size_t part = 0;
+    const int64_t Kt = L.tr_tok ? P.M : B.M8;   // contraction length of the token GEMMs
     if (dx) {
         take(L.wt, K * N * ce);
         if (P.rank > 0) take(L.dt, K * R * ce);
@@ -481,15 +504,19 @@ BwdLayout bwd_layout(const Bwd& B) {
         if (L.ks_dx > 1) part = std::max(part, (size_t)L.ks_dx * M * K * 4);
     }
     if (dd) {
-        take(L.xt, K * M8 * ce);
-        take(L.ght, R * M8 * ce);
-        L.ks_dd = lyc::gemm_ksplit(P.rank, P.K, B.M8, P.c_dt);
+        if (!L.tr_tok) {
+            take(L.xt, K * M8 * ce);
+            take(L.ght, R * M8 * ce);
+        }
+        L.ks_dd = L.tr_tok ? tok_ksplit(P.rank, P.K, Kt, P.c_dt) : lyc::gemm_ksplit(P.rank, P.K, Kt, P.c_dt);
         if (L.ks_dd > 1) part = std::max(part, (size_t)L.ks_dd * (size_t)P.rank * K * 4);
     }
     if (du) {
-        take(L.dyt, N * M8 * ce);
-        take(L.ht, R * M8 * ce);
-        L.ks_du = lyc::gemm_ksplit(P.N, P.rank, B.M8, P.c_dt);
+        if (!L.tr_tok) {
+            take(L.dyt, N * M8 * ce);
+            take(L.ht, R * M8 * ce);
+        }
+        L.ks_du = L.tr_tok ? tok_ksplit(P.N, P.rank, Kt, P.c_dt) : lyc::gemm_ksplit(P.N, P.rank, Kt, P.c_dt);
         if (L.ks_du > 1) part = std::max(part, (size_t)L.ks_du * N * (size_t)P.rank * 4);
     }
     if (part > 0) take(L.partial, part);
@@ -576,7 +603,7 @@ int backward(const Bwd& B, const void* x, const void* w, const void* down, const
     }
 
     // h_r, recomputed exactly as the forward computes it (only dUp reads it)
-    if (L.need_h && M > 0) {
+    if (L.need_prep && M > 0) {
         lyc::PrepParams pp{};
         pp.down = down;
         pp.down_dt = P.d_dt;
@@ -595,6 +622,8 @@ int backward(const Bwd& B, const void* x, const void* w, const void* down, const
         pp.c_dt = P.c_dt;
         pp.vec = aligned(down, 16) ? 1 : 0;
         if (timed(LYC_KERNEL_PREP, s, [&] { return lyc::launch_prep(pp, s); }) != hipSuccess) return LYC_ERR_HIP;
+    }
+    if (L.need_h && M > 0) {
         lyc::XrParams hp{};
         hp.x = xa;
         hp.b = W + (split ? L.dh : L.dc);
@@ -644,15 +673,15 @@ int backward(const Bwd& B, const void* x, const void* w, const void* down, const
 
     // dx = round_x(dy_c . W_c + gh_r . down_c): the forward's GEMM with W^T, the fold over down^T
     if (wdx && M > 0 && K > 0) {
+        lyc::GemmParams g{};
         if (N > 0 && !transpose(w, P.w_dt, N, K, W + L.wt, N, K)) return LYC_ERR_HIP;
         if (r > 0 && !transpose(down, P.d_dt, r, K, W + L.dt, P.r_pad, K)) return LYC_ERR_HIP;
-        lyc::GemmParams g{};
         g.a = W + L.wt;
+        g.af = r > 0 ? (const void*)(W + L.dt) : nullptr;
         g.b = ga;
         g.M = M;
         g.N = K;
         g.K = N;
-        g.af = r > 0 ? (const void*)(W + L.dt) : nullptr;
         g.bf = r > 0 ? (const void*)(W + L.gh) : nullptr;
         g.rf = r > 0 ? P.r_pad : 0;
         g.scale = 1.0f;
@@ -667,16 +696,26 @@ int backward(const Bwd& B, const void* x, const void* w, const void* down, const
 
     // dDown = round_down(gh_r^T . x_c), over the tokens
     if (wdd && r > 0 && K > 0) {
-        if (M > 0) {
-            if (!transpose(x, P.x_dt, M, K, W + L.xt, B.M8, K)) return LYC_ERR_HIP;
-            if (!transpose(W + L.gh, P.c_dt, M, P.r_pad, W + L.ght, B.M8, P.r_pad)) return LYC_ERR_HIP;
-        }
         lyc::GemmParams g{};
-        g.a = W + L.xt;
-        g.b = W + L.ght;
+        if (L.tr_tok) {
+            // x_c [M][K] and gh_r [M][r_pad] as stored: tokens are their rows
+            g.a = M > 0 ? xa : W;
+            g.b = W + L.gh;
+            g.ta = g.tb = 1;
+            g.lda_t = K;
+            g.ldb_t = P.r_pad;
+            g.K = M;
+        } else {
+            if (M > 0) {
+                if (!transpose(x, P.x_dt, M, K, W + L.xt, B.M8, K)) return LYC_ERR_HIP;
+                if (!transpose(W + L.gh, P.c_dt, M, P.r_pad, W + L.ght, B.M8, P.r_pad)) return LYC_ERR_HIP;
+            }
+            g.a = W + L.xt;
+            g.b = W + L.ght;
+            g.K = B.M8;
+        }
         g.M = r;
         g.N = K;
-        g.K = B.M8;
         g.rf = 0;
         g.scale = 1.0f;
         g.post = 1.0f;
@@ -690,16 +729,26 @@ int backward(const Bwd& B, const void* x, const void* w, const void* down, const
 
     // dUp = round_up(scale * dy_c^T . h_r), over the tokens
     if (wdu && r > 0 && N > 0) {
-        if (M > 0) {
-            if (!transpose(dy, B.dy_dt, M, N, W + L.dyt, B.M8, N)) return LYC_ERR_HIP;
-            if (!transpose(W + L.h, P.c_dt, M, P.r_pad, W + L.ht, B.M8, P.r_pad)) return LYC_ERR_HIP;
-        }
         lyc::GemmParams g{};
-        g.a = W + L.ht;
-        g.b = W + L.dyt;
+        if (L.tr_tok) {
+            // h_r [M][r_pad] and dy_c [M][N] as stored: tokens are their rows
+            g.a = W + L.h;
+            g.b = M > 0 ? ga : W;
+            g.ta = g.tb = 1;
+            g.lda_t = P.r_pad;
+            g.ldb_t = N;
+            g.K = M;
+        } else {
+            if (M > 0) {
+                if (!transpose(dy, B.dy_dt, M, N, W + L.dyt, B.M8, N)) return LYC_ERR_HIP;
+                if (!transpose(W + L.h, P.c_dt, M, P.r_pad, W + L.ht, B.M8, P.r_pad)) return LYC_ERR_HIP;
+            }
+            g.a = W + L.ht;
+            g.b = W + L.dyt;
+            g.K = B.M8;
+        }
         g.M = N;
         g.N = r;
-        g.K = B.M8;
         g.rf = 0;
         g.scale = 1.0f;
         g.post = (float)scale;

@@ -111,17 +111,18 @@ struct Loader {
     // rows past a tile's valid rows read zeros through the buffer range check
     // (the row offset is in the range-checked vector offset), and in the last,
     // ragged step the chunks past the row end are sent out of range too
+    template <bool DO_A = true, bool DO_B = true>
     __device__ __forceinline__ void issue(char* stage, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                           uint32_t row_bytes, uint32_t kb0, int wave, int lane) const {
         const bool ok = kb0 + TL::BKB <= row_bytes || kb0 + chunk16(lane) < row_bytes;
 #pragma unroll
-        for (int q = 0; q < QA; ++q) {
+        for (int q = 0; q < (DO_A ? QA : 0); ++q) {
             const uint32_t v = ok ? va + (uint32_t)q * sa : OOB;
             auto* dst = (__attribute__((address_space(3))) void*)(stage + (wave + q * TL::NW) * 1024);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, v, (int)kb0, 0, 0);
         }
 #pragma unroll
-        for (int q = 0; q < QB; ++q) {
+        for (int q = 0; q < (DO_B ? QB : 0); ++q) {
             const uint32_t v = ok ? vb + (uint32_t)q * sb : OOB;
             auto* dst = (__attribute__((address_space(3))) void*)(stage + (wave + (QA + q) * TL::NW) * 1024);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, v, (int)kb0, 0, 0);
@@ -129,17 +130,81 @@ struct Loader {
     }
 };
 
+// An operand stored with the contraction index as rows ([contraction][ld],
+// 16-bit; x, dy and W in the backward): a K step is 64 contraction rows of
+// Chunk permutation of a transposed tile's row r (CPR 16-byte chunks a row):
+// 32-byte pairs of chunks move by a row-dependent amount so that the rows one
+// half-wave's transposing read touches (r = 0..3 and 8..11 of a group of 16,
+// or 4..7 and 12..15) fall on distinct banks.  Rows of 256 bytes or more
+// start on the same bank, so the pair index takes bits 0, 1 and 3 of r; rows
+// of 128 bytes alternate halves of the banks, so it takes bits 1 and 3.
+template <int CPR>
+__device__ __forceinline__ int tswz(int r) {
+    static_assert(CPR >= 8, "transposed tile rows of 128 bytes or more");
+    if constexpr (CPR >= 16) return 2 * ((r & 3) | ((r >> 1) & 4));
+    else return 2 * (((r >> 1) & 1) | ((r >> 2) & 2));
+}
+
+// ROWS consecutive columns, kept in LDS in that orientation (rows of ROWS*2
+// bytes, 16-byte slot s of row r holding chunk s ^ tswz(r)) and turned into
+// MFMA fragments by the transposing LDS read.  A wave load still fills 1 KiB
+// (KRB whole rows), and a side still takes ROWS/8 of them per step.  The step
+// advance is in the per-lane offset (rows past the matrix fall outside the
+// buffer range); lanes whose columns lie past the stored row read nothing.
+template <class TL, int ROWS>
+struct LoaderT {
+    static constexpr int CPR = ROWS / 8;                 // 16-byte chunks per LDS row
+    static constexpr int KRB = 64 / CPR;                 // contraction rows per 1 KiB wave load
+    uint32_t off;    // lane's byte offset in its first block at step 0 (OOB: nothing to read)
+    uint32_t sa;     // byte stride between a wave's consecutive blocks
+    uint32_t step;   // bytes per K step (64 rows)
+    __device__ __forceinline__ void init(int64_t col0, int64_t ld, int wave, int lane) {
+        // (a wave's later blocks start 16 rows on: the same permutation)
+        static_assert(CPR * KRB == 64 && (TL::NW * KRB) % 16 == 0, "transposed tile");
+        const int r = wave * KRB + lane / CPR;               // contraction row within the step
+        const int64_t col = col0 + 8 * ((lane % CPR) ^ tswz<CPR>(r));
+        off = col < ld ? (uint32_t)((r * ld + col) * 2) : OOB;
+        sa = (uint32_t)(TL::NW * KRB * ld * 2);
+        step = (uint32_t)(64 * ld * 2);
+    }
+};
+
+// 8 consecutive contraction indices of one column from a transposed tile:
+// two transposing reads.  Lane l (group G = l/16, j = l%16) addresses row
+// 8G + j/4 (+4) and column base + 4 (j%4); the read hands lane l the values of
+// column base + l%16 for rows 8G .. 8G+3 (+4), the MFMA operand layout.
+template <int ROWS>
+__device__ __forceinline__ i32x4 frag_t(const char* tile, int row0, int col0, int lane) {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4 lds_s4;
+    const int G = lane >> 4, j = lane & 15;
+    const int col = col0 + 4 * (j & 3);
+    const int r1 = row0 + 8 * G + (j >> 2), r2 = r1 + 4;
+    const char* p1 = tile + r1 * (ROWS * 2) + (((col >> 3) ^ tswz<ROWS / 8>(r1)) << 4) + ((col >> 2) & 1) * 8;
+    const char* p2 = tile + r2 * (ROWS * 2) + (((col >> 3) ^ tswz<ROWS / 8>(r2)) << 4) + ((col >> 2) & 1) * 8;
+    const s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(__attribute__((address_space(3))) char*)p1);
+    const s4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(__attribute__((address_space(3))) char*)p2);
+    const i32x2 ai = __builtin_bit_cast(i32x2, a), bi = __builtin_bit_cast(i32x2, b);
+    return i32x4{ai[0], ai[1], bi[0], bi[1]};
+}
+
 // This wave's operand fragments of MFMA substep `sub` (64 bytes per row) from
 // an LDS stage: FN 16-row blocks of the A tile, FM of the B tile.
-template <class TL>
+template <class TL, bool TA = false, bool TB = false>
 __device__ __forceinline__ void read_frags(const char* st, int sub, i32x4 (&fa)[TL::FN], i32x4 (&fb)[TL::FM],
                                            int lane, int wn, int wm) {
     const int kc = sub * 4 + (lane >> 4);
     const char* sb = st + TL::TN * TL::BKB;
 #pragma unroll
-    for (int i = 0; i < TL::FN; ++i) fa[i] = *(const i32x4*)(st + lds_at<TL>(wn * TL::WN + i * 16 + (lane & 15), kc));
+    for (int i = 0; i < TL::FN; ++i) {
+        if constexpr (TA) fa[i] = frag_t<TL::TN>(st, sub * 32, wn * TL::WN + i * 16, lane);
+        else fa[i] = *(const i32x4*)(st + lds_at<TL>(wn * TL::WN + i * 16 + (lane & 15), kc));
+    }
 #pragma unroll
-    for (int j = 0; j < TL::FM; ++j) fb[j] = *(const i32x4*)(sb + lds_at<TL>(wm * TL::WM + j * 16 + (lane & 15), kc));
+    for (int j = 0; j < TL::FM; ++j) {
+        if constexpr (TB) fb[j] = frag_t<TL::TM>(sb, sub * 32, wm * TL::WM + j * 16, lane);
+        else fb[j] = *(const i32x4*)(sb + lds_at<TL>(wm * TL::WM + j * 16 + (lane & 15), kc));
+    }
 }
 
 template <class CT, class TL>
@@ -156,9 +221,13 @@ __device__ __forceinline__ void mma(const i32x4 (&fa)[TL::FN], const i32x4 (&fb)
 // KT are issued too, entirely out of range: they write zeros into a stage that
 // is never read again, so every pipeline step issues exactly Q loads per wave
 // and the vmcnt bookkeeping needs no branches.
-template <class TL>
+template <class TL, bool TA = false, bool TB = false>
 struct Steps {
     Loader<TL> lf, lm;
+    LoaderT<TL, TL::TN> tma;         // transposed A side (main steps; no fold)
+    LoaderT<TL, TL::TM> tmb;         // transposed B side
+    const char *tma_p, *tmb_p;
+    uint32_t tma_n, tmb_n;           // whole-matrix byte extents
     const char *fa, *fb, *ma, *mb;   // operand rows of this tile
     uint32_t nfa, nfb, nma, nmb;     // their byte extents (buffer range)
     uint32_t fbytes, kbytes;
@@ -177,7 +246,29 @@ struct Steps {
         l.sa = fold ? lf.sa : lm.sa;
         l.sb = fold ? lf.sb : lm.sb;
         const uint32_t row_bytes = s < KT ? (fold ? fbytes : kbytes) : 0u;   // 0: all out of range
-        l.issue(st, ra, rb, row_bytes, (uint32_t)(fold ? s : s - RF + k0) * TL::BKB, wave, lane);
+        const uint32_t sidx = (uint32_t)(fold ? s : s - RF + k0);          // step within the fold / main
+        l.template issue<!TA, !TB>(st, ra, rb, row_bytes, sidx * TL::BKB, wave, lane);
+        if constexpr (TA) {
+            const auto rt = make_rsrc(tma_p, tma_n);
+            const uint32_t adv = sidx * tma.step;
+#pragma unroll
+            for (int q = 0; q < Loader<TL>::QA; ++q) {
+                const uint32_t v = (s < KT && tma.off != OOB) ? tma.off + (uint32_t)q * tma.sa + adv : OOB;
+                auto* dst = (__attribute__((address_space(3))) void*)(st + (wave + q * TL::NW) * 1024);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, dst, 16, v, 0, 0, 0);
+            }
+        }
+        if constexpr (TB) {
+            const auto rt = make_rsrc(tmb_p, tmb_n);
+            const uint32_t adv = sidx * tmb.step;
+#pragma unroll
+            for (int q = 0; q < Loader<TL>::QB; ++q) {
+                const uint32_t v = (s < KT && tmb.off != OOB) ? tmb.off + (uint32_t)q * tmb.sa + adv : OOB;
+                auto* dst =
+                    (__attribute__((address_space(3))) void*)(st + (wave + (Loader<TL>::QA + q) * TL::NW) * 1024);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, dst, 16, v, 0, 0, 0);
+            }
+        }
     }
 };
 
@@ -205,14 +296,15 @@ __device__ __forceinline__ void mma_spread(const i32x4 (&fa)[TL::FN], const i32x
 //   substep 1: wait until step kt+1 has landed (NS-2 steps after it may still be
 //              in flight), barrier, refill the stage of step kt with step
 //              kt+NS, read step kt+1's substep 0 into (f0a, f0b); MFMAs on (f1a, f1b)
-template <class CT, class TL>
-__device__ __forceinline__ void k_step(const Steps<TL>& S, char* smem, int kt, i32x4 (&f0a)[TL::FN],
+template <class CT, class TL, bool TA = false, bool TB = false>
+__device__ __forceinline__ void k_step(const Steps<TL, TA, TB>& S, char* smem, int kt, i32x4 (&f0a)[TL::FN],
                                        i32x4 (&f0b)[TL::FM], i32x4 (&f1a)[TL::FN], i32x4 (&f1b)[TL::FM],
                                        f32x4 (&acc)[TL::FN][TL::FM], int wave, int lane, int wn, int wm) {
     static_assert(TL::SUB == 2, "two substeps per K step");
+    constexpr int ND = (TA ? 2 : 1) * TL::FN + (TB ? 2 : 1) * TL::FM;   // LDS reads per substep
     __builtin_amdgcn_s_waitcnt(0xC07F);   // substep 0's fragments have landed
-    read_frags<TL>(smem + (kt % TL::NS) * TL::STAGE, 1, f1a, f1b, lane, wn, wm);
-    mma_spread<CT, TL, 0, TL::FN + TL::FM>(f0a, f0b, acc);
+    read_frags<TL, TA, TB>(smem + (kt % TL::NS) * TL::STAGE, 1, f1a, f1b, lane, wn, wm);
+    mma_spread<CT, TL, 0, ND>(f0a, f0b, acc);
     // every MFMA of substep 0 is issued before this wave waits on memory
     __builtin_amdgcn_sched_barrier(0);
 
@@ -220,13 +312,16 @@ __device__ __forceinline__ void k_step(const Steps<TL>& S, char* smem, int kt, i
     lds_barrier();
     S.issue(smem, kt + TL::NS, wave, lane);
     // (past the last step this reads a stage that is never used: in bounds)
-    read_frags<TL>(smem + ((kt + 1) % TL::NS) * TL::STAGE, 0, f0a, f0b, lane, wn, wm);
-    mma_spread<CT, TL, TL::Q, TL::FN + TL::FM>(f1a, f1b, acc);
+    read_frags<TL, TA, TB>(smem + ((kt + 1) % TL::NS) * TL::STAGE, 0, f0a, f0b, lane, wn, wm);
+    mma_spread<CT, TL, TL::Q, ND>(f1a, f1b, acc);
 }
 
 // GAIN: a per-output-feature factor gain[n] in place of post (an instance of
 // its own, so the others carry no registers for it)
-template <class CT, class TL, bool GAIN>
+// TA / TB: the A / B operand stored with the contraction index as rows
+// (LoaderT; main steps only, launched with both and no fold); otherwise
+// operands as the forward stores them.
+template <class CT, class TL, bool GAIN, bool TA = false, bool TB = false>
 __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles_n, int tiles_m, int group_m) {
     __shared__ __attribute__((aligned(16))) char smem[TL::NS * TL::STAGE];
     constexpr int FN = TL::FN, FM = TL::FM;
@@ -250,7 +345,7 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
     // 1-2. fold and main contraction in one pipeline of K steps: NS LDS stages
     //      filled straight from global memory, NS steps ahead of their use;
     //      fragments are read one step ahead into a second register set.
-    Steps<TL> S;
+    Steps<TL, TA, TB> S;
     S.fbytes = (uint32_t)(p.rf * CT::es);
     S.kbytes = (uint32_t)(p.K * CT::es);
     // K split (blockIdx.y of gridDim.y): a contiguous range of the main steps;
@@ -271,6 +366,16 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
     S.nmb = (uint32_t)rows_b * S.kbytes;
     S.lf.init(S.fbytes, S.fbytes, wave, lane);
     S.lm.init(S.kbytes, S.kbytes, wave, lane);
+    if constexpr (TA) {
+        S.tma.init(n0, p.lda_t, wave, lane);
+        S.tma_p = (const char*)p.a;
+        S.tma_n = (uint32_t)(p.K * p.lda_t * 2);
+    }
+    if constexpr (TB) {
+        S.tmb.init(m0, p.ldb_t, wave, lane);
+        S.tmb_p = (const char*)p.b;
+        S.tmb_n = (uint32_t)(p.K * p.ldb_t * 2);
+    }
     const int KT = S.KT;
     if (KT > 0) {
         i32x4 f0a[FN], f0b[FM], f1a[FN], f1b[FM];
@@ -279,17 +384,17 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
         for (int s0 = 0; s0 < TL::NS; ++s0) S.issue(smem, s0, wave, lane);
         wait_vm<(TL::NS - 1) * TL::Q>();
         lds_barrier();
-        read_frags<TL>(smem, 0, f0a, f0b, lane, wn, wm);
+        read_frags<TL, TA, TB>(smem, 0, f0a, f0b, lane, wn, wm);
         // fold steps, then acc = scale * (h_r . up_c^T) once, then the main steps:
         // the accumulators see no vector ALU work inside either loop
-        for (int kt = 0; kt < S.RF; ++kt) k_step<CT, TL>(S, smem, kt, f0a, f0b, f1a, f1b, acc, wave, lane, wn, wm);
+        for (int kt = 0; kt < S.RF; ++kt) k_step<CT, TL, TA, TB>(S, smem, kt, f0a, f0b, f1a, f1b, acc, wave, lane, wn, wm);
         if (S.RF > 0) {
 #pragma unroll
             for (int i = 0; i < FN; ++i)
 #pragma unroll
                 for (int j = 0; j < FM; ++j) acc[i][j] *= p.scale;
         }
-        for (int kt = S.RF; kt < KT; ++kt) k_step<CT, TL>(S, smem, kt, f0a, f0b, f1a, f1b, acc, wave, lane, wn, wm);
+        for (int kt = S.RF; kt < KT; ++kt) k_step<CT, TL, TA, TB>(S, smem, kt, f0a, f0b, f1a, f1b, acc, wave, lane, wn, wm);
         wait_vm<0>();   // the out-of-range loads past the last step still write LDS
     }
 
@@ -395,7 +500,14 @@ static hipError_t run(const GemmParams& p, hipStream_t s) {
     const int nblk = tiles_n * tiles_m;
     const int ks = p.ksplit > 1 ? p.ksplit : 1;
     // (a K split applies the gain in its reduction)
-    if (p.gain != nullptr && ks == 1)
+    if constexpr (CT::dt != DT_F32 && TL::TN != 192) {
+        if (p.ta && p.tb)
+            hipLaunchKernelGGL((gemm_kernel<CT, TL, false, true, true>), dim3(nblk, ks), dim3(TL::NT), 0, s, p, tiles_n,
+                               tiles_m, 4);
+    }
+    if (p.ta || p.tb) {
+        // (no transposed instance for fp32 compute or the 192-row tile: refused above)
+    } else if (p.gain != nullptr && ks == 1)
         hipLaunchKernelGGL((gemm_kernel<CT, TL, true>), dim3(nblk, ks), dim3(TL::NT), 0, s, p, tiles_n, tiles_m, 4);
     else
         hipLaunchKernelGGL((gemm_kernel<CT, TL, false>), dim3(nblk, ks), dim3(TL::NT), 0, s, p, tiles_n, tiles_m, 4);
@@ -510,6 +622,11 @@ int gemm_plan(int64_t M, int64_t N, int64_t K, int64_t rf, int c_dt, GemmCand* o
 hipError_t launch_gemm(int c_dt, const GemmParams& p, hipStream_t s) {
     int t = p.tile >= 0 ? p.tile : pick_tile(p.M, p.N, c_dt == DT_F32);
     if (c_dt == DT_F32 && t != T_M && t != T_S) return hipErrorInvalidValue;   // no fp32 instance
+    if (p.ta || p.tb) {
+        // transposed operands: both of them, 16-bit compute, no fold, no 192-row tile
+        if (c_dt == DT_F32 || !p.ta || !p.tb || p.rf > 0) return hipErrorInvalidValue;
+        if (t == T_G) t = T_L;
+    }
     if (c_dt == DT_F16) {
         switch (t) {
         case T_L: return run<CF16, TileL>(p, s);

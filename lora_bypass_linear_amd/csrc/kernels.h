@@ -41,6 +41,11 @@ struct GemmParams {
     // per output feature n: y = round_out(gain[n] * acc + b) in place of post
     // (the DoRA forward's m_n / norm_n; nullptr: none)
     const float* gain = nullptr;
+    // both operands stored with the contraction index as rows (16-bit
+    // compute, no fold): ta and tb together, a [K][lda_t] and b [K][ldb_t].
+    // Each such matrix must stay below 1 GiB (one buffer range covers it).
+    int ta = 0, tb = 0;
+    int64_t lda_t = 0, ldb_t = 0;
 };
 
 struct GemmCand {

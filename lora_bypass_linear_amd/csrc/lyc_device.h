@@ -111,6 +111,16 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double d) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// A buffer resource from values the compiler may hold in vector registers:
+// each piece is taken from the first lane (they are uniform), so that the
+// loads through it need no per-lane loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_uniform(const void* base, uint32_t bytes) {
+    const uint64_t b = (uint64_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    return make_rsrc((const void*)(((uint64_t)hi << 32) | lo), __builtin_amdgcn_readfirstlane(bytes));
+}
+
 // An offset that is always beyond num_records (which stays below 2^31).
 constexpr uint32_t OOB = 0x80000000u;
 

@@ -29,16 +29,6 @@ constexpr int BOFF = MC * 128;          // byte offset of the up_c chunk behind 
 static_assert((MT + MC) * 128 <= LDS, "operand chunk fits the exchange buffer");
 }  // namespace
 
-// A buffer resource from values the compiler may hold in vector registers:
-// each piece is taken from the first lane (they are uniform), so that the
-// loads through it need no per-lane loop.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_uniform(const void* base, uint32_t bytes) {
-    const uint64_t b = (uint64_t)base;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-    return make_rsrc((const void*)(((uint64_t)hi << 32) | lo), __builtin_amdgcn_readfirstlane(bytes));
-}
-
 // One rank chunk (128 bytes of every row) of the 128 down^T_c rows (ra) and
 // the 128 up_c rows (rb) of a tile: 8 rows per 32-thread group, one 16-byte
 // slot per thread.

@@ -228,9 +228,16 @@ def test_backward_workspace_sizes():
     n_all = L.lora_bwd_workspace_size(300, 64, 128, 17, 1, 1, 0, 1, 1, 1, 7)
     n_dx = L.lora_bwd_workspace_size(300, 64, 128, 17, 1, 1, 0, 1, 1, 1, 1)
     n_du = L.lora_bwd_workspace_size(300, 64, 128, 17, 1, 1, 0, 1, 1, 1, 4)
-    # dx needs W^T [K][N] and gh; dUp needs dy^T [N][M8] and h^T; all of it for the three
-    assert n_dx >= 128 * 64 * 2 + 300 * 32 * 2 and n_du >= 64 * 304 * 2 + 32 * 304 * 2
+    # dx needs W^T [K][N], down^T [K][32] and gh [M][32]; under 16-bit compute dUp reads dy as
+    # stored and needs h [M][32] (and down_c for it), no dy^T [N][M8]
+    assert n_dx >= 128 * 64 * 2 + 128 * 32 * 2 + 300 * 32 * 2
+    # h [M][32] + down_c with its two splits + up_c + norms: room for no dy^T copy (64 * 304 * 2)
+    assert 300 * 32 * 2 <= n_du < 300 * 32 * 2 + 4 * 128 * 32 * 2 + 64 * 32 * 2 + 2048
     assert n_all >= max(n_dx, n_du)
+    # fp32 compute: transposed copies, W^T [K][N] for dx and dy^T [N][M8] with h^T for dUp
+    n_dx32 = L.lora_bwd_workspace_size(300, 64, 128, 17, 3, 3, 0, 3, 3, 3, 1)
+    n_du32 = L.lora_bwd_workspace_size(300, 64, 128, 17, 3, 3, 0, 3, 3, 3, 4)
+    assert n_dx32 >= 128 * 64 * 4 + 300 * 32 * 4 and n_du32 >= 64 * 304 * 4 + 32 * 304 * 4
     ho, go, ld, fo = L.lora_bwd_workspace_layout(300, 64, 128, 17, 1, 1, 0, 1, 1, 1, 1)
     assert ho == 2 ** 64 - 1 and go % 256 == 0 and ld == 32      # dx alone recomputes no h
     ho, go, ld, fo = L.lora_bwd_workspace_layout(300, 64, 128, 17, 3, 3, 0, 3, 3, 3, 7)

@@ -130,6 +130,8 @@ EDGE = [
     ("scale_neg", "lora_bf16_16384x8192x8192_r128", dict(M=64, N=96, K=256, r=32), -0.75),
     ("scale_zero", "lora_f16_4096x3072x3072_r16", dict(M=64, N=64, K=64, r=16), 0.0),
     ("fp32_all", "sweep_xf32_wf32_2048x1280x5120_r32", dict(M=100, N=136, K=72, r=32), None),
+    # token contractions split four ways over 1000 tokens (the last split ragged)
+    ("tok_split", "lora_bf16_16384x8192x8192_r128", dict(M=1000, N=72, K=136, r=17), None),
 ]
 
 
