@@ -132,6 +132,8 @@ EDGE = [
     ("fp32_all", "sweep_xf32_wf32_2048x1280x5120_r32", dict(M=100, N=136, K=72, r=32), None),
     # token contractions split four ways over 1000 tokens (the last split ragged)
     ("tok_split", "lora_bf16_16384x8192x8192_r128", dict(M=1000, N=72, K=136, r=17), None),
+    # the largest token count the backward takes (2^20): token sums of 16384 K steps
+    ("m_max", "lora_bf16_16384x8192x8192_r128", dict(M=1 << 20, N=16, K=16, r=8), None),
 ]
 
 

@@ -145,6 +145,10 @@ EDGE = [
     ("scale_neg", "lora_bf16_16384x8192x8192_r128", dict(M=64, N=96, K=256, r=32), -0.75),
     ("affine_k8", "affine_f16_1024x768x1024", dict(M=3, N=5, K=8), None),
     ("affine_odd_n", "affine_f16_1024x768x1024", dict(M=70, N=99, K=64), None),
+    # the largest K the library takes (2^20): the longest accumulation chains and row offsets
+    ("k_max_f16", "lora_f16_4096x3072x3072_r16", dict(M=20, N=40, K=1 << 20, r=16), None),
+    ("k_max_bf16", "lora_bf16_16384x8192x8192_r128", dict(M=17, N=24, K=1 << 20, r=8), None),
+    ("affine_k_max", "affine_f16_1024x768x1024", dict(M=9, N=24, K=1 << 20), None),
 ]
 
 
