@@ -80,6 +80,13 @@ def test_norms_ragged_k(K):
     _norm_check(BASE["lora_f16_4096x3072x3072_r16"].resized(N=70, K=K))
 
 
+@pytest.mark.parametrize("name", ["lora_bf16_16384x8192x8192_r128", "lora_f16_4096x3072x3072_r16"])
+def test_norms_many_tiles_ragged(name):
+    """2145 tiles of 128 x 128, ragged in N and K, more than the resident
+    workgroups (several rounds per CU)."""
+    _norm_check(BASE[name].resized(N=8197, K=4104))
+
+
 def test_norms_rank_zero_and_negative_scale():
     _norm_check(BASE["lora_bf16_16384x8192x8192_r128"].resized(N=130, K=136, r=0))
     _norm_check(BASE["lora_bf16_16384x8192x8192_r128"].resized(N=130, K=136, r=17), scale=-0.5)

@@ -110,6 +110,16 @@ def test_edge_cases(tag, N, K, r, scale, dt):
     _check(w, d, u, scale, f"{tag}_{dt}")
 
 
+@pytest.mark.parametrize("tag,name,r", [("bf16", "lora_bf16_16384x8192x8192_r128", 128),
+                                        ("f16_bf16out", "lora_f16_4096x3072x3072_r16", 16)])
+def test_many_tiles_ragged_full_output(tag, name, r):
+    """2145 tiles of 128 x 128, ragged in N and K, more than the resident
+    workgroups (several rounds per CU); in place too."""
+    w, d, u = _weights(name, 8197, 4104, r)
+    y, _ = _check(w, d, u, BASE[name].scale, f"many tiles {tag}")
+    assert torch.equal(_gpu(w, d, u, BASE[name].scale, f"many tiles {tag} in place", inplace=True), y)
+
+
 def test_rank_zero_is_a_copy():
     w, d, u = _weights("lora_bf16_16384x8192x8192_r128", 70, 200, 0)
     y = _gpu(w, d, u, 2.0, "rank0 copy")
