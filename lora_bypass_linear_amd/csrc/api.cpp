@@ -418,7 +418,7 @@ struct BwdLayout {
     // tr_tok: dDown and dUp read x, dy, h_r and gh_r as stored, the token
     // index as their contraction rows (16-bit compute, each operand below
     // 1 GiB); else they read transposed copies.  dx reads W^T and down^T copies.
-    bool tr_tok = false, need_prep = false;
+    bool tr_tok = false;
     int ks_dx = 1, ks_dd = 1, ks_du = 1;
 };
 
@@ -473,21 +473,20 @@ BwdLayout bwd_layout(const Bwd& B) {
     L.need_gh = P.rank > 0 && (dx || dd);   // gh_r feeds dx's fold and dDown
     const size_t G1 = (size_t)1 << 30;
     L.tr_tok = split && (size_t)P.M * (size_t)P.K * 2 < G1 && (size_t)P.M * (size_t)P.N * 2 < G1;
-    L.need_prep = L.need_h;
     L.cast_x = P.x_dt == LYC_F32 && P.c_dt != LYC_F32 && (L.need_h || (L.tr_tok && dd));
     L.cast_g = B.dy_dt == LYC_F32 && P.c_dt != LYC_F32 && (L.need_gh || dx || (L.tr_tok && du));
     auto take = [&](size_t& at, size_t bytes) { at = off; off = align256(off + bytes); };
     const size_t M = (size_t)P.M, N = (size_t)P.N, K = (size_t)P.K, R = (size_t)P.r_pad, M8 = (size_t)B.M8;
     if (L.cast_x) take(L.xc, M * K * 2);
     if (L.cast_g) take(L.gc, M * N * 2);
-    if (L.need_prep) {
+    if (L.need_h) {
         take(L.dc, R * K * ce);
         if (split) { take(L.dh, R * K * ce); take(L.dl, R * K * ce); }
         take(L.uc, N * R * ce);
         take(L.dnorm, R * 2 * sizeof(double));
         take(L.flag_h, sizeof(unsigned));
+        take(L.h, M * R * ce);
     }
-    if (L.need_h) take(L.h, M * R * ce);
     if (L.need_gh) {
         take(L.ut, R * N * ce);
         if (split) { take(L.uth, R * N * ce); take(L.utl, R * N * ce); }
@@ -603,7 +602,7 @@ int backward(const Bwd& B, const void* x, const void* w, const void* down, const
     }
 
     // h_r, recomputed exactly as the forward computes it (only dUp reads it)
-    if (L.need_prep && M > 0) {
+    if (L.need_h && M > 0) {
         lyc::PrepParams pp{};
         pp.down = down;
         pp.down_dt = P.d_dt;
@@ -622,8 +621,6 @@ int backward(const Bwd& B, const void* x, const void* w, const void* down, const
         pp.c_dt = P.c_dt;
         pp.vec = aligned(down, 16) ? 1 : 0;
         if (timed(LYC_KERNEL_PREP, s, [&] { return lyc::launch_prep(pp, s); }) != hipSuccess) return LYC_ERR_HIP;
-    }
-    if (L.need_h && M > 0) {
         lyc::XrParams hp{};
         hp.x = xa;
         hp.b = W + (split ? L.dh : L.dc);
