@@ -166,8 +166,12 @@ def test_mixed_halves_refused():
         _gpu(inp, wl)
 
 
-def test_deterministic():
-    wl = BASE["lora_bf16_16384x8192x8192_r128"].resized(M=200, N=136, K=264)
+@pytest.mark.parametrize("dims", [dict(M=200, N=136, K=264), dict(M=1000, N=72, K=136, r=17)],
+                         ids=["one_split", "token_sums_split"])
+def test_deterministic(dims):
+    """Bit-identical gradients on repeated calls, also where the token sums
+    are split over K (their partial sums are added in a fixed order)."""
+    wl = BASE["lora_bf16_16384x8192x8192_r128"].resized(**dims)
     inp = _inputs(wl)
     a, b = _gpu(inp, wl), _gpu(inp, wl)
     for u, v in zip(a[:3], b[:3]):
