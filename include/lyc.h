@@ -173,7 +173,10 @@ int lyc_linear_workspace_layout(int64_t M, int64_t N, int64_t K, int x_dt, int w
  *    rank <= 256, else LYC_ERR_UNSUPPORTED.  N == 0 or K == 0 launches
  *    nothing.  scale must be finite and within the fp32 range.
  *  - The workspace (256-byte aligned, lyc_lora_merge_workspace_size bytes,
- *    0 when rank == 0) receives compute-dtype copies of down^T and up.
+ *    0 when rank == 0) receives compute-dtype copies of down^T and up.  When
+ *    down and up are already in a 16-bit compute dtype, rank and K are
+ *    multiples of 8 and both are 16-byte aligned, they are read as stored
+ *    and the workspace is left untouched (it is still required).
  * The same stream, ownership and error conventions as the forward calls.
  */
 int lyc_lora_merge_workspace_size(int64_t N, int64_t K, int64_t rank, int w_dt, int down_dt, int up_dt,

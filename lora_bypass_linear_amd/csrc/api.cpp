@@ -349,6 +349,14 @@ int check_merge(Merge& G) {
     return LYC_OK;
 }
 
+// down and up can be read as stored (no preparation pass): both already in a
+// 16-bit compute dtype, rank and K multiples of 8 (16-byte chunks), 16-byte
+// aligned, and down below 2 GiB (one buffer range)
+bool merge_reads_as_stored(const Merge& G, const void* down, const void* up) {
+    return G.rank > 0 && G.c_dt != LYC_F32 && G.d_dt == G.c_dt && G.u_dt == G.c_dt && G.rank % 8 == 0 &&
+           G.K % 8 == 0 && aligned(down, 16) && aligned(up, 16) && G.rank * G.K * 2 < ((int64_t)1 << 31);
+}
+
 int merge(const Merge& G, const void* w, const void* down, const void* up, double scale, void* out, int out_dt,
           void* ws, size_t ws_bytes, void* stream) {
     if (out_dt != G.o_dt) return LYC_ERR_DTYPE_MISMATCH;
@@ -368,7 +376,8 @@ int merge(const Merge& G, const void* w, const void* down, const void* up, doubl
     hipStream_t s = (hipStream_t)stream;
     char* W = (char*)ws;
     (void)hipGetLastError();
-    if (G.r_pad > 0) {
+    const bool raw = merge_reads_as_stored(G, down, up);
+    if (G.r_pad > 0 && !raw) {
         lyc::MergePrepParams mp{};
         mp.down = down;
         mp.down_dt = G.d_dt;
@@ -397,6 +406,11 @@ int merge(const Merge& G, const void* w, const void* down, const void* up, doubl
     // 8 elements per lane chunk when W and W' are both 16-bit, else 4
     const int E = (G.w_dt == LYC_F32 || out_dt == LYC_F32) ? 4 : 8;
     mg.vec = (G.K % E == 0) && aligned(w, E * esize(G.w_dt)) && aligned(out, E * esize(out_dt));
+    if (raw) {
+        mg.down_raw = down;
+        mg.up_raw = up;
+        mg.rank = G.rank;
+    }
     if (timed(LYC_KERNEL_GEMM, s, [&] { return lyc::launch_merge(G.c_dt, mg, s); }) != hipSuccess) return LYC_ERR_HIP;
     return LYC_OK;
 }
@@ -947,7 +961,8 @@ int lyc_dora_norms(const void* w, int w_dt, const void* down, int down_dt, const
         lyc::TransposeParams tp{norms, LYC_F32, 0, 0, norms, LYC_F32, N, 1};
         return lyc::launch_transpose(tp, s) == hipSuccess ? LYC_OK : LYC_ERR_HIP;
     }
-    if (G.r_pad > 0) {
+    const bool raw = merge_reads_as_stored(G, down, up);
+    if (G.r_pad > 0 && !raw) {
         lyc::MergePrepParams mp{};
         mp.down = down;
         mp.down_dt = down_dt;
@@ -977,6 +992,11 @@ int lyc_dora_norms(const void* w, int w_dt, const void* down, int down_dt, const
     mg.vec = (K % E == 0) && aligned(w, E * esize(w_dt));
     mg.norm_partial = (float*)(W + part);
     mg.norms = norms;
+    if (raw) {
+        mg.down_raw = down;
+        mg.up_raw = up;
+        mg.rank = G.rank;
+    }
     if (timed(LYC_KERNEL_GEMM, s, [&] { return lyc::launch_merge(G.c_dt, mg, s); }) != hipSuccess) return LYC_ERR_HIP;
     if (timed(LYC_KERNEL_PREP, s, [&] { return lyc::launch_norm_finish(mg, s); }) != hipSuccess) return LYC_ERR_HIP;
     return LYC_OK;

@@ -132,19 +132,6 @@ struct Loader {
 
 // An operand stored with the contraction index as rows ([contraction][ld],
 // 16-bit; x, dy and W in the backward): a K step is 64 contraction rows of
-// Chunk permutation of a transposed tile's row r (CPR 16-byte chunks a row):
-// 32-byte pairs of chunks move by a row-dependent amount so that the rows one
-// half-wave's transposing read touches (r = 0..3 and 8..11 of a group of 16,
-// or 4..7 and 12..15) fall on distinct banks.  Rows of 256 bytes or more
-// start on the same bank, so the pair index takes bits 0, 1 and 3 of r; rows
-// of 128 bytes alternate halves of the banks, so it takes bits 1 and 3.
-template <int CPR>
-__device__ __forceinline__ int tswz(int r) {
-    static_assert(CPR >= 8, "transposed tile rows of 128 bytes or more");
-    if constexpr (CPR >= 16) return 2 * ((r & 3) | ((r >> 1) & 4));
-    else return 2 * (((r >> 1) & 1) | ((r >> 2) & 2));
-}
-
 // ROWS consecutive columns, kept in LDS in that orientation (rows of ROWS*2
 // bytes, 16-byte slot s of row r holding chunk s ^ tswz(r)) and turned into
 // MFMA fragments by the transposing LDS read.  A wave load still fills 1 KiB
@@ -168,25 +155,6 @@ struct LoaderT {
         step = (uint32_t)(64 * ld * 2);
     }
 };
-
-// 8 consecutive contraction indices of one column from a transposed tile:
-// two transposing reads.  Lane l (group G = l/16, j = l%16) addresses row
-// 8G + j/4 (+4) and column base + 4 (j%4); the read hands lane l the values of
-// column base + l%16 for rows 8G .. 8G+3 (+4), the MFMA operand layout.
-template <int ROWS>
-__device__ __forceinline__ i32x4 frag_t(const char* tile, int row0, int col0, int lane) {
-    typedef short s4 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) s4 lds_s4;
-    const int G = lane >> 4, j = lane & 15;
-    const int col = col0 + 4 * (j & 3);
-    const int r1 = row0 + 8 * G + (j >> 2), r2 = r1 + 4;
-    const char* p1 = tile + r1 * (ROWS * 2) + (((col >> 3) ^ tswz<ROWS / 8>(r1)) << 4) + ((col >> 2) & 1) * 8;
-    const char* p2 = tile + r2 * (ROWS * 2) + (((col >> 3) ^ tswz<ROWS / 8>(r2)) << 4) + ((col >> 2) & 1) * 8;
-    const s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(__attribute__((address_space(3))) char*)p1);
-    const s4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(__attribute__((address_space(3))) char*)p2);
-    const i32x2 ai = __builtin_bit_cast(i32x2, a), bi = __builtin_bit_cast(i32x2, b);
-    return i32x4{ai[0], ai[1], bi[0], bi[1]};
-}
 
 // This wave's operand fragments of MFMA substep `sub` (64 bytes per row) from
 // an LDS stage: FN 16-row blocks of the A tile, FM of the B tile.

@@ -39,6 +39,12 @@ struct MergeParams {
     // squares [K tiles][N] fp32, then norms[n] = sqrt of their sum in tile order
     float* norm_partial = nullptr;
     float* norms = nullptr;
+    // down [rank][K] and up [N][rank] read as stored, in place of dt_c and uc
+    // (16-bit compute, both already in it, rank and K multiples of 8, 16-byte
+    // aligned, rank * K * 2 below 2^31); nullptr: the prepared copies
+    const void* down_raw = nullptr;
+    const void* up_raw = nullptr;
+    int64_t rank = 0;
 };
 hipError_t launch_merge(int c_dt, const MergeParams& p, hipStream_t s);
 // after launch_merge in the norm mode: norms[n] = sqrt(sum of the tiles' partials, in tile order)

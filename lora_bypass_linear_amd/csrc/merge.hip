@@ -10,7 +10,9 @@
 //      non-temporally (W and W' pass through once; the rank operands, re-read
 //      by every tile, stay in L2);
 //   2. while W is in flight, the rank contraction runs on MFMA from LDS
-//      (chunks of 128 bytes of every operand row, 16-byte slots swizzled);
+//      (chunks of 128 bytes of every operand row, 16-byte slots swizzled;
+//      or, with down and up read as stored, down's rank rows as a
+//      contraction-major tile read through the transposing LDS read);
 //   3. the fp32 accumulators go through LDS once more, so that
 //   4. each lane meets the W elements it loaded: W' = fma(scale, acc, W),
 //      rounded once, stored 16 bytes per lane in row order.
@@ -32,31 +34,61 @@ static_assert((MT + MC) * 128 <= LDS, "operand chunk fits the exchange buffer");
 // One rank chunk (128 bytes of every row) of the 128 down^T_c rows (ra) and
 // the 128 up_c rows (rb) of a tile: 8 rows per 32-thread group, one 16-byte
 // slot per thread.
+//
+// RAW (down and up as the caller stores them, already in the compute dtype):
+// chunk c of the A side is rank rows 64c .. 64c+63 of down [rank][K] over the
+// tile's 128 k columns, kept as a contraction-major tile (256-byte rows,
+// 16-byte chunks permuted by tswz) for the transposing LDS read; rows past the
+// rank and columns past K fall outside the range and read 0.  The B side reads
+// up [N][rank] rows with their own stride rowb_u (rank elements).
+template <bool RAW>
 __device__ __forceinline__ void merge_chunk_loads(i32x4 (&st)[8], __amdgpu_buffer_rsrc_t ra,
                                                   __amdgpu_buffer_rsrc_t rb, int c, uint32_t rowb, int orow,
-                                                  int okc) {
+                                                  int okc, int tid, int64_t K, int64_t k0, uint32_t rowb_u) {
     const uint32_t byte = (uint32_t)c * 128 + okc * 16;
+    if constexpr (RAW) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) st[q] = buf_load16(ra, byte < rowb ? (uint32_t)(q * 32 + orow) * rowb + byte : OOB);
+        for (int q = 0; q < 4; ++q) {
+            const int i = q * 256 + tid, r = i >> 4, s = i & 15;
+            const int64_t k = k0 + 8 * (s ^ tswz<16>(r));
+            st[q] = buf_load16(ra, k < K ? (uint32_t)(((int64_t)(64 * c + r) * K + k) * 2) : OOB);
+        }
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        st[4 + q] = buf_load16(rb, byte < rowb ? (uint32_t)(q * 32 + orow) * rowb + byte : OOB);
+        for (int q = 0; q < 4; ++q)
+            st[4 + q] = buf_load16(rb, byte < rowb_u ? (uint32_t)(q * 32 + orow) * rowb_u + byte : OOB);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) st[q] = buf_load16(ra, byte < rowb ? (uint32_t)(q * 32 + orow) * rowb + byte : OOB);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            st[4 + q] = buf_load16(rb, byte < rowb ? (uint32_t)(q * 32 + orow) * rowb + byte : OOB);
+    }
 }
 
 // Chunk c to LDS (16-byte slots swizzled per row), then its one or two
 // 64-byte MFMA substeps: this wave's 64 k x 64 n quadrant.
-template <class CT>
+template <class CT, bool RAW>
 __device__ __forceinline__ void merge_chunk_mma(char* smem, const i32x4 (&st)[8], f32x4 (&acc)[4][4], int c,
-                                                uint32_t rowb, int orow, int okc, int lane, int wn, int wk) {
+                                                uint32_t rowb, int orow, int okc, int lane, int wn, int wk, int tid) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) *(i32x4*)(smem + (q < 4 ? 0 : BOFF) + lds_off((q & 3) * 32 + orow, okc)) = st[q];
+    for (int q = 0; q < 8; ++q) {
+        if (RAW && q < 4) {
+            const int i = q * 256 + tid;
+            *(i32x4*)(smem + (i >> 4) * 256 + (i & 15) * 16) = st[q];
+        } else {
+            *(i32x4*)(smem + (q < 4 ? 0 : BOFF) + lds_off((q & 3) * 32 + orow, okc)) = st[q];
+        }
+    }
     lds_barrier();
     const int nsub = (uint32_t)c * 128 + 64 < rowb ? 2 : 1;
     for (int s = 0; s < nsub; ++s) {
         i32x4 fa[4], fb[4];
         const int kc = 4 * s + (lane >> 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fa[i] = *(const i32x4*)(smem + lds_off(64 * wk + 16 * i + (lane & 15), kc));
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (RAW) fa[i] = frag_t<MC>(smem, 32 * s, 64 * wk + 16 * i, lane);
+            else fa[i] = *(const i32x4*)(smem + lds_off(64 * wk + 16 * i + (lane & 15), kc));
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) fb[j] = *(const i32x4*)(smem + BOFF + lds_off(64 * wn + 16 * j + (lane & 15), kc));
 #pragma unroll
@@ -66,10 +98,19 @@ __device__ __forceinline__ void merge_chunk_mma(char* smem, const i32x4 (&st)[8]
     }
 }
 
+// The A-side resource of a tile: prepared, its 128 rows of down^T_c; RAW, all
+// of down [rank][K] (the offsets carry the tile's columns)
+template <bool RAW>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t merge_rsrc_a(const MergeParams& p, int64_t k0, int64_t ka,
+                                                               uint32_t rowb) {
+    if constexpr (RAW) return make_rsrc_uniform(p.down_raw, (uint32_t)(p.rank * p.K * 2));
+    else return make_rsrc_uniform((const char*)p.dt_c + k0 * rowb, (uint32_t)ka * rowb);
+}
+
 // NORM: instead of storing W', each tile adds up v^2 over its columns for
 // every row and writes that partial sum to norm_partial[tile column][n] (the
 // DoRA row norms of the merged weight, which is never stored).
-template <class CT, bool WF, bool OF, bool VEC, bool NORM>
+template <class CT, bool WF, bool OF, bool VEC, bool NORM, bool RAW>
 __global__ __launch_bounds__(256, (WF || !VEC) ? 2 : 3) void merge_kernel(MergeParams p, int tiles_k) {
     __shared__ __attribute__((aligned(16))) char smem[LDS];
     // a thread's share of the tile: E consecutive elements of one row per pass
@@ -93,13 +134,14 @@ __global__ __launch_bounds__(256, (WF || !VEC) ? 2 : 3) void merge_kernel(MergeP
     const uint32_t rowb = (uint32_t)p.r_pad * CT::es;
     const int nchunk = (int)((rowb + 127) / 128);
     const int64_t ka = p.K - k0 < MC ? p.K - k0 : MC, nb_ = p.N - n0 < MT ? p.N - n0 : MT;
-    const auto ra = make_rsrc_uniform((const char*)p.dt_c + k0 * rowb, (uint32_t)ka * rowb);
-    const auto rb = make_rsrc_uniform((const char*)p.uc + n0 * rowb, (uint32_t)nb_ * rowb);
+    const uint32_t rowb_u = RAW ? (uint32_t)p.rank * CT::es : rowb;   // up's row stride
+    const auto ra = merge_rsrc_a<RAW>(p, k0, ka, rowb);
+    const auto rb = make_rsrc_uniform((const char*)(RAW ? p.up_raw : p.uc) + n0 * rowb_u, (uint32_t)nb_ * rowb_u);
     const int orow = tid >> 3, okc = tid & 7;   // operand row (of 32 per load) and 16-byte slot
     // (unconditional: without a rank every offset is out of range and reads 0;
     // a branch here would cost the exact wait counts below)
     i32x4 st[8];
-    merge_chunk_loads(st, ra, rb, 0, rowb, orow, okc);
+    merge_chunk_loads<RAW>(st, ra, rb, 0, rowb, orow, okc, tid, p.K, k0, rowb_u);
 
     // 1b. the W tile, behind the operand chunk in the memory queue.  VEC: K
     //     is a multiple of E and the rows are aligned, so a lane's chunk is
@@ -146,11 +188,11 @@ __global__ __launch_bounds__(256, (WF || !VEC) ? 2 : 3) void merge_kernel(MergeP
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    merge_chunk_mma<CT>(smem, st, acc, 0, rowb, orow, okc, lane, wn, wk);
+    merge_chunk_mma<CT, RAW>(smem, st, acc, 0, rowb, orow, okc, lane, wn, wk, tid);
     for (int c = 1; c < nchunk; ++c) {
-        merge_chunk_loads(st, ra, rb, c, rowb, orow, okc);
+        merge_chunk_loads<RAW>(st, ra, rb, c, rowb, orow, okc, tid, p.K, k0, rowb_u);
         lds_barrier();   // every wave is done reading the previous chunk
-        merge_chunk_mma<CT>(smem, st, acc, c, rowb, orow, okc, lane, wn, wk);
+        merge_chunk_mma<CT, RAW>(smem, st, acc, c, rowb, orow, okc, lane, wn, wk, tid);
     }
 
     // 3-4. in two halves of 64 rows: the accumulators of the waves that own
@@ -335,18 +377,29 @@ hipError_t launch_merge_prep(const MergePrepParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <class CT, bool WF, bool OF>
-static hipError_t run_merge(const MergeParams& p, hipStream_t s) {
+template <class CT, bool WF, bool OF, bool RAW>
+static hipError_t run_merge_raw(const MergeParams& p, hipStream_t s) {
     const int tiles_n = (int)((p.N + MT - 1) / MT), tiles_k = (int)((p.K + MC - 1) / MC);
     const dim3 g((unsigned)(tiles_n * tiles_k));
     if (p.norm_partial != nullptr) {
-        if (p.vec) hipLaunchKernelGGL((merge_kernel<CT, WF, OF, true, true>), g, dim3(256), 0, s, p, tiles_k);
-        else hipLaunchKernelGGL((merge_kernel<CT, WF, OF, false, true>), g, dim3(256), 0, s, p, tiles_k);
+        if (p.vec) hipLaunchKernelGGL((merge_kernel<CT, WF, OF, true, true, RAW>), g, dim3(256), 0, s, p, tiles_k);
+        else hipLaunchKernelGGL((merge_kernel<CT, WF, OF, false, true, RAW>), g, dim3(256), 0, s, p, tiles_k);
         return hipGetLastError();
     }
-    if (p.vec) hipLaunchKernelGGL((merge_kernel<CT, WF, OF, true, false>), g, dim3(256), 0, s, p, tiles_k);
-    else hipLaunchKernelGGL((merge_kernel<CT, WF, OF, false, false>), g, dim3(256), 0, s, p, tiles_k);
+    if (p.vec) hipLaunchKernelGGL((merge_kernel<CT, WF, OF, true, false, RAW>), g, dim3(256), 0, s, p, tiles_k);
+    else hipLaunchKernelGGL((merge_kernel<CT, WF, OF, false, false, RAW>), g, dim3(256), 0, s, p, tiles_k);
     return hipGetLastError();
+}
+
+// RAW (down and up read as stored) for 16-bit compute only
+template <class CT, bool WF, bool OF>
+static hipError_t run_merge(const MergeParams& p, hipStream_t s) {
+    if constexpr (CT::dt != DT_F32) {
+        if (p.down_raw != nullptr) return run_merge_raw<CT, WF, OF, true>(p, s);
+    } else {
+        if (p.down_raw != nullptr) return hipErrorInvalidValue;
+    }
+    return run_merge_raw<CT, WF, OF, false>(p, s);
 }
 
 hipError_t launch_merge(int c_dt, const MergeParams& p, hipStream_t s) {
