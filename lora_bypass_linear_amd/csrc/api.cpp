@@ -277,6 +277,9 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
     g.vec_store = (P.N % 4 == 0) && aligned(y, vec_align);
 
     if (P.r_pad > 0) {
+        // up already in the compute dtype, unpadded (rank == r_pad) and 16-byte
+        // aligned: the fold reads it as stored and the prep makes no copy
+        const bool up_stored = P.u_dt == P.c_dt && P.rank == P.r_pad && aligned(up, 16);
         lyc::PrepParams pp{};
         pp.down = down;
         pp.down_dt = P.d_dt;
@@ -285,7 +288,7 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
         pp.dc = W + L.dc;
         pp.dh = W + L.dh;
         pp.dl = W + L.dl;
-        pp.uc = W + L.uc;
+        pp.uc = up_stored ? nullptr : W + L.uc;
         pp.dnorm = (double2*)(W + L.dnorm);
         pp.flagged = (unsigned*)(W + L.flagged);
         pp.N = P.N;
@@ -315,7 +318,7 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
         if (timed(LYC_KERNEL_HPASS, s, [&] { return lyc::launch_xr(P.c_dt, hp, s); }) != hipSuccess)
             return LYC_ERR_HIP;
 
-        g.af = W + L.uc;
+        g.af = up_stored ? up : (const void*)(W + L.uc);
         g.bf = W + L.h;
         g.rf = P.r_pad;
     }
@@ -496,7 +499,6 @@ BwdLayout bwd_layout(const Bwd& B) {
     if (L.need_h) {
         take(L.dc, R * K * ce);
         if (split) { take(L.dh, R * K * ce); take(L.dl, R * K * ce); }
-        take(L.uc, N * R * ce);
         take(L.dnorm, R * 2 * sizeof(double));
         take(L.flag_h, sizeof(unsigned));
         take(L.h, M * R * ce);
@@ -625,7 +627,7 @@ int backward(const Bwd& B, const void* x, const void* w, const void* down, const
         pp.dc = W + L.dc;
         pp.dh = W + L.dh;
         pp.dl = W + L.dl;
-        pp.uc = W + L.uc;
+        pp.uc = nullptr;   // the backward's products read up^T (gh) only
         pp.dnorm = (double2*)(W + L.dnorm);
         pp.flagged = (unsigned*)(W + L.flag_h);
         pp.N = N;

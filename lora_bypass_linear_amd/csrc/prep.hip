@@ -192,10 +192,11 @@ hipError_t launch_rownorm(const void* b, int c_dt, int64_t rows, int64_t K, void
 }
 
 hipError_t launch_prep(const PrepParams& p, hipStream_t s) {
-    const int64_t total = p.N * (int64_t)p.r_pad;
+    // no up copy wanted (uc == nullptr): the down rows only
+    const int64_t total = p.uc != nullptr ? p.N * (int64_t)p.r_pad : 0;
     int64_t up_blocks = (total + 255) / 256;
     if (up_blocks > 2048) up_blocks = 2048;
-    if (up_blocks < 1) up_blocks = 1;
+    if (up_blocks < 1 && p.uc != nullptr) up_blocks = 1;
     hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(p.r_pad + up_blocks)), dim3(256), 0, s, p);
     return hipGetLastError();
 }
