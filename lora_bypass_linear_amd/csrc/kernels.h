@@ -94,7 +94,7 @@ struct PrepParams {
     void* dc;
     void* dh;   // hi part of down_c (16-bit compute), else unused
     void* dl;   // lo part
-    void* uc;         // up_c [N][r_pad]; nullptr: no copy (the caller reads up as stored, or not at all)
+    void* uc;
     double2* dnorm;   // {|down_c,j|, |lo_j|}
     int vec;          // down rows start 16-byte aligned: vector loads
     unsigned* flagged;

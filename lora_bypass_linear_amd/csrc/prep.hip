@@ -192,7 +192,8 @@ hipError_t launch_rownorm(const void* b, int c_dt, int64_t rows, int64_t K, void
 }
 
 hipError_t launch_prep(const PrepParams& p, hipStream_t s) {
-    // no up copy wanted (uc == nullptr): the down rows only
+    // uc == nullptr: no up copy is wanted (the caller reads up as stored, or
+    // not at all), so only the down rows are prepared
     const int64_t total = p.uc != nullptr ? p.N * (int64_t)p.r_pad : 0;
     int64_t up_blocks = (total + 255) / 256;
     if (up_blocks > 2048) up_blocks = 2048;
