@@ -120,6 +120,25 @@ def test_many_tiles_ragged_full_output(tag, name, r):
     assert torch.equal(_gpu(w, d, u, BASE[name].scale, f"many tiles {tag} in place", inplace=True), y)
 
 
+def test_unaligned_factors_same_result():
+    """down and up one element into their buffers: the merge prepares copies
+    instead of reading them as stored, with the same W'."""
+    w, d, u = _weights("lora_bf16_16384x8192x8192_r128", 300, 520, 128)
+    y, _ = _check(w, d, u, 2.0, "aligned factors")
+    dev = torch.device("cuda:0")
+
+    def shift(t):   # t copied one element into a fresh buffer
+        buf = torch.zeros(t.numel() + 1, dtype=t.dtype, device=dev)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        return v
+
+    say("merge", "unaligned factors")
+    y_un = L.lora_merge(w.to(dev), shift(d.to(dev)), shift(u.to(dev)), 2.0)
+    torch.cuda.synchronize()
+    assert torch.equal(y_un.cpu(), y)
+
+
 def test_rank_zero_is_a_copy():
     w, d, u = _weights("lora_bf16_16384x8192x8192_r128", 70, 200, 0)
     y = _gpu(w, d, u, 2.0, "rank0 copy")

@@ -158,6 +158,29 @@ def test_edge_cases(tag, name, dims, scale):
     _check(wl, scale=scale)
 
 
+def _shifted(t):
+    """t copied one element into a fresh buffer: element-aligned, not 16-byte aligned."""
+    buf = torch.zeros(t.numel() + 1, dtype=t.dtype, device=t.device)
+    v = buf[1:].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+def test_unaligned_factors():
+    """down and up one element into their buffers: the prepared copies are used
+    instead of reading them as stored, with the same results."""
+    wl = BASE["lora_f16_4096x3072x3072_r16"].resized(M=130, N=136, K=264)
+    inputs = WL.generate(wl)
+    d = {k: v.to(torch.device("cuda:0")) for k, v in inputs.items()}
+    say("unaligned factors", wl.name)
+    y_al = L.lora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, d.get("b"))
+    y_un = L.lora_linear(d["x"], d["w"], _shifted(d["down"]), _shifted(d["up"]), wl.scale, d.get("b"))
+    torch.cuda.synchronize()
+    s = score(y_un.cpu(), oracle_forward(inputs, wl), None, wl.K, wl.r)
+    assert s["fail"] == 0, s
+    assert torch.equal(y_al.cpu(), y_un.cpu())
+
+
 def test_rank_zero_is_single_rounding():
     wl = BASE["lora_f16_4096x3072x3072_r16"].resized(M=40, N=48, K=64, r=0)
     _check(wl)
