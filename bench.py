@@ -4,14 +4,17 @@
 
 A step is one full forward -- operand preparation, the h contraction with its
 rounding guard, and the fused main contraction with the bypass fold and the
-bias/cast epilogue -- over inputs already resident in HBM.  W untimed steps,
-then K timed steps bracketed by device synchronisation (this sets `value`),
-then the same K steps again with a HIP event pair around every kernel launch
-for per-kernel device durations.  One JSON line is printed with throughput
-(algorithmic TFLOP/s), the fraction of the MFMA fp16/bf16 dense peak, max/RMS
-ULP against the fp64 oracle on sampled rows, the roofline of the dominant
-kernel, the oracle's own throughput on host cores, and the eager two-GEMM
-torch chain as a comparator.
+bias/cast epilogue -- over inputs already resident in HBM.  The default
+workload is the largest single-GPU one (bf16 16384x8192x8192, rank 128, bias,
+log-normal rows).  W untimed steps, then K timed steps bracketed by device
+synchronisation (this sets `value`), split into up to 15 blocks with events
+between them (median and range), then the same K steps again with a HIP event
+pair around every kernel launch for per-kernel device durations.  One JSON
+line is printed with throughput (algorithmic TFLOP/s), the fraction of the
+MFMA fp16/bf16 dense peak, max/RMS ULP against the fp64 oracle on sampled
+rows, the roofline of the dominant kernel, the oracle's own throughput on the
+host's cores, the eager two-GEMM torch chain as a comparator, and the same
+figures for the other two large LoRA workloads (`large_configs`).
 """
 from __future__ import annotations
 
@@ -28,20 +31,23 @@ if ROOT not in sys.path:
 METRIC = "fused LoRA-linear TFLOP/s & % MFMA peak (fp16/bf16); max ULP vs fp64 oracle"
 PEAK_TFLOPS = {1: 2500.0, 2: 2500.0, 3: 157.3}   # MI355X dense MFMA: fp16/bf16, fp32
 HBM_GBS = 8000.0
-DEFAULT = "lora_f16_4096x3072x3072_r16"
+# the largest single-GPU workload sets `value`; the other two large LoRA
+# workloads are reported beside it (`large_configs`)
+DEFAULT = "lora_bf16_16384x8192x8192_r128"
+LARGE = ("lora_f16_4096x3072x3072_r16", "lora_bf16x_f32w_8192x4096x4096_r64", "lora_bf16_16384x8192x8192_r128")
+BLOCKS = 15   # timed blocks (median and range), as in the Luminal page's protocol
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # the GPU's clocks take a few hundred steps of the fp16 r16 problem to settle
-    # (10 warm-up steps measure ~15% below the steady state)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-eager", action="store_true")
+    ap.add_argument("--no-large-configs", action="store_true", help="skip the other large LoRA workloads")
     ap.add_argument("--no-small-m", action="store_true", help="skip the small-M (decode-like) timings")
     ap.add_argument("--no-merge", action="store_true", help="skip the LoRA merge timing")
     ap.add_argument("--merge-only", action="store_true",
@@ -50,10 +56,10 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the LoRA-bypass backward timing")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the backward of the workload (profiling runs)")
-    ap.add_argument("--backward-steps", type=int, default=50)
+    ap.add_argument("--backward-steps", type=int, default=30)
     ap.add_argument("--no-dora", action="store_true", help="skip the DoRA timing")
     ap.add_argument("--dora-only", action="store_true", help="time only DoRA's norms and forward (profiling runs)")
-    ap.add_argument("--dora-steps", type=int, default=100)
+    ap.add_argument("--dora-steps", type=int, default=50)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (HBM counter calibration)")
     args = ap.parse_args()
@@ -62,49 +68,111 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    import lora_bypass_linear_amd as L
     import workloads as WL
 
     wl = WL.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     inputs = WL.generate(wl)
+    lora = wl.kind == "lora"
+
+    if args.merge_only or args.dora_only or args.backward_only:
+        if args.copy_calibration_mib > 0:
+            _copy_calibration(dev, args.copy_calibration_mib)
+        if args.merge_only:
+            r = {"merge": _merge(dev, wl, inputs, args.merge_steps, args.merge_steps, not args.no_cpu_baseline)}
+        elif args.dora_only:
+            r = {"dora": _dora(dev, wl, inputs, args.dora_steps, args.dora_steps, not args.no_cpu_baseline)}
+        else:
+            r = {"backward": _backward(dev, wl, inputs, args.backward_steps, args.backward_steps,
+                                       not args.no_cpu_baseline, not args.no_eager)}
+        print(json.dumps(dict(workload=wl.name, **r)))
+        return
+
+    if args.copy_calibration_mib > 0:
+        _copy_calibration(dev, args.copy_calibration_mib)
+    fb = _forward_bench(dev, wl, inputs, args.steps, args.warmup)
+    c_dt, y = fb.pop("_c_dt"), fb.pop("_y")
+    d = fb.pop("_d")
+    out = {"metric": METRIC, "value": fb["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": fb["ms_per_step"], "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": {1: "f16", 2: "bf16", 3: "f32"}[c_dt],
+           "data": "synthetic (seeded Philox draws, shapes and distributions of the workload)",
+           "config": {"workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K, "rank": wl.r, "scale": wl.scale,
+                      "x_dtype": WL.NAME[wl.x_dt], "w_dtype": WL.NAME[wl.w_dt],
+                      "bias": WL.NAME[wl.b_dt] if wl.b_dt else None, "accumulate": "f32",
+                      "parallelism": "single GPU"}}
+    out.update({k: v for k, v in fb.items() if k not in ("tflops", "ms_per_step")})
+
+    # accuracy on sampled rows against the fp64 oracle; the same oracle run,
+    # timed, is the CPU baseline (rank 0, one GPU)
+    rows = res = None
+    if not args.no_cpu_baseline:
+        acc, cpu, rows, res = _accuracy(wl, inputs, y, args.cpu_seconds, timed=True)
+        out.update(acc)
+        out["cpu_baseline"] = cpu
+        if not args.no_eager:
+            out["eager_baseline"] = _eager(d, wl, c_dt, rows, res, args.steps)
+    del y, d
+    if lora and not args.no_large_configs:
+        out["large_configs"] = {}
+        for name in LARGE:
+            if name == wl.name:
+                continue
+            w2 = WL.WORKLOADS[name]
+            in2 = WL.generate(w2)
+            f2 = _forward_bench(dev, w2, in2, args.steps, args.warmup)
+            c2, y2, d2 = f2.pop("_c_dt"), f2.pop("_y"), f2.pop("_d")
+            for k in ("input_digest", "instrumented_ms_per_step"):
+                f2.pop(k, None)
+            if not args.no_cpu_baseline:
+                acc2, _, rows2, res2 = _accuracy(w2, in2, y2, 4.0, timed=False)
+                f2.update(acc2)
+                if not args.no_eager:
+                    f2["eager_baseline"] = _eager(d2, w2, c2, rows2, res2, args.steps)
+            out["large_configs"][name] = f2
+            del y2, d2, in2
+            torch.cuda.empty_cache()
+
+    if not args.no_small_m:
+        out["small_m"] = _small_m(dev)
+    if lora and wl.r > 0 and not args.no_merge:
+        out["merge"] = _merge(dev, wl, inputs, args.merge_steps, 20, not args.no_cpu_baseline)
+    if lora and wl.r > 0 and not args.no_dora:
+        out["dora"] = _dora(dev, wl, inputs, args.dora_steps, 10, not args.no_cpu_baseline)
+    if lora and wl.r > 0 and not args.no_backward:
+        out["backward"] = _backward(dev, wl, inputs, args.backward_steps, 10, not args.no_cpu_baseline,
+                                    not args.no_eager)
+    print(json.dumps(out))
+
+
+def _forward_bench(dev, wl, inputs, steps, warmup):
+    """One workload's forward: W untimed steps, then K timed steps bracketed by
+    device synchronisation (wall clock: `tflops`, `ms_per_step`), split into
+    up to 15 blocks with events on the launch stream between them (median and
+    range per step); then the same K steps with a HIP event pair around every
+    kernel launch (per-kernel device durations; the dominant kernel's
+    roofline).  Returns a dict (plus the output and device inputs under
+    private keys)."""
+    import torch
+
+    import lora_bypass_linear_amd as L
+    import workloads as WL
+
     d = {k: v.to(dev) for k, v in inputs.items()}
     lora = wl.kind == "lora"
-    dts = [L.dtype_code(d["x"]), L.dtype_code(d["w"])] + ([L.dtype_code(d["b"])] if "b" in d else []) + \
+    b_dt = L.dtype_code(d["b"]) if "b" in d else 0
+    dts = [L.dtype_code(d["x"]), L.dtype_code(d["w"])] + ([b_dt] if b_dt else []) + \
           ([L.dtype_code(d["down"]), L.dtype_code(d["up"])] if lora else [])
     c_dt, o_dt = L.resolve_dtypes(dts)
     y = torch.empty((wl.M, wl.N), dtype=L.torch_dtype(o_dt), device=dev)
     if lora:
-        nws = L.lora_workspace_size(wl.M, wl.N, wl.K, wl.r, dts[0], dts[1], L.dtype_code(d["b"]) if "b" in d else 0,
-                                    L.dtype_code(d["down"]), L.dtype_code(d["up"]))
+        nws = L.lora_workspace_size(wl.M, wl.N, wl.K, wl.r, dts[0], dts[1], b_dt, L.dtype_code(d["down"]),
+                                    L.dtype_code(d["up"]))
     else:
-        nws = L.linear_workspace_size(wl.M, wl.N, wl.K, dts[0], dts[1], L.dtype_code(d["b"]) if "b" in d else 0)
+        nws = L.linear_workspace_size(wl.M, wl.N, wl.K, dts[0], dts[1], b_dt)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
-
-    if args.merge_only:
-        if args.copy_calibration_mib > 0:
-            _copy_calibration(dev, args.copy_calibration_mib)
-        print(json.dumps({"workload": wl.name, "merge": _merge(dev, wl, inputs, args.merge_steps, args.merge_steps,
-                                                                 not args.no_cpu_baseline)}))
-        return
-
-    if args.dora_only:
-        if args.copy_calibration_mib > 0:
-            _copy_calibration(dev, args.copy_calibration_mib)
-        print(json.dumps({"workload": wl.name, "dora": _dora(dev, wl, inputs, args.dora_steps, args.dora_steps,
-                                                               not args.no_cpu_baseline)}))
-        return
-
-    if args.backward_only:
-        if args.copy_calibration_mib > 0:
-            _copy_calibration(dev, args.copy_calibration_mib)
-        print(json.dumps({"workload": wl.name, "backward": _backward(dev, wl, inputs, args.backward_steps,
-                                                                       args.backward_steps, not args.no_cpu_baseline,
-                                                                       not args.no_eager)}))
-        return
 
     def step():
         if lora:
@@ -112,43 +180,47 @@ def main():
         else:
             L.linear(d["x"], d["w"], d.get("b"), out=y, workspace=ws)
 
-    if args.copy_calibration_mib > 0:
-        _copy_calibration(dev, args.copy_calibration_mib)
-
-    print(f"[bench] {wl.name}: warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
+    print(f"[bench] {wl.name}: warmup {warmup}", file=sys.stderr, flush=True)
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K whole steps, nothing else on the stream
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    # timed region: K whole steps, nothing else on the stream but the block events
+    nb = max(1, min(BLOCKS, steps))
+    sizes = [steps // nb + (1 if i < steps % nb else 0) for i in range(nb)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
+    print(f"[bench] timing {steps} steps in {nb} blocks", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    ev[0].record()
+    for i, n in enumerate(sizes):
+        for _ in range(n):
+            step()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    tflops = wl.flops / (ms_per_step * 1e-3) / 1e12
+    ms_per_step = wall * 1e3 / steps
+    per_block = sorted(ev[i].elapsed_time(ev[i + 1]) / sizes[i] for i in range(nb) if sizes[i] > 0)
+    med = per_block[len(per_block) // 2] if len(per_block) % 2 else \
+        0.5 * (per_block[len(per_block) // 2 - 1] + per_block[len(per_block) // 2])
 
     # the same K steps again with a HIP event pair around every kernel launch,
     # on the launch stream, for per-kernel device durations (the event records
-    # add gaps between kernels, so this region does not set `value`)
-    print(f"[bench] timing {args.steps} instrumented steps", file=sys.stderr, flush=True)
-    L.profile_begin(8 * args.steps)
+    # add gaps between kernels, so this region sets neither value nor blocks)
+    print(f"[bench] timing {steps} instrumented steps", file=sys.stderr, flush=True)
+    L.profile_begin(8 * steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
     wall_i = time.perf_counter() - t0
     prof = L.profile_end()
 
     # dominant kernel: the fused main contraction (fold + K loop + epilogue) of
-    # the LoRA path, or the exactly rounded projection of the plain affine path
-    # (both are recorded as the GEMM kind: the plain affine path's contraction
-    # is the exact-rounding kernel built from the h-pass sources)
-    dom = "gemm" if lora else "hpass"
+    # the LoRA path, or the plain affine path's contraction (recorded as the
+    # GEMM kind)
+    dom = "gemm" if lora else "affine"
     n_g, t_g = prof["gemm"]
     dom_ms = t_g / max(n_g, 1)
     dom_flops = 2.0 * wl.M * wl.N * wl.K + (2.0 * wl.M * wl.r * wl.N if lora else 0.0)
@@ -156,87 +228,89 @@ def main():
     peak = PEAK_TFLOPS[c_dt]
     from lora_bypass_linear_amd.profsum import read_traffic
     traffic = read_traffic(os.path.join(ROOT, "profiles", f"traffic_{dom}_{wl.name}.txt"), dom)
-    roofline = {"bound": "mfma", "kernel": {"gemm": "gemm_kernel", "hpass": "xr_kernel"}[dom],
-                "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+    tflops = wl.flops / (ms_per_step * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "gemm_kernel", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": None if traffic is None else int(traffic),
                 "flops_per_launch": dom_flops, "avg_us": round(dom_ms * 1e3, 3)}
     kernels = {k: {"launches": n, "avg_us": round(t * 1e3 / n, 3)} for k, (n, t) in prof.items() if n}
     guard = None
     if lora and wl.r > 0 and c_dt != L.F32:
-        _, _, fo = L.lora_workspace_layout(wl.M, wl.N, wl.K, wl.r, dts[0], dts[1],
-                                           L.dtype_code(d["b"]) if "b" in d else 0, L.dtype_code(d["down"]),
+        _, _, fo = L.lora_workspace_layout(wl.M, wl.N, wl.K, wl.r, dts[0], dts[1], b_dt, L.dtype_code(d["down"]),
                                            L.dtype_code(d["up"]))
         nflag = int(ws[fo: fo + 4].cpu().view(torch.int32).item())
         guard = {"h_reevaluated_fp64": nflag, "of": wl.M * wl.r, "fraction": round(nflag / (wl.M * wl.r), 6)}
+    elif not lora and c_dt != L.F32:
+        fo = L.linear_workspace_layout(wl.M, wl.N, wl.K, dts[0], dts[1], b_dt)
+        nflag = int(ws[fo: fo + 4].cpu().view(torch.int32).item())
+        guard = {"projection_reevaluated_fp64": nflag, "of": wl.M * wl.N,
+                 "fraction": round(nflag / (wl.M * wl.N), 6)}
+    return {"tflops": round(tflops, 2), "ms_per_step": round(ms_per_step, 5),
+            "blocks": {"n": nb, "steps_per_block": sizes, "median_ms_per_step": round(med, 5),
+                       "min_ms_per_step": round(per_block[0], 5), "max_ms_per_step": round(per_block[-1], 5),
+                       "median_tflops": round(wl.flops / (med * 1e-3) / 1e12, 2)},
+            "frac_of_peak": round(tflops / peak, 4), "hbm_gbs": round(wl.bytes / (ms_per_step * 1e-3) / 1e9, 1),
+            "instrumented_ms_per_step": round(wall_i * 1e3 / steps, 5), "input_digest": WL.digest(inputs),
+            "kernels": kernels, "h_guard": guard, "roofline": roofline,
+            "_c_dt": c_dt, "_y": y, "_d": d}
 
-    out = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
-           "scaling": "weak", "vs_baseline": None, "dtype": {1: "f16", 2: "bf16", 3: "f32"}[c_dt],
-           "data": "synthetic (seeded Philox draws, shapes and distributions of the workload)",
-           "config": {"workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K, "rank": wl.r, "scale": wl.scale,
-                      "x_dtype": WL.NAME[wl.x_dt], "w_dtype": WL.NAME[wl.w_dt],
-                      "bias": WL.NAME[wl.b_dt] if wl.b_dt else None, "accumulate": "f32",
-                      "parallelism": "single GPU"},
-           "frac_of_peak": round(tflops / peak, 4), "hbm_gbs": round(wl.bytes / (ms_per_step * 1e-3) / 1e9, 1),
-           "instrumented_ms_per_step": round(wall_i * 1e3 / args.steps, 5),
-           "input_digest": WL.digest(inputs), "kernels": kernels, "h_guard": guard, "roofline": roofline}
 
-    if not args.no_small_m:
-        out["small_m"] = _small_m(dev)
-    if lora and wl.r > 0 and not args.no_merge:
-        out["merge"] = _merge(dev, wl, inputs, args.merge_steps, 20, not args.no_cpu_baseline)
-    if lora and wl.r > 0 and not args.no_dora:
-        out["dora"] = _dora(dev, wl, inputs, args.dora_steps, 20, not args.no_cpu_baseline)
-    if lora and wl.r > 0 and not args.no_backward:
-        out["backward"] = _backward(dev, wl, inputs, args.backward_steps, 20, not args.no_cpu_baseline,
-                                    not args.no_eager)
+def _accuracy(wl, inputs, y, cpu_seconds, timed):
+    """Max/RMS ULP and the per-element tolerance on sampled output rows against
+    the fp64 oracle, which runs on every host CPU this process may use.  With
+    `timed`, the sample is sized from two timed probes (a call costs a fixed
+    part, widening every operand, plus a part per output row) to about
+    `cpu_seconds` of oracle work, and the oracle's throughput is returned as
+    the CPU baseline."""
+    import numpy as np
 
-    # accuracy on sampled rows against the fp64 oracle (this is also the CPU-baseline leg)
-    if not args.no_cpu_baseline:
-        import oracle
-        from tests.gpu_cases import oracle_forward, score
+    import oracle
+    import workloads as WL
+    from tests.gpu_cases import score
 
-        y_cpu = y.cpu()
-        cores = oracle.default_threads()
+    bits = {k: WL.raw_bits(v) for k, v in inputs.items()}
+    dt = {k: WL.dtype_code(v) for k, v in inputs.items()}
+    cores, aff, quota = oracle.host_cpus()
+
+    def run(rows):
+        return oracle.forward(bits["x"], dt["x"], bits["w"], dt["w"], bits.get("b"), dt.get("b"), bits.get("down"),
+                              dt.get("down"), bits.get("up"), dt.get("up"), scale=wl.scale, rows=rows,
+                              nthreads=cores, lora=wl.kind == "lora")
+
+    y_cpu = y.cpu()
+    rng = np.random.default_rng(wl.seed)
+    probe_rows = np.sort(rng.choice(wl.M, size=min(wl.M, 4 * cores), replace=False))
+    small = probe_rows[: max(1, probe_rows.size // 4)]
+    run(small)
+    t1 = time.perf_counter()
+    run(small)
+    t_small = time.perf_counter() - t1
+    t1 = time.perf_counter()
+    run(probe_rows)
+    t_big = time.perf_counter() - t1
+    per_row = max((t_big - t_small) / max(probe_rows.size - small.size, 1), 1e-6)
+    fixed = max(t_small - per_row * small.size, 0.0)
+    want_rows = max(cpu_seconds - fixed, per_row) / per_row
+    n_rows = int(min(wl.M, max(cores, want_rows)))
+    # a workload whose every row fits in the budget is passed over whole, several times
+    passes = int(max(1, min(20, round(cpu_seconds / (fixed + per_row * wl.M))))) if (timed and n_rows == wl.M) else 1
+    rows = np.sort(rng.choice(wl.M, size=n_rows, replace=False))
+    print(f"[bench] oracle on {n_rows} rows x {passes}, {cores} threads", file=sys.stderr, flush=True)
+    t1 = time.perf_counter()
+    for _ in range(passes):
+        res = run(rows)
+    t_cpu = time.perf_counter() - t1
+    s = score(y_cpu, res, rows, wl.K, wl.r)
+    acc = {"max_ulp": round(s["ulp_max"], 4), "rms_ulp": round(s["ulp_rms"], 4), "tol_fail": s["fail"],
+           "tol_checked": s["n"], "worst_err_over_tol": round(s["worst"], 4), "rows_checked": int(n_rows)}
+    cpu = None
+    if timed:
         row_flops = wl.flops / wl.M
-        rng = np.random.default_rng(wl.seed)
-        # size the sample from two timed probes of different sizes (after one
-        # warm call): a call costs a fixed part (widening every operand) plus a
-        # part per output row
-        probe_rows = np.sort(rng.choice(wl.M, size=min(wl.M, 4 * cores), replace=False))
-        small = probe_rows[: max(1, probe_rows.size // 4)]
-        oracle_forward(inputs, wl, rows=small)
-        t1 = time.perf_counter()
-        oracle_forward(inputs, wl, rows=small)
-        t_small = time.perf_counter() - t1
-        t1 = time.perf_counter()
-        oracle_forward(inputs, wl, rows=probe_rows)
-        t_big = time.perf_counter() - t1
-        per_row = max((t_big - t_small) / max(probe_rows.size - small.size, 1), 1e-6)
-        fixed = max(t_small - per_row * small.size, 0.0)
-        want_rows = max(args.cpu_seconds - fixed, per_row) / per_row
-        n_rows = int(min(wl.M, max(cores, want_rows)))
-        # a workload whose every row fits in the budget is passed over whole, several times
-        passes = int(max(1, min(20, round(args.cpu_seconds / (fixed + per_row * wl.M))))) if n_rows == wl.M else 1
-        rows = np.sort(rng.choice(wl.M, size=n_rows, replace=False))
-        print(f"[bench] oracle on {n_rows} rows x {passes}, {cores} threads", file=sys.stderr, flush=True)
-        t1 = time.perf_counter()
-        for _ in range(passes):
-            res = oracle_forward(inputs, wl, rows=rows)
-        t_cpu = time.perf_counter() - t1
-        s = score(y_cpu, res, rows, wl.K, wl.r)
-        out["max_ulp"] = round(s["ulp_max"], 4)
-        out["rms_ulp"] = round(s["ulp_rms"], 4)
-        out["tol_fail"] = s["fail"]
-        out["tol_checked"] = s["n"]
-        out["worst_err_over_tol"] = round(s["worst"], 4)
-        out["cpu_baseline"] = {"value": round(row_flops * n_rows * passes / t_cpu / 1e12, 6), "unit": "TFLOP/s",
-                               "cores": cores, "kind": "oracle",
-                               "sample": f"{n_rows} of {wl.M} output rows (all {wl.N} columns)"
-                                         + (f", {passes} passes" if passes > 1 else "") + f", {t_cpu:.1f} s"}
-        if not args.no_eager:
-            out["eager_baseline"] = _eager(d, wl, c_dt, o_dt, rows, res, args.steps, score)
-    print(json.dumps(out))
+        cpu = {"value": round(row_flops * n_rows * passes / t_cpu / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+               "cores_affinity": aff, "cpu_quota": quota, "kind": "oracle",
+               "sample": f"{n_rows} of {wl.M} output rows (all {wl.N} columns)"
+                         + (f", {passes} passes" if passes > 1 else "") + f", {t_cpu:.1f} s"}
+    return acc, cpu, rows, res
 
 
 def _copy_calibration(dev, mib):
@@ -575,23 +649,18 @@ def _small_m(dev, reps=50):
     return res
 
 
-def _oracle_args(inputs, wl):
-    import workloads as WL
-    bits = {k: WL.raw_bits(v) for k, v in inputs.items()}
-    dt = {k: WL.dtype_code(v) for k, v in inputs.items()}
-    return (bits["x"], dt["x"], bits["w"], dt["w"], bits.get("b"), dt.get("b"), bits.get("down"), dt.get("down"),
-            bits.get("up"), dt.get("up"), wl.scale)
-
-
-def _eager(d, wl, c_dt, o_dt, rows, res, steps, score):
-    """The unfused torch chain, each op rounding to the compute dtype (comparator only)."""
+def _eager(d, wl, c_dt, rows, res, steps):
+    """The unfused torch chain, each op rounding to the compute dtype, then cast
+    to the output dtype (comparator only): time per call and its ULP against
+    the fp64 oracle on the same sampled rows."""
     import torch
     import torch.nn.functional as F
 
     import lora_bypass_linear_amd as L
+    from tests.gpu_cases import score
 
     ct = L.torch_dtype(c_dt)
-    ot = L.torch_dtype(o_dt)
+    ot = L.torch_dtype(res["output"])
 
     def run():
         x = d["x"].to(ct)
@@ -599,15 +668,14 @@ def _eager(d, wl, c_dt, o_dt, rows, res, steps, score):
         if wl.kind == "lora":
             h = F.linear(x, d["down"].to(ct))
             yv = F.linear(x, w) + wl.scale * F.linear(h, d["up"].to(ct))
-            if "b" in d:
-                yv = yv + d["b"].to(ct)
         else:
             yv = F.linear(x, w)
-            if "b" in d:
-                yv = yv + d["b"].to(ct)
+        if "b" in d:
+            yv = yv + d["b"].to(ct)
         return yv.to(ot)
 
-    yv = run()
+    for _ in range(3):
+        yv = run()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     n = max(5, steps // 2)

@@ -143,6 +143,40 @@ def _stream(dev) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
+def _shape(t: Optional[torch.Tensor], shape, name: str) -> None:
+    """Raise ValueError unless t (if given) has exactly this shape.  The C ABI
+    takes bare pointers, so a mis-shaped operand would be read (or an output
+    written) out of bounds: every shape is checked here before any call."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(int(s) for s in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(int(s) for s in shape)}")
+
+
+def _dims(t: torch.Tensor, n: int, name: str) -> Tuple[int, ...]:
+    if t.dim() != n:
+        raise ValueError(f"{name} must be {n}-D, got shape {tuple(t.shape)}")
+    return tuple(t.shape)
+
+
+def _out_dtype(out: Optional[torch.Tensor], code: int, name: str = "out") -> None:
+    if out is not None and out.dtype != _TORCH[code]:
+        raise ValueError(f"{name} has dtype {out.dtype}, the dtype policy gives {_TORCH[code]}")
+
+
+def _lora_shapes(x, w, down, up, bias, out):
+    """(M, N, K, r) of a LoRA-bypass call, every operand's shape checked."""
+    M, K = _dims(x, 2, "x")
+    N, _ = _dims(w, 2, "w")
+    r, _ = _dims(down, 2, "down")
+    _shape(w, (N, K), "w")
+    _shape(down, (r, K), "down")
+    _shape(up, (N, r), "up")
+    _shape(bias, (N,), "bias")
+    _shape(out, (M, N), "out")
+    return M, N, K, r
+
+
 def _need_device(*ts):
     dev = None
     for t in ts:
@@ -152,6 +186,8 @@ def _need_device(*ts):
             raise ValueError("lyc operands must be GPU tensors")
         if not t.is_contiguous():
             raise ValueError("lyc operands must be contiguous")
+        if t.dtype not in _CODE and t.dtype != torch.uint8:
+            raise TypeError(f"unsupported dtype {t.dtype}")
         if dev is None:
             dev = t.device
         elif t.device != dev:
@@ -301,12 +337,16 @@ def _workspace(nbytes: int, dev, workspace: Optional[torch.Tensor]) -> Optional[
 def linear(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None,
            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y = round_out(round_out(x.W^T) + b) on the GPU (plain affine contract)."""
-    dev = _need_device(x, w, bias, out)
-    M, K = x.shape
-    N = w.shape[0]
+    M, K = _dims(x, 2, "x")
+    N, _ = _dims(w, 2, "w")
+    _shape(w, (N, K), "w")
+    _shape(bias, (N,), "bias")
+    _shape(out, (M, N), "out")
     x_dt, w_dt = dtype_code(x), dtype_code(w)
     b_dt = dtype_code(bias) if bias is not None else 0
     _, o_dt = resolve_dtypes([x_dt, w_dt] + ([b_dt] if b_dt else []))
+    _out_dtype(out, o_dt)
+    dev = _need_device(x, w, bias, out, workspace)
     if out is None:
         out = torch.empty((M, N), dtype=_TORCH[o_dt], device=dev)
     ws = _workspace(linear_workspace_size(M, N, K, x_dt, w_dt, b_dt), dev, workspace)
@@ -324,13 +364,12 @@ def lora_linear(x: torch.Tensor, w: torch.Tensor, down: torch.Tensor, up: torch.
     x [M,K], w [N,K], down [r,K], up [N,r], bias [N] (optional).  With
     ``return_workspace`` the workspace tensor is returned too (h_r and the
     guard counter live in it; see ``lora_workspace_layout``)."""
-    dev = _need_device(x, w, down, up, bias, out)
-    M, K = x.shape
-    N = w.shape[0]
-    r = down.shape[0]
+    M, N, K, r = _lora_shapes(x, w, down, up, bias, out)
     x_dt, w_dt, d_dt, u_dt = dtype_code(x), dtype_code(w), dtype_code(down), dtype_code(up)
     b_dt = dtype_code(bias) if bias is not None else 0
     _, o_dt = resolve_dtypes([x_dt, w_dt] + ([b_dt] if b_dt else []) + [d_dt, u_dt])
+    _out_dtype(out, o_dt)
+    dev = _need_device(x, w, down, up, bias, out, workspace)
     if out is None:
         out = torch.empty((M, N), dtype=_TORCH[o_dt], device=dev)
     ws = _workspace(lora_workspace_size(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt), dev, workspace)
@@ -347,11 +386,15 @@ def lora_merge(w: torch.Tensor, down: torch.Tensor, up: torch.Tensor, scale: flo
 
     w [N,K], down [r,K], up [N,r].  ``out`` may be ``w`` itself (in-place
     merge, when W already has the output dtype)."""
-    dev = _need_device(w, down, up, out)
-    N, K = w.shape
-    r = down.shape[0]
+    N, K = _dims(w, 2, "w")
+    r, _ = _dims(down, 2, "down")
+    _shape(down, (r, K), "down")
+    _shape(up, (N, r), "up")
+    _shape(out, (N, K), "out")
     w_dt, d_dt, u_dt = dtype_code(w), dtype_code(down), dtype_code(up)
     _, o_dt = resolve_dtypes([w_dt, d_dt, u_dt])
+    _out_dtype(out, o_dt)
+    dev = _need_device(w, down, up, out, workspace)
     if out is None:
         out = torch.empty((N, K), dtype=_TORCH[o_dt], device=dev)
     ws = _workspace(lora_merge_workspace_size(N, K, r, w_dt, d_dt, u_dt), dev, workspace)
@@ -368,10 +411,9 @@ def lora_linear_backward(x: torch.Tensor, w: torch.Tensor, down: torch.Tensor, u
     """Gradients (dx, d_down, d_up) of the LoRA-bypass linear for dy, each in
     its leaf's dtype (None where not wanted).  W and the bias are frozen;
     ``bias_dtype`` is the forward's bias dtype (it enters the dtype policy)."""
-    dev = _need_device(x, w, down, up, dy)
-    M, K = x.shape
-    N = w.shape[0]
-    r = down.shape[0]
+    M, N, K, r = _lora_shapes(x, w, down, up, None, None)
+    _shape(dy, (M, N), "dy")
+    dev = _need_device(x, w, down, up, dy, workspace)
     x_dt, w_dt, d_dt, u_dt, g_dt = (dtype_code(t) for t in (x, w, down, up, dy))
     b_dt = dtype_code(torch.empty(0, dtype=bias_dtype)) if bias_dtype is not None else 0
     want = (BWD_DX if want_dx else 0) | (BWD_DDOWN if want_ddown else 0) | (BWD_DUP if want_dup else 0)
@@ -395,13 +437,12 @@ def lora_linear_tune(x: torch.Tensor, w: torch.Tensor, down: torch.Tensor, up: t
     """Time the planner's shortlist for this forward (blocking) and keep the
     fastest for later calls of the same shape.  Returns (tile_n, tile_m,
     ksplit, ms, [ms of each shortlisted candidate, in gemm_plan order])."""
-    dev = _need_device(x, w, down, up, bias, out)
-    M, K = x.shape
-    N = w.shape[0]
-    r = down.shape[0]
+    M, N, K, r = _lora_shapes(x, w, down, up, bias, out)
     x_dt, w_dt, d_dt, u_dt = dtype_code(x), dtype_code(w), dtype_code(down), dtype_code(up)
     b_dt = dtype_code(bias) if bias is not None else 0
     _, o_dt = resolve_dtypes([x_dt, w_dt] + ([b_dt] if b_dt else []) + [d_dt, u_dt])
+    _out_dtype(out, o_dt)
+    dev = _need_device(x, w, down, up, bias, out, workspace)
     if out is None:
         out = torch.empty((M, N), dtype=_TORCH[o_dt], device=dev)
     ws = _workspace(lora_workspace_size(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt), dev, workspace)
@@ -420,9 +461,13 @@ def lora_linear_tune(x: torch.Tensor, w: torch.Tensor, down: torch.Tensor, up: t
 def dora_norms(w: torch.Tensor, down: torch.Tensor, up: torch.Tensor, scale: float,
                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """DoRA row norms ||W + scale * up_c.down_c||_2 per row of W [N,K], fp32 [N]."""
-    dev = _need_device(w, down, up, out)
-    N, K = w.shape
-    r = down.shape[0]
+    N, K = _dims(w, 2, "w")
+    r, _ = _dims(down, 2, "down")
+    _shape(down, (r, K), "down")
+    _shape(up, (N, r), "up")
+    _shape(out, (N,), "out")
+    _out_dtype(out, F32)
+    dev = _need_device(w, down, up, out, workspace)
     w_dt, d_dt, u_dt = dtype_code(w), dtype_code(down), dtype_code(up)
     if out is None:
         out = torch.empty(N, dtype=torch.float32, device=dev)
@@ -439,15 +484,16 @@ def dora_linear(x: torch.Tensor, w: torch.Tensor, down: torch.Tensor, up: torch.
                 magnitude: torch.Tensor, norms: torch.Tensor, bias: Optional[torch.Tensor] = None,
                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y = round_out((m/norm) * (x.W^T + scale * round_c(x.down^T).up^T) + b) on the GPU."""
-    dev = _need_device(x, w, down, up, magnitude, norms, bias, out)
+    M, N, K, r = _lora_shapes(x, w, down, up, bias, out)
+    _shape(magnitude, (N,), "magnitude")
+    _shape(norms, (N,), "norms")
     if norms.dtype != torch.float32:
         raise ValueError("DoRA norms are fp32")
-    M, K = x.shape
-    N = w.shape[0]
-    r = down.shape[0]
     x_dt, w_dt, d_dt, u_dt, m_dt = (dtype_code(t) for t in (x, w, down, up, magnitude))
     b_dt = dtype_code(bias) if bias is not None else 0
     _, o_dt = resolve_dtypes([x_dt, w_dt] + ([b_dt] if b_dt else []) + [d_dt, u_dt, m_dt])
+    _out_dtype(out, o_dt)
+    dev = _need_device(x, w, down, up, magnitude, norms, bias, out, workspace)
     if out is None:
         out = torch.empty((M, N), dtype=_TORCH[o_dt], device=dev)
     n = ctypes.c_size_t(0)

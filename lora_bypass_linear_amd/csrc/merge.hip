@@ -39,19 +39,22 @@ static_assert((MT + MC) * 128 <= LDS, "operand chunk fits the exchange buffer");
 // chunk c of the A side is rank rows 64c .. 64c+63 of down [rank][K] over the
 // tile's 128 k columns, kept as a contraction-major tile (256-byte rows,
 // 16-byte chunks permuted by tswz) for the transposing LDS read; rows past the
-// rank and columns past K fall outside the range and read 0.  The B side reads
-// up [N][rank] rows with their own stride rowb_u (rank elements).
+// rank and columns past K are sent out of range explicitly (no offset is
+// formed for them, so none can wrap back into down) and read 0.  The B side
+// reads up [N][rank] rows with their own stride rowb_u (rank elements).
 template <bool RAW>
 __device__ __forceinline__ void merge_chunk_loads(i32x4 (&st)[8], __amdgpu_buffer_rsrc_t ra,
                                                   __amdgpu_buffer_rsrc_t rb, int c, uint32_t rowb, int orow,
-                                                  int okc, int tid, int64_t K, int64_t k0, uint32_t rowb_u) {
+                                                  int okc, int tid, int64_t K, int64_t k0, uint32_t rowb_u,
+                                                  int64_t rank) {
     const uint32_t byte = (uint32_t)c * 128 + okc * 16;
     if constexpr (RAW) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int i = q * 256 + tid, r = i >> 4, s = i & 15;
             const int64_t k = k0 + 8 * (s ^ tswz<16>(r));
-            st[q] = buf_load16(ra, k < K ? (uint32_t)(((int64_t)(64 * c + r) * K + k) * 2) : OOB);
+            const int64_t rr = 64 * c + r;
+            st[q] = buf_load16(ra, (rr < rank && k < K) ? (uint32_t)((rr * K + k) * 2) : OOB);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(256, (WF || !VEC) ? 2 : 3) void merge_kernel(MergeP
     // (unconditional: without a rank every offset is out of range and reads 0;
     // a branch here would cost the exact wait counts below)
     i32x4 st[8];
-    merge_chunk_loads<RAW>(st, ra, rb, 0, rowb, orow, okc, tid, p.K, k0, rowb_u);
+    merge_chunk_loads<RAW>(st, ra, rb, 0, rowb, orow, okc, tid, p.K, k0, rowb_u, p.rank);
 
     // 1b. the W tile, behind the operand chunk in the memory queue.  VEC: K
     //     is a multiple of E and the rows are aligned, so a lane's chunk is
@@ -190,7 +193,7 @@ __global__ __launch_bounds__(256, (WF || !VEC) ? 2 : 3) void merge_kernel(MergeP
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     merge_chunk_mma<CT, RAW>(smem, st, acc, 0, rowb, orow, okc, lane, wn, wk, tid);
     for (int c = 1; c < nchunk; ++c) {
-        merge_chunk_loads<RAW>(st, ra, rb, c, rowb, orow, okc, tid, p.K, k0, rowb_u);
+        merge_chunk_loads<RAW>(st, ra, rb, c, rowb, orow, okc, tid, p.K, k0, rowb_u, p.rank);
         lds_barrier();   // every wave is done reading the previous chunk
         merge_chunk_mma<CT, RAW>(smem, st, acc, c, rowb, orow, okc, lane, wn, wk, tid);
     }

@@ -95,12 +95,30 @@ def _ptr(a: Optional[np.ndarray]):
 
 
 def default_threads() -> int:
-    """Host threads for the oracle: the CPUs this process may run on, at most 16."""
+    """Host threads for the oracle in the test suite: the CPUs this process may
+    run on, at most 16."""
+    return max(1, min(16, host_cpus()[0]))
+
+
+def host_cpus():
+    """(usable, affinity, quota): the CPUs this process may run on
+    (sched_getaffinity), the cgroup CPU quota when one is set (cpu.max, in
+    CPUs, else None), and their minimum -- every host core the process can
+    actually use, which is what the benchmark's oracle baseline runs on."""
     try:
-        n = len(os.sched_getaffinity(0))
+        aff = len(os.sched_getaffinity(0))
     except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
+        aff = os.cpu_count() or 1
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, p = f.read().split()[:2]
+        if q != "max" and int(p) > 0:
+            quota = max(1, int(int(q) // int(p)))
+    except (OSError, ValueError):
+        quota = None
+    usable = aff if quota is None else max(1, min(aff, quota))
+    return usable, aff, quota
 
 
 def storage_np(dt: int):

@@ -8,6 +8,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import lora_bypass_linear_amd as L
 import oracle
@@ -273,3 +274,64 @@ def test_dora_argument_errors():
     assert f(y_dt=3) == L.ERR_DTYPE_MISMATCH
     assert f(nm=V(4098)) == L.ERR_UNSUPPORTED
     assert f() == L.ERR_WORKSPACE
+
+
+# ---- the binding checks every operand's shape (and out's dtype) before any call -----
+
+def _t(*shape, dt=torch.float16):
+    return torch.zeros(shape, dtype=dt)
+
+
+@pytest.mark.parametrize("case", [
+    dict(w=(64, 40)),            # W's K differs from x's
+    dict(down=(8, 40)),          # down's K
+    dict(up=(8, 64)),            # up passed as [r, N]
+    dict(up=(64, 4)),            # up's rank differs from down's
+    dict(bias=(63,)),            # bias length
+    dict(out=(32, 63)),          # out shape
+    dict(x=(32, 48, 1)),         # x not 2-D
+])
+def test_binding_rejects_misshaped_lora_operands(case):
+    shapes = dict(x=(32, 48), w=(64, 48), down=(8, 48), up=(64, 8), bias=(64,), out=(32, 64))
+    shapes.update(case)
+    ts = {k: _t(*v) for k, v in shapes.items()}
+    with pytest.raises(ValueError, match="shape|-D"):
+        L.lora_linear(ts["x"], ts["w"], ts["down"], ts["up"], 1.0, ts["bias"], out=ts["out"])
+    if "bias" not in case and "out" not in case:
+        with pytest.raises(ValueError, match="shape|-D"):
+            L.lora_linear_backward(ts["x"], ts["w"], ts["down"], ts["up"], 1.0, _t(32, 64))
+        with pytest.raises(ValueError, match="shape|-D"):
+            L.dora_linear(ts["x"], ts["w"], ts["down"], ts["up"], 1.0, _t(64), _t(64, dt=torch.float32))
+
+
+def test_binding_rejects_misshaped_other_operands():
+    x, w = _t(32, 48), _t(64, 48)
+    with pytest.raises(ValueError, match="shape"):
+        L.linear(x, _t(64, 40))
+    with pytest.raises(ValueError, match="shape"):
+        L.linear(x, w, _t(60))
+    with pytest.raises(ValueError, match="shape"):
+        L.linear(x, w, out=_t(32, 60))
+    with pytest.raises(ValueError, match="dtype"):
+        L.linear(x, w, out=_t(32, 64, dt=torch.bfloat16))                 # the policy gives fp16
+    with pytest.raises(ValueError, match="shape"):
+        L.lora_merge(w, _t(8, 40), _t(64, 8), 1.0)
+    with pytest.raises(ValueError, match="shape"):
+        L.lora_merge(w, _t(8, 48), _t(8, 64), 1.0)
+    with pytest.raises(ValueError, match="shape"):
+        L.lora_merge(w, _t(8, 48), _t(64, 8), 1.0, out=_t(48, 64))              # in-place view of the wrong shape
+    with pytest.raises(ValueError, match="dtype"):
+        L.lora_merge(w, _t(8, 48), _t(64, 8), 1.0, out=_t(64, 48, dt=torch.float32))
+    with pytest.raises(ValueError, match="shape"):
+        L.lora_linear_backward(x, w, _t(8, 48), _t(64, 8), 1.0, _t(64, 32))   # dy transposed
+    with pytest.raises(ValueError, match="shape"):
+        L.dora_norms(w, _t(8, 48), _t(64, 8), 1.0, out=_t(63, dt=torch.float32))
+    with pytest.raises(ValueError, match="dtype"):
+        L.dora_norms(w, _t(8, 48), _t(64, 8), 1.0, out=_t(64))
+    with pytest.raises(ValueError, match="shape"):
+        L.dora_linear(x, w, _t(8, 48), _t(64, 8), 1.0, _t(60), _t(64, dt=torch.float32))
+    with pytest.raises(ValueError, match="shape"):
+        L.lora_linear_tune(x, w, _t(8, 48), _t(8, 64), 1.0)
+    # well-shaped CPU operands get past the shape checks and are refused as host memory
+    with pytest.raises(ValueError, match="GPU"):
+        L.lora_linear(x, w, _t(8, 48), _t(64, 8), 1.0, _t(64))

@@ -224,12 +224,25 @@ def test_unaligned_output_rows():
     assert buf[0].item() == 0
 
 
-def test_deterministic():
-    wl = BASE["lora_bf16_16384x8192x8192_r128"].resized(M=300, N=400, K=520)
+@pytest.mark.parametrize("name,dims,ksplit", [
+    ("lora_bf16_16384x8192x8192_r128", dict(M=300, N=400, K=520), 2),   # 64x64 tiles, K split 2
+    ("lora_f16_4096x3072x3072_r16", dict(M=16), 5),                       # decode-sized M, K split 5
+])
+def test_deterministic(name, dims, ksplit):
+    """Bitwise-identical results on repeated calls, also where the GEMM splits
+    K over several workgroups (fp32 partial sums reduced in split order by a
+    second kernel) and where the h pass's guard appends elements to its work
+    list with LDS atomics (each listed element is re-evaluated on its own, so
+    the list's order does not reach the result)."""
+    wl = BASE[name].resized(**dims)
+    c_dt = L.resolve_dtypes([wl.x_dt, wl.w_dt] + ([wl.b_dt] if wl.b_dt else []) + [wl.w_dt, wl.w_dt])[0]
+    r_pad = 16 if wl.r <= 16 else 128
+    assert L.gemm_plan(wl.M, wl.N, wl.K, r_pad, c_dt)[0][2] == ksplit
     inputs = WL.generate(wl)
-    y1, h1, _ = gpu_forward(inputs, wl)
-    y2, h2, _ = gpu_forward(inputs, wl)
-    assert torch.equal(y1, y2) and np.array_equal(h1, h2)
+    y1, h1, f1 = gpu_forward(inputs, wl)
+    for _ in range(2):
+        y2, h2, f2 = gpu_forward(inputs, wl)
+        assert torch.equal(y1, y2) and np.array_equal(h1, h2) and f1 == f2
 
 
 def test_h_guard_resolves_midpoints():
