@@ -61,7 +61,8 @@ enum {
     LYC_ERR_UNSUPPORTED = 4,    /* K not a multiple of 8, misaligned x/W, rank > 256, sizes too large */
     LYC_ERR_HIP = 5,            /* the HIP runtime refused a launch */
     LYC_ERR_WORKSPACE = 6,      /* workspace missing, too small or not 256-byte aligned */
-    LYC_ERR_IO = 7              /* tuning table file could not be read, parsed or written */
+    LYC_ERR_IO = 7,             /* tuning table file could not be read, parsed or written */
+    LYC_ERR_SCRATCH = 8         /* the problem needs more scratch than lyc_lora_linear_fwd_noalloc holds */
 };
 
 /*
@@ -127,6 +128,34 @@ int lyc_lora_linear_fwd(const void* x, int x_dt, const void* w, int w_dt, const 
                         const void* down, int down_dt, const void* up, int up_dt, int64_t rank, double scale,
                         void* y, int y_dt, int64_t M, int64_t N, int64_t K,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The LoRA-bypass forward for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, checks, kernels and results as
+ * lyc_lora_linear_fwd, without the workspace: the scratch the kernels need
+ * (the size lyc_lora_linear_workspace_size reports) lives in a static device
+ * array of LYC_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it
+ * runs on, from the first call on that GPU until the process ends.
+ *   - Allocates nothing: no hipMalloc, hipFree or allocating library routine.
+ *     The caller still passes x, w, down, up, bias and y.  The first call on a
+ *     GPU looks up the array's device address (hipGetSymbolAddress, with that
+ *     GPU current, the caller's current device restored after).
+ *   - Problems whose scratch need exceeds LYC_NOALLOC_SCRATCH_BYTES are
+ *     refused with LYC_ERR_SCRATCH before any GPU work.
+ *   - Every call on a GPU shares that GPU's array and leaves its contents
+ *     behind; each call clears what must start at zero (the guard counter)
+ *     with a kernel of its own.  Calls that overlap on one GPU (other streams,
+ *     other host threads) race on the array: serialise them.
+ *   - stream: the array of the stream's device is used (NULL: the current
+ *     device's).
+ * Returns the codes of lyc_lora_linear_fwd, LYC_ERR_SCRATCH, or LYC_ERR_HIP
+ * when the array's address cannot be looked up.
+ */
+#define LYC_NOALLOC_SCRATCH_BYTES (64u << 20)
+int lyc_lora_linear_fwd_noalloc(const void* x, int x_dt, const void* w, int w_dt, const void* bias, int bias_dt,
+                                const void* down, int down_dt, const void* up, int up_dt, int64_t rank, double scale,
+                                void* y, int y_dt, int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * Where lyc_lora_linear_fwd leaves its intermediate results inside the

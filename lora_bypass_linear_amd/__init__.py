@@ -14,14 +14,16 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 __all__ = ["F16", "BF16", "F32", "LycError", "MixedHalfError", "lib", "resolve_dtypes", "linear", "lora_linear",
-           "lora_merge", "lora_linear_backward", "dora_norms", "dora_linear", "linear_workspace_size", "lora_workspace_size", "lora_workspace_layout",
+           "lora_linear_noalloc", "lora_merge", "lora_linear_backward", "dora_norms", "dora_linear", "linear_workspace_size", "lora_workspace_size", "lora_workspace_layout",
            "linear_workspace_layout", "lora_merge_workspace_size", "lora_bwd_workspace_size",
            "lora_bwd_workspace_layout", "gemm_tile", "gemm_plan", "lora_linear_tune", "tuning_save",
            "tuning_load", "tuning_clear", "tuning_count", "tuning_key", "tuning_lookup", "tuning_cache_path", "profile_begin", "profile_end",
            "dtype_code", "torch_dtype"]
 
 F16, BF16, F32 = 1, 2, 3
-OK, ERR_MIXED_HALF, ERR_INVALID_ARG, ERR_DTYPE_MISMATCH, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE, ERR_IO = range(8)
+OK, ERR_MIXED_HALF, ERR_INVALID_ARG, ERR_DTYPE_MISMATCH, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE, ERR_IO, ERR_SCRATCH = range(9)
+# the static device array of lyc_lora_linear_fwd_noalloc (LYC_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblyc.so")
@@ -57,6 +59,8 @@ def lib():
                                                      ctypes.POINTER(c_sz)]
         L.lyc_lora_linear_fwd.argtypes = [c_vp, c_int, c_vp, c_int, c_vp, c_int, c_vp, c_int, c_vp, c_int, c_i64,
                                           ctypes.c_double, c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_sz, c_vp]
+        L.lyc_lora_linear_fwd_noalloc.argtypes = [c_vp, c_int, c_vp, c_int, c_vp, c_int, c_vp, c_int, c_vp, c_int,
+                                                  c_i64, ctypes.c_double, c_vp, c_int, c_i64, c_i64, c_i64, c_vp]
         L.lyc_lora_workspace_layout.argtypes = [c_i64, c_i64, c_i64, c_i64, c_int, c_int, c_int, c_int, c_int,
                                                 ctypes.POINTER(c_sz), ctypes.POINTER(c_i64), ctypes.POINTER(c_sz)]
         L.lyc_linear_workspace_layout.argtypes = [c_i64, c_i64, c_i64, c_int, c_int, c_int, ctypes.POINTER(c_sz)]
@@ -98,7 +102,8 @@ def lib():
         L.lyc_status_str.argtypes = [c_int]
         L.lyc_status_str.restype = ctypes.c_char_p
         for fn in (L.lyc_resolve_dtypes, L.lyc_linear_workspace_size, L.lyc_linear_fwd,
-                   L.lyc_lora_linear_workspace_size, L.lyc_lora_linear_fwd, L.lyc_lora_workspace_layout,
+                   L.lyc_lora_linear_workspace_size, L.lyc_lora_linear_fwd, L.lyc_lora_linear_fwd_noalloc,
+                   L.lyc_lora_workspace_layout,
                    L.lyc_linear_workspace_layout, L.lyc_lora_merge_workspace_size, L.lyc_lora_merge_fwd,
                    L.lyc_lora_linear_bwd_workspace_size, L.lyc_lora_linear_bwd, L.lyc_lora_linear_bwd_workspace_layout,
                    L.lyc_gemm_plan, L.lyc_lora_linear_tune, L.lyc_tuning_key, L.lyc_tuning_lookup, L.lyc_tuning_save,
@@ -378,6 +383,26 @@ def lora_linear(x: torch.Tensor, w: torch.Tensor, down: torch.Tensor, up: torch.
                                      u_dt, r, float(scale), _ptr(out), dtype_code(out), M, N, K, _ptr(ws), nbytes,
                                      _stream(dev)))
     return (out, ws) if return_workspace else out
+
+
+def lora_linear_noalloc(x: torch.Tensor, w: torch.Tensor, down: torch.Tensor, up: torch.Tensor, scale: float,
+                        bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """lora_linear through the allocation-free entry point: the library's
+    kernels use its static per-GPU scratch array instead of a workspace (for
+    callers that cannot allocate device memory; pass ``out`` to allocate
+    nothing here either).  Calls that overlap on one GPU race on that array."""
+    M, N, K, r = _lora_shapes(x, w, down, up, bias, out)
+    x_dt, w_dt, d_dt, u_dt = dtype_code(x), dtype_code(w), dtype_code(down), dtype_code(up)
+    b_dt = dtype_code(bias) if bias is not None else 0
+    _, o_dt = resolve_dtypes([x_dt, w_dt] + ([b_dt] if b_dt else []) + [d_dt, u_dt])
+    _out_dtype(out, o_dt)
+    dev = _need_device(x, w, down, up, bias, out)
+    if out is None:
+        out = torch.empty((M, N), dtype=_TORCH[o_dt], device=dev)
+    _check(lib().lyc_lora_linear_fwd_noalloc(_ptr(x), x_dt, _ptr(w), w_dt, _ptr(bias), b_dt, _ptr(down), d_dt,
+                                             _ptr(up), u_dt, r, float(scale), _ptr(out), dtype_code(out), M, N, K,
+                                             _stream(dev)))
+    return out
 
 
 def lora_merge(w: torch.Tensor, down: torch.Tensor, up: torch.Tensor, scale: float,

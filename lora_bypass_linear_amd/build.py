@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liblyc.so")
-SRCS = ["csrc/api.cpp", "csrc/gemm.hip", "csrc/hpass.hip", "csrc/prep.hip", "csrc/merge.hip", "csrc/bwd.hip", "csrc/tune.cpp"]
+SRCS = ["csrc/api.cpp", "csrc/gemm.hip", "csrc/hpass.hip", "csrc/prep.hip", "csrc/merge.hip", "csrc/bwd.hip", "csrc/tune.cpp", "csrc/noalloc.hip"]
 ARCH = "gfx950"
 
 

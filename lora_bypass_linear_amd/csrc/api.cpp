@@ -1182,6 +1182,7 @@ const char* lyc_status_str(int status) {
     case LYC_ERR_HIP: return "HIP runtime error while launching";
     case LYC_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     case LYC_ERR_IO: return "tuning table file could not be read, parsed or written";
+    case LYC_ERR_SCRATCH: return "the problem needs more scratch than the allocation-free forward holds";
     default: return "unknown status";
     }
 }

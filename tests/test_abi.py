@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = L.lib()
-    for s in range(8):
+    for s in range(9):
         assert lib.lyc_status_str(s) != b"unknown status"
     assert lib.lyc_status_str(99) == b"unknown status"
 
@@ -335,3 +335,23 @@ def test_binding_rejects_misshaped_other_operands():
     # well-shaped CPU operands get past the shape checks and are refused as host memory
     with pytest.raises(ValueError, match="GPU"):
         L.lora_linear(x, w, _t(8, 48), _t(64, 8), 1.0, _t(64))
+
+
+def test_noalloc_refuses_before_any_gpu_call():
+    """The allocation-free forward checks the problem and its scratch need
+    before it touches the GPU (fake pointers: nothing is dereferenced)."""
+    lib = L.lib()
+    call = lambda **kw: lib.lyc_lora_linear_fwd_noalloc(*[{**dict(
+        x=P, x_dt=1, w=P, w_dt=1, b=None, b_dt=0, d=P, d_dt=1, u=P, u_dt=1, r=16, scale=ctypes.c_double(1.0), y=P,
+        y_dt=1, M=64, N=64, K=64, s=None), **kw}[k] for k in ("x", "x_dt", "w", "w_dt", "b", "b_dt", "d", "d_dt", "u",
+                                                              "u_dt", "r", "scale", "y", "y_dt", "M", "N", "K", "s")])
+    assert call(w_dt=2) == L.ERR_MIXED_HALF
+    assert call(K=12) == L.ERR_UNSUPPORTED
+    assert call(r=-1) == L.ERR_INVALID_ARG
+    # scratch need beyond the static array: bf16 x with fp32 weights keeps a bf16 copy of W (128 MiB here)
+    need = L.lora_workspace_size(16384, 8192, 8192, 128, 2, 3, 0, 3, 3)
+    assert need > L.NOALLOC_SCRATCH_BYTES
+    assert call(M=16384, N=8192, K=8192, r=128, x_dt=2, w_dt=3, d_dt=3, u_dt=3, y_dt=3) == L.ERR_SCRATCH
+    assert b"allocation-free" in lib.lyc_status_str(L.ERR_SCRATCH)
+    # the largest workload's need fits
+    assert L.lora_workspace_size(16384, 8192, 8192, 128, 2, 2, 2, 2, 2) <= L.NOALLOC_SCRATCH_BYTES
