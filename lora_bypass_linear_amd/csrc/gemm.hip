@@ -506,6 +506,10 @@ static int pick_tile(int64_t M, int64_t N, bool f32) {
     return best;
 }
 
+// The fp32 partial sums of a K split ([ksplit][M][N]) stay below this: splits
+// pay off only where few output tiles leave CUs idle, i.e. at small M * N.
+constexpr double KSPLIT_PARTIAL_MAX = 32.0 * 1024 * 1024;
+
 int gemm_ksplit(int64_t M, int64_t N, int64_t K, int c_dt) {
     int tn, tm;
     gemm_tile_shape(M, N, c_dt, &tn, &tm);
@@ -516,6 +520,7 @@ int gemm_ksplit(int64_t M, int64_t N, int64_t K, int c_dt) {
     int64_t ks = 256 / tiles;
     if (ks > ksteps / 4) ks = ksteps / 4;
     if (ks > 8) ks = 8;
+    while (ks > 1 && (double)M * (double)N * 4.0 * (double)ks > KSPLIT_PARTIAL_MAX) --ks;
     return ks > 1 ? (int)ks : 1;
 }
 
@@ -570,7 +575,9 @@ int gemm_plan(int64_t M, int64_t N, int64_t K, int64_t rf, int c_dt, GemmCand* o
         if (ts[i].id == t0) pen0 = ts[i].pen;
         const double tiles = (double)((N + tn - 1) / tn) * (double)((M + tm - 1) / tm);
         for (int ks = 1; ks <= 8; ks *= 2) {
-            if (ks > 1 && (tiles >= 256 || ks > ksteps / 4)) continue;
+            if (ks > 1 && (tiles >= 256 || ks > ksteps / 4 ||
+                           (double)M * (double)N * 4.0 * (double)ks > KSPLIT_PARTIAL_MAX))
+                continue;
             all[n++] = GemmCand{ts[i].id, ks, cost(ts[i].id, ks, ts[i].pen)};
         }
     }
