@@ -284,6 +284,78 @@ __device__ __forceinline__ void k_step(const Steps<TL, TA, TB>& S, char* smem, i
     mma_spread<CT, TL, TL::Q, ND>(f1a, f1b, acc);
 }
 
+// One main K step (operands as the forward stores them) with its memory work
+// interleaved by hand.  Substep 1's MFMAs are cut into G groups of FN/G
+// A-side blocks.  The first group is issued before the wait and the barrier
+// (it needs only registers, so the matrix pipe has work while the waves
+// meet); the loads of step kt+NS and the fragment reads of step kt+1 then go
+// between the remaining groups, fenced by scheduling barriers.  (Left to the
+// scheduler, the eight loads were issued back to back after the barrier with
+// the matrix pipe idle: the GEMM took 4-5% longer.)
+template <class CT, class TL>
+__device__ __forceinline__ void k_step_main(const Steps<TL>& S, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                            char* smem, int kt, i32x4 (&f0a)[TL::FN], i32x4 (&f0b)[TL::FM],
+                                            i32x4 (&f1a)[TL::FN], i32x4 (&f1b)[TL::FM], f32x4 (&acc)[TL::FN][TL::FM],
+                                            int wave, int lane, int wn, int wm) {
+    constexpr int ND = TL::FN + TL::FM;
+    constexpr int G = TL::FN % 4 == 0 ? 4 : (TL::FN % 3 == 0 ? 3 : 2), FNG = TL::FN / G;
+    static_assert(TL::FN % G == 0, "MFMA groups");
+    using LD = Loader<TL>;
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    read_frags<TL>(smem + (kt % TL::NS) * TL::STAGE, 1, f1a, f1b, lane, wn, wm);
+    mma_spread<CT, TL, 0, ND>(f0a, f0b, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+#pragma unroll
+    for (int i = 0; i < FNG; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::FM; ++j) acc[i][j] = CT::step(f1a[i], f1b[j], acc[i][j]);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<(TL::NS - 2) * TL::Q>();
+    lds_barrier();
+    // step kt+NS into the stage just consumed (out of range past the end)
+    const int s = kt + TL::NS;
+    char* st = smem + (s % TL::NS) * TL::STAGE;
+    const uint32_t row_bytes = s < S.KT ? S.kbytes : 0u;
+    const uint32_t kb0 = (uint32_t)(s - S.RF + S.k0) * TL::BKB;
+    const bool ok = kb0 + TL::BKB <= row_bytes || kb0 + LD::chunk16(lane) < row_bytes;
+    const char* nx = smem + ((kt + 1) % TL::NS) * TL::STAGE;
+    const int kc = lane >> 4;
+#pragma unroll
+    for (int g = 1; g < G; ++g) {
+        // loads: the A side with groups 1-2, the B side with group 3 (and the rest)
+#pragma unroll
+        for (int q = 0; q < LD::QA + LD::QB; ++q) {
+            const int grp = 1 + (q * (G - 1)) / (LD::QA + LD::QB);
+            if (grp != g) continue;
+            if (q < LD::QA) {
+                const uint32_t v = ok ? S.lm.va + (uint32_t)q * S.lm.sa : OOB;
+                auto* dst = (__attribute__((address_space(3))) void*)(st + (wave + q * TL::NW) * 1024);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, v, (int)kb0, 0, 0);
+            } else {
+                const int qb = q - LD::QA;
+                const uint32_t v = ok ? S.lm.vb + (uint32_t)qb * S.lm.sb : OOB;
+                auto* dst = (__attribute__((address_space(3))) void*)(st + (wave + q * TL::NW) * 1024);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, v, (int)kb0, 0, 0);
+            }
+        }
+        // fragment reads of step kt+1, substep 0 (spread over the groups)
+#pragma unroll
+        for (int i = 0; i < TL::FN; ++i)
+            if (i * (G - 1) / TL::FN + 1 == g)
+                f0a[i] = *(const i32x4*)(nx + lds_at<TL>(wn * TL::WN + i * 16 + (lane & 15), kc));
+#pragma unroll
+        for (int j = 0; j < TL::FM; ++j)
+            if (j * (G - 1) / TL::FM + 1 == g)
+                f0b[j] = *(const i32x4*)(nx + TL::TN * TL::BKB + lds_at<TL>(wm * TL::WM + j * 16 + (lane & 15), kc));
+#pragma unroll
+        for (int i = g * FNG; i < (g + 1) * FNG; ++i)
+#pragma unroll
+            for (int j = 0; j < TL::FM; ++j) acc[i][j] = CT::step(f1a[i], f1b[j], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // GAIN: a per-output-feature factor gain[n] in place of post (an instance of
 // its own, so the others carry no registers for it)
 // TA / TB: the A / B operand stored with the contraction index as rows
@@ -291,7 +363,12 @@ __device__ __forceinline__ void k_step(const Steps<TL, TA, TB>& S, char* smem, i
 // operands as the forward stores them.
 template <class CT, class TL, bool GAIN, bool TA = false, bool TB = false>
 __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles_n, int tiles_m, int group_m) {
-    __shared__ __attribute__((aligned(16))) char smem[TL::NS * TL::STAGE];
+    // the operand stages, then the tile's bias widened to fp32.  One LDS
+    // object: with a second __shared__ array the compiler could no longer
+    // tell the direct-to-LDS loads from the fragment reads and waited for
+    // every load right after issuing it.
+    __shared__ __attribute__((aligned(16))) char smem[TL::NS * TL::STAGE + TL::TN * 4];
+    float* sbias = (float*)(smem + TL::NS * TL::STAGE);
     constexpr int FN = TL::FN, FM = TL::FM;
     const int tid = threadIdx.x, lane = tid & 63;
     // wave index in a scalar register: everything derived from it stays uniform
@@ -345,6 +422,11 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
         S.tmb_n = (uint32_t)(p.K * p.ldb_t * 2);
     }
     const int KT = S.KT;
+    // the tile's bias, loaded before the first operand loads (so it lands
+    // first) and written to LDS after them; the epilogue reads it from there
+    float bv = 0.f;
+    if (p.bias != nullptr && p.ksplit <= 1 && tid < TL::TN)
+        bv = n0 + tid < p.N ? load_as_f32(p.bias, p.bias_dt, n0 + tid) : 0.f;
     if (KT > 0) {
         i32x4 f0a[FN], f0b[FM], f1a[FN], f1b[FM];
         // steps 0 .. NS-1 fill every stage; step 0 must land (NS-1 steps follow it)
@@ -352,6 +434,7 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
         for (int s0 = 0; s0 < TL::NS; ++s0) S.issue(smem, s0, wave, lane);
         wait_vm<(TL::NS - 1) * TL::Q>();
         lds_barrier();
+        if (tid < TL::TN) sbias[tid] = bv;
         read_frags<TL, TA, TB>(smem, 0, f0a, f0b, lane, wn, wm);
         // fold steps, then acc = scale * (h_r . up_c^T) once, then the main steps:
         // the accumulators see no vector ALU work inside either loop
@@ -362,8 +445,18 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
 #pragma unroll
                 for (int j = 0; j < FM; ++j) acc[i][j] *= p.scale;
         }
-        for (int kt = S.RF; kt < KT; ++kt) k_step<CT, TL, TA, TB>(S, smem, kt, f0a, f0b, f1a, f1b, acc, wave, lane, wn, wm);
+        if constexpr (!TA && !TB) {
+            const auto ra = make_rsrc(S.ma, S.nma);
+            const auto rb = make_rsrc(S.mb, S.nmb);
+            for (int kt = S.RF; kt < KT; ++kt)
+                k_step_main<CT, TL>(S, ra, rb, smem, kt, f0a, f0b, f1a, f1b, acc, wave, lane, wn, wm);
+        } else {
+            for (int kt = S.RF; kt < KT; ++kt)
+                k_step<CT, TL, TA, TB>(S, smem, kt, f0a, f0b, f1a, f1b, acc, wave, lane, wn, wm);
+        }
         wait_vm<0>();   // the out-of-range loads past the last step still write LDS
+    } else if (tid < TL::TN) {
+        sbias[tid] = bv;
     }
 
     // 3. epilogue: lane holds, per 16x16 block, 4 consecutive n for one m.
@@ -389,13 +482,16 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
         }
         return;
     }
-    //    The bias (and a per-feature gain) of every block is loaded before the first store.
+    //    The bias of every block comes from LDS (a per-feature gain from global
+    //    memory), all before the first store.
     float biasv[FN * 4] = {};
     if (p.bias != nullptr) {
-        int64_t idx[FN * 4];
+        __syncthreads();
 #pragma unroll
-        for (int i = 0; i < FN * 4; ++i) idx[i] = n0 + wn * TL::WN + (i >> 2) * 16 + 4 * (lane >> 4) + (i & 3);
-        load_n_as_f32<FN * 4>(p.bias, p.bias_dt, idx, p.N, biasv);
+        for (int i = 0; i < FN; ++i) {
+            const f32x4 b4 = *(const f32x4*)(sbias + wn * TL::WN + i * 16 + 4 * (lane >> 4));
+            biasv[4 * i] = b4[0]; biasv[4 * i + 1] = b4[1]; biasv[4 * i + 2] = b4[2]; biasv[4 * i + 3] = b4[3];
+        }
     }
     float gainv[GAIN ? FN * 4 : 1];
     if constexpr (GAIN) {
