@@ -195,20 +195,19 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
 
     const void* xa = x;
     const void* wa = w;
-    if (L.cast_x && P.K > 0) {
-        if (timed(LYC_KERNEL_CAST, s, [&] { return lyc::launch_cast((const float*)x, W + L.xc, P.M * P.K, P.c_dt, s); }) !=
-            hipSuccess)
-            return LYC_ERR_HIP;
-        xa = W + L.xc;
-    }
-    if (L.cast_w && P.K > 0) {
-        if (timed(LYC_KERNEL_CAST, s, [&] { return lyc::launch_cast((const float*)w, W + L.wc, P.N * P.K, P.c_dt, s); }) !=
-            hipSuccess)
-            return LYC_ERR_HIP;
-        wa = W + L.wc;
-    }
+    const bool cx = L.cast_x && P.K > 0, cw = L.cast_w && P.K > 0;
+    if (cx) xa = W + L.xc;
+    if (cw) wa = W + L.wc;
 
     if (!P.lora) {
+        if (cx && timed(LYC_KERNEL_CAST, s, [&] {
+                return lyc::launch_cast((const float*)x, W + L.xc, P.M * P.K, P.c_dt, s);
+            }) != hipSuccess)
+            return LYC_ERR_HIP;
+        if (cw && timed(LYC_KERNEL_CAST, s, [&] {
+                return lyc::launch_cast((const float*)w, W + L.wc, P.N * P.K, P.c_dt, s);
+            }) != hipSuccess)
+            return LYC_ERR_HIP;
         // plain affine: exact-rounding contraction with the round-then-add-bias epilogue
         const bool guard = P.c_dt != LYC_F32 && y_dt != LYC_F32;
         double2* wn = (double2*)(W + L.wnorm);
@@ -276,28 +275,36 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
     const uintptr_t vec_align = y_dt == LYC_F32 ? 16 : 8;
     g.vec_store = (P.N % 4 == 0) && aligned(y, vec_align);
 
-    if (P.r_pad > 0) {
-        // up already in the compute dtype, unpadded (rank == r_pad) and 16-byte
-        // aligned: the fold reads it as stored and the prep makes no copy
-        const bool up_stored = P.u_dt == P.c_dt && P.rank == P.r_pad && aligned(up, 16);
+    // up already in the compute dtype, unpadded (rank == r_pad) and 16-byte
+    // aligned: the fold reads it as stored and the prep makes no copy
+    const bool up_stored = P.r_pad > 0 && P.u_dt == P.c_dt && P.rank == P.r_pad && aligned(up, 16);
+    if (P.r_pad > 0 || cx || cw) {
+        // one launch: the factors' preparation and the fp32 operand casts
         lyc::PrepParams pp{};
-        pp.down = down;
-        pp.down_dt = P.d_dt;
-        pp.up = up;
-        pp.up_dt = P.u_dt;
-        pp.dc = W + L.dc;
-        pp.dh = W + L.dh;
-        pp.dl = W + L.dl;
-        pp.uc = up_stored ? nullptr : W + L.uc;
-        pp.dnorm = (double2*)(W + L.dnorm);
-        pp.flagged = (unsigned*)(W + L.flagged);
+        if (P.r_pad > 0) {
+            pp.down = down;
+            pp.down_dt = P.d_dt;
+            pp.up = up;
+            pp.up_dt = P.u_dt;
+            pp.dc = W + L.dc;
+            pp.dh = W + L.dh;
+            pp.dl = W + L.dl;
+            pp.uc = up_stored ? nullptr : W + L.uc;
+            pp.dnorm = (double2*)(W + L.dnorm);
+            pp.flagged = (unsigned*)(W + L.flagged);
+            pp.vec = aligned(down, 16) ? 1 : 0;
+        }
         pp.N = P.N;
         pp.K = P.K;
         pp.rank = P.rank;
         pp.r_pad = P.r_pad;
         pp.c_dt = P.c_dt;
-        pp.vec = aligned(down, 16) ? 1 : 0;
+        int nc = 0;
+        if (cx) { pp.cast_src[nc] = (const float*)x; pp.cast_dst[nc] = W + L.xc; pp.cast_n[nc++] = P.M * P.K; }
+        if (cw) { pp.cast_src[nc] = (const float*)w; pp.cast_dst[nc] = W + L.wc; pp.cast_n[nc++] = P.N * P.K; }
         if (timed(LYC_KERNEL_PREP, s, [&] { return lyc::launch_prep(pp, s); }) != hipSuccess) return LYC_ERR_HIP;
+    }
+    if (P.r_pad > 0) {
 
         lyc::XrParams hp{};
         const bool split = P.c_dt != LYC_F32;

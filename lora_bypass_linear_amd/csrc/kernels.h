@@ -85,7 +85,7 @@ struct XrParams {
 
 // Compute-dtype copies of down [rank,K] -> [r_pad,K] (+ its hi/lo split per
 // 64-k block and row norms) and up [N,rank] -> [N,r_pad]; zero padding;
-// clears *flagged.
+// clears *flagged (if not null); and the fp32 operand casts, in one launch.
 struct PrepParams {
     const void* down;
     int down_dt;
@@ -101,6 +101,12 @@ struct PrepParams {
     int64_t N, K, rank;
     int r_pad;
     int c_dt;
+    // fp32 operands narrowed to the 16-bit compute dtype in the same launch
+    // (cast_n[i] == 0: none); dst 256-byte aligned
+    const float* cast_src[2] = {nullptr, nullptr};
+    void* cast_dst[2] = {nullptr, nullptr};
+    int64_t cast_n[2] = {0, 0};
+    int up_blocks = 0;   // set by launch_prep
 };
 
 hipError_t launch_gemm(int c_dt, const GemmParams& p, hipStream_t s);

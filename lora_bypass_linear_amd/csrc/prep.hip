@@ -155,18 +155,49 @@ __device__ void row_pass(const void* src, int src_dt, int c_dt, int64_t row, int
     }
 }
 
-// blocks [0, r_pad): one row of down each (+ its split and norms); the rest:
-// up, grid-stride
+// fp32 -> 16-bit compute copy of elements [8 i0, 8 i1) and the tail past
+// n8: 8 elements per thread and iteration, two 16-byte loads and one
+// 16-byte store (src 16-byte aligned, dst 256-byte aligned)
+__device__ __forceinline__ void cast_range(const float* __restrict__ src, uint16_t* __restrict__ dst, int64_t n,
+                                           int c_dt, int64_t first, int64_t stride) {
+    const int64_t n8 = n / 8;
+    for (int64_t i = first; i < n8; i += stride) {
+        const f32x4 a = ((const f32x4*)src)[2 * i];
+        const f32x4 b = ((const f32x4*)src)[2 * i + 1];
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            o[e] = c_dt == DT_F16 ? pack_f16x2(a[2 * e], a[2 * e + 1]) : pack_bf16x2(a[2 * e], a[2 * e + 1]);
+            o[2 + e] = c_dt == DT_F16 ? pack_f16x2(b[2 * e], b[2 * e + 1]) : pack_bf16x2(b[2 * e], b[2 * e + 1]);
+        }
+        ((i32x4*)dst)[i] = i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+    }
+    for (int64_t i = n8 * 8 + first; i < n; i += stride)
+        dst[i] = c_dt == DT_F16 ? f32_to_f16(src[i]) : f32_to_bf16(src[i]);
+}
+
+// blocks [0, r_pad): one row of down each (+ its split and norms); then up,
+// grid-stride over up_blocks; then the fp32 operand casts (a2: x and W stored
+// in fp32 under a 16-bit policy), grid-stride over the remaining blocks.  The
+// row passes are latency-bound and the casts stream through HBM, so one
+// launch runs both at once.
 __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
     const int b = blockIdx.x, tid = threadIdx.x;
-    if (b == 0 && tid == 0) *p.flagged = 0u;
+    if (b == 0 && tid == 0 && p.flagged != nullptr) *p.flagged = 0u;
+    if (b >= p.r_pad + p.up_blocks) {
+        const int64_t cb = b - (p.r_pad + p.up_blocks), nb = (int64_t)gridDim.x - (p.r_pad + p.up_blocks);
+        for (int c = 0; c < 2; ++c)
+            if (p.cast_n[c] > 0)
+                cast_range(p.cast_src[c], (uint16_t*)p.cast_dst[c], p.cast_n[c], p.c_dt, cb * 256 + tid, nb * 256);
+        return;
+    }
     if (b < p.r_pad) {
         const bool split = p.c_dt != DT_F32;
         row_pass(p.down, p.down_dt, p.c_dt, b, p.K, b >= p.rank, p.vec, p.dc, split ? p.dh : nullptr,
                  split ? p.dl : nullptr, &p.dnorm[b]);
     } else {
         const int64_t total = p.N * (int64_t)p.r_pad;
-        const int64_t stride = (int64_t)(gridDim.x - p.r_pad) * 256;
+        const int64_t stride = (int64_t)p.up_blocks * 256;
         for (int64_t i = (int64_t)(b - p.r_pad) * 256 + tid; i < total; i += stride) {
             const int64_t n = i / p.r_pad;
             const int j = (int)(i - n * p.r_pad);
@@ -191,37 +222,29 @@ hipError_t launch_rownorm(const void* b, int c_dt, int64_t rows, int64_t K, void
     return hipGetLastError();
 }
 
-hipError_t launch_prep(const PrepParams& p, hipStream_t s) {
+hipError_t launch_prep(const PrepParams& p_in, hipStream_t s) {
+    PrepParams p = p_in;
     // uc == nullptr: no up copy is wanted (the caller reads up as stored, or
     // not at all), so only the down rows are prepared
     const int64_t total = p.uc != nullptr ? p.N * (int64_t)p.r_pad : 0;
     int64_t up_blocks = (total + 255) / 256;
     if (up_blocks > 2048) up_blocks = 2048;
     if (up_blocks < 1 && p.uc != nullptr) up_blocks = 1;
-    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(p.r_pad + up_blocks)), dim3(256), 0, s, p);
+    p.up_blocks = (int)up_blocks;
+    // cast blocks: one 8-element chunk per thread up to 8192 blocks
+    const int64_t cast8 = (p.cast_n[0] + p.cast_n[1]) / 8 + 1;
+    int64_t cast_blocks = (p.cast_n[0] + p.cast_n[1]) > 0 ? (cast8 + 255) / 256 : 0;
+    if (cast_blocks > 8192) cast_blocks = 8192;
+    const int64_t blocks = p.r_pad + up_blocks + cast_blocks;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
-// fp32 -> 16-bit compute copy (x or W stored in fp32 under a 16-bit policy):
-// 8 elements per thread and iteration, two 16-byte loads and one 16-byte
-// store (src is 16-byte aligned and dst 256-byte aligned).
+// fp32 -> 16-bit compute copy on its own (the backward's casts)
 __global__ __launch_bounds__(256) void cast_kernel(const float* __restrict__ src, uint16_t* __restrict__ dst,
                                                    int64_t n, int c_dt) {
-    const int64_t n8 = n / 8;
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
-        const f32x4 a = ((const f32x4*)src)[2 * i];
-        const f32x4 b = ((const f32x4*)src)[2 * i + 1];
-        uint32_t o[4];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            o[e] = c_dt == DT_F16 ? pack_f16x2(a[2 * e], a[2 * e + 1]) : pack_bf16x2(a[2 * e], a[2 * e + 1]);
-            o[2 + e] = c_dt == DT_F16 ? pack_f16x2(b[2 * e], b[2 * e + 1]) : pack_bf16x2(b[2 * e], b[2 * e + 1]);
-        }
-        ((i32x4*)dst)[i] = i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-    }
-    for (int64_t i = n8 * 8 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
-        dst[i] = c_dt == DT_F16 ? f32_to_f16(src[i]) : f32_to_bf16(src[i]);
+    cast_range(src, dst, n, c_dt, (int64_t)blockIdx.x * 256 + threadIdx.x, (int64_t)gridDim.x * 256);
 }
 
 hipError_t launch_cast(const float* src, void* dst, int64_t n, int c_dt, hipStream_t s) {
