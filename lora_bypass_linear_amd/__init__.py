@@ -26,7 +26,9 @@ OK, ERR_MIXED_HALF, ERR_INVALID_ARG, ERR_DTYPE_MISMATCH, ERR_UNSUPPORTED, ERR_HI
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblyc.so")
+# LYC_LIB: another build of the same library (the sanitizer build of the host
+# code, for the CPU test suite)
+LIB_PATH = os.environ.get("LYC_LIB") or os.path.join(_HERE, "liblyc.so")
 _lib = None
 
 _CODE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}

@@ -1,9 +1,14 @@
 """Build liblyc.so (the C-ABI library) for gfx950 with hipcc, in-tree.
 
-    python -m lora_bypass_linear_amd.build
+    python -m lora_bypass_linear_amd.build              # lora_bypass_linear_amd/liblyc.so
+    python -m lora_bypass_linear_amd.build --sanitize   # _build/san/liblyc.so
 
 Each source compiles to an object under ``_build/`` in parallel, then the
-objects link into ``lora_bypass_linear_amd/liblyc.so``.
+objects link into ``lora_bypass_linear_amd/liblyc.so``.  ``--sanitize``
+builds the host code (argument checks, policy, layouts, the tuning table)
+with AddressSanitizer and UndefinedBehaviorSanitizer -- the device code is
+built as usual -- for the CPU test suite, run with the clang sanitizer
+runtime preloaded and ``LYC_LIB`` pointing at that build.
 """
 from __future__ import annotations
 
@@ -35,9 +40,14 @@ def flags():
             "-I", os.path.join(ROOT, "include")]
 
 
-def _compile(src: str) -> str:
-    out = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + flags() + ["-c", os.path.join(HERE, src), "-o", out]
+SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-Xarch_host",
+       "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src: str, sanitize: bool = False) -> str:
+    d = os.path.join(BUILD, "san") if sanitize else BUILD
+    out = os.path.join(d, os.path.basename(src) + ".o")
+    cmd = [hipcc()] + flags() + (SAN if sanitize else []) + ["-c", os.path.join(HERE, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in (r.stderr or "").splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
@@ -47,20 +57,22 @@ def _compile(src: str) -> str:
     return out
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = True, sanitize: bool = False) -> str:
+    d = os.path.join(BUILD, "san") if sanitize else BUILD
+    os.makedirs(d, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(4, len(SRCS))) as ex:
-        objs = list(ex.map(_compile, SRCS))
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+        objs = list(ex.map(lambda src: _compile(src, sanitize), SRCS))
+    lib = os.path.join(d, "liblyc.so") if sanitize else LIB
+    tmp = lib + f".tmp{os.getpid()}"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs + (SAN if sanitize else [])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
-    build()
+    build(sanitize="--sanitize" in sys.argv[1:])

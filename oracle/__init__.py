@@ -27,14 +27,19 @@ _LIB_OVERRIDE = os.environ.get("ORACLE_LIB_OVERRIDE")
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c with gcc (IEEE semantics: no fast-math, no contraction)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + f".tmp{os.getpid()}"
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile oracle.c with gcc (IEEE semantics: no fast-math, no contraction).
+    With ``sanitize``: an AddressSanitizer + UndefinedBehaviorSanitizer build,
+    liboracle_san.so, for the CPU tests (run with gcc's libasan preloaded and
+    ORACLE_LIB_OVERRIDE pointing at it)."""
+    lib = _LIB.replace(".so", "_san.so") if sanitize else _LIB
+    if force or not os.path.exists(lib):
+        tmp = lib + f".tmp{os.getpid()}"
+        san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-                               "-fno-fast-math", "-o", tmp, _SRC, "-lm", "-lpthread"])
-        os.replace(tmp, _LIB)
-    return _LIB
+                               "-fno-fast-math"] + (san if sanitize else []) + ["-o", tmp, _SRC, "-lm", "-lpthread"])
+        os.replace(tmp, lib)
+    return lib
 
 
 def lib():
