@@ -520,11 +520,30 @@ def _backward(dev, wl, inputs, reps, warm, accuracy, eager):
     peak = PEAK_TFLOPS[c_dt]
     names = {"cast": "transposes + casts", "prep": "prep + row norms", "hpass": "h and gh passes",
              "gemm": "dx, dDown, dUp GEMMs"}
+    # the same calls with a caller-kept W_c^T (W frozen across steps): no W^T copy per call
+    w_t = d["w"].to(L.torch_dtype(c_dt)).t().contiguous()
+    for _ in range(3):
+        call(w_t=w_t)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        call(w_t=w_t)
+    torch.cuda.synchronize()
+    ms_wt = (time.perf_counter() - t0) * 1e3 / reps
+    L.profile_begin(32 * reps)
+    for _ in range(reps):
+        call(w_t=w_t)
+    torch.cuda.synchronize()
+    prof_wt = L.profile_end()
+    del w_t
     out = {"shape": f"M {M}, N {N}, K {K}, rank {r}, dy {WL.NAME[WL.dtype_code(dy_cpu)]}",
            "ms_per_call": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
            "flops_per_call": flops,
            "kernels": {names[k]: {"launches": n // reps, "us_per_call": round(t * 1e3 / reps, 2)}
                        for k, (n, t) in prof.items() if n},
+           "with_caller_wt": {"ms_per_call": round(ms_wt, 4), "tflops": round(flops / (ms_wt * 1e-3) / 1e12, 2),
+                              "kernels": {names[k]: {"launches": n // reps, "us_per_call": round(t * 1e3 / reps, 2)}
+                                          for k, (n, t) in prof_wt.items() if n}},
            "roofline": {"bound": "mfma", "kernel": "gemm_kernel (dx = dy_c.W_c + gh_r.down_c)",
                         "achieved": round(dx_flops / (g_us * 1e-6) / 1e12, 2), "peak": peak, "unit": "TFLOP/s",
                         "frac": round(dx_flops / (g_us * 1e-6) / 1e12 / peak, 4), "traffic": None,

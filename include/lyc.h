@@ -245,7 +245,8 @@ int lyc_lora_merge_fwd(const void* w, int w_dt, const void* down, int down_dt, c
  *    compute (or larger operands) transposed copies of those are made in the
  *    workspace too.  Its size comes from
  *    lyc_lora_linear_bwd_workspace_size with `want` = 1 (dx) | 2 (dDown) |
- *    4 (dUp), the set of non-NULL outputs of the call.
+ *    4 (dUp), the set of non-NULL outputs of the call (| 8 for
+ *    lyc_lora_linear_bwd_wt, which needs no W^T copy).
  * Same stream, ownership and error conventions as the forward.
  */
 int lyc_lora_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt,
@@ -254,6 +255,23 @@ int lyc_lora_linear_bwd(const void* x, int x_dt, const void* w, int w_dt, int bi
                         int down_dt, const void* up, int up_dt, int64_t rank, double scale, const void* dy,
                         int dy_dt, void* dx, void* d_down, void* d_up, int64_t M, int64_t N, int64_t K,
                         void* workspace, size_t workspace_bytes, void* stream);
+/*
+ * The same backward with a caller-kept transposed weight, for LoRA training
+ * where W is frozen across steps (LyCORIS "Precision" page, "VRAM": the
+ * frozen base weight is used as stored, nothing of its size is rebuilt per
+ * step).  w_t is W_c^T: [K][N] row-major in the compute dtype c of the call,
+ * each element W[n][k] rounded to nearest even to c (the caller rounds and
+ * transposes once; for 16-bit W already in c it is the plain transpose).  It
+ * must be 16-byte aligned and must not overlap any output.  w_dt is still the
+ * stored dtype of W (a policy operand).  dx reads w_t in place: the
+ * workspace skips the W^T copy -- its size comes from
+ * lyc_lora_linear_bwd_workspace_size with bit 8 added to `want`.  Results
+ * are identical to lyc_lora_linear_bwd's.
+ */
+int lyc_lora_linear_bwd_wt(const void* x, int x_dt, const void* w_t, int w_dt, int bias_dt, const void* down,
+                           int down_dt, const void* up, int up_dt, int64_t rank, double scale, const void* dy,
+                           int dy_dt, void* dx, void* d_down, void* d_up, int64_t M, int64_t N, int64_t K,
+                           void* workspace, size_t workspace_bytes, void* stream);
 /*
  * Where lyc_lora_linear_bwd leaves h_r and gh_r in its workspace (both
  * [M][ld] in the compute dtype; SIZE_MAX when the call set `want` does not

@@ -426,7 +426,7 @@ int merge(const Merge& G, const void* w, const void* down, const void* up, doubl
 }
 
 // ---- LoRA-bypass backward ------------------------------------------------------
-enum { BWD_DX = 1, BWD_DDOWN = 2, BWD_DUP = 4 };
+enum { BWD_DX = 1, BWD_DDOWN = 2, BWD_DUP = 4, BWD_WT = 8 };   // BWD_WT: the caller passes W_c^T
 
 struct Bwd {
     Problem P;       // the forward's problem; c_dt resolved over (x, W, b, down, up, dy)
@@ -448,7 +448,7 @@ struct BwdLayout {
 
 int check_bwd(Bwd& B) {
     Problem& P = B.P;
-    if (P.M < 0 || P.N < 0 || P.K < 0 || P.rank < 0 || B.want < 0 || B.want > 7) return LYC_ERR_INVALID_ARG;
+    if (P.M < 0 || P.N < 0 || P.K < 0 || P.rank < 0 || B.want < 0 || B.want > 15) return LYC_ERR_INVALID_ARG;
     if (!valid_dt(P.x_dt) || !valid_dt(P.w_dt) || !valid_dt(P.d_dt) || !valid_dt(P.u_dt) || !valid_dt(B.dy_dt))
         return LYC_ERR_INVALID_ARG;
     if (P.b_dt != 0 && !valid_dt(P.b_dt)) return LYC_ERR_INVALID_ARG;
@@ -520,7 +520,7 @@ BwdLayout bwd_layout(const Bwd& B) {
     size_t part = 0;
     const int64_t Kt = L.tr_tok ? P.M : B.M8;   // contraction length of the token GEMMs
     if (dx) {
-        take(L.wt, K * N * ce);
+        if (!(B.want & BWD_WT)) take(L.wt, K * N * ce);
         if (P.rank > 0) take(L.dt, K * R * ce);
         L.ks_dx = lyc::gemm_ksplit(P.M, P.K, P.N, P.c_dt);
         if (L.ks_dx > 1) part = std::max(part, (size_t)L.ks_dx * M * K * 4);
@@ -553,19 +553,23 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 int backward(const Bwd& B, const void* x, const void* w, const void* down, const void* up, double scale,
-             const void* dy, void* dx, void* d_down, void* d_up, void* ws, size_t ws_bytes, void* stream) {
+             const void* dy, void* dx, void* d_down, void* d_up, void* ws, size_t ws_bytes, void* stream,
+             const void* w_t = nullptr) {
     const Problem& P = B.P;
     if (!(scale == scale) || scale > 3.4e38 || scale < -3.4e38) return LYC_ERR_INVALID_ARG;
     const bool wdx = B.want & BWD_DX, wdd = B.want & BWD_DDOWN, wdu = B.want & BWD_DUP;
+    const bool wt_given = B.want & BWD_WT;
     const int64_t M = P.M, N = P.N, K = P.K, r = P.rank;
     // which inputs the wanted gradients read
     const bool use_x = (wdd || wdu) && r > 0 && M > 0 && K > 0;
     const bool use_dy = M > 0 && N > 0 && (wdx || r > 0);
     const bool use_w = wdx && M > 0 && N > 0 && K > 0;
     const bool use_f = r > 0 && M > 0;
-    if ((use_x && x == nullptr) || (use_dy && dy == nullptr) || (use_w && w == nullptr) ||
+    if ((use_x && x == nullptr) || (use_dy && dy == nullptr) || (use_w && (wt_given ? w_t : w) == nullptr) ||
         (use_f && (down == nullptr || up == nullptr)))
         return LYC_ERR_INVALID_ARG;
+    // a caller-kept W_c^T [K][N] is read in place by the dx GEMM: 16-byte rows
+    if (wt_given && use_w && !aligned(w_t, 16)) return LYC_ERR_UNSUPPORTED;
     const size_t ndx = (size_t)(M * K) * esize(P.x_dt), ndd = (size_t)(r * K) * esize(P.d_dt),
                  ndu = (size_t)(N * r) * esize(P.u_dt);
     if ((wdx && ndx > 0 && dx == nullptr) || (wdd && ndd > 0 && d_down == nullptr) || (wdu && ndu > 0 && d_up == nullptr))
@@ -581,14 +585,14 @@ int backward(const Bwd& B, const void* x, const void* w, const void* down, const
         (wdu && d_up && !aligned(d_up, esize(P.u_dt))))
         return LYC_ERR_UNSUPPORTED;
     // the gradients overlap neither the inputs nor each other
-    const void* ins[5] = {x, w, down, up, dy};
-    const size_t nin[5] = {(size_t)(M * K) * esize(P.x_dt), (size_t)(N * K) * esize(P.w_dt),
+    const void* ins[6] = {x, w, down, up, dy, wt_given ? w_t : nullptr};
+    const size_t nin[6] = {(size_t)(M * K) * esize(P.x_dt), (size_t)(N * K) * esize(P.w_dt),
                            (size_t)(r * K) * esize(P.d_dt), (size_t)(N * r) * esize(P.u_dt),
-                           (size_t)(M * N) * esize(B.dy_dt)};
+                           (size_t)(M * N) * esize(B.dy_dt), (size_t)(K * N) * esize(P.c_dt)};
     void* outs[3] = {wdx ? dx : nullptr, wdd ? d_down : nullptr, wdu ? d_up : nullptr};
     const size_t nout[3] = {ndx, ndd, ndu};
     for (int i = 0; i < 3; ++i) {
-        for (int j = 0; j < 5; ++j)
+        for (int j = 0; j < 6; ++j)
             if (overlaps(outs[i], nout[i], ins[j], nin[j])) return LYC_ERR_INVALID_ARG;
         for (int j = i + 1; j < 3; ++j)
             if (overlaps(outs[i], nout[i], outs[j], nout[j])) return LYC_ERR_INVALID_ARG;
@@ -694,9 +698,9 @@ int backward(const Bwd& B, const void* x, const void* w, const void* down, const
     // dx = round_x(dy_c . W_c + gh_r . down_c): the forward's GEMM with W^T, the fold over down^T
     if (wdx && M > 0 && K > 0) {
         lyc::GemmParams g{};
-        if (N > 0 && !transpose(w, P.w_dt, N, K, W + L.wt, N, K)) return LYC_ERR_HIP;
+        if (!wt_given && N > 0 && !transpose(w, P.w_dt, N, K, W + L.wt, N, K)) return LYC_ERR_HIP;
         if (r > 0 && !transpose(down, P.d_dt, r, K, W + L.dt, P.r_pad, K)) return LYC_ERR_HIP;
-        g.a = W + L.wt;
+        g.a = wt_given ? w_t : (const void*)(W + L.wt);
         g.af = r > 0 ? (const void*)(W + L.dt) : nullptr;
         g.b = ga;
         g.M = M;
@@ -920,6 +924,17 @@ int lyc_lora_linear_bwd(const void* x, int x_dt, const void* w, int w_dt, int bi
     const int st = check_bwd(B);
     if (st != LYC_OK) return st;
     return backward(B, x, w, down, up, scale, dy, dx, d_down, d_up, workspace, workspace_bytes, stream);
+}
+
+int lyc_lora_linear_bwd_wt(const void* x, int x_dt, const void* w_t, int w_dt, int bias_dt, const void* down,
+                           int down_dt, const void* up, int up_dt, int64_t rank, double scale, const void* dy,
+                           int dy_dt, void* dx, void* d_down, void* d_up, int64_t M, int64_t N, int64_t K,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    const int want = (dx ? BWD_DX : 0) | (d_down ? BWD_DDOWN : 0) | (d_up ? BWD_DUP : 0) | BWD_WT;
+    Bwd B{Problem{true, M, N, K, rank, x_dt, w_dt, bias_dt, down_dt, up_dt, 0, 0, 0}, dy_dt, want, 0};
+    const int st = check_bwd(B);
+    if (st != LYC_OK) return st;
+    return backward(B, x, nullptr, down, up, scale, dy, dx, d_down, d_up, workspace, workspace_bytes, stream, w_t);
 }
 
 int lyc_lora_linear_bwd_workspace_layout(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt,

@@ -355,3 +355,24 @@ def test_noalloc_refuses_before_any_gpu_call():
     assert b"allocation-free" in lib.lyc_status_str(L.ERR_SCRATCH)
     # the largest workload's need fits
     assert L.lora_workspace_size(16384, 8192, 8192, 128, 2, 2, 2, 2, 2) <= L.NOALLOC_SCRATCH_BYTES
+
+
+def test_backward_with_caller_kept_wt_checks():
+    """lyc_lora_linear_bwd_wt: W^T read in place (16-byte aligned, no overlap
+    with an output) and no W^T copy in the workspace (want bit 8)."""
+    lib = L.lib()
+    a = dict(x=P, x_dt=1, wt=V(1 << 28), w_dt=1, b_dt=0, d=P, d_dt=1, u=P, u_dt=1, r=4, scale=1.0, g=P, g_dt=1,
+             dx=V(1 << 30), dd=V(1 << 31), du=V(1 << 32), M=16, N=64, K=64, ws=None, nws=0, s=None)
+    call = lambda **kw: _refused(lib.lyc_lora_linear_bwd_wt(*[{**a, **kw}[k] for k in (
+        "x", "x_dt", "wt", "w_dt", "b_dt", "d", "d_dt", "u", "u_dt", "r")], ctypes.c_double({**a, **kw}["scale"]),
+        *[{**a, **kw}[k] for k in ("g", "g_dt", "dx", "dd", "du", "M", "N", "K", "ws", "nws", "s")]))
+    assert call(wt=None) == L.ERR_INVALID_ARG
+    assert call(wt=V((1 << 28) + 8)) == L.ERR_UNSUPPORTED        # W^T rows are read 16 bytes at a time
+    assert call(wt=V(1 << 30)) == L.ERR_INVALID_ARG              # overlaps dx
+    assert call(g_dt=2) == L.ERR_MIXED_HALF
+    assert call() == L.ERR_WORKSPACE
+    full = L.lora_bwd_workspace_size(300, 64, 128, 17, 1, 1, 0, 1, 1, 1, 7)
+    kept = L.lora_bwd_workspace_size(300, 64, 128, 17, 1, 1, 0, 1, 1, 1, 7 | 8)
+    assert full - kept == 128 * 64 * 2                           # exactly the W^T [K][N] copy
+    with pytest.raises(L.LycError):
+        L.lora_bwd_workspace_size(300, 64, 128, 17, 1, 1, 0, 1, 1, 1, 16)

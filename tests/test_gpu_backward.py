@@ -189,3 +189,32 @@ def test_full_size_sampled(name):
     rng = np.random.default_rng(wl.seed)
     _check(wl, dx_rows=sample_rows(wl.M, 16, seed=wl.seed), js=np.sort(rng.choice(wl.r, 4, replace=False)),
            dd_cols=sample_rows(wl.K, 24, seed=wl.seed + 1), du_rows=sample_rows(wl.N, 24, seed=wl.seed + 2))
+
+
+@pytest.mark.parametrize("name,dims", [
+    ("lora_f16_4096x3072x3072_r16", dict(M=300, N=264, K=136)),
+    ("lora_bf16_16384x8192x8192_r128", dict(M=130, N=520, K=264)),
+    ("lora_bf16x_f32w_8192x4096x4096_r64", dict(M=200, N=136, K=72)),   # fp32 W: w_t is W rounded to bf16
+    ("lora_f16_4096x3072x3072_r16", dict(M=16)),                         # dx splits K at this size
+])
+def test_caller_kept_wt_gives_identical_gradients(name, dims):
+    """lyc_lora_linear_bwd_wt (W_c^T passed in, no per-call copy) against
+    lyc_lora_linear_bwd: every gradient bit for bit."""
+    wl = BASE[name].resized(**dims)
+    inp = _inputs(wl)
+    dev = torch.device("cuda:0")
+    d = {k: v.to(dev) for k, v in inp.items()}
+    b_dtype = inp["b"].dtype if "b" in inp else None
+    codes = [WL.dtype_code(inp[k]) for k in ("x", "w", "down", "up", "dy")] + \
+            ([WL.dtype_code(inp["b"])] if "b" in inp else [])
+    c_dt, _ = L.resolve_dtypes(codes)
+    w_t = d["w"].to(_T[c_dt]).t().contiguous()
+    say("backward w_t", wl.name, dims)
+    ref = L.lora_linear_backward(d["x"], d["w"], d["down"], d["up"], wl.scale, d["dy"], bias_dtype=b_dtype)
+    got = L.lora_linear_backward(d["x"], d["w"], d["down"], d["up"], wl.scale, d["dy"], bias_dtype=b_dtype, w_t=w_t)
+    dxo = L.lora_linear_backward(d["x"], d["w"], d["down"], d["up"], wl.scale, d["dy"], bias_dtype=b_dtype, w_t=w_t,
+                                 want_ddown=False, want_dup=False)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+    assert torch.equal(ref[0], dxo[0]) and dxo[1] is None and dxo[2] is None
