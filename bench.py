@@ -241,8 +241,8 @@ def _forward_bench(dev, wl, inputs, steps, warmup):
         nflag = int(ws[fo: fo + 4].cpu().view(torch.int32).item())
         guard = {"h_reevaluated_fp64": nflag, "of": wl.M * wl.r, "fraction": round(nflag / (wl.M * wl.r), 6)}
     elif not lora and c_dt != L.F32:
-        fo = L.linear_workspace_layout(wl.M, wl.N, wl.K, dts[0], dts[1], b_dt)
-        nflag = int(ws[fo: fo + 4].cpu().view(torch.int32).item())
+        fo, ns = L.linear_workspace_layout(wl.M, wl.N, wl.K, dts[0], dts[1], b_dt)
+        nflag = int(ws[fo: fo + 4 * ns].cpu().view(torch.int32).sum().item())
         guard = {"projection_reevaluated_fp64": nflag, "of": wl.M * wl.N,
                  "fraction": round(nflag / (wl.M * wl.N), 6)}
     return {"tflops": round(tflops, 2), "ms_per_step": round(ms_per_step, 5),

@@ -78,10 +78,12 @@ int lyc_resolve_dtypes(const int* operand_dtypes, int n, int* compute, int* outp
 
 /*
  * Workspace bytes lyc_linear_fwd needs for this problem: for 16-bit compute
- * the hi/lo split of W_c (per 64-k block) and its row norms, used by the
- * projection's rounding guard, a counter, plus compute-dtype copies of fp32
- * operands that feed a 16-bit contraction.  Returns the same argument errors
- * as lyc_linear_fwd.
+ * the projection guard's counts and, where at least 256 output tiles of
+ * 64 x 64 keep every CU busy, the hi/lo split of W_c (per 64-k block) and its
+ * row norms from a preparation pass (with fewer tiles the contraction splits
+ * W itself, in one launch), plus compute-dtype copies of fp32 operands that
+ * feed a 16-bit contraction.  Returns the same argument errors as
+ * lyc_linear_fwd.
  */
 int lyc_linear_workspace_size(int64_t M, int64_t N, int64_t K, int x_dt, int w_dt, int bias_dt,
                               size_t* bytes);
@@ -171,15 +173,18 @@ int lyc_lora_workspace_layout(int64_t M, int64_t N, int64_t K, int64_t rank, int
                               int down_dt, int up_dt, size_t* h_offset, int64_t* h_ld, size_t* flagged_offset);
 
 /*
- * Where lyc_linear_fwd keeps its guard counter inside the workspace:
- *   flagged_offset: byte offset of a uint32 count of projection elements that
- *              the rounding guard re-evaluated in fp64 during the last call
- *              (16-bit compute; 0 when the output is fp32, which needs no
- *              guard; not written at all under fp32 compute).
- * The out-pointer may be NULL.  Same argument errors as the size query.
+ * Where lyc_linear_fwd keeps its guard counts inside the workspace:
+ *   flagged_offset: byte offset of `*flagged_slots` uint32 counts (one, or
+ *              one per workgroup where the contraction splits W itself) whose
+ *              sum is the number of
+ *              projection elements the rounding guard re-evaluated in fp64
+ *              during the last call (16-bit compute; all 0 when the output is
+ *              fp32, which needs no guard);
+ *   flagged_slots: their number (0 under fp32 compute: nothing is written).
+ * Any out-pointer may be NULL.  Same argument errors as the size query.
  */
 int lyc_linear_workspace_layout(int64_t M, int64_t N, int64_t K, int x_dt, int w_dt, int bias_dt,
-                                size_t* flagged_offset);
+                                size_t* flagged_offset, int64_t* flagged_slots);
 
 /*
  * LoRA merge (LyCORIS "Precision" page: "Dtype policy", whose "input" is here

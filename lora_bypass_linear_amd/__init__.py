@@ -65,7 +65,8 @@ def lib():
                                                   c_i64, ctypes.c_double, c_vp, c_int, c_i64, c_i64, c_i64, c_vp]
         L.lyc_lora_workspace_layout.argtypes = [c_i64, c_i64, c_i64, c_i64, c_int, c_int, c_int, c_int, c_int,
                                                 ctypes.POINTER(c_sz), ctypes.POINTER(c_i64), ctypes.POINTER(c_sz)]
-        L.lyc_linear_workspace_layout.argtypes = [c_i64, c_i64, c_i64, c_int, c_int, c_int, ctypes.POINTER(c_sz)]
+        L.lyc_linear_workspace_layout.argtypes = [c_i64, c_i64, c_i64, c_int, c_int, c_int, ctypes.POINTER(c_sz),
+                                                  ctypes.POINTER(c_i64)]
         L.lyc_lora_merge_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_int, c_int, c_int, ctypes.POINTER(c_sz)]
         L.lyc_lora_merge_fwd.argtypes = [c_vp, c_int, c_vp, c_int, c_vp, c_int, c_i64, ctypes.c_double, c_vp, c_int,
                                          c_i64, c_i64, c_vp, c_sz, c_vp]
@@ -224,11 +225,12 @@ def lora_workspace_layout(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt):
     return ho.value, ld.value, fo.value
 
 
-def linear_workspace_layout(M, N, K, x_dt, w_dt, b_dt=0) -> int:
-    """flagged_offset: the guard counter inside the plain affine workspace."""
-    fo = ctypes.c_size_t(0)
-    _check(lib().lyc_linear_workspace_layout(M, N, K, x_dt, w_dt, b_dt, ctypes.byref(fo)))
-    return fo.value
+def linear_workspace_layout(M, N, K, x_dt, w_dt, b_dt=0):
+    """(flagged_offset, slots): the guard's per-workgroup uint32 counts inside
+    the plain affine workspace (their sum is the re-evaluated count)."""
+    fo, ns = ctypes.c_size_t(0), ctypes.c_int64(0)
+    _check(lib().lyc_linear_workspace_layout(M, N, K, x_dt, w_dt, b_dt, ctypes.byref(fo), ctypes.byref(ns)))
+    return fo.value, ns.value
 
 
 def lora_merge_workspace_size(N, K, r, w_dt, d_dt, u_dt) -> int:

@@ -87,6 +87,10 @@ int check_problem(Problem& P) {
 struct Layout {
     size_t xc = 0, wc = 0, dc = 0, dh = 0, dl = 0, uc = 0, h = 0, dnorm = 0, wh = 0, wl = 0, wnorm = 0, flagged = 0,
            partial = 0, gain = 0, total = 0;
+    // plain affine form: guard counts (one, or one per workgroup where the
+    // contraction splits W itself: w_split_pass false)
+    int64_t flag_slots = 0;
+    bool w_split_pass = false;
     int ksplit = 1, ks_max = 1;
     bool cast_x = false, cast_w = false;
 };
@@ -124,14 +128,19 @@ Layout layout(const Problem& P) {
         // DoRA: the per-feature gain m / norm in fp32
         if (P.m_dt != 0) { L.gain = off; off = align256(off + (size_t)P.N * 4); }
     }
-    if (!P.lora) {
-        // the projection's rounding guard: hi/lo split and row norms of W_c, a counter
-        if (split) {
+    if (!P.lora && split) {
+        // the projection's rounding guard: W's hi/lo split and row norms from the
+        // row-norm pass and one counter, or, where the contraction splits W
+        // itself, one count per workgroup
+        const int64_t wgs = lyc::xr_affine_workgroups(P.M, P.N);
+        L.w_split_pass = wgs == 0;
+        if (L.w_split_pass) {
             L.wh = off; off = align256(off + (size_t)P.N * (size_t)P.K * ce);
             L.wl = off; off = align256(off + (size_t)P.N * (size_t)P.K * ce);
+            L.wnorm = off; off = align256(off + (size_t)P.N * 2 * sizeof(double));
         }
-        L.wnorm = off; off = align256(off + (size_t)P.N * 2 * sizeof(double));
-        L.flagged = off; off = align256(off + sizeof(unsigned));
+        L.flag_slots = L.w_split_pass ? 1 : wgs;
+        L.flagged = off; off = align256(off + (size_t)L.flag_slots * sizeof(unsigned));
     }
     L.total = off;
     return L;
@@ -208,26 +217,27 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
                 return lyc::launch_cast((const float*)w, W + L.wc, P.N * P.K, P.c_dt, s);
             }) != hipSuccess)
             return LYC_ERR_HIP;
-        // plain affine: exact-rounding contraction with the round-then-add-bias epilogue
+        // plain affine: exact-rounding contraction with the round-then-add-bias
+        // epilogue; W's split and row norms from the row-norm pass (which also
+        // clears the counter) or inside the contraction
         const bool guard = P.c_dt != LYC_F32 && y_dt != LYC_F32;
-        double2* wn = (double2*)(W + L.wnorm);
-        unsigned* fl = (unsigned*)(W + L.flagged);
-        const bool split = P.c_dt != LYC_F32;
-        if (split && timed(LYC_KERNEL_PREP, s, [&] {
-                return lyc::launch_rownorm(wa, P.c_dt, P.N, P.K, W + L.wh, W + L.wl, wn, fl, s);
+        if (L.w_split_pass && timed(LYC_KERNEL_PREP, s, [&] {
+                return lyc::launch_rownorm(wa, P.c_dt, P.N, P.K, W + L.wh, W + L.wl, (double2*)(W + L.wnorm),
+                                           (unsigned*)(W + L.flagged), s);
             }) != hipSuccess)
             return LYC_ERR_HIP;
         lyc::XrParams xp{};
         xp.x = xa;
-        xp.b = split ? (const void*)(W + L.wh) : wa;
-        xp.b_lo = split ? (const void*)(W + L.wl) : nullptr;
+        xp.b = L.w_split_pass ? (const void*)(W + L.wh) : wa;
+        xp.b_lo = L.w_split_pass ? (const void*)(W + L.wl) : nullptr;
         xp.b_full = wa;
-        xp.bnorm = wn;
+        xp.bnorm = L.w_split_pass ? (const double2*)(W + L.wnorm) : nullptr;
         xp.M = P.M;
         xp.Nc = P.N;
         xp.K = P.K;
         xp.guard = guard ? 1 : 0;
-        xp.flagged = fl;
+        xp.flagged = L.flag_slots > 0 ? (unsigned*)(W + L.flagged) : nullptr;
+        xp.flag_slots = L.flag_slots;
         xp.mode = lyc::XR_AFFINE;
         xp.out = y;
         xp.ld_out = P.N;
@@ -1125,11 +1135,13 @@ int lyc_lora_workspace_layout(int64_t M, int64_t N, int64_t K, int64_t rank, int
 }
 
 int lyc_linear_workspace_layout(int64_t M, int64_t N, int64_t K, int x_dt, int w_dt, int bias_dt,
-                                size_t* flagged_offset) {
+                                size_t* flagged_offset, int64_t* flagged_slots) {
     Problem P{false, M, N, K, 0, x_dt, w_dt, bias_dt, 0, 0, 0, 0, 0};
     const int st = check_problem(P);
     if (st != LYC_OK) return st;
-    if (flagged_offset) *flagged_offset = layout(P).flagged;
+    const Layout L = layout(P);
+    if (flagged_offset) *flagged_offset = L.flagged;
+    if (flagged_slots) *flagged_slots = L.flag_slots;
     return LYC_OK;
 }
 

@@ -206,10 +206,10 @@ __device__ __forceinline__ float pick4(f32x4 v, int e) {
 
 // Epilogue of one wave's accumulators: rounding guard (flagged elements are
 // appended to the workgroup's work list), then h_r or the affine output.
-template <class CT, int JB>
+template <class CT, int JB, bool SB>
 __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB][4], double xm2, double xl2, bool wide,
                                             int64_t wg_m0, int64_t j0, int my_row, int c0, int cols_wg, int lane,
-                                            unsigned* lcount, uint32_t* list) {
+                                            unsigned* lcount, uint32_t* list, const float (&bsq)[SB ? JB : 1][2]) {
     constexpr bool SPLIT = CT::dt != DT_F32;
     const int64_t m = wg_m0 + my_row;
     const bool row_ok = m < p.M;
@@ -250,7 +250,18 @@ __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB]
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int jl = c0 + jb * 16 + 4 * (lane >> 4) + e;
-                b2[e] = (guard && jl < cols_wg) ? p.bnorm[j0 + jl] : double2{0.0, 0.0};
+                if constexpr (SB) {
+                    // the lane's column c of this block: its row's squared norms
+                    // sit in lane c (shuffled whatever the lane's own columns)
+                    const int c = 4 * (lane >> 4) + e;
+                    const float vb = __shfl(bsq[SB ? jb : 0][0], c), vl = __shfl(bsq[SB ? jb : 0][1], c);
+                    const double slack = 1.0 + 0x1p-20;
+                    const double2 v{__builtin_sqrt((double)vb) * slack,
+                                    vl < __builtin_inff() ? __builtin_sqrt((double)vl) * slack : __builtin_inf()};
+                    b2[e] = (guard && jl < cols_wg) ? v : double2{0.0, 0.0};
+                } else {
+                    b2[e] = (guard && jl < cols_wg) ? p.bnorm[j0 + jl] : double2{0.0, 0.0};
+                }
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -342,9 +353,9 @@ __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB]
 // row groups of a workgroup with KS k groups: 4 / KS (16 rows per group), at least 1
 constexpr int xr_row_groups(int KS) { return KS >= 4 ? 1 : 4 / KS; }
 
-template <int JB, int KS, int CG, int RW_, bool SPLIT>
+template <int JB, int KS, int CG, int RW_, bool SPLIT, bool SB = false>
 struct XrStage {
-    static constexpr int NB = SPLIT ? 2 : 1;
+    static constexpr int NB = (SPLIT && !SB) ? 2 : 1;   // b_hi and b_lo tiles, or b itself
     static constexpr int RW = RW_, RP = JB * 16 * CG, NW = RW * KS * CG;
     static constexpr int TILE = RP * 128, XT = RW * 16 * 128;
     static constexpr int BYTES = KS * (NB * TILE + XT);
@@ -356,11 +367,17 @@ struct XrStage {
     static_assert(NS * BYTES <= 160 * 1024 && (NS - 1) * Q < 64, "LDS stages");
 };
 
-template <class CT, int JB, int KS, int CG, int RW_>
+// SB (plain affine form): b = W_c is loaded as stored and split in the kernel
+// exactly as x is (per 64-k block of each row), its row norms taken from the
+// diagonals of MFMA Gram matrices; no preparation pass.  The guard's count is
+// then written per workgroup (p.flagged[workgroup], a plain store), so that
+// nothing needs clearing beforehand.
+template <class CT, int JB, int KS, int CG, int RW_, bool SB = false>
 __global__ __launch_bounds__(64 * RW_ * KS * CG) __attribute__((amdgpu_num_vgpr(256)))
 void xr_kernel(XrParams p) {
     constexpr bool SPLIT = CT::dt != DT_F32;     // 16-bit compute: hi/lo split and guard
-    using ST = XrStage<JB, KS, CG, RW_, SPLIT>;
+    static_assert(!SB || (SPLIT && JB <= 4), "in-kernel split of b: 16-bit compute, at most 4 column blocks");
+    using ST = XrStage<JB, KS, CG, RW_, SPLIT, SB>;
     constexpr int NB = ST::NB, RW = ST::RW, RP = ST::RP, TILE = ST::TILE, NS = ST::NS, Q = ST::Q, NW = ST::NW;
     __shared__ __attribute__((aligned(16))) char sd[NS * ST::BYTES];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -376,7 +393,7 @@ void xr_kernel(XrParams p) {
     const int my_row = rg * 16 + (lane & 15);   // row within the workgroup
     const auto rsx = make_rsrc((const char*)p.x + wg_m0 * kbytes, (uint32_t)rows_wg * kbytes);
     const auto rsh = make_rsrc((const char*)p.b + j0 * kbytes, (uint32_t)cols_wg * kbytes);
-    const auto rsl = make_rsrc((const char*)(SPLIT ? p.b_lo : p.b) + j0 * kbytes, (uint32_t)cols_wg * kbytes);
+    const auto rsl = make_rsrc((const char*)((SPLIT && !SB) ? p.b_lo : p.b) + j0 * kbytes, (uint32_t)cols_wg * kbytes);
 
     double acc[JB][4];
 #pragma unroll
@@ -385,6 +402,17 @@ void xr_kernel(XrParams p) {
         for (int e = 0; e < 4; ++e) acc[jb][e] = 0.0;
     double xm2 = 0.0, xl2 = 0.0;   // |x_m|^2 and |x_lo,m|^2 of this lane's row (16-bit compute)
     f32x4 gx = f32x4{0.f, 0.f, 0.f, 0.f}, gl = f32x4{0.f, 0.f, 0.f, 0.f};   // Gram accumulators
+    // SB: Gram accumulators of the b rows of each column block (b and b_lo), and
+    // whether a block of the lane's b row could not be split
+    constexpr int JBS = SB ? JB : 1;
+    f32x4 gbb[JBS], gbl[JBS];
+    bool wideb[JBS];
+#pragma unroll
+    for (int jb = 0; jb < JBS; ++jb) {
+        gbb[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        gbl[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        wideb[jb] = false;
+    }
 
     const int KT = (int)((kbytes + 127) / 128);   // k blocks of 128 bytes
     const int ROUNDS = (KT + KS - 1) / KS;
@@ -476,11 +504,39 @@ void xr_kernel(XrParams p) {
             for (int jb = 0; jb < JB; ++jb) {
                 const int row = c0 + jb * 16 + (lane & 15);
                 f32x4 hh = f32x4{0.f, 0.f, 0.f, 0.f};
+                i32x4 bsh[2], bsl[2];   // SB: this block's split of the b row
+                if constexpr (SB) {
+                    i32x4 br[2];
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) br[s] = *(const i32x4*)(th + lds_off(row, s * 4 + (lane >> 4)));
+                    uint32_t mbb = absmax_bits(br[0]);
+                    const uint32_t n1 = absmax_bits(br[1]);
+                    mbb = mbb > n1 ? mbb : n1;
+                    const uint32_t q1 = (uint32_t)__shfl_xor((int)mbb, 16);
+                    mbb = mbb > q1 ? mbb : q1;
+                    const uint32_t q2 = (uint32_t)__shfl_xor((int)mbb, 32);
+                    mbb = mbb > q2 ? mbb : q2;
+                    const int gb = grid_exp<CT>(mbb);
+                    wideb[jb] |= (gb > 100);
+                    if (CT::dt == DT_F16 && __all(gb <= 5)) {
+                        split16_pk(br[0], gb, bsh[0], bsl[0]);
+                        split16_pk(br[1], gb, bsh[1], bsl[1]);
+                    } else {
+                        const float magic = __builtin_ldexpf(1.5f, (gb > 100 ? 100 : gb) + 23);
+                        split16<CT>(br[0], magic, bsh[0], bsl[0]);
+                        split16<CT>(br[1], magic, bsh[1], bsl[1]);
+                    }
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        gbb[SB ? jb : 0] = CT::step(br[s], br[s], gbb[SB ? jb : 0]);
+                        gbl[SB ? jb : 0] = CT::step(bsl[s], bsl[s], gbl[SB ? jb : 0]);
+                    }
+                }
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     const int kc = s * 4 + (lane >> 4);
-                    const i32x4 bh = *(const i32x4*)(th + lds_off(row, kc));
-                    const i32x4 bl = *(const i32x4*)(tl + lds_off(row, kc));
+                    const i32x4 bh = SB ? bsh[s] : *(const i32x4*)(th + lds_off(row, kc));
+                    const i32x4 bl = SB ? bsl[s] : *(const i32x4*)(tl + lds_off(row, kc));
                     hh = CT::step(bh, xh[s], hh);                                   // exact
                     f32x4 cx = CT::step(bl, xr[s], f32x4{0.f, 0.f, 0.f, 0.f});      // cross chain
                     cx = CT::step(bh, xlo[s], cx);
@@ -516,7 +572,7 @@ void xr_kernel(XrParams p) {
     __syncthreads();   // every wave is done with the stages (they hold the k-group reduction next)
 
     // LDS after the main loop: [k-group reduction][count][work list of guarded elements]
-    constexpr int W = JB * 4 + 3;
+    constexpr int W = JB * 4 + 3 + (SB ? JB * 2 : 0);
     constexpr int RED = KS > 1 ? (KS - 1) * CG * RW * 64 * W * 8 : 0;
     constexpr int CAP = RW * 16 * RP;                      // every element of the workgroup
     static_assert(RED + 16 + CAP * 4 <= NS * ST::BYTES, "reduction buffer and work list");
@@ -538,6 +594,22 @@ void xr_kernel(XrParams p) {
         xm2 = (double)__shfl(dx, src) * infl + steps * 0x1p-120;
         xl2 = (double)__shfl(dl, src) * infl + steps * 0x1p-120;
     }
+    // SB: the same for the b rows of every column block (lane l: the row
+    // l & 15 of the block; |b_lo|^2 = inf where a block of the row could not
+    // be split); the epilogue takes its columns' values from those lanes
+    float bsq[JBS][2];
+    if constexpr (SB) {
+        const int r = lane & 15, e = r & 3;
+        const int src = r + 16 * (r >> 2);
+        const double steps = 2.0 * ROUNDS;
+        const double infl = 1.0 + 2.0 * (GUARD_CROSS / 2) * 0x1p-24 * (steps + 1.0) + 0x1p-20;
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) {
+            const float db = __shfl(pick4(gbb[jb], e), src), dlo = __shfl(pick4(gbl[jb], e), src);
+            bsq[jb][0] = (float)((double)db * infl + steps * 0x1p-120);
+            bsq[jb][1] = wideb[jb] ? __builtin_inff() : (float)((double)dlo * infl + steps * 0x1p-120);
+        }
+    }
     // meet the k groups' partial sums in LDS (the B tiles are no longer needed)
     if (KS > 1) {
         double* red = (double*)sd;                 // [KS-1][CG][RW][64 lanes][W]
@@ -550,6 +622,13 @@ void xr_kernel(XrParams p) {
             dst[JB * 4] = xm2;
             dst[JB * 4 + 1] = xl2;
             dst[JB * 4 + 2] = wide ? 1.0 : 0.0;
+            if constexpr (SB) {
+#pragma unroll
+                for (int jb = 0; jb < JB; ++jb) {
+                    dst[JB * 4 + 3 + 2 * jb] = bsq[jb][0];
+                    dst[JB * 4 + 3 + 2 * jb + 1] = bsq[jb][1];
+                }
+            }
         }
     }
     __syncthreads();   // partial sums and the cleared count are visible
@@ -565,9 +644,17 @@ void xr_kernel(XrParams p) {
                 xm2 += src[JB * 4];
                 xl2 += src[JB * 4 + 1];
                 wide |= src[JB * 4 + 2] != 0.0;
+                if constexpr (SB) {
+                    // (the fp32 sums are rounded up by the epilogue's slack)
+#pragma unroll
+                    for (int jb = 0; jb < JB; ++jb) {
+                        bsq[jb][0] = (float)((double)bsq[jb][0] + src[JB * 4 + 3 + 2 * jb]);
+                        bsq[jb][1] = (float)((double)bsq[jb][1] + src[JB * 4 + 3 + 2 * jb + 1]);
+                    }
+                }
             }
         }
-        xr_epilogue<CT, JB>(p, acc, xm2, xl2, wide, wg_m0, j0, my_row, c0, cols_wg, lane, lcount, list);
+        xr_epilogue<CT, JB, SB>(p, acc, xm2, xl2, wide, wg_m0, j0, my_row, c0, cols_wg, lane, lcount, list, bsq);
     }
     // The guarded elements: every wave takes its share of the list and
     // overwrites the stored output with the value rounded from the fp64 dot
@@ -602,15 +689,23 @@ void xr_kernel(XrParams p) {
                 }
             }
         }
-        if (tid == 0 && n) atomicAdd(p.flagged, n);
+        if constexpr (SB) {
+            if (tid == 0) p.flagged[blockIdx.y * gridDim.x + blockIdx.x] = n;
+        } else {
+            if (tid == 0 && n) atomicAdd(p.flagged, n);
+        }
+    } else if (SB && tid == 0) {
+        p.flagged[blockIdx.y * gridDim.x + blockIdx.x] = 0u;   // no guard: nothing re-evaluated
     }
 }
 
-template <class CT, int JB, int KS, int CG, int RW = xr_row_groups(KS)>
+template <class CT, int JB, int KS, int CG, int RW = xr_row_groups(KS), bool SB = false>
 static hipError_t run_xr(const XrParams& p, hipStream_t s) {
     constexpr int RP = JB * 16 * CG;
     const dim3 grid((unsigned)((p.M + RW * 16 - 1) / (RW * 16)), (unsigned)((p.Nc + RP - 1) / RP));
-    hipLaunchKernelGGL((xr_kernel<CT, JB, KS, CG, RW>), grid, dim3(64 * RW * KS * CG), 0, s, p);
+    // per-workgroup guard counts: the caller's slots must cover the grid
+    if (SB && (int64_t)grid.x * grid.y > p.flag_slots) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((xr_kernel<CT, JB, KS, CG, RW, SB>), grid, dim3(64 * RW * KS * CG), 0, s, p);
     return hipGetLastError();
 }
 
@@ -623,13 +718,35 @@ static int pick_ks(int64_t M, int64_t col_tiles) {
 
 // KSMAX 8: where 16 rows per workgroup are needed, 8 k groups (two waves per
 // SIMD) instead of 4
-template <class CT, int JB, int CG, int KSMAX>
+template <class CT, int JB, int CG, int KSMAX, bool SB = false>
 static hipError_t run_xr_jb(const XrParams& p, hipStream_t s) {
     const int64_t col_tiles = (p.Nc + JB * 16 * CG - 1) / (JB * 16 * CG);
     const int ks = pick_ks(p.M, col_tiles);
-    if (ks == 1 || KSMAX == 1) return run_xr<CT, JB, 1, CG>(p, s);
-    if (ks == 2 || KSMAX == 2) return run_xr<CT, JB, (KSMAX >= 2 ? 2 : 1), CG>(p, s);
-    return run_xr<CT, JB, (KSMAX >= 4 ? KSMAX : 1), CG>(p, s);
+    constexpr int K2 = KSMAX >= 2 ? 2 : 1, K4 = KSMAX >= 4 ? KSMAX : 1;
+    // (with b split in the kernel, one b tile per stage: a single k group's
+    // loads would not divide among its waves, so it takes two)
+    if constexpr (!SB) {
+        if (ks == 1 || KSMAX == 1) return run_xr<CT, JB, 1, CG, xr_row_groups(1), SB>(p, s);
+    }
+    if (ks <= 2 || KSMAX == 2) return run_xr<CT, JB, K2, CG, xr_row_groups(K2), SB>(p, s);
+    return run_xr<CT, JB, K4, CG, xr_row_groups(K4), SB>(p, s);
+}
+
+// The plain affine form under 16-bit compute: 64 x 64 tiles (8 waves, two k
+// groups) where there are at least 256 of them, W split beforehand by the
+// row-norm pass (its four row-group waves would each split the same 64 W rows
+// again: measured 28.5 + 7.1 us against 40.6 us in one launch at
+// 1024 x 768 x 1024); else 16-column workgroups with up to 8 k groups and W
+// split in the kernel (one launch: 19.0 -> 12.0 us at M = 16, 24.4 -> 15.7 us
+// at M = 128).  Returns the latter launch's workgroup count (its guard-count
+// slots), or 0 where the row-norm pass is used.
+int64_t xr_affine_workgroups(int64_t M, int64_t N) {
+    const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
+    if (t64 >= 256) return 0;
+    const int64_t col_tiles = (N + 15) / 16;
+    const int ks = pick_ks(M, col_tiles);
+    const int rw = ks <= 2 ? xr_row_groups(2) : xr_row_groups(8);   // run_xr_jb<CT, 1, 1, 8, true>
+    return ((M + rw * 16 - 1) / (rw * 16)) * col_tiles;
 }
 
 // Columns per wave (JB blocks of 16), column groups (CG), k groups (KS) and
@@ -639,13 +756,11 @@ static hipError_t run_xr_jb(const XrParams& p, hipStream_t s) {
 template <class CT>
 static hipError_t run_xr_ct(const XrParams& p, hipStream_t s) {
     if (p.mode == XR_AFFINE) {
-        // 16-bit compute: with at least 256 tiles of 64 x 64, 8 waves (two
-        // k groups) per tile; with fewer, 16 columns per workgroup and 8 k
-        // groups, so that more CUs share the rows of W.  fp32 compute keeps the
-        // 4-wave 64-column split.
+        // 16-bit compute: the launches xr_affine_workgroups describes; fp32
+        // compute keeps the 4-wave 64-column split
         if constexpr (CT::dt != DT_F32) {
             if (((p.M + 63) / 64) * ((p.Nc + 63) / 64) >= 256) return run_xr<CT, 4, 2, 1, 4>(p, s);
-            return run_xr_jb<CT, 1, 1, 8>(p, s);
+            return run_xr_jb<CT, 1, 1, 8, true>(p, s);
         }
         return run_xr_jb<CT, 4, 1, 4>(p, s);
     }

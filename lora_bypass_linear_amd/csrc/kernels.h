@@ -66,13 +66,17 @@ void gemm_tile_dims(int tile, int* tn, int* tm);
 enum { XR_H = 0, XR_AFFINE = 1 };
 struct XrParams {
     const void* x;          // [M,K] compute dtype
-    const void* b;          // [Nc,K] compute dtype: b_hi (16-bit compute) or b itself (fp32)
-    const void* b_lo;       // [Nc,K] b - b_hi (16-bit compute)
+    const void* b;          // [Nc,K] compute dtype: b_hi (16-bit h pass), else b itself
+    const void* b_lo;       // [Nc,K] b - b_hi (16-bit h pass)
     const void* b_full;     // [Nc,K] b (down_c or W_c), for the fp64 re-evaluation
-    const double2* bnorm;   // [Nc] {|b_j|_2, |b_lo,j|_2}
+    const double2* bnorm;   // [Nc] {|b_j|_2, |b_lo,j|_2} (16-bit h pass)
     int64_t M, Nc, K;
     int guard;              // 1: apply the rounding guard (16-bit rounding target)
-    unsigned* flagged;      // count of re-evaluated elements (zeroed beforehand)
+    // count of re-evaluated elements: h pass, one counter (zeroed beforehand);
+    // plain affine form under 16-bit compute, one per workgroup (flag_slots
+    // of them, each written by its workgroup; their sum is the count)
+    unsigned* flagged;
+    int64_t flag_slots = 0;
     int mode;               // XR_H or XR_AFFINE
     void* out;              // h [M][ld_out] (compute dtype) or y [M][ld_out] (out_dt)
     int64_t ld_out;
@@ -116,6 +120,9 @@ int gemm_ksplit(int64_t M, int64_t N, int64_t K, int c_dt);
 // the output tile launch_gemm uses for this shape
 void gemm_tile_shape(int64_t M, int64_t N, int c_dt, int* tn, int* tm);
 hipError_t launch_xr(int c_dt, const XrParams& p, hipStream_t s);
+// workgroups of the plain affine form's launch under 16-bit compute (its
+// guard-count slots)
+int64_t xr_affine_workgroups(int64_t M, int64_t N);
 // hi/lo split (per 64-k block) of each row of b [rows,K] (16-bit compute
 // dtype) and {|b_j|_2, |b_lo,j|_2}; also clears *flagged (if not null)
 hipError_t launch_rownorm(const void* b, int c_dt, int64_t rows, int64_t K, void* b_hi, void* b_lo, double2* out,

@@ -49,8 +49,8 @@ def gpu_forward(inputs: Dict[str, torch.Tensor], wl: WL.Workload, scale: Optiona
     ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
     y = L.linear(d["x"], d["w"], d.get("b"), workspace=ws)
     torch.cuda.synchronize()
-    fo = L.linear_workspace_layout(*args)
-    flagged = int(ws[fo: fo + 4].cpu().view(torch.int32).item()) if nb > 0 else None
+    fo, ns = L.linear_workspace_layout(*args)
+    flagged = int(ws[fo: fo + 4 * ns].cpu().view(torch.int32).sum().item()) if ns > 0 else None
     return y.cpu(), None, flagged
 
 

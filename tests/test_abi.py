@@ -134,9 +134,15 @@ def test_workspace_sizes():
     assert n16 >= 1000 * 32 * 2 + 32 * 64 * 2 + 300 * 32 * 2 + 32 * 8
     ho, ld, fo = L.lora_workspace_layout(1000, 300, 64, 17, 1, 1, 0, 1, 1)
     assert ld == 32 and ho % 256 == 0 and fo % 256 == 0 and fo < n16
-    # affine: row norms of W for the projection guard (+ a bf16 copy of an fp32 W)
-    assert L.linear_workspace_size(64, 64, 64, 1, 1) >= 64 * 16
-    assert L.linear_workspace_size(64, 32, 64, 2, 3) >= 32 * 64 * 2 + 32 * 16
+    # affine: one guard count per workgroup of the contraction (+ a bf16 copy of an fp32 W)
+    fo, ns = L.linear_workspace_layout(64, 64, 64, 1, 1)
+    assert ns >= 1 and L.linear_workspace_size(64, 64, 64, 1, 1) >= fo + 4 * ns
+    assert L.linear_workspace_layout(1024, 1024, 768, 1, 1)[1] == 1           # 64 x 64 tiles: W split beforehand
+    assert L.linear_workspace_size(1024, 1024, 768, 1, 1) >= 2 * 1024 * 768 * 2
+    assert L.linear_workspace_layout(16, 1024, 768, 1, 1)[1] == 64            # 16 x 16 workgroups, 8 k groups
+    assert L.linear_workspace_layout(256, 512, 768, 1, 1)[1] == 8 * 32        # 32-row workgroups, 2 k groups
+    assert L.linear_workspace_size(64, 32, 64, 2, 3) >= 32 * 64 * 2
+    assert L.linear_workspace_layout(64, 32, 64, 3, 3)[1] == 0                # fp32 compute: no guard
     assert L.lora_workspace_size(8, 8, 8, 0, 1, 1, 0, 1, 1) == 0        # rank 0: no bypass
     for r, pad in ((1, 16), (16, 16), (17, 32), (32, 32), (33, 64), (64, 64), (65, 128), (129, 256), (256, 256)):
         assert L.lora_workspace_layout(16, 16, 16, r, 2, 2, 0, 2, 2)[1] == pad
