@@ -220,7 +220,7 @@ def _forward_bench(dev, wl, inputs, steps, warmup):
     # dominant kernel: the fused main contraction (fold + K loop + epilogue) of
     # the LoRA path, or the plain affine path's contraction (recorded as the
     # GEMM kind)
-    dom = "gemm" if lora else "affine"
+    dom = "gemm" if lora else "hpass"
     n_g, t_g = prof["gemm"]
     dom_ms = t_g / max(n_g, 1)
     dom_flops = 2.0 * wl.M * wl.N * wl.K + (2.0 * wl.M * wl.r * wl.N if lora else 0.0)
@@ -229,7 +229,8 @@ def _forward_bench(dev, wl, inputs, steps, warmup):
     from lora_bypass_linear_amd.profsum import read_traffic
     traffic = read_traffic(os.path.join(ROOT, "profiles", f"traffic_{dom}_{wl.name}.txt"), dom)
     tflops = wl.flops / (ms_per_step * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": "gemm_kernel", "achieved": round(achieved, 2), "peak": peak,
+    roofline = {"bound": "mfma", "kernel": "gemm_kernel" if lora else "xr_kernel", "achieved": round(achieved, 2),
+                "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": None if traffic is None else int(traffic),
                 "flops_per_launch": dom_flops, "avg_us": round(dom_ms * 1e3, 3)}
