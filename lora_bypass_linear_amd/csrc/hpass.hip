@@ -11,21 +11,23 @@
 //
 // Method (16-bit compute).  K is cut into blocks of 64.  In each block a row
 // of x and a row of b (down_c or W_c) are split as v = v_hi + v_lo, v_hi the
-// value rounded to the grid 2^(e-7), e = floor(log2 max|v|) over the block.
+// value rounded to the grid 2^(e-8), e = floor(log2 max|v|) over the block
+// (v_hi is at most 2^9 grid units and representable in either 16-bit format).
 //   hh:    b_hi . x_hi   every product is an integer times the block's grid
-//                        product with magnitude <= 2^16, so every partial sum
-//                        of the block's 64 products is an integer below 2^22
-//                        times that grid: exact in fp32 however the MFMA
-//                        orders or aligns its additions.  Added to an fp64
-//                        accumulator once per block (exact).
-//   cross: b_lo . x + b_hi . x_lo   small (|v_lo| <= 2^(e-8)); one MFMA chain
+//                        product with magnitude <= 2^18, so every partial sum
+//                        of the block's 64 products is an integer of magnitude
+//                        at most 2^24 times that grid: exact in fp32 however
+//                        the MFMA orders or aligns its additions.  Added to an
+//                        fp64 accumulator once per block (exact).
+//   cross: b_lo . x + b_hi . x_lo   small (|v_lo| <= 2^(e-9)); one MFMA chain
 //                        per 32-k step, added to the fp64 accumulator.
 // gfx950 MFMA steps keep about two bits below the ulp of their running sum
 // and truncate (measured), so a step adding terms of total magnitude S to an
 // accumulator C errs by less than 18 * 2^-24 * (|C| + S); the cross chain of
 // a step therefore errs by less than 36 * 2^-24 * S_cross, and over all steps
 // (Cauchy-Schwarz on the sums of |products|)
-//   E(m, j) = 36 * 2^-24 * (|x_m| |b_lo,j| + |x_lo,m| (|b_j| + |b_lo,j|)) + fp64 slack,
+//   E(m, j) = 36 * 2^-24 * (|x_m| |b_lo,j| + |x_lo,m| (|b_j| + |b_lo,j|)) + fp64 slack
+//             + K * 2^-120 (fp32 underflow: products of bf16 values far below 1),
 // with |x_m| and |x_lo,m| the diagonals of the MFMA Gram matrices of x and
 // x_lo (inflated by their own step error) and the norms of b from the
 // preparation pass.
@@ -84,17 +86,17 @@ __device__ __forceinline__ uint32_t absmax_bits(i32x4 v) {
     return m;
 }
 
-// grid exponent g = floor(log2 m) - 7 of a positive 16-bit magnitude m (bits)
+// grid exponent g = floor(log2 m) - 8 of a positive 16-bit magnitude m (bits)
 template <class CT>
 __device__ __forceinline__ int grid_exp(uint32_t m) {
     if (CT::dt == DT_F16) {
         const int E = (int)(m >> 10);
         const int e = E > 0 ? E - 15 : (31 - __builtin_clz(m | 1u)) - 24;
-        return e - 7;
+        return e - 8;
     }
     const int E = (int)(m >> 7);
     const int e = E > 0 ? E - 127 : (31 - __builtin_clz(m | 1u)) - 133;
-    return e - 7;
+    return e - 8;
 }
 
 // Split a fragment on the grid 2^g (round to nearest): hi on the grid, lo = v - hi.
@@ -114,10 +116,13 @@ __device__ __forceinline__ void split16(i32x4 v, float magic, i32x4& hi, i32x4& 
 
 // The same split for fp16 in packed fp16 arithmetic (three v_pk_add_f16 per
 // 4 bytes instead of the unpack / fp32 / repack sequence): with
-// M = 1.5 * 2^(g+10), v + M lies in [1.25, 1.75] * 2^(g+10) for |v| < 2^(g+8)
-// and rounds to a multiple of 2^g (ties to even), t - M is exact, and so is
-// v - hi (hi is a multiple of the ulp of v, and hi = 0 wherever |v| < 2^(g-2)).
-// M must be a normal fp16 value: g <= 5 (callers check), and a grid finer
+// M = 1.5 * 2^(g+10), v + M lies in (1, 2) * 2^(g+10) for |v| < 2^(g+9) and
+// rounds to a multiple of 2^g (ties to even; 2^(g+11) at most), t - M is
+// exact, and so is v - hi (2^g is a multiple of the ulp of every v of the
+// block, and hi = 0 wherever |v| < 2^(g-1)).
+// The sum stays finite and M is a normal fp16 value for g <= 4 (callers
+// check: at g = 5 values just below 2^14 would round v + M up to 2^16, which
+// overflows fp16), and a grid finer
 // than fp16's smallest subnormal 2^-24 is taken as 2^-24 (every value of such
 // a block is on it: hi = v, lo = 0).
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -244,6 +249,13 @@ __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB]
         const double as = __builtin_fabs(p.scale);
         const double A = 0x1p-24 * GUARD_CROSS * xn2 * slack * as, B = 0x1p-24 * GUARD_CROSS * xln * slack * as;
         const double C = 0x1p-37 * xn2 * slack * as;
+        // fp32 products and partial sums below 2^-126 (bf16 operands far
+        // below 1) may be flushed, or rounded on fp32's subnormal grid, and a
+        // grid product below 2^-149 makes the hi.hi sums inexact: either way
+        // an MFMA step loses less than 33 * 2^-126 (32 products and its
+        // result), and an element takes 6 steps per 64-k block, so an
+        // absolute K * 2^-120 covers the whole contraction
+        const double D = (double)p.K * 0x1p-120 * as;
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) {
             double2 b2[4];   // {|b|, |b_lo|} of the lane's 4 columns of this block
@@ -267,7 +279,7 @@ __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB]
             for (int e = 0; e < 4; ++e) {
                 const int jl = c0 + jb * 16 + 4 * (lane >> 4) + e;
                 const double h = acc[jb][e] * p.scale;
-                const double E = A * b2[e].y + B * (b2[e].x + b2[e].y) + C * b2[e].x;
+                const double E = A * b2[e].y + B * (b2[e].x + b2[e].y) + C * b2[e].x + D;
                 const uint16_t lo = round16<CT>(h - E);
                 r16[jb][e] = lo;
                 const bool bwide = !(b2[e].y < 1e300);   // a block of b could not be split
@@ -484,7 +496,7 @@ void xr_kernel(XrParams p) {
             const int g = grid_exp<CT>(mb);
             wide |= (g > 100);
             i32x4 xh[2], xlo[2];
-            if (CT::dt == DT_F16 && __all(g <= 5)) {
+            if (CT::dt == DT_F16 && __all(g <= 4)) {
                 split16_pk(xr[0], g, xh[0], xlo[0]);
                 split16_pk(xr[1], g, xh[1], xlo[1]);
             } else {
@@ -518,7 +530,7 @@ void xr_kernel(XrParams p) {
                     mbb = mbb > q2 ? mbb : q2;
                     const int gb = grid_exp<CT>(mbb);
                     wideb[jb] |= (gb > 100);
-                    if (CT::dt == DT_F16 && __all(gb <= 5)) {
+                    if (CT::dt == DT_F16 && __all(gb <= 4)) {
                         split16_pk(br[0], gb, bsh[0], bsl[0]);
                         split16_pk(br[1], gb, bsh[1], bsl[1]);
                     } else {

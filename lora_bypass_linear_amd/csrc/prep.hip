@@ -42,7 +42,7 @@ __device__ __forceinline__ void store16(void* dst, int64_t i, float v, int c_dt)
 // the 8 consecutive elements k0 + 8t .. 8t+7, so an aligned 64-k block is held
 // by 8 neighbouring lanes.  Optionally writes the row's compute-dtype copy;
 // for 16-bit compute also its split v = hi + lo per 64-k block (hi = v rounded
-// to the grid 2^(e-7), e = floor(log2 max|v|) of the block, the same split the
+// to the grid 2^(e-8), e = floor(log2 max|v|) of the block, the same split the
 // contraction applies to x); returns {|v|_2, |lo|_2}.  A block whose grid
 // exponent exceeds 100 cannot be split with the fp32 rounding constant: |lo|_2
 // is then reported as +inf, which makes the contraction re-evaluate that row's
@@ -114,7 +114,7 @@ __device__ void row_pass(const void* src, int src_dt, int c_dt, int64_t row, int
             int g = 0;
             float magic = 0.f;
             if (mx > 0.f) {
-                g = floor_log2(mx) - 7;
+                g = floor_log2(mx) - 8;
                 wide |= g > 100;
                 magic = __builtin_ldexpf(1.5f, (g > 100 ? 100 : g) + 23);
             }

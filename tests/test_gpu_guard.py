@@ -3,10 +3,10 @@
 The h pass marks an element (m, j) for fp64 re-evaluation when the interval
 [h - E, h + E] straddles a rounding boundary of the 16-bit compute format, with
 
-    E = 36 * 2^-24 * (|x_m| |b_lo,j| + |x_lo,m| (|b_j| + |b_lo,j|)) + 2^-37 |x_m| |b_j|
+    E = 36 * 2^-24 * (|x_m| |b_lo,j| + |x_lo,m| (|b_j| + |b_lo,j|)) + 2^-37 |x_m| |b_j| + K 2^-120
 
 where v = v_hi + v_lo is the split of every 64-k block of a row on the grid
-2^(floor(log2 max|v|) - 7).  A guard whose E came out too small (a wrong norm,
+2^(floor(log2 max|v|) - 8).  A guard whose E came out too small (a wrong norm,
 a dropped term) would still pass the element-wise parity tests as long as no
 rounding happened to flip, so the number of flagged elements is checked here
 against the same bound evaluated on the CPU from the exact h and exact norms.
@@ -30,7 +30,7 @@ def _split(v: np.ndarray):
     pad = (-K) % 64
     vb = np.pad(v, ((0, 0), (0, pad))).reshape(rows, -1, 64)
     mx = np.abs(vb).max(axis=2, keepdims=True)
-    g = np.floor(np.log2(np.where(mx > 0, mx, 1.0))) - 7
+    g = np.floor(np.log2(np.where(mx > 0, mx, 1.0))) - 8
     q = np.ldexp(1.0, g.astype(np.int64))
     hi = np.round(vb / q) * q
     lo = (vb - hi).reshape(rows, -1)[:, :K]
@@ -46,7 +46,7 @@ def _expected_flags(inputs, ct, b_name="down") -> int:
     xln = np.linalg.norm(xl, axis=1)[:, None]
     bn = np.linalg.norm(b, axis=1)[None, :]
     bln = np.linalg.norm(bl, axis=1)[None, :]
-    E = 36 * 2.0 ** -24 * (xn * bln + xln * (bn + bln)) + 2.0 ** -37 * xn * bn
+    E = 36 * 2.0 ** -24 * (xn * bln + xln * (bn + bln)) + 2.0 ** -37 * xn * bn + x.shape[1] * 2.0 ** -120
 
     def r16(v):
         return torch.from_numpy(v).to(ct).double().numpy()   # fp64 -> 16-bit, round to nearest even

@@ -272,6 +272,19 @@ def test_h_guard_resolves_midpoints():
     _check(wl, inputs=inputs)
 
 
+@pytest.mark.parametrize("shift", [58, 62, 66])
+def test_h_exact_near_fp32_underflow(shift):
+    """bf16 x and down scaled by 2^-shift, so that the h products sit near and
+    below fp32's smallest normal 2^-126 (and h itself, at the largest shift,
+    in bf16's subnormal range): h_r must still be the correctly rounded exact
+    value however the fp32 MFMA partial sums treat values that small."""
+    wl = BASE["lora_bf16_16384x8192x8192_r128"].resized(M=96, N=64, K=640, r=16)
+    inputs = WL.generate(wl)
+    for k in ("x", "down"):
+        inputs[k] = (inputs[k].double() * 2.0 ** -shift).to(torch.bfloat16)
+    _check(wl, inputs=inputs)
+
+
 # ---- the full-size workloads, in the launch configuration the benchmark uses -----
 
 FULL = ["affine_f16_1024x768x1024", "lora_f16_4096x3072x3072_r16", "lora_bf16x_f32w_8192x4096x4096_r64",

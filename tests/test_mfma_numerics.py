@@ -217,18 +217,22 @@ def test_fp32_step_layout_exact():
 
 def _split(v, dt):
     """hi/lo split of [T,16,64] blocks as the kernels do it: hi = v rounded to
-    the grid 2^(floor(log2 max|v|) - 7) of its row's 64-k block, lo = v - hi."""
+    the grid 2^(floor(log2 max|v|) - 8) of its row's 64-k block, lo = v - hi."""
     mx = np.abs(v).max(axis=-1, keepdims=True)
     e = np.floor(np.log2(np.where(mx > 0, mx, 1.0)))
-    q = 2.0 ** (e - 7)
+    q = 2.0 ** (e - 8)
     hi = np.rint(v / q) * q
     return hi, v - hi
 
 
 @pytest.mark.parametrize("dt", [1, 2])
-@pytest.mark.parametrize("kind", ["gaussian", "lognormal", "wide"])
+@pytest.mark.parametrize("kind", ["gaussian", "lognormal", "wide", "extreme"])
 def test_split_hi_steps_exact(dt, kind):
-    """Two chained 32-k steps of hi parts (one 64-k block) are exact."""
+    """Two chained 32-k steps of hi parts (one 64-k block) are exact.
+    "extreme": one sign per row, most elements just below 2 (hi parts of 2^9
+    grid units under fp16, 510 under bf16) and a quarter of them small grid
+    multiples (1..255 units), so that the block's sum comes within 2^18 units
+    of the 2^24 the exactness argument allows and needs every low bit."""
     rng = np.random.default_rng(7)
     T = 512
     if kind == "gaussian":
@@ -236,9 +240,16 @@ def test_split_hi_steps_exact(dt, kind):
     elif kind == "lognormal":
         x = rng.standard_normal((T, 16, 64)) * np.exp(rng.standard_normal((T, 16, 1)) * 2)
         d = rng.standard_normal((T, 16, 64)) * np.exp(rng.standard_normal((T, 16, 1)))
-    else:
+    elif kind == "wide":
         x = rng.choice([-1, 1], (T, 16, 64)) * 2.0 ** rng.integers(-10, 10, (T, 16, 64))
         d = rng.choice([-1, 1], (T, 16, 64)) * 2.0 ** rng.integers(-10, 10, (T, 16, 64))
+    else:
+        top = 2.0 - (2.0 ** -10 if dt == 1 else 2.0 ** -7)
+        small = lambda: rng.integers(1, 256, (T, 16, 64)) * 2.0 ** -8
+        pick = lambda: rng.random((T, 16, 64)) < 0.25
+        x = np.where(pick(), small(), top) * rng.choice([-1, 1], (T, 1, 1))
+        d = np.where(pick(), small(), top) * rng.choice([-1, 1], (T, 1, 1))
+        x[:, :, 0] = d[:, :, 0] = top                       # every row keeps its block maximum
     x = _bits(x, dt).double().numpy()
     d = _bits(d, dt).double().numpy()
     xh, _ = _split(x, dt)
