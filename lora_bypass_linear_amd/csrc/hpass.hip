@@ -20,13 +20,18 @@
 //                        the MFMA orders or aligns its additions.  Added to an
 //                        fp64 accumulator once per block (exact).
 //   cross: b_lo . x + b_hi . x_lo   small (|v_lo| <= 2^(e-9)); one MFMA chain
-//                        per 32-k step, added to the fp64 accumulator.
+//                        per 32-k step, the block's two chains added in fp32
+//                        and then to the fp64 accumulator.
+// Both sums of a column block are added to the fp64 accumulator while the
+// MFMAs of the next column block run (the conversions and fp64 adds are a
+// large part of the vector work, and they then overlap the matrix pipe).
 // gfx950 MFMA steps keep about two bits below the ulp of their running sum
 // and truncate (measured), so a step adding terms of total magnitude S to an
 // accumulator C errs by less than 18 * 2^-24 * (|C| + S); the cross chain of
-// a step therefore errs by less than 36 * 2^-24 * S_cross, and over all steps
-// (Cauchy-Schwarz on the sums of |products|)
-//   E(m, j) = 36 * 2^-24 * (|x_m| |b_lo,j| + |x_lo,m| (|b_j| + |b_lo,j|)) + fp64 slack
+// a 32-k step therefore errs by less than 36 * 2^-24 * S_chain, the fp32 sum
+// of a block's two chains adds at most 2^-24 * (S_0 + S_1) (1 + 36 * 2^-24),
+// and over all blocks (Cauchy-Schwarz on the sums of |products|)
+//   E(m, j) = 38 * 2^-24 * (|x_m| |b_lo,j| + |x_lo,m| (|b_j| + |b_lo,j|)) + fp64 slack
 //             + K * 2^-120 (fp32 underflow: products of bf16 values far below 1),
 // with |x_m| and |x_lo,m| the diagonals of the MFMA Gram matrices of x and
 // x_lo (inflated by their own step error) and the norms of b from the
@@ -53,9 +58,12 @@
 
 namespace lyc {
 
-// Step error factor of the cross chain, in units of 2^-24 of its absolute sums
-// (two chained steps, each below 18 * 2^-24 of |accumulator| + sum|products|).
-constexpr double GUARD_CROSS = 36.0;
+// Error of one MFMA step, in units of 2^-24 of |accumulator| + sum|products|
+// (measured bound), and of a block's cross sum, in units of 2^-24 of its
+// absolute sums: two chains of two steps (2 * STEP_ERR) and the fp32 add of
+// the two (1, rounded up to leave room for the second-order term).
+constexpr double STEP_ERR = 18.0;
+constexpr double GUARD_CROSS = 2.0 * STEP_ERR + 2.0;
 
 template <class CT>
 __device__ __forceinline__ float unpack_lo(uint32_t u) {
@@ -468,6 +476,10 @@ void xr_kernel(XrParams p) {
     } while (0)
 
     bool wide = false;   // a block beyond the split's exponent range: re-evaluate the row
+    // hi.hi sum and the two cross sums of the column block before the current
+    // one (16-bit compute, b split beforehand; after a k block's last column
+    // block, those of JB - 1), added to acc while the current one's MFMAs run
+    f32x4 phh = f32x4{0.f, 0.f, 0.f, 0.f}, pc0 = phh, pc1 = phh;
     if (ROUNDS > 0) {
         // rounds 0 .. NS-1 fill every stage; round 0 must land
 #pragma unroll
@@ -512,13 +524,11 @@ void xr_kernel(XrParams p) {
                 gl = CT::step(xlo[s], xlo[s], gl);
             }
             const char* tl = th + TILE;             // this k group's b_lo tile
+            if constexpr (SB) {
 #pragma unroll
-            for (int jb = 0; jb < JB; ++jb) {
-                const int row = c0 + jb * 16 + (lane & 15);
-                f32x4 hh = f32x4{0.f, 0.f, 0.f, 0.f};
-                i32x4 bsh[2], bsl[2];   // SB: this block's split of the b row
-                if constexpr (SB) {
-                    i32x4 br[2];
+                for (int jb = 0; jb < JB; ++jb) {
+                    const int row = c0 + jb * 16 + (lane & 15);
+                    i32x4 br[2], bsh[2], bsl[2];   // this block's b row and its split
 #pragma unroll
                     for (int s = 0; s < 2; ++s) br[s] = *(const i32x4*)(th + lds_off(row, s * 4 + (lane >> 4)));
                     uint32_t mbb = absmax_bits(br[0]);
@@ -529,7 +539,7 @@ void xr_kernel(XrParams p) {
                     const uint32_t q2 = (uint32_t)__shfl_xor((int)mbb, 32);
                     mbb = mbb > q2 ? mbb : q2;
                     const int gb = grid_exp<CT>(mbb);
-                    wideb[jb] |= (gb > 100);
+                    wideb[SB ? jb : 0] |= (gb > 100);
                     if (CT::dt == DT_F16 && __all(gb <= 4)) {
                         split16_pk(br[0], gb, bsh[0], bsl[0]);
                         split16_pk(br[1], gb, bsh[1], bsl[1]);
@@ -538,25 +548,78 @@ void xr_kernel(XrParams p) {
                         split16<CT>(br[0], magic, bsh[0], bsl[0]);
                         split16<CT>(br[1], magic, bsh[1], bsl[1]);
                     }
+                    f32x4 hh = f32x4{0.f, 0.f, 0.f, 0.f}, cs = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s = 0; s < 2; ++s) {
                         gbb[SB ? jb : 0] = CT::step(br[s], br[s], gbb[SB ? jb : 0]);
                         gbl[SB ? jb : 0] = CT::step(bsl[s], bsl[s], gbl[SB ? jb : 0]);
+                        hh = CT::step(bsh[s], xh[s], hh);                                   // exact
+                        f32x4 cx = CT::step(bsl[s], xr[s], f32x4{0.f, 0.f, 0.f, 0.f});      // cross chain
+                        cx = CT::step(bsh[s], xlo[s], cx);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) cs[e] = s == 0 ? cx[e] : cs[e] + cx[e];
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc[jb][e] += (double)hh[e];
+                        acc[jb][e] += (double)cs[e];
                     }
                 }
+            } else {
+                // b fragments {hi, lo} x {k half 0, 1} of a column block, read one
+                // column block ahead; each column block's MFMAs share their
+                // stretch of the schedule with the fold of the previous one's sums
+                i32x4 bq[4];
+                const int kc0 = lane >> 4, rl = c0 + (lane & 15);
+                bq[0] = *(const i32x4*)(th + lds_off(rl, kc0));
+                bq[1] = *(const i32x4*)(tl + lds_off(rl, kc0));
+                bq[2] = *(const i32x4*)(th + lds_off(rl, 4 + kc0));
+                bq[3] = *(const i32x4*)(tl + lds_off(rl, 4 + kc0));
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const int kc = s * 4 + (lane >> 4);
-                    const i32x4 bh = SB ? bsh[s] : *(const i32x4*)(th + lds_off(row, kc));
-                    const i32x4 bl = SB ? bsl[s] : *(const i32x4*)(tl + lds_off(row, kc));
-                    hh = CT::step(bh, xh[s], hh);                                   // exact
-                    f32x4 cx = CT::step(bl, xr[s], f32x4{0.f, 0.f, 0.f, 0.f});      // cross chain
-                    cx = CT::step(bh, xlo[s], cx);
+                for (int jb = 0; jb < JB; ++jb) {
+                    // the previous column block's sums enter this stretch here (an
+                    // empty asm pins them, so the fold below cannot move up to
+                    // the MFMAs that produce them)
+                    asm volatile("" : "+v"(phh), "+v"(pc0), "+v"(pc1));
+                    i32x4 bn[4];
+                    if (jb + 1 < JB) {
+                        const int rn = rl + (jb + 1) * 16;
+                        bn[0] = *(const i32x4*)(th + lds_off(rn, kc0));
+                        bn[1] = *(const i32x4*)(tl + lds_off(rn, kc0));
+                        bn[2] = *(const i32x4*)(th + lds_off(rn, 4 + kc0));
+                        bn[3] = *(const i32x4*)(tl + lds_off(rn, 4 + kc0));
+                    }
+                    const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+                    f32x4 hh = CT::step(bq[0], xh[0], z);          // exact
+                    f32x4 c0 = CT::step(bq[1], xr[0], z);          // cross chains
+                    f32x4 c1 = CT::step(bq[3], xr[1], z);
+                    hh = CT::step(bq[2], xh[1], hh);
+                    c0 = CT::step(bq[0], xlo[0], c0);
+                    c1 = CT::step(bq[2], xlo[1], c1);
+                    const int pj = jb == 0 ? JB - 1 : jb - 1;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[jb][e] += (double)cx[e];
+                    for (int e = 0; e < 4; ++e) {
+                        acc[pj][e] += (double)phh[e];
+                        acc[pj][e] += (double)(pc0[e] + pc1[e]);
+                    }
+                    // ... and the fold is done before the stretch ends
+                    asm volatile("" : "+v"(acc[pj][0]), "+v"(acc[pj][1]), "+v"(acc[pj][2]), "+v"(acc[pj][3]));
+                    phh = hh;
+                    pc0 = c0;
+                    pc1 = c1;
+                    if (jb + 1 < JB) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) bq[i] = bn[i];
+                    }
+                    // MFMA, then a few vector ops, in turn (next fragments' reads first)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+                    for (int i = 0; i < 6; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[jb][e] += (double)hh[e];
             }
         } else {
 #pragma unroll
@@ -581,6 +644,13 @@ void xr_kernel(XrParams p) {
         }
     }
 #undef LYC_ISSUE_ROUND
+    if (SPLIT && !SB) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[JB - 1][e] += (double)phh[e];
+            acc[JB - 1][e] += (double)(pc0[e] + pc1[e]);
+        }
+    }
     __syncthreads();   // every wave is done with the stages (they hold the k-group reduction next)
 
     // LDS after the main loop: [k-group reduction][count][work list of guarded elements]
@@ -602,7 +672,7 @@ void xr_kernel(XrParams p) {
         const float dx = pick4(gx, e), dl = pick4(gl, e);
         const int src = r + 16 * (r >> 2);
         const double steps = 2.0 * ROUNDS;
-        const double infl = 1.0 + 2.0 * (GUARD_CROSS / 2) * 0x1p-24 * (steps + 1.0) + 0x1p-20;
+        const double infl = 1.0 + 2.0 * STEP_ERR * 0x1p-24 * (steps + 1.0) + 0x1p-20;
         xm2 = (double)__shfl(dx, src) * infl + steps * 0x1p-120;
         xl2 = (double)__shfl(dl, src) * infl + steps * 0x1p-120;
     }
@@ -614,7 +684,7 @@ void xr_kernel(XrParams p) {
         const int r = lane & 15, e = r & 3;
         const int src = r + 16 * (r >> 2);
         const double steps = 2.0 * ROUNDS;
-        const double infl = 1.0 + 2.0 * (GUARD_CROSS / 2) * 0x1p-24 * (steps + 1.0) + 0x1p-20;
+        const double infl = 1.0 + 2.0 * STEP_ERR * 0x1p-24 * (steps + 1.0) + 0x1p-20;
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) {
             const float db = __shfl(pick4(gbb[jb], e), src), dlo = __shfl(pick4(gbl[jb], e), src);

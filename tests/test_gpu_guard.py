@@ -3,7 +3,7 @@
 The h pass marks an element (m, j) for fp64 re-evaluation when the interval
 [h - E, h + E] straddles a rounding boundary of the 16-bit compute format, with
 
-    E = 36 * 2^-24 * (|x_m| |b_lo,j| + |x_lo,m| (|b_j| + |b_lo,j|)) + 2^-37 |x_m| |b_j| + K 2^-120
+    E = 38 * 2^-24 * (|x_m| |b_lo,j| + |x_lo,m| (|b_j| + |b_lo,j|)) + 2^-37 |x_m| |b_j| + K 2^-120
 
 where v = v_hi + v_lo is the split of every 64-k block of a row on the grid
 2^(floor(log2 max|v|) - 8).  A guard whose E came out too small (a wrong norm,
@@ -46,7 +46,7 @@ def _expected_flags(inputs, ct, b_name="down") -> int:
     xln = np.linalg.norm(xl, axis=1)[:, None]
     bn = np.linalg.norm(b, axis=1)[None, :]
     bln = np.linalg.norm(bl, axis=1)[None, :]
-    E = 36 * 2.0 ** -24 * (xn * bln + xln * (bn + bln)) + 2.0 ** -37 * xn * bn + x.shape[1] * 2.0 ** -120
+    E = 38 * 2.0 ** -24 * (xn * bln + xln * (bn + bln)) + 2.0 ** -37 * xn * bn + x.shape[1] * 2.0 ** -120
 
     def r16(v):
         return torch.from_numpy(v).to(ct).double().numpy()   # fp64 -> 16-bit, round to nearest even

@@ -29,7 +29,7 @@ SRC = os.path.join(os.path.dirname(HERE), "lora_bypass_linear_amd", "csrc", "hpa
 
 
 def step_factor():
-    return float(re.search(r"GUARD_CROSS\s*=\s*([0-9.]+)", open(SRC).read()).group(1)) / 2
+    return float(re.search(r"STEP_ERR\s*=\s*([0-9.]+)", open(SRC).read()).group(1))
 
 
 def check_model(A, B, D, C=None):
