@@ -365,12 +365,13 @@ def _merge(dev, wl, inputs, reps, warm, accuracy):
     dev_us = sum(ms for _, ms in prof.values()) * 1e3 / reps
     from lora_bypass_linear_amd.profsum import read_traffic
     traffic = read_traffic(os.path.join(ROOT, "profiles", f"traffic_merge_{wl.name}.txt"), "merge")
+    kname = _merge_kernel_name(c_dt, dts[0], dts[1], dts[2], o_dt, wl.K, wl.r)
     r = {"shape": f"W [{wl.N},{wl.K}] {WL.NAME[wl.w_dt]}, rank {wl.r}, scale {wl.scale}",
          "wall_us_per_call": round(wall_us, 2), "device_us_per_call": round(dev_us, 2),
-         "kernels": {{"prep": "merge_prep_kernel", "gemm": "merge_kernel"}.get(k, k):
+         "kernels": {{"prep": "merge_prep_kernel", "gemm": kname}.get(k, k):
                      {"launches": n, "avg_us": round(ms * 1e3 / n, 3)} for k, (n, ms) in prof.items() if n},
          "hbm_gbs_call": round(nbytes / (dev_us * 1e-6) / 1e9, 1),
-         "roofline": {"bound": "hbm", "kernel": "merge_kernel",
+         "roofline": {"bound": "hbm", "kernel": kname,
                       "achieved": round(nbytes / (g_us * 1e-6) / 1e9, 1), "peak": HBM_GBS, "unit": "GB/s",
                       "frac": round(nbytes / (g_us * 1e-6) / 1e9 / HBM_GBS, 4),
                       "traffic": None if traffic is None else int(traffic), "bytes_per_launch": nbytes,
@@ -392,6 +393,15 @@ def _merge(dev, wl, inputs, reps, warm, accuracy):
                   "eager": {"max_ulp": round(se["ulp_max"], 4), "rms_ulp": round(se["ulp_rms"], 4),
                             "tol_fail": se["fail"]}})
     return r
+
+
+def _merge_kernel_name(c_dt, w_dt, d_dt, u_dt, o_dt, K, r):
+    """The merge kernel the library launches for these dtypes and sizes: the
+    streaming form takes 16-bit compute with W, W' and both factors in it (read
+    as stored, so rank and K multiples of 8) and a padded rank up to 128."""
+    import lora_bypass_linear_amd as L
+    half = c_dt in (L.F16, L.BF16) and w_dt == c_dt and o_dt == c_dt and d_dt == c_dt and u_dt == c_dt
+    return "merge_stream_kernel" if half and K % 8 == 0 and r % 8 == 0 and 0 < r <= 128 else "merge_kernel"
 
 
 def _dora(dev, wl, inputs, reps, warm, accuracy):
@@ -433,6 +443,8 @@ def _dora(dev, wl, inputs, reps, warm, accuracy):
     nbytes = wl.N * wl.K * es[w_dt] + wl.r * wl.K * es[d_dt] + wl.N * wl.r * es[u_dt] + wl.N * 4
     n_g, t_g = prof_n["gemm"]
     g_us = t_g * 1e3 / max(n_g, 1)
+    c_dt, o_dt = L.resolve_dtypes([w_dt, d_dt, u_dt])
+    kname = _merge_kernel_name(c_dt, w_dt, d_dt, u_dt, c_dt, wl.K, wl.r)
     y = L.dora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, m, norms, d.get("b"))
     wall_f, prof_f = timed_calls(lambda: L.dora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, m, norms,
                                                        d.get("b"), out=y))
@@ -442,7 +454,7 @@ def _dora(dev, wl, inputs, reps, warm, accuracy):
     dev_us = lambda prof: round(sum(ms for _, ms in prof.values()) * 1e3 / reps, 2)
     out = {"shape": f"M {wl.M}, N {wl.N}, K {wl.K}, rank {wl.r}, magnitude {WL.NAME[L.dtype_code(m)]}",
            "norms": {"wall_us_per_call": round(wall_n, 2), "device_us_per_call": dev_us(prof_n),
-                     "roofline": {"bound": "hbm", "kernel": "merge_kernel (row norms)",
+                     "roofline": {"bound": "hbm", "kernel": kname + " (row norms)",
                                   "achieved": round(nbytes / (g_us * 1e-6) / 1e9, 1), "peak": HBM_GBS,
                                   "unit": "GB/s", "frac": round(nbytes / (g_us * 1e-6) / 1e9 / HBM_GBS, 4),
                                   "traffic": None, "bytes_per_launch": nbytes, "avg_us": round(g_us, 3)}},

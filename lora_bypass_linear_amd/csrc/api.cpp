@@ -377,6 +377,25 @@ bool merge_reads_as_stored(const Merge& G, const void* down, const void* up) {
            G.K % 8 == 0 && aligned(down, 16) && aligned(up, 16) && G.rank * G.K * 2 < ((int64_t)1 << 31);
 }
 
+// The factors' preparation pass (down^T_c and up_c), unless both are read as stored
+int merge_prepare(const Merge& G, const void* down, const void* up, bool raw, char* W, hipStream_t s) {
+    if (G.r_pad == 0 || raw) return LYC_OK;
+    lyc::MergePrepParams mp{};
+    mp.down = down;
+    mp.down_dt = G.d_dt;
+    mp.up = up;
+    mp.up_dt = G.u_dt;
+    mp.dt_c = W + G.dt_c;
+    mp.uc = W + G.uc;
+    mp.N = G.N;
+    mp.K = G.K;
+    mp.rank = G.rank;
+    mp.r_pad = G.r_pad;
+    mp.c_dt = G.c_dt;
+    return timed(LYC_KERNEL_PREP, s, [&] { return lyc::launch_merge_prep(mp, s); }) == hipSuccess ? LYC_OK
+                                                                                               : LYC_ERR_HIP;
+}
+
 int merge(const Merge& G, const void* w, const void* down, const void* up, double scale, void* out, int out_dt,
           void* ws, size_t ws_bytes, void* stream) {
     if (out_dt != G.o_dt) return LYC_ERR_DTYPE_MISMATCH;
@@ -397,21 +416,6 @@ int merge(const Merge& G, const void* w, const void* down, const void* up, doubl
     char* W = (char*)ws;
     (void)hipGetLastError();
     const bool raw = merge_reads_as_stored(G, down, up);
-    if (G.r_pad > 0 && !raw) {
-        lyc::MergePrepParams mp{};
-        mp.down = down;
-        mp.down_dt = G.d_dt;
-        mp.up = up;
-        mp.up_dt = G.u_dt;
-        mp.dt_c = W + G.dt_c;
-        mp.uc = W + G.uc;
-        mp.N = G.N;
-        mp.K = G.K;
-        mp.rank = G.rank;
-        mp.r_pad = G.r_pad;
-        mp.c_dt = G.c_dt;
-        if (timed(LYC_KERNEL_PREP, s, [&] { return lyc::launch_merge_prep(mp, s); }) != hipSuccess) return LYC_ERR_HIP;
-    }
     lyc::MergeParams mg{};
     mg.w = w;
     mg.w_dt = G.w_dt;
@@ -431,6 +435,7 @@ int merge(const Merge& G, const void* w, const void* down, const void* up, doubl
         mg.up_raw = up;
         mg.rank = G.rank;
     }
+    if (merge_prepare(G, down, up, raw, W, s) != LYC_OK) return LYC_ERR_HIP;
     if (timed(LYC_KERNEL_GEMM, s, [&] { return lyc::launch_merge(G.c_dt, mg, s); }) != hipSuccess) return LYC_ERR_HIP;
     return LYC_OK;
 }
@@ -996,21 +1001,6 @@ int lyc_dora_norms(const void* w, int w_dt, const void* down, int down_dt, const
         return lyc::launch_transpose(tp, s) == hipSuccess ? LYC_OK : LYC_ERR_HIP;
     }
     const bool raw = merge_reads_as_stored(G, down, up);
-    if (G.r_pad > 0 && !raw) {
-        lyc::MergePrepParams mp{};
-        mp.down = down;
-        mp.down_dt = down_dt;
-        mp.up = up;
-        mp.up_dt = up_dt;
-        mp.dt_c = W + G.dt_c;
-        mp.uc = W + G.uc;
-        mp.N = N;
-        mp.K = K;
-        mp.rank = rank;
-        mp.r_pad = G.r_pad;
-        mp.c_dt = G.c_dt;
-        if (timed(LYC_KERNEL_PREP, s, [&] { return lyc::launch_merge_prep(mp, s); }) != hipSuccess) return LYC_ERR_HIP;
-    }
     lyc::MergeParams mg{};
     mg.w = w;
     mg.w_dt = w_dt;
@@ -1031,8 +1021,9 @@ int lyc_dora_norms(const void* w, int w_dt, const void* down, int down_dt, const
         mg.up_raw = up;
         mg.rank = G.rank;
     }
+    if (merge_prepare(G, down, up, raw, W, s) != LYC_OK) return LYC_ERR_HIP;
     if (timed(LYC_KERNEL_GEMM, s, [&] { return lyc::launch_merge(G.c_dt, mg, s); }) != hipSuccess) return LYC_ERR_HIP;
-    if (timed(LYC_KERNEL_PREP, s, [&] { return lyc::launch_norm_finish(mg, s); }) != hipSuccess) return LYC_ERR_HIP;
+    if (timed(LYC_KERNEL_PREP, s, [&] { return lyc::launch_norm_finish(G.c_dt, mg, s); }) != hipSuccess) return LYC_ERR_HIP;
     return LYC_OK;
 }
 

@@ -47,8 +47,11 @@ struct MergeParams {
     int64_t rank = 0;
 };
 hipError_t launch_merge(int c_dt, const MergeParams& p, hipStream_t s);
-// after launch_merge in the norm mode: norms[n] = sqrt(sum of the tiles' partials, in tile order)
-hipError_t launch_norm_finish(const MergeParams& p, hipStream_t s);
+// whether launch_merge takes the streaming form for these parameters (16-bit
+// compute, W and W' in it, down and up read as stored, K a multiple of 8)
+bool merge_streams(int c_dt, const MergeParams& p);
+// after launch_merge in the norm mode: norms[n] = sqrt(sum of the partials, in order)
+hipError_t launch_norm_finish(int c_dt, const MergeParams& p, hipStream_t s);
 // gain[n] = m[n] / norms[n] in fp32 (the DoRA forward's per-feature factor)
 hipError_t launch_dora_gain(const void* m, int m_dt, const float* norms, int64_t N, float* gain, hipStream_t s);
 

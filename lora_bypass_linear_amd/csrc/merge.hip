@@ -1,10 +1,17 @@
 // merge.hip -- the LoRA merge W' = round_out(W + scale * up_c . down_c)
 // (LyCORIS "Precision" page: "Dtype policy" with the original weight as the
-// input operand, and the merge figure of "Measured accuracy").
+// input operand, and the merge figure of "Measured accuracy"), and the DoRA
+// row norms of the merged weight (same page, "VRAM").
 //
 // The merge streams W in and W' out once: 4-6 bytes per element against
-// 2 r flops, so it is bound by HBM for every rank the library takes.  One
-// workgroup owns a 128 x 128 tile of W:
+// 2 r flops, so it is bound by HBM for every rank the library takes.  Two
+// forms:
+//  * streaming (merge_stream_kernel, below): 16-bit W, W' and factors read
+//    as stored, rank up to 128 -- one workgroup per CU walks 16-row tiles
+//    down a band of 512 columns, W staged through LDS several tiles ahead,
+//    down's band held as MFMA fragments in registers;
+//  * general (merge_kernel): any dtypes, ranks and alignments.  One
+//    workgroup owns a 128 x 128 tile of W:
 //   1. the first rank chunk of up_c and down^T_c is requested, then the whole
 //      W tile, 16 bytes per lane in row order (coalesced), into registers,
 //      non-temporally (W and W' pass through once; the rank operands, re-read
@@ -16,7 +23,7 @@
 //   3. the fp32 accumulators go through LDS once more, so that
 //   4. each lane meets the W elements it loaded: W' = fma(scale, acc, W),
 //      rounded once, stored 16 bytes per lane in row order.
-// 67.5 KiB of LDS and at most 256 VGPRs: two workgroups per CU.
+//   67.5 KiB of LDS and at most 256 VGPRs: two workgroups per CU.
 #include "lyc_device.h"
 #include "merge.h"
 
@@ -279,6 +286,287 @@ __global__ __launch_bounds__(256, (WF || !VEC) ? 2 : 3) void merge_kernel(MergeP
     }
 }
 
+// ---- streaming form: 16-bit W, W' and factors, read as stored ----------------
+// One workgroup of 8 waves per CU owns a band of 512 columns of W and walks a
+// run of 16-row tiles down it, so that W is read and written in pieces of 1
+// KiB per row.  down's 512 columns of the band are turned into MFMA fragments
+// once (staged in LDS, read by the transposing LDS read) and stay in
+// registers; each tile of W (16 rows x 1 KiB) and the tile's 16 rows of up
+// are staged in LDS by direct-to-LDS loads NS-1 tiles ahead.  Wave w owns the
+// tile's columns 64w .. 64w+63: after its MFMAs every lane holds 4
+// consecutive k of one row per 16 x 16 block, an 8-byte piece of the staged W
+// row, so W' = round_out(fma(scale, acc, W)) is written back over it in
+// place, and the tile then leaves LDS one row per wave store.  The norm mode
+// sums v^2 per row and tile instead (one partial per row and band, added up
+// after the next tile's barrier).
+namespace {
+constexpr int ST_N = 16, ST_K = 512;         // tile rows (n) and band columns (k)
+constexpr int ST_RB = ST_K * 2;              // bytes of a staged W row
+constexpr int ST_W = ST_N * ST_RB;           // bytes of a staged W tile
+constexpr int ST_STORES = ST_W / 16 / 512;   // 16-byte stores per thread and tile
+// up rows of a tile: one sub-tile of 16 rows x 128 bytes per 64 of the padded rank
+template <int RP> constexpr int st_sub() { return RP <= 64 ? 1 : RP / 64; }
+template <int RP> constexpr int st_bytes() { return ST_W + st_sub<RP>() * ST_N * 128; }
+template <int RP> constexpr int st_ql() { return st_bytes<RP>() / 1024; }   // 1 KiB loads per tile
+// stages: as many as fit beside 1 KiB of sums (6 or 7 tiles in flight), so
+// that enough bytes are on their way from HBM to cover its latency
+template <int RP> constexpr int st_ns() { return (159 * 1024) / st_bytes<RP>() > 8 ? 8 : (159 * 1024) / st_bytes<RP>(); }
+template <int RP> constexpr int st_stages() { return st_ns<RP>() * st_bytes<RP>(); }
+// down's band: max(RP, 32) rank rows of 1 KiB, behind the stages where that
+// fits, else over them (it is read once, before the stages fill)
+template <int RP> constexpr int st_setup() { return (RP < 32 ? 32 : RP) * ST_RB; }
+template <int RP> constexpr bool st_apart() { return st_stages<RP>() + st_setup<RP>() + 1024 <= 150 * 1024; }
+template <int RP> constexpr int st_setup_at() { return st_apart<RP>() ? st_stages<RP>() : 0; }
+template <int RP> constexpr int st_red_at() {
+    return st_apart<RP>() ? st_stages<RP>() + st_setup<RP>()
+                          : (st_stages<RP>() > st_setup<RP>() ? st_stages<RP>() : st_setup<RP>());
+}
+template <int RP> constexpr int st_lds() { return st_red_at<RP>() + 2 * 8 * ST_N * 4; }
+}  // namespace
+
+// s_waitcnt vmcnt(min(n, N)) for a wave-uniform n (a smaller count only waits longer)
+template <int N>
+__device__ __forceinline__ void wait_vm_dyn(int n) {
+    if constexpr (N == 0) {
+        wait_vm<0>();
+    } else {
+        if (n >= N) wait_vm<N>();
+        else wait_vm_dyn<N - 1>(n);
+    }
+}
+
+// buffer resource over rows n0 .. n0+15 of a [N][K] 16-bit matrix (fewer at the end)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rows(const void* base, int64_t n0, int64_t N, int64_t K) {
+    const int64_t rows = N - n0 < ST_N ? N - n0 : ST_N;
+    return make_rsrc_uniform((const char*)base + n0 * K * 2, (uint32_t)(rows * K * 2));
+}
+
+// Direct-to-LDS loads of one tile: W's 16 rows over the band, one row per
+// load (chunk c of row r in slot c ^ (r & 15) of its 1 KiB row), and up's 16
+// rows, 64 rank values per sub-tile (chunk c of row r in slot c ^ (r & 7),
+// lds_off), two loads per sub-tile.  Wave w takes loads w, w + 8, ...
+// Offsets past K, the rank or the tile's rows read zeros.
+template <int RP>
+__device__ __forceinline__ void stream_issue(char* stage, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t ru,
+                                             int64_t kb0, int64_t K, int64_t rank, int wave, int lane) {
+    constexpr int QL = st_ql<RP>();
+#pragma unroll
+    for (int u = 0; u < (QL + 7) / 8; ++u) {
+        const int q = wave + 8 * u;   // loads 0..15: W; then up, 2 per sub-tile
+        if (q >= QL) break;
+        auto* dst = (__attribute__((address_space(3))) void*)(stage + q * 1024);
+        if (u < ST_N / 8) {
+            const int row = q, c = lane ^ (row & 15);
+            const int64_t k = kb0 + 8 * c;
+            const uint32_t off = k < K ? (uint32_t)(((int64_t)row * K + k) * 2) : OOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, off, 0, 0, 0);
+        } else {
+            const int qu = q - ST_N, sub = qu >> 1, row = (qu & 1) * 8 + (lane >> 3);
+            const int64_t r = 64 * sub + 8 * ((lane & 7) ^ (row & 7));
+            const uint32_t off = r < rank ? (uint32_t)(((int64_t)row * rank + r) * 2) : OOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, dst, 16, off, 0, 0, 0);
+        }
+    }
+}
+
+template <class CT, int RP, bool NORM>
+__global__ __launch_bounds__(512, 1) void merge_stream_kernel(MergeParams p, int runs) {
+    constexpr int SB = st_bytes<RP>(), NS = st_ns<RP>();
+    constexpr int RS = RP < 32 ? 1 : RP / 32;   // 32-wide rank steps
+    constexpr int QW = st_ql<RP>() / 8;         // loads per wave and tile, at least
+    __shared__ __attribute__((aligned(16))) char sm[st_lds<RP>()];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // the wave's 64 columns of the band
+
+    // the workgroup's band of columns and run of row tiles
+    const int band = (int)blockIdx.x / runs, run = (int)blockIdx.x % runs;
+    const int64_t kb0 = (int64_t)band * ST_K;
+    const int NT = (int)((p.N + ST_N - 1) / ST_N);
+    const int t0 = (int)((int64_t)NT * run / runs), nt = (int)((int64_t)NT * (run + 1) / runs) - t0;
+
+    // down's band (rank rows past its end and columns past K read 0), then its
+    // fragments for the wave's 64 columns into registers
+    i32x4 af[4][RS];
+    {
+        constexpr int DR = RP < 32 ? 32 : RP;
+        char* setup = sm + st_setup_at<RP>();
+        const auto rd = make_rsrc_uniform(p.down_raw, (uint32_t)(p.rank * p.K * 2));
+#pragma unroll
+        for (int u = 0; u < DR / 8; ++u) {
+            const int row = wave + 8 * u;
+            const int64_t k = kb0 + 8 * (lane ^ tswz<64>(row));
+            const uint32_t off = (row < p.rank && k < p.K) ? (uint32_t)(((int64_t)row * p.K + k) * 2) : OOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (__attribute__((address_space(3))) void*)(setup + row * 1024),
+                                                     16, off, 0, 0, 0);
+        }
+        wait_vm<0>();
+        lds_barrier();
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int rs = 0; rs < RS; ++rs) af[kb][rs] = frag_t<ST_K>(setup, 32 * rs, 64 * wave + 16 * kb, lane);
+        // the stages may overlay the band: every wave has its fragments first
+        lds_barrier();
+    }
+
+    for (int i = 0; i < NS - 1; ++i)
+        if (i < nt) {
+            const int64_t n0 = (int64_t)(t0 + i) * ST_N;
+            stream_issue<RP>(sm + i * SB, stream_rows(p.w, n0, p.N, p.K), stream_rows(p.up_raw, n0, p.N, p.rank), kb0,
+                             p.K, p.rank, wave, lane);
+        }
+    // norm mode: per-row sums of the 8 waves, [tile parity][wave][16 rows]; a
+    // tile's are added up after the next tile's barrier
+    float* red = (float*)(sm + st_red_at<RP>());
+
+    // unrolled by the stage count: every stage address is a constant offset
+    for (int i0 = 0; i0 < nt; i0 += NS)
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+        const int i = i0 + u;
+        if (i >= nt) break;
+        // tile i has landed once at most the operations issued after its loads
+        // are outstanding: the loads of the tiles after it and, storing, the
+        // stores of the tiles before it issued since
+        const int la = nt - 1 - i < NS - 2 ? nt - 1 - i : NS - 2;
+        const int sa = NORM ? 0 : (i < NS - 1 ? i : NS - 1);
+        wait_vm_dyn<31>(QW * la + ST_STORES * sa);
+        lds_barrier();   // every wave's loads of tile i are in; tile i-1's stage is free
+        if (NORM && i > 0 && tid < ST_N) {
+            const float* rp = red + ((i - 1) & 1) * (8 * ST_N);
+            const int64_t n = (int64_t)(t0 + i - 1) * ST_N + tid;
+            float t = rp[tid];
+#pragma unroll
+            for (int w = 1; w < 8; ++w) t += rp[w * ST_N + tid];
+            if (n < p.N) p.norm_partial[(int64_t)band * p.N + n] = t;
+        }
+        if (i + NS - 1 < nt) {
+            const int64_t nn = (int64_t)(t0 + i + NS - 1) * ST_N;
+            stream_issue<RP>(sm + ((u + NS - 1) % NS) * SB, stream_rows(p.w, nn, p.N, p.K),
+                             stream_rows(p.up_raw, nn, p.N, p.rank), kb0, p.K, p.rank, wave, lane);
+        }
+        char* st = sm + u * SB;
+        const int64_t n0 = (int64_t)(t0 + i) * ST_N;
+
+        i32x4 bq[RS];
+        const int row = lane & 15;
+#pragma unroll
+        for (int rs = 0; rs < RS; ++rs)
+            bq[rs] = *(const i32x4*)(st + ST_W + (rs >> 1) * (ST_N * 128) + lds_off(row, (rs & 1) * 4 + (lane >> 4)));
+        // the lane's 4 pieces of the staged W row, all read before any is
+        // written back (a store first would make the compiler wait for it
+        // before the next read), then the 4 column blocks' MFMAs interleaved
+        char* wa[4];
+        i32x2 wv[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int cb = 128 * wave + 32 * kb + 8 * (lane >> 4);   // byte of the lane's 4 columns in the row
+            wa[kb] = st + row * ST_RB + (((cb >> 4) ^ row) << 4) + (cb & 15);
+            wv[kb] = *(const i32x2*)wa[kb];
+        }
+        f32x4 acc[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rs = 0; rs < RS; ++rs)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) acc[kb] = CT::step(af[kb][rs], bq[rs], acc[kb]);
+        float ss = 0.f;   // norm mode: the lane's sum of v^2 over its 16 columns of the tile
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int64_t kc = kb0 + 64 * wave + 16 * kb + 4 * (lane >> 4);   // the lane's first column
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint16_t b = (uint16_t)((uint32_t)wv[kb][e >> 1] >> ((e & 1) * 16));
+                const float w = CT::dt == DT_F16 ? f16_to_f32(b) : bf16_to_f32(b);
+                v[e] = __builtin_fmaf(p.scale, acc[kb][e], w);
+            }
+            if constexpr (NORM) {
+                const bool rin = n0 + row < p.N;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool in = rin && kc + e < p.K;
+                    ss = __builtin_fmaf(in ? v[e] : 0.f, in ? v[e] : 0.f, ss);
+                }
+            } else {
+                const uint32_t o0 = CT::dt == DT_F16 ? pack_f16x2(v[0], v[1]) : pack_bf16x2(v[0], v[1]);
+                const uint32_t o1 = CT::dt == DT_F16 ? pack_f16x2(v[2], v[3]) : pack_bf16x2(v[2], v[3]);
+                *(i32x2*)wa[kb] = i32x2{(int)o0, (int)o1};
+            }
+        }
+        if constexpr (NORM) {
+            // the 4 lanes of each row (a fixed butterfly); the waves' sums are
+            // added in order after the next barrier
+            ss += __shfl_xor(ss, 16, 64);
+            ss += __shfl_xor(ss, 32, 64);
+            if (lane < 16) red[(i & 1) * (8 * ST_N) + wave * ST_N + row] = ss;
+        } else {
+            lds_barrier();   // the tile's merged values are all in LDS
+            // out one 1 KiB row per wave store, nontemporal (W' is not read
+            // again here; 46.8 against 52.0 us at bf16 8192 x 8192); every store
+            // is issued (past K or past the tile's rows its offset is out of
+            // range), so the wait counts above hold
+            const auto ro = stream_rows(p.out, n0, p.N, p.K);
+#pragma unroll
+            for (int h = 0; h < ST_STORES; ++h) {
+                const int r = 8 * h + wave, c = lane;
+                const i32x4 v = *(const i32x4*)(st + r * ST_RB + ((c ^ r) << 4));
+                const int64_t k = kb0 + 8 * c;
+                const uint32_t off = k < p.K ? (uint32_t)(((int64_t)r * p.K + k) * 2) : OOB;
+                __builtin_amdgcn_raw_buffer_store_b128(v, ro, off, 0, 2);   // nontemporal
+            }
+        }
+    }
+    if constexpr (NORM) {
+        lds_barrier();
+        if (nt > 0 && tid < ST_N) {
+            const float* rp = red + ((nt - 1) & 1) * (8 * ST_N);
+            const int64_t n = (int64_t)(t0 + nt - 1) * ST_N + tid;
+            float t = rp[tid];
+#pragma unroll
+            for (int w = 1; w < 8; ++w) t += rp[w * ST_N + tid];
+            if (n < p.N) p.norm_partial[(int64_t)band * p.N + n] = t;
+        }
+    }
+}
+
+bool merge_streams(int c_dt, const MergeParams& p) {
+    if (c_dt != DT_F16 && c_dt != DT_BF16) return false;
+    if (p.w_dt != c_dt || (p.norm_partial == nullptr && p.out_dt != c_dt)) return false;
+    return p.vec && p.down_raw != nullptr && p.up_raw != nullptr && p.rank > 0 && p.r_pad <= 128 &&
+           p.K * 2 * ST_N < ((int64_t)1 << 31) && p.rank * p.K * 2 < ((int64_t)1 << 31) &&
+           p.rank * 2 * ST_N < ((int64_t)1 << 31);
+}
+
+// runs (of row tiles) per band of 512 columns: about one workgroup per CU in all
+static int merge_stream_runs(const MergeParams& p) {
+    const int64_t bands = (p.K + ST_K - 1) / ST_K, nt = (p.N + ST_N - 1) / ST_N;
+    int64_t runs = 256 / bands;
+    if (runs > nt) runs = nt;
+    return runs < 1 ? 1 : (int)runs;
+}
+
+template <class CT, int RP>
+static hipError_t run_merge_stream(const MergeParams& p, hipStream_t s) {
+    const int runs = merge_stream_runs(p);
+    const dim3 g((unsigned)(((p.K + ST_K - 1) / ST_K) * runs));
+    if (p.norm_partial != nullptr) hipLaunchKernelGGL((merge_stream_kernel<CT, RP, true>), g, dim3(512), 0, s, p, runs);
+    else hipLaunchKernelGGL((merge_stream_kernel<CT, RP, false>), g, dim3(512), 0, s, p, runs);
+    return hipGetLastError();
+}
+
+template <class CT>
+static hipError_t run_merge_stream_rp(const MergeParams& p, hipStream_t s) {
+    switch (p.r_pad) {
+    case 16: return run_merge_stream<CT, 16>(p, s);
+    case 32: return run_merge_stream<CT, 32>(p, s);
+    case 64: return run_merge_stream<CT, 64>(p, s);
+    case 128: return run_merge_stream<CT, 128>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 // DoRA row norms: the tiles' partial sums of squares of each row, added in
 // tile order, then the square root (fp32)
 __global__ __launch_bounds__(256) void norm_finish_kernel(const float* partial, int tiles_k, int64_t N, float* norms) {
@@ -296,9 +584,10 @@ __global__ __launch_bounds__(256) void norm_finish_kernel(const float* partial, 
     norms[n] = (float)__builtin_sqrt((double)s);
 }
 
-hipError_t launch_norm_finish(const MergeParams& p, hipStream_t s) {
+hipError_t launch_norm_finish(int c_dt, const MergeParams& p, hipStream_t s) {
     if (p.N <= 0) return hipSuccess;
-    const int tiles_k = (int)((p.K + MC - 1) / MC);
+    // partials per row: one per band of 256 columns (streaming form), else per 128-column tile
+    const int tiles_k = (int)((p.K + (merge_streams(c_dt, p) ? ST_K : MC) - 1) / (merge_streams(c_dt, p) ? ST_K : MC));
     hipLaunchKernelGGL(norm_finish_kernel, dim3((unsigned)((p.N + 255) / 256)), dim3(256), 0, s, p.norm_partial,
                        tiles_k, p.N, p.norms);
     return hipGetLastError();
@@ -406,6 +695,8 @@ static hipError_t run_merge(const MergeParams& p, hipStream_t s) {
 }
 
 hipError_t launch_merge(int c_dt, const MergeParams& p, hipStream_t s) {
+    if (merge_streams(c_dt, p))
+        return c_dt == DT_F16 ? run_merge_stream_rp<CF16>(p, s) : run_merge_stream_rp<CBF16>(p, s);
     const bool wf = p.w_dt == DT_F32, of = p.out_dt == DT_F32;
     if (wf && !of) return hipErrorInvalidValue;   // the policy promotes an fp32 W to an fp32 W'
     switch (c_dt) {
