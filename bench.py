@@ -237,9 +237,9 @@ def _forward_bench(dev, wl, inputs, steps, warmup):
     kernels = {k: {"launches": n, "avg_us": round(t * 1e3 / n, 3)} for k, (n, t) in prof.items() if n}
     guard = None
     if lora and wl.r > 0 and c_dt != L.F32:
-        _, _, fo = L.lora_workspace_layout(wl.M, wl.N, wl.K, wl.r, dts[0], dts[1], b_dt, L.dtype_code(d["down"]),
-                                           L.dtype_code(d["up"]))
-        nflag = int(ws[fo: fo + 4].cpu().view(torch.int32).item())
+        _, _, fo, ns = L.lora_workspace_layout(wl.M, wl.N, wl.K, wl.r, dts[0], dts[1], b_dt,
+                                               L.dtype_code(d["down"]), L.dtype_code(d["up"]))
+        nflag = int(ws[fo: fo + 4 * ns].cpu().view(torch.int32).sum().item())
         guard = {"h_reevaluated_fp64": nflag, "of": wl.M * wl.r, "fraction": round(nflag / (wl.M * wl.r), 6)}
     elif not lora and c_dt != L.F32:
         fo, ns = L.linear_workspace_layout(wl.M, wl.N, wl.K, dts[0], dts[1], b_dt)

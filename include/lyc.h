@@ -165,12 +165,18 @@ int lyc_lora_linear_fwd_noalloc(const void* x, int x_dt, const void* w, int w_dt
  *   h_offset:  byte offset of h_r, [M][h_ld] in the compute dtype (columns
  *              >= rank are zero);
  *   h_ld:      leading dimension of h_r in elements (r_pad);
- *   flagged_offset: byte offset of a uint32 count of h elements that the
- *              guard re-evaluated in fp64 during the last call.
+ *   flagged_offset: byte offset of `*flagged_slots` uint32 counts whose sum
+ *              is the number of h elements that the rounding guard
+ *              re-evaluated during the last call: in fp64 after the split
+ *              contraction (one count), or, for few token rows (M <= 128 and
+ *              M * r_pad * K <= 2^25, h as one fp64 dot per element), by a
+ *              compensated re-summation (one count per workgroup);
+ *   flagged_slots: their number.
  * Any out-pointer may be NULL.  Same argument errors as the size query.
  */
 int lyc_lora_workspace_layout(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt, int bias_dt,
-                              int down_dt, int up_dt, size_t* h_offset, int64_t* h_ld, size_t* flagged_offset);
+                              int down_dt, int up_dt, size_t* h_offset, int64_t* h_ld, size_t* flagged_offset,
+                              int64_t* flagged_slots);
 
 /*
  * Where lyc_linear_fwd keeps its guard counts inside the workspace:

@@ -64,7 +64,8 @@ def lib():
         L.lyc_lora_linear_fwd_noalloc.argtypes = [c_vp, c_int, c_vp, c_int, c_vp, c_int, c_vp, c_int, c_vp, c_int,
                                                   c_i64, ctypes.c_double, c_vp, c_int, c_i64, c_i64, c_i64, c_vp]
         L.lyc_lora_workspace_layout.argtypes = [c_i64, c_i64, c_i64, c_i64, c_int, c_int, c_int, c_int, c_int,
-                                                ctypes.POINTER(c_sz), ctypes.POINTER(c_i64), ctypes.POINTER(c_sz)]
+                                                ctypes.POINTER(c_sz), ctypes.POINTER(c_i64), ctypes.POINTER(c_sz),
+                                                ctypes.POINTER(c_i64)]
         L.lyc_linear_workspace_layout.argtypes = [c_i64, c_i64, c_i64, c_int, c_int, c_int, ctypes.POINTER(c_sz),
                                                   ctypes.POINTER(c_i64)]
         L.lyc_lora_merge_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_int, c_int, c_int, ctypes.POINTER(c_sz)]
@@ -218,11 +219,13 @@ def lora_workspace_size(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt) -> int:
 
 
 def lora_workspace_layout(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt):
-    """(h_offset, h_ld, flagged_offset) inside the LoRA workspace."""
-    ho, ld, fo = ctypes.c_size_t(0), ctypes.c_int64(0), ctypes.c_size_t(0)
+    """(h_offset, h_ld, flagged_offset, flagged_slots) inside the LoRA
+    workspace: the guard's uint32 counts at flagged_offset, flagged_slots of
+    them, sum to the number of re-evaluated h elements."""
+    ho, ld, fo, ns = ctypes.c_size_t(0), ctypes.c_int64(0), ctypes.c_size_t(0), ctypes.c_int64(0)
     _check(lib().lyc_lora_workspace_layout(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt, ctypes.byref(ho),
-                                           ctypes.byref(ld), ctypes.byref(fo)))
-    return ho.value, ld.value, fo.value
+                                           ctypes.byref(ld), ctypes.byref(fo), ctypes.byref(ns)))
+    return ho.value, ld.value, fo.value, ns.value
 
 
 def linear_workspace_layout(M, N, K, x_dt, w_dt, b_dt=0):

@@ -95,6 +95,12 @@ struct Layout {
     bool cast_x = false, cast_w = false;
 };
 
+// h for few token rows: one wave per element (fp64 dots), in place of the
+// split contraction, whose single workgroup would walk all of K
+bool hdot_path(const Problem& P) {
+    return P.lora && P.r_pad > 0 && P.K > 0 && P.M <= 128 && (double)P.M * (double)P.r_pad * (double)P.K <= 33554432.0;
+}
+
 Layout layout(const Problem& P) {
     Layout L;
     size_t off = 0;
@@ -113,7 +119,9 @@ Layout layout(const Problem& P) {
         L.uc = off; off = align256(off + (size_t)P.N * (size_t)P.r_pad * ce);
         L.h = off; off = align256(off + (size_t)P.M * (size_t)P.r_pad * ce);
         L.dnorm = off; off = align256(off + (size_t)P.r_pad * 2 * sizeof(double));
-        L.flagged = off; off = align256(off + sizeof(unsigned));
+        // the guard's count: one counter, or one per workgroup of the few-row h kernel
+        L.flag_slots = hdot_path(P) ? lyc::hdot_workgroups(P.M, P.r_pad) : 1;
+        L.flagged = off; off = align256(off + (size_t)L.flag_slots * sizeof(unsigned));
     }
     if (P.lora) {
         // fp32 partial sums of a K-split GEMM (few output tiles), sized for
@@ -288,7 +296,11 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
     // up already in the compute dtype, unpadded (rank == r_pad) and 16-byte
     // aligned: the fold reads it as stored and the prep makes no copy
     const bool up_stored = P.r_pad > 0 && P.u_dt == P.c_dt && P.rank == P.r_pad && aligned(up, 16);
-    if (P.r_pad > 0 || cx || cw) {
+    // few token rows, factors and operands already in the compute dtype: no
+    // preparation at all (h reads down as stored, the fold reads up as stored)
+    const bool hdot = hdot_path(P);
+    const bool prep = (P.r_pad > 0 && !(hdot && up_stored && P.d_dt == P.c_dt)) || cx || cw;
+    if (prep) {
         // one launch: the factors' preparation and the fp32 operand casts
         lyc::PrepParams pp{};
         if (P.r_pad > 0) {
@@ -314,8 +326,23 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
         if (cw) { pp.cast_src[nc] = (const float*)w; pp.cast_dst[nc] = W + L.wc; pp.cast_n[nc++] = P.N * P.K; }
         if (timed(LYC_KERNEL_PREP, s, [&] { return lyc::launch_prep(pp, s); }) != hipSuccess) return LYC_ERR_HIP;
     }
-    if (P.r_pad > 0) {
-
+    if (P.r_pad > 0 && hdot) {
+        lyc::HdotParams hq{};
+        hq.x = xa;
+        hq.down = P.d_dt == P.c_dt ? down : (const void*)(W + L.dc);
+        hq.M = P.M;
+        hq.K = P.K;
+        hq.rank = P.rank;
+        hq.r_pad = P.r_pad;
+        hq.vec = ((P.K * (int64_t)esize(P.c_dt)) % 16 == 0 && aligned(xa, 16) && aligned(hq.down, 16)) ? 1 : 0;
+        hq.out = W + L.h;
+        hq.flagged = (unsigned*)(W + L.flagged);
+        if (timed(LYC_KERNEL_HPASS, s, [&] { return lyc::launch_hdot(P.c_dt, hq, s); }) != hipSuccess)
+            return LYC_ERR_HIP;
+        g.af = up_stored ? up : (const void*)(W + L.uc);
+        g.bf = W + L.h;
+        g.rf = P.r_pad;
+    } else if (P.r_pad > 0) {
         lyc::XrParams hp{};
         const bool split = P.c_dt != LYC_F32;
         hp.x = xa;
@@ -1114,7 +1141,8 @@ int lyc_lora_linear_fwd(const void* x, int x_dt, const void* w, int w_dt, const 
 }
 
 int lyc_lora_workspace_layout(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt, int bias_dt,
-                              int down_dt, int up_dt, size_t* h_offset, int64_t* h_ld, size_t* flagged_offset) {
+                              int down_dt, int up_dt, size_t* h_offset, int64_t* h_ld, size_t* flagged_offset,
+                              int64_t* flagged_slots) {
     Problem P{true, M, N, K, rank, x_dt, w_dt, bias_dt, down_dt, up_dt, 0, 0, 0};
     const int st = check_problem(P);
     if (st != LYC_OK) return st;
@@ -1122,6 +1150,7 @@ int lyc_lora_workspace_layout(int64_t M, int64_t N, int64_t K, int64_t rank, int
     if (h_offset) *h_offset = L.h;
     if (h_ld) *h_ld = P.r_pad;
     if (flagged_offset) *flagged_offset = L.flagged;
+    if (flagged_slots) *flagged_slots = L.flag_slots;
     return LYC_OK;
 }
 

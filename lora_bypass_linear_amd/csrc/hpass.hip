@@ -865,6 +865,166 @@ static hipError_t run_xr_ct(const XrParams& p, hipStream_t s) {
     }
 }
 
+// ---- few token rows: one wave per h element ------------------------------------
+// With few rows of x the split contraction above is latency-bound: one
+// workgroup walks all of K.  There each element h[m][j] gets a wave of its
+// own instead: the fp64 dot of x_m and down_j (exact products; lane l takes
+// the 16-byte chunks l, l + 64, ..., then a butterfly over the lanes), with a
+// bound on that sum's own rounding error, gamma_n * sum|p| (n: the longest
+// chain of additions a product goes through).  Where [s - E, s + E] straddles
+// a rounding boundary of the compute dtype, the wave sums again carrying each
+// addition's rounding error (TwoSum) and rounds that compensated sum, whose
+// error is of the order of 2^-100 sum|p|.  Workgroup w writes the number of
+// such elements to slot w of p.flagged (no clearing needed).
+template <class CT>
+__device__ __forceinline__ void vals_f64(i32x4 v, double (&o)[CT::dt == DT_F32 ? 4 : 8]) {
+    if constexpr (CT::dt == DT_F32) {
+        const f32x4 f = __builtin_bit_cast(f32x4, v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = (double)f[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = (double)unpack_lo<CT>((uint32_t)v[i]);
+            o[2 * i + 1] = (double)unpack_hi<CT>((uint32_t)v[i]);
+        }
+    }
+}
+
+__device__ __forceinline__ double load_widen(const void* base, int dt, int64_t i) {
+    if (dt == DT_F32) return (double)((const float*)base)[i];
+    const uint16_t b = ((const uint16_t*)base)[i];
+    return (double)(dt == DT_F16 ? f16_to_f32(b) : bf16_to_f32(b));
+}
+
+// s + t = a + b exactly (Knuth's TwoSum)
+__device__ __forceinline__ void two_sum(double a, double b, double& s, double& t) {
+    s = a + b;
+    const double bb = s - a;
+    t = (a - (s - bb)) + (b - bb);
+}
+
+template <class CT>
+__global__ __launch_bounds__(256) void hdot_kernel(HdotParams p) {
+    constexpr int V = CT::dt == DT_F32 ? 4 : 8;   // values per 16-byte chunk
+    const int lane = threadIdx.x & 63;
+    const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // element m * r_pad + j
+    __shared__ unsigned wflag[4];
+    unsigned straddled = 0;
+    if (e < p.M * p.r_pad) {
+        const int64_t m = e / p.r_pad;
+        const int j = (int)(e % p.r_pad);
+        double v = 0.0;
+        if (j < p.rank) {
+            const char* xr = (const char*)p.x + m * p.K * CT::es;
+            const char* dr = (const char*)p.down + (int64_t)j * p.K * CT::es;
+            // lane sums: s (the dot) and a (sum of |products|), and the chain length n
+            double s = 0.0, a = 0.0;
+            int64_t n;
+            if (p.vec) {
+                // 4 chunks of each row per lane in flight at a time: one memory
+                // round trip per 4 (the chunk order of the sums is unchanged)
+                const int64_t nch = p.K / V;
+                for (int64_t c0 = lane; c0 < nch; c0 += 4 * 64) {
+                    i32x4 xq[4], dq[4];
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const int64_t c = c0 + 64 * b;
+                        xq[b] = c < nch ? ((const i32x4*)xr)[c] : i32x4{0, 0, 0, 0};
+                        dq[b] = c < nch ? ((const i32x4*)dr)[c] : i32x4{0, 0, 0, 0};
+                    }
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        double xv[V], dv[V];
+                        vals_f64<CT>(xq[b], xv);
+                        vals_f64<CT>(dq[b], dv);
+#pragma unroll
+                        for (int i = 0; i < V; ++i) {
+                            s = __builtin_fma(xv[i], dv[i], s);
+                            a = __builtin_fma(__builtin_fabs(xv[i]), __builtin_fabs(dv[i]), a);
+                        }
+                    }
+                }
+                n = ((nch + 63) / 64) * V;
+            } else {
+                for (int64_t k = lane; k < p.K; k += 64) {
+                    const double xv = load_widen(p.x, CT::dt, m * p.K + k), dv = load_widen(p.down, CT::dt, (int64_t)j * p.K + k);
+                    s = __builtin_fma(xv, dv, s);
+                    a = __builtin_fma(__builtin_fabs(xv), __builtin_fabs(dv), a);
+                }
+                n = (p.K + 63) / 64;
+            }
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                s += __shfl_xor(s, o, 64);
+                a += __shfl_xor(a, o, 64);
+            }
+            s = __shfl(s, 0, 64);   // every lane takes lane 0's sums (the butterfly's orders differ)
+            a = __shfl(a, 0, 64);
+            n += 6;
+            const double u = 0x1p-53, g = (double)n * u / (1.0 - (double)n * u);
+            const double E = g * a * (1.0 + 2.0 * g) + 0x1p-1060;
+            bool cross;
+            if constexpr (CT::dt == DT_F32) cross = (float)(s - E) != (float)(s + E);
+            else cross = round16<CT>(s - E) != round16<CT>(s + E);
+            v = s;
+            if (cross) {
+                straddled = 1;
+                double S = 0.0, C = 0.0, t, err;
+                if (p.vec) {
+                    const int64_t nch = p.K / V;
+                    for (int64_t c = lane; c < nch; c += 64) {
+                        double xv[V], dv[V];
+                        vals_f64<CT>(((const i32x4*)xr)[c], xv);
+                        vals_f64<CT>(((const i32x4*)dr)[c], dv);
+#pragma unroll
+                        for (int i = 0; i < V; ++i) {
+                            two_sum(S, xv[i] * dv[i], t, err);   // the product is exact
+                            S = t;
+                            C += err;
+                        }
+                    }
+                } else {
+                    for (int64_t k = lane; k < p.K; k += 64) {
+                        two_sum(S, load_widen(p.x, CT::dt, m * p.K + k) * load_widen(p.down, CT::dt, (int64_t)j * p.K + k),
+                                t, err);
+                        S = t;
+                        C += err;
+                    }
+                }
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1) {
+                    const double So = __shfl_xor(S, o, 64), Co = __shfl_xor(C, o, 64);
+                    two_sum(S, So, t, err);
+                    S = t;
+                    C = (C + Co) + err;
+                }
+                v = __shfl(S, 0, 64) + __shfl(C, 0, 64);
+            }
+        }
+        if (lane == 0) {
+            const int64_t at = m * p.r_pad + j;
+            if constexpr (CT::dt == DT_F32) ((float*)p.out)[at] = (float)v;
+            else ((uint16_t*)p.out)[at] = round16<CT>(v);
+        }
+    }
+    if (lane == 0) wflag[threadIdx.x >> 6] = straddled;
+    __syncthreads();
+    if (threadIdx.x == 0) p.flagged[blockIdx.x] = wflag[0] + wflag[1] + wflag[2] + wflag[3];
+}
+
+int64_t hdot_workgroups(int64_t M, int64_t r_pad) { return (M * r_pad + 3) / 4; }
+
+hipError_t launch_hdot(int c_dt, const HdotParams& p, hipStream_t s) {
+    const int64_t g = hdot_workgroups(p.M, p.r_pad);
+    if (g <= 0) return hipSuccess;
+    if (g > 65535) return hipErrorInvalidValue;
+    if (c_dt == DT_F16) hipLaunchKernelGGL(hdot_kernel<CF16>, dim3((unsigned)g), dim3(256), 0, s, p);
+    else if (c_dt == DT_BF16) hipLaunchKernelGGL(hdot_kernel<CBF16>, dim3((unsigned)g), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(hdot_kernel<CF32>, dim3((unsigned)g), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_xr(int c_dt, const XrParams& p, hipStream_t s) {
     if (c_dt == DT_F16) return run_xr_ct<CF16>(p, s);
     if (c_dt == DT_BF16) return run_xr_ct<CBF16>(p, s);

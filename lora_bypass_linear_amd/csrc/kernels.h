@@ -87,6 +87,22 @@ struct XrParams {
     double scale;           // XR_H: the value rounded is scale * C (1 in the forward)
 };
 
+// h for few token rows, one wave per element: h[m][j] (j < r_pad; 0 from
+// rank on) = round_c of the fp64 dot of x_m and down_j, both [.,K] in the
+// compute dtype with row stride K; the per-workgroup counts of elements that
+// took the compensated re-summation go to flagged[workgroup].
+struct HdotParams {
+    const void* x;       // [M][K]
+    const void* down;    // [rank][K] (rows >= rank never read)
+    int64_t M, K, rank;
+    int r_pad;
+    int vec;             // rows 16-byte aligned and K * es a multiple of 16: 16-byte loads
+    void* out;           // h [M][r_pad]
+    unsigned* flagged;   // [hdot_workgroups(M, r_pad)]
+};
+int64_t hdot_workgroups(int64_t M, int64_t r_pad);
+hipError_t launch_hdot(int c_dt, const HdotParams& p, hipStream_t s);
+
 // Compute-dtype copies of down [rank,K] -> [r_pad,K] (+ its hi/lo split per
 // 64-k block and row norms) and up [N,rank] -> [N,r_pad]; zero padding;
 // clears *flagged (if not null); and the fp32 operand casts, in one launch.

@@ -34,7 +34,7 @@ def gpu_forward(inputs: Dict[str, torch.Tensor], wl: WL.Workload, scale: Optiona
             args = (wl.M, wl.N, wl.K, wl.r, L.dtype_code(d["x"]), L.dtype_code(d["w"]),
                     L.dtype_code(d["b"]) if "b" in d else 0, L.dtype_code(d["down"]), L.dtype_code(d["up"]))
             c_dt, _ = L.resolve_dtypes([a for a in (args[4], args[5], args[6], args[7], args[8]) if a])
-            ho, ld, fo = L.lora_workspace_layout(*args)
+            ho, ld, fo, ns = L.lora_workspace_layout(*args)
             es = 4 if c_dt == L.F32 else 2
             raw = ws[ho: ho + wl.M * ld * es].cpu()
             if c_dt == L.F32:
@@ -42,7 +42,7 @@ def gpu_forward(inputs: Dict[str, torch.Tensor], wl: WL.Workload, scale: Optiona
             else:
                 hv = oracle.as_float64(raw.view(torch.int16).numpy().view(np.uint16).reshape(wl.M, ld), c_dt)
             h = hv[:, :wl.r]
-            flagged = int(ws[fo: fo + 4].cpu().view(torch.int32).item())
+            flagged = int(ws[fo: fo + 4 * ns].cpu().view(torch.int32).sum().item())
         return y.cpu(), h, flagged
     args = (wl.M, wl.N, wl.K, L.dtype_code(d["x"]), L.dtype_code(d["w"]), L.dtype_code(d["b"]) if "b" in d else 0)
     nb = L.linear_workspace_size(*args)

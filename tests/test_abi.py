@@ -132,8 +132,14 @@ def test_workspace_sizes():
     # LoRA workspace = h [M, r_pad] + down/up copies + norms + counter (+ casts of fp32 x/W)
     n16 = L.lora_workspace_size(1000, 300, 64, 17, 1, 1, 0, 1, 1)
     assert n16 >= 1000 * 32 * 2 + 32 * 64 * 2 + 300 * 32 * 2 + 32 * 8
-    ho, ld, fo = L.lora_workspace_layout(1000, 300, 64, 17, 1, 1, 0, 1, 1)
-    assert ld == 32 and ho % 256 == 0 and fo % 256 == 0 and fo < n16
+    ho, ld, fo, ns = L.lora_workspace_layout(1000, 300, 64, 17, 1, 1, 0, 1, 1)
+    assert ld == 32 and ho % 256 == 0 and fo % 256 == 0 and ns == 1 and fo + 4 * ns <= n16
+    # few token rows: h one fp64 dot per element, one guard count per workgroup of 4 waves
+    n_small = L.lora_workspace_size(16, 3072, 3072, 16, 1, 1, 0, 1, 1)
+    ho, ld, fo, ns = L.lora_workspace_layout(16, 3072, 3072, 16, 1, 1, 0, 1, 1)
+    assert ld == 16 and ns == 16 * 16 // 4 and fo + 4 * ns <= n_small
+    assert L.lora_workspace_layout(129, 3072, 3072, 16, 1, 1, 0, 1, 1)[3] == 1     # above 128 rows: the split form
+    assert L.lora_workspace_layout(128, 8192, 8192, 128, 2, 2, 0, 2, 2)[3] == 1   # M r_pad K above 2^25
     # affine: one guard count per workgroup of the contraction (+ a bf16 copy of an fp32 W)
     fo, ns = L.linear_workspace_layout(64, 64, 64, 1, 1)
     assert ns >= 1 and L.linear_workspace_size(64, 64, 64, 1, 1) >= fo + 4 * ns

@@ -245,11 +245,13 @@ def test_deterministic(name, dims, ksplit):
         assert torch.equal(y1, y2) and np.array_equal(h1, h2) and f1 == f2
 
 
-def test_h_guard_resolves_midpoints():
+@pytest.mark.parametrize("M", [64, 192])   # one fp64 dot per element (M <= 128), the split contraction
+def test_h_guard_resolves_midpoints(M):
     """h values placed exactly on fp16 rounding midpoints, or 2^-20 either side,
     behind large terms that cancel exactly in pairs (so fp32 partial sums are
-    inexact): h_r must still be the correctly rounded exact value."""
-    K, r, M = 64, 16, 64
+    inexact): h_r must still be the correctly rounded exact value, and the
+    guard must have re-evaluated the elements on the midpoints."""
+    K, r = 64, 16
     rng = np.random.default_rng(5)
     x = np.zeros((M, K))
     down = np.zeros((r, K))
@@ -270,15 +272,19 @@ def test_h_guard_resolves_midpoints():
     inputs["down"] = torch.from_numpy(down).half()
     assert np.array_equal(inputs["x"].double().numpy(), x) and np.array_equal(inputs["down"].double().numpy(), down)
     _check(wl, inputs=inputs)
+    _, _, flagged = gpu_forward(inputs, wl)
+    on_mid = int((x[:, 2] == 0).sum()) * r   # these rows' h sit exactly on a midpoint
+    assert flagged >= on_mid > 0, (flagged, on_mid)
 
 
+@pytest.mark.parametrize("M", [96, 160])   # one fp64 dot per element (M <= 128), the split contraction
 @pytest.mark.parametrize("shift", [58, 62, 66])
-def test_h_exact_near_fp32_underflow(shift):
+def test_h_exact_near_fp32_underflow(shift, M):
     """bf16 x and down scaled by 2^-shift, so that the h products sit near and
     below fp32's smallest normal 2^-126 (and h itself, at the largest shift,
     in bf16's subnormal range): h_r must still be the correctly rounded exact
     value however the fp32 MFMA partial sums treat values that small."""
-    wl = BASE["lora_bf16_16384x8192x8192_r128"].resized(M=96, N=64, K=640, r=16)
+    wl = BASE["lora_bf16_16384x8192x8192_r128"].resized(M=M, N=64, K=640, r=16)
     inputs = WL.generate(wl)
     for k in ("x", "down"):
         inputs[k] = (inputs[k].double() * 2.0 ** -shift).to(torch.bfloat16)
