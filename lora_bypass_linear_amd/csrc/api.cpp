@@ -283,6 +283,9 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
         g.ksplit = tc.ksplit;
     }
     g.partial = g.ksplit > 1 ? (float*)(W + L.partial) : nullptr;
+    // few token rows, no stored pick: one workgroup per 16 output features
+    // over all of K (no K split, no second kernel)
+    g.skinny = P.M <= 32 ? 1 : 0;
     if (P.m_dt != 0) {
         float* gain = (float*)(W + L.gain);
         if (timed(LYC_KERNEL_PREP, s, [&] { return lyc::launch_dora_gain(mag, P.m_dt, norms, P.N, gain, s); }) !=

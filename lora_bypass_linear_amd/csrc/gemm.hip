@@ -690,7 +690,154 @@ int gemm_plan(int64_t M, int64_t N, int64_t K, int64_t rf, int c_dt, GemmCand* o
     return m;
 }
 
+// ---- few token rows: one workgroup per 16 output features ----------------------
+// y[0:M, n0:n0+16] = round_out(post * (scale * (af . bf^T) + a . b^T) + b) for
+// M <= 32 with fp32 accumulation and all of K in one workgroup, so that no
+// K split and no second kernel are needed.  Wave w of the NW takes the w-th
+// share of the 64-byte K steps, reading its fragments of W (a) and x (b)
+// straight from global memory D steps ahead: every fragment is used by one
+// wave once, so nothing is staged in LDS.  Wave 0 also takes the fold, first,
+// as the tiled kernel does.  The waves' sums meet in LDS in wave order.
+// (x is read by every workgroup: beyond 32 rows that L2 traffic outgrows W's
+// and the tiled kernel with its K split is faster.)
+template <class CT, int MT, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void skinny_kernel(GemmParams p) {
+    __shared__ __attribute__((aligned(16))) f32x4 red[NW - 1][MT][64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const uint32_t kb = (uint32_t)(p.K * CT::es);   // bytes of a row
+    const int nrows = (int)(p.N - n0 < 16 ? p.N - n0 : 16);
+    const auto rw = make_rsrc_uniform((const char*)p.a + n0 * kb, (uint32_t)nrows * kb);
+    const auto rx = make_rsrc_uniform(p.b, (uint32_t)(p.M * kb));
+    const uint32_t lo = (uint32_t)(lane >> 4) * 16;        // the lane's 16 bytes of a 64-byte step
+    const uint32_t wrow = (uint32_t)(lane & 15) * kb + lo;
+    f32x4 acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (wave == 0 && p.rf > 0) {
+        // fold: scale * (up rows n0.. . h rows^T), rank padded with zeros
+        const uint32_t fb = (uint32_t)(p.rf * CT::es);
+        const auto ru = make_rsrc_uniform((const char*)p.af + n0 * fb, (uint32_t)nrows * fb);
+        const auto rh = make_rsrc_uniform(p.bf, (uint32_t)(p.M * fb));
+        for (uint32_t f = 0; f < fb; f += 64) {
+            const i32x4 ua = buf_load16(ru, f + lo < fb ? (uint32_t)(lane & 15) * fb + f + lo : OOB);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const i32x4 hb = buf_load16(rh, f + lo < fb ? (uint32_t)(16 * t + (lane & 15)) * fb + f + lo : OOB);
+                acc[t] = CT::step(ua, hb, acc[t]);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[t] *= p.scale;
+    }
+
+    // the wave's K steps, D in flight: ring slot u holds step s0 + u (mod D);
+    // the run is padded to a multiple of D with steps that read zeros, so the
+    // loop body has no exit in it (the compiler then keeps the ring in flight
+    // across iterations instead of waiting for all of it at the loop head)
+    const int steps = (int)((kb + 63) / 64);
+    const int s0 = steps * wave / NW, s1 = steps * (wave + 1) / NW;
+    const int se = s0 + ((s1 - s0 + D - 1) / D) * D;
+    i32x4 wa[D], xa[D][MT];
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+        const uint32_t k = (uint32_t)(s0 + u) * 64;
+        const bool in = s0 + u < s1 && k + lo < kb;
+        wa[u] = buf_load16(rw, in ? wrow + k : OOB);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) xa[u][t] = buf_load16(rx, in ? (uint32_t)(16 * t + (lane & 15)) * kb + lo + k : OOB);
+    }
+    for (int sb = s0; sb < se; sb += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t) acc[t] = CT::step(wa[u], xa[u][t], acc[t]);
+            const int sn = sb + u + D;
+            const uint32_t k = (uint32_t)sn * 64;
+            const bool in = sn < s1 && k + lo < kb;
+            wa[u] = buf_load16(rw, in ? wrow + k : OOB);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) xa[u][t] = buf_load16(rx, in ? (uint32_t)(16 * t + (lane & 15)) * kb + lo + k : OOB);
+        }
+    }
+
+    if (wave > 0) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t) red[wave - 1][t][lane] = acc[t];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    // lane: rows m = 16 t + (lane & 15), features n0 + 4 (lane >> 4) .. +3
+    const int64_t nb = n0 + 4 * (lane >> 4);
+    float bias[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bias[e] = (p.bias != nullptr && nb + e < p.N) ? load_as_f32(p.bias, p.bias_dt, nb + e) : 0.f;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        f32x4 sum = acc[t];
+#pragma unroll
+        for (int w = 0; w < NW - 1; ++w) sum += red[w][t][lane];
+        const int64_t m = 16 * t + (lane & 15);
+        if (m >= p.M) continue;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = sum[e] * p.post + bias[e];
+        const int64_t base = m * p.N + nb;
+        if (p.y_dt == DT_F32) {
+            float* y = (float*)p.y;
+            if (p.vec_store && nb + 3 < p.N) {
+                *(f32x4*)(y + base) = f32x4{v[0], v[1], v[2], v[3]};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (nb + e < p.N) y[base + e] = v[e];
+            }
+        } else {
+            const uint32_t l2 = p.y_dt == DT_F16 ? pack_f16x2(v[0], v[1]) : pack_bf16x2(v[0], v[1]);
+            const uint32_t h2 = p.y_dt == DT_F16 ? pack_f16x2(v[2], v[3]) : pack_bf16x2(v[2], v[3]);
+            uint16_t* y = (uint16_t*)p.y;
+            if (p.vec_store && nb + 3 < p.N) {
+                *(i32x2*)(y + base) = i32x2{(int)l2, (int)h2};
+            } else {
+                const uint16_t o[4] = {(uint16_t)l2, (uint16_t)(l2 >> 16), (uint16_t)h2, (uint16_t)(h2 >> 16)};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (nb + e < p.N) y[base + e] = o[e];
+            }
+        }
+    }
+}
+
+template <class CT>
+static hipError_t run_skinny(const GemmParams& p, hipStream_t s) {
+    const int64_t kb = p.K * CT::es, fb = p.rf * CT::es;
+    if (kb % 16 != 0 || fb % 16 != 0 || p.M * kb >= ((int64_t)1 << 31) || 16 * kb >= ((int64_t)1 << 31) ||
+        p.M * fb >= ((int64_t)1 << 31) || 16 * fb >= ((int64_t)1 << 31))
+        return hipErrorInvalidValue;
+    const dim3 g((unsigned)((p.N + 15) / 16));
+    // (4 waves: 8, each with the same ring, measured slower at 16 x 3072 x 3072)
+    if (p.M <= 16) hipLaunchKernelGGL((skinny_kernel<CT, 1, 8, 4>), g, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((skinny_kernel<CT, 2, 6, 4>), g, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+// the few-row kernel takes the forward's plain case: no gain, operands as
+// rows, 16-byte row pieces, 32-bit offsets
+bool gemm_skinny(int c_dt, const GemmParams& p) {
+    if (p.M < 1 || p.M > 32 || p.gain != nullptr || p.ta || p.tb || p.tile != GEMM_TILE_AUTO) return false;
+    const int64_t es = c_dt == DT_F32 ? 4 : 2, kb = p.K * es, fb = p.rf * es;
+    return kb % 16 == 0 && fb % 16 == 0 && p.M * kb < ((int64_t)1 << 31) && 16 * kb < ((int64_t)1 << 31) &&
+           p.M * fb < ((int64_t)1 << 31) && 16 * fb < ((int64_t)1 << 31);
+}
+
 hipError_t launch_gemm(int c_dt, const GemmParams& p, hipStream_t s) {
+    if (p.skinny && gemm_skinny(c_dt, p)) {
+        if (c_dt == DT_F16) return run_skinny<CF16>(p, s);
+        if (c_dt == DT_BF16) return run_skinny<CBF16>(p, s);
+        return run_skinny<CF32>(p, s);
+    }
     int t = p.tile >= 0 ? p.tile : pick_tile(p.M, p.N, c_dt == DT_F32);
     if (c_dt == DT_F32 && t != T_M && t != T_S) return hipErrorInvalidValue;   // no fp32 instance
     if (p.ta || p.tb) {

@@ -46,6 +46,10 @@ struct GemmParams {
     // Each such matrix must stay below 1 GiB (one buffer range covers it).
     int ta = 0, tb = 0;
     int64_t lda_t = 0, ldb_t = 0;
+    // 1: few token rows (M <= 32, tile left to the analytic pick, no gain):
+    // one workgroup per 16 output features over all of K (gemm_skinny says
+    // whether the launch takes it; ksplit and partial are then unused)
+    int skinny = 0;
 };
 
 struct GemmCand {
@@ -130,6 +134,7 @@ struct PrepParams {
 };
 
 hipError_t launch_gemm(int c_dt, const GemmParams& p, hipStream_t s);
+bool gemm_skinny(int c_dt, const GemmParams& p);
 // K splits launch_gemm uses for this shape (1: none; the partial sums then
 // need ksplit * M * N * 4 bytes of workspace)
 int gemm_ksplit(int64_t M, int64_t N, int64_t K, int c_dt);

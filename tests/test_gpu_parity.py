@@ -198,14 +198,41 @@ def test_empty_tokens():
     assert y.shape == (0, 32)
 
 
-def test_overflow_to_inf_matches():
-    wl = BASE["lora_f16_4096x3072x3072_r16"].resized(M=32, N=40, K=64, r=16)
+@pytest.mark.parametrize("M", [32, 160])   # the few-row GEMM (M <= 128) and the tiled one
+def test_overflow_to_inf_matches(M):
+    """Outputs beyond fp16's range: +-inf on both sides, sign for sign.  These
+    inputs are scaled far past the pages' workloads, and some finite outputs
+    cancel from sum|terms| ~ 5e5 to below 1, where any fp32 accumulation order
+    errs by far more than the per-element bound of the pages' validation
+    (Luminal FP16 page, "Validation and Experimental Design", which assumes
+    their workloads).  Finite outputs are therefore held to that bound plus
+    the fp32 accumulation term of oracle.tolerance_sum over the K + r products
+    (the bound the gradients use), computed from the exact terms."""
+    wl = BASE["lora_f16_4096x3072x3072_r16"].resized(M=M, N=40, K=64, r=16)
     inputs = WL.generate(wl)
     inputs["x"] = (inputs["x"].float() * 3000).clamp(-60000, 60000).half()
     inputs["w"] = (inputs["w"].float() * 200).half()                          # many outputs beyond fp16 range
     res = oracle_forward(inputs, wl)
-    assert np.isinf(oracle.as_float64(res["y"], oracle.F16)).mean() > 0.2
-    _check(wl, inputs=inputs)
+    ref = oracle.as_float64(res["y"], oracle.F16)
+    assert np.isinf(ref).mean() > 0.2
+    y, _, _ = gpu_forward(inputs, wl)
+    g = oracle.as_float64(WL.raw_bits(y), oracle.F16)
+    inf = np.isinf(ref)
+    # at the overflow threshold (max + half an ulp) the fp32 sum may land either side
+    near = np.abs(np.abs(res["ref"]) - (65504.0 + 16.0)) <= oracle.tolerance(np.full(ref.shape, 65520.0), oracle.F16,
+                                                                           wl.K, wl.r)
+    agree = (np.isinf(g) == inf) | near
+    assert agree.all(), np.argwhere(~agree)[:5]
+    assert (np.sign(g[inf & np.isinf(g)]) == np.sign(ref[inf & np.isinf(g)])).all()
+    # finite outputs: the pages' bound plus the fp32 accumulation term over the terms
+    x, w = inputs["x"].double().numpy(), inputs["w"].double().numpy()
+    d, u = inputs["down"].double().numpy(), inputs["up"].double().numpy()
+    h = torch.from_numpy(x @ d.T).half().double().numpy()
+    rss = np.sqrt((x ** 2) @ (w ** 2).T + wl.scale ** 2 * (h ** 2) @ (u ** 2).T)
+    tol = oracle.tolerance_sum(ref, rss, oracle.F16, wl.K + wl.r)
+    fin = np.isfinite(ref) & np.isfinite(g)
+    err = np.abs(g - ref)
+    assert (err[fin] <= tol[fin]).all(), np.argwhere(fin & (err > tol))[:5]
 
 
 def test_unaligned_output_rows():
