@@ -168,9 +168,12 @@ int lyc_lora_linear_fwd_noalloc(const void* x, int x_dt, const void* w, int w_dt
  *   flagged_offset: byte offset of `*flagged_slots` uint32 counts whose sum
  *              is the number of h elements that the rounding guard
  *              re-evaluated during the last call: in fp64 after the split
- *              contraction (one count), or, for few token rows (M <= 128 and
+ *              contraction (one count; one per workgroup at rank 16 with down
+ *              in the 16-bit compute dtype, which the contraction then splits
+ *              itself), or, for few token rows (M <= 128 and
  *              M * r_pad * K <= 2^25, h as one fp64 dot per element), by a
- *              compensated re-summation (one count per workgroup);
+ *              compensated re-summation (one count per workgroup); every
+ *              slot is written by each call;
  *   flagged_slots: their number.
  * Any out-pointer may be NULL.  Same argument errors as the size query.
  */

@@ -101,6 +101,13 @@ bool hdot_path(const Problem& P) {
     return P.lora && P.r_pad > 0 && P.K > 0 && P.M <= 128 && (double)P.M * (double)P.r_pad * (double)P.K <= 33554432.0;
 }
 
+// rank 16 with down already in the compute dtype: the split contraction
+// splits down itself (no preparation pass; its guard counts per workgroup)
+bool h_split_b_shape(const Problem& P) {
+    return P.lora && !hdot_path(P) && P.c_dt != LYC_F32 && P.rank == 16 && P.r_pad == 16 && P.d_dt == P.c_dt &&
+           P.M > 0 && P.K > 0;
+}
+
 Layout layout(const Problem& P) {
     Layout L;
     size_t off = 0;
@@ -119,8 +126,11 @@ Layout layout(const Problem& P) {
         L.uc = off; off = align256(off + (size_t)P.N * (size_t)P.r_pad * ce);
         L.h = off; off = align256(off + (size_t)P.M * (size_t)P.r_pad * ce);
         L.dnorm = off; off = align256(off + (size_t)P.r_pad * 2 * sizeof(double));
-        // the guard's count: one counter, or one per workgroup of the few-row h kernel
-        L.flag_slots = hdot_path(P) ? lyc::hdot_workgroups(P.M, P.r_pad) : 1;
+        // the guard's count: one counter, or one per workgroup of the few-row h
+        // kernel or of the h pass that splits down itself
+        L.flag_slots = hdot_path(P)         ? lyc::hdot_workgroups(P.M, P.r_pad)
+                       : h_split_b_shape(P) ? lyc::xr_h_split_b_workgroups(P.M, P.r_pad)
+                                            : 1;
         L.flagged = off; off = align256(off + (size_t)L.flag_slots * sizeof(unsigned));
     }
     if (P.lora) {
@@ -299,14 +309,16 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
     // up already in the compute dtype, unpadded (rank == r_pad) and 16-byte
     // aligned: the fold reads it as stored and the prep makes no copy
     const bool up_stored = P.r_pad > 0 && P.u_dt == P.c_dt && P.rank == P.r_pad && aligned(up, 16);
-    // few token rows, factors and operands already in the compute dtype: no
-    // preparation at all (h reads down as stored, the fold reads up as stored)
+    // few token rows, or rank 16, with the factors already in the compute
+    // dtype: no preparation of them (h reads down as stored, the fold reads
+    // up as stored)
     const bool hdot = hdot_path(P);
-    const bool prep = (P.r_pad > 0 && !(hdot && up_stored && P.d_dt == P.c_dt)) || cx || cw;
-    if (prep) {
+    const bool hsb = h_split_b_shape(P) && aligned(down, 16);
+    const bool factors = P.r_pad > 0 && !((hdot || hsb) && up_stored && P.d_dt == P.c_dt);
+    if (factors || cx || cw) {
         // one launch: the factors' preparation and the fp32 operand casts
         lyc::PrepParams pp{};
-        if (P.r_pad > 0) {
+        if (factors) {
             pp.down = down;
             pp.down_dt = P.d_dt;
             pp.up = up;
@@ -316,13 +328,16 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
             pp.dl = W + L.dl;
             pp.uc = up_stored ? nullptr : W + L.uc;
             pp.dnorm = (double2*)(W + L.dnorm);
+            // (where the workspace has a count per workgroup of a form this
+            // call does not take, every slot is cleared: their sum is the count)
             pp.flagged = (unsigned*)(W + L.flagged);
+            pp.flag_slots = L.flag_slots;
             pp.vec = aligned(down, 16) ? 1 : 0;
         }
         pp.N = P.N;
         pp.K = P.K;
         pp.rank = P.rank;
-        pp.r_pad = P.r_pad;
+        pp.r_pad = factors ? P.r_pad : 0;
         pp.c_dt = P.c_dt;
         int nc = 0;
         if (cx) { pp.cast_src[nc] = (const float*)x; pp.cast_dst[nc] = W + L.xc; pp.cast_n[nc++] = P.M * P.K; }
@@ -349,10 +364,17 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
         lyc::XrParams hp{};
         const bool split = P.c_dt != LYC_F32;
         hp.x = xa;
-        hp.b = W + (split ? L.dh : L.dc);
-        hp.b_lo = split ? (const void*)(W + L.dl) : nullptr;
-        hp.b_full = W + L.dc;
-        hp.bnorm = (const double2*)(W + L.dnorm);
+        if (hsb) {
+            hp.b = down;
+            hp.b_full = down;
+            hp.split_b = 1;
+            hp.flag_slots = L.flag_slots;
+        } else {
+            hp.b = W + (split ? L.dh : L.dc);
+            hp.b_lo = split ? (const void*)(W + L.dl) : nullptr;
+            hp.b_full = W + L.dc;
+            hp.bnorm = (const double2*)(W + L.dnorm);
+        }
         hp.M = P.M;
         hp.Nc = P.r_pad;
         hp.K = P.K;

@@ -387,7 +387,8 @@ struct XrStage {
     static_assert(NS * BYTES <= 160 * 1024 && (NS - 1) * Q < 64, "LDS stages");
 };
 
-// SB (plain affine form): b = W_c is loaded as stored and split in the kernel
+// SB (plain affine form, and h at rank 16 with down in the compute dtype):
+// b = W_c or down_c is loaded as stored and split in the kernel
 // exactly as x is (per 64-k block of each row), its row norms taken from the
 // diagonals of MFMA Gram matrices; no preparation pass.  The guard's count is
 // then written per workgroup (p.flagged[workgroup], a plain store), so that
@@ -822,14 +823,22 @@ static hipError_t run_xr_jb(const XrParams& p, hipStream_t s) {
 // split in the kernel (one launch: 19.0 -> 12.0 us at M = 16, 24.4 -> 15.7 us
 // at M = 128).  Returns the latter launch's workgroup count (its guard-count
 // slots), or 0 where the row-norm pass is used.
-int64_t xr_affine_workgroups(int64_t M, int64_t N) {
-    const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
-    if (t64 >= 256) return 0;
-    const int64_t col_tiles = (N + 15) / 16;
+static int64_t xr_split_b_wgs(int64_t M, int64_t Nc) {
+    const int64_t col_tiles = (Nc + 15) / 16;
     const int ks = pick_ks(M, col_tiles);
     const int rw = ks <= 2 ? xr_row_groups(2) : xr_row_groups(8);   // run_xr_jb<CT, 1, 1, 8, true>
     return ((M + rw * 16 - 1) / (rw * 16)) * col_tiles;
 }
+
+int64_t xr_affine_workgroups(int64_t M, int64_t N) {
+    const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
+    if (t64 >= 256) return 0;
+    return xr_split_b_wgs(M, N);
+}
+
+// h at rank 16 with down already in the compute dtype: the same 16-column
+// launch with down split in the kernel, so that no preparation pass runs
+int64_t xr_h_split_b_workgroups(int64_t M, int64_t Nc) { return Nc == 16 ? xr_split_b_wgs(M, Nc) : 0; }
 
 // Columns per wave (JB blocks of 16), column groups (CG), k groups (KS) and
 // row groups (RW) per workgroup: at least 256 workgroups where M allows,
@@ -845,6 +854,12 @@ static hipError_t run_xr_ct(const XrParams& p, hipStream_t s) {
             return run_xr_jb<CT, 1, 1, 8, true>(p, s);
         }
         return run_xr_jb<CT, 4, 1, 4>(p, s);
+    }
+    if (p.split_b) {
+        if constexpr (CT::dt != DT_F32) {
+            if (p.Nc == 16) return run_xr_jb<CT, 1, 1, 8, true>(p, s);
+        }
+        return hipErrorInvalidValue;
     }
     switch (p.Nc) {
     case 16:   // 16-bit compute only (fp32 compute pads the rank to 32)

@@ -89,6 +89,10 @@ struct XrParams {
     int bias_dt;
     int vec_store;          // XR_AFFINE: rows allow 4-element vector stores
     double scale;           // XR_H: the value rounded is scale * C (1 in the forward)
+    // XR_H, 16-bit compute, Nc = 16: b = down as stored, split in the kernel
+    // and its norms taken there (b_lo and bnorm unused); the guard's count is
+    // then written per workgroup (flag_slots of them)
+    int split_b = 0;
 };
 
 // h for few token rows, one wave per element: h[m][j] (j < r_pad; 0 from
@@ -121,7 +125,8 @@ struct PrepParams {
     void* uc;
     double2* dnorm;   // {|down_c,j|, |lo_j|}
     int vec;          // down rows start 16-byte aligned: vector loads
-    unsigned* flagged;
+    unsigned* flagged;        // guard counts, all flag_slots of them cleared
+    int64_t flag_slots = 1;
     int64_t N, K, rank;
     int r_pad;
     int c_dt;
@@ -144,6 +149,9 @@ hipError_t launch_xr(int c_dt, const XrParams& p, hipStream_t s);
 // workgroups of the plain affine form's launch under 16-bit compute (its
 // guard-count slots)
 int64_t xr_affine_workgroups(int64_t M, int64_t N);
+// workgroups of the h pass that splits b in the kernel (XrParams::split_b;
+// its guard-count slots); 0 where that form does not apply (Nc != 16)
+int64_t xr_h_split_b_workgroups(int64_t M, int64_t Nc);
 // hi/lo split (per 64-k block) of each row of b [rows,K] (16-bit compute
 // dtype) and {|b_j|_2, |b_lo,j|_2}; also clears *flagged (if not null)
 hipError_t launch_rownorm(const void* b, int c_dt, int64_t rows, int64_t K, void* b_hi, void* b_lo, double2* out,

@@ -183,7 +183,8 @@ __device__ __forceinline__ void cast_range(const float* __restrict__ src, uint16
 // launch runs both at once.
 __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
     const int b = blockIdx.x, tid = threadIdx.x;
-    if (b == 0 && tid == 0 && p.flagged != nullptr) *p.flagged = 0u;
+    if (b == 0 && p.flagged != nullptr)
+        for (int64_t i = tid; i < p.flag_slots; i += 256) p.flagged[i] = 0u;
     if (b >= p.r_pad + p.up_blocks) {
         const int64_t cb = b - (p.r_pad + p.up_blocks), nb = (int64_t)gridDim.x - (p.r_pad + p.up_blocks);
         for (int c = 0; c < 2; ++c)

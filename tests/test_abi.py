@@ -138,7 +138,14 @@ def test_workspace_sizes():
     n_small = L.lora_workspace_size(16, 3072, 3072, 16, 1, 1, 0, 1, 1)
     ho, ld, fo, ns = L.lora_workspace_layout(16, 3072, 3072, 16, 1, 1, 0, 1, 1)
     assert ld == 16 and ns == 16 * 16 // 4 and fo + 4 * ns <= n_small
-    assert L.lora_workspace_layout(129, 3072, 3072, 16, 1, 1, 0, 1, 1)[3] == 1     # above 128 rows: the split form
+    # above 128 rows: the split form; at rank 16 with down in the compute dtype
+    # it splits down itself and counts per workgroup (16 rows each, 8 k groups
+    # up to 4096 rows; 32 rows, 2 k groups, from 8192)
+    assert L.lora_workspace_layout(129, 3072, 3072, 16, 1, 1, 0, 1, 1)[3] == 9
+    assert L.lora_workspace_layout(4096, 3072, 3072, 16, 1, 1, 0, 1, 1)[3] == 256
+    assert L.lora_workspace_layout(16384, 3072, 3072, 16, 2, 2, 0, 2, 2)[3] == 512
+    assert L.lora_workspace_layout(4096, 3072, 3072, 16, 1, 1, 0, 3, 1)[3] == 1   # fp32 down: prepared, one counter
+    assert L.lora_workspace_layout(4096, 3072, 3072, 12, 1, 1, 0, 1, 1)[3] == 1   # rank padded to 16: prepared
     assert L.lora_workspace_layout(128, 8192, 8192, 128, 2, 2, 0, 2, 2)[3] == 1   # M r_pad K above 2^25
     # affine: one guard count per workgroup of the contraction (+ a bf16 copy of an fp32 W)
     fo, ns = L.linear_workspace_layout(64, 64, 64, 1, 1)

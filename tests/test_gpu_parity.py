@@ -173,12 +173,23 @@ def test_unaligned_factors():
     inputs = WL.generate(wl)
     d = {k: v.to(torch.device("cuda:0")) for k, v in inputs.items()}
     say("unaligned factors", wl.name)
-    y_al = L.lora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, d.get("b"))
-    y_un = L.lora_linear(d["x"], d["w"], _shifted(d["down"]), _shifted(d["up"]), wl.scale, d.get("b"))
+    y_al, ws = L.lora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, d.get("b"), return_workspace=True)
+    args = (wl.M, wl.N, wl.K, wl.r, L.dtype_code(d["x"]), L.dtype_code(d["w"]),
+            L.dtype_code(d["b"]) if "b" in d else 0, L.dtype_code(d["down"]), L.dtype_code(d["up"]))
+    _, _, fo, ns = L.lora_workspace_layout(*args)
+    # aligned, rank 16: the h pass splits down itself and counts per workgroup;
+    # unaligned: down is prepared, one counter, and every other slot cleared
+    assert ns > 1
     torch.cuda.synchronize()
+    flagged_al = int(ws[fo: fo + 4 * ns].cpu().view(torch.int32).sum().item())
+    ws.fill_(0xFF)
+    y_un = L.lora_linear(d["x"], d["w"], _shifted(d["down"]), _shifted(d["up"]), wl.scale, d.get("b"), workspace=ws)
+    torch.cuda.synchronize()
+    flagged_un = int(ws[fo: fo + 4 * ns].cpu().view(torch.int32).sum().item())
     s = score(y_un.cpu(), oracle_forward(inputs, wl), None, wl.K, wl.r)
     assert s["fail"] == 0, s
     assert torch.equal(y_al.cpu(), y_un.cpu())
+    assert flagged_al == flagged_un, (flagged_al, flagged_un)
 
 
 def test_rank_zero_is_single_rounding():
