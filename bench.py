@@ -135,6 +135,12 @@ def main():
             del y2, d2, in2
             torch.cuda.empty_cache()
 
+    # the tile planner's device model, measured on this GPU (its shortlist
+    # order in small_m[].tuned follows these rates)
+    rates = L.measure_device_rates(dev)
+    out["device_rates"] = {"cus": rates["cus"], "mfma16_tflops": round(rates["mfma16_flops"] / 1e12, 1),
+                           "mfma32_tflops": round(rates["mfma32_flops"] / 1e12, 1),
+                           "hbm_copy_gbs": round(rates["hbm_bytes_per_s"] / 1e9, 1)}
     if not args.no_small_m:
         out["small_m"] = _small_m(dev)
     if lora and wl.r > 0 and not args.no_merge:

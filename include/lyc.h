@@ -340,15 +340,30 @@ int lyc_dora_linear_fwd(const void* x, int x_dt, const void* w, int w_dt, const 
  *   (padded rank) steps in compute dtype compute_dt, best first -- first the
  *   pick the forward makes on its own, then the other (tile, K split) pairs
  *   in the order of the model's time, which counts rounds of workgroups over
- *   256 CUs at the MFMA peak, a per-tile re-read penalty, and the partial
- *   sums' HBM round trip of a K split.  Writes up to max_out (at most 7)
+ *   the device's CUs at its MFMA rate, a per-tile re-read penalty, and the
+ *   partial sums' round trip through HBM at its rate for a K split (the
+ *   rates lyc_device_rates reports).  Writes up to max_out (at most 7)
  *   entries into the host arrays tile_n, tile_m (output tile: rows of W x rows
  *   of x), ksplit, cost_us (any may be NULL) and their number into *count.
  *   Host only.
+ * lyc_device_rates: the planner's model of the current device: its CU
+ *   count (hipDeviceAttributeMultiprocessorCount) and its dense MFMA rates
+ *   with 16-bit and fp32 operands (flop/s) and HBM rate (bytes/s).  Until
+ *   measured on the device (*measured = 0) the rates are MI355X's published
+ *   peaks per CU (2.5 PFLOP/s and 157.3 TFLOP/s over 256 CUs) times the CU
+ *   count, and 8 TB/s; without a device, 256 CUs.  Any pointer may be NULL.
+ * lyc_measure_device_rates: measures those rates on the device of `stream`
+ *   and keeps them for the planner (per device, for the process): a 256 MiB
+ *   device-to-device copy (read + write bytes over time) and MFMA loops of
+ *   16 waves per CU (v_mfma_f32_16x16x32_f16, whose published peak bf16
+ *   shares, and v_mfma_f32_16x16x4_f32), each the best of three timed runs.  BLOCKS the host; allocates 512 MiB of
+ *   device memory for the copy and frees it.  LYC_ERR_HIP on a HIP failure.
  * lyc_lora_linear_tune: the same arguments as lyc_lora_linear_fwd (whose
  *   output y it overwrites), plus the winner's tile, split and time (any
  *   may be NULL) and, in cand_ms (NULL or 7 doubles), the best time of
- *   each shortlisted candidate in lyc_gemm_plan's order.  Runs the whole
+ *   each shortlisted candidate in lyc_gemm_plan's order.  It first measures
+ *   the device's rates (lyc_measure_device_rates) if not yet done, so the
+ *   shortlist is ordered by them.  Runs the whole
  *   forward once and then three times timed
  *   with each shortlisted configuration on `stream`, and stores the fastest
  *   under the key of this device and shape; later lyc_lora_linear_fwd calls
@@ -375,6 +390,9 @@ int lyc_dora_linear_fwd(const void* x, int x_dt, const void* w, int w_dt, const 
  */
 int lyc_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t rf, int compute_dt, int max_out, int* count, int* tile_n,
                   int* tile_m, int* ksplit, double* cost_us);
+int lyc_device_rates(int64_t* cus, double* mfma16_flops, double* mfma32_flops, double* hbm_bytes_per_s,
+                     int* measured);
+int lyc_measure_device_rates(void* stream);
 int lyc_lora_linear_tune(const void* x, int x_dt, const void* w, int w_dt, const void* bias, int bias_dt,
                          const void* down, int down_dt, const void* up, int up_dt, int64_t rank, double scale,
                          void* y, int y_dt, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,

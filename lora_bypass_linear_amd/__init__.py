@@ -83,6 +83,8 @@ def lib():
                                                            ctypes.POINTER(c_sz)]
         pi, pd = ctypes.POINTER(c_int), ctypes.POINTER(ctypes.c_double)
         L.lyc_gemm_plan.argtypes = [c_i64, c_i64, c_i64, c_i64, c_int, c_int, pi, pi, pi, pi, pd]
+        L.lyc_device_rates.argtypes = [ctypes.POINTER(c_i64), pd, pd, pd, pi]
+        L.lyc_measure_device_rates.argtypes = [c_vp]
         L.lyc_lora_linear_tune.argtypes = [c_vp, c_int, c_vp, c_int, c_vp, c_int, c_vp, c_int, c_vp, c_int, c_i64,
                                            ctypes.c_double, c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_sz, c_vp,
                                            pi, pi, pi, pd, pd]
@@ -112,7 +114,7 @@ def lib():
                    L.lyc_linear_workspace_layout, L.lyc_lora_merge_workspace_size, L.lyc_lora_merge_fwd,
                    L.lyc_lora_linear_bwd_workspace_size, L.lyc_lora_linear_bwd, L.lyc_lora_linear_bwd_wt,
                    L.lyc_lora_linear_bwd_workspace_layout,
-                   L.lyc_gemm_plan, L.lyc_lora_linear_tune, L.lyc_tuning_key, L.lyc_tuning_lookup, L.lyc_tuning_save,
+                   L.lyc_gemm_plan, L.lyc_device_rates, L.lyc_measure_device_rates, L.lyc_lora_linear_tune, L.lyc_tuning_key, L.lyc_tuning_lookup, L.lyc_tuning_save,
                    L.lyc_tuning_load, L.lyc_tuning_clear, L.lyc_tuning_count, L.lyc_dora_norms_workspace_size,
                    L.lyc_dora_norms, L.lyc_dora_linear_workspace_size, L.lyc_dora_linear_fwd,
                    L.lyc_gemm_tile, L.lyc_profile_begin, L.lyc_profile_end):
@@ -269,6 +271,28 @@ def gemm_plan(M: int, N: int, K: int, rf: int, compute_dt: int, max_out: int = 7
     n = ctypes.c_int(0)
     _check(lib().lyc_gemm_plan(M, N, K, rf, compute_dt, max_out, ctypes.byref(n), tn, tm, ks, cost))
     return [(tn[i], tm[i], ks[i], cost[i]) for i in range(n.value)]
+
+
+def device_rates() -> dict:
+    """The planner's model of the current device: CU count, dense MFMA rates
+    (16-bit and fp32 operands, flop/s), HBM rate (bytes/s), and whether they
+    were measured on it (else MI355X's published peaks per CU)."""
+    cus = ctypes.c_int64(0)
+    m16, m32, hbm = ctypes.c_double(0), ctypes.c_double(0), ctypes.c_double(0)
+    measured = ctypes.c_int(0)
+    _check(lib().lyc_device_rates(ctypes.byref(cus), ctypes.byref(m16), ctypes.byref(m32), ctypes.byref(hbm),
+                                  ctypes.byref(measured)))
+    return {"cus": cus.value, "mfma16_flops": m16.value, "mfma32_flops": m32.value, "hbm_bytes_per_s": hbm.value,
+            "measured": bool(measured.value)}
+
+
+def measure_device_rates(device=None) -> dict:
+    """Measure the current (or given) CUDA device's rates for the planner
+    (blocks; allocates 512 MiB meanwhile) and return them."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    with torch.cuda.device(dev):
+        _check(lib().lyc_measure_device_rates(_stream(dev)))
+        return device_rates()
 
 
 def tuning_cache_path() -> str:

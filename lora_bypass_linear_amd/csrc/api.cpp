@@ -135,12 +135,9 @@ Layout layout(const Problem& P) {
     }
     if (P.lora) {
         // fp32 partial sums of a K-split GEMM (few output tiles), sized for
-        // the largest split of the planner's shortlist (a tuned pick may take it)
+        // the largest split the planner can shortlist (a tuned pick may take it)
         L.ksplit = lyc::gemm_ksplit(P.M, P.N, P.K, P.c_dt);
-        lyc::GemmCand plan[8];
-        const int np = lyc::gemm_plan(P.M, P.N, P.K, P.r_pad, P.c_dt, plan, 8);
-        int ks_max = L.ksplit;
-        for (int i = 0; i < np; ++i) ks_max = std::max(ks_max, plan[i].ksplit);
+        const int ks_max = lyc::gemm_plan_ksplit_max(P.M, P.N, P.K, P.c_dt);
         L.ks_max = ks_max;
         if (ks_max > 1) { L.partial = off; off = align256(off + (size_t)ks_max * (size_t)(P.M * P.N) * 4); }
         // DoRA: the per-feature gain m / norm in fp32
@@ -874,6 +871,21 @@ int lyc_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t rf, int compute_dt, i
     return LYC_OK;
 }
 
+int lyc_device_rates(int64_t* cus, double* mfma16_flops, double* mfma32_flops, double* hbm_bytes_per_s,
+                     int* measured) {
+    const lyc::DeviceRates r = lyc::device_rates();
+    if (cus) *cus = r.cus;
+    if (mfma16_flops) *mfma16_flops = r.mfma16;
+    if (mfma32_flops) *mfma32_flops = r.mfma32;
+    if (hbm_bytes_per_s) *hbm_bytes_per_s = r.hbm;
+    if (measured) *measured = r.measured;
+    return LYC_OK;
+}
+
+int lyc_measure_device_rates(void* stream) {
+    return lyc::measure_device_rates((hipStream_t)stream) == hipSuccess ? LYC_OK : LYC_ERR_HIP;
+}
+
 int lyc_lora_linear_tune(const void* x, int x_dt, const void* w, int w_dt, const void* bias, int bias_dt,
                          const void* down, int down_dt, const void* up, int up_dt, int64_t rank, double scale,
                          void* y, int y_dt, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
@@ -885,11 +897,14 @@ int lyc_lora_linear_tune(const void* x, int x_dt, const void* w, int w_dt, const
     if (!(scale == scale) || scale > 3.4e38 || scale < -3.4e38) return LYC_ERR_INVALID_ARG;
     const std::string key = lyc::tune_key("lora_fwd", M, N, K, P.r_pad, P.c_dt, P.o_dt);
     if (key.empty()) return LYC_ERR_HIP;
+    const char* env = std::getenv("LYC_KERNEL_TUNE");
+    const bool timing = !(env && (std::strcmp(env, "off") == 0 || std::strcmp(env, "0") == 0));
+    // the shortlist is ordered by this device's measured rates
+    if (timing && !lyc::device_rates().measured && lyc::measure_device_rates((hipStream_t)stream) != hipSuccess)
+        return LYC_ERR_HIP;
     lyc::GemmCand plan[8];
     const int np = lyc::gemm_plan(M, N, K, P.r_pad, P.c_dt, plan, 7);
     lyc::TuneChoice best{plan[0].tile, plan[0].ksplit, 0.0};
-    const char* env = std::getenv("LYC_KERNEL_TUNE");
-    const bool timing = !(env && (std::strcmp(env, "off") == 0 || std::strcmp(env, "0") == 0));
     if (timing && M > 0 && N > 0) {
         hipStream_t s = (hipStream_t)stream;
         hipEvent_t a, b;

@@ -16,6 +16,8 @@
 // never formed ("VRAM" section).
 #include <algorithm>
 #include <cmath>
+#include <map>
+#include <mutex>
 
 #include "kernels.h"
 #include "lyc_device.h"
@@ -582,8 +584,120 @@ static hipError_t run(const GemmParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Tile choice: fewest "rounds" of workgroups over 256 CUs, weighted by tile
-// area and a per-shape efficiency penalty (smaller tiles re-read more).
+// ---- the planner's device model ------------------------------------------------
+// Published MI355X dense peaks per CU (256 CUs: 2.5 PFLOP/s with 16-bit
+// operands, 157.3 TFLOP/s fp32) and its 8 TB/s of HBM, the defaults until the
+// device's own rates are measured.
+constexpr double PUB_MFMA16_PER_CU = 2500e12 / 256.0, PUB_MFMA32_PER_CU = 157.3e12 / 256.0, PUB_HBM = 8.0e12;
+
+static std::mutex rates_mu;
+static std::map<int, DeviceRates> rates_by_dev;
+
+DeviceRates device_rates() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return DeviceRates{256, 256 * PUB_MFMA16_PER_CU, 256 * PUB_MFMA32_PER_CU, PUB_HBM, 0};
+    }
+    std::lock_guard<std::mutex> lk(rates_mu);
+    auto it = rates_by_dev.find(dev);
+    if (it != rates_by_dev.end()) return it->second;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+        (void)hipGetLastError();
+        cus = 256;
+    }
+    const DeviceRates r{cus, cus * PUB_MFMA16_PER_CU, cus * PUB_MFMA32_PER_CU, PUB_HBM, 0};
+    rates_by_dev[dev] = r;
+    return r;
+}
+
+// Dense MFMA issue: every wave runs 8 independent accumulator chains of its
+// compute type's step on operands of 1.0 (`one`: the pattern of 1.0 in each
+// element; exact sums, no special values).
+// (The VGPR budget makes the compiler keep the chains in VGPRs, in the
+// MFMA's VGPR form; with accumulation registers it copied the 16-bit chains
+// through VGPRs every iteration.)
+template <class CT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(128))) void mfma_rate_kernel(f32x4* out, int iters,
+                                                                                          uint32_t one) {
+    const i32x4 a = i32x4{(int)one, (int)one, (int)one, (int)one};
+    f32x4 acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] = CT::step(a, a, acc[c]);
+    }
+    // every chain is stored, so none is dropped
+#pragma unroll
+    for (int c = 0; c < 8; ++c) out[((size_t)blockIdx.x * 256 + threadIdx.x) * 8 + c] = acc[c];
+}
+
+// best of three timed launches of fn on s, in seconds
+template <class F>
+static hipError_t best_of_3(hipStream_t s, hipEvent_t a, hipEvent_t b, F fn, double* sec) {
+    double best = 1e300;
+    hipError_t e = fn();   // warm-up
+    for (int rep = 0; rep < 3 && e == hipSuccess; ++rep) {
+        float ms = 0.f;
+        if ((e = hipEventRecord(a, s)) != hipSuccess) break;
+        if ((e = fn()) != hipSuccess) break;
+        if ((e = hipEventRecord(b, s)) != hipSuccess || (e = hipEventSynchronize(b)) != hipSuccess ||
+            (e = hipEventElapsedTime(&ms, a, b)) != hipSuccess)
+            break;
+        best = std::min(best, (double)ms * 1e-3);
+    }
+    *sec = best;
+    return e;
+}
+
+hipError_t measure_device_rates(hipStream_t s) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    DeviceRates r = device_rates();
+    constexpr size_t COPY = 256u << 20;
+    constexpr int ITERS = 2048, WG_PER_CU = 4;   // 16 waves per CU
+    const unsigned grid = (unsigned)(r.cus * WG_PER_CU);
+    // the rate kernels' outputs (8 vectors per thread) reuse the copy's buffer
+    if ((size_t)grid * 256 * 8 * sizeof(f32x4) > 2 * COPY) return hipErrorInvalidValue;
+    char* buf = nullptr;
+    hipEvent_t a = nullptr, b = nullptr;
+    if ((e = hipMalloc(&buf, 2 * COPY)) != hipSuccess) return e;
+    if ((e = hipEventCreate(&a)) == hipSuccess && (e = hipEventCreate(&b)) == hipSuccess) {
+        double t_copy = 0, t16 = 0, t32 = 0;
+        e = best_of_3(s, a, b, [&] { return hipMemcpyAsync(buf + COPY, buf, COPY, hipMemcpyDeviceToDevice, s); },
+                      &t_copy);
+        f32x4* out = (f32x4*)buf;   // grid * 256 * 8 vectors: 32 MiB at 256 CUs
+        if (e == hipSuccess)
+            e = best_of_3(s, a, b, [&] {
+                hipLaunchKernelGGL(mfma_rate_kernel<CF16>, dim3(grid), dim3(256), 0, s, out, ITERS, 0x3C003C00u);
+                return hipGetLastError();
+            }, &t16);
+        if (e == hipSuccess)
+            e = best_of_3(s, a, b, [&] {
+                hipLaunchKernelGGL(mfma_rate_kernel<CF32>, dim3(grid), dim3(256), 0, s, out, ITERS / 4, 0x3F800000u);
+                return hipGetLastError();
+            }, &t32);
+        if (e == hipSuccess && t_copy > 0 && t16 > 0 && t32 > 0) {
+            const double waves = (double)grid * 4.0;
+            r.hbm = 2.0 * (double)COPY / t_copy;                                  // read + write
+            r.mfma16 = waves * ITERS * 8.0 * (2.0 * 16 * 16 * 32) / t16;           // 16x16x32 steps
+            r.mfma32 = waves * (ITERS / 4) * 8.0 * 4.0 * (2.0 * 16 * 16 * 4) / t32;   // 4 x 16x16x4 per step
+            r.measured = 1;
+            std::lock_guard<std::mutex> lk(rates_mu);
+            rates_by_dev[dev] = r;
+        }
+    }
+    if (a) (void)hipEventDestroy(a);
+    if (b) (void)hipEventDestroy(b);
+    const hipError_t ef = hipFree(buf);
+    return e != hipSuccess ? e : ef;
+}
+
+// Tile choice: fewest "rounds" of workgroups over the device's CUs, weighted
+// by tile area and a per-shape efficiency penalty (smaller tiles re-read more).
 enum { T_L, T_G, T_M, T_S };
 static int pick_tile(int64_t M, int64_t N, bool f32) {
     struct C { int id, tn, tm; double pen; };
@@ -593,9 +707,10 @@ static int pick_tile(int64_t M, int64_t N, bool f32) {
     const int nc = f32 ? 2 : 4;
     int best = c[0].id;
     double best_cost = 1e300;
+    const double cus = (double)device_rates().cus;
     for (int i = 0; i < nc; ++i) {
         const double tiles = (double)((N + c[i].tn - 1) / c[i].tn) * (double)((M + c[i].tm - 1) / c[i].tm);
-        const double rounds = (double)(int64_t)((tiles + 255) / 256);
+        const double rounds = std::ceil(tiles / cus);
         const double cost = rounds * c[i].tn * c[i].tm * c[i].pen;
         if (cost < best_cost) { best_cost = cost; best = c[i].id; }
     }
@@ -611,9 +726,10 @@ int gemm_ksplit(int64_t M, int64_t N, int64_t K, int c_dt) {
     gemm_tile_shape(M, N, c_dt, &tn, &tm);
     const int64_t tiles = ((N + tn - 1) / tn) * ((M + tm - 1) / tm);
     const int64_t ksteps = (K * (c_dt == DT_F32 ? 4 : 2) + 127) / 128;
-    if (tiles >= 128 || tiles == 0) return 1;
-    // about 256 workgroups, at least 4 K steps each, at most 8 splits
-    int64_t ks = 256 / tiles;
+    const int64_t cus = device_rates().cus;
+    if (tiles >= cus / 2 || tiles == 0) return 1;
+    // about one workgroup per CU, at least 4 K steps each, at most 8 splits
+    int64_t ks = cus / tiles;
     if (ks > ksteps / 4) ks = ksteps / 4;
     if (ks > 8) ks = 8;
     while (ks > 1 && (double)M * (double)N * 4.0 * (double)ks > KSPLIT_PARTIAL_MAX) --ks;
@@ -635,15 +751,38 @@ void gemm_tile_dims(int tile, int* tn, int* tm) {
 }
 
 // The cost model: every workgroup of a tile runs its share of the K steps on
-// one CU (one workgroup per CU for every tile); the MFMA rate of a CU falls
-// with the tile's operand re-reads (the penalties of pick_tile); a K split
-// adds the fp32 partial sums' round trip through HBM and a second launch.
+// one CU (one workgroup per CU for every tile) at the device's MFMA rate per
+// CU; that rate falls with the tile's operand re-reads (the penalties of
+// pick_tile); a K split adds the fp32 partial sums' round trip through HBM at
+// the device's rate and a second launch.  The set of candidates does not
+// depend on the rates, only their order does.
+static bool plan_candidate(int64_t M, int64_t N, int64_t K, int tile, int ks, int c_dt) {
+    if (ks == 1) return true;
+    int tn, tm;
+    gemm_tile_dims(tile, &tn, &tm);
+    const int64_t tiles = ((N + tn - 1) / tn) * ((M + tm - 1) / tm);
+    const int64_t ksteps = (K * (c_dt == DT_F32 ? 4 : 2) + 127) / 128;
+    return tiles < device_rates().cus && ks <= ksteps / 4 && (double)M * (double)N * 4.0 * (double)ks <= KSPLIT_PARTIAL_MAX;
+}
+
+int gemm_plan_ksplit_max(int64_t M, int64_t N, int64_t K, int c_dt) {
+    int ks_max = gemm_ksplit(M, N, K, c_dt);
+    const bool f32 = c_dt == DT_F32;
+    const int tiles16[] = {T_L, T_G, T_M, T_S}, tiles32[] = {T_M, T_S};
+    for (int i = 0; i < (f32 ? 2 : 4); ++i)
+        for (int ks = 2; ks <= 8; ks *= 2)
+            if (plan_candidate(M, N, K, f32 ? tiles32[i] : tiles16[i], ks, c_dt)) ks_max = std::max(ks_max, ks);
+    return ks_max;
+}
+
 int gemm_plan(int64_t M, int64_t N, int64_t K, int64_t rf, int c_dt, GemmCand* out, int max_out) {
     if (max_out <= 0) return 0;
     const bool f32 = c_dt == DT_F32;
     const double es = f32 ? 4.0 : 2.0;
-    const double cu_rate = (f32 ? 157.3e12 : 2500e12) / 256.0;   // flop/s per CU at the published peak
-    const double hbm = 8.0e12;
+    const DeviceRates dr = device_rates();
+    const double cus = (double)dr.cus;
+    const double cu_rate = (f32 ? dr.mfma32 : dr.mfma16) / cus;   // flop/s per CU
+    const double hbm = dr.hbm;
     struct T { int id; double pen; };
     const T t16[] = {{T_L, 1.0}, {T_G, 1.0}, {T_M, 1.3}, {T_S, 2.0}};
     const T t32[] = {{T_M, 1.0}, {T_S, 1.5}};
@@ -654,7 +793,7 @@ int gemm_plan(int64_t M, int64_t N, int64_t K, int64_t rf, int c_dt, GemmCand* o
         int tn, tm;
         gemm_tile_dims(tile, &tn, &tm);
         const double tiles = (double)((N + tn - 1) / tn) * (double)((M + tm - 1) / tm);
-        const double rounds = std::ceil(tiles * ks / 256.0);
+        const double rounds = std::ceil(tiles * ks / cus);
         const double steps = std::ceil((double)ksteps / ks) + (double)((rf * (int64_t)es + 127) / 128);
         const double step_s = 2.0 * tn * tm * (128.0 / es) / cu_rate * pen;
         double t = rounds * steps * step_s + 2e-6;
@@ -666,14 +805,9 @@ int gemm_plan(int64_t M, int64_t N, int64_t K, int64_t rf, int c_dt, GemmCand* o
     double pen0 = 1.0;
     const int t0 = pick_tile(M, N, f32), k0 = gemm_ksplit(M, N, K, c_dt);
     for (int i = 0; i < nt; ++i) {
-        int tn, tm;
-        gemm_tile_dims(ts[i].id, &tn, &tm);
         if (ts[i].id == t0) pen0 = ts[i].pen;
-        const double tiles = (double)((N + tn - 1) / tn) * (double)((M + tm - 1) / tm);
         for (int ks = 1; ks <= 8; ks *= 2) {
-            if (ks > 1 && (tiles >= 256 || ks > ksteps / 4 ||
-                           (double)M * (double)N * 4.0 * (double)ks > KSPLIT_PARTIAL_MAX))
-                continue;
+            if (!plan_candidate(M, N, K, ts[i].id, ks, c_dt)) continue;
             all[n++] = GemmCand{ts[i].id, ks, cost(ts[i].id, ks, ts[i].pen)};
         }
     }

@@ -61,7 +61,26 @@ struct GemmCand {
 // itself), then the other tile / K-split pairs by modelled time.  Returns
 // the number written (at most max_out, at most 7).
 int gemm_plan(int64_t M, int64_t N, int64_t K, int64_t rf, int c_dt, GemmCand* out, int max_out);
+// the largest K split among every candidate the planner may shortlist for
+// this shape, whatever the device rates order them by (the workspace is
+// sized for it)
+int gemm_plan_ksplit_max(int64_t M, int64_t N, int64_t K, int c_dt);
 void gemm_tile_dims(int tile, int* tn, int* tm);
+
+// The planner's device model: CU count of the current device and its dense
+// MFMA rates (16-bit and fp32 operands, flop/s) and HBM rate (bytes/s).  Until
+// measured on the device, the rates are MI355X's published per-CU peaks
+// scaled by the CU count (measured = 0); without a device, 256 CUs.
+struct DeviceRates {
+    int64_t cus;
+    double mfma16, mfma32, hbm;
+    int measured;
+};
+DeviceRates device_rates();
+// times a 256 MiB device-to-device copy and MFMA loops on the device of
+// stream s (blocking; 512 MiB allocated for the copy meanwhile) and keeps the
+// rates for that device
+hipError_t measure_device_rates(hipStream_t s);
 
 // Exact-rounding contraction (h pass and plain affine projection):
 // C = x_c . b^T with fp64-folded MFMA steps, a rounding guard and in-kernel

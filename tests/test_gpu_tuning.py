@@ -93,3 +93,26 @@ def test_table_round_trip_on_the_device(tmp_path):
     # the key buckets M: a call of 100 tokens shares the 128-token entry
     assert L.tuning_key(100, *codes[1:]) == L.tuning_key(*codes)
     L.tuning_clear()
+
+
+def test_planner_takes_the_measured_device_rates():
+    """The planner's model counts the device's CUs and, once measured, its own
+    MFMA and HBM rates.  A sustained MFMA loop runs below the published peak
+    (the clock under load stays under the 2.4 GHz it assumes), a device copy
+    below 8 TB/s; the modelled time of a one-round GEMM (256 tiles of
+    256 x 256 over 128 + 2 steps of 64 k) is then that of the measured rate."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert L.device_rates()["cus"] == cus
+    say("measure device rates")
+    r = L.measure_device_rates()
+    print(r)
+    assert r["measured"] and r["cus"] == cus
+    assert 1e12 < r["hbm_bytes_per_s"] < 8e12
+    assert 0.5e15 < r["mfma16_flops"] < cus * 2500e12 / 256 * 1.01
+    assert 0.03e15 < r["mfma32_flops"] < cus * 157.3e12 / 256 * 1.01
+    assert L.device_rates() == r
+    (tn, tm, ks, cost), = L.gemm_plan(4096, 4096, 8192, 128, L.BF16, max_out=1)
+    assert (tn, tm, ks) == (256, 256, 1)
+    step_s = 2.0 * 256 * 256 * 64 / (r["mfma16_flops"] / cus)
+    rounds = -(-256 // cus)
+    assert cost == pytest.approx((rounds * 130 * step_s + 2e-6) * 1e6, rel=1e-9)

@@ -34,6 +34,26 @@ def test_workspace_covers_every_shortlisted_split():
     ks = max(p[2] for p in L.gemm_plan(M, N, K, 16, L.F16))
     assert ks > 1
     assert L.lora_workspace_size(M, N, K, r, L.F16, L.F16, 0, L.F16, L.F16) >= ks * M * N * 4
+    # every split the planner could shortlist, whatever order the device's
+    # measured rates give: 8 for the 64 x 64 tiles at this shape
+    assert L.lora_workspace_size(M, N, K, r, L.F16, L.F16, 0, L.F16, L.F16) >= 8 * M * N * 4
+
+
+def test_device_rates_without_a_device():
+    """No device: 256 CUs and MI355X's published peaks, not measured."""
+    r = L.device_rates()
+    assert r == {"cus": 256, "mfma16_flops": 2500e12, "mfma32_flops": 157.3e12, "hbm_bytes_per_s": 8e12,
+                 "measured": False}
+
+
+def test_model_time_follows_the_rates():
+    """One round of 256 workgroups of 256 x 256 tiles over 8192 K (128 steps of
+    64 k plus two fold steps): 2 * 256 * 256 * 64 flops per step at the
+    published per-CU rate, plus the fixed launch term."""
+    (tn, tm, ks, cost), = L.gemm_plan(4096, 4096, 8192, 128, L.BF16, max_out=1)
+    assert (tn, tm, ks) == (256, 256, 1)
+    step_s = 2.0 * 256 * 256 * 64 / (2500e12 / 256)
+    assert cost == pytest.approx((130 * step_s + 2e-6) * 1e6, rel=1e-12)
 
 
 def _table(path, lines):
