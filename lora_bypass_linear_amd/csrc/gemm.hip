@@ -358,12 +358,82 @@ __device__ __forceinline__ void k_step_main(const Steps<TL>& S, __amdgpu_buffer_
     }
 }
 
+// The output tile through LDS, so that every store writes whole rows of it.
+// A lane's MFMA results are 4 consecutive n of one token row m for each 16x16
+// block, so a store straight from them covers 16 rows x 8-16 bytes: at the
+// bf16 16384 x 8192 x 8192 size those partial-line stores took ~9 us at the
+// end of each tile.  Here the waves write their blocks (scaled, biased,
+// rounded to y's dtype) into the free pipeline stages as rows of the tile
+// (16-byte chunk c of row r at slot c ^ (r & 7)), and then store 16-byte
+// chunks in row order: a wave's store covers 1 KiB of consecutive rows.  A
+// tile larger than the stages (fp32 output of the 256-row tiles) goes in two
+// passes of half its rows.  Needs N * ES a multiple of 16 and y 16-byte
+// aligned (a chunk is then all inside y's row or all past its end).
+template <class TL, int ES, bool GAIN>
+__device__ __forceinline__ void epilogue_rows(const GemmParams& p, char* smem, const f32x4 (&acc)[TL::FN][TL::FM],
+                                              const float* biasv, const float* gainv, int64_t n0, int64_t m0,
+                                              int wave, int lane, int wn, int wm) {
+    constexpr int RB = TL::TN * ES, CHR = RB / 16;   // bytes and 16-byte chunks of a tile row
+    constexpr int CAP = TL::NS * TL::STAGE;
+    constexpr int TMP = TL::TM * RB <= CAP ? TL::TM : TL::TM / 2;   // rows per pass
+    constexpr int PASSES = TL::TM / TMP, IT = TMP * CHR / (TL::NW * 64);
+    static_assert(TMP * RB <= CAP && TL::TM % TMP == 0 && TMP % TL::WM == 0 && CHR % 8 == 0, "staged rows");
+    static_assert(IT * TL::NW * 64 == TMP * CHR, "whole wave stores");
+    const int64_t yrow = p.N * ES;
+    // (the barriers fence the scheduler, and the stores go four chunks at a
+    // time: with two passes the second pass's writers still hold their
+    // accumulators during the first pass's stores, and a deeper batch, or
+    // outputs computed ahead of a barrier, made the registers spill)
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+        __syncthreads();   // the stages (then the previous pass's rows) are free
+        __builtin_amdgcn_sched_barrier(0);
+        if ((wm * TL::WM) / TMP == ps) {
+#pragma unroll
+            for (int i = 0; i < TL::FN; ++i) {
+                const int nl = wn * TL::WN + i * 16 + 4 * (lane >> 4);
+                const float* bias = biasv + 4 * i;
+                const float* gain = gainv + (GAIN ? 4 * i : 0);
+#pragma unroll
+                for (int j = 0; j < TL::FM; ++j) {
+                    const int r = wm * TL::WM + j * 16 + (lane & 15) - ps * TMP;
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e] * (GAIN ? gain[e] : p.post) + bias[e];
+                    const int cb = nl * ES;   // byte column
+                    char* dst = smem + r * RB + ((((cb >> 4) ^ (r & 7)) << 4) | (cb & 15));
+                    if constexpr (ES == 4) {
+                        *(f32x4*)dst = f32x4{v[0], v[1], v[2], v[3]};
+                    } else {
+                        const uint32_t lo = p.y_dt == DT_F16 ? pack_f16x2(v[0], v[1]) : pack_bf16x2(v[0], v[1]);
+                        const uint32_t hi = p.y_dt == DT_F16 ? pack_f16x2(v[2], v[3]) : pack_bf16x2(v[2], v[3]);
+                        *(i32x2*)dst = i32x2{(int)lo, (int)hi};
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll 4
+        for (int it = 0; it < IT; ++it) {
+            const int idx = (it * TL::NW + wave) * 64 + lane;
+            const int r = idx / CHR, c = idx % CHR;
+            const i32x4 d = *(const i32x4*)(smem + r * RB + ((c ^ (r & 7)) << 4));
+            const int64_t m = m0 + ps * TMP + r, n = n0 + c * (16 / ES);
+            if (m < p.M && n < p.N) *(i32x4*)((char*)p.y + m * yrow + n * ES) = d;
+        }
+    }
+}
+
 // GAIN: a per-output-feature factor gain[n] in place of post (an instance of
 // its own, so the others carry no registers for it)
 // TA / TB: the A / B operand stored with the contraction index as rows
 // (LoaderT; main steps only, launched with both and no fold); otherwise
 // operands as the forward stores them.
-template <class CT, class TL, bool GAIN, bool TA = false, bool TB = false>
+// ROWS: the outputs go out through LDS as whole rows (epilogue_rows; no K
+// split, N * bytes of y's dtype a multiple of 16, y 16-byte aligned): an
+// instance of its own, since both epilogues in one kernel made it spill.
+template <class CT, class TL, bool GAIN, bool TA = false, bool TB = false, bool ROWS = false>
 __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles_n, int tiles_m, int group_m) {
     // the operand stages, then the tile's bias widened to fp32.  One LDS
     // object: with a second __shared__ array the compiler could no longer
@@ -502,6 +572,11 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_kernel(GemmParams p, int tiles
         for (int i = 0; i < FN * 4; ++i) idx[i] = n0 + wn * TL::WN + (i >> 2) * 16 + 4 * (lane >> 4) + (i & 3);
         load_n_as_f32<FN * 4>(p.gain, DT_F32, idx, p.N, gainv);
     }
+    if constexpr (ROWS) {
+        if (p.y_dt == DT_F32) epilogue_rows<TL, 4, GAIN>(p, smem, acc, biasv, gainv, n0, m0, wave, lane, wn, wm);
+        else epilogue_rows<TL, 2, GAIN>(p, smem, acc, biasv, gainv, n0, m0, wave, lane, wn, wm);
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
         const int64_t nb = n0 + wn * TL::WN + i * 16 + 4 * (lane >> 4);
@@ -571,12 +646,22 @@ static hipError_t run(const GemmParams& p, hipStream_t s) {
             hipLaunchKernelGGL((gemm_kernel<CT, TL, false, true, true>), dim3(nblk, ks), dim3(TL::NT), 0, s, p, tiles_n,
                                tiles_m, 4);
     }
+    // whole-row stores of the output (epilogue_rows)
+    const bool rows = ks == 1 && (p.N * (p.y_dt == DT_F32 ? 4 : 2)) % 16 == 0 && ((uintptr_t)p.y & 15) == 0;
     if (p.ta || p.tb) {
         // (no transposed instance for fp32 compute or the 192-row tile: refused above)
-    } else if (p.gain != nullptr && ks == 1)
-        hipLaunchKernelGGL((gemm_kernel<CT, TL, true>), dim3(nblk, ks), dim3(TL::NT), 0, s, p, tiles_n, tiles_m, 4);
-    else
+    } else if (p.gain != nullptr && ks == 1) {
+        if (rows)
+            hipLaunchKernelGGL((gemm_kernel<CT, TL, true, false, false, true>), dim3(nblk, ks), dim3(TL::NT), 0, s, p,
+                               tiles_n, tiles_m, 4);
+        else
+            hipLaunchKernelGGL((gemm_kernel<CT, TL, true>), dim3(nblk, ks), dim3(TL::NT), 0, s, p, tiles_n, tiles_m, 4);
+    } else if (rows) {
+        hipLaunchKernelGGL((gemm_kernel<CT, TL, false, false, false, true>), dim3(nblk, ks), dim3(TL::NT), 0, s, p,
+                           tiles_n, tiles_m, 4);
+    } else {
         hipLaunchKernelGGL((gemm_kernel<CT, TL, false>), dim3(nblk, ks), dim3(TL::NT), 0, s, p, tiles_n, tiles_m, 4);
+    }
     if (ks > 1) {
         const int64_t blocks = (p.M * p.N + 255) / 256;
         hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, p);
