@@ -123,6 +123,21 @@ def test_k_split_gemm(name, dims):
 def test_every_tile_configuration_is_covered():
     tiles = {L.gemm_tile(M, N, L.F16) for M, N, _ in TILE_SHAPES}
     assert tiles == {(64, 64), (128, 128), (192, 256), (256, 256)}
+    assert {L.gemm_tile(M, N, L.F16) for M, N, _ in TILE_SHAPES_ROWS} == tiles
+
+
+# the same tiles with y's rows a multiple of 16 bytes: the epilogue that stores
+# whole rows through LDS (16-bit y in one pass; fp32 y of the 256-row tiles in
+# two), with ragged M and K
+TILE_SHAPES_ROWS = [(300, 336, 264), (1000, 2504, 392), (2600, 3104, 264), (3100, 4000, 136)]
+
+
+@pytest.mark.parametrize("M,N,K", TILE_SHAPES_ROWS)
+@pytest.mark.parametrize("name", ["lora_f16_4096x3072x3072_r16", "lora_bf16_16384x8192x8192_r128",
+                                  "lora_bf16x_f32w_8192x4096x4096_r64"])
+def test_tiles_whole_row_stores(name, M, N, K):
+    wl = BASE[name].resized(M=M, N=N, K=K)
+    _check(wl, rows=sample_rows(M, 24, seed=N))
 
 
 def test_fp32_compute_tiles():
