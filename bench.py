@@ -137,6 +137,7 @@ def main():
 
     # the tile planner's device model, measured on this GPU (its shortlist
     # order in small_m[].tuned follows these rates)
+    import lora_bypass_linear_amd as L
     rates = L.measure_device_rates(dev)
     out["device_rates"] = {"cus": rates["cus"], "mfma16_tflops": round(rates["mfma16_flops"] / 1e12, 1),
                            "mfma32_tflops": round(rates["mfma32_flops"] / 1e12, 1),
