@@ -459,12 +459,16 @@ def _dora(dev, wl, inputs, reps, warm, accuracy):
     wall_l, prof_l = timed_calls(lambda: L.lora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, d.get("b"),
                                                        out=yl))
     dev_us = lambda prof: round(sum(ms for _, ms in prof.values()) * 1e3 / reps, 2)
+    # the norm pass's HBM bytes from its counter profile (null once its sources changed)
+    from lora_bypass_linear_amd.profsum import read_traffic
+    traffic = read_traffic(os.path.join(ROOT, "profiles", f"traffic_doranorm_{wl.name}.txt"), "merge")
     out = {"shape": f"M {wl.M}, N {wl.N}, K {wl.K}, rank {wl.r}, magnitude {WL.NAME[L.dtype_code(m)]}",
            "norms": {"wall_us_per_call": round(wall_n, 2), "device_us_per_call": dev_us(prof_n),
                      "roofline": {"bound": "hbm", "kernel": kname + " (row norms)",
                                   "achieved": round(nbytes / (g_us * 1e-6) / 1e9, 1), "peak": HBM_GBS,
                                   "unit": "GB/s", "frac": round(nbytes / (g_us * 1e-6) / 1e9 / HBM_GBS, 4),
-                                  "traffic": None, "bytes_per_launch": nbytes, "avg_us": round(g_us, 3)}},
+                                  "traffic": None if traffic is None else int(traffic), "bytes_per_launch": nbytes,
+                                  "avg_us": round(g_us, 3)}},
            "forward": {"wall_us_per_call": round(wall_f, 2), "device_us_per_call": dev_us(prof_f),
                        "tflops": round(wl.flops / (dev_us(prof_f) * 1e-6) / 1e12, 2),
                        "lora_forward_device_us": dev_us(prof_l)}}
