@@ -508,6 +508,7 @@ struct BwdLayout {
     // 1 GiB); else they read transposed copies.  dx reads W^T and down^T copies.
     bool tr_tok = false;
     int ks_dx = 1, ks_dd = 1, ks_du = 1;
+    int tile_dd = lyc::GEMM_TILE_AUTO, tile_du = lyc::GEMM_TILE_AUTO;   // tr_tok: lyc::gemm_tok_plan's tiles
 };
 
 int check_bwd(Bwd& B) {
@@ -533,21 +534,6 @@ int check_bwd(Bwd& B) {
     P.r_pad = P.rank == 0 ? 0 : (P.rank <= 16 && P.c_dt != LYC_F32) ? 16 : (P.rank <= 32 ? 32 : P.rank <= 64 ? 64 : P.rank <= 128 ? 128 : 256);
     B.M8 = (P.M + 7) & ~(int64_t)7;
     return LYC_OK;
-}
-
-// K split of a token contraction read in place (dDown, dUp): the token
-// count against few output tiles; about two workgroups per compute unit (512),
-// at least 4 K steps each, at most 8 splits
-int tok_ksplit(int64_t M, int64_t N, int64_t K, int c_dt) {
-    int tn, tm;
-    lyc::gemm_tile_shape(M, N, c_dt, &tn, &tm);
-    const int64_t tiles = ((N + tn - 1) / tn) * ((M + tm - 1) / tm);
-    const int64_t ksteps = (K * 2 + 127) / 128;
-    if (tiles == 0) return 1;
-    int64_t ks = (512 + tiles - 1) / tiles;
-    if (ks > ksteps / 4) ks = ksteps / 4;
-    if (ks > 8) ks = 8;
-    return ks > 1 ? (int)ks : 1;
 }
 
 BwdLayout bwd_layout(const Bwd& B) {
@@ -594,7 +580,7 @@ BwdLayout bwd_layout(const Bwd& B) {
             take(L.xt, K * M8 * ce);
             take(L.ght, R * M8 * ce);
         }
-        L.ks_dd = L.tr_tok ? tok_ksplit(P.rank, P.K, Kt, P.c_dt) : lyc::gemm_ksplit(P.rank, P.K, Kt, P.c_dt);
+        L.ks_dd = L.tr_tok ? lyc::gemm_tok_plan(P.rank, P.K, Kt, &L.tile_dd) : lyc::gemm_ksplit(P.rank, P.K, Kt, P.c_dt);
         if (L.ks_dd > 1) part = std::max(part, (size_t)L.ks_dd * (size_t)P.rank * K * 4);
     }
     if (du) {
@@ -602,7 +588,7 @@ BwdLayout bwd_layout(const Bwd& B) {
             take(L.dyt, N * M8 * ce);
             take(L.ht, R * M8 * ce);
         }
-        L.ks_du = L.tr_tok ? tok_ksplit(P.N, P.rank, Kt, P.c_dt) : lyc::gemm_ksplit(P.N, P.rank, Kt, P.c_dt);
+        L.ks_du = L.tr_tok ? lyc::gemm_tok_plan(P.N, P.rank, Kt, &L.tile_du) : lyc::gemm_ksplit(P.N, P.rank, Kt, P.c_dt);
         if (L.ks_du > 1) part = std::max(part, (size_t)L.ks_du * N * (size_t)P.rank * 4);
     }
     if (part > 0) take(L.partial, part);
@@ -809,6 +795,7 @@ int backward(const Bwd& B, const void* x, const void* w, const void* down, const
         g.post = 1.0f;
         g.y = d_down;
         g.y_dt = P.d_dt;
+        g.tile = L.tile_dd;
         g.ksplit = L.ks_dd;
         g.partial = L.ks_dd > 1 ? (float*)(W + L.partial) : nullptr;
         g.vec_store = (K % 4 == 0) && aligned(d_down, P.d_dt == LYC_F32 ? 16 : 8);
@@ -842,6 +829,7 @@ int backward(const Bwd& B, const void* x, const void* w, const void* down, const
         g.post = (float)scale;
         g.y = d_up;
         g.y_dt = P.u_dt;
+        g.tile = L.tile_du;
         g.ksplit = L.ks_du;
         g.partial = L.ks_du > 1 ? (float*)(W + L.partial) : nullptr;
         g.vec_store = (r % 4 == 0) && aligned(d_up, P.u_dt == LYC_F32 ? 16 : 8);

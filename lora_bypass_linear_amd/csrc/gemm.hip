@@ -821,6 +821,28 @@ int gemm_ksplit(int64_t M, int64_t N, int64_t K, int c_dt) {
     return ks > 1 ? (int)ks : 1;
 }
 
+// A contraction over the tokens read in place (the backward's dDown and dUp:
+// an M x N output with one side the rank, K the token count): the output tile
+// covers the rank side whole, so that the token-major operand (x or dy, the
+// large one) streams through once; a 64-wide tile read it twice at rank 128.
+// The K split then gives about one workgroup per CU (two for the 64 x 64 tile,
+// whose stages take half the LDS), at least 4 K steps each, at most 8 splits.
+int gemm_tok_plan(int64_t M, int64_t N, int64_t K, int* tile) {
+    const int64_t r = M < N ? M : N;
+    const int t = r <= 64 ? T_S : (r <= 128 ? T_M : T_L);
+    int tn, tm;
+    gemm_tile_dims(t, &tn, &tm);
+    *tile = t;
+    const int64_t tiles = ((N + tn - 1) / tn) * ((M + tm - 1) / tm);
+    const int64_t ksteps = (K * 2 + 127) / 128;
+    if (tiles == 0) return 1;
+    const int64_t want = device_rates().cus * (t == T_S ? 2 : 1);
+    int64_t ks = (want + tiles - 1) / tiles;
+    if (ks > ksteps / 4) ks = ksteps / 4;
+    if (ks > 8) ks = 8;
+    return ks > 1 ? (int)ks : 1;
+}
+
 void gemm_tile_shape(int64_t M, int64_t N, int c_dt, int* tn, int* tm) {
     static const int shape[4][2] = {{256, 256}, {192, 256}, {128, 128}, {64, 64}};
     const int t = pick_tile(M, N, c_dt == DT_F32);

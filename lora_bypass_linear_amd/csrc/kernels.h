@@ -66,6 +66,9 @@ int gemm_plan(int64_t M, int64_t N, int64_t K, int64_t rf, int c_dt, GemmCand* o
 // sized for it)
 int gemm_plan_ksplit_max(int64_t M, int64_t N, int64_t K, int c_dt);
 void gemm_tile_dims(int tile, int* tn, int* tm);
+// tile (written to *tile) and K split of a 16-bit contraction over the tokens
+// read in place (M x N output, one side the rank, K tokens)
+int gemm_tok_plan(int64_t M, int64_t N, int64_t K, int* tile);
 
 // The planner's device model: CU count of the current device and its dense
 // MFMA rates (16-bit and fp32 operands, flop/s) and HBM rate (bytes/s).  Until
