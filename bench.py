@@ -559,7 +559,23 @@ def _backward(dev, wl, inputs, reps, warm, accuracy, eager):
         call(w_t=w_t)
     torch.cuda.synchronize()
     prof_wt = L.profile_end()
-    del w_t
+    # ... and with the h_r its forward left as well (what a training step keeps): no h pass
+    _, fws = L.lora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, d.get("b"), return_workspace=True)
+    h = L.lora_saved_h(fws, d["x"], d["w"], d["down"], d["up"], d.get("b"))
+    for _ in range(3):
+        call(w_t=w_t, h=h)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        call(w_t=w_t, h=h)
+    torch.cuda.synchronize()
+    ms_st = (time.perf_counter() - t0) * 1e3 / reps
+    L.profile_begin(32 * reps)
+    for _ in range(reps):
+        call(w_t=w_t, h=h)
+    torch.cuda.synchronize()
+    prof_st = L.profile_end()
+    del w_t, h, fws
     out = {"shape": f"M {M}, N {N}, K {K}, rank {r}, dy {WL.NAME[WL.dtype_code(dy_cpu)]}",
            "ms_per_call": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
            "flops_per_call": flops,
@@ -568,6 +584,10 @@ def _backward(dev, wl, inputs, reps, warm, accuracy, eager):
            "with_caller_wt": {"ms_per_call": round(ms_wt, 4), "tflops": round(flops / (ms_wt * 1e-3) / 1e12, 2),
                               "kernels": {names[k]: {"launches": n // reps, "us_per_call": round(t * 1e3 / reps, 2)}
                                           for k, (n, t) in prof_wt.items() if n}},
+           "with_caller_wt_and_saved_h": {
+               "ms_per_call": round(ms_st, 4), "tflops": round(flops / (ms_st * 1e-3) / 1e12, 2),
+               "kernels": {names[k]: {"launches": n // reps, "us_per_call": round(t * 1e3 / reps, 2)}
+                           for k, (n, t) in prof_st.items() if n}},
            "roofline": {"bound": "mfma", "kernel": "gemm_kernel (dx = dy_c.W_c + gh_r.down_c)",
                         "achieved": round(dx_flops / (g_us * 1e-6) / 1e12, 2), "peak": peak, "unit": "TFLOP/s",
                         "frac": round(dx_flops / (g_us * 1e-6) / 1e12 / peak, 4), "traffic": None,

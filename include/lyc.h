@@ -260,7 +260,8 @@ int lyc_lora_merge_fwd(const void* w, int w_dt, const void* down, int down_dt, c
  *    workspace too.  Its size comes from
  *    lyc_lora_linear_bwd_workspace_size with `want` = 1 (dx) | 2 (dDown) |
  *    4 (dUp), the set of non-NULL outputs of the call (| 8 for
- *    lyc_lora_linear_bwd_wt, which needs no W^T copy).
+ *    lyc_lora_linear_bwd_wt, which needs no W^T copy; | 16 for
+ *    lyc_lora_linear_bwd_saved given h_r, which needs no h region).
  * Same stream, ownership and error conventions as the forward.
  */
 int lyc_lora_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt,
@@ -286,6 +287,30 @@ int lyc_lora_linear_bwd_wt(const void* x, int x_dt, const void* w_t, int w_dt, i
                            int down_dt, const void* up, int up_dt, int64_t rank, double scale, const void* dy,
                            int dy_dt, void* dx, void* d_down, void* d_up, int64_t M, int64_t N, int64_t K,
                            void* workspace, size_t workspace_bytes, void* stream);
+/*
+ * The backward with what a training step keeps from its forward: the
+ * forward's h_r = round_c(x_c . down_c^T), which dUp = round_up(scale * dy_c^T
+ * . h_r) reads (the forward computes it anyway; LyCORIS "Precision" page,
+ * "Measured accuracy": h is rounded to the storage dtype before its second
+ * dot, so the saved value is the one the backward needs), and optionally the
+ * caller-kept W_c^T of lyc_lora_linear_bwd_wt.
+ *   w, w_t: at most one non-NULL (LYC_ERR_INVALID_ARG otherwise); w_t as for
+ *           lyc_lora_linear_bwd_wt.  Neither is read unless dx is wanted.
+ *   h_r:    NULL (recomputed, as lyc_lora_linear_bwd does), or [M][r_pad] in
+ *           the compute dtype, 16-byte aligned, exactly as lyc_lora_linear_fwd
+ *           left it in its workspace (h_offset and h_ld = r_pad from
+ *           lyc_lora_workspace_layout) for the same x, down and dtypes: no h
+ *           pass runs.  Read only when dUp is wanted; it must not overlap an
+ *           output (LYC_ERR_INVALID_ARG).
+ * The workspace size comes from lyc_lora_linear_bwd_workspace_size with bit
+ * 16 added to `want` when h_r is given (and 8 when w_t is).  Given the
+ * forward's h_r, results are identical to lyc_lora_linear_bwd's.
+ */
+int lyc_lora_linear_bwd_saved(const void* x, int x_dt, const void* w, const void* w_t, int w_dt, int bias_dt,
+                              const void* down, int down_dt, const void* up, int up_dt, const void* h_r,
+                              int64_t rank, double scale, const void* dy, int dy_dt, void* dx, void* d_down,
+                              void* d_up, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                              void* stream);
 /*
  * Where lyc_lora_linear_bwd leaves h_r and gh_r in its workspace (both
  * [M][ld] in the compute dtype; SIZE_MAX when the call set `want` does not

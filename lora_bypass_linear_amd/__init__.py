@@ -77,6 +77,9 @@ def lib():
                                           ctypes.c_double, c_vp, c_int, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64,
                                           c_vp, c_sz, c_vp]
         L.lyc_lora_linear_bwd_wt.argtypes = list(L.lyc_lora_linear_bwd.argtypes)
+        L.lyc_lora_linear_bwd_saved.argtypes = [c_vp, c_int, c_vp, c_vp, c_int, c_int, c_vp, c_int, c_vp, c_int, c_vp,
+                                                c_i64, ctypes.c_double, c_vp, c_int, c_vp, c_vp, c_vp, c_i64, c_i64,
+                                                c_i64, c_vp, c_sz, c_vp]
         L.lyc_lora_linear_bwd_workspace_layout.argtypes = [c_i64, c_i64, c_i64, c_i64, c_int, c_int, c_int, c_int,
                                                            c_int, c_int, c_int, ctypes.POINTER(c_sz),
                                                            ctypes.POINTER(c_sz), ctypes.POINTER(c_i64),
@@ -113,6 +116,7 @@ def lib():
                    L.lyc_lora_workspace_layout,
                    L.lyc_linear_workspace_layout, L.lyc_lora_merge_workspace_size, L.lyc_lora_merge_fwd,
                    L.lyc_lora_linear_bwd_workspace_size, L.lyc_lora_linear_bwd, L.lyc_lora_linear_bwd_wt,
+                   L.lyc_lora_linear_bwd_saved,
                    L.lyc_lora_linear_bwd_workspace_layout,
                    L.lyc_gemm_plan, L.lyc_device_rates, L.lyc_measure_device_rates, L.lyc_lora_linear_tune, L.lyc_tuning_key, L.lyc_tuning_lookup, L.lyc_tuning_save,
                    L.lyc_tuning_load, L.lyc_tuning_clear, L.lyc_tuning_count, L.lyc_dora_norms_workspace_size,
@@ -244,7 +248,7 @@ def lora_merge_workspace_size(N, K, r, w_dt, d_dt, u_dt) -> int:
     return n.value
 
 
-BWD_DX, BWD_DDOWN, BWD_DUP, BWD_WT = 1, 2, 4, 8
+BWD_DX, BWD_DDOWN, BWD_DUP, BWD_WT, BWD_H = 1, 2, 4, 8, 16
 
 
 def lora_bwd_workspace_size(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt, dy_dt, want=7) -> int:
@@ -462,28 +466,48 @@ def lora_merge(w: torch.Tensor, down: torch.Tensor, up: torch.Tensor, scale: flo
     return out
 
 
+def lora_saved_h(workspace: torch.Tensor, x: torch.Tensor, w: torch.Tensor, down: torch.Tensor, up: torch.Tensor,
+                 bias: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The h_r [M, r_pad] that lora_linear left in ``workspace`` (returned by
+    it with ``return_workspace``) for these operands: a view, valid until the
+    workspace is reused; pass it to lora_linear_backward as ``h``."""
+    M, N, K, r = _lora_shapes(x, w, down, up, bias, None)
+    codes = [dtype_code(t) for t in (x, w)] + [dtype_code(bias) if bias is not None else 0] + \
+        [dtype_code(down), dtype_code(up)]
+    ho, ld, _, _ = lora_workspace_layout(M, N, K, r, *codes)
+    c_dt = resolve_dtypes([c for c in codes if c])[0]
+    es = 4 if c_dt == F32 else 2
+    return workspace[ho: ho + M * ld * es].view(_TORCH[c_dt]).view(M, ld)
+
+
 def lora_linear_backward(x: torch.Tensor, w: torch.Tensor, down: torch.Tensor, up: torch.Tensor, scale: float,
                          dy: torch.Tensor, bias_dtype: Optional[torch.dtype] = None, want_dx: bool = True,
                          want_ddown: bool = True, want_dup: bool = True, workspace: Optional[torch.Tensor] = None,
-                         return_workspace: bool = False, w_t: Optional[torch.Tensor] = None):
+                         return_workspace: bool = False, w_t: Optional[torch.Tensor] = None,
+                         h: Optional[torch.Tensor] = None):
     """Gradients (dx, d_down, d_up) of the LoRA-bypass linear for dy, each in
     its leaf's dtype (None where not wanted).  W and the bias are frozen;
     ``bias_dtype`` is the forward's bias dtype (it enters the dtype policy).
     ``w_t``: optional caller-kept W_c^T [K, N] in the compute dtype (W rounded
     to it, then transposed; kept across steps while W is frozen): dx reads it
-    in place and no W^T copy is made per call."""
+    in place and no W^T copy is made per call.  ``h``: optional h_r [M, r_pad]
+    the forward left (``lora_saved_h``): dUp reads it and no h pass runs."""
     M, N, K, r = _lora_shapes(x, w, down, up, None, None)
     _shape(dy, (M, N), "dy")
     _shape(w_t, (K, N), "w_t")
-    dev = _need_device(x, w, down, up, dy, workspace, w_t)
+    dev = _need_device(x, w, down, up, dy, workspace, w_t, h)
     x_dt, w_dt, d_dt, u_dt, g_dt = (dtype_code(t) for t in (x, w, down, up, dy))
     b_dt = dtype_code(torch.empty(0, dtype=bias_dtype)) if bias_dtype is not None else 0
-    if w_t is not None:
-        c_dt = resolve_dtypes([x_dt, w_dt] + ([b_dt] if b_dt else []) + [d_dt, u_dt, g_dt])[0]
-        if w_t.dtype != _TORCH[c_dt]:
-            raise ValueError(f"w_t has dtype {w_t.dtype}, the compute dtype is {_TORCH[c_dt]}")
+    c_dt = resolve_dtypes([x_dt, w_dt] + ([b_dt] if b_dt else []) + [d_dt, u_dt, g_dt])[0]
+    if w_t is not None and w_t.dtype != _TORCH[c_dt]:
+        raise ValueError(f"w_t has dtype {w_t.dtype}, the compute dtype is {_TORCH[c_dt]}")
+    if h is not None:
+        r_pad = lora_bwd_workspace_layout(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt, g_dt, BWD_DUP)[2]
+        _shape(h, (M, r_pad), "h")
+        if h.dtype != _TORCH[c_dt]:
+            raise ValueError(f"h has dtype {h.dtype}, the compute dtype is {_TORCH[c_dt]}")
     want = (BWD_DX if want_dx else 0) | (BWD_DDOWN if want_ddown else 0) | (BWD_DUP if want_dup else 0) | \
-        (BWD_WT if w_t is not None else 0)
+        (BWD_WT if w_t is not None else 0) | (BWD_H if h is not None else 0)
     dx = torch.empty((M, K), dtype=x.dtype, device=dev) if want_dx else None
     dd = torch.empty((r, K), dtype=down.dtype, device=dev) if want_ddown else None
     du = torch.empty((N, r), dtype=up.dtype, device=dev) if want_dup else None
@@ -491,9 +515,15 @@ def lora_linear_backward(x: torch.Tensor, w: torch.Tensor, down: torch.Tensor, u
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     # an empty output still has to be passed (non-NULL) to be "wanted"
     p = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr() if t.numel() else 256)
-    fn, wp = (lib().lyc_lora_linear_bwd_wt, w_t) if w_t is not None else (lib().lyc_lora_linear_bwd, w)
-    _check(fn(_ptr(x), x_dt, _ptr(wp), w_dt, b_dt, _ptr(down), d_dt, _ptr(up), u_dt, r, float(scale), _ptr(dy), g_dt,
-              p(dx), p(dd), p(du), M, N, K, _ptr(ws), nbytes, _stream(dev)))
+    if h is not None:
+        _check(lib().lyc_lora_linear_bwd_saved(_ptr(x), x_dt, None if w_t is not None else _ptr(w), _ptr(w_t), w_dt,
+                                               b_dt, _ptr(down), d_dt, _ptr(up), u_dt, _ptr(h), r, float(scale),
+                                               _ptr(dy), g_dt, p(dx), p(dd), p(du), M, N, K, _ptr(ws), nbytes,
+                                               _stream(dev)))
+    else:
+        fn, wp = (lib().lyc_lora_linear_bwd_wt, w_t) if w_t is not None else (lib().lyc_lora_linear_bwd, w)
+        _check(fn(_ptr(x), x_dt, _ptr(wp), w_dt, b_dt, _ptr(down), d_dt, _ptr(up), u_dt, r, float(scale), _ptr(dy),
+                  g_dt, p(dx), p(dd), p(du), M, N, K, _ptr(ws), nbytes, _stream(dev)))
     out = (dx, dd, du)
     return (out, ws) if return_workspace else out
 

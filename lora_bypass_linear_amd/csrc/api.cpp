@@ -490,7 +490,8 @@ int merge(const Merge& G, const void* w, const void* down, const void* up, doubl
 }
 
 // ---- LoRA-bypass backward ------------------------------------------------------
-enum { BWD_DX = 1, BWD_DDOWN = 2, BWD_DUP = 4, BWD_WT = 8 };   // BWD_WT: the caller passes W_c^T
+// BWD_WT: the caller passes W_c^T; BWD_H: the caller passes the forward's h_r
+enum { BWD_DX = 1, BWD_DDOWN = 2, BWD_DUP = 4, BWD_WT = 8, BWD_H = 16 };
 
 struct Bwd {
     Problem P;       // the forward's problem; c_dt resolved over (x, W, b, down, up, dy)
@@ -513,7 +514,7 @@ struct BwdLayout {
 
 int check_bwd(Bwd& B) {
     Problem& P = B.P;
-    if (P.M < 0 || P.N < 0 || P.K < 0 || P.rank < 0 || B.want < 0 || B.want > 15) return LYC_ERR_INVALID_ARG;
+    if (P.M < 0 || P.N < 0 || P.K < 0 || P.rank < 0 || B.want < 0 || B.want > 31) return LYC_ERR_INVALID_ARG;
     if (!valid_dt(P.x_dt) || !valid_dt(P.w_dt) || !valid_dt(P.d_dt) || !valid_dt(P.u_dt) || !valid_dt(B.dy_dt))
         return LYC_ERR_INVALID_ARG;
     if (P.b_dt != 0 && !valid_dt(P.b_dt)) return LYC_ERR_INVALID_ARG;
@@ -543,7 +544,7 @@ BwdLayout bwd_layout(const Bwd& B) {
     const size_t ce = esize(P.c_dt);
     const bool split = P.c_dt != LYC_F32;
     const bool dx = B.want & BWD_DX, dd = (B.want & BWD_DDOWN) && P.rank > 0, du = (B.want & BWD_DUP) && P.rank > 0;
-    L.need_h = du;                          // h_r feeds dUp only
+    L.need_h = du && !(B.want & BWD_H);     // h_r feeds dUp only (recomputed unless the caller passes it)
     L.need_gh = P.rank > 0 && (dx || dd);   // gh_r feeds dx's fold and dDown
     const size_t G1 = (size_t)1 << 30;
     L.tr_tok = split && (size_t)P.M * (size_t)P.K * 2 < G1 && (size_t)P.M * (size_t)P.N * 2 < G1;
@@ -604,7 +605,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 int backward(const Bwd& B, const void* x, const void* w, const void* down, const void* up, double scale,
              const void* dy, void* dx, void* d_down, void* d_up, void* ws, size_t ws_bytes, void* stream,
-             const void* w_t = nullptr) {
+             const void* w_t = nullptr, const void* h_r = nullptr) {
     const Problem& P = B.P;
     if (!(scale == scale) || scale > 3.4e38 || scale < -3.4e38) return LYC_ERR_INVALID_ARG;
     const bool wdx = B.want & BWD_DX, wdd = B.want & BWD_DDOWN, wdu = B.want & BWD_DUP;
@@ -620,6 +621,11 @@ int backward(const Bwd& B, const void* x, const void* w, const void* down, const
         return LYC_ERR_INVALID_ARG;
     // a caller-kept W_c^T [K][N] is read in place by the dx GEMM: 16-byte rows
     if (wt_given && use_w && !aligned(w_t, 16)) return LYC_ERR_UNSUPPORTED;
+    // the forward's h_r [M][r_pad], read in place by dUp (16-byte rows)
+    const bool h_given = B.want & BWD_H;
+    const bool use_h = h_given && wdu && r > 0 && M > 0 && N > 0;
+    if (use_h && h_r == nullptr) return LYC_ERR_INVALID_ARG;
+    if (use_h && !aligned(h_r, 16)) return LYC_ERR_UNSUPPORTED;
     const size_t ndx = (size_t)(M * K) * esize(P.x_dt), ndd = (size_t)(r * K) * esize(P.d_dt),
                  ndu = (size_t)(N * r) * esize(P.u_dt);
     if ((wdx && ndx > 0 && dx == nullptr) || (wdd && ndd > 0 && d_down == nullptr) || (wdu && ndu > 0 && d_up == nullptr))
@@ -635,14 +641,15 @@ int backward(const Bwd& B, const void* x, const void* w, const void* down, const
         (wdu && d_up && !aligned(d_up, esize(P.u_dt))))
         return LYC_ERR_UNSUPPORTED;
     // the gradients overlap neither the inputs nor each other
-    const void* ins[6] = {x, w, down, up, dy, wt_given ? w_t : nullptr};
-    const size_t nin[6] = {(size_t)(M * K) * esize(P.x_dt), (size_t)(N * K) * esize(P.w_dt),
+    const void* ins[7] = {x, w, down, up, dy, wt_given ? w_t : nullptr, use_h ? h_r : nullptr};
+    const size_t nin[7] = {(size_t)(M * K) * esize(P.x_dt), (size_t)(N * K) * esize(P.w_dt),
                            (size_t)(r * K) * esize(P.d_dt), (size_t)(N * r) * esize(P.u_dt),
-                           (size_t)(M * N) * esize(B.dy_dt), (size_t)(K * N) * esize(P.c_dt)};
+                           (size_t)(M * N) * esize(B.dy_dt), (size_t)(K * N) * esize(P.c_dt),
+                           (size_t)(M * P.r_pad) * esize(P.c_dt)};
     void* outs[3] = {wdx ? dx : nullptr, wdd ? d_down : nullptr, wdu ? d_up : nullptr};
     const size_t nout[3] = {ndx, ndd, ndu};
     for (int i = 0; i < 3; ++i) {
-        for (int j = 0; j < 6; ++j)
+        for (int j = 0; j < 7; ++j)
             if (overlaps(outs[i], nout[i], ins[j], nin[j])) return LYC_ERR_INVALID_ARG;
         for (int j = i + 1; j < 3; ++j)
             if (overlaps(outs[i], nout[i], outs[j], nout[j])) return LYC_ERR_INVALID_ARG;
@@ -805,9 +812,10 @@ int backward(const Bwd& B, const void* x, const void* w, const void* down, const
     // dUp = round_up(scale * dy_c^T . h_r), over the tokens
     if (wdu && r > 0 && N > 0) {
         lyc::GemmParams g{};
+        const void* hs = use_h ? h_r : (const void*)(W + L.h);
         if (L.tr_tok) {
             // h_r [M][r_pad] and dy_c [M][N] as stored: tokens are their rows
-            g.a = W + L.h;
+            g.a = hs;
             g.b = M > 0 ? ga : W;
             g.ta = g.tb = 1;
             g.lda_t = P.r_pad;
@@ -816,7 +824,7 @@ int backward(const Bwd& B, const void* x, const void* w, const void* down, const
         } else {
             if (M > 0) {
                 if (!transpose(dy, B.dy_dt, M, N, W + L.dyt, B.M8, N)) return LYC_ERR_HIP;
-                if (!transpose(W + L.h, P.c_dt, M, P.r_pad, W + L.ht, B.M8, P.r_pad)) return LYC_ERR_HIP;
+                if (!transpose(hs, P.c_dt, M, P.r_pad, W + L.ht, B.M8, P.r_pad)) return LYC_ERR_HIP;
             }
             g.a = W + L.ht;
             g.b = W + L.dyt;
@@ -1005,6 +1013,20 @@ int lyc_lora_linear_bwd_wt(const void* x, int x_dt, const void* w_t, int w_dt, i
     const int st = check_bwd(B);
     if (st != LYC_OK) return st;
     return backward(B, x, nullptr, down, up, scale, dy, dx, d_down, d_up, workspace, workspace_bytes, stream, w_t);
+}
+
+int lyc_lora_linear_bwd_saved(const void* x, int x_dt, const void* w, const void* w_t, int w_dt, int bias_dt,
+                              const void* down, int down_dt, const void* up, int up_dt, const void* h_r,
+                              int64_t rank, double scale, const void* dy, int dy_dt, void* dx, void* d_down,
+                              void* d_up, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    if (w != nullptr && w_t != nullptr) return LYC_ERR_INVALID_ARG;
+    const int want = (dx ? BWD_DX : 0) | (d_down ? BWD_DDOWN : 0) | (d_up ? BWD_DUP : 0) | (w_t ? BWD_WT : 0) |
+                     (h_r ? BWD_H : 0);
+    Bwd B{Problem{true, M, N, K, rank, x_dt, w_dt, bias_dt, down_dt, up_dt, 0, 0, 0}, dy_dt, want, 0};
+    const int st = check_bwd(B);
+    if (st != LYC_OK) return st;
+    return backward(B, x, w, down, up, scale, dy, dx, d_down, d_up, workspace, workspace_bytes, stream, w_t, h_r);
 }
 
 int lyc_lora_linear_bwd_workspace_layout(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt,

@@ -394,4 +394,29 @@ def test_backward_with_caller_kept_wt_checks():
     kept = L.lora_bwd_workspace_size(300, 64, 128, 17, 1, 1, 0, 1, 1, 1, 7 | 8)
     assert full - kept == 128 * 64 * 2                           # exactly the W^T [K][N] copy
     with pytest.raises(L.LycError):
-        L.lora_bwd_workspace_size(300, 64, 128, 17, 1, 1, 0, 1, 1, 1, 16)
+        L.lora_bwd_workspace_size(300, 64, 128, 17, 1, 1, 0, 1, 1, 1, 32)
+
+
+def test_backward_with_saved_h_checks():
+    """lyc_lora_linear_bwd_saved: at most one of W and W^T, h_r read in place
+    (16-byte aligned, no overlap with an output), and no h pass's regions in
+    the workspace (want bit 16)."""
+    lib = L.lib()
+    a = dict(x=P, x_dt=1, w=P, wt=None, w_dt=1, b_dt=0, d=P, d_dt=1, u=P, u_dt=1, h=V(1 << 29), r=4, scale=1.0,
+             g=P, g_dt=1, dx=V(1 << 30), dd=V(1 << 31), du=V(1 << 32), M=16, N=64, K=64, ws=None, nws=0, s=None)
+    call = lambda **kw: _refused(lib.lyc_lora_linear_bwd_saved(*[{**a, **kw}[k] for k in (
+        "x", "x_dt", "w", "wt", "w_dt", "b_dt", "d", "d_dt", "u", "u_dt", "h", "r")],
+        ctypes.c_double({**a, **kw}["scale"]),
+        *[{**a, **kw}[k] for k in ("g", "g_dt", "dx", "dd", "du", "M", "N", "K", "ws", "nws", "s")]))
+    assert call(wt=V(1 << 28)) == L.ERR_INVALID_ARG               # W and W^T both given
+    assert call(h=V((1 << 29) + 8)) == L.ERR_UNSUPPORTED           # h_r rows are read 16 bytes at a time
+    assert call(h=V(1 << 32)) == L.ERR_INVALID_ARG                 # overlaps dUp
+    assert call(g_dt=2) == L.ERR_MIXED_HALF
+    assert call() == L.ERR_WORKSPACE
+    assert call(h=None) == L.ERR_WORKSPACE                         # no h_r: recomputed, as lyc_lora_linear_bwd
+    full = L.lora_bwd_workspace_size(300, 64, 128, 17, 1, 1, 0, 1, 1, 1, 7)
+    saved = L.lora_bwd_workspace_size(300, 64, 128, 17, 1, 1, 0, 1, 1, 1, 7 | 16)
+    # the h pass's regions (rank 17 pads to 32): down_c and its hi/lo split
+    # [32][128], the norms, the guard count, h_r [300][32]
+    assert full - saved == 3 * 32 * 128 * 2 + 512 + 256 + 300 * 32 * 2
+    assert L.lora_bwd_workspace_layout(300, 64, 128, 17, 1, 1, 0, 1, 1, 1, 7 | 16)[0] == 2 ** 64 - 1

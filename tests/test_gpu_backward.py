@@ -218,3 +218,37 @@ def test_caller_kept_wt_gives_identical_gradients(name, dims):
     for a, b in zip(ref, got):
         assert torch.equal(a, b)
     assert torch.equal(ref[0], dxo[0]) and dxo[1] is None and dxo[2] is None
+
+
+@pytest.mark.parametrize("name,dims", [
+    ("lora_f16_4096x3072x3072_r16", dict(M=300, N=264, K=136)),
+    ("lora_bf16_16384x8192x8192_r128", dict(M=1030, N=520, K=264)),     # bias; dUp on 128x128 tiles, K split
+    ("lora_bf16x_f32w_8192x4096x4096_r64", dict(M=200, N=136, K=72)),
+    ("sweep_xf32_wf32_2048x1280x5120_r32", dict(M=130, N=96, K=64)),     # fp32 compute: dUp reads a copy of h_r^T
+])
+def test_saved_h_gives_identical_gradients(name, dims):
+    """lyc_lora_linear_bwd_saved with the h_r the forward left in its
+    workspace (no h pass), alone and with a caller-kept W_c^T, against
+    lyc_lora_linear_bwd: every gradient bit for bit."""
+    wl = BASE[name].resized(**dims)
+    inp = _inputs(wl)
+    dev = torch.device("cuda:0")
+    d = {k: v.to(dev) for k, v in inp.items()}
+    b_dtype = inp["b"].dtype if "b" in inp else None
+    codes = [WL.dtype_code(inp[k]) for k in ("x", "w", "down", "up", "dy")] + \
+            ([WL.dtype_code(inp["b"])] if "b" in inp else [])
+    c_dt, _ = L.resolve_dtypes(codes)
+    say("backward saved h", wl.name, dims)
+    _, ws = L.lora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, d.get("b"), return_workspace=True)
+    h = L.lora_saved_h(ws, d["x"], d["w"], d["down"], d["up"], d.get("b"))
+    ref = L.lora_linear_backward(d["x"], d["w"], d["down"], d["up"], wl.scale, d["dy"], bias_dtype=b_dtype)
+    got = L.lora_linear_backward(d["x"], d["w"], d["down"], d["up"], wl.scale, d["dy"], bias_dtype=b_dtype, h=h)
+    w_t = d["w"].to(_T[c_dt]).t().contiguous()
+    both = L.lora_linear_backward(d["x"], d["w"], d["down"], d["up"], wl.scale, d["dy"], bias_dtype=b_dtype, h=h,
+                                  w_t=w_t)
+    duo = L.lora_linear_backward(d["x"], d["w"], d["down"], d["up"], wl.scale, d["dy"], bias_dtype=b_dtype, h=h,
+                                 want_dx=False, want_ddown=False)
+    torch.cuda.synchronize()
+    for a, b, c in zip(ref, got, both):
+        assert torch.equal(a, b) and torch.equal(a, c)
+    assert duo[0] is None and duo[1] is None and torch.equal(ref[2], duo[2])
