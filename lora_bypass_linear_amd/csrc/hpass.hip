@@ -94,6 +94,20 @@ __device__ __forceinline__ uint32_t absmax_bits(i32x4 v) {
     return m;
 }
 
+// maximum of v over the lanes l, l^16, l^32 and l^48 (the four lanes that
+// hold one row of a 64-k block in the MFMA fragment layout), with gfx950's row
+// swaps: v_permlane16_swap of v with itself hands lane l of rows 0 and 1 (2
+// and 3) the values of rows 0 and 1 (2 and 3) at its position, and
+// v_permlane32_swap does the same for the two halves.  Plain vector
+// instructions: a shuffle through the LDS crossbar (ds_bpermute) took a round
+// trip each, twice at the start of every k block.
+__device__ __forceinline__ uint32_t max_row_lanes(uint32_t v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    const uint32_t m = a[0] > a[1] ? a[0] : a[1];
+    const auto b = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+    return b[0] > b[1] ? b[0] : b[1];
+}
+
 // grid exponent g = floor(log2 m) - 8 of a positive 16-bit magnitude m (bits)
 template <class CT>
 __device__ __forceinline__ int grid_exp(uint32_t m) {
@@ -502,10 +516,7 @@ void xr_kernel(XrParams p) {
             uint32_t mb = absmax_bits(xr[0]);
             const uint32_t m1 = absmax_bits(xr[1]);
             mb = mb > m1 ? mb : m1;
-            const uint32_t o1 = (uint32_t)__shfl_xor((int)mb, 16);
-            mb = mb > o1 ? mb : o1;
-            const uint32_t o2 = (uint32_t)__shfl_xor((int)mb, 32);
-            mb = mb > o2 ? mb : o2;
+            mb = max_row_lanes(mb);
             const int g = grid_exp<CT>(mb);
             wide |= (g > 100);
             i32x4 xh[2], xlo[2];
@@ -535,10 +546,7 @@ void xr_kernel(XrParams p) {
                     uint32_t mbb = absmax_bits(br[0]);
                     const uint32_t n1 = absmax_bits(br[1]);
                     mbb = mbb > n1 ? mbb : n1;
-                    const uint32_t q1 = (uint32_t)__shfl_xor((int)mbb, 16);
-                    mbb = mbb > q1 ? mbb : q1;
-                    const uint32_t q2 = (uint32_t)__shfl_xor((int)mbb, 32);
-                    mbb = mbb > q2 ? mbb : q2;
+                    mbb = max_row_lanes(mbb);
                     const int gb = grid_exp<CT>(mbb);
                     wideb[SB ? jb : 0] |= (gb > 100);
                     if (CT::dt == DT_F16 && __all(gb <= 4)) {
