@@ -511,6 +511,18 @@ void xr_kernel(XrParams p) {
         i32x4 xr[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) xr[s] = *(const i32x4*)(xs + lds_off(my_row, s * 4 + (lane >> 4)));
+        // (b split beforehand) the first column block's b fragments {hi, lo} x
+        // {k half 0, 1}, read with x's so that their latency overlaps the split
+        i32x4 bq[4];
+        const int kc0 = lane >> 4, rl = c0 + (lane & 15);
+        if constexpr (SPLIT && !SB) {
+            const char* tl0 = th + TILE;
+            bq[0] = *(const i32x4*)(th + lds_off(rl, kc0));
+            bq[1] = *(const i32x4*)(tl0 + lds_off(rl, kc0));
+            bq[2] = *(const i32x4*)(th + lds_off(rl, 4 + kc0));
+            bq[3] = *(const i32x4*)(tl0 + lds_off(rl, 4 + kc0));
+            __builtin_amdgcn_sched_barrier(0);   // (issued here, not after the split)
+        }
         if (SPLIT) {
             // block maximum of |x| for the lane's row (4 lane groups x 16 values)
             uint32_t mb = absmax_bits(xr[0]);
@@ -575,15 +587,9 @@ void xr_kernel(XrParams p) {
                     }
                 }
             } else {
-                // b fragments {hi, lo} x {k half 0, 1} of a column block, read one
-                // column block ahead; each column block's MFMAs share their
+                // b fragments of a column block, read one column block ahead
+                // (the first with x's); each column block's MFMAs share their
                 // stretch of the schedule with the fold of the previous one's sums
-                i32x4 bq[4];
-                const int kc0 = lane >> 4, rl = c0 + (lane & 15);
-                bq[0] = *(const i32x4*)(th + lds_off(rl, kc0));
-                bq[1] = *(const i32x4*)(tl + lds_off(rl, kc0));
-                bq[2] = *(const i32x4*)(th + lds_off(rl, 4 + kc0));
-                bq[3] = *(const i32x4*)(tl + lds_off(rl, 4 + kc0));
 #pragma unroll
                 for (int jb = 0; jb < JB; ++jb) {
                     // the previous column block's sums enter this stretch here (an
