@@ -498,8 +498,16 @@ __global__ __launch_bounds__(512, 1) void merge_stream_kernel(MergeParams p, int
         if constexpr (NORM) {
             // the 4 lanes of each row (a fixed butterfly); the waves' sums are
             // added in order after the next barrier
-            ss += __shfl_xor(ss, 16, 64);
-            ss += __shfl_xor(ss, 32, 64);
+            // (gfx950 row swaps: the same sums as shuffles with lanes l^16 and
+            // l^32, which went through the LDS crossbar; the pair of results is
+            // reinterpreted whole, as a bit_cast of one element of a vector
+            // folds to element 0)
+            const uint32_t u = __builtin_bit_cast(uint32_t, ss);
+            const f32x2_t a = __builtin_bit_cast(f32x2_t, __builtin_amdgcn_permlane16_swap(u, u, false, false));
+            ss = a[0] + a[1];
+            const uint32_t w = __builtin_bit_cast(uint32_t, ss);
+            const f32x2_t b = __builtin_bit_cast(f32x2_t, __builtin_amdgcn_permlane32_swap(w, w, false, false));
+            ss = b[0] + b[1];
             if (lane < 16) red[(i & 1) * (8 * ST_N) + wave * ST_N + row] = ss;
         } else {
             lds_barrier();   // the tile's merged values are all in LDS
