@@ -131,6 +131,9 @@ def main():
                 f2.update(acc2)
                 if not args.no_eager:
                     f2["eager_baseline"] = _eager(d2, w2, c2, rows2, res2, args.steps)
+            if w2.w_dt == WL.F32 and c2 != WL.F32:
+                # fp32 master weights: the same forward with their bf16 copy kept
+                f2["with_kept_compute_copy"] = _kept_copy_bench(dev, w2, in2, args.steps, args.warmup)
             out["large_configs"][name] = f2
             del y2, d2, in2
             torch.cuda.empty_cache()
@@ -152,6 +155,39 @@ def main():
         out["backward"] = _backward(dev, wl, inputs, args.backward_steps, 10, not args.no_cpu_baseline,
                                     not args.no_eager)
     print(json.dumps(out))
+
+
+def _kept_copy_bench(dev, wl, inputs, steps, warmup):
+    """The forward of an fp32-weight workload with W's compute-dtype copy kept
+    by the caller (made once, not cast per call): wall time per step over K
+    steps after W warm-up steps, and each kernel kind's device time."""
+    import torch
+
+    import lora_bypass_linear_amd as L
+
+    d = {k: v.to(dev) for k, v in inputs.items()}
+    dts = [L.dtype_code(d[k]) for k in ("x", "w", "down", "up")] + ([L.dtype_code(d["b"])] if "b" in d else [])
+    c_dt, o_dt = L.resolve_dtypes(dts)
+    w_c = d["w"].to(L.torch_dtype(c_dt)).contiguous()
+    y, ws = L.lora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, d.get("b"), return_workspace=True, w_c=w_c)
+    step = lambda: L.lora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, d.get("b"), out=y, workspace=ws,
+                                 w_c=w_c)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    L.profile_begin(8 * steps)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    prof = L.profile_end()
+    return {"ms_per_step": round(ms, 5), "tflops": round(wl.flops / (ms * 1e-3) / 1e12, 2),
+            "kernels": {k: {"launches": n, "avg_us": round(t * 1e3 / max(n, 1), 3)} for k, (n, t) in prof.items()
+                        if n}}
 
 
 def _forward_bench(dev, wl, inputs, steps, warmup):

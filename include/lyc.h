@@ -132,6 +132,27 @@ int lyc_lora_linear_fwd(const void* x, int x_dt, const void* w, int w_dt, const 
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The same forward with W's compute-dtype copy kept by the caller
+ * ("Mixed-Precision Kernels" explainer, "The Three-Tier Storage Pattern": the
+ * fp32 master weights and their 16-bit working copy are both carried; with W
+ * frozen, as in LoRA training, the copy is made once instead of per call).
+ *   w_c:  [N][K], W rounded to nearest even to the compute dtype (for an fp32 W
+ *         under a 16-bit policy; otherwise W itself), 16-byte aligned; it must
+ *         not overlap y (LYC_ERR_INVALID_ARG).
+ *   w_dt: W's own (master) dtype: it enters the dtype policy as in
+ *         lyc_lora_linear_fwd, so y's dtype is unchanged.
+ * The workspace size comes from lyc_lora_linear_wc_workspace_size (no W copy);
+ * lyc_lora_workspace_layout gives the same offsets for both forwards.  Given
+ * w_c = round_c(W), results are identical to lyc_lora_linear_fwd's.
+ */
+int lyc_lora_linear_wc_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt,
+                                      int bias_dt, int down_dt, int up_dt, size_t* bytes);
+int lyc_lora_linear_fwd_wc(const void* x, int x_dt, const void* w_c, int w_dt, const void* bias, int bias_dt,
+                           const void* down, int down_dt, const void* up, int up_dt, int64_t rank, double scale,
+                           void* y, int y_dt, int64_t M, int64_t N, int64_t K, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
  * The LoRA-bypass forward for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc).  Same arguments, checks, kernels and results as

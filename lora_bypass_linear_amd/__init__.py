@@ -77,6 +77,8 @@ def lib():
                                           ctypes.c_double, c_vp, c_int, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64,
                                           c_vp, c_sz, c_vp]
         L.lyc_lora_linear_bwd_wt.argtypes = list(L.lyc_lora_linear_bwd.argtypes)
+        L.lyc_lora_linear_wc_workspace_size.argtypes = list(L.lyc_lora_linear_workspace_size.argtypes)
+        L.lyc_lora_linear_fwd_wc.argtypes = list(L.lyc_lora_linear_fwd.argtypes)
         L.lyc_lora_linear_bwd_saved.argtypes = [c_vp, c_int, c_vp, c_vp, c_int, c_int, c_vp, c_int, c_vp, c_int, c_vp,
                                                 c_i64, ctypes.c_double, c_vp, c_int, c_vp, c_vp, c_vp, c_i64, c_i64,
                                                 c_i64, c_vp, c_sz, c_vp]
@@ -116,7 +118,7 @@ def lib():
                    L.lyc_lora_workspace_layout,
                    L.lyc_linear_workspace_layout, L.lyc_lora_merge_workspace_size, L.lyc_lora_merge_fwd,
                    L.lyc_lora_linear_bwd_workspace_size, L.lyc_lora_linear_bwd, L.lyc_lora_linear_bwd_wt,
-                   L.lyc_lora_linear_bwd_saved,
+                   L.lyc_lora_linear_bwd_saved, L.lyc_lora_linear_wc_workspace_size, L.lyc_lora_linear_fwd_wc,
                    L.lyc_lora_linear_bwd_workspace_layout,
                    L.lyc_gemm_plan, L.lyc_device_rates, L.lyc_measure_device_rates, L.lyc_lora_linear_tune, L.lyc_tuning_key, L.lyc_tuning_lookup, L.lyc_tuning_save,
                    L.lyc_tuning_load, L.lyc_tuning_clear, L.lyc_tuning_count, L.lyc_dora_norms_workspace_size,
@@ -400,25 +402,35 @@ def linear(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None
 
 def lora_linear(x: torch.Tensor, w: torch.Tensor, down: torch.Tensor, up: torch.Tensor, scale: float,
                 bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                workspace: Optional[torch.Tensor] = None, return_workspace: bool = False):
+                workspace: Optional[torch.Tensor] = None, return_workspace: bool = False,
+                w_c: Optional[torch.Tensor] = None):
     """y = round_out(x.W^T + scale * round_c(x.down^T).up^T + b) on the GPU.
 
     x [M,K], w [N,K], down [r,K], up [N,r], bias [N] (optional).  With
     ``return_workspace`` the workspace tensor is returned too (h_r and the
-    guard counter live in it; see ``lora_workspace_layout``)."""
+    guard counter live in it; see ``lora_workspace_layout``).  ``w_c``:
+    optional caller-kept copy of W rounded to the compute dtype [N,K] (an
+    fp32 W's working copy, made once while W is frozen): the GEMM reads it
+    and W is not cast per call; w still sets the dtype policy."""
     M, N, K, r = _lora_shapes(x, w, down, up, bias, out)
     x_dt, w_dt, d_dt, u_dt = dtype_code(x), dtype_code(w), dtype_code(down), dtype_code(up)
     b_dt = dtype_code(bias) if bias is not None else 0
-    _, o_dt = resolve_dtypes([x_dt, w_dt] + ([b_dt] if b_dt else []) + [d_dt, u_dt])
+    c_dt, o_dt = resolve_dtypes([x_dt, w_dt] + ([b_dt] if b_dt else []) + [d_dt, u_dt])
     _out_dtype(out, o_dt)
-    dev = _need_device(x, w, down, up, bias, out, workspace)
+    _shape(w_c, (N, K), "w_c")
+    if w_c is not None and w_c.dtype != _TORCH[c_dt]:
+        raise ValueError(f"w_c has dtype {w_c.dtype}, the compute dtype is {_TORCH[c_dt]}")
+    dev = _need_device(x, w, down, up, bias, out, workspace, w_c)
     if out is None:
         out = torch.empty((M, N), dtype=_TORCH[o_dt], device=dev)
-    ws = _workspace(lora_workspace_size(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt), dev, workspace)
+    size = lib().lyc_lora_linear_wc_workspace_size if w_c is not None else lib().lyc_lora_linear_workspace_size
+    n = ctypes.c_size_t(0)
+    _check(size(M, N, K, r, x_dt, w_dt, b_dt, d_dt, u_dt, ctypes.byref(n)))
+    ws = _workspace(n.value, dev, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().lyc_lora_linear_fwd(_ptr(x), x_dt, _ptr(w), w_dt, _ptr(bias), b_dt, _ptr(down), d_dt, _ptr(up),
-                                     u_dt, r, float(scale), _ptr(out), dtype_code(out), M, N, K, _ptr(ws), nbytes,
-                                     _stream(dev)))
+    fn, wp = (lib().lyc_lora_linear_fwd_wc, w_c) if w_c is not None else (lib().lyc_lora_linear_fwd, w)
+    _check(fn(_ptr(x), x_dt, _ptr(wp), w_dt, _ptr(bias), b_dt, _ptr(down), d_dt, _ptr(up), u_dt, r, float(scale),
+              _ptr(out), dtype_code(out), M, N, K, _ptr(ws), nbytes, _stream(dev)))
     return (out, ws) if return_workspace else out
 
 

@@ -54,6 +54,7 @@ struct Problem {
     int c_dt, o_dt;
     int r_pad;
     int m_dt = 0;    // DoRA: the magnitude vector's dtype (a policy operand); 0 otherwise
+    bool w_kept = false;   // the caller passes W already rounded to the compute dtype
 };
 
 // Shape and dtype checks shared by the size queries and the forward calls.
@@ -113,9 +114,8 @@ Layout layout(const Problem& P) {
     size_t off = 0;
     const size_t ce = esize(P.c_dt);
     L.cast_x = P.x_dt == LYC_F32 && P.c_dt != LYC_F32;
-    L.cast_w = P.w_dt == LYC_F32 && P.c_dt != LYC_F32;
+    L.cast_w = P.w_dt == LYC_F32 && P.c_dt != LYC_F32 && !P.w_kept;
     if (L.cast_x) { L.xc = off; off = align256(off + (size_t)(P.M * P.K) * 2); }
-    if (L.cast_w) { L.wc = off; off = align256(off + (size_t)(P.N * P.K) * 2); }
     const bool split = P.c_dt != LYC_F32;   // hi/lo split of the second contraction operand
     if (P.r_pad > 0) {
         L.dc = off; off = align256(off + (size_t)P.r_pad * (size_t)P.K * ce);
@@ -157,11 +157,21 @@ Layout layout(const Problem& P) {
         L.flag_slots = L.w_split_pass ? 1 : wgs;
         L.flagged = off; off = align256(off + (size_t)L.flag_slots * sizeof(unsigned));
     }
+    // the compute-dtype copy of an fp32 W last: a caller that keeps that copy
+    // (lyc_lora_linear_fwd_wc) needs the same workspace without it, every
+    // other region at the same offset
+    if (L.cast_w) { L.wc = off; off = align256(off + (size_t)(P.N * P.K) * 2); }
     L.total = off;
     return L;
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
 
 // ---- optional per-kernel timing (lyc_profile_begin / lyc_profile_end) -------
 struct ProfSlot {
@@ -195,6 +205,7 @@ hipError_t timed(int kind, hipStream_t s, F fn) {
 int forward(const Problem& P, const void* x, const void* w, const void* bias, const void* down, const void* up,
             double scale, void* y, int y_dt, void* ws, size_t ws_bytes, void* stream,
             const lyc::TuneChoice* force = nullptr, const void* mag = nullptr, const float* norms = nullptr) {
+    // (P.w_kept: w is W_c, W already rounded to the compute dtype)
     if (y_dt != P.o_dt) return LYC_ERR_DTYPE_MISMATCH;
     if ((bias == nullptr) != (P.b_dt == 0)) return LYC_ERR_INVALID_ARG;
     if (P.M == 0 || P.N == 0) return LYC_OK;
@@ -203,6 +214,8 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
         if (x == nullptr || w == nullptr) return LYC_ERR_INVALID_ARG;
         if (!aligned(x, 16) || !aligned(w, 16)) return LYC_ERR_UNSUPPORTED;
     }
+    if (P.w_kept && P.K > 0 && overlaps(y, (size_t)(P.M * P.N) * esize(y_dt), w, (size_t)(P.N * P.K) * esize(P.c_dt)))
+        return LYC_ERR_INVALID_ARG;
     if (P.rank > 0) {
         if (up == nullptr || (P.K > 0 && down == nullptr)) return LYC_ERR_INVALID_ARG;
         if (!aligned(up, esize(P.u_dt)) || !aligned(down, esize(P.d_dt))) return LYC_ERR_UNSUPPORTED;
@@ -595,12 +608,6 @@ BwdLayout bwd_layout(const Bwd& B) {
     if (part > 0) take(L.partial, part);
     L.total = off;
     return L;
-}
-
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-    if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
-    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
-    return a0 < b0 + nb && b0 < a0 + na;
 }
 
 int backward(const Bwd& B, const void* x, const void* w, const void* down, const void* up, double scale,
@@ -1188,6 +1195,29 @@ int lyc_lora_linear_fwd(const void* x, int x_dt, const void* w, int w_dt, const 
     if (!valid_dt(y_dt)) return LYC_ERR_INVALID_ARG;
     if (!(scale == scale) || scale > 3.4e38 || scale < -3.4e38) return LYC_ERR_INVALID_ARG;
     return forward(P, x, w, bias, down, up, scale, y, y_dt, workspace, workspace_bytes, stream);
+}
+
+int lyc_lora_linear_wc_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt,
+                                      int bias_dt, int down_dt, int up_dt, size_t* bytes) {
+    Problem P{true, M, N, K, rank, x_dt, w_dt, bias_dt, down_dt, up_dt, 0, 0, 0};
+    P.w_kept = true;
+    const int st = check_problem(P);
+    if (st != LYC_OK) return st;
+    if (bytes) *bytes = layout(P).total;
+    return LYC_OK;
+}
+
+int lyc_lora_linear_fwd_wc(const void* x, int x_dt, const void* w_c, int w_dt, const void* bias, int bias_dt,
+                           const void* down, int down_dt, const void* up, int up_dt, int64_t rank, double scale,
+                           void* y, int y_dt, int64_t M, int64_t N, int64_t K, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    Problem P{true, M, N, K, rank, x_dt, w_dt, bias_dt, down_dt, up_dt, 0, 0, 0};
+    P.w_kept = true;
+    const int st = check_problem(P);
+    if (st != LYC_OK) return st;
+    if (!valid_dt(y_dt)) return LYC_ERR_INVALID_ARG;
+    if (!(scale == scale) || scale > 3.4e38 || scale < -3.4e38) return LYC_ERR_INVALID_ARG;
+    return forward(P, x, w_c, bias, down, up, scale, y, y_dt, workspace, workspace_bytes, stream);
 }
 
 int lyc_lora_workspace_layout(int64_t M, int64_t N, int64_t K, int64_t rank, int x_dt, int w_dt, int bias_dt,

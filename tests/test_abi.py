@@ -420,3 +420,27 @@ def test_backward_with_saved_h_checks():
     # [32][128], the norms, the guard count, h_r [300][32]
     assert full - saved == 3 * 32 * 128 * 2 + 512 + 256 + 300 * 32 * 2
     assert L.lora_bwd_workspace_layout(300, 64, 128, 17, 1, 1, 0, 1, 1, 1, 7 | 16)[0] == 2 ** 64 - 1
+
+
+def test_forward_with_kept_compute_copy_checks():
+    """lyc_lora_linear_fwd_wc: W_c read in place (16-byte aligned, no overlap
+    with y), W's dtype still in the policy, and a workspace without the W copy
+    with every other region at the same offset."""
+    lib = L.lib()
+    a = dict(x=P, x_dt=2, w=V(1 << 28), w_dt=3, b=None, b_dt=0, d=P, d_dt=3, u=P, u_dt=3, r=4, scale=1.0,
+             y=V(1 << 30), y_dt=3, M=4, N=64, K=64, ws=None, nws=0, s=None)
+    call = lambda **kw: _refused(lib.lyc_lora_linear_fwd_wc(*[{**a, **kw}[k] for k in (
+        "x", "x_dt", "w", "w_dt", "b", "b_dt", "d", "d_dt", "u", "u_dt", "r")], ctypes.c_double({**a, **kw}["scale"]),
+        *[{**a, **kw}[k] for k in ("y", "y_dt", "M", "N", "K", "ws", "nws", "s")]))
+    assert call(w=None) == L.ERR_INVALID_ARG
+    assert call(w=V((1 << 28) + 8)) == L.ERR_UNSUPPORTED          # W_c rows are read 16 bytes at a time
+    assert call(w=V((1 << 30) + 512)) == L.ERR_INVALID_ARG         # overlaps y
+    assert call(y_dt=2) == L.ERR_DTYPE_MISMATCH                    # fp32 W keeps y fp32
+    assert call() == L.ERR_WORKSPACE
+    # fp32 W under bf16 compute: exactly the bf16 copy of W less; bf16 W: no difference
+    full = L.lora_workspace_size(300, 520, 264, 64, 2, 3, 0, 3, 3)
+    n = ctypes.c_size_t(0)
+    assert lib.lyc_lora_linear_wc_workspace_size(300, 520, 264, 64, 2, 3, 0, 3, 3, ctypes.byref(n)) == L.OK
+    assert full - n.value == -(-520 * 264 * 2 // 256) * 256   # (regions are 256-byte aligned)
+    assert lib.lyc_lora_linear_wc_workspace_size(300, 520, 264, 64, 2, 2, 0, 2, 2, ctypes.byref(n)) == L.OK
+    assert n.value == L.lora_workspace_size(300, 520, 264, 64, 2, 2, 0, 2, 2)

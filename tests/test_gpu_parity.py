@@ -360,3 +360,31 @@ def test_full_size_sampled_rows(name):
         return
     rows = sample_rows(wl.M, 24 if wl.M * wl.N * wl.K > 1e11 else 48, seed=wl.seed)
     _check(wl, rows=rows)
+
+
+@pytest.mark.parametrize("name,dims", [
+    ("lora_bf16x_f32w_8192x4096x4096_r64", dict(M=257, N=200, K=264)),   # fp32 W, factors and y under bf16
+    ("sweep_xf32_wf32_2048x1280x5120_r32", dict(M=130, N=96, K=136)),    # fp32 x still cast per call
+    ("lora_bf16_16384x8192x8192_r128", dict(M=270, N=300, K=520)),       # 16-bit W: W_c is W itself
+    ("lora_bf16x_f32w_8192x4096x4096_r64", dict()),                      # full size
+])
+def test_kept_compute_copy_gives_identical_output(name, dims):
+    """lyc_lora_linear_fwd_wc (W rounded to the compute dtype once, by the
+    caller) against lyc_lora_linear_fwd: y and h_r bit for bit."""
+    wl = BASE[name].resized(**dims) if dims else BASE[name]
+    inputs = WL.generate(wl)
+    dev = torch.device("cuda:0")
+    d = {k: v.to(dev) for k, v in inputs.items()}
+    codes = [WL.dtype_code(inputs[k]) for k in ("x", "w", "down", "up")] + \
+            ([WL.dtype_code(inputs["b"])] if "b" in inputs else [])
+    c_dt, _ = L.resolve_dtypes(codes)
+    w_c = d["w"].to(L.torch_dtype(c_dt)).contiguous()
+    say("kept compute copy", wl.name, dims)
+    y0, ws0 = L.lora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, d.get("b"), return_workspace=True)
+    y1, ws1 = L.lora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, d.get("b"), return_workspace=True,
+                            w_c=w_c)
+    h0 = L.lora_saved_h(ws0, d["x"], d["w"], d["down"], d["up"], d.get("b"))
+    h1 = L.lora_saved_h(ws1, d["x"], d["w"], d["down"], d["up"], d.get("b"))
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    assert torch.equal(h0, h1)
