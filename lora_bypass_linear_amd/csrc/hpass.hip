@@ -65,6 +65,17 @@ namespace lyc {
 constexpr double STEP_ERR = 18.0;
 constexpr double GUARD_CROSS = 2.0 * STEP_ERR + 2.0;
 
+// The guard's per-column factors: with n = |x_m| and n_lo = |x_lo,m| (each
+// inflated by `slack`), the bound is E = n P + n_lo Q + D, where
+//   P = slack |scale| (GUARD_CROSS 2^-24 |b_lo,j| + 2^-37 |b_j|),
+//   Q = slack |scale| GUARD_CROSS 2^-24 (|b_j| + |b_lo,j|),
+// D the underflow term.  |b_lo,j| = inf (a block of b that could not be
+// split) makes P infinite, which flags the column.
+__device__ __forceinline__ double2 guard_pq(double b, double bl, double as) {
+    const double slack = 1.0 + 0x1p-20;
+    return double2{slack * as * (0x1p-24 * GUARD_CROSS * bl + 0x1p-37 * b), slack * as * 0x1p-24 * GUARD_CROSS * (b + bl)};
+}
+
 template <class CT>
 __device__ __forceinline__ float unpack_lo(uint32_t u) {
     return CT::dt == DT_F16 ? f16_to_f32((uint16_t)u) : bf16_to_f32((uint16_t)u);
@@ -236,22 +247,18 @@ __device__ __forceinline__ float pick4(f32x4 v, int e) {
 template <class CT, int JB, bool SB>
 __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB][4], double xm2, double xl2, bool wide,
                                             int64_t wg_m0, int64_t j0, int my_row, int c0, int cols_wg, int lane,
-                                            unsigned* lcount, uint32_t* list, const float (&bsq)[SB ? JB : 1][2]) {
+                                            unsigned* lcount, uint32_t* list, const float (&bsq)[SB ? JB : 1][2],
+                                            const double2* lbn, const float* lbias) {
     constexpr bool SPLIT = CT::dt != DT_F32;
     const int64_t m = wg_m0 + my_row;
     const bool row_ok = m < p.M;
-    // the bias (plain affine form) is loaded before the first store: the
-    // compiler cannot move a load past a store that may alias it.  The affine
-    // form runs with JB = 4; wider instances never read it.
+    // the bias (plain affine form), from the workgroup's copy in LDS (zero
+    // past the last column).  The affine form runs with JB = 4; wider
+    // instances never read it.
     float bias[JB][4] = {};
     if (JB <= 4 && p.mode != XR_H && p.bias != nullptr) {
-        int64_t idx[JB * 4];
-        float v[JB * 4];
 #pragma unroll
-        for (int i = 0; i < JB * 4; ++i) idx[i] = j0 + c0 + (i >> 2) * 16 + 4 * (lane >> 4) + (i & 3);
-        load_n_as_f32<JB * 4>(p.bias, p.bias_dt, idx, j0 + cols_wg, v);
-#pragma unroll
-        for (int i = 0; i < JB * 4; ++i) bias[i >> 2][i & 3] = v[i];
+        for (int i = 0; i < JB * 4; ++i) bias[i >> 2][i & 3] = lbias[c0 + (i >> 2) * 16 + 4 * (lane >> 4) + (i & 3)];
     }
 
     // guard: flag the elements whose error interval straddles a rounding
@@ -269,8 +276,6 @@ __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB]
         // h = scale * C: the bound scales with |scale| (the fp64 product's own
         // rounding, 2^-53 relative, lies far inside the 2^-37 slack term)
         const double as = __builtin_fabs(p.scale);
-        const double A = 0x1p-24 * GUARD_CROSS * xn2 * slack * as, B = 0x1p-24 * GUARD_CROSS * xln * slack * as;
-        const double C = 0x1p-37 * xn2 * slack * as;
         // fp32 products and partial sums below 2^-126 (bf16 operands far
         // below 1) may be flushed, or rounded on fp32's subnormal grid, and a
         // grid product below 2^-149 makes the hi.hi sums inexact: either way
@@ -280,7 +285,7 @@ __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB]
         const double D = (double)p.K * 0x1p-120 * as;
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) {
-            double2 b2[4];   // {|b|, |b_lo|} of the lane's 4 columns of this block
+            double2 pq[4];   // the guard's factors {P, Q} of the lane's 4 columns of this block
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int jl = c0 + jb * 16 + 4 * (lane >> 4) + e;
@@ -289,25 +294,27 @@ __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB]
                     // sit in lane c (shuffled whatever the lane's own columns)
                     const int c = 4 * (lane >> 4) + e;
                     const float vb = __shfl(bsq[SB ? jb : 0][0], c), vl = __shfl(bsq[SB ? jb : 0][1], c);
-                    const double slack = 1.0 + 0x1p-20;
-                    const double2 v{__builtin_sqrt((double)vb) * slack,
-                                    vl < __builtin_inff() ? __builtin_sqrt((double)vl) * slack : __builtin_inf()};
-                    b2[e] = (guard && jl < cols_wg) ? v : double2{0.0, 0.0};
+                    const double2 v = guard_pq(__builtin_sqrt((double)vb) * slack,
+                                               vl < __builtin_inff() ? __builtin_sqrt((double)vl) * slack
+                                                                     : __builtin_inf(),
+                                               as);
+                    pq[e] = (guard && jl < cols_wg) ? v : double2{0.0, 0.0};
                 } else {
-                    b2[e] = (guard && jl < cols_wg) ? p.bnorm[j0 + jl] : double2{0.0, 0.0};
+                    pq[e] = (guard && jl < cols_wg) ? lbn[jl] : double2{0.0, 0.0};
                 }
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int jl = c0 + jb * 16 + 4 * (lane >> 4) + e;
                 const double h = acc[jb][e] * p.scale;
-                const double E = A * b2[e].y + B * (b2[e].x + b2[e].y) + C * b2[e].x + D;
+                const double E = __builtin_fma(xn2, pq[e].x, __builtin_fma(xln, pq[e].y, D));
                 const uint16_t lo = round16<CT>(h - E);
                 r16[jb][e] = lo;
-                const bool bwide = !(b2[e].y < 1e300);   // a block of b could not be split
-                const bool flag =
-                    guard && row_ok && jl < cols_wg && (wide || bwide || lo != round16<CT>(h + E));
-                flags |= flag ? (1u << (jb * 4 + e)) : 0u;
+                // (the second conversion stays conditional: computed for every
+                // element up front, the 8-block instance runs out of registers)
+                const bool bwide = !(pq[e].x < 1e300);   // a block of b could not be split
+                const bool flag = (guard & row_ok & (jl < cols_wg)) && (wide || bwide || lo != round16<CT>(h + E));
+                flags |= (uint32_t)flag << (jb * 4 + e);
             }
         }
         // guarded elements go to the workgroup's work list: one LDS atomic per lane
@@ -475,18 +482,24 @@ void xr_kernel(XrParams p) {
         voff[q] = (uint32_t)row * kbytes + kpos[q];
     }
     auto stage_at = [&](int r) { return sd + (r % NS) * ST::BYTES; };
+#define LYC_ISSUE_LOADS(ST_, KB0_, V_)                                                              \
+    _Pragma("unroll") for (int q = 0; q < Q; ++q) {                                                 \
+        const int blk = wave + q * NW;                                                              \
+        const uint32_t v = V_;                                                                      \
+        auto* dst = (__attribute__((address_space(3))) void*)((ST_) + blk * 1024);                  \
+        if (blk >= ST::NBB) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, dst, 16, v, (int)(KB0_), 0, 0); \
+        else if ((blk / (RP / 8)) % NB) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsl, dst, 16, v, (int)(KB0_), 0, 0); \
+        else __builtin_amdgcn_raw_ptr_buffer_load_lds(rsh, dst, 16, v, (int)(KB0_), 0, 0);          \
+    }
+    // (a round that lies wholly inside K takes no per-lane range test)
 #define LYC_ISSUE_ROUND(R)                                                                          \
     do {                                                                                            \
         char* st_ = stage_at(R);                                                                    \
         const uint32_t kb0_ = (uint32_t)((R) * KS) * 128;                                           \
-        const bool full_ = kb0_ + KS * 128 <= kbytes;                                               \
-        _Pragma("unroll") for (int q = 0; q < Q; ++q) {                                             \
-            const int blk = wave + q * NW;                                                          \
-            const uint32_t v = (full_ || kb0_ + kpos[q] < kbytes) ? voff[q] : OOB;                  \
-            auto* dst = (__attribute__((address_space(3))) void*)(st_ + blk * 1024);                \
-            if (blk >= ST::NBB) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, dst, 16, v, (int)kb0_, 0, 0); \
-            else if ((blk / (RP / 8)) % NB) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsl, dst, 16, v, (int)kb0_, 0, 0); \
-            else __builtin_amdgcn_raw_ptr_buffer_load_lds(rsh, dst, 16, v, (int)kb0_, 0, 0);        \
+        if (kb0_ + KS * 128 <= kbytes) {                                                            \
+            LYC_ISSUE_LOADS(st_, kb0_, voff[q])                                                     \
+        } else {                                                                                    \
+            LYC_ISSUE_LOADS(st_, kb0_, kb0_ + kpos[q] < kbytes ? voff[q] : OOB)                     \
         }                                                                                           \
     } while (0)
 
@@ -659,6 +672,7 @@ void xr_kernel(XrParams p) {
         }
     }
 #undef LYC_ISSUE_ROUND
+#undef LYC_ISSUE_LOADS
     if (SPLIT && !SB) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -666,16 +680,34 @@ void xr_kernel(XrParams p) {
             acc[JB - 1][e] += (double)(pc0[e] + pc1[e]);
         }
     }
+    // The epilogue's per-column inputs, one per thread: the guard's factors
+    // from the norms {|b|, |b_lo|} (b split beforehand) and the bias (plain
+    // affine form).
+    // Their loads are issued here and land in LDS with the k groups' partial
+    // sums, so that one memory round trip overlaps the reduction (read in the
+    // epilogue, each lane's 4 JB columns would take JB round trips in turn).
+    static_assert(64 * NW >= RP, "one thread per column");
+    const bool ld_bn = SPLIT && !SB && p.guard && tid < cols_wg;
+    const bool ld_bias = p.mode != XR_H && p.bias != nullptr && tid < RP;
+    double2 bnv = double2{0.0, 0.0};
+    float biasv = 0.f;
+    if (ld_bn) bnv = p.bnorm[j0 + tid];
+    if (ld_bias && tid < cols_wg) biasv = load_as_f32(p.bias, p.bias_dt, j0 + tid);
     __syncthreads();   // every wave is done with the stages (they hold the k-group reduction next)
 
-    // LDS after the main loop: [k-group reduction][count][work list of guarded elements]
+    // LDS after the main loop: [k-group reduction][count][work list of guarded
+    // elements][column guard factors][bias]
     constexpr int W = JB * 4 + 3 + (SB ? JB * 2 : 0);
     constexpr int RED = KS > 1 ? (KS - 1) * CG * RW * 64 * W * 8 : 0;
     constexpr int CAP = RW * 16 * RP;                      // every element of the workgroup
-    static_assert(RED + 16 + CAP * 4 <= NS * ST::BYTES, "reduction buffer and work list");
+    static_assert(RED + 16 + CAP * 4 + RP * 20 <= NS * ST::BYTES, "reduction buffer, work list, column inputs");
     unsigned* lcount = (unsigned*)(sd + RED);
     uint32_t* list = (uint32_t*)(sd + RED + 16);
+    double2* lbn = (double2*)(sd + RED + 16 + CAP * 4);
+    float* lbias = (float*)(sd + RED + 16 + CAP * 4 + RP * 16);
     if (tid == 0) *lcount = 0u;
+    if (ld_bn) lbn[tid] = guard_pq(bnv.x, bnv.y, __builtin_fabs(p.scale));
+    if (ld_bias) lbias[tid] = biasv;
 
     if (SPLIT) {
         // Gram diagonal: row r of the wave sits in lane r + 16 (r >> 2), element
@@ -751,7 +783,7 @@ void xr_kernel(XrParams p) {
                 }
             }
         }
-        xr_epilogue<CT, JB, SB>(p, acc, xm2, xl2, wide, wg_m0, j0, my_row, c0, cols_wg, lane, lcount, list, bsq);
+        xr_epilogue<CT, JB, SB>(p, acc, xm2, xl2, wide, wg_m0, j0, my_row, c0, cols_wg, lane, lcount, list, bsq, lbn, lbias);
     }
     // The guarded elements: every wave takes its share of the list and
     // overwrites the stored output with the value rounded from the fp64 dot
@@ -763,9 +795,9 @@ void xr_kernel(XrParams p) {
         const i32x4* xbase = (const i32x4*)((const char*)p.x + wg_m0 * kbytes);
         const i32x4* bbase = (const i32x4*)((const char*)p.b_full + j0 * kbytes);
         // entries per wave and pass: as many as keep every lane's share of a
-        // row within one batch of B chunks (B = 8 where the accumulators of
-        // 8 column blocks leave fewer registers)
-        constexpr int B = JB >= 8 ? 8 : 16;
+        // row within one batch of B chunks (one memory round trip per pass up
+        // to K = 64 B / G values; the accumulators are dead by now)
+        constexpr int B = 16;
         const int G = nch <= 16 * B ? 4 : (nch <= 32 * B ? 2 : 1);
         const int L = 64 / G, j = lane & (L - 1);
         for (unsigned i0 = (unsigned)(wave * G); i0 < n; i0 += (unsigned)(ST::NW * G)) {
