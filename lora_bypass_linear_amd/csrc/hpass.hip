@@ -242,13 +242,15 @@ __device__ __forceinline__ float pick4(f32x4 v, int e) {
     return __builtin_bit_cast(float, r);
 }
 
-// Epilogue of one wave's accumulators: rounding guard (flagged elements are
-// appended to the workgroup's work list), then h_r or the affine output.
+// Epilogue of one wave's accumulators, for the column blocks in `owned` (a
+// wave-uniform bit mask; the k groups split a workgroup's blocks): rounding
+// guard (flagged elements are appended to the workgroup's work list), then
+// h_r or the affine output.
 template <class CT, int JB, bool SB>
 __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB][4], double xm2, double xl2, bool wide,
                                             int64_t wg_m0, int64_t j0, int my_row, int c0, int cols_wg, int lane,
                                             unsigned* lcount, uint32_t* list, const float (&bsq)[SB ? JB : 1][2],
-                                            const double2* lbn, const float* lbias) {
+                                            const double2* lbn, const float* lbias, uint32_t owned) {
     constexpr bool SPLIT = CT::dt != DT_F32;
     const int64_t m = wg_m0 + my_row;
     const bool row_ok = m < p.M;
@@ -285,6 +287,7 @@ __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB]
         const double D = (double)p.K * 0x1p-120 * as;
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) {
+            if (!((owned >> jb) & 1u)) continue;   // (uniform: another k group's block)
             double2 pq[4];   // the guard's factors {P, Q} of the lane's 4 columns of this block
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -332,6 +335,7 @@ __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB]
             // h_r [M][ld_out] in the compute dtype (all RP columns, padding included)
 #pragma unroll
             for (int jb = 0; jb < JB; ++jb) {
+                if (!((owned >> jb) & 1u)) continue;
                 const int64_t jg = j0 + c0 + jb * 16 + 4 * (lane >> 4);
                 if (CT::dt == DT_F32) {
                     float* hp = (float*)p.out + m * p.ld_out + jg;
@@ -348,6 +352,7 @@ __device__ __forceinline__ void xr_epilogue(const XrParams& p, double (&acc)[JB]
             // rounds to fp32 for an fp32 output, else to the compute dtype (= output)
 #pragma unroll
             for (int jb = 0; jb < JB; ++jb) {
+                if (!((owned >> jb) & 1u)) continue;
                 const int jl0 = c0 + jb * 16 + 4 * (lane >> 4);
                 const int64_t n0 = j0 + jl0;
                 float v[4];
@@ -696,9 +701,15 @@ void xr_kernel(XrParams p) {
     __syncthreads();   // every wave is done with the stages (they hold the k-group reduction next)
 
     // LDS after the main loop: [k-group reduction][count][work list of guarded
-    // elements][column guard factors][bias]
-    constexpr int W = JB * 4 + 3 + (SB ? JB * 2 : 0);
-    constexpr int RED = KS > 1 ? (KS - 1) * CG * RW * 64 * W * 8 : 0;
+    // elements][column guard factors][bias].  The k groups' partial sums meet
+    // column block by column block: block jb belongs to k group jb % KS, and
+    // every wave writes the partial sums of the blocks it does not own (SLOTS
+    // of them) and the statistics of its rows (NST values), so that the
+    // epilogue's work is spread over all k groups.
+    constexpr int SLOTS = JB - JB / KS;
+    constexpr int NST = 3 + (SB ? JB * 2 : 0);
+    constexpr int W = SLOTS * 4 + NST;
+    constexpr int RED = KS > 1 ? KS * CG * RW * 64 * W * 8 : 0;
     constexpr int CAP = RW * 16 * RP;                      // every element of the workgroup
     static_assert(RED + 16 + CAP * 4 + RP * 20 <= NS * ST::BYTES, "reduction buffer, work list, column inputs");
     unsigned* lcount = (unsigned*)(sd + RED);
@@ -739,52 +750,90 @@ void xr_kernel(XrParams p) {
             bsq[jb][1] = wideb[jb] ? __builtin_inff() : (float)((double)dlo * infl + steps * 0x1p-120);
         }
     }
-    // meet the k groups' partial sums in LDS (the B tiles are no longer needed)
+    // meet the k groups' partial sums in LDS (the B tiles are no longer needed):
+    // slot t of wave g holds the t-th block among those g does not own
+    uint32_t owned = 0;
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) owned |= (uint32_t)(jb % KS == kg) << jb;
     if (KS > 1) {
-        double* red = (double*)sd;                 // [KS-1][CG][RW][64 lanes][W]
-        if (kg > 0) {
-            double* dst = red + ((size_t)(((kg - 1) * CG + cg) * RW + rg) * 64 + lane) * W;
+        double* red = (double*)sd;                 // [KS][CG][RW][64 lanes][W]
+        double* dst = red + ((size_t)((kg * CG + cg) * RW + rg) * 64 + lane) * W;
+        int t = 0;
 #pragma unroll
-            for (int jb = 0; jb < JB; ++jb)
+        for (int jb = 0; jb < JB; ++jb) {
+            if ((owned >> jb) & 1u) continue;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) dst[jb * 4 + e] = acc[jb][e];
-            dst[JB * 4] = xm2;
-            dst[JB * 4 + 1] = xl2;
-            dst[JB * 4 + 2] = wide ? 1.0 : 0.0;
+            for (int e = 0; e < 4; ++e) dst[t * 4 + e] = acc[jb][e];
+            ++t;
+        }
+        double* st = dst + SLOTS * 4;
+        st[0] = xm2;
+        st[1] = xl2;
+        st[2] = wide ? 1.0 : 0.0;
+        if constexpr (SB) {
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb) {
+                st[3 + 2 * jb] = bsq[jb][0];
+                st[3 + 2 * jb + 1] = bsq[jb][1];
+            }
+        }
+    }
+    __syncthreads();   // partial sums, the cleared count and the column inputs are visible
+    if (KS > 1 && owned != 0u) {   // (a wave without blocks, where KS > JB, has nothing to sum)
+        // each owned block and the row statistics summed over the k groups in
+        // the order 0, 1, ..., KS-1 (the wave's own part from its registers)
+        const double* red = (const double*)sd;
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) {
+            if (!((owned >> jb) & 1u)) continue;   // (uniform)
+            double t4[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+            for (int g2 = 0; g2 < KS; ++g2) {
+                // block jb's slot in wave g2 (which does not own it): jb less
+                // the blocks below jb that g2 owns
+                const int t = jb - (jb > g2 ? (jb - 1 - g2) / KS + 1 : 0);
+                const double* src = red + ((size_t)((g2 * CG + cg) * RW + rg) * 64 + lane) * W + t * 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t4[e] += g2 == kg ? acc[jb][e] : src[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[jb][e] = t4[e];
+        }
+        double txm = 0.0, txl = 0.0;
+        bool twide = false;
+        float tb[JBS][2];
+#pragma unroll
+        for (int jb = 0; jb < JBS; ++jb) tb[jb][0] = tb[jb][1] = 0.f;
+#pragma unroll
+        for (int g2 = 0; g2 < KS; ++g2) {
+            const bool mine = g2 == kg;
+            const double* st = red + ((size_t)((g2 * CG + cg) * RW + rg) * 64 + lane) * W + SLOTS * 4;
+            txm += mine ? xm2 : st[0];
+            txl += mine ? xl2 : st[1];
+            twide |= mine ? wide : st[2] != 0.0;
             if constexpr (SB) {
+                // (the fp32 sums are rounded up by the epilogue's slack)
 #pragma unroll
                 for (int jb = 0; jb < JB; ++jb) {
-                    dst[JB * 4 + 3 + 2 * jb] = bsq[jb][0];
-                    dst[JB * 4 + 3 + 2 * jb + 1] = bsq[jb][1];
+                    tb[jb][0] = (float)((double)tb[jb][0] + (mine ? bsq[jb][0] : (float)st[3 + 2 * jb]));
+                    tb[jb][1] = (float)((double)tb[jb][1] + (mine ? bsq[jb][1] : (float)st[3 + 2 * jb + 1]));
                 }
             }
         }
-    }
-    __syncthreads();   // partial sums and the cleared count are visible
-    if (kg == 0) {
-        if (KS > 1) {
-            const double* red = (const double*)sd;
-            for (int g2 = 1; g2 < KS; ++g2) {
-                const double* src = red + ((size_t)(((g2 - 1) * CG + cg) * RW + rg) * 64 + lane) * W;
+        xm2 = txm;
+        xl2 = txl;
+        wide = twide;
+        if constexpr (SB) {
 #pragma unroll
-                for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[jb][e] += src[jb * 4 + e];
-                xm2 += src[JB * 4];
-                xl2 += src[JB * 4 + 1];
-                wide |= src[JB * 4 + 2] != 0.0;
-                if constexpr (SB) {
-                    // (the fp32 sums are rounded up by the epilogue's slack)
-#pragma unroll
-                    for (int jb = 0; jb < JB; ++jb) {
-                        bsq[jb][0] = (float)((double)bsq[jb][0] + src[JB * 4 + 3 + 2 * jb]);
-                        bsq[jb][1] = (float)((double)bsq[jb][1] + src[JB * 4 + 3 + 2 * jb + 1]);
-                    }
-                }
+            for (int jb = 0; jb < JB; ++jb) {
+                bsq[jb][0] = tb[jb][0];
+                bsq[jb][1] = tb[jb][1];
             }
         }
-        xr_epilogue<CT, JB, SB>(p, acc, xm2, xl2, wide, wg_m0, j0, my_row, c0, cols_wg, lane, lcount, list, bsq, lbn, lbias);
     }
+    if (owned != 0u)
+        xr_epilogue<CT, JB, SB>(p, acc, xm2, xl2, wide, wg_m0, j0, my_row, c0, cols_wg, lane, lcount, list, bsq, lbn,
+                                lbias, owned);
     // The guarded elements: every wave takes its share of the list and
     // overwrites the stored output with the value rounded from the fp64 dot
     // product.  The barrier's release makes the first stores complete before.

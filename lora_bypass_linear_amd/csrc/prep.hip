@@ -48,92 +48,111 @@ __device__ __forceinline__ void store16(void* dst, int64_t i, float v, int c_dt)
 // is then reported as +inf, which makes the contraction re-evaluate that row's
 // elements in fp64.  With `vec` the source row is read, and the outputs
 // written, 16 bytes at a time (rows start 16-byte aligned and K % 8 == 0).
-__device__ void row_pass(const void* src, int src_dt, int c_dt, int64_t row, int64_t K, bool zero, bool vec,
-                         void* dst, void* dst_hi, void* dst_lo, double2* norm_out) {
+// The stored and compute dtypes and `vec` are template arguments: with them
+// as run-time values every element took the branches of all combinations.
+template <int SRC_DT, int C_DT, bool VEC>
+__device__ __forceinline__ void row_pass_t(const void* src, int64_t row, int64_t K, bool zero, void* dst, void* dst_hi,
+                                           void* dst_lo, double2* norm_out) {
+    constexpr int src_dt = SRC_DT, c_dt = C_DT;
+    constexpr bool vec = VEC;
     __shared__ double red[2][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     double ss = 0.0, ll = 0.0;
     bool wide = false;
-    for (int64_t k0 = 0; k0 < K; k0 += 2048) {
-        const int64_t kt = k0 + 8 * tid;
-        const bool in = kt < K;   // K % 8 == 0: a thread's 8 elements are all in or all out
-        float c[8];
-        if (vec && in && !zero) {
-            if (src_dt == DT_F32) {
-                const f32x4 a = *(const f32x4*)((const float*)src + row * K + kt);
-                const f32x4 b = *(const f32x4*)((const float*)src + row * K + kt + 4);
+    // RB chunks of 2048 values per round: a thread's loads of a round are
+    // issued together (one memory round trip per 8192 values of the row)
+    constexpr int RB = 4;
+    for (int64_t kr = 0; kr < K; kr += 2048 * RB) {
+        float cr[RB][8];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) { c[i] = a[i]; c[i + 4] = b[i]; }
-            } else {
-                const i32x4 v = *(const i32x4*)((const uint16_t*)src + row * K + kt);
-                const i32x4 w = v;
+        for (int rb = 0; rb < RB; ++rb) {
+            const int64_t kt = kr + 2048 * rb + 8 * tid;
+            const bool in = kt < K;   // K % 8 == 0: a thread's 8 elements are all in or all out
+            float* c = cr[rb];
+            if (vec && in && !zero) {
+                if (src_dt == DT_F32) {
+                    const f32x4 a = *(const f32x4*)((const float*)src + row * K + kt);
+                    const f32x4 b = *(const f32x4*)((const float*)src + row * K + kt + 4);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t u = (uint32_t)w[i];
-                    c[2 * i] = src_dt == DT_F16 ? f16_to_f32((uint16_t)u) : bf16_to_f32((uint16_t)u);
-                    c[2 * i + 1] = src_dt == DT_F16 ? f16_to_f32((uint16_t)(u >> 16)) : bf16_to_f32((uint16_t)(u >> 16));
-                }
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) c[i] = (in && !zero) ? load_as_f32(src, src_dt, row * K + kt + i) : 0.f;
-        }
-        // round to the compute dtype (exact when the stored dtype is the compute dtype)
-        uint16_t h16[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            if (c_dt == DT_F16) { h16[i] = f32_to_f16(c[i]); c[i] = f16_to_f32(h16[i]); }
-            else if (c_dt == DT_BF16) { h16[i] = f32_to_bf16(c[i]); c[i] = bf16_to_f32(h16[i]); }
-        }
-        if (dst && in) {
-            if (c_dt == DT_F32) {
-                float* d = (float*)dst + row * K + kt;
-                if (vec) {
-                    *(f32x4*)d = f32x4{c[0], c[1], c[2], c[3]};
-                    *(f32x4*)(d + 4) = f32x4{c[4], c[5], c[6], c[7]};
+                    for (int i = 0; i < 4; ++i) { c[i] = a[i]; c[i + 4] = b[i]; }
                 } else {
+                    const i32x4 v = *(const i32x4*)((const uint16_t*)src + row * K + kt);
+                    const i32x4 w = v;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) d[i] = c[i];
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t u = (uint32_t)w[i];
+                        c[2 * i] = src_dt == DT_F16 ? f16_to_f32((uint16_t)u) : bf16_to_f32((uint16_t)u);
+                        c[2 * i + 1] = src_dt == DT_F16 ? f16_to_f32((uint16_t)(u >> 16)) : bf16_to_f32((uint16_t)(u >> 16));
+                    }
                 }
             } else {
-                *(i32x4*)((uint16_t*)dst + row * K + kt) =
-                    i32x4{(int)(h16[0] | ((uint32_t)h16[1] << 16)), (int)(h16[2] | ((uint32_t)h16[3] << 16)),
-                          (int)(h16[4] | ((uint32_t)h16[5] << 16)), (int)(h16[6] | ((uint32_t)h16[7] << 16))};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) c[i] = (in && !zero) ? load_as_f32(src, src_dt, row * K + kt + i) : 0.f;
             }
         }
-        float mx = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            ss = __builtin_fma((double)c[i], (double)c[i], ss);
-            mx = __builtin_fmaxf(mx, __builtin_fabsf(c[i]));
-        }
-        if (dst_hi) {
-            // maximum over the 64-k block: 8 lanes
-#pragma unroll
-            for (int o = 4; o >= 1; o >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, o));
-            int g = 0;
-            float magic = 0.f;
-            if (mx > 0.f) {
-                g = floor_log2(mx) - 8;
-                wide |= g > 100;
-                magic = __builtin_ldexpf(1.5f, (g > 100 ? 100 : g) + 23);
-            }
-            uint16_t hb[8], lb[8];
+        for (int rb = 0; rb < RB; ++rb) {
+            const int64_t kt = kr + 2048 * rb + 8 * tid;
+            const bool in = kt < K;
+            float* c = cr[rb];
+            if (kr + 2048 * rb >= K) break;   // (uniform over the workgroup)
+            // round to the compute dtype (exact when the stored dtype is the compute dtype)
+            uint16_t h16[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float hi = mx > 0.f ? (c[i] + magic) - magic : 0.f;
-                const float lo = c[i] - hi;
-                hb[i] = c_dt == DT_F16 ? f32_to_f16(hi) : f32_to_bf16(hi);
-                lb[i] = c_dt == DT_F16 ? f32_to_f16(lo) : f32_to_bf16(lo);
-                ll = __builtin_fma((double)lo, (double)lo, ll);
+                if (c_dt == DT_F16) { h16[i] = f32_to_f16(c[i]); c[i] = f16_to_f32(h16[i]); }
+                else if (c_dt == DT_BF16) { h16[i] = f32_to_bf16(c[i]); c[i] = bf16_to_f32(h16[i]); }
             }
-            if (in) {
-                *(i32x4*)((uint16_t*)dst_hi + row * K + kt) =
-                    i32x4{(int)(hb[0] | ((uint32_t)hb[1] << 16)), (int)(hb[2] | ((uint32_t)hb[3] << 16)),
-                          (int)(hb[4] | ((uint32_t)hb[5] << 16)), (int)(hb[6] | ((uint32_t)hb[7] << 16))};
-                *(i32x4*)((uint16_t*)dst_lo + row * K + kt) =
-                    i32x4{(int)(lb[0] | ((uint32_t)lb[1] << 16)), (int)(lb[2] | ((uint32_t)lb[3] << 16)),
-                          (int)(lb[4] | ((uint32_t)lb[5] << 16)), (int)(lb[6] | ((uint32_t)lb[7] << 16))};
+            if (dst && in) {
+                if (c_dt == DT_F32) {
+                    float* d = (float*)dst + row * K + kt;
+                    if (vec) {
+                        *(f32x4*)d = f32x4{c[0], c[1], c[2], c[3]};
+                        *(f32x4*)(d + 4) = f32x4{c[4], c[5], c[6], c[7]};
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) d[i] = c[i];
+                    }
+                } else {
+                    *(i32x4*)((uint16_t*)dst + row * K + kt) =
+                        i32x4{(int)(h16[0] | ((uint32_t)h16[1] << 16)), (int)(h16[2] | ((uint32_t)h16[3] << 16)),
+                              (int)(h16[4] | ((uint32_t)h16[5] << 16)), (int)(h16[6] | ((uint32_t)h16[7] << 16))};
+                }
+            }
+            float mx = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                ss = __builtin_fma((double)c[i], (double)c[i], ss);
+                mx = __builtin_fmaxf(mx, __builtin_fabsf(c[i]));
+            }
+            if (dst_hi) {
+                // maximum over the 64-k block: 8 lanes
+#pragma unroll
+                for (int o = 4; o >= 1; o >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, o));
+                int g = 0;
+                float magic = 0.f;
+                if (mx > 0.f) {
+                    g = floor_log2(mx) - 8;
+                    wide |= g > 100;
+                    magic = __builtin_ldexpf(1.5f, (g > 100 ? 100 : g) + 23);
+                }
+                uint16_t hb[8], lb[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float hi = mx > 0.f ? (c[i] + magic) - magic : 0.f;
+                    const float lo = c[i] - hi;
+                    hb[i] = c_dt == DT_F16 ? f32_to_f16(hi) : f32_to_bf16(hi);
+                    lb[i] = c_dt == DT_F16 ? f32_to_f16(lo) : f32_to_bf16(lo);
+                    ll = __builtin_fma((double)lo, (double)lo, ll);
+                }
+                if (in) {
+                    *(i32x4*)((uint16_t*)dst_hi + row * K + kt) =
+                        i32x4{(int)(hb[0] | ((uint32_t)hb[1] << 16)), (int)(hb[2] | ((uint32_t)hb[3] << 16)),
+                              (int)(hb[4] | ((uint32_t)hb[5] << 16)), (int)(hb[6] | ((uint32_t)hb[7] << 16))};
+                    *(i32x4*)((uint16_t*)dst_lo + row * K + kt) =
+                        i32x4{(int)(lb[0] | ((uint32_t)lb[1] << 16)), (int)(lb[2] | ((uint32_t)lb[3] << 16)),
+                              (int)(lb[4] | ((uint32_t)lb[5] << 16)), (int)(lb[6] | ((uint32_t)lb[7] << 16))};
+                }
             }
         }
     }
@@ -153,6 +172,26 @@ __device__ void row_pass(const void* src, int src_dt, int c_dt, int64_t row, int
         const double l2 = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
         *norm_out = double2{__builtin_sqrt(s2), wide ? __builtin_inf() : __builtin_sqrt(l2)};
     }
+}
+
+__device__ __forceinline__ void row_pass(const void* src, int src_dt, int c_dt, int64_t row, int64_t K, bool zero,
+                                         bool vec, void* dst, void* dst_hi, void* dst_lo, double2* norm_out) {
+#define LYC_ROW_PASS(S, C)                                                                             \
+    if (src_dt == S && c_dt == C) {                                                                    \
+        if (vec) row_pass_t<S, C, true>(src, row, K, zero, dst, dst_hi, dst_lo, norm_out);             \
+        else row_pass_t<S, C, false>(src, row, K, zero, dst, dst_hi, dst_lo, norm_out);                \
+        return;                                                                                        \
+    }
+    LYC_ROW_PASS(DT_F16, DT_F16)
+    LYC_ROW_PASS(DT_BF16, DT_BF16)
+    LYC_ROW_PASS(DT_F32, DT_F16)
+    LYC_ROW_PASS(DT_F32, DT_BF16)
+    LYC_ROW_PASS(DT_F32, DT_F32)
+    LYC_ROW_PASS(DT_F16, DT_F32)
+    LYC_ROW_PASS(DT_BF16, DT_F32)
+    LYC_ROW_PASS(DT_F16, DT_BF16)
+    LYC_ROW_PASS(DT_BF16, DT_F16)
+#undef LYC_ROW_PASS
 }
 
 // fp32 -> 16-bit compute copy of elements [8 i0, 8 i1) and the tail past
