@@ -843,11 +843,11 @@ void xr_kernel(XrParams p) {
         const uint32_t nch = kbytes / 16;
         const i32x4* xbase = (const i32x4*)((const char*)p.x + wg_m0 * kbytes);
         const i32x4* bbase = (const i32x4*)((const char*)p.b_full + j0 * kbytes);
-        // entries per wave and pass: as many as keep every lane's share of a
-        // row within one batch of B chunks (one memory round trip per pass up
-        // to K = 64 B / G values; the accumulators are dead by now)
+        // entries per wave and pass: as many (up to 8) as keep every lane's
+        // share of a row within one batch of B chunks (one memory round trip
+        // per pass; the accumulators are dead by now)
         constexpr int B = 16;
-        const int G = nch <= 16 * B ? 4 : (nch <= 32 * B ? 2 : 1);
+        const int G = nch <= 8 * B ? 8 : (nch <= 16 * B ? 4 : (nch <= 32 * B ? 2 : 1));
         const int L = 64 / G, j = lane & (L - 1);
         for (unsigned i0 = (unsigned)(wave * G); i0 < n; i0 += (unsigned)(ST::NW * G)) {
             const unsigned i = i0 + (unsigned)(lane / L);
