@@ -308,9 +308,13 @@ constexpr int ST_STORES = ST_W / 16 / 512;   // 16-byte stores per thread and ti
 template <int RP> constexpr int st_sub() { return RP <= 64 ? 1 : RP / 64; }
 template <int RP> constexpr int st_bytes() { return ST_W + st_sub<RP>() * ST_N * 128; }
 template <int RP> constexpr int st_ql() { return st_bytes<RP>() / 1024; }   // 1 KiB loads per tile
-// stages: as many as fit beside 1 KiB of sums (6 or 7 tiles in flight), so
-// that enough bytes are on their way from HBM to cover its latency
-template <int RP> constexpr int st_ns() { return (159 * 1024) / st_bytes<RP>() > 8 ? 8 : (159 * 1024) / st_bytes<RP>(); }
+// stages: at most 4 (3 tiles in flight per CU, about 60 KiB).  Filling the
+// LDS (6 or 7 tiles in flight) was slower, and so were two workgroups per CU
+// with 3 stages each: with more requests outstanding the HBM stream loses
+// locality (bf16 8192 x 8192 r128: merge 49.8 -> 47.6 us, row norms 36.5 ->
+// 33.5 us against 7 stages; 59.4 and 35.7 us with two workgroups; a plain
+// read sweep likewise runs fastest with one 16-byte load per lane in flight)
+template <int RP> constexpr int st_ns() { return (159 * 1024) / st_bytes<RP>() > 4 ? 4 : (159 * 1024) / st_bytes<RP>(); }
 template <int RP> constexpr int st_stages() { return st_ns<RP>() * st_bytes<RP>(); }
 // down's band: max(RP, 32) rank rows of 1 KiB, behind the stages where that
 // fits, else over them (it is read once, before the stages fill)
