@@ -35,6 +35,7 @@ HBM_GBS = 8000.0
 # workloads are reported beside it (`large_configs`)
 DEFAULT = "lora_bf16_16384x8192x8192_r128"
 LARGE = ("lora_f16_4096x3072x3072_r16", "lora_bf16x_f32w_8192x4096x4096_r64", "lora_bf16_16384x8192x8192_r128")
+AFFINE = "affine_f16_1024x768x1024"   # the plain affine configuration
 BLOCKS = 15   # timed blocks (median and range), as in the Luminal page's protocol
 
 
@@ -138,6 +139,24 @@ def main():
             del y2, d2, in2
             torch.cuda.empty_cache()
 
+    if lora and not args.no_large_configs:
+        # the plain affine configuration, and the same with W prepared once
+        wa = WL.WORKLOADS[AFFINE]
+        ina = WL.generate(wa)
+        fa = _forward_bench(dev, wa, ina, args.steps, args.warmup)
+        ya = fa.pop("_y")
+        for k in ("_c_dt", "_d", "input_digest", "instrumented_ms_per_step"):
+            fa.pop(k, None)
+        if not args.no_cpu_baseline:
+            acca, _, _, _ = _accuracy(wa, ina, ya, 2.0, timed=False)
+            fa.update(acca)
+        fa["with_prepared_weight"] = _prepared_affine_bench(dev, wa, ina, args.steps, args.warmup)
+        out["affine"] = fa
+        del ya, ina
+        torch.cuda.empty_cache()
+    elif not lora:
+        out["with_prepared_weight"] = _prepared_affine_bench(dev, wl, inputs, args.steps, args.warmup)
+
     # the tile planner's device model, measured on this GPU (its shortlist
     # order in small_m[].tuned follows these rates)
     import lora_bypass_linear_amd as L
@@ -172,6 +191,37 @@ def _kept_copy_bench(dev, wl, inputs, steps, warmup):
     y, ws = L.lora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, d.get("b"), return_workspace=True, w_c=w_c)
     step = lambda: L.lora_linear(d["x"], d["w"], d["down"], d["up"], wl.scale, d.get("b"), out=y, workspace=ws,
                                  w_c=w_c)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    L.profile_begin(8 * steps)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    prof = L.profile_end()
+    return {"ms_per_step": round(ms, 5), "tflops": round(wl.flops / (ms * 1e-3) / 1e12, 2),
+            "kernels": {k: {"launches": n, "avg_us": round(t * 1e3 / max(n, 1), 3)} for k, (n, t) in prof.items()
+                        if n}}
+
+
+def _prepared_affine_bench(dev, wl, inputs, steps, warmup):
+    """The plain affine forward with W prepared once (its split kept in the
+    workspace by the caller): wall time per step over K steps after W warm-up
+    steps, and each kernel kind's device time."""
+    import torch
+
+    import lora_bypass_linear_amd as L
+
+    d = {k: v.to(dev) for k, v in inputs.items()}
+    x, w, b = d["x"], d["w"], d.get("b")
+    ws = L.linear_prepare(w, wl.M, x.dtype, b.dtype if b is not None else None)
+    y = L.linear(x, w, b, workspace=ws, prepared=True)
+    step = lambda: L.linear(x, w, b, out=y, workspace=ws, prepared=True)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()

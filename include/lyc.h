@@ -100,6 +100,30 @@ int lyc_linear_fwd(const void* x, int x_dt, const void* w, int w_dt, const void*
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The plain affine form with W prepared once: weights kept as prepared data
+ * next to their stored values ("Mixed-Precision Kernels" explainer, "The
+ * Three-Tier Storage Pattern").  lyc_linear_prepare writes into the caller's
+ * workspace (lyc_linear_workspace_size bytes for the same M, N, K and
+ * dtypes, 256-byte aligned) what lyc_linear_fwd derives from W on every
+ * call: W's compute-dtype copy when W is fp32 under 16-bit compute, and,
+ * where the contraction takes W split beforehand, W_c's hi/lo split and row
+ * norms.  lyc_linear_fwd_prepared is lyc_linear_fwd without those launches
+ * (one launch where x needs no cast): it reads them from the workspace and W
+ * itself only to re-evaluate guarded elements.  The caller keeps W and that
+ * workspace unchanged between the two calls (lyc_linear_fwd with the same W,
+ * shapes and dtypes also leaves the workspace prepared); a workspace
+ * prepared for another W gives wrong results, which the library cannot
+ * detect.  y is bitwise the result of lyc_linear_fwd.  Calls that share a
+ * workspace are ordered by their stream.  Arguments and errors as
+ * lyc_linear_fwd (lyc_linear_prepare reads no x, bias or y).
+ */
+int lyc_linear_prepare(const void* w, int w_dt, int x_dt, int bias_dt, int64_t M, int64_t N, int64_t K,
+                       void* workspace, size_t workspace_bytes, void* stream);
+int lyc_linear_fwd_prepared(const void* x, int x_dt, const void* w, int w_dt, const void* bias, int bias_dt,
+                            void* y, int y_dt, int64_t M, int64_t N, int64_t K,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Workspace bytes lyc_lora_linear_fwd needs.  It holds the rounded h
  * [M, r_pad] in the compute dtype (r_pad: the rank rounded up to 16 -- under
  * 16-bit compute only --, 32, 64, 128 or 256), compute-dtype copies of down and up (rank padded with zeros), for
@@ -204,8 +228,8 @@ int lyc_lora_workspace_layout(int64_t M, int64_t N, int64_t K, int64_t rank, int
 
 /*
  * Where lyc_linear_fwd keeps its guard counts inside the workspace:
- *   flagged_offset: byte offset of `*flagged_slots` uint32 counts (one, or
- *              one per workgroup where the contraction splits W itself) whose
+ *   flagged_offset: byte offset of `*flagged_slots` uint32 counts (one per
+ *              workgroup of the contraction, each written by it) whose
  *              sum is the number of
  *              projection elements the rounding guard re-evaluated in fp64
  *              during the last call (16-bit compute; all 0 when the output is

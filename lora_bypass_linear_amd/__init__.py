@@ -15,7 +15,7 @@ import torch
 
 __all__ = ["F16", "BF16", "F32", "LycError", "MixedHalfError", "lib", "resolve_dtypes", "linear", "lora_linear",
            "lora_linear_noalloc", "lora_merge", "lora_linear_backward", "dora_norms", "dora_linear", "linear_workspace_size", "lora_workspace_size", "lora_workspace_layout",
-           "linear_workspace_layout", "lora_merge_workspace_size", "lora_bwd_workspace_size",
+           "linear_workspace_layout", "linear_prepare", "lora_merge_workspace_size", "lora_bwd_workspace_size",
            "lora_bwd_workspace_layout", "gemm_tile", "gemm_plan", "lora_linear_tune", "tuning_save",
            "tuning_load", "tuning_clear", "tuning_count", "tuning_key", "tuning_lookup", "tuning_cache_path", "profile_begin", "profile_end",
            "dtype_code", "torch_dtype"]
@@ -57,6 +57,9 @@ def lib():
         L.lyc_linear_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_int, c_int, c_int, ctypes.POINTER(c_sz)]
         L.lyc_linear_fwd.argtypes = [c_vp, c_int, c_vp, c_int, c_vp, c_int, c_vp, c_int, c_i64, c_i64, c_i64,
                                      c_vp, c_sz, c_vp]
+        L.lyc_linear_fwd_prepared.argtypes = [c_vp, c_int, c_vp, c_int, c_vp, c_int, c_vp, c_int, c_i64, c_i64,
+                                              c_i64, c_vp, c_sz, c_vp]
+        L.lyc_linear_prepare.argtypes = [c_vp, c_int, c_int, c_int, c_i64, c_i64, c_i64, c_vp, c_sz, c_vp]
         L.lyc_lora_linear_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_i64, c_int, c_int, c_int, c_int, c_int,
                                                      ctypes.POINTER(c_sz)]
         L.lyc_lora_linear_fwd.argtypes = [c_vp, c_int, c_vp, c_int, c_vp, c_int, c_vp, c_int, c_vp, c_int, c_i64,
@@ -113,7 +116,8 @@ def lib():
         L.lyc_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_int)]
         L.lyc_status_str.argtypes = [c_int]
         L.lyc_status_str.restype = ctypes.c_char_p
-        for fn in (L.lyc_resolve_dtypes, L.lyc_linear_workspace_size, L.lyc_linear_fwd,
+        for fn in (L.lyc_resolve_dtypes, L.lyc_linear_workspace_size, L.lyc_linear_fwd, L.lyc_linear_fwd_prepared,
+                   L.lyc_linear_prepare,
                    L.lyc_lora_linear_workspace_size, L.lyc_lora_linear_fwd, L.lyc_lora_linear_fwd_noalloc,
                    L.lyc_lora_workspace_layout,
                    L.lyc_linear_workspace_layout, L.lyc_lora_merge_workspace_size, L.lyc_lora_merge_fwd,
@@ -379,8 +383,13 @@ def _workspace(nbytes: int, dev, workspace: Optional[torch.Tensor]) -> Optional[
 
 
 def linear(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None,
-           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """y = round_out(round_out(x.W^T) + b) on the GPU (plain affine contract)."""
+           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+           prepared: bool = False) -> torch.Tensor:
+    """y = round_out(round_out(x.W^T) + b) on the GPU (plain affine contract).
+
+    ``prepared``: ``workspace`` already holds what the call derives from W
+    (``linear_prepare``, or an earlier call with the same W, shapes and
+    dtypes), and the call skips those launches."""
     M, K = _dims(x, 2, "x")
     N, _ = _dims(w, 2, "w")
     _shape(w, (N, K), "w")
@@ -393,11 +402,31 @@ def linear(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None
     dev = _need_device(x, w, bias, out, workspace)
     if out is None:
         out = torch.empty((M, N), dtype=_TORCH[o_dt], device=dev)
+    if prepared and workspace is None:
+        raise ValueError("prepared: pass the prepared workspace")
     ws = _workspace(linear_workspace_size(M, N, K, x_dt, w_dt, b_dt), dev, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().lyc_linear_fwd(_ptr(x), x_dt, _ptr(w), w_dt, _ptr(bias), b_dt, _ptr(out), dtype_code(out),
-                                M, N, K, _ptr(ws), nbytes, _stream(dev)))
+    fn = lib().lyc_linear_fwd_prepared if prepared else lib().lyc_linear_fwd
+    _check(fn(_ptr(x), x_dt, _ptr(w), w_dt, _ptr(bias), b_dt, _ptr(out), dtype_code(out),
+              M, N, K, _ptr(ws), nbytes, _stream(dev)))
     return out
+
+
+def linear_prepare(w: torch.Tensor, M: int, x_dtype: torch.dtype, bias_dtype: Optional[torch.dtype] = None,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Prepare W [N,K] for ``linear(..., prepared=True)`` calls with M token
+    rows of dtype ``x_dtype`` (and a bias of ``bias_dtype``): writes W's
+    compute-dtype copy (fp32 W) and split into the workspace, which is returned
+    (allocated when not given)."""
+    N, K = _dims(w, 2, "w")
+    x_dt, w_dt = _CODE[x_dtype], dtype_code(w)
+    b_dt = _CODE[bias_dtype] if bias_dtype is not None else 0
+    dev = _need_device(w, workspace)
+    nb = linear_workspace_size(M, N, K, x_dt, w_dt, b_dt)
+    ws = workspace if workspace is not None else torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    nbytes = ws.numel() * ws.element_size()
+    _check(lib().lyc_linear_prepare(_ptr(w), w_dt, x_dt, b_dt, M, N, K, _ptr(ws), nbytes, _stream(dev)))
+    return ws
 
 
 def lora_linear(x: torch.Tensor, w: torch.Tensor, down: torch.Tensor, up: torch.Tensor, scale: float,

@@ -55,6 +55,10 @@ struct Problem {
     int r_pad;
     int m_dt = 0;    // DoRA: the magnitude vector's dtype (a policy operand); 0 otherwise
     bool w_kept = false;   // the caller passes W already rounded to the compute dtype
+    // plain affine form: the workspace already holds W's compute-dtype copy
+    // (fp32 W) and its split and row norms, from lyc_linear_prepare or an
+    // earlier forward with the same W, shapes and dtypes
+    bool w_prepared = false;
 };
 
 // Shape and dtype checks shared by the size queries and the forward calls.
@@ -88,8 +92,7 @@ int check_problem(Problem& P) {
 struct Layout {
     size_t xc = 0, wc = 0, dc = 0, dh = 0, dl = 0, uc = 0, h = 0, dnorm = 0, wh = 0, wl = 0, wnorm = 0, flagged = 0,
            partial = 0, gain = 0, total = 0;
-    // plain affine form: guard counts (one, or one per workgroup where the
-    // contraction splits W itself: w_split_pass false)
+    // plain affine form: guard counts, one per workgroup of the contraction
     int64_t flag_slots = 0;
     bool w_split_pass = false;
     int ksplit = 1, ks_max = 1;
@@ -154,7 +157,7 @@ Layout layout(const Problem& P) {
             L.wl = off; off = align256(off + (size_t)P.N * (size_t)P.K * ce);
             L.wnorm = off; off = align256(off + (size_t)P.N * 2 * sizeof(double));
         }
-        L.flag_slots = L.w_split_pass ? 1 : wgs;
+        L.flag_slots = L.w_split_pass ? lyc::xr_affine_split_pass_workgroups(P.M, P.N) : wgs;
         L.flagged = off; off = align256(off + (size_t)L.flag_slots * sizeof(unsigned));
     }
     // the compute-dtype copy of an fp32 W last: a caller that keeps that copy
@@ -241,17 +244,18 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
                 return lyc::launch_cast((const float*)x, W + L.xc, P.M * P.K, P.c_dt, s);
             }) != hipSuccess)
             return LYC_ERR_HIP;
-        if (cw && timed(LYC_KERNEL_CAST, s, [&] {
+        if (cw && !P.w_prepared && timed(LYC_KERNEL_CAST, s, [&] {
                 return lyc::launch_cast((const float*)w, W + L.wc, P.N * P.K, P.c_dt, s);
             }) != hipSuccess)
             return LYC_ERR_HIP;
         // plain affine: exact-rounding contraction with the round-then-add-bias
-        // epilogue; W's split and row norms from the row-norm pass (which also
-        // clears the counter) or inside the contraction
+        // epilogue; W's split and row norms from the row-norm pass (skipped
+        // when the workspace already holds them) or inside the contraction;
+        // one guard count per workgroup, nothing to clear
         const bool guard = P.c_dt != LYC_F32 && y_dt != LYC_F32;
-        if (L.w_split_pass && timed(LYC_KERNEL_PREP, s, [&] {
+        if (L.w_split_pass && !P.w_prepared && timed(LYC_KERNEL_PREP, s, [&] {
                 return lyc::launch_rownorm(wa, P.c_dt, P.N, P.K, W + L.wh, W + L.wl, (double2*)(W + L.wnorm),
-                                           (unsigned*)(W + L.flagged), s);
+                                           nullptr, s);
             }) != hipSuccess)
             return LYC_ERR_HIP;
         lyc::XrParams xp{};
@@ -266,6 +270,7 @@ int forward(const Problem& P, const void* x, const void* w, const void* bias, co
         xp.guard = guard ? 1 : 0;
         xp.flagged = L.flag_slots > 0 ? (unsigned*)(W + L.flagged) : nullptr;
         xp.flag_slots = L.flag_slots;
+        xp.flag_per_wg = 1;
         xp.mode = lyc::XR_AFFINE;
         xp.out = y;
         xp.ld_out = P.N;
@@ -1173,6 +1178,45 @@ int lyc_linear_fwd(const void* x, int x_dt, const void* w, int w_dt, const void*
     const int st = check_problem(P);
     if (st != LYC_OK) return st;
     if (!valid_dt(y_dt)) return LYC_ERR_INVALID_ARG;
+    return forward(P, x, w, bias, nullptr, nullptr, 1.0, y, y_dt, workspace, workspace_bytes, stream);
+}
+
+int lyc_linear_prepare(const void* w, int w_dt, int x_dt, int bias_dt, int64_t M, int64_t N, int64_t K,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    Problem P{false, M, N, K, 0, x_dt, w_dt, bias_dt, 0, 0, 0, 0, 0};
+    const int st = check_problem(P);
+    if (st != LYC_OK) return st;
+    if (P.M == 0 || P.N == 0 || P.K == 0) return LYC_OK;
+    if (w == nullptr) return LYC_ERR_INVALID_ARG;
+    if (!aligned(w, 16)) return LYC_ERR_UNSUPPORTED;
+    const Layout L = layout(P);
+    if (L.total > 0 && (workspace == nullptr || workspace_bytes < L.total || !aligned(workspace, 256)))
+        return LYC_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    char* W = (char*)workspace;
+    (void)hipGetLastError();
+    const void* wa = w;
+    if (L.cast_w) {
+        wa = W + L.wc;
+        if (timed(LYC_KERNEL_CAST, s, [&] { return lyc::launch_cast((const float*)w, W + L.wc, P.N * P.K, P.c_dt, s); }) !=
+            hipSuccess)
+            return LYC_ERR_HIP;
+    }
+    if (L.w_split_pass && timed(LYC_KERNEL_PREP, s, [&] {
+            return lyc::launch_rownorm(wa, P.c_dt, P.N, P.K, W + L.wh, W + L.wl, (double2*)(W + L.wnorm), nullptr, s);
+        }) != hipSuccess)
+        return LYC_ERR_HIP;
+    return LYC_OK;
+}
+
+int lyc_linear_fwd_prepared(const void* x, int x_dt, const void* w, int w_dt, const void* bias, int bias_dt, void* y,
+                            int y_dt, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    Problem P{false, M, N, K, 0, x_dt, w_dt, bias_dt, 0, 0, 0, 0, 0};
+    const int st = check_problem(P);
+    if (st != LYC_OK) return st;
+    if (!valid_dt(y_dt)) return LYC_ERR_INVALID_ARG;
+    P.w_prepared = true;
     return forward(P, x, w, bias, nullptr, nullptr, 1.0, y, y_dt, workspace, workspace_bytes, stream);
 }
 

@@ -867,12 +867,12 @@ void xr_kernel(XrParams p) {
                 }
             }
         }
-        if constexpr (SB) {
+        if (SB || p.flag_per_wg) {
             if (tid == 0) p.flagged[blockIdx.y * gridDim.x + blockIdx.x] = n;
         } else {
             if (tid == 0 && n) atomicAdd(p.flagged, n);
         }
-    } else if (SB && tid == 0) {
+    } else if ((SB || p.flag_per_wg) && tid == 0) {
         p.flagged[blockIdx.y * gridDim.x + blockIdx.x] = 0u;   // no guard: nothing re-evaluated
     }
 }
@@ -882,7 +882,7 @@ static hipError_t run_xr(const XrParams& p, hipStream_t s) {
     constexpr int RP = JB * 16 * CG;
     const dim3 grid((unsigned)((p.M + RW * 16 - 1) / (RW * 16)), (unsigned)((p.Nc + RP - 1) / RP));
     // per-workgroup guard counts: the caller's slots must cover the grid
-    if (SB && (int64_t)grid.x * grid.y > p.flag_slots) return hipErrorInvalidValue;
+    if ((SB || p.flag_per_wg) && (int64_t)grid.x * grid.y > p.flag_slots) return hipErrorInvalidValue;
     hipLaunchKernelGGL((xr_kernel<CT, JB, KS, CG, RW, SB>), grid, dim3(64 * RW * KS * CG), 0, s, p);
     return hipGetLastError();
 }
@@ -930,6 +930,9 @@ int64_t xr_affine_workgroups(int64_t M, int64_t N) {
     if (t64 >= 256) return 0;
     return xr_split_b_wgs(M, N);
 }
+
+// the 64 x 64 tiles of run_xr<CT, 4, 2, 1, 4> (W split beforehand)
+int64_t xr_affine_split_pass_workgroups(int64_t M, int64_t N) { return ((M + 63) / 64) * ((N + 63) / 64); }
 
 // h at rank 16 with down already in the compute dtype: the same 16-column
 // launch with down split in the kernel, so that no preparation pass runs

@@ -99,10 +99,12 @@ struct XrParams {
     int64_t M, Nc, K;
     int guard;              // 1: apply the rounding guard (16-bit rounding target)
     // count of re-evaluated elements: h pass, one counter (zeroed beforehand);
-    // plain affine form under 16-bit compute, one per workgroup (flag_slots
-    // of them, each written by its workgroup; their sum is the count)
+    // with flag_per_wg (and where the kernel splits b itself), one per
+    // workgroup (flag_slots of them, each written by its workgroup with a
+    // plain store, nothing cleared beforehand; their sum is the count)
     unsigned* flagged;
     int64_t flag_slots = 0;
+    int flag_per_wg = 0;
     int mode;               // XR_H or XR_AFFINE
     void* out;              // h [M][ld_out] (compute dtype) or y [M][ld_out] (out_dt)
     int64_t ld_out;
@@ -171,6 +173,9 @@ hipError_t launch_xr(int c_dt, const XrParams& p, hipStream_t s);
 // workgroups of the plain affine form's launch under 16-bit compute (its
 // guard-count slots)
 int64_t xr_affine_workgroups(int64_t M, int64_t N);
+// workgroups of the plain affine contraction when W is split beforehand (its
+// guard-count slots)
+int64_t xr_affine_split_pass_workgroups(int64_t M, int64_t N);
 // workgroups of the h pass that splits b in the kernel (XrParams::split_b;
 // its guard-count slots); 0 where that form does not apply (Nc != 16)
 int64_t xr_h_split_b_workgroups(int64_t M, int64_t Nc);

@@ -150,7 +150,8 @@ def test_workspace_sizes():
     # affine: one guard count per workgroup of the contraction (+ a bf16 copy of an fp32 W)
     fo, ns = L.linear_workspace_layout(64, 64, 64, 1, 1)
     assert ns >= 1 and L.linear_workspace_size(64, 64, 64, 1, 1) >= fo + 4 * ns
-    assert L.linear_workspace_layout(1024, 1024, 768, 1, 1)[1] == 1           # 64 x 64 tiles: W split beforehand
+    assert L.linear_workspace_layout(1024, 1024, 768, 1, 1)[1] == 256         # 64 x 64 tiles: W split beforehand
+    assert L.linear_workspace_layout(1000, 1100, 768, 1, 1)[1] == 16 * 18     # (ragged: tiles over M and N)
     assert L.linear_workspace_size(1024, 1024, 768, 1, 1) >= 2 * 1024 * 768 * 2
     assert L.linear_workspace_layout(16, 1024, 768, 1, 1)[1] == 64            # 16 x 16 workgroups, 8 k groups
     assert L.linear_workspace_layout(256, 512, 768, 1, 1)[1] == 8 * 32        # 32-row workgroups, 2 k groups
@@ -444,3 +445,30 @@ def test_forward_with_kept_compute_copy_checks():
     assert full - n.value == -(-520 * 264 * 2 // 256) * 256   # (regions are 256-byte aligned)
     assert lib.lyc_lora_linear_wc_workspace_size(300, 520, 264, 64, 2, 2, 0, 2, 2, ctypes.byref(n)) == L.OK
     assert n.value == L.lora_workspace_size(300, 520, 264, 64, 2, 2, 0, 2, 2)
+
+
+def test_prepared_affine_checks():
+    """lyc_linear_prepare / lyc_linear_fwd_prepared: the arguments and errors of
+    lyc_linear_fwd (prepare reads only W), and nothing done for empty shapes."""
+    lib = L.lib()
+    ws_need = L.linear_workspace_size(1024, 1024, 768, 1, 1, 1)
+    assert ws_need > 0
+    prep = lambda ok=False, **kw: _refused(lib.lyc_linear_prepare(
+        *[{**dict(w=V(1 << 28), w_dt=1, x_dt=1, b_dt=1, M=1024, N=1024, K=768, ws=None, nws=0, s=None), **kw}[k]
+          for k in ("w", "w_dt", "x_dt", "b_dt", "M", "N", "K", "ws", "nws", "s")]), ok)
+    assert prep(w=None) == L.ERR_INVALID_ARG
+    assert prep(w=V((1 << 28) + 8)) == L.ERR_UNSUPPORTED
+    assert prep() == L.ERR_WORKSPACE
+    assert prep(ws=V(1 << 29), nws=ws_need - 1) == L.ERR_WORKSPACE
+    assert prep(ws=V((1 << 29) + 16), nws=ws_need) == L.ERR_WORKSPACE   # not 256-byte aligned
+    assert prep(x_dt=1, w_dt=2) == L.ERR_MIXED_HALF
+    assert prep(True, M=0) == L.OK and prep(True, K=0) == L.OK
+    fwd = lambda **kw: _refused(lib.lyc_linear_fwd_prepared(*[{**dict(x=V(1 << 27), x_dt=1, w=V(1 << 28), w_dt=1,
+                                                                        b=V(1 << 26), b_dt=1, y=V(1 << 30), y_dt=1,
+                                                                        M=1024, N=1024, K=768, ws=None, nws=0,
+                                                                        s=None), **kw}[k]
+                                                             for k in ("x", "x_dt", "w", "w_dt", "b", "b_dt", "y",
+                                                                       "y_dt", "M", "N", "K", "ws", "nws", "s")]))
+    assert fwd(w=None) == L.ERR_INVALID_ARG
+    assert fwd(y_dt=3) == L.ERR_DTYPE_MISMATCH
+    assert fwd() == L.ERR_WORKSPACE

@@ -362,6 +362,36 @@ def test_full_size_sampled_rows(name):
     _check(wl, rows=rows)
 
 
+@pytest.mark.parametrize("dims", [
+    dict(),                                    # W split beforehand: 256 tiles of 64 x 64
+    dict(M=1000, N=1100, K=520),               # ragged tiles
+    dict(M=16),                                # W split inside the one contraction: nothing prepared
+    dict(M=1000, N=1100, K=520, w_dt=WL.F32),  # fp32 W: its fp16 copy prepared too (fp32 y: no guard)
+])
+def test_prepared_weight_gives_identical_output(dims):
+    """lyc_linear_prepare once, then lyc_linear_fwd_prepared (two calls, a
+    second x) against lyc_linear_fwd: y bit for bit and the same guard counts."""
+    wl = BASE["affine_f16_1024x768x1024"].resized(**dims)
+    inputs = WL.generate(wl)
+    x2 = WL.generate(wl.resized(seed=wl.seed + 7))["x"]
+    dev = torch.device("cuda:0")
+    d = {k: v.to(dev) for k, v in inputs.items()}
+    x, w, b = d["x"], d["w"], d.get("b")
+    say("prepared weight", wl.name, dims)
+    args = (wl.M, wl.N, wl.K, L.dtype_code(x), L.dtype_code(w), L.dtype_code(b) if b is not None else 0)
+    fo, ns = L.linear_workspace_layout(*args)
+    counts = lambda ws: int(ws[fo: fo + 4 * ns].cpu().view(torch.int32).sum().item()) if ns else 0
+    for xx in (x, x2.to(dev)):
+        ws0 = torch.empty(max(L.linear_workspace_size(*args), 1), dtype=torch.uint8, device=dev)
+        y0 = L.linear(xx, w, b, workspace=ws0)
+        ws1 = L.linear_prepare(w, wl.M, xx.dtype, b.dtype if b is not None else None)
+        y1 = L.linear(xx, w, b, workspace=ws1, prepared=True)
+        y2 = L.linear(xx, w, b, workspace=ws1, prepared=True)
+        torch.cuda.synchronize()
+        assert torch.equal(y0, y1) and torch.equal(y0, y2)
+        assert counts(ws0) == counts(ws1)
+
+
 @pytest.mark.parametrize("name,dims", [
     ("lora_bf16x_f32w_8192x4096x4096_r64", dict(M=257, N=200, K=264)),   # fp32 W, factors and y under bf16
     ("sweep_xf32_wf32_2048x1280x5120_r32", dict(M=130, N=96, K=136)),    # fp32 x still cast per call
