@@ -362,6 +362,13 @@ def test_full_size_sampled_rows(name):
     _check(wl, rows=rows)
 
 
+# every output row of the four configurations (the oracle on the host's cores:
+# about 40 s for the 16384 x 8192 x 8192 one), element by element
+@pytest.mark.parametrize("name", FULL[:4])
+def test_full_size_all_rows(name):
+    _check(BASE[name])
+
+
 @pytest.mark.parametrize("dims", [
     dict(),                                    # W split beforehand: 256 tiles of 64 x 64
     dict(M=1000, N=1100, K=520),               # ragged tiles
