@@ -394,8 +394,9 @@ def test_prepared_weight_gives_identical_output(dims):
         ws1 = L.linear_prepare(w, wl.M, xx.dtype, b.dtype if b is not None else None)
         y1 = L.linear(xx, w, b, workspace=ws1, prepared=True)
         y2 = L.linear(xx, w, b, workspace=ws1, prepared=True)
+        y3 = L.linear(xx, w, b, workspace=ws0, prepared=True)   # a plain call's workspace is prepared too
         torch.cuda.synchronize()
-        assert torch.equal(y0, y1) and torch.equal(y0, y2)
+        assert torch.equal(y0, y1) and torch.equal(y0, y2) and torch.equal(y0, y3)
         assert counts(ws0) == counts(ws1)
 
 
