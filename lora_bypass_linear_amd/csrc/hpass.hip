@@ -690,7 +690,7 @@ void xr_kernel(XrParams p) {
     // affine form).
     // Their loads are issued here and land in LDS with the k groups' partial
     // sums, so that one memory round trip overlaps the reduction (read in the
-    // epilogue, the 4 JB columns of each lane would take JB round trips in turn).
+    // epilogue, each lane's 4 JB columns would take JB round trips in turn).
     static_assert(64 * NW >= RP, "one thread per column");
     const bool ld_bn = SPLIT && !SB && p.guard && tid < cols_wg;
     const bool ld_bias = p.mode != XR_H && p.bias != nullptr && tid < RP;
