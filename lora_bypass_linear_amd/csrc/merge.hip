@@ -339,20 +339,17 @@ __device__ __forceinline__ void wait_vm_dyn(int n) {
     }
 }
 
-// buffer resource over rows n0 .. n0+15 of a [N][K] 16-bit matrix (fewer at the end)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rows(const void* base, int64_t n0, int64_t N, int64_t K) {
-    const int64_t rows = N - n0 < ST_N ? N - n0 : ST_N;
-    return make_rsrc_uniform((const char*)base + n0 * K * 2, (uint32_t)(rows * K * 2));
-}
-
 // Direct-to-LDS loads of one tile: W's 16 rows over the band, one row per
 // load (chunk c of row r in slot c ^ (r & 15) of its 1 KiB row), and up's 16
 // rows, 64 rank values per sub-tile (chunk c of row r in slot c ^ (r & 7),
 // lds_off), two loads per sub-tile.  Wave w takes loads w, w + 8, ...
 // Offsets past K, the rank or the tile's rows read zeros.
+// rw and ru cover all of W and up; wb and ub are the byte offsets of the
+// tile's first row in them (rows past N then lie past the resource: zeros).
 template <int RP>
 __device__ __forceinline__ void stream_issue(char* stage, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t ru,
-                                             int64_t kb0, int64_t K, int64_t rank, int wave, int lane) {
+                                             uint32_t wb, uint32_t ub, int64_t kb0, int64_t K, int64_t rank, int wave,
+                                             int lane) {
     constexpr int QL = st_ql<RP>();
 #pragma unroll
     for (int u = 0; u < (QL + 7) / 8; ++u) {
@@ -363,12 +360,12 @@ __device__ __forceinline__ void stream_issue(char* stage, __amdgpu_buffer_rsrc_t
             const int row = q, c = lane ^ (row & 15);
             const int64_t k = kb0 + 8 * c;
             const uint32_t off = k < K ? (uint32_t)(((int64_t)row * K + k) * 2) : OOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, off == OOB ? OOB : off + wb, 0, 0, 0);
         } else {
             const int qu = q - ST_N, sub = qu >> 1, row = (qu & 1) * 8 + (lane >> 3);
             const int64_t r = 64 * sub + 8 * ((lane & 7) ^ (row & 7));
             const uint32_t off = r < rank ? (uint32_t)(((int64_t)row * rank + r) * 2) : OOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, dst, 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, dst, 16, off == OOB ? OOB : off + ub, 0, 0, 0);
         }
     }
 }
@@ -413,12 +410,14 @@ __global__ __launch_bounds__(512, 1) void merge_stream_kernel(MergeParams p, int
         lds_barrier();
     }
 
+    // whole-matrix resources, made once (W, up and W' below 2 GiB); a tile's
+    // rows are a byte offset in them
+    const auto rw = make_rsrc_uniform(p.w, (uint32_t)(p.N * p.K * 2));
+    const auto ru = make_rsrc_uniform(p.up_raw, (uint32_t)(p.N * p.rank * 2));
+    const uint32_t wrow = (uint32_t)(ST_N * p.K * 2), urow = (uint32_t)(ST_N * p.rank * 2);   // bytes per tile
     for (int i = 0; i < NS - 1; ++i)
-        if (i < nt) {
-            const int64_t n0 = (int64_t)(t0 + i) * ST_N;
-            stream_issue<RP>(sm + i * SB, stream_rows(p.w, n0, p.N, p.K), stream_rows(p.up_raw, n0, p.N, p.rank), kb0,
-                             p.K, p.rank, wave, lane);
-        }
+        if (i < nt) stream_issue<RP>(sm + i * SB, rw, ru, (uint32_t)(t0 + i) * wrow, (uint32_t)(t0 + i) * urow, kb0,
+                                     p.K, p.rank, wave, lane);
     // norm mode: per-row sums of the 8 waves, [tile parity][wave][16 rows]; a
     // tile's are added up after the next tile's barrier
     float* red = (float*)(sm + st_red_at<RP>());
@@ -434,7 +433,7 @@ __global__ __launch_bounds__(512, 1) void merge_stream_kernel(MergeParams p, int
         // stores of the tiles before it issued since
         const int la = nt - 1 - i < NS - 2 ? nt - 1 - i : NS - 2;
         const int sa = NORM ? 0 : (i < NS - 1 ? i : NS - 1);
-        wait_vm_dyn<31>(QW * la + ST_STORES * sa);
+        wait_vm_dyn<QW * (NS - 2) + (NORM ? 0 : ST_STORES * (NS - 1))>(QW * la + ST_STORES * sa);
         lds_barrier();   // every wave's loads of tile i are in; tile i-1's stage is free
         if (NORM && i > 0 && tid < ST_N) {
             const float* rp = red + ((i - 1) & 1) * (8 * ST_N);
@@ -444,11 +443,9 @@ __global__ __launch_bounds__(512, 1) void merge_stream_kernel(MergeParams p, int
             for (int w = 1; w < 8; ++w) t += rp[w * ST_N + tid];
             if (n < p.N) p.norm_partial[(int64_t)band * p.N + n] = t;
         }
-        if (i + NS - 1 < nt) {
-            const int64_t nn = (int64_t)(t0 + i + NS - 1) * ST_N;
-            stream_issue<RP>(sm + ((u + NS - 1) % NS) * SB, stream_rows(p.w, nn, p.N, p.K),
-                             stream_rows(p.up_raw, nn, p.N, p.rank), kb0, p.K, p.rank, wave, lane);
-        }
+        if (i + NS - 1 < nt)
+            stream_issue<RP>(sm + ((u + NS - 1) % NS) * SB, rw, ru, (uint32_t)(t0 + i + NS - 1) * wrow,
+                             (uint32_t)(t0 + i + NS - 1) * urow, kb0, p.K, p.rank, wave, lane);
         char* st = sm + u * SB;
         const int64_t n0 = (int64_t)(t0 + i) * ST_N;
 
@@ -478,7 +475,6 @@ __global__ __launch_bounds__(512, 1) void merge_stream_kernel(MergeParams p, int
         float ss = 0.f;   // norm mode: the lane's sum of v^2 over its 16 columns of the tile
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            const int64_t kc = kb0 + 64 * wave + 16 * kb + 4 * (lane >> 4);   // the lane's first column
             float v[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -487,12 +483,10 @@ __global__ __launch_bounds__(512, 1) void merge_stream_kernel(MergeParams p, int
                 v[e] = __builtin_fmaf(p.scale, acc[kb][e], w);
             }
             if constexpr (NORM) {
-                const bool rin = n0 + row < p.N;
+                // (rows past N and columns past K are 0: W, up and down all
+                // read zeros there)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool in = rin && kc + e < p.K;
-                    ss = __builtin_fmaf(in ? v[e] : 0.f, in ? v[e] : 0.f, ss);
-                }
+                for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(v[e], v[e], ss);
             } else {
                 const uint32_t o0 = CT::dt == DT_F16 ? pack_f16x2(v[0], v[1]) : pack_bf16x2(v[0], v[1]);
                 const uint32_t o1 = CT::dt == DT_F16 ? pack_f16x2(v[2], v[3]) : pack_bf16x2(v[2], v[3]);
@@ -519,13 +513,13 @@ __global__ __launch_bounds__(512, 1) void merge_stream_kernel(MergeParams p, int
             // again here; 46.8 against 52.0 us at bf16 8192 x 8192); every store
             // is issued (past K or past the tile's rows its offset is out of
             // range), so the wait counts above hold
-            const auto ro = stream_rows(p.out, n0, p.N, p.K);
+            const auto ro = make_rsrc_uniform((const char*)p.out, (uint32_t)(p.N * p.K * 2));
 #pragma unroll
             for (int h = 0; h < ST_STORES; ++h) {
                 const int r = 8 * h + wave, c = lane;
                 const i32x4 v = *(const i32x4*)(st + r * ST_RB + ((c ^ r) << 4));
                 const int64_t k = kb0 + 8 * c;
-                const uint32_t off = k < p.K ? (uint32_t)(((int64_t)r * p.K + k) * 2) : OOB;
+                const uint32_t off = k < p.K ? (uint32_t)(((int64_t)r * p.K + k) * 2) + (uint32_t)(t0 + i) * wrow : OOB;
                 __builtin_amdgcn_raw_buffer_store_b128(v, ro, off, 0, 2);   // nontemporal
             }
         }
@@ -547,8 +541,8 @@ bool merge_streams(int c_dt, const MergeParams& p) {
     if (c_dt != DT_F16 && c_dt != DT_BF16) return false;
     if (p.w_dt != c_dt || (p.norm_partial == nullptr && p.out_dt != c_dt)) return false;
     return p.vec && p.down_raw != nullptr && p.up_raw != nullptr && p.rank > 0 && p.r_pad <= 128 &&
-           p.K * 2 * ST_N < ((int64_t)1 << 31) && p.rank * p.K * 2 < ((int64_t)1 << 31) &&
-           p.rank * 2 * ST_N < ((int64_t)1 << 31);
+           (p.N + ST_N) * p.K * 2 < ((int64_t)1 << 31) && p.rank * p.K * 2 < ((int64_t)1 << 31) &&
+           (p.N + ST_N) * p.rank * 2 < ((int64_t)1 << 31);
 }
 
 // runs (of row tiles) per band of 512 columns: about one workgroup per CU in all
