@@ -464,11 +464,7 @@ def _merge(dev, wl, inputs, reps, warm, accuracy):
          "kernels": {{"prep": "merge_prep_kernel", "gemm": kname}.get(k, k):
                      {"launches": n, "avg_us": round(ms * 1e3 / n, 3)} for k, (n, ms) in prof.items() if n},
          "hbm_gbs_call": round(nbytes / (dev_us * 1e-6) / 1e9, 1),
-         "roofline": {"bound": "hbm", "kernel": kname,
-                      "achieved": round(nbytes / (g_us * 1e-6) / 1e9, 1), "peak": HBM_GBS, "unit": "GB/s",
-                      "frac": round(nbytes / (g_us * 1e-6) / 1e9 / HBM_GBS, 4),
-                      "traffic": None if traffic is None else int(traffic), "bytes_per_launch": nbytes,
-                      "avg_us": round(g_us, 3)}}
+         "roofline": _stream_roofline(kname, nbytes, 2 * wl.N * wl.K * wl.r, c_dt, g_us, traffic)}
     if accuracy:
         import oracle
         from tests.gpu_cases import sample_rows, score
@@ -486,6 +482,26 @@ def _merge(dev, wl, inputs, reps, warm, accuracy):
                   "eager": {"max_ulp": round(se["ulp_max"], 4), "rms_ulp": round(se["ulp_rms"], 4),
                             "tol_fail": se["fail"]}})
     return r
+
+
+def _stream_roofline(kname, nbytes, flops, c_dt, avg_us, traffic):
+    """Roofline of a merge or row-norm launch: whichever of its HBM bytes at
+    8 TB/s and its contraction at the compute dtype's MFMA peak takes longer
+    is the bound (the fp32 contraction at 157.3 TFLOP/s can take longer than
+    the weight's stream)."""
+    hbm_us = nbytes / (HBM_GBS * 1e9) * 1e6
+    mfma_us = flops / (PEAK_TFLOPS[c_dt] * 1e12) * 1e6
+    floors = {"hbm_floor_us": round(hbm_us, 3), "mfma_floor_us": round(mfma_us, 3)}
+    if mfma_us > hbm_us:
+        ach = flops / (avg_us * 1e-6) / 1e12
+        return {"bound": "mfma", "kernel": kname, "achieved": round(ach, 2), "peak": PEAK_TFLOPS[c_dt],
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS[c_dt], 4),
+                "traffic": None if traffic is None else int(traffic), "bytes_per_launch": nbytes,
+                "flops_per_launch": flops, "avg_us": round(avg_us, 3), **floors}
+    ach = nbytes / (avg_us * 1e-6) / 1e9
+    return {"bound": "hbm", "kernel": kname, "achieved": round(ach, 1), "peak": HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_GBS, 4), "traffic": None if traffic is None else int(traffic),
+            "bytes_per_launch": nbytes, "flops_per_launch": flops, "avg_us": round(avg_us, 3), **floors}
 
 
 def _merge_kernel_name(c_dt, w_dt, d_dt, u_dt, o_dt, K, r):
@@ -550,11 +566,8 @@ def _dora(dev, wl, inputs, reps, warm, accuracy):
     traffic = read_traffic(os.path.join(ROOT, "profiles", f"traffic_doranorm_{wl.name}.txt"), "merge")
     out = {"shape": f"M {wl.M}, N {wl.N}, K {wl.K}, rank {wl.r}, magnitude {WL.NAME[L.dtype_code(m)]}",
            "norms": {"wall_us_per_call": round(wall_n, 2), "device_us_per_call": dev_us(prof_n),
-                     "roofline": {"bound": "hbm", "kernel": kname + " (row norms)",
-                                  "achieved": round(nbytes / (g_us * 1e-6) / 1e9, 1), "peak": HBM_GBS,
-                                  "unit": "GB/s", "frac": round(nbytes / (g_us * 1e-6) / 1e9 / HBM_GBS, 4),
-                                  "traffic": None if traffic is None else int(traffic), "bytes_per_launch": nbytes,
-                                  "avg_us": round(g_us, 3)}},
+                     "roofline": _stream_roofline(kname + " (row norms)", nbytes, 2 * wl.N * wl.K * wl.r,
+                                                  c_dt, g_us, traffic)},
            "forward": {"wall_us_per_call": round(wall_f, 2), "device_us_per_call": dev_us(prof_f),
                        "tflops": round(wl.flops / (dev_us(prof_f) * 1e-6) / 1e12, 2),
                        "lora_forward_device_us": dev_us(prof_l)}}
