@@ -438,10 +438,14 @@ int check_merge(Merge& G) {
 
 // down and up can be read as stored (no preparation pass): both already in a
 // 16-bit compute dtype, rank and K multiples of 8 (16-byte chunks), 16-byte
-// aligned, and down below 2 GiB (one buffer range)
+// aligned, and down below 2 GiB (one buffer range).  Rank rows past the rank
+// (up to the next multiple of 64) are read through offsets past the range,
+// which return zero; those rows too must lie below 2 GiB, or their 32-bit
+// offsets could wrap back into down.
 bool merge_reads_as_stored(const Merge& G, const void* down, const void* up) {
     return G.rank > 0 && G.c_dt != LYC_F32 && G.d_dt == G.c_dt && G.u_dt == G.c_dt && G.rank % 8 == 0 &&
-           G.K % 8 == 0 && aligned(down, 16) && aligned(up, 16) && G.rank * G.K * 2 < ((int64_t)1 << 31);
+           G.K % 8 == 0 && aligned(down, 16) && aligned(up, 16) &&
+           ((G.rank + 63) / 64) * 64 * G.K * 2 < ((int64_t)1 << 31);
 }
 
 // The factors' preparation pass (down^T_c and up_c), unless both are read as stored
